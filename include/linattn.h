@@ -1,0 +1,167 @@
+/*
+ * linattn.h -- C ABI of the MI355X (gfx950) causal linear-attention library.
+ *
+ * The method (phi = elu + 1 feature map; prefix states S_i, Z_i; readout
+ * phi(Q_i)^T S_i / phi(Q_i)^T Z_i) is defined on the page
+ * "[Paper walkthrough] Transformers are RNNs" (wkq9411.github.io):
+ *   section 2  -- phi(x) = elu(x) + 1 with alpha = 1, and the non-causal
+ *                 form phi(Q)(phi(K)^T V) (eq:linear);
+ *   section 3  -- the causal mask (eq:mask), S_i = sum_{j<=i} phi(K_j) V_j^T,
+ *                 Z_i = sum_{j<=i} phi(K_j), readout eq:output;
+ *   section 3.1 -- the cumulative-sum gradients eq:gq .. eq:gv;
+ *   section 4  -- the RNN form s_i = s_{i-1} + phi(k_i) v_i^T,
+ *                 z_i = z_{i-1} + phi(k_i), s_0 = z_0 = 0.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is DEVICE memory owned by the caller.  The library
+ *    allocates no device memory; scratch space comes from the caller's
+ *    `workspace` (size from la_workspace_bytes).  It keeps no state between
+ *    calls except a thread-local error string.
+ *  - Tensors are contiguous row-major: q, k [B,H,N,D]; v, out, dout
+ *    [B,H,N,M]; den [B,H,N]; decode state S [B,H,D,M], Z [B,H,D]; decode
+ *    inputs q, k [B,H,D], v, out [B,H,M].
+ *  - `dtype` (la_dtype) applies to q, k, v, out, dout, dq, dk, dv.  All
+ *    accumulation is fp32; den, S and Z are always fp32.  bf16 results are
+ *    rounded to nearest even.
+ *  - Sizes: B, H, N >= 1; 1 <= D, M <= 256 (LA_ERR_UNSUPPORTED otherwise).
+ *    bf16 tensors need 4-byte alignment, fp32 tensors 4-byte alignment;
+ *    16-byte alignment enables the vectorised fast paths.
+ *  - Outputs must not overlap inputs (LA_ERR_INVALID), except the decode
+ *    state S, Z, which is updated in place by design.
+ *  - Validation runs before any HIP call: null pointers, sizes < 1, unknown
+ *    dtype, overlapping buffers and a too-small workspace return at once
+ *    with LA_ERR_INVALID (or LA_ERR_UNSUPPORTED) and set la_last_error().
+ *  - Calls enqueue work on `stream` (NULL = the default stream) and return
+ *    without synchronising.  A launch failure returns LA_ERR_DEVICE; a fault
+ *    inside a kernel surfaces at the caller's next synchronisation.
+ *  - No atomics are used in reductions: for a fixed plan the results are
+ *    bitwise reproducible.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum la_status {
+  LA_OK = 0,
+  LA_ERR_INVALID = 1,     /* bad argument: null, size < 1, overlap, workspace */
+  LA_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. D or M > 256)   */
+  LA_ERR_DEVICE = 3       /* a HIP call failed (launch, stream)              */
+} la_status;
+
+typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+typedef enum la_op {
+  LA_OP_FORWARD = 0,
+  LA_OP_BACKWARD = 1,
+  LA_OP_PREFIX_STATE = 2,
+  LA_OP_DECODE = 3
+} la_op;
+
+/* Kernel family choice for the *_ex entry points (0 = automatic). */
+typedef enum la_kernel { LA_KERNEL_AUTO = 0, LA_KERNEL_GENERIC = 1, LA_KERNEL_MFMA = 2 } la_kernel;
+
+/* Tuning plan.  Every field 0 means "let the library choose".
+ *   chunk    -- tokens per intra-chunk tile (generic: 16/32/64; MFMA: 64)
+ *   segments -- how many independent pieces each sequence is cut into along
+ *               N; each piece's state is carried in by an exclusive scan of
+ *               the pieces before it (the prefix sums split exactly by
+ *               associativity).
+ *   kernel   -- la_kernel. */
+typedef struct la_plan {
+  int32_t chunk;
+  int32_t segments;
+  int32_t kernel;
+} la_plan;
+
+/* Forward.  out_i = phi(Q_i)^T S_i / phi(Q_i)^T Z_i (causal != 0, the sums
+ * run over j <= i: "Transformers are RNNs" walkthrough, section 3, eq:mask
+ * and eq:output) or phi(Q_i)^T S_N / phi(Q_i)^T Z_N (causal == 0: section 2,
+ * eq:linear).  No scale and no epsilon are applied.
+ *   q, k: [B,H,N,D]; v: [B,H,N,M]  (inputs, dtype)
+ *   out:  [B,H,N,M]                 (output, dtype)
+ *   den_out: [B,H,N] fp32 row denominators phi(Q_i)^T Z_i, or NULL.  Keep it
+ *            for la_backward, which can then skip recomputing it. */
+la_status la_forward(const void* q, const void* k, const void* v, void* out,
+                     int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                     int causal, int dtype, float* den_out,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+la_status la_forward_ex(const void* q, const void* k, const void* v, void* out,
+                        int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                        int causal, int dtype, float* den_out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream,
+                        const la_plan* plan);
+
+/* Backward of L = sum(dout * out) with respect to the RAW q, k, v.
+ * Numerator terms: "Transformers are RNNs" walkthrough, section 3.1,
+ * eq:gq (prefix matrix) and the phi(K) / V equations up to eq:gv (suffix
+ * matrix).  Normaliser terms (left there to autograd) by the chain rule:
+ * g_i = dout_i / den_i, c_i = -(dout_i . out_i) / den_i,
+ *   grad phi(Q_i) = S_i g_i + c_i Z_i,
+ *   grad phi(K_i) = R_i V_i + r_i,   grad V_i = R_i^T phi(K_i),
+ * with R_i = sum_{j>=i} phi(Q_j) g_j^T, r_i = sum_{j>=i} c_j phi(Q_j); then
+ * dq = grad phi(Q) * phi'(q), dk = grad phi(K) * phi'(k), dv = grad V.
+ *   q, k, v: forward inputs; out: the forward's output; dout: upstream grad
+ *   den: [B,H,N] fp32 from la_forward, or NULL (then it is recomputed)
+ *   dq, dk: [B,H,N,D]; dv: [B,H,N,M] (outputs, dtype) */
+la_status la_backward(const void* q, const void* k, const void* v, const void* out,
+                      const void* dout, const float* den, void* dq, void* dk, void* dv,
+                      int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                      int causal, int dtype,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+la_status la_backward_ex(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* den, void* dq, void* dk, void* dv,
+                         int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                         int causal, int dtype,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream,
+                         const la_plan* plan);
+
+/* One RNN decode step per (b,h), in place ("Transformers are RNNs"
+ * walkthrough, section 4; the state is updated first, then read):
+ *   S <- S + phi(k) v^T;  Z <- Z + phi(k);  out = phi(q)^T S / phi(q)^T Z.
+ *   S: [B,H,D,M] fp32, Z: [B,H,D] fp32 (in/out; caller-owned, so a saved
+ *      copy of S, Z is a checkpoint of the session)
+ *   q, k: [B,H,D]; v, out: [B,H,M] (dtype).  Needs no workspace. */
+la_status la_decode_step(float* S, float* Z, const void* q, const void* k, const void* v,
+                         void* out, int64_t B, int64_t H, int64_t D, int64_t M,
+                         int dtype, hipStream_t stream);
+
+/* State after a prefix (section 3's S_N, Z_N; overwrites S and Z):
+ *   S = sum_j phi(K_j) V_j^T, Z = sum_j phi(K_j) over the N tokens.
+ *   k: [B,H,N,D]; v: [B,H,N,M] (dtype); S: [B,H,D,M], Z: [B,H,D] fp32. */
+la_status la_prefix_state(const void* k, const void* v, float* S, float* Z,
+                          int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                          int dtype, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Workspace bytes an entry point needs for these sizes (0 if none).
+ * `op` is la_op; `plan` may be NULL (automatic plan, as the plain calls). */
+size_t la_workspace_bytes(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                          int causal, int dtype);
+size_t la_workspace_bytes_ex(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                             int causal, int dtype, const la_plan* plan);
+
+/* Resolve the automatic plan for a call (what la_forward / la_backward use). */
+la_status la_resolve_plan(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                          int causal, int dtype, const la_plan* requested, la_plan* resolved);
+
+const char* la_status_str(int status);
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* la_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int la_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

@@ -1,0 +1,203 @@
+"""MI355X-native causal linear attention (phi = elu + 1), "Transformers are RNNs".
+
+Thin Python binding over the C ABI of ``_lib/liblinattn.so`` (hand-written HIP
+kernels for gfx950).  The functions here only check tensor metadata, allocate
+outputs and workspace through torch and pass raw device pointers plus the
+current HIP stream; every step of the computation runs in the library's
+kernels.  Names follow the C ABI: ``forward`` -> ``la_forward``,
+``backward`` -> ``la_backward``, ``decode_step`` -> ``la_decode_step``,
+``prefix_state`` -> ``la_prefix_state``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+from . import _native
+from ._native import LinAttnError, la_plan  # noqa: F401
+
+__all__ = [
+    "forward", "backward", "decode_step", "prefix_state", "workspace_bytes", "resolve_plan",
+    "LinAttnError", "library_path", "version",
+]
+
+library_path = _native.LIB_PATH
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return _native.LA_F32
+    if t.dtype == torch.bfloat16:
+        return _native.LA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _plan(plan) -> Optional[la_plan]:
+    if plan is None:
+        return None
+    if isinstance(plan, la_plan):
+        return plan
+    return la_plan(int(plan.get("chunk", 0)), int(plan.get("segments", 0)), int(plan.get("kernel", 0)))
+
+
+def _plan_ref(p: Optional[la_plan]):
+    return None if p is None else ctypes.byref(p)
+
+
+def version() -> int:
+    return _native.load().la_version()
+
+
+def workspace_bytes(op: str, B, H, N, D, M, causal=True, dtype="f32", plan=None) -> int:
+    ops = {"forward": _native.LA_OP_FORWARD, "backward": _native.LA_OP_BACKWARD,
+           "prefix_state": _native.LA_OP_PREFIX_STATE, "decode": _native.LA_OP_DECODE}
+    dt = {"f32": _native.LA_F32, "bf16": _native.LA_BF16}[dtype]
+    p = _plan(plan)
+    return int(_native.load().la_workspace_bytes_ex(ops[op], B, H, N, D, M, int(bool(causal)), dt, _plan_ref(p)))
+
+
+def resolve_plan(op: str, B, H, N, D, M, causal=True, dtype="f32", plan=None) -> dict:
+    ops = {"forward": _native.LA_OP_FORWARD, "backward": _native.LA_OP_BACKWARD,
+           "prefix_state": _native.LA_OP_PREFIX_STATE}
+    dt = {"f32": _native.LA_F32, "bf16": _native.LA_BF16}[dtype]
+    out = la_plan()
+    _native.check(_native.load().la_resolve_plan(ops[op], B, H, N, D, M, int(bool(causal)), dt,
+                                                 _plan_ref(_plan(plan)), ctypes.byref(out)))
+    return {"chunk": out.chunk, "segments": out.segments, "kernel": out.kernel}
+
+
+def _workspace(nbytes: int, device):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def forward(q, k, v, causal: bool = True, return_den: bool = False, plan=None, stream=None,
+            out=None, den=None, workspace=None):
+    """V' = phi(Q) S / phi(Q) Z (causal) or phi(Q)(phi(K)^T V) normalised.
+
+    q, k: [B,H,N,D]; v: [B,H,N,M]; float32 or bfloat16 (all the same).
+    Returns out [B,H,N,M] (and den [B,H,N] fp32 when return_den).
+    """
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    B, H, N, D = q.shape
+    M = v.shape[3]
+    dt = _dtype_code(q)
+    p = _plan(plan)
+    lib = _native.load()
+    if out is None:
+        out = torch.empty((B, H, N, M), dtype=q.dtype, device=q.device)
+    if return_den and den is None:
+        den = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    need = int(lib.la_workspace_bytes_ex(_native.LA_OP_FORWARD, B, H, N, D, M, int(bool(causal)), dt, _plan_ref(p)))
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    _native.check(lib.la_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, D, M,
+                                    int(bool(causal)), dt, _ptr(den), _ptr(ws), wsz, _stream(stream),
+                                    _plan_ref(p)))
+    return (out, den) if return_den else out
+
+
+def backward(q, k, v, out, dout, den=None, causal: bool = True, plan=None, stream=None,
+             workspace=None) -> Tuple:
+    """Gradients (dq, dk, dv) of sum(dout * out) w.r.t. the raw q, k, v."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _dev(t, n)
+    B, H, N, D = q.shape
+    M = v.shape[3]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or out.shape != v.shape or dout.shape != v.shape:
+        raise ValueError("shape mismatch")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise TypeError("q, k, v, out, dout must share one dtype")
+    if den is not None:
+        _dev(den, "den")
+        if den.dtype != torch.float32 or tuple(den.shape) != (B, H, N):
+            raise ValueError("den must be float32 [B,H,N]")
+    dt = _dtype_code(q)
+    p = _plan(plan)
+    lib = _native.load()
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    need = int(lib.la_workspace_bytes_ex(_native.LA_OP_BACKWARD, B, H, N, D, M, int(bool(causal)), dt, _plan_ref(p)))
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    _native.check(lib.la_backward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                                     _ptr(den), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, M,
+                                     int(bool(causal)), dt, _ptr(ws), wsz, _stream(stream), _plan_ref(p)))
+    return dq, dk, dv
+
+
+def decode_step(S, Z, q, k, v, out=None, stream=None):
+    """One in-place RNN step: S += phi(k) v^T, Z += phi(k); returns
+    out = phi(q)^T S / phi(q)^T Z.  S [B,H,D,M] fp32, Z [B,H,D] fp32,
+    q, k [B,H,D], v [B,H,M] (float32 or bfloat16)."""
+    torch = _torch()
+    for t, n in ((S, "S"), (Z, "Z"), (q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    if S.dtype != torch.float32 or Z.dtype != torch.float32:
+        raise TypeError("S and Z are float32")
+    B, H, D, M = S.shape
+    if tuple(Z.shape) != (B, H, D) or tuple(q.shape) != (B, H, D) or k.shape != q.shape or tuple(v.shape) != (B, H, M):
+        raise ValueError("shape mismatch")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, H, M), dtype=q.dtype, device=q.device)
+    _native.check(_native.load().la_decode_step(S.data_ptr(), Z.data_ptr(), q.data_ptr(), k.data_ptr(),
+                                                v.data_ptr(), out.data_ptr(), B, H, D, M, dt, _stream(stream)))
+    return out
+
+
+def prefix_state(k, v, S=None, Z=None, stream=None):
+    """S = sum_j phi(K_j) V_j^T, Z = sum_j phi(K_j) over the N tokens of k, v."""
+    torch = _torch()
+    _dev(k, "k")
+    _dev(v, "v")
+    B, H, N, D = k.shape
+    M = v.shape[3]
+    dt = _dtype_code(k)
+    if S is None:
+        S = torch.empty((B, H, D, M), dtype=torch.float32, device=k.device)
+    if Z is None:
+        Z = torch.empty((B, H, D), dtype=torch.float32, device=k.device)
+    lib = _native.load()
+    need = int(lib.la_workspace_bytes(_native.LA_OP_PREFIX_STATE, B, H, N, D, M, 1, dt))
+    ws = _workspace(need, k.device)
+    wsz = 0 if ws is None else ws.numel()
+    _native.check(lib.la_prefix_state(k.data_ptr(), v.data_ptr(), S.data_ptr(), Z.data_ptr(), B, H, N, D, M, dt,
+                                      _ptr(ws), wsz, _stream(stream)))
+    return S, Z

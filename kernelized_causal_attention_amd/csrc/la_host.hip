@@ -1,0 +1,494 @@
+// C ABI of the library: argument validation (before any HIP call), plan
+// choice, workspace carving and kernel dispatch.  See include/linattn.h.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "la_internal.h"
+#include "linattn.h"
+
+#define LA_API extern "C" __attribute__((visibility("default")))
+
+namespace la {
+int mfma_supported(int op, int64_t D, int64_t M, int dtype);
+hipError_t launch_forward_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
+                               void* out, float* den_out, const float* carry, hipStream_t st);
+hipError_t launch_seg_state_mfma(const SegGeom& g, const void* k, const void* v, float* s_out,
+                                 int64_t s_stride, float* z_out, int64_t z_stride, hipStream_t st);
+hipError_t launch_bwd_dq_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
+                              const void* out, const void* dout, const float* den, const float* carry_s,
+                              void* dq, float* r_agg, hipStream_t st);
+hipError_t launch_bwd_dkdv_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
+                                const void* out, const void* dout, const float* den, const float* carry_r,
+                                void* dk, void* dv, hipStream_t st);
+}  // namespace la
+
+namespace {
+
+thread_local std::string g_err;
+
+la_status fail(la_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+la_status ok() {
+  g_err.clear();
+  return LA_OK;
+}
+
+la_status dev(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(LA_ERR_DEVICE, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxFeat = 256;
+constexpr int64_t kMaxState = 16384;  // D*M floats of state per head
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr size_t kAlign = 256;
+
+size_t dtype_size(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
+
+struct Span {
+  const char* name;
+  uintptr_t lo, hi;
+};
+
+Span span(const char* name, const void* p, int64_t elems, size_t esz) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Span{name, lo, lo + static_cast<uintptr_t>(elems) * esz};
+}
+
+bool overlap(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+la_status check_sizes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype) {
+  if (B < 1 || H < 1 || N < 1 || D < 1 || M < 1)
+    return fail(LA_ERR_INVALID, "sizes must be >= 1 (B=%lld H=%lld N=%lld D=%lld M=%lld)", (long long)B,
+                (long long)H, (long long)N, (long long)D, (long long)M);
+  if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (D > kMaxFeat || M > kMaxFeat || D * M > kMaxState)
+    return fail(LA_ERR_UNSUPPORTED, "D=%lld, M=%lld: need D, M <= 256 and D*M <= 16384", (long long)D,
+                (long long)M);
+  if (B * H > kMaxElems || B * H * N > kMaxElems || B * H * N * std::max(D, M) > kMaxElems)
+    return fail(LA_ERR_UNSUPPORTED, "problem too large (B*H*N*max(D,M) > 2^40)");
+  return LA_OK;
+}
+
+la_status check_ptr(const void* p, const char* name, int dtype) {
+  if (!p) return fail(LA_ERR_INVALID, "%s is NULL", name);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const size_t need = dtype_size(dtype);
+  if (a % need) return fail(LA_ERR_INVALID, "%s is not %zu-byte aligned", name, need);
+  return LA_OK;
+}
+
+la_status check_disjoint(const Span* outs, int nout, const Span* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    if (!outs[i].lo) continue;
+    for (int j = 0; j < nin; ++j)
+      if (ins[j].lo && overlap(outs[i], ins[j]))
+        return fail(LA_ERR_INVALID, "output %s overlaps input %s", outs[i].name, ins[j].name);
+    for (int j = i + 1; j < nout; ++j)
+      if (outs[j].lo && overlap(outs[i], outs[j]))
+        return fail(LA_ERR_INVALID, "outputs %s and %s overlap", outs[i].name, outs[j].name);
+  }
+  return LA_OK;
+}
+
+// ---------------------------------------------------------------- plans ----
+struct Plan {
+  int kernel;    // LA_KERNEL_GENERIC or LA_KERNEL_MFMA
+  int P;         // segments
+  int seg_len;   // tokens per segment
+  int chunk;     // chunk used by the forward-type kernels (informational)
+};
+
+la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal, int dtype,
+                  const la_plan* req, Plan* out) {
+  (void)causal;
+  int kernel = req ? req->kernel : LA_KERNEL_AUTO;
+  if (kernel < LA_KERNEL_AUTO || kernel > LA_KERNEL_MFMA) return fail(LA_ERR_INVALID, "plan.kernel=%d", kernel);
+  const int mfma_ok = la::mfma_supported(op, D, M, dtype);
+  if (kernel == LA_KERNEL_MFMA && !mfma_ok)
+    return fail(LA_ERR_UNSUPPORTED, "no MFMA kernel for op %d, D=%lld, M=%lld, dtype %d", op, (long long)D,
+                (long long)M, dtype);
+  if (kernel == LA_KERNEL_AUTO) kernel = mfma_ok ? LA_KERNEL_MFMA : LA_KERNEL_GENERIC;
+  const int unit = kernel == LA_KERNEL_MFMA ? 64 : 32;  // segment granularity
+  int chunk = req ? req->chunk : 0;
+  if (kernel == LA_KERNEL_GENERIC) {
+    if (chunk != 0 && chunk != 16 && chunk != 32)
+      return fail(LA_ERR_INVALID, "plan.chunk=%d (generic kernels take 16 or 32)", chunk);
+    const int tc = la::generic_chunk_for((int)D, (int)M, op == LA_OP_BACKWARD ? 3 : 0);
+    if (tc == 0) return fail(LA_ERR_UNSUPPORTED, "D=%lld, M=%lld do not fit in LDS", (long long)D, (long long)M);
+    if (chunk == 0 || chunk > tc) chunk = tc;
+  } else {
+    if (chunk != 0 && chunk != 64) return fail(LA_ERR_INVALID, "plan.chunk=%d (MFMA kernels take 64)", chunk);
+    chunk = 64;
+  }
+  const int64_t nunits = (N + unit - 1) / unit;
+  const int64_t BH = B * H;
+  int64_t P = req && req->segments > 0 ? req->segments : 0;
+  if (req && req->segments < 0) return fail(LA_ERR_INVALID, "plan.segments=%d", req->segments);
+  if (P == 0) {
+    // Enough independent workgroups to cover 256 CUs about twice over,
+    // with segments of at least 4 units.
+    const int64_t want = (512 + BH - 1) / BH;
+    P = std::min<int64_t>(want, std::max<int64_t>(1, nunits / 4));
+  }
+  P = std::max<int64_t>(1, std::min<int64_t>(P, nunits));
+  const int64_t seg_units = (nunits + P - 1) / P;
+  const int64_t seg_len = seg_units * unit;
+  P = (N + seg_len - 1) / seg_len;
+  if (BH * P > 0xffffffffLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
+  if (seg_len > 0x7fffffffLL) return fail(LA_ERR_UNSUPPORTED, "segment too long");
+  out->kernel = kernel;
+  out->P = static_cast<int>(P);
+  out->seg_len = static_cast<int>(seg_len);
+  out->chunk = chunk;
+  return LA_OK;
+}
+
+// Workspace carving: regions of floats, each 256-byte aligned.
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t floats) {
+    const size_t at = off;
+    off += (floats * sizeof(float) + kAlign - 1) / kAlign * kAlign;
+    return at;
+  }
+};
+
+struct WsLayout {
+  size_t aggS = 0, totS = 0, aggR = 0, totR = 0, den = 0;
+  size_t bytes = 0;
+};
+
+WsLayout layout(int op, int64_t BH, int64_t N, int64_t D, int64_t M, int causal, const Plan& p) {
+  WsLayout w;
+  Carve c;
+  const size_t E = static_cast<size_t>(D * M + D);
+  const size_t recs = static_cast<size_t>(BH) * p.P * E;
+  if (op == LA_OP_FORWARD) {
+    if (causal) {
+      if (p.P > 1) w.aggS = c.take(recs);
+    } else {
+      w.aggS = c.take(recs);
+      w.totS = c.take(static_cast<size_t>(BH) * E);
+    }
+  } else if (op == LA_OP_BACKWARD) {
+    w.aggS = c.take(recs);
+    w.totS = c.take(static_cast<size_t>(BH) * E);
+    w.aggR = c.take(recs);
+    w.totR = c.take(static_cast<size_t>(BH) * E);
+    w.den = c.take(static_cast<size_t>(BH) * N);
+  } else if (op == LA_OP_PREFIX_STATE) {
+    if (p.P > 1) w.aggS = c.take(recs);
+  }
+  w.bytes = c.off;
+  return w;
+}
+
+float* at(void* ws, size_t off) { return reinterpret_cast<float*>(static_cast<char*>(ws) + off); }
+
+}  // namespace
+
+// ============================================================ dispatch ====
+namespace {
+
+la::SegGeom geom(int64_t BH, int64_t N, int64_t D, int64_t M, const Plan& p, int chunk) {
+  la::SegGeom g;
+  g.BH = BH;
+  g.N = N;
+  g.D = static_cast<int>(D);
+  g.M = static_cast<int>(M);
+  g.P = p.P;
+  g.seg_len = p.seg_len;
+  g.chunk = chunk;
+  return g;
+}
+
+// Segment aggregates of (S, Z) into ws records [BH][P][E].
+hipError_t seg_state(int dtype, const Plan& p, const la::SegGeom& gbase, const void* k, const void* v,
+                     float* recs, hipStream_t st) {
+  const int64_t E = la::state_elems(gbase.D, gbase.M);
+  const int64_t DM = static_cast<int64_t>(gbase.D) * gbase.M;
+  if (p.kernel == LA_KERNEL_MFMA) return la::launch_seg_state_mfma(gbase, k, v, recs, E, recs + DM, E, st);
+  la::SegGeom g = gbase;
+  g.chunk = la::generic_chunk_for(g.D, g.M, 1);
+  return la::launch_seg_state_generic(dtype, g, k, v, recs, E, recs + DM, E, st);
+}
+
+hipError_t fwd_pass(int dtype, int causal, const Plan& p, const la::SegGeom& gbase, const void* q,
+                    const void* k, const void* v, void* out, float* den_out, const float* carry,
+                    hipStream_t st) {
+  if (p.kernel == LA_KERNEL_MFMA) return la::launch_forward_mfma(causal, gbase, q, k, v, out, den_out, carry, st);
+  la::SegGeom g = gbase;
+  g.chunk = std::min(p.chunk, la::generic_chunk_for(g.D, g.M, 0));
+  return la::launch_forward_generic(dtype, causal, g, q, k, v, out, den_out, carry, st);
+}
+
+la_status do_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H, int64_t N,
+                     int64_t D, int64_t M, int causal, int dtype, float* den_out, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream, const la_plan* plan) {
+  la_status s = check_sizes(B, H, N, D, M, dtype);
+  if (s != LA_OK) return s;
+  causal = causal ? 1 : 0;
+  if ((s = check_ptr(q, "q", dtype)) || (s = check_ptr(k, "k", dtype)) || (s = check_ptr(v, "v", dtype)) ||
+      (s = check_ptr(out, "out", dtype)))
+    return s;
+  if (den_out && (reinterpret_cast<uintptr_t>(den_out) & 3)) return fail(LA_ERR_INVALID, "den_out misaligned");
+  const int64_t BH = B * H;
+  const size_t es = dtype_size(dtype);
+  const Span ins[] = {span("q", q, BH * N * D, es), span("k", k, BH * N * D, es), span("v", v, BH * N * M, es),
+                      span("workspace", workspace, workspace ? (int64_t)workspace_bytes : 0, 1)};
+  const Span outs[] = {span("out", out, BH * N * M, es), span("den_out", den_out, den_out ? BH * N : 0, 4)};
+  if ((s = check_disjoint(outs, 2, ins, 4))) return s;
+  Plan p;
+  if ((s = resolve(LA_OP_FORWARD, B, H, N, D, M, causal, dtype, plan, &p))) return s;
+  const WsLayout w = layout(LA_OP_FORWARD, BH, N, D, M, causal, p);
+  if (workspace_bytes < w.bytes)
+    return fail(LA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, w.bytes);
+  if (w.bytes && !workspace) return fail(LA_ERR_INVALID, "workspace is NULL (%zu bytes needed)", w.bytes);
+  if (w.bytes && (reinterpret_cast<uintptr_t>(workspace) & 15))
+    return fail(LA_ERR_INVALID, "workspace must be 16-byte aligned");
+
+  const la::SegGeom g = geom(BH, N, D, M, p, p.chunk);
+  hipError_t e;
+  if (causal) {
+    const float* carry = nullptr;
+    if (p.P > 1) {
+      float* agg = at(workspace, w.aggS);
+      if ((e = seg_state(dtype, p, g, k, v, agg, stream))) return dev(e, "segment state");
+      if ((e = la::launch_seg_scan(agg, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream)))
+        return dev(e, "segment scan");
+      carry = agg;
+    }
+    return dev(fwd_pass(dtype, 1, p, g, q, k, v, out, den_out, carry, stream), "forward");
+  }
+  float* agg = at(workspace, w.aggS);
+  float* tot = at(workspace, w.totS);
+  const int64_t E = la::state_elems(g.D, g.M);
+  if ((e = seg_state(dtype, p, g, k, v, agg, stream))) return dev(e, "segment state");
+  if ((e = la::launch_seg_scan(agg, BH, p.P, g.D, g.M, 0, tot, E, tot + D * M, E, stream)))
+    return dev(e, "segment scan");
+  return dev(fwd_pass(dtype, 0, p, g, q, k, v, out, den_out, tot, stream), "forward");
+}
+
+la_status do_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* den, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
+                      int64_t D, int64_t M, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream, const la_plan* plan) {
+  la_status s = check_sizes(B, H, N, D, M, dtype);
+  if (s != LA_OK) return s;
+  causal = causal ? 1 : 0;
+  if ((s = check_ptr(q, "q", dtype)) || (s = check_ptr(k, "k", dtype)) || (s = check_ptr(v, "v", dtype)) ||
+      (s = check_ptr(out, "out", dtype)) || (s = check_ptr(dout, "dout", dtype)) ||
+      (s = check_ptr(dq, "dq", dtype)) || (s = check_ptr(dk, "dk", dtype)) || (s = check_ptr(dv, "dv", dtype)))
+    return s;
+  if (den && (reinterpret_cast<uintptr_t>(den) & 3)) return fail(LA_ERR_INVALID, "den misaligned");
+  const int64_t BH = B * H;
+  const size_t es = dtype_size(dtype);
+  const Span ins[] = {span("q", q, BH * N * D, es),       span("k", k, BH * N * D, es),
+                      span("v", v, BH * N * M, es),       span("out", out, BH * N * M, es),
+                      span("dout", dout, BH * N * M, es), span("den", den, den ? BH * N : 0, 4),
+                      span("workspace", workspace, workspace ? (int64_t)workspace_bytes : 0, 1)};
+  const Span outs[] = {span("dq", dq, BH * N * D, es), span("dk", dk, BH * N * D, es),
+                       span("dv", dv, BH * N * M, es)};
+  if ((s = check_disjoint(outs, 3, ins, 7))) return s;
+  Plan p;
+  if ((s = resolve(LA_OP_BACKWARD, B, H, N, D, M, causal, dtype, plan, &p))) return s;
+  const WsLayout w = layout(LA_OP_BACKWARD, BH, N, D, M, causal, p);
+  if (workspace_bytes < w.bytes)
+    return fail(LA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, w.bytes);
+  if (!workspace) return fail(LA_ERR_INVALID, "workspace is NULL (%zu bytes needed)", w.bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 15) return fail(LA_ERR_INVALID, "workspace must be 16-byte aligned");
+
+  const la::SegGeom g = geom(BH, N, D, M, p, p.chunk);
+  const int64_t E = la::state_elems(g.D, g.M);
+  float* aggS = at(workspace, w.aggS);
+  float* totS = at(workspace, w.totS);
+  float* aggR = at(workspace, w.aggR);
+  float* totR = at(workspace, w.totR);
+  hipError_t e;
+  const float* carry_s = nullptr;
+  if (causal) {
+    if (p.P > 1) {
+      if ((e = seg_state(dtype, p, g, k, v, aggS, stream))) return dev(e, "segment state");
+      if ((e = la::launch_seg_scan(aggS, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream)))
+        return dev(e, "segment scan");
+      carry_s = aggS;
+    }
+  } else {
+    if ((e = seg_state(dtype, p, g, k, v, aggS, stream))) return dev(e, "segment state");
+    if ((e = la::launch_seg_scan(aggS, BH, p.P, g.D, g.M, 0, totS, E, totS + D * M, E, stream)))
+      return dev(e, "segment scan");
+    carry_s = totS;
+  }
+  if (!den) {
+    float* dw = at(workspace, w.den);
+    if ((e = fwd_pass(dtype, causal, p, g, q, k, v, nullptr, dw, carry_s, stream))) return dev(e, "denominator");
+    den = dw;
+  }
+  float* r_agg = (causal && p.P == 1) ? nullptr : aggR;
+  if (p.kernel == LA_KERNEL_MFMA) {
+    e = la::launch_bwd_dq_mfma(causal, g, q, k, v, out, dout, den, carry_s, dq, r_agg, stream);
+  } else {
+    la::SegGeom gd = g;
+    gd.chunk = std::min(p.chunk, la::generic_chunk_for(g.D, g.M, 2));
+    e = la::launch_bwd_dq_generic(dtype, causal, gd, q, k, v, out, dout, den, carry_s, dq, r_agg, stream);
+  }
+  if (e) return dev(e, "backward dq");
+  const float* carry_r = nullptr;
+  if (causal) {
+    if (p.P > 1) {
+      if ((e = la::launch_seg_scan(aggR, BH, p.P, g.D, g.M, 1, nullptr, 0, nullptr, 0, stream)))
+        return dev(e, "suffix scan");
+      carry_r = aggR;
+    }
+  } else {
+    if ((e = la::launch_seg_scan(aggR, BH, p.P, g.D, g.M, 1, totR, E, totR + D * M, E, stream)))
+      return dev(e, "suffix scan");
+    carry_r = totR;
+  }
+  if (p.kernel == LA_KERNEL_MFMA) {
+    e = la::launch_bwd_dkdv_mfma(causal, g, q, k, v, out, dout, den, carry_r, dk, dv, stream);
+  } else {
+    la::SegGeom gk = g;
+    gk.chunk = std::min(p.chunk, la::generic_chunk_for(g.D, g.M, 3));
+    e = la::launch_bwd_dkdv_generic(dtype, causal, gk, q, k, v, out, dout, den, carry_r, dk, dv, stream);
+  }
+  return dev(e, "backward dk/dv");
+}
+
+}  // namespace
+
+// ================================================================ ABI ====
+LA_API la_status la_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
+                            int64_t N, int64_t D, int64_t M, int causal, int dtype, float* den_out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return do_forward(q, k, v, out, B, H, N, D, M, causal, dtype, den_out, workspace, workspace_bytes, stream,
+                    nullptr);
+}
+
+LA_API la_status la_forward_ex(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
+                               int64_t N, int64_t D, int64_t M, int causal, int dtype, float* den_out,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream,
+                               const la_plan* plan) {
+  return do_forward(q, k, v, out, B, H, N, D, M, causal, dtype, den_out, workspace, workspace_bytes, stream,
+                    plan);
+}
+
+LA_API la_status la_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                             const float* den, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
+                             int64_t D, int64_t M, int causal, int dtype, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return do_backward(q, k, v, out, dout, den, dq, dk, dv, B, H, N, D, M, causal, dtype, workspace,
+                     workspace_bytes, stream, nullptr);
+}
+
+LA_API la_status la_backward_ex(const void* q, const void* k, const void* v, const void* out,
+                                const void* dout, const float* den, void* dq, void* dk, void* dv, int64_t B,
+                                int64_t H, int64_t N, int64_t D, int64_t M, int causal, int dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                const la_plan* plan) {
+  return do_backward(q, k, v, out, dout, den, dq, dk, dv, B, H, N, D, M, causal, dtype, workspace,
+                     workspace_bytes, stream, plan);
+}
+
+LA_API la_status la_decode_step(float* S, float* Z, const void* q, const void* k, const void* v, void* out,
+                                int64_t B, int64_t H, int64_t D, int64_t M, int dtype, hipStream_t stream) {
+  la_status s = check_sizes(B, H, 1, D, M, dtype);
+  if (s != LA_OK) return s;
+  if ((s = check_ptr(S, "S", LA_F32)) || (s = check_ptr(Z, "Z", LA_F32)) || (s = check_ptr(q, "q", dtype)) ||
+      (s = check_ptr(k, "k", dtype)) || (s = check_ptr(v, "v", dtype)) || (s = check_ptr(out, "out", dtype)))
+    return s;
+  const int64_t BH = B * H;
+  const size_t es = dtype_size(dtype);
+  const Span ins[] = {span("q", q, BH * D, es), span("k", k, BH * D, es), span("v", v, BH * M, es)};
+  const Span outs[] = {span("S", S, BH * D * M, 4), span("Z", Z, BH * D, 4), span("out", out, BH * M, es)};
+  if ((s = check_disjoint(outs, 3, ins, 3))) return s;
+  if (BH > 0xffffffffLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
+  return dev(la::launch_decode_step(dtype, BH, (int)D, (int)M, S, Z, q, k, v, out, stream), "decode step");
+}
+
+LA_API la_status la_prefix_state(const void* k, const void* v, float* S, float* Z, int64_t B, int64_t H,
+                                 int64_t N, int64_t D, int64_t M, int dtype, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  la_status s = check_sizes(B, H, N, D, M, dtype);
+  if (s != LA_OK) return s;
+  if ((s = check_ptr(k, "k", dtype)) || (s = check_ptr(v, "v", dtype)) || (s = check_ptr(S, "S", LA_F32)) ||
+      (s = check_ptr(Z, "Z", LA_F32)))
+    return s;
+  const int64_t BH = B * H;
+  const size_t es = dtype_size(dtype);
+  const Span ins[] = {span("k", k, BH * N * D, es), span("v", v, BH * N * M, es),
+                      span("workspace", workspace, workspace ? (int64_t)workspace_bytes : 0, 1)};
+  const Span outs[] = {span("S", S, BH * D * M, 4), span("Z", Z, BH * D, 4)};
+  if ((s = check_disjoint(outs, 2, ins, 3))) return s;
+  Plan p;
+  if ((s = resolve(LA_OP_PREFIX_STATE, B, H, N, D, M, 1, dtype, nullptr, &p))) return s;
+  const WsLayout w = layout(LA_OP_PREFIX_STATE, BH, N, D, M, 1, p);
+  if (workspace_bytes < w.bytes)
+    return fail(LA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, w.bytes);
+  if (w.bytes && !workspace) return fail(LA_ERR_INVALID, "workspace is NULL (%zu bytes needed)", w.bytes);
+  const la::SegGeom g = geom(BH, N, D, M, p, p.chunk);
+  hipError_t e;
+  if (p.P == 1) {
+    if (p.kernel == LA_KERNEL_MFMA) return dev(la::launch_seg_state_mfma(g, k, v, S, D * M, Z, D, stream), "prefix state");
+    la::SegGeom gs = g;
+    gs.chunk = la::generic_chunk_for(g.D, g.M, 1);
+    return dev(la::launch_seg_state_generic(dtype, gs, k, v, S, D * M, Z, D, stream), "prefix state");
+  }
+  float* agg = at(workspace, w.aggS);
+  if ((e = seg_state(dtype, p, g, k, v, agg, stream))) return dev(e, "prefix state");
+  return dev(la::launch_seg_scan(agg, BH, p.P, g.D, g.M, 0, S, D * M, Z, D, stream), "prefix scan");
+}
+
+LA_API size_t la_workspace_bytes_ex(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
+                                    int dtype, const la_plan* plan) {
+  if (op == LA_OP_DECODE) return 0;
+  if (check_sizes(B, H, N, D, M, dtype) != LA_OK) return 0;
+  Plan p;
+  if (resolve(op, B, H, N, D, M, causal ? 1 : 0, dtype, op == LA_OP_PREFIX_STATE ? nullptr : plan, &p) != LA_OK)
+    return 0;
+  return layout(op, B * H, N, D, M, causal ? 1 : 0, p).bytes;
+}
+
+LA_API size_t la_workspace_bytes(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
+                                 int dtype) {
+  return la_workspace_bytes_ex(op, B, H, N, D, M, causal, dtype, nullptr);
+}
+
+LA_API la_status la_resolve_plan(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
+                                 int dtype, const la_plan* requested, la_plan* resolved) {
+  la_status s = check_sizes(B, H, N, D, M, dtype);
+  if (s != LA_OK) return s;
+  if (!resolved) return fail(LA_ERR_INVALID, "resolved is NULL");
+  Plan p;
+  if ((s = resolve(op, B, H, N, D, M, causal ? 1 : 0, dtype, requested, &p))) return s;
+  resolved->chunk = p.chunk;
+  resolved->segments = p.P;
+  resolved->kernel = p.kernel;
+  return ok();
+}
+
+LA_API const char* la_status_str(int status) {
+  switch (status) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_INVALID: return "LA_ERR_INVALID";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
+    case LA_ERR_DEVICE: return "LA_ERR_DEVICE";
+    default: return "LA_UNKNOWN_STATUS";
+  }
+}
+
+LA_API const char* la_last_error(void) { return g_err.c_str(); }
+
+LA_API int la_version(void) { return 100; }

@@ -1,0 +1,67 @@
+// Host-side launch interface between the C ABI (la_host.hip) and the kernel
+// translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+// Per-head state record in a workspace: D*M floats of S (row-major [D][M])
+// followed by D floats of Z; E = D*M + D.
+inline int64_t state_elems(int D, int M) { return static_cast<int64_t>(D) * M + D; }
+
+struct SegGeom {
+  int64_t BH;   // B * H independent sequences
+  int64_t N;    // tokens per sequence
+  int D, M;     // feature widths
+  int P;        // segments per sequence
+  int seg_len;  // tokens per segment (a multiple of the chunk)
+  int chunk;    // tokens per intra-chunk tile
+};
+
+// ---- generic kernels (any D, M with D*M <= 16384, fp32 or bf16 inputs) ----
+// dtype: 0 = fp32, 1 = bf16 (raw 16-bit).
+
+// Largest chunk (32 or 16) whose LDS footprint fits a CU for kernel `which`
+// (0 forward, 1 segment state, 2 backward dq, 3 backward dk/dv); 0 if none.
+int generic_chunk_for(int D, int M, int which);
+
+// Segment aggregates dS = sum phi(K_j) V_j^T, dZ = sum phi(K_j) over each
+// segment; written at s_out + (bh*P + s)*s_stride and z_out + (bh*P + s)*z_stride.
+hipError_t launch_seg_state_generic(int dtype, const SegGeom& g, const void* k, const void* v,
+                                    float* s_out, int64_t s_stride, float* z_out, int64_t z_stride,
+                                    hipStream_t st);
+
+// In-place exclusive scan of [BH][P][E] records over the segment axis
+// (reverse = suffix sums).  The inclusive total of each head goes to
+// tot_s + bh*ts_stride (first D*M entries) and tot_z + bh*tz_stride (last D),
+// when tot_s is not null.
+hipError_t launch_seg_scan(float* agg, int64_t BH, int P, int D, int M, int reverse,
+                           float* tot_s, int64_t ts_stride, float* tot_z, int64_t tz_stride,
+                           hipStream_t st);
+
+// Chunked forward.  carry: per-(bh, segment) exclusive prefix records
+// (causal) or per-bh totals (non-causal), or null for a zero state (P == 1).
+// out may be null (then only den_out is produced).
+hipError_t launch_forward_generic(int dtype, int causal, const SegGeom& g, const void* q, const void* k,
+                                  const void* v, void* out, float* den_out, const float* carry,
+                                  hipStream_t st);
+
+// Backward, forward sweep: dq and, as a by-product, the per-segment suffix
+// aggregates (R, r) written to r_agg [BH][P][E].
+hipError_t launch_bwd_dq_generic(int dtype, int causal, const SegGeom& g, const void* q, const void* k,
+                                 const void* v, const void* out, const void* dout, const float* den,
+                                 const float* carry_s, void* dq, float* r_agg, hipStream_t st);
+
+// Backward, reverse sweep: dk, dv from the suffix carry (exclusive suffix
+// records for causal, per-bh totals for non-causal).
+hipError_t launch_bwd_dkdv_generic(int dtype, int causal, const SegGeom& g, const void* q, const void* k,
+                                   const void* v, const void* out, const void* dout, const float* den,
+                                   const float* carry_r, void* dk, void* dv, hipStream_t st);
+
+// ---- decode ----
+hipError_t launch_decode_step(int dtype, int64_t BH, int D, int M, float* S, float* Z, const void* q,
+                              const void* k, const void* v, void* out, hipStream_t st);
+
+}  // namespace la

@@ -1,0 +1,153 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+symbol include/linattn.h declares, and rejects bad arguments before any HIP
+call.  Pointers below are fake addresses; every call is built so that
+validation fails first, and the tests are skipped on a host with a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from kernelized_causal_attention_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_native.LIB_PATH):
+        from kernelized_causal_attention_amd import build
+
+        build.build(verbose=False)
+    return _native.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_symbols()
+    for required in ("la_forward", "la_backward", "la_decode_step"):
+        assert required in names
+    assert set(names) == set(_native.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    assert lib.la_status_str(0) == b"LA_OK"
+    assert lib.la_status_str(1) == b"LA_ERR_INVALID"
+    assert lib.la_status_str(2) == b"LA_ERR_UNSUPPORTED"
+    assert lib.la_status_str(3) == b"LA_ERR_DEVICE"
+    assert lib.la_version() >= 100
+
+
+def test_workspace_bytes(lib):
+    # causal forward over one segment needs nothing; non-causal needs the
+    # per-segment records and a total; backward always needs records + den.
+    one = _native.la_plan(0, 1, 1)
+    assert lib.la_workspace_bytes_ex(0, 1, 1, 64, 16, 16, 1, 0, ctypes.byref(one)) == 0
+    nc = lib.la_workspace_bytes_ex(0, 1, 1, 64, 16, 16, 0, 0, ctypes.byref(one))
+    assert nc >= 2 * (16 * 16 + 16) * 4
+    bw = lib.la_workspace_bytes(1, 2, 3, 100, 8, 4, 1, 0)
+    assert bw >= 2 * 3 * 100 * 4
+    assert lib.la_workspace_bytes(3, 2, 3, 1, 8, 4, 1, 0) == 0  # decode
+    assert lib.la_workspace_bytes(0, 1, 1, 64, 300, 16, 1, 0) == 0  # unsupported -> 0
+
+
+def test_resolve_plan(lib):
+    out = _native.la_plan()
+    st = lib.la_resolve_plan(0, 4, 8, 2048, 64, 64, 1, 0, None, ctypes.byref(out))
+    assert st == 0
+    assert out.segments >= 1 and out.chunk in (16, 32, 64) and out.kernel in (1, 2)
+    req = _native.la_plan(16, 3, 1)
+    assert lib.la_resolve_plan(0, 1, 1, 1000, 16, 16, 1, 0, ctypes.byref(req), ctypes.byref(out)) == 0
+    assert (out.chunk, out.segments, out.kernel) == (16, 3, 1)
+    bad = _native.la_plan(48, 0, 1)
+    assert lib.la_resolve_plan(0, 1, 1, 100, 16, 16, 1, 0, ctypes.byref(bad), ctypes.byref(out)) == 1
+    bad = _native.la_plan(0, 0, 7)
+    assert lib.la_resolve_plan(0, 1, 1, 100, 16, 16, 1, 0, ctypes.byref(bad), ctypes.byref(out)) == 1
+
+
+nogpu = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer validation tests run on hosts without a GPU")
+
+A = 0x10000000  # fake, 256-byte aligned "device" addresses, far apart
+Bp = 0x20000000
+C = 0x30000000
+Dp = 0x40000000
+
+
+@nogpu
+def test_forward_rejects_bad_arguments(lib):
+    def fwd(q=A, k=Bp, v=C, out=Dp, B=1, H=1, N=8, D=4, M=4, causal=1, dtype=0, den=None, ws=None, wsz=0):
+        return lib.la_forward(q, k, v, out, B, H, N, D, M, causal, dtype, den, ws, wsz, None)
+
+    assert fwd(q=None) == 1 and b"q is NULL" in lib.la_last_error()
+    assert fwd(out=None) == 1
+    assert fwd(N=0) == 1 and b"sizes" in lib.la_last_error()
+    assert fwd(B=-1) == 1
+    assert fwd(dtype=5) == 1 and b"dtype" in lib.la_last_error()
+    assert fwd(D=300) == 2 and b"D=300" in lib.la_last_error()
+    assert fwd(D=200, M=200) == 2
+    assert fwd(q=A + 2) == 1 and b"aligned" in lib.la_last_error()  # fp32 needs 4-byte alignment
+    assert fwd(out=A + 64) == 1 and b"overlaps" in lib.la_last_error()
+    assert fwd(den=A) == 1 and b"overlaps" in lib.la_last_error()
+    # non-causal always needs a workspace: none given -> rejected before launch
+    assert fwd(causal=0) == 1 and b"workspace" in lib.la_last_error()
+    need = lib.la_workspace_bytes(0, 1, 1, 8, 4, 4, 0, 0)
+    assert fwd(causal=0, ws=0x50000000, wsz=need - 1) == 1 and b"too small" in lib.la_last_error()
+
+
+@nogpu
+def test_backward_rejects_bad_arguments(lib):
+    E = 0x50000000
+    F = 0x60000000
+    G = 0x70000000
+    H_ = 0x80000000
+
+    def bwd(dq=F, dk=G, dv=H_, ws=None, wsz=0, N=8, den=None):
+        return lib.la_backward(A, Bp, C, Dp, E, den, dq, dk, dv, 1, 1, N, 4, 4, 1, 0, ws, wsz, None)
+
+    assert bwd(dq=None) == 1
+    assert bwd(dk=A) == 1 and b"overlaps" in lib.la_last_error()
+    assert bwd(dv=F) == 1 and b"overlap" in lib.la_last_error()
+    assert bwd() == 1 and b"workspace" in lib.la_last_error()  # backward needs a workspace
+    need = lib.la_workspace_bytes(1, 1, 1, 8, 4, 4, 1, 0)
+    assert bwd(ws=0x90000000, wsz=need - 4) == 1 and b"too small" in lib.la_last_error()
+
+
+@nogpu
+def test_decode_and_prefix_reject_bad_arguments(lib):
+    assert lib.la_decode_step(None, Bp, C, Dp, A + 0x100000, 0x50000000, 2, 2, 4, 4, 0, None) == 1
+    # out overlapping q
+    assert lib.la_decode_step(A, Bp, C, Dp, 0x50000000, C + 4, 2, 2, 4, 4, 0, None) == 1
+    assert b"overlaps" in lib.la_last_error()
+    assert lib.la_decode_step(A, Bp, C, Dp, 0x50000000, 0x60000000, 2, 2, 4, 512, 0, None) == 2
+    assert lib.la_prefix_state(A, Bp, None, Dp, 1, 1, 8, 4, 4, 0, None, 0, None) == 1
+    assert lib.la_prefix_state(A, Bp, A, Dp, 1, 1, 8, 4, 4, 0, None, 0, None) == 1
+
+
+def test_binding_requires_built_library_loudly(monkeypatch, tmp_path):
+    # With the library path pointing nowhere, loading raises instead of
+    # falling back to anything.
+    monkeypatch.setattr(_native, "_lib", None)
+    monkeypatch.setattr(_native, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _native.load()
