@@ -1,0 +1,252 @@
+"""Benchmark: causal linear attention forward+backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+
+A step is one pass of the training hot path over one batch: la_forward
+(causal, keeping the row denominators) followed by la_backward, on the
+bf16 workload B=8, H=16, N=8192, D=M=64 (Q, K, V ~ N(0,1)/sqrt(D), dout ~
+N(0,1), synthetic, drawn on the device, resident in HBM before timing).
+The timed region is exactly K steps between two synchronisations, timed with
+HIP events on the working stream.  Prints ONE JSON line.
+
+Extra fields:
+  roofline      -- the dominant kernel's algorithmic bytes per launch over its
+                   average launch time (HIP events around every launch inside
+                   the timed region), against 8 TB/s.
+  cpu_baseline  -- the fp64 oracle (test infrastructure, timed here only) on a
+                   bounded sample of the same workload's heads, scaled to
+                   tokens/s of the whole batch.
+  decode        -- the batched decode step (B=256, H=32, D=M=128, fp32 state,
+                   1024 consecutive steps after a 512-token prefix): steps/s
+                   and HBM GB/s.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- bytes ----
+def kernel_bytes(name: str, B, H, N, D, M, es, P=1):
+    """Algorithmic HBM bytes one launch of `name` must move (inputs read once,
+    outputs written once), for B*H heads of N tokens."""
+    ht = B * H * N
+    base = name.split(".", 1)[-1]
+    if base == "forward":
+        return ht * (es * (2 * D + M) + es * M + 4)
+    if base == "forward_den":
+        return ht * (es * (2 * D + M) + 4)
+    if base == "seg_state":
+        return ht * es * (D + M)
+    if base == "bwd_dq":
+        return ht * (es * (2 * D + 3 * M) + 4 + es * D)
+    if base == "bwd_dkdv":
+        return ht * (es * (2 * D + 3 * M) + 4 + es * (D + M))
+    if base == "seg_scan":
+        return B * H * (P * 2 + 1) * (D * M + D) * 4
+    if base == "decode":
+        return B * H * (2 * D * M * 4 + 2 * D * 4 + es * (2 * D + M) + es * M)
+    return 0
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported by this build "
+              "(every (b,h) head is independent; multi-GPU sharding is described in the design notes, "
+              "not run).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kernelized_causal_attention_amd as la
+    from workloads import WORKLOADS, device_inputs
+
+    w = WORKLOADS["fwdbwd_bf16"]
+    B, H, N, D, M = w.B, w.H, w.N, w.D, w.M
+    es = 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v, g = device_inputs(B, H, N, D, M, "bf16", seed=0, scale=1.0 / D ** 0.5, device="cuda")
+    plan_f = la.resolve_plan("forward", B, H, N, D, M, True, "bf16")
+    plan_b = la.resolve_plan("backward", B, H, N, D, M, True, "bf16")
+    ws_f = torch.empty(max(1, la.workspace_bytes("forward", B, H, N, D, M, True, "bf16")), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(1, la.workspace_bytes("backward", B, H, N, D, M, True, "bf16")), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, H, N, M), dtype=torch.bfloat16, device=dev)
+    den = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+    def step():
+        la.forward(q, k, v, causal=True, out=out, den=den, return_den=True, workspace=ws_f)
+        return la.backward(q, k, v, out, g, den=den, causal=True, workspace=ws_b)
+
+    log(f"workload fwdbwd_bf16 B={B} H={H} N={N} D={D} M={M}; plan fwd {plan_f} bwd {plan_b}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    la.profile_enable(True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    prof = la.profile_report()
+    la.profile_enable(False)
+    ms = t0.elapsed_time(t1) / args.steps
+    tokens = B * N
+    value = tokens / (ms / 1e3)
+    log(f"{ms:.3f} ms/step, {value:.4g} tokens/s; kernels: {prof}")
+
+    # dominant kernel by total time in the timed region
+    kname, (nl, tot_ms) = max(prof.items(), key=lambda kv: kv[1][1])
+    P = plan_b["segments"] if "bwd" in kname or "scan" in kname else plan_f["segments"]
+    kb = kernel_bytes(kname, B, H, N, D, M, es, P)
+    avg_ms = tot_ms / nl
+    achieved = kb / (avg_ms / 1e3) / 1e9
+    kernels = {}
+    for name, (n, t) in sorted(prof.items()):
+        b = kernel_bytes(name, B, H, N, D, M, es, P)
+        avg = t / n
+        kernels[name] = {"launches_per_step": n / args.steps, "avg_ms": round(avg, 4),
+                         "alg_bytes": b, "GBps": round(b / (avg / 1e3) / 1e9, 1) if b else None}
+    result = {
+        "metric": "causal linear-attn fwd+bwd tokens/sec",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (Q,K,V ~ N(0,1)/sqrt(D), dout ~ N(0,1), device RNG seed 0)",
+        "config": {"workload": "causal forward+backward, bf16 in / fp32 accumulate", "B": B, "H": H,
+                   "N": N, "D": D, "M": M, "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)",
+                   "plan_forward": plan_f, "plan_backward": plan_b},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": kb, "avg_launch_ms": round(avg_ms, 4)},
+        "kernels": kernels,
+    }
+
+    if not args.no_extra:
+        result["decode"] = bench_decode(la, torch, args.decode_steps)
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(q, k, v, g, B, H, N, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def bench_decode(la, torch, steps):
+    from workloads import WORKLOADS, decode_inputs
+
+    w = WORKLOADS["decode_f32"]
+    dev = "cuda"
+    (pq, pk, pv), (sq, sk, sv) = decode_inputs(w, seed=0, device=dev)
+    del pq
+    S, Z = la.prefix_state(pk, pv)
+    outs = torch.empty((steps, w.B, w.H, w.M), dtype=torch.float32, device=dev)
+    for t in range(4):  # warm-up on scratch copies of the state
+        la.decode_step(S.clone(), Z.clone(), sq[t], sk[t], sv[t])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    la.profile_enable(True)
+    e0.record(stream)
+    for t in range(steps):
+        la.decode_step(S, Z, sq[t % w.steps], sk[t % w.steps], sv[t % w.steps], out=outs[t])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    prof = la.profile_report()
+    la.profile_enable(False)
+    ms = e0.elapsed_time(e1)
+    n, kms = prof.get("decode", (steps, ms))
+    b = kernel_bytes("decode", w.B, w.H, 1, w.D, w.M, 4)
+    kavg = kms / n
+    gbs = b / (kavg / 1e3) / 1e9
+    log(f"decode: {steps} steps in {ms:.2f} ms, kernel avg {kavg * 1e3:.1f} us, {gbs:.0f} GB/s")
+    return {"metric": "decode steps/sec", "value": round(steps / (ms / 1e3), 1), "unit": "steps/s",
+            "config": {"workload": "batched RNN decode step, fp32 state", "B": w.B, "H": w.H, "D": w.D,
+                       "M": w.M, "prefix": w.prefix, "steps": steps},
+            "roofline": {"bound": "hbm", "kernel": "decode", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "alg_bytes_per_launch": b, "avg_launch_ms": round(kavg, 5)}}
+
+
+def cpu_baseline(q, k, v, g, B, H, N, budget_s):
+    """Time the fp64 oracle's backward (which runs the forward recurrence
+    and both gradient sweeps) on a sample of heads, single-threaded."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    def host(t, sel):
+        return t[sel].detach().float().cpu().numpy().astype(np.float64)
+
+    heads = [(b, h) for b in range(B) for h in range(H)]
+
+    def run(n):
+        sel = (np.array([b for b, _ in heads[:n]]), np.array([h for _, h in heads[:n]]))
+        qq, kk, vv, gg = (host(t, sel) for t in (q, k, v, g))
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            oracle.backward(qq, kk, vv, gg, True)
+            return time.perf_counter() - t0
+
+    t_probe = run(2)
+    n = int(min(len(heads), max(2, 2 * budget_s / max(t_probe, 1e-3))))
+    t = run(n) if n > 2 else t_probe
+    tokens_per_s = n * N / (H * t)
+    cpu = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    log(f"cpu oracle: {n} heads x {N} tokens in {t:.2f} s -> {tokens_per_s:.4g} tokens/s")
+    return {"value": round(tokens_per_s, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 numpy oracle backward (forward recurrence + both gradient sweeps) on {n} of "
+                      f"{B * H} heads at full N={N}, {t:.2f} s, single thread; scaled to the batch as "
+                      f"n*N/(H*t)", "cpu": cpu}
+
+
+if __name__ == "__main__":
+    main()

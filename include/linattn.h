@@ -154,6 +154,16 @@ size_t la_workspace_bytes_ex(int op, int64_t B, int64_t H, int64_t N, int64_t D,
 la_status la_resolve_plan(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                           int causal, int dtype, const la_plan* requested, la_plan* resolved);
 
+/* Per-kernel timing (a tracing aid for benchmarks and profiling runs).
+ * la_profile_enable(1) clears earlier records and starts bracketing every
+ * kernel the library launches with a pair of HIP events recorded on that
+ * launch's stream; la_profile_enable(0) stops.  la_profile_report waits for
+ * the recorded events, writes one line per kernel name into buf,
+ *   "<name> <launches> <total milliseconds>\n",
+ * and clears the records.  LA_ERR_INVALID if buf is NULL or too small. */
+la_status la_profile_enable(int on);
+la_status la_profile_report(char* buf, size_t len);
+
 const char* la_status_str(int status);
 /* Detail of the last non-OK status returned on this thread ("" if none). */
 const char* la_last_error(void);

@@ -19,7 +19,7 @@ from ._native import LinAttnError, la_plan  # noqa: F401
 
 __all__ = [
     "forward", "backward", "decode_step", "prefix_state", "workspace_bytes", "resolve_plan",
-    "LinAttnError", "library_path", "version",
+    "LinAttnError", "library_path", "version", "profile_enable", "profile_report",
 ]
 
 library_path = _native.LIB_PATH
@@ -72,6 +72,22 @@ def _plan_ref(p: Optional[la_plan]):
 
 def version() -> int:
     return _native.load().la_version()
+
+
+def profile_enable(on: bool = True) -> None:
+    """Start (clearing old records) or stop per-kernel HIP-event timing."""
+    _native.check(_native.load().la_profile_enable(int(bool(on))))
+
+
+def profile_report() -> dict:
+    """{kernel name: (launches, total ms)} since profile_enable(True); clears."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    _native.check(_native.load().la_profile_report(buf, len(buf)))
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, n, ms = line.split()
+        out[name] = (int(n), float(ms))
+    return out
 
 
 def workspace_bytes(op: str, B, H, N, D, M, causal=True, dtype="f32", plan=None) -> int:

@@ -21,7 +21,7 @@ LA_KERNEL_AUTO, LA_KERNEL_GENERIC, LA_KERNEL_MFMA = 0, 1, 2
 EXPORTS = (
     "la_forward", "la_forward_ex", "la_backward", "la_backward_ex", "la_decode_step",
     "la_prefix_state", "la_workspace_bytes", "la_workspace_bytes_ex", "la_resolve_plan",
-    "la_status_str", "la_last_error", "la_version",
+    "la_status_str", "la_last_error", "la_version", "la_profile_enable", "la_profile_report",
 )
 
 
@@ -71,6 +71,8 @@ def load() -> ctypes.CDLL:
         "la_status_str": ([i32], ctypes.c_char_p),
         "la_last_error": ([], ctypes.c_char_p),
         "la_version": ([], i32),
+        "la_profile_enable": ([i32], i32),
+        "la_profile_report": ([ctypes.c_char_p, sz], i32),
     }
     for name, (args, res) in sigs.items():
         f = getattr(lib, name)

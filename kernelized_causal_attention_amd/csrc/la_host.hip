@@ -2,9 +2,13 @@
 // choice, workspace carving and kernel dispatch.  See include/linattn.h.
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "la_internal.h"
 #include "linattn.h"
@@ -199,6 +203,57 @@ float* at(void* ws, size_t off) { return reinterpret_cast<float*>(static_cast<ch
 
 }  // namespace
 
+
+// ============================================================ tracing ====
+// Optional per-kernel timing: while enabled, every launch is bracketed by a
+// pair of HIP events recorded on the launch stream.
+namespace {
+
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t pool_get() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <typename F>
+hipError_t timed(const char* name, hipStream_t st, F&& f) {
+  if (!g_prof_on) return f();
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    a = pool_get();
+    b = pool_get();
+  }
+  if (!a || !b) return f();
+  hipEventRecord(a, st);
+  const hipError_t e = f();
+  hipEventRecord(b, st);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof.push_back({name, a, b});
+  return e;
+}
+
+const char* kname(int kernel, const char* generic_name, const char* mfma_name) {
+  return kernel == LA_KERNEL_MFMA ? mfma_name : generic_name;
+}
+
+}  // namespace
+
 // ============================================================ dispatch ====
 namespace {
 
@@ -219,19 +274,32 @@ hipError_t seg_state(int dtype, const Plan& p, const la::SegGeom& gbase, const v
                      float* recs, hipStream_t st) {
   const int64_t E = la::state_elems(gbase.D, gbase.M);
   const int64_t DM = static_cast<int64_t>(gbase.D) * gbase.M;
-  if (p.kernel == LA_KERNEL_MFMA) return la::launch_seg_state_mfma(gbase, k, v, recs, E, recs + DM, E, st);
+  if (p.kernel == LA_KERNEL_MFMA)
+    return timed("mfma.seg_state", st, [&] { return la::launch_seg_state_mfma(gbase, k, v, recs, E, recs + DM, E, st); });
   la::SegGeom g = gbase;
   g.chunk = la::generic_chunk_for(g.D, g.M, 1);
-  return la::launch_seg_state_generic(dtype, g, k, v, recs, E, recs + DM, E, st);
+  return timed("generic.seg_state", st,
+               [&] { return la::launch_seg_state_generic(dtype, g, k, v, recs, E, recs + DM, E, st); });
 }
 
 hipError_t fwd_pass(int dtype, int causal, const Plan& p, const la::SegGeom& gbase, const void* q,
                     const void* k, const void* v, void* out, float* den_out, const float* carry,
                     hipStream_t st) {
-  if (p.kernel == LA_KERNEL_MFMA) return la::launch_forward_mfma(causal, gbase, q, k, v, out, den_out, carry, st);
+  const char* name = out ? kname(p.kernel, "generic.forward", "mfma.forward")
+                         : kname(p.kernel, "generic.forward_den", "mfma.forward_den");
+  if (p.kernel == LA_KERNEL_MFMA)
+    return timed(name, st, [&] { return la::launch_forward_mfma(causal, gbase, q, k, v, out, den_out, carry, st); });
   la::SegGeom g = gbase;
   g.chunk = std::min(p.chunk, la::generic_chunk_for(g.D, g.M, 0));
-  return la::launch_forward_generic(dtype, causal, g, q, k, v, out, den_out, carry, st);
+  return timed(name, st,
+               [&] { return la::launch_forward_generic(dtype, causal, g, q, k, v, out, den_out, carry, st); });
+}
+
+hipError_t scan(float* agg, int64_t BH, int P, int D, int M, int reverse, float* tot_s, int64_t ts_stride,
+                float* tot_z, int64_t tz_stride, hipStream_t st) {
+  return timed("seg_scan", st, [&] {
+    return la::launch_seg_scan(agg, BH, P, D, M, reverse, tot_s, ts_stride, tot_z, tz_stride, st);
+  });
 }
 
 la_status do_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H, int64_t N,
@@ -266,7 +334,7 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
     if (p.P > 1) {
       float* agg = at(workspace, w.aggS);
       if ((e = seg_state(dtype, p, g, k, v, agg, stream))) return dev(e, "segment state");
-      if ((e = la::launch_seg_scan(agg, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream)))
+      if ((e = scan(agg, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream)))
         return dev(e, "segment scan");
       carry = agg;
     }
@@ -276,7 +344,7 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
   float* tot = at(workspace, w.totS);
   const int64_t E = la::state_elems(g.D, g.M);
   if ((e = seg_state(dtype, p, g, k, v, agg, stream))) return dev(e, "segment state");
-  if ((e = la::launch_seg_scan(agg, BH, p.P, g.D, g.M, 0, tot, E, tot + D * M, E, stream)))
+  if ((e = scan(agg, BH, p.P, g.D, g.M, 0, tot, E, tot + D * M, E, stream)))
     return dev(e, "segment scan");
   return dev(fwd_pass(dtype, 0, p, g, q, k, v, out, den_out, tot, stream), "forward");
 }
@@ -321,13 +389,13 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
   if (causal) {
     if (p.P > 1) {
       if ((e = seg_state(dtype, p, g, k, v, aggS, stream))) return dev(e, "segment state");
-      if ((e = la::launch_seg_scan(aggS, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream)))
+      if ((e = scan(aggS, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream)))
         return dev(e, "segment scan");
       carry_s = aggS;
     }
   } else {
     if ((e = seg_state(dtype, p, g, k, v, aggS, stream))) return dev(e, "segment state");
-    if ((e = la::launch_seg_scan(aggS, BH, p.P, g.D, g.M, 0, totS, E, totS + D * M, E, stream)))
+    if ((e = scan(aggS, BH, p.P, g.D, g.M, 0, totS, E, totS + D * M, E, stream)))
       return dev(e, "segment scan");
     carry_s = totS;
   }
@@ -338,31 +406,37 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
   }
   float* r_agg = (causal && p.P == 1) ? nullptr : aggR;
   if (p.kernel == LA_KERNEL_MFMA) {
-    e = la::launch_bwd_dq_mfma(causal, g, q, k, v, out, dout, den, carry_s, dq, r_agg, stream);
+    e = timed("mfma.bwd_dq", stream,
+              [&] { return la::launch_bwd_dq_mfma(causal, g, q, k, v, out, dout, den, carry_s, dq, r_agg, stream); });
   } else {
     la::SegGeom gd = g;
     gd.chunk = std::min(p.chunk, la::generic_chunk_for(g.D, g.M, 2));
-    e = la::launch_bwd_dq_generic(dtype, causal, gd, q, k, v, out, dout, den, carry_s, dq, r_agg, stream);
+    e = timed("generic.bwd_dq", stream, [&] {
+      return la::launch_bwd_dq_generic(dtype, causal, gd, q, k, v, out, dout, den, carry_s, dq, r_agg, stream);
+    });
   }
   if (e) return dev(e, "backward dq");
   const float* carry_r = nullptr;
   if (causal) {
     if (p.P > 1) {
-      if ((e = la::launch_seg_scan(aggR, BH, p.P, g.D, g.M, 1, nullptr, 0, nullptr, 0, stream)))
+      if ((e = scan(aggR, BH, p.P, g.D, g.M, 1, nullptr, 0, nullptr, 0, stream)))
         return dev(e, "suffix scan");
       carry_r = aggR;
     }
   } else {
-    if ((e = la::launch_seg_scan(aggR, BH, p.P, g.D, g.M, 1, totR, E, totR + D * M, E, stream)))
+    if ((e = scan(aggR, BH, p.P, g.D, g.M, 1, totR, E, totR + D * M, E, stream)))
       return dev(e, "suffix scan");
     carry_r = totR;
   }
   if (p.kernel == LA_KERNEL_MFMA) {
-    e = la::launch_bwd_dkdv_mfma(causal, g, q, k, v, out, dout, den, carry_r, dk, dv, stream);
+    e = timed("mfma.bwd_dkdv", stream,
+              [&] { return la::launch_bwd_dkdv_mfma(causal, g, q, k, v, out, dout, den, carry_r, dk, dv, stream); });
   } else {
     la::SegGeom gk = g;
     gk.chunk = std::min(p.chunk, la::generic_chunk_for(g.D, g.M, 3));
-    e = la::launch_bwd_dkdv_generic(dtype, causal, gk, q, k, v, out, dout, den, carry_r, dk, dv, stream);
+    e = timed("generic.bwd_dkdv", stream, [&] {
+      return la::launch_bwd_dkdv_generic(dtype, causal, gk, q, k, v, out, dout, den, carry_r, dk, dv, stream);
+    });
   }
   return dev(e, "backward dk/dv");
 }
@@ -415,7 +489,9 @@ LA_API la_status la_decode_step(float* S, float* Z, const void* q, const void* k
   const Span outs[] = {span("S", S, BH * D * M, 4), span("Z", Z, BH * D, 4), span("out", out, BH * M, es)};
   if ((s = check_disjoint(outs, 3, ins, 3))) return s;
   if (BH > 0xffffffffLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
-  return dev(la::launch_decode_step(dtype, BH, (int)D, (int)M, S, Z, q, k, v, out, stream), "decode step");
+  return dev(timed("decode", stream,
+                   [&] { return la::launch_decode_step(dtype, BH, (int)D, (int)M, S, Z, q, k, v, out, stream); }),
+             "decode step");
 }
 
 LA_API la_status la_prefix_state(const void* k, const void* v, float* S, float* Z, int64_t B, int64_t H,
@@ -441,14 +517,18 @@ LA_API la_status la_prefix_state(const void* k, const void* v, float* S, float* 
   const la::SegGeom g = geom(BH, N, D, M, p, p.chunk);
   hipError_t e;
   if (p.P == 1) {
-    if (p.kernel == LA_KERNEL_MFMA) return dev(la::launch_seg_state_mfma(g, k, v, S, D * M, Z, D, stream), "prefix state");
+    if (p.kernel == LA_KERNEL_MFMA)
+      return dev(timed("mfma.seg_state", stream, [&] { return la::launch_seg_state_mfma(g, k, v, S, D * M, Z, D, stream); }),
+                 "prefix state");
     la::SegGeom gs = g;
     gs.chunk = la::generic_chunk_for(g.D, g.M, 1);
-    return dev(la::launch_seg_state_generic(dtype, gs, k, v, S, D * M, Z, D, stream), "prefix state");
+    return dev(timed("generic.seg_state", stream,
+                     [&] { return la::launch_seg_state_generic(dtype, gs, k, v, S, D * M, Z, D, stream); }),
+               "prefix state");
   }
   float* agg = at(workspace, w.aggS);
   if ((e = seg_state(dtype, p, g, k, v, agg, stream))) return dev(e, "prefix state");
-  return dev(la::launch_seg_scan(agg, BH, p.P, g.D, g.M, 0, S, D * M, Z, D, stream), "prefix scan");
+  return dev(scan(agg, BH, p.P, g.D, g.M, 0, S, D * M, Z, D, stream), "prefix scan");
 }
 
 LA_API size_t la_workspace_bytes_ex(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
@@ -492,3 +572,43 @@ LA_API const char* la_status_str(int status) {
 LA_API const char* la_last_error(void) { return g_err.c_str(); }
 
 LA_API int la_version(void) { return 100; }
+
+LA_API la_status la_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (const ProfRec& r : g_prof) {
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_prof.clear();
+  g_prof_on = on != 0;
+  return ok();
+}
+
+LA_API la_status la_profile_report(char* buf, size_t len) {
+  if (!buf || len == 0) return fail(LA_ERR_INVALID, "buffer is NULL or empty");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  std::map<std::string, std::pair<long, double>> agg;
+  hipError_t err = hipSuccess;
+  for (const ProfRec& r : g_prof) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) err = e;
+    auto& a = agg[r.name];
+    a.first += 1;
+    a.second += ms;
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_prof.clear();
+  std::string text;
+  for (const auto& kv : agg) {
+    char line[256];
+    snprintf(line, sizeof line, "%s %ld %.6f\n", kv.first.c_str(), kv.second.first, kv.second.second);
+    text += line;
+  }
+  if (text.size() + 1 > len) return fail(LA_ERR_INVALID, "buffer too small (%zu bytes needed)", text.size() + 1);
+  memcpy(buf, text.c_str(), text.size() + 1);
+  if (err != hipSuccess) return dev(err, "profile events");
+  return ok();
+}

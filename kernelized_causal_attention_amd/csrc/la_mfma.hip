@@ -1,18 +1,414 @@
-// bf16 MFMA kernels (placeholder until the MFMA path lands).
+// bf16 MFMA kernels for the chunked causal / non-causal forward (gfx950).
+//
+// Method ("[Paper walkthrough] Transformers are RNNs", wkq9411.github.io):
+// phi = elu + 1 (section 2); S_i = sum_{j<=i} phi(K_j) V_j^T,
+// Z_i = sum_{j<=i} phi(K_j), out_i = phi(Q_i)^T S_i / phi(Q_i)^T Z_i
+// (section 3, eq:mask and eq:output); non-causal phi(Q)(phi(K)^T V)
+// (section 2, eq:linear).
+//
+// Layout of the work.  One workgroup (4 wave64s) walks one segment of one
+// (b,h) sequence in chunks of T = 64 tokens.  For a chunk that starts after
+// state (S, Z) the causal sums split exactly (the sums are associative):
+//   num_i = phi(Q_i)^T S + sum_{j<=i in chunk} (phi(Q_i).phi(K_j)) V_j
+//   den_i = phi(Q_i)^T Z + sum_{j<=i in chunk}  phi(Q_i).phi(K_j)
+// Wave w owns rows i = 16w .. 16w+15 of the chunk.  It computes the scores
+// transposed, A^T = phi(K) phi(Q)^T, one 16x16 tile per key tile j <= i; in
+// the MFMA accumulator layout a lane then holds four consecutive keys of one
+// query, so two key tiles, rounded to bf16, are directly the B operand of
+// the next product O^T = V^T A^T (with the key index permuted the same way
+// on the V side, read with LDS transpose loads).  Scores are split into a
+// bf16 high part and a bf16 remainder so that the near-constant scores
+// phi(Q).phi(K) ~ D keep their small spread through the bf16 operand.  The
+// carried state enters as O^T += S^T phi(Q)^T with S^T kept in LDS as bf16;
+// S itself stays fp32 in MFMA accumulators (each wave owns D/4 rows of it)
+// and Z is fp32.
+// Denominators use the same (hi + lo) scores and bf16 phi(Q) as the
+// numerator, so each output row is a convex combination of the weights
+// actually applied.
+//
+// Operands per chunk: phi(Q) rows go straight from HBM to registers (only
+// their wave needs them); phi(K) and V are staged once per chunk in LDS,
+// token-major.  The next chunk's Q, K, V are loaded into registers while the
+// current chunk computes.
 #include "la_internal.h"
+#include "la_mfma_common.h"
 
 namespace la {
-int mfma_supported(int, int64_t, int64_t, int) { return 0; }
-hipError_t launch_forward_mfma(int, const SegGeom&, const void*, const void*, const void*, void*, float*,
-                               const float*, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_seg_state_mfma(const SegGeom&, const void*, const void*, float*, int64_t, float*, int64_t,
-                                 hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_bwd_dq_mfma(int, const SegGeom&, const void*, const void*, const void*, const void*,
-                              const void*, const float*, const float*, void*, float*, hipStream_t) {
+namespace {
+
+using namespace mf;
+
+constexpr int NT = 256;
+constexpr int T = 64;
+
+template <int DIM>
+struct Geo {
+  static constexpr int LD = DIM + 8;              // padded LDS row stride (elements)
+  static constexpr int NTL = DIM / 16;            // 16-wide tiles along D (= M)
+  static constexpr int KS = DIM / 32;             // 32-deep k-steps along D (= M)
+  static constexpr int PC = T * DIM / 8 / NT;     // 16-byte pieces per thread per T x DIM tile
+  static constexpr int DT = NTL / 4;              // state row tiles owned by each wave
+  static constexpr int ROW8 = DIM / 8;            // 16-byte pieces per row
+};
+
+// Global -> registers: thread's pieces of a T x DIM token-major tile.
+template <int DIM>
+__device__ __forceinline__ void load_tile(i32x4 (&raw)[Geo<DIM>::PC], const bf16_t* __restrict__ src,
+                                          int64_t c0, int nrow) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int r = 0; r < G::PC; ++r) {
+    const int p = threadIdx.x + NT * r;
+    const int j = p / G::ROW8, c8 = p % G::ROW8;
+    raw[r] = j < nrow ? gload16(src + (c0 + j) * DIM + c8 * 8) : i32x4{0, 0, 0, 0};
+  }
+}
+
+// Registers -> LDS (phi applied when asked); rows past nrow are zero.
+template <int DIM, bool PHI>
+__device__ __forceinline__ void store_tile(uint16_t* lds, const i32x4 (&raw)[Geo<DIM>::PC], int nrow) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int r = 0; r < G::PC; ++r) {
+    const int p = threadIdx.x + NT * r;
+    const int j = p / G::ROW8, c8 = p % G::ROW8;
+    i16x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (j < nrow) val = PHI ? phi8(raw[r]) : __builtin_bit_cast(i16x8, raw[r]);
+    *reinterpret_cast<i16x8*>(lds + j * G::LD + c8 * 8) = val;
+  }
+}
+
+// This wave's query rows (i = 16w + li), 8 features per k-step.
+template <int DIM>
+__device__ __forceinline__ void load_q(i32x4 (&raw)[Geo<DIM>::KS], const bf16_t* __restrict__ src, int64_t c0,
+                                       int nrow, int i, int g) {
+#pragma unroll
+  for (int s = 0; s < Geo<DIM>::KS; ++s)
+    raw[s] = i < nrow ? gload16(src + (c0 + i) * DIM + 8 * g + 32 * s) : i32x4{0, 0, 0, 0};
+}
+
+// S (fp32 accumulators) -> S^T bf16 in LDS, Z -> LDS.
+template <int DIM>
+__device__ __forceinline__ void write_state(uint16_t* sST, float* sZ, const f32x4_t (&Sacc)[Geo<DIM>::DT][Geo<DIM>::NTL],
+                                            const f32x4_t (&zacc)[Geo<DIM>::DT], int w, int g, int li) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int dt = 0; dt < G::DT; ++dt) {
+    const int d0 = 16 * (w * G::DT + dt);
+#pragma unroll
+    for (int n = 0; n < G::NTL; ++n)
+      *reinterpret_cast<i16x4*>(sST + (16 * n + li) * G::LD + d0 + 4 * g) = pack4(Sacc[dt][n]);
+    if (li == 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sZ[d0 + 4 * g + u] = zacc[dt][u];
+    }
+  }
+}
+
+// S += phi(K_c)^T V_c and Z += colsum phi(K_c) for this wave's state rows.
+template <int DIM>
+__device__ __forceinline__ void state_update(f32x4_t (&Sacc)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&zacc)[Geo<DIM>::DT],
+                                             const uint16_t* sKf, const uint16_t* sV, int w, int g, int li) {
+  using G = Geo<DIM>;
+  const short one = 0x3f80;  // bf16 1.0
+  const i16x8 ones = {one, one, one, one, one, one, one, one};
+#pragma unroll
+  for (int dt = 0; dt < G::DT; ++dt) {
+    const int d0 = 16 * (w * G::DT + dt);
+#pragma unroll
+    for (int s = 0; s < T / 32; ++s) {
+      const int jr = 32 * s + 8 * g + li / 4;
+      const int cc = 4 * (li % 4);
+      const i16x8 a = cat(lds_tr(sKf + jr * G::LD + d0 + cc), lds_tr(sKf + (jr + 4) * G::LD + d0 + cc));
+      zacc[dt] = mfma(a, ones, zacc[dt]);
+#pragma unroll
+      for (int n = 0; n < G::NTL; ++n) {
+        const i16x8 b = cat(lds_tr(sV + jr * G::LD + 16 * n + cc), lds_tr(sV + (jr + 4) * G::LD + 16 * n + cc));
+        Sacc[dt][n] = mfma(a, b, Sacc[dt][n]);
+      }
+    }
+  }
+}
+
+template <int DIM>
+__device__ __forceinline__ void init_state(f32x4_t (&Sacc)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&zacc)[Geo<DIM>::DT],
+                                           const float* __restrict__ cs, int w, int g, int li) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int dt = 0; dt < G::DT; ++dt) {
+    const int d0 = 16 * (w * G::DT + dt);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d = d0 + 4 * g + u;
+#pragma unroll
+      for (int n = 0; n < G::NTL; ++n) Sacc[dt][n][u] = cs ? cs[d * DIM + 16 * n + li] : 0.f;
+      zacc[dt][u] = cs ? cs[DIM * DIM + d] : 0.f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int DIM, bool CAUSAL>
+__global__ __launch_bounds__(NT) void k_fwd_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                 const bf16_t* __restrict__ v, bf16_t* __restrict__ out,
+                                                 float* __restrict__ den_out, const float* __restrict__ carry,
+                                                 int64_t N, int P, int seg_len) {
+  using G = Geo<DIM>;
+  constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* sKf = smem;
+  uint16_t* sV = sKf + T * LD;
+  uint16_t* sST = sV + T * LD;
+  float* sZ = reinterpret_cast<float*>(sST + DIM * LD);
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+  const int64_t bh = blockIdx.x / P;
+  const int seg = blockIdx.x % P;
+  const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
+  const int64_t r1 = min(N, r0 + seg_len);
+  constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;
+  const float* cs = carry ? (CAUSAL ? carry + (bh * P + seg) * E : carry + bh * E) : nullptr;
+  const bf16_t* qh = q + bh * N * DIM;
+  const bf16_t* kh = k + bh * N * DIM;
+  const bf16_t* vh = v + bh * N * DIM;
+  bf16_t* oh = out ? out + bh * N * DIM : nullptr;
+  float* dh = den_out ? den_out + bh * N : nullptr;
+  const int i = 16 * w + li;  // this lane's query row within the chunk
+
+  f32x4_t Sacc[DT][NTL];
+  f32x4_t zacc[DT];
+  init_state<DIM>(Sacc, zacc, cs, w, g, li);
+  write_state<DIM>(sST, sZ, Sacc, zacc, w, g, li);
+
+  int64_t c0 = r0;
+  int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
+  i32x4 kraw[PC], vraw[PC], qraw[KS];
+  if (CAUSAL) {
+    load_tile<DIM>(kraw, kh, c0, nrow);
+    load_tile<DIM>(vraw, vh, c0, nrow);
+  }
+  load_q<DIM>(qraw, qh, c0, nrow, i, g);
+
+  while (c0 < r1) {
+    if (CAUSAL) {
+      store_tile<DIM, true>(sKf, kraw, nrow);
+      store_tile<DIM, false>(sV, vraw, nrow);
+    }
+    i16x8 qf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = i < nrow ? phi8(qraw[s]) : i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    __syncthreads();
+
+    // prefetch the next chunk while this one computes
+    const int64_t c1 = c0 + T;
+    const int nrow1 = c1 < r1 ? static_cast<int>(min(static_cast<int64_t>(T), r1 - c1)) : 0;
+    if (nrow1 > 0) {
+      if (CAUSAL) {
+        load_tile<DIM>(kraw, kh, c1, nrow1);
+        load_tile<DIM>(vraw, vh, c1, nrow1);
+      }
+      load_q<DIM>(qraw, qh, c1, nrow1, i, g);
+    }
+
+    // Intra-chunk scores A^T (key tiles t <= w), masked.  With phi ~ 1 + x
+    // the scores sit near D with a small spread, so one bf16 rounding would
+    // lose most of that spread; each score is carried as hi + lo, two bf16
+    // values whose sum keeps ~16 significant bits, and both enter the MFMA.
+    i16x4 ahi[4], alo[4];
+    float rs = 0.f;
+    if (CAUSAL) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        ahi[t] = i16x4{0, 0, 0, 0};
+        alo[t] = i16x4{0, 0, 0, 0};
+        if (t <= w) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) acc = mfma(lds8(sKf + (16 * t + li) * LD + 8 * g + 32 * s), qf[s], acc);
+          if (t == w) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (4 * g + u > li) acc[u] = 0.f;
+          }
+          ahi[t] = pack4(acc);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float h = fb(ahi[t][u]);
+            alo[t][u] = bf(acc[u] - h);
+            rs += h + fb(alo[t][u]);
+          }
+        }
+      }
+      rs = shfl_sum_groups(rs);
+    }
+    // inter-chunk denominator phi(Q_i)^T Z (fp32)
+    float di = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const float* zp = sZ + 8 * g + 32 * s;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) di += fb(qf[s][e]) * zp[e];
+    }
+    di = shfl_sum_groups(di);
+    const float den = rs + di;
+
+    // O^T = S^T phi(Q)^T (+ V^T A^T)
+    f32x4_t o[NTL];
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) {
+      o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) o[n] = mfma(lds8(sST + (16 * n + li) * LD + 8 * g + 32 * s), qf[s], o[n]);
+    }
+    if (CAUSAL) {
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp) {
+        if (2 * tp <= w) {
+          const i16x8 bh = cat(ahi[2 * tp], ahi[2 * tp + 1]);
+          const i16x8 bl = cat(alo[2 * tp], alo[2 * tp + 1]);
+          const int jr = 32 * tp + 4 * g + li / 4;
+          const int cc = 4 * (li % 4);
+#pragma unroll
+          for (int n = 0; n < NTL; ++n) {
+            const i16x8 a = cat(lds_tr(sV + jr * LD + 16 * n + cc), lds_tr(sV + (jr + 16) * LD + 16 * n + cc));
+            o[n] = mfma(a, bh, o[n]);
+            o[n] = mfma(a, bl, o[n]);
+          }
+        }
+      }
+    }
+    if (i < nrow) {
+      if (oh) {
+#pragma unroll
+        for (int n = 0; n < NTL; ++n) {
+          i16x4 ov;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) ov[u] = bf(o[n][u] / den);
+          *reinterpret_cast<i16x4*>(oh + (c0 + i) * DIM + 16 * n + 4 * g) = ov;
+        }
+      }
+      if (dh && g == 0) dh[c0 + i] = den;
+    }
+
+    if (CAUSAL) state_update<DIM>(Sacc, zacc, sKf, sV, w, g, li);
+    __syncthreads();
+    if (CAUSAL) write_state<DIM>(sST, sZ, Sacc, zacc, w, g, li);
+    c0 = c1;
+    nrow = nrow1;
+  }
+}
+
+// Segment aggregates dS = phi(K)^T V, dZ = colsum phi(K) over one segment.
+template <int DIM>
+__global__ __launch_bounds__(NT) void k_seg_state_mfma(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                                                       float* __restrict__ s_out, int64_t s_stride,
+                                                       float* __restrict__ z_out, int64_t z_stride, int64_t N,
+                                                       int P, int seg_len) {
+  using G = Geo<DIM>;
+  constexpr int LD = G::LD, NTL = G::NTL, PC = G::PC, DT = G::DT;
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* sKf = smem;
+  uint16_t* sV = sKf + T * LD;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+  const int64_t bh = blockIdx.x / P;
+  const int seg = blockIdx.x % P;
+  const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
+  const int64_t r1 = min(N, r0 + seg_len);
+  const bf16_t* kh = k + bh * N * DIM;
+  const bf16_t* vh = v + bh * N * DIM;
+  f32x4_t Sacc[DT][NTL];
+  f32x4_t zacc[DT];
+  init_state<DIM>(Sacc, zacc, nullptr, w, g, li);
+  int64_t c0 = r0;
+  int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
+  i32x4 kraw[PC], vraw[PC];
+  load_tile<DIM>(kraw, kh, c0, nrow);
+  load_tile<DIM>(vraw, vh, c0, nrow);
+  while (c0 < r1) {
+    store_tile<DIM, true>(sKf, kraw, nrow);
+    store_tile<DIM, false>(sV, vraw, nrow);
+    __syncthreads();
+    const int64_t c1 = c0 + T;
+    const int nrow1 = c1 < r1 ? static_cast<int>(min(static_cast<int64_t>(T), r1 - c1)) : 0;
+    if (nrow1 > 0) {
+      load_tile<DIM>(kraw, kh, c1, nrow1);
+      load_tile<DIM>(vraw, vh, c1, nrow1);
+    }
+    state_update<DIM>(Sacc, zacc, sKf, sV, w, g, li);
+    __syncthreads();
+    c0 = c1;
+    nrow = nrow1;
+  }
+  const int64_t rec = bh * P + seg;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int d0 = 16 * (w * DT + dt);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d = d0 + 4 * g + u;
+#pragma unroll
+      for (int n = 0; n < NTL; ++n) s_out[rec * s_stride + d * DIM + 16 * n + li] = Sacc[dt][n][u];
+      if (li == 0) z_out[rec * z_stride + d] = zacc[dt][u];
+    }
+  }
+}
+
+size_t lds_fwd(int dim) { return (2 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + dim * sizeof(float); }
+size_t lds_seg(int dim) { return 2 * T * (dim + 8) * sizeof(uint16_t); }
+
+#define LA_MLAUNCH(kernel, grid, lds, st, ...)                                                          \
+  do {                                                                                                  \
+    hipError_t e_ = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),                          \
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)); \
+    if (e_ != hipSuccess) return e_;                                                                    \
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(NT), lds, st, __VA_ARGS__);      \
+    return hipGetLastError();                                                                           \
+  } while (0)
+
+}  // namespace
+
+int mfma_supported(int op, int64_t D, int64_t M, int dtype) {
+  if (dtype != 1 || D != M || (D != 64 && D != 128)) return 0;
+  return op == 0 /* forward */ || op == 2 /* prefix state */;
+}
+
+hipError_t launch_forward_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
+                               void* out, float* den_out, const float* carry, hipStream_t st) {
+  const int64_t grid = g.BH * g.P;
+  const bf16_t* Q = static_cast<const bf16_t*>(q);
+  const bf16_t* K = static_cast<const bf16_t*>(k);
+  const bf16_t* V = static_cast<const bf16_t*>(v);
+  bf16_t* O = static_cast<bf16_t*>(out);
+  if (g.D == 64) {
+    if (causal) LA_MLAUNCH((k_fwd_mfma<64, true>), grid, lds_fwd(64), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
+    LA_MLAUNCH((k_fwd_mfma<64, false>), grid, lds_fwd(64), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
+  }
+  if (g.D == 128) {
+    if (causal) LA_MLAUNCH((k_fwd_mfma<128, true>), grid, lds_fwd(128), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
+    LA_MLAUNCH((k_fwd_mfma<128, false>), grid, lds_fwd(128), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
+  }
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_seg_state_mfma(const SegGeom& g, const void* k, const void* v, float* s_out, int64_t s_stride,
+                                 float* z_out, int64_t z_stride, hipStream_t st) {
+  const int64_t grid = g.BH * g.P;
+  const bf16_t* K = static_cast<const bf16_t*>(k);
+  const bf16_t* V = static_cast<const bf16_t*>(v);
+  if (g.D == 64)
+    LA_MLAUNCH((k_seg_state_mfma<64>), grid, lds_seg(64), st, K, V, s_out, s_stride, z_out, z_stride, g.N, g.P, g.seg_len);
+  if (g.D == 128)
+    LA_MLAUNCH((k_seg_state_mfma<128>), grid, lds_seg(128), st, K, V, s_out, s_stride, z_out, z_stride, g.N, g.P, g.seg_len);
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_bwd_dq_mfma(int, const SegGeom&, const void*, const void*, const void*, const void*, const void*,
+                              const float*, const float*, void*, float*, hipStream_t) {
   return hipErrorNotSupported;
 }
 hipError_t launch_bwd_dkdv_mfma(int, const SegGeom&, const void*, const void*, const void*, const void*,
                                 const void*, const float*, const float*, void*, void*, hipStream_t) {
   return hipErrorNotSupported;
 }
+
 }  // namespace la

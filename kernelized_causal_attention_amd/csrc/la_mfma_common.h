@@ -1,0 +1,78 @@
+// Shared pieces of the bf16 MFMA kernels (gfx950, wave64).
+//
+// MFMA used: v_mfma_f32_16x16x32_bf16 (D = A(16x32) * B(32x16) + C, fp32
+// accumulate).  Lane layouts (l = lane, g = l / 16, li = l % 16):
+//   A operand: A[li][8g + e], e = 0..7        (8 bf16 per lane)
+//   B operand: B[8g + e][li]                   (8 bf16 per lane)
+//   C / D    : C[4g + u][li], u = 0..3         (4 fp32 per lane)
+// ds_read_tr16_b64 (LDS transpose read) within each 16-lane group returns to
+// lane i the elements  out[i][u] = in[lane 4u + i/4][i % 4]  where in[L] is
+// the 4 x 16-bit block lane L addresses.  With it, a token-major LDS tile
+// X[j][c] gives an operand whose k index runs along tokens j: lane li of
+// group g points at row (j0 + li / 4), column (c0 + 4 (li % 4)) and receives
+// X[j0 + u][c0 + li] for u = 0..3.
+#pragma once
+
+#include "la_device.h"
+
+namespace la {
+namespace mf {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ f32x4_t mfma(i16x8 a, i16x8 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+// 16-byte LDS read of 8 consecutive bf16.
+__device__ __forceinline__ i16x8 lds8(const uint16_t* p) { return *reinterpret_cast<const i16x8*>(p); }
+
+// Transposing 8-byte LDS read (see the header comment).
+__device__ __forceinline__ i16x4 lds_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+__device__ __forceinline__ i16x8 cat(i16x4 a, i16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ short bf(float x) { return static_cast<short>(f32_to_bf16(x)); }
+__device__ __forceinline__ float fb(short h) { return bf16_to_f32(static_cast<uint16_t>(h)); }
+
+__device__ __forceinline__ i16x4 pack4(f32x4_t v) {
+  i16x4 r;
+  r[0] = bf(v[0]);
+  r[1] = bf(v[1]);
+  r[2] = bf(v[2]);
+  r[3] = bf(v[3]);
+  return r;
+}
+
+// phi applied to 8 bf16 values (raw 16-byte vector), result rounded to bf16.
+__device__ __forceinline__ i16x8 phi8(i32x4 raw) {
+  const i16x8 h = __builtin_bit_cast(i16x8, raw);
+  i16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = bf(phi(fb(h[e])));
+  return r;
+}
+
+__device__ __forceinline__ float shfl_sum_groups(float x) {
+  // sum over the four 16-lane groups (lanes li, li+16, li+32, li+48)
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+__device__ __forceinline__ i32x4 gload16(const bf16_t* p) { return *reinterpret_cast<const i32x4*>(p); }
+
+}  // namespace mf
+}  // namespace la
