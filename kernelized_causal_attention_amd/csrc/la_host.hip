@@ -22,10 +22,10 @@ hipError_t launch_forward_mfma(int causal, const SegGeom& g, const void* q, cons
 hipError_t launch_seg_state_mfma(const SegGeom& g, const void* k, const void* v, float* s_out,
                                  int64_t s_stride, float* z_out, int64_t z_stride, hipStream_t st);
 hipError_t launch_bwd_dq_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
-                              const void* out, const void* dout, const float* den, const float* carry_s,
-                              void* dq, float* r_agg, hipStream_t st);
+                              const void* dout, const float* carry_s, void* dq, float* r_agg, float* c_out,
+                              float* den_out, hipStream_t st);
 hipError_t launch_bwd_dkdv_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
-                                const void* out, const void* dout, const float* den, const float* carry_r,
+                                const void* dout, const float* den, const float* c, const float* carry_r,
                                 void* dk, void* dv, hipStream_t st);
 }  // namespace la
 
@@ -170,7 +170,7 @@ struct Carve {
 };
 
 struct WsLayout {
-  size_t aggS = 0, totS = 0, aggR = 0, totR = 0, den = 0;
+  size_t aggS = 0, totS = 0, aggR = 0, totR = 0, den = 0, cvec = 0;
   size_t bytes = 0;
 };
 
@@ -192,6 +192,7 @@ WsLayout layout(int op, int64_t BH, int64_t N, int64_t D, int64_t M, int causal,
     w.aggR = c.take(recs);
     w.totR = c.take(static_cast<size_t>(BH) * E);
     w.den = c.take(static_cast<size_t>(BH) * N);
+    if (p.kernel == LA_KERNEL_MFMA) w.cvec = c.take(static_cast<size_t>(BH) * N);
   } else if (op == LA_OP_PREFIX_STATE) {
     if (p.P > 1) w.aggS = c.take(recs);
   }
@@ -399,16 +400,22 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
       return dev(e, "segment scan");
     carry_s = totS;
   }
-  if (!den) {
-    float* dw = at(workspace, w.den);
-    if ((e = fwd_pass(dtype, causal, p, g, q, k, v, nullptr, dw, carry_s, stream))) return dev(e, "denominator");
-    den = dw;
-  }
   float* r_agg = (causal && p.P == 1) ? nullptr : aggR;
+  // The MFMA path recomputes num and den in fp32 inside its forward sweep
+  // (it reads neither out nor den) and passes den and c to the reverse sweep
+  // through the workspace.
+  float* cw = at(workspace, w.cvec);
   if (p.kernel == LA_KERNEL_MFMA) {
+    float* dw = at(workspace, w.den);
     e = timed("mfma.bwd_dq", stream,
-              [&] { return la::launch_bwd_dq_mfma(causal, g, q, k, v, out, dout, den, carry_s, dq, r_agg, stream); });
+              [&] { return la::launch_bwd_dq_mfma(causal, g, q, k, v, dout, carry_s, dq, r_agg, cw, dw, stream); });
+    den = dw;
   } else {
+    if (!den) {
+      float* dw = at(workspace, w.den);
+      if ((e = fwd_pass(dtype, causal, p, g, q, k, v, nullptr, dw, carry_s, stream))) return dev(e, "denominator");
+      den = dw;
+    }
     la::SegGeom gd = g;
     gd.chunk = std::min(p.chunk, la::generic_chunk_for(g.D, g.M, 2));
     e = timed("generic.bwd_dq", stream, [&] {
@@ -430,7 +437,7 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
   }
   if (p.kernel == LA_KERNEL_MFMA) {
     e = timed("mfma.bwd_dkdv", stream,
-              [&] { return la::launch_bwd_dkdv_mfma(causal, g, q, k, v, out, dout, den, carry_r, dk, dv, stream); });
+              [&] { return la::launch_bwd_dkdv_mfma(causal, g, q, k, v, dout, den, cw, carry_r, dk, dv, stream); });
   } else {
     la::SegGeom gk = g;
     gk.chunk = std::min(p.chunk, la::generic_chunk_for(g.D, g.M, 3));

@@ -38,54 +38,8 @@ namespace {
 
 using namespace mf;
 
-constexpr int NT = 256;
-constexpr int T = 64;
-
-template <int DIM>
-struct Geo {
-  static constexpr int LD = DIM + 8;              // padded LDS row stride (elements)
-  static constexpr int NTL = DIM / 16;            // 16-wide tiles along D (= M)
-  static constexpr int KS = DIM / 32;             // 32-deep k-steps along D (= M)
-  static constexpr int PC = T * DIM / 8 / NT;     // 16-byte pieces per thread per T x DIM tile
-  static constexpr int DT = NTL / 4;              // state row tiles owned by each wave
-  static constexpr int ROW8 = DIM / 8;            // 16-byte pieces per row
-};
-
-// Global -> registers: thread's pieces of a T x DIM token-major tile.
-template <int DIM>
-__device__ __forceinline__ void load_tile(i32x4 (&raw)[Geo<DIM>::PC], const bf16_t* __restrict__ src,
-                                          int64_t c0, int nrow) {
-  using G = Geo<DIM>;
-#pragma unroll
-  for (int r = 0; r < G::PC; ++r) {
-    const int p = threadIdx.x + NT * r;
-    const int j = p / G::ROW8, c8 = p % G::ROW8;
-    raw[r] = j < nrow ? gload16(src + (c0 + j) * DIM + c8 * 8) : i32x4{0, 0, 0, 0};
-  }
-}
-
-// Registers -> LDS (phi applied when asked); rows past nrow are zero.
-template <int DIM, bool PHI>
-__device__ __forceinline__ void store_tile(uint16_t* lds, const i32x4 (&raw)[Geo<DIM>::PC], int nrow) {
-  using G = Geo<DIM>;
-#pragma unroll
-  for (int r = 0; r < G::PC; ++r) {
-    const int p = threadIdx.x + NT * r;
-    const int j = p / G::ROW8, c8 = p % G::ROW8;
-    i16x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (j < nrow) val = PHI ? phi8(raw[r]) : __builtin_bit_cast(i16x8, raw[r]);
-    *reinterpret_cast<i16x8*>(lds + j * G::LD + c8 * 8) = val;
-  }
-}
-
-// This wave's query rows (i = 16w + li), 8 features per k-step.
-template <int DIM>
-__device__ __forceinline__ void load_q(i32x4 (&raw)[Geo<DIM>::KS], const bf16_t* __restrict__ src, int64_t c0,
-                                       int nrow, int i, int g) {
-#pragma unroll
-  for (int s = 0; s < Geo<DIM>::KS; ++s)
-    raw[s] = i < nrow ? gload16(src + (c0 + i) * DIM + 8 * g + 32 * s) : i32x4{0, 0, 0, 0};
-}
+constexpr int NT = kNT;
+constexpr int T = kT;
 
 // S (fp32 accumulators) -> S^T bf16 in LDS, Z -> LDS.
 template <int DIM>
@@ -161,7 +115,10 @@ __global__ __launch_bounds__(NT) void k_fwd_mfma(const bf16_t* __restrict__ q, c
   uint16_t* sST = sV + T * LD;
   float* sZ = reinterpret_cast<float*>(sST + DIM * LD);
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+  // w is made wave-uniform (an SGPR) so that branches on it are scalar: an
+  // MFMA under an EXEC-masked branch still writes every lane.
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
@@ -309,7 +266,10 @@ __global__ __launch_bounds__(NT) void k_seg_state_mfma(const bf16_t* __restrict_
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* sKf = smem;
   uint16_t* sV = sKf + T * LD;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+  // w is made wave-uniform (an SGPR) so that branches on it are scalar: an
+  // MFMA under an EXEC-masked branch still writes every lane.
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
@@ -369,7 +329,7 @@ size_t lds_seg(int dim) { return 2 * T * (dim + 8) * sizeof(uint16_t); }
 
 int mfma_supported(int op, int64_t D, int64_t M, int dtype) {
   if (dtype != 1 || D != M || (D != 64 && D != 128)) return 0;
-  return op == 0 /* forward */ || op == 2 /* prefix state */;
+  return op == 0 /* forward */ || op == 1 /* backward */ || op == 2 /* prefix state */;
 }
 
 hipError_t launch_forward_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
@@ -399,15 +359,6 @@ hipError_t launch_seg_state_mfma(const SegGeom& g, const void* k, const void* v,
     LA_MLAUNCH((k_seg_state_mfma<64>), grid, lds_seg(64), st, K, V, s_out, s_stride, z_out, z_stride, g.N, g.P, g.seg_len);
   if (g.D == 128)
     LA_MLAUNCH((k_seg_state_mfma<128>), grid, lds_seg(128), st, K, V, s_out, s_stride, z_out, z_stride, g.N, g.P, g.seg_len);
-  return hipErrorNotSupported;
-}
-
-hipError_t launch_bwd_dq_mfma(int, const SegGeom&, const void*, const void*, const void*, const void*, const void*,
-                              const float*, const float*, void*, float*, hipStream_t) {
-  return hipErrorNotSupported;
-}
-hipError_t launch_bwd_dkdv_mfma(int, const SegGeom&, const void*, const void*, const void*, const void*,
-                                const void*, const float*, const float*, void*, void*, hipStream_t) {
   return hipErrorNotSupported;
 }
 

@@ -1,0 +1,571 @@
+// bf16 MFMA kernels for the cumulative-sum backward (gfx950).
+//
+// Gradients of L = sum(dout * out) ("[Paper walkthrough] Transformers are
+// RNNs", wkq9411.github.io, section 3.1: a prefix matrix for phi(Q),
+// eq:gq; a suffix matrix for phi(K) and V, up to eq:gv).  The page leaves
+// the denominator to autograd; by the chain rule through out = num / den,
+// with g_i = dout_i / den_i and c_i = -(dout_i . out_i) / den_i:
+//   grad phi(Q_i) = S_i g_i + c_i Z_i
+//   grad phi(K_j) = R_j V_j + r_j,   grad V_j = R_j^T phi(K_j)
+//   R_j = sum_{i>=j} phi(Q_i) g_i^T,  r_j = sum_{i>=j} c_i phi(Q_i)
+// and dq = grad phi(Q) * phi'(q), dk = grad phi(K) * phi'(k).
+//
+// Chunked (T = 64 tokens), per chunk with prefix state (S, Z) before it and
+// suffix state (R, r) after it:
+//   grad phi(Q_i) = S g_i + c_i Z + sum_{j<=i in chunk} (g_i.V_j + c_i) phi(K_j)
+//   grad phi(K_j) = R V_j + r + sum_{i>=j in chunk} (g_i.V_j + c_i) phi(Q_i)
+//   grad V_j      = R^T phi(K_j) + sum_{i>=j in chunk} (phi(Q_i).phi(K_j)) g_i
+// k_bwd_dq_mfma walks a segment forwards (S, Z carried in fp32 MFMA
+// accumulators, bf16 copy of S in LDS) and, as a by-product, sums the
+// segment's own (R, r) for the suffix scan; k_bwd_dkdv_mfma walks a segment
+// backwards carrying (R, r).  As in the forward kernels, the chunk's score
+// tiles are computed transposed so that the accumulator layout is directly
+// the next MFMA's B operand (keys or queries permuted consistently on the
+// other operand, read with LDS transpose loads), scores are carried as bf16
+// hi + lo pairs, and Z and r are accumulated in fp32 through MFMAs against a
+// ones / c operand.
+#include "la_internal.h"
+#include "la_mfma_common.h"
+
+namespace la {
+namespace {
+
+using namespace mf;
+
+constexpr int NT = kNT;
+constexpr int T = kT;
+
+// Split a masked fp32 score tile into bf16 hi + lo.
+__device__ __forceinline__ void split(const f32x4_t& acc, i16x4& hi, i16x4& lo) {
+  hi = pack4(acc);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) lo[u] = bf(acc[u] - fb(hi[u]));
+}
+
+// c values of tokens 32s + 8g .. +7 as bf16 hi / lo A operands (every row
+// of the operand is the same, so the MFMA result is sum_i c_i X[i][col]).
+__device__ __forceinline__ void c_operand(const float* sC, int s, int g, i16x8& hi, i16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float c = sC[32 * s + 8 * g + e];
+    hi[e] = bf(c);
+    lo[e] = bf(c - fb(hi[e]));
+  }
+}
+
+// Per-wave state layout used by both kernels: X^T accumulators (X = S or R)
+// for the wave's column tiles mt = w*MT + a, all row tiles n:
+//   lane holds X[d = 16n + li][m = 16mt + 4g + u];
+// vector accumulators (Z or r) for the wave's row tiles dt = w*DT + b:
+//   lane holds x[16dt + li] (the same in all four u).
+template <int DIM>
+__device__ __forceinline__ void init_xt(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&x)[Geo<DIM>::DT],
+                                        const float* __restrict__ src, int w, int g, int li) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int a = 0; a < G::DT; ++a) {
+    const int mt = w * G::DT + a;
+#pragma unroll
+    for (int n = 0; n < G::NTL; ++n)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) X[a][n][u] = src ? src[(16 * n + li) * DIM + 16 * mt + 4 * g + u] : 0.f;
+    const float z = src ? src[DIM * DIM + 16 * mt + li] : 0.f;
+    x[a] = f32x4_t{z, z, z, z};
+  }
+}
+
+// bf16 row-major copy X[d][m] and fp32 vector x[d] into LDS.
+template <int DIM>
+__device__ __forceinline__ void write_xt(uint16_t* sX, float* sx, const f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL],
+                                         const f32x4_t (&x)[Geo<DIM>::DT], int w, int g, int li) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int a = 0; a < G::DT; ++a) {
+    const int mt = w * G::DT + a;
+#pragma unroll
+    for (int n = 0; n < G::NTL; ++n)
+      *reinterpret_cast<i16x4*>(sX + (16 * n + li) * G::LD + 16 * mt + 4 * g) = pack4(X[a][n]);
+    if (g == 0) sx[16 * mt + li] = x[a][0];
+  }
+}
+
+template <int DIM>
+__device__ __forceinline__ void store_xt(float* __restrict__ rec, const f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL],
+                                         const f32x4_t (&x)[Geo<DIM>::DT], int w, int g, int li) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int a = 0; a < G::DT; ++a) {
+    const int mt = w * G::DT + a;
+#pragma unroll
+    for (int n = 0; n < G::NTL; ++n)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rec[(16 * n + li) * DIM + 16 * mt + 4 * g + u] = X[a][n][u];
+    if (g == 0) rec[DIM * DIM + 16 * mt + li] = x[a][0];
+  }
+}
+
+// X^T[m][d] += sum_j A[j][m] B[j][d] over the chunk's 64 tokens, and
+// x[d] += sum_j w_j B[j][d] (w = ones, or c as hi + lo when WC).
+template <int DIM, bool WC>
+__device__ __forceinline__ void outer_update(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&x)[Geo<DIM>::DT],
+                                             const uint16_t* sA, const uint16_t* sB, const float* sC, int w, int g,
+                                             int li) {
+  using G = Geo<DIM>;
+  const short one = 0x3f80;
+  const i16x8 ones = {one, one, one, one, one, one, one, one};
+#pragma unroll
+  for (int s = 0; s < T / 32; ++s) {
+    const int jr = 32 * s + 8 * g + li / 4;
+    const int cc = 4 * (li % 4);
+    i16x8 chi = ones, clo = ones;
+    if (WC) c_operand(sC, s, g, chi, clo);
+    i16x8 aop[G::DT];
+#pragma unroll
+    for (int a = 0; a < G::DT; ++a) {
+      const int mt = w * G::DT + a;
+      aop[a] = cat(lds_tr(sA + jr * G::LD + 16 * mt + cc), lds_tr(sA + (jr + 4) * G::LD + 16 * mt + cc));
+    }
+#pragma unroll
+    for (int n = 0; n < G::NTL; ++n) {
+      const i16x8 b = cat(lds_tr(sB + jr * G::LD + 16 * n + cc), lds_tr(sB + (jr + 4) * G::LD + 16 * n + cc));
+#pragma unroll
+      for (int a = 0; a < G::DT; ++a) X[a][n] = mfma(aop[a], b, X[a][n]);
+      if (n / G::DT == w) {
+        const int b_ = n % G::DT;
+        x[b_] = mfma(chi, b, x[b_]);
+        if (WC) x[b_] = mfma(clo, b, x[b_]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Forward sweep: dq, the per-row c and den for the reverse sweep, and the
+// segment's (R, r) aggregate when r_agg != null.
+//
+// The normaliser terms are recomputed here in fp32 rather than read from the
+// forward's (rounded) output: grad phi(Q_i) = sum_j phi(K_j) g_i.(V_j - out_i)
+// is a near-cancellation of S g_i against c_i Z, so c_i must be formed from
+// the same rounded g_i the MFMAs use and from an unrounded out_i.  The chunk
+// therefore first repeats the forward computation (num_i, den_i), then sets
+//   g_i = bf16(dout_i / den_i),  c_i = -(g_i . num_i) / den_i.
+// ---------------------------------------------------------------------------
+template <int DIM, bool CAUSAL>
+__global__ __launch_bounds__(NT) void k_bwd_dq_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                    const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
+                                                    const float* __restrict__ carry_s, bf16_t* __restrict__ dq,
+                                                    float* __restrict__ r_agg, float* __restrict__ c_out,
+                                                    float* __restrict__ den_out, int64_t N, int P, int seg_len) {
+  using G = Geo<DIM>;
+  constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* sKf = smem;
+  uint16_t* sV = sKf + T * LD;
+  uint16_t* sQf = sV + T * LD;
+  uint16_t* sG = sQf + T * LD;
+  uint16_t* sS = sG + T * LD;
+  float* sZ = reinterpret_cast<float*>(sS + DIM * LD);
+  float* sC = sZ + DIM;
+
+  // w is made wave-uniform (an SGPR) so that branches on it are scalar: an
+  // MFMA under an EXEC-masked branch still writes every lane.
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.x / P;
+  const int seg = blockIdx.x % P;
+  const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
+  const int64_t r1 = min(N, r0 + seg_len);
+  constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;
+  const float* cs = carry_s ? (CAUSAL ? carry_s + (bh * P + seg) * E : carry_s + bh * E) : nullptr;
+  const int64_t hoff = bh * N * DIM;
+  float* ch = c_out + bh * N;
+  float* dh = den_out + bh * N;
+  const bool want_r = r_agg != nullptr;
+  const int i = 16 * w + li;
+  const int cc = 4 * (li % 4);
+
+  f32x4_t Sacc[DT][NTL], zacc[DT], Racc[DT][NTL], racc[DT];
+  init_xt<DIM>(Sacc, zacc, cs, w, g, li);
+  init_xt<DIM>(Racc, racc, nullptr, w, g, li);
+  write_xt<DIM>(sS, sZ, Sacc, zacc, w, g, li);
+
+  int64_t c0 = r0;
+  int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
+  i32x4 kraw[PC], vraw[PC], qraw[PC], graw[KS];
+  auto fetch = [&](int64_t cc0, int nr) {
+    if (CAUSAL) {
+      load_tile<DIM>(kraw, k + hoff, cc0, nr);
+      load_tile<DIM>(vraw, v + hoff, cc0, nr);
+    }
+    load_tile<DIM>(qraw, q + hoff, cc0, nr);
+    load_q<DIM>(graw, dout + hoff, cc0, nr, i, g);
+  };
+  fetch(c0, nrow);
+
+  while (c0 < r1) {
+    if (CAUSAL) {
+      store_tile<DIM, true>(sKf, kraw, nrow);
+      store_tile<DIM, false>(sV, vraw, nrow);
+    }
+    store_tile<DIM, true>(sQf, qraw, nrow);
+    __syncthreads();
+    const bool valid = i < nrow;
+    i32x4 gcur[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) gcur[s] = graw[s];
+    const int64_t c1 = c0 + T;
+    const int nrow1 = c1 < r1 ? static_cast<int>(min(static_cast<int64_t>(T), r1 - c1)) : 0;
+    if (nrow1 > 0) fetch(c1, nrow1);
+
+    // --- the forward quantities num_i (fp32) and den_i for this wave's rows
+    i16x8 qf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = lds8(sQf + i * LD + 8 * g + 32 * s);
+    i16x4 ahi[4], alo[4];
+    float rs = 0.f;
+    if (CAUSAL) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        ahi[t] = alo[t] = i16x4{0, 0, 0, 0};
+        if (t <= w) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) acc = mfma(lds8(sKf + (16 * t + li) * LD + 8 * g + 32 * s), qf[s], acc);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (t == w && 4 * g + u > li) acc[u] = 0.f;
+          split(acc, ahi[t], alo[t]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) rs += fb(ahi[t][u]) + fb(alo[t][u]);
+        }
+      }
+      rs = shfl_sum_groups(rs);
+    }
+    float di = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) di += fb(qf[s][e]) * sZ[8 * g + 32 * s + e];
+    di = shfl_sum_groups(di);
+    const float den = rs + di;
+    f32x4_t num[NTL];
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) {
+      num[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int dr = 32 * s + 8 * g + li / 4;
+        const i16x8 a = cat(lds_tr(sS + dr * LD + 16 * n + cc), lds_tr(sS + (dr + 4) * LD + 16 * n + cc));
+        num[n] = mfma(a, qf[s], num[n]);
+      }
+      if (CAUSAL) {
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+          if (2 * tp <= w) {
+            const int jr = 32 * tp + 4 * g + li / 4;
+            const i16x8 a = cat(lds_tr(sV + jr * LD + 16 * n + cc), lds_tr(sV + (jr + 16) * LD + 16 * n + cc));
+            num[n] = mfma(a, cat(ahi[2 * tp], ahi[2 * tp + 1]), num[n]);
+            num[n] = mfma(a, cat(alo[2 * tp], alo[2 * tp + 1]), num[n]);
+          }
+        }
+      }
+    }
+    // --- g_i = bf16(dout_i / den_i) (to registers and sG), then c_i
+    const float inv = valid ? 1.f / den : 0.f;
+    i16x8 gq[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const i16x8 hg = __builtin_bit_cast(i16x8, gcur[s]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gq[s][e] = bf(fb(hg[e]) * inv);
+      *reinterpret_cast<i16x8*>(sG + i * LD + 8 * g + 32 * s) = gq[s];
+    }
+    __syncthreads();
+    float dot = 0.f;
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) {
+      const i16x4 gv = *reinterpret_cast<const i16x4*>(sG + i * LD + 16 * n + 4 * g);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) dot += fb(gv[u]) * num[n][u];
+    }
+    dot = shfl_sum_groups(dot);
+    const float c = -dot * inv;
+    if (g == 0) {
+      sC[i] = c;
+      if (valid) {
+        ch[c0 + i] = c;
+        dh[c0 + i] = den;
+      }
+    }
+    __syncthreads();
+
+    // --- B^T[j][i] = g_i.V_j + c_i for key tiles t <= w, masked j <= i
+    i16x4 bhi[4], blo[4];
+    if (CAUSAL) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bhi[t] = blo[t] = i16x4{0, 0, 0, 0};
+        if (t <= w) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) acc = mfma(lds8(sV + (16 * t + li) * LD + 8 * g + 32 * s), gq[s], acc);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[u] = (t == w && 4 * g + u > li) ? 0.f : acc[u] + c;
+          split(acc, bhi[t], blo[t]);
+        }
+      }
+    }
+    // --- grad phi(Q)^T[d][i] = S g_i (+ phi(K)^T B^T) + c_i Z[d]
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) {
+      f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) o = mfma(lds8(sS + (16 * n + li) * LD + 8 * g + 32 * s), gq[s], o);
+      if (CAUSAL) {
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+          if (2 * tp <= w) {
+            const int jr = 32 * tp + 4 * g + li / 4;
+            const i16x8 a = cat(lds_tr(sKf + jr * LD + 16 * n + cc), lds_tr(sKf + (jr + 16) * LD + 16 * n + cc));
+            o = mfma(a, cat(bhi[2 * tp], bhi[2 * tp + 1]), o);
+            o = mfma(a, cat(blo[2 * tp], blo[2 * tp + 1]), o);
+          }
+        }
+      }
+      if (valid) {
+        const i16x4 qv = *reinterpret_cast<const i16x4*>(sQf + i * LD + 16 * n + 4 * g);
+        i16x4 r;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u] = bf((o[u] + c * sZ[16 * n + 4 * g + u]) * fminf(fb(qv[u]), 1.f));
+        *reinterpret_cast<i16x4*>(dq + hoff + (c0 + i) * DIM + 16 * n + 4 * g) = r;
+      }
+    }
+    if (CAUSAL) outer_update<DIM, false>(Sacc, zacc, sV, sKf, nullptr, w, g, li);
+    if (want_r) outer_update<DIM, true>(Racc, racc, sG, sQf, sC, w, g, li);
+    __syncthreads();
+    if (CAUSAL) write_xt<DIM>(sS, sZ, Sacc, zacc, w, g, li);
+    c0 = c1;
+    nrow = nrow1;
+  }
+  if (want_r) store_xt<DIM>(r_agg + (bh * P + seg) * E, Racc, racc, w, g, li);
+}
+
+// ---------------------------------------------------------------------------
+// Reverse sweep: dk, dv with the suffix state (R, r) carried in.
+// ---------------------------------------------------------------------------
+template <int DIM, bool CAUSAL>
+__global__ __launch_bounds__(NT) void k_bwd_dkdv_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
+                                                      const float* __restrict__ den_in,
+                                                      const float* __restrict__ c_in,
+                                                      const float* __restrict__ carry_r, bf16_t* __restrict__ dk,
+                                                      bf16_t* __restrict__ dv, int64_t N, int P, int seg_len) {
+  using G = Geo<DIM>;
+  constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* sKf = smem;
+  uint16_t* sV = sKf + T * LD;
+  uint16_t* sQf = sV + T * LD;
+  uint16_t* sG = sQf + T * LD;
+  uint16_t* sR = sG + T * LD;
+  float* sRv = reinterpret_cast<float*>(sR + DIM * LD);
+  float* sC = sRv + DIM;
+
+  // w is made wave-uniform (an SGPR) so that branches on it are scalar: an
+  // MFMA under an EXEC-masked branch still writes every lane.
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.x / P;
+  const int seg = blockIdx.x % P;
+  const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
+  const int64_t r1 = min(N, r0 + seg_len);
+  constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;
+  const float* cr = carry_r ? (CAUSAL ? carry_r + (bh * P + seg) * E : carry_r + bh * E) : nullptr;
+  const int64_t hoff = bh * N * DIM;
+  const float* denh = den_in + bh * N;
+  const float* chh = c_in + bh * N;
+  const int j = 16 * w + li;  // this lane's key row (outputs); also its query row for g, c
+
+  f32x4_t Racc[DT][NTL], racc[DT];
+  init_xt<DIM>(Racc, racc, cr, w, g, li);
+  write_xt<DIM>(sR, sRv, Racc, racc, w, g, li);
+
+  const int64_t nch = (r1 - r0 + T - 1) / T;
+  int64_t ci = nch - 1;
+  int64_t c0 = r0 + ci * T;
+  int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
+  i32x4 kraw[PC], vraw[PC], qraw[PC], graw[KS];
+  float dnr = 1.f, cnr = 0.f;
+  auto fetch = [&](int64_t cc0, int nr) {
+    load_tile<DIM>(kraw, k + hoff, cc0, nr);
+    load_tile<DIM>(vraw, v + hoff, cc0, nr);
+    if (CAUSAL) {
+      load_tile<DIM>(qraw, q + hoff, cc0, nr);
+      load_q<DIM>(graw, dout + hoff, cc0, nr, j, g);
+      dnr = j < nr ? denh[cc0 + j] : 1.f;
+      cnr = j < nr ? chh[cc0 + j] : 0.f;
+    }
+  };
+  fetch(c0, nrow);
+
+  while (ci >= 0) {
+    store_tile<DIM, true>(sKf, kraw, nrow);
+    store_tile<DIM, false>(sV, vraw, nrow);
+    if (CAUSAL) {
+      // the same g_i = bf16(dout_i / den_i) and c_i as the forward sweep used
+      store_tile<DIM, true>(sQf, qraw, nrow);
+      const float inv = j < nrow ? 1.f / dnr : 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const i16x8 hg = __builtin_bit_cast(i16x8, graw[s]);
+        i16x8 gv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gv[e] = bf(fb(hg[e]) * inv);
+        *reinterpret_cast<i16x8*>(sG + j * LD + 8 * g + 32 * s) = gv;
+      }
+      if (g == 0) sC[j] = j < nrow ? cnr : 0.f;
+    }
+    __syncthreads();
+
+    const int64_t cp = c0 - T;
+    const int nrowp = ci > 0 ? T : 0;  // earlier chunks of a segment are always full
+    if (ci > 0) fetch(cp, nrowp);
+
+    const bool valid = j < nrow;
+    i16x8 kreg[KS], vreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      kreg[s] = lds8(sKf + j * LD + 8 * g + 32 * s);
+      vreg[s] = lds8(sV + j * LD + 8 * g + 32 * s);
+    }
+    // A[i][j] = phi(Q_i).phi(K_j) and Bm[i][j] = g_i.V_j + c_i for query
+    // tiles t >= w, masked i >= j, hi + lo
+    i16x4 ahi[4], alo[4], bhi[4], blo[4];
+    if (CAUSAL) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        ahi[t] = alo[t] = bhi[t] = blo[t] = i16x4{0, 0, 0, 0};
+        if (t >= w) {
+          f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            a = mfma(lds8(sQf + (16 * t + li) * LD + 8 * g + 32 * s), kreg[s], a);
+            b = mfma(lds8(sG + (16 * t + li) * LD + 8 * g + 32 * s), vreg[s], b);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const bool keep = !(t == w && 4 * g + u < li);
+            a[u] = keep ? a[u] : 0.f;
+            b[u] = keep ? b[u] + sC[16 * t + 4 * g + u] : 0.f;
+          }
+          split(a, ahi[t], alo[t]);
+          split(b, bhi[t], blo[t]);
+        }
+      }
+    }
+    const int cc = 4 * (li % 4);
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) {
+      // grad V^T[m][j] = R^T phi(K_j) (+ g^T A)
+      f32x4_t ov = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int dr = 32 * s + 8 * g + li / 4;
+        const i16x8 a = cat(lds_tr(sR + dr * LD + 16 * n + cc), lds_tr(sR + (dr + 4) * LD + 16 * n + cc));
+        ov = mfma(a, kreg[s], ov);
+      }
+      // grad phi(K)^T[d][j] = R V_j (+ phi(Q)^T Bm) + r[d]
+      f32x4_t ok = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) ok = mfma(lds8(sR + (16 * n + li) * LD + 8 * g + 32 * s), vreg[s], ok);
+      if (CAUSAL) {
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+          if (2 * tp + 1 >= w) {
+            const int ir = 32 * tp + 4 * g + li / 4;
+            const i16x8 ag = cat(lds_tr(sG + ir * LD + 16 * n + cc), lds_tr(sG + (ir + 16) * LD + 16 * n + cc));
+            ov = mfma(ag, cat(ahi[2 * tp], ahi[2 * tp + 1]), ov);
+            ov = mfma(ag, cat(alo[2 * tp], alo[2 * tp + 1]), ov);
+            const i16x8 aq = cat(lds_tr(sQf + ir * LD + 16 * n + cc), lds_tr(sQf + (ir + 16) * LD + 16 * n + cc));
+            ok = mfma(aq, cat(bhi[2 * tp], bhi[2 * tp + 1]), ok);
+            ok = mfma(aq, cat(blo[2 * tp], blo[2 * tp + 1]), ok);
+          }
+        }
+      }
+      if (valid) {
+        i16x4 rv, rk;
+        const i16x4 kv = *reinterpret_cast<const i16x4*>(sKf + j * LD + 16 * n + 4 * g);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          rv[u] = bf(ov[u]);
+          rk[u] = bf((ok[u] + sRv[16 * n + 4 * g + u]) * fminf(fb(kv[u]), 1.f));
+        }
+        *reinterpret_cast<i16x4*>(dv + hoff + (c0 + j) * DIM + 16 * n + 4 * g) = rv;
+        *reinterpret_cast<i16x4*>(dk + hoff + (c0 + j) * DIM + 16 * n + 4 * g) = rk;
+      }
+    }
+    if (CAUSAL) outer_update<DIM, true>(Racc, racc, sG, sQf, sC, w, g, li);
+    __syncthreads();
+    if (CAUSAL) write_xt<DIM>(sR, sRv, Racc, racc, w, g, li);
+    --ci;
+    c0 = cp;
+    nrow = nrowp;
+  }
+}
+
+size_t lds_bwd(int dim) {
+  return (4 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + (dim + T) * sizeof(float);
+}
+
+#define LA_MLAUNCH(kernel, grid, lds, st, ...)                                                              \
+  do {                                                                                                      \
+    hipError_t e_ = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),                              \
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)); \
+    if (e_ != hipSuccess) return e_;                                                                        \
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(NT), lds, st, __VA_ARGS__);          \
+    return hipGetLastError();                                                                               \
+  } while (0)
+
+}  // namespace
+
+hipError_t launch_bwd_dq_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
+                              const void* dout, const float* carry_s, void* dq, float* r_agg, float* c_out,
+                              float* den_out, hipStream_t st) {
+  const int64_t grid = g.BH * g.P;
+#define LA_DQ(D, C)                                                                                          \
+  LA_MLAUNCH((k_bwd_dq_mfma<D, C>), grid, lds_bwd(D), st, static_cast<const bf16_t*>(q),                    \
+             static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), \
+             carry_s, static_cast<bf16_t*>(dq), r_agg, c_out, den_out, g.N, g.P, g.seg_len)
+  if (g.D == 64) {
+    if (causal) LA_DQ(64, true);
+    LA_DQ(64, false);
+  }
+  if (g.D == 128) {
+    if (causal) LA_DQ(128, true);
+    LA_DQ(128, false);
+  }
+#undef LA_DQ
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_bwd_dkdv_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
+                                const void* dout, const float* den, const float* c, const float* carry_r,
+                                void* dk, void* dv, hipStream_t st) {
+  const int64_t grid = g.BH * g.P;
+#define LA_KV(D, C)                                                                                          \
+  LA_MLAUNCH((k_bwd_dkdv_mfma<D, C>), grid, lds_bwd(D), st, static_cast<const bf16_t*>(q),                  \
+             static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), \
+             den, c, carry_r, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), g.N, g.P, g.seg_len)
+  if (g.D == 64) {
+    if (causal) LA_KV(64, true);
+    LA_KV(64, false);
+  }
+  if (g.D == 128) {
+    if (causal) LA_KV(128, true);
+    LA_KV(128, false);
+  }
+#undef LA_KV
+  return hipErrorNotSupported;
+}
+
+}  // namespace la

@@ -74,5 +74,54 @@ __device__ __forceinline__ float shfl_sum_groups(float x) {
 
 __device__ __forceinline__ i32x4 gload16(const bf16_t* p) { return *reinterpret_cast<const i32x4*>(p); }
 
+constexpr int kNT = 256;  // threads per workgroup (4 wave64s)
+constexpr int kT = 64;    // tokens per chunk
+
+template <int DIM>
+struct Geo {
+  static constexpr int LD = DIM + 8;            // padded LDS row stride (elements)
+  static constexpr int NTL = DIM / 16;          // 16-wide tiles along D (= M)
+  static constexpr int KS = DIM / 32;             // 32-deep k-steps along D (= M)
+  static constexpr int PC = kT * DIM / 8 / kNT; // 16-byte pieces per thread per T x DIM tile
+  static constexpr int DT = NTL / 4;            // state row tiles owned by each wave
+  static constexpr int ROW8 = DIM / 8;            // 16-byte pieces per row
+};
+
+// Global -> registers: thread's pieces of a T x DIM token-major tile.
+template <int DIM>
+__device__ __forceinline__ void load_tile(i32x4 (&raw)[Geo<DIM>::PC], const bf16_t* __restrict__ src,
+                                          int64_t c0, int nrow) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int r = 0; r < G::PC; ++r) {
+    const int p = threadIdx.x + kNT * r;
+    const int j = p / G::ROW8, c8 = p % G::ROW8;
+    raw[r] = j < nrow ? gload16(src + (c0 + j) * DIM + c8 * 8) : i32x4{0, 0, 0, 0};
+  }
+}
+
+// Registers -> LDS (phi applied when asked); rows past nrow are zero.
+template <int DIM, bool PHI>
+__device__ __forceinline__ void store_tile(uint16_t* lds, const i32x4 (&raw)[Geo<DIM>::PC], int nrow) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int r = 0; r < G::PC; ++r) {
+    const int p = threadIdx.x + kNT * r;
+    const int j = p / G::ROW8, c8 = p % G::ROW8;
+    i16x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (j < nrow) val = PHI ? phi8(raw[r]) : __builtin_bit_cast(i16x8, raw[r]);
+    *reinterpret_cast<i16x8*>(lds + j * G::LD + c8 * 8) = val;
+  }
+}
+
+// This wave's query rows (i = 16w + li), 8 features per k-step.
+template <int DIM>
+__device__ __forceinline__ void load_q(i32x4 (&raw)[Geo<DIM>::KS], const bf16_t* __restrict__ src, int64_t c0,
+                                       int nrow, int i, int g) {
+#pragma unroll
+  for (int s = 0; s < Geo<DIM>::KS; ++s)
+    raw[s] = i < nrow ? gload16(src + (c0 + i) * DIM + 8 * g + 32 * s) : i32x4{0, 0, 0, 0};
+}
+
 }  // namespace mf
 }  // namespace la

@@ -71,7 +71,7 @@ def check_forward(tq, tk, tv, causal, dtype, plan=None, heads=None, null_guard=F
     return out, den
 
 
-def check_backward(tq, tk, tv, tg, causal, dtype, plan=None, heads=None, use_den=True):
+def check_backward(tq, tk, tv, tg, causal, dtype, plan=None, heads=None, use_den=True, floor_factor=None):
     out, den = la.forward(tq, tk, tv, causal=causal, return_den=True, plan=plan)
     dq, dk, dv = la.backward(tq, tk, tv, out, tg, den=den if use_den else None, causal=causal, plan=plan)
     torch.cuda.synchronize()
@@ -81,10 +81,11 @@ def check_backward(tq, tk, tv, tg, causal, dtype, plan=None, heads=None, use_den
     hi = [h for _, h in sel]
     q64, k64, v64, g64 = (f64(t[bi, hi]) for t in (tq, tk, tv, tg))
     rq, rk, rv, _, _ = oracle.backward(q64, k64, v64, g64, causal)
-    # rel-L2, with the denominator floored at 1e-3 * ||dout||: at N = 1 (and
+    # rel-L2, with the denominator floored at 1e-2 * ||dv||: at N = 1 (and
     # other degenerate inputs) dq and dk are exactly zero, so a plain relative
-    # error would divide rounding noise by zero.
-    floor = 1e-3 * np.linalg.norm(g64.ravel())
+    # error would divide rounding noise by zero; dv never degenerates (its
+    # rows sum to the rows of dout).
+    floor = 1e-2 * np.linalg.norm(rv.ravel())
 
     def err(x, r):
         return float(np.linalg.norm((x - r).ravel()) / max(np.linalg.norm(r.ravel()), floor))
@@ -94,6 +95,16 @@ def check_backward(tq, tk, tv, tg, causal, dtype, plan=None, heads=None, use_den
         + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     for n, e in errs.items():
         assert e < TOL[dtype], (n, e)
+    if dtype == "bf16" and floor_factor:
+        # The bf16 kernels feed phi(Q), phi(K) (~1 + x, so rounding to bf16
+        # keeps few bits of x) and g = dout/den to the MFMAs as bf16; an exact
+        # emulation of that arithmetic gives gradient errors of a few times
+        # the rounding of the gradients themselves.  Bar: floor_factor x that
+        # rounding error, or 1e-2 (half the tolerance) where it is tiny.
+        for n, r in (("dq", rq), ("dk", rk), ("dv", rv)):
+            e_round = err(f64(torch.from_numpy(r).float().to(torch.bfloat16)), r)
+            say(f"  {n}: bf16 rounding floor {e_round:.2e}")
+            assert errs[n] < max(floor_factor * e_round, 1e-2), (n, errs[n], e_round)
     return dq, dk, dv
 
 
@@ -252,7 +263,10 @@ def test_decode_shapes(DM, dtype):
     got = np.stack([f64(o) for o in outs])
     tol = TOL[dtype]
     assert rel_l2(got, o1) < tol
-    assert rel_l2(f64(S), S1) < 1e-5 and rel_l2(f64(Z), Z1) < 1e-5
+    # bf16 prefixes at D = M in {64, 128} go through the MFMA state kernel,
+    # which feeds phi(K) to the MFMA as bf16 (~2^-9 relative per element)
+    tol_state = 1e-5 if dtype == "f32" else 5e-3
+    assert rel_l2(f64(S), S1) < tol_state and rel_l2(f64(Z), Z1) < tol_state
 
 
 # ----------------------------------------------------- bf16 MFMA path ----
@@ -291,3 +305,37 @@ def test_mfma_prefix_state(D):
     # phi(K) enters the MFMA as bf16, so S carries that rounding (~2^-9)
     assert rel_l2(f64(S), S0) < 5e-3
     assert rel_l2(f64(Z), Z0) < 5e-3
+
+
+@pytest.mark.parametrize("shape", MFMA_SHAPES)
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("segments", [1, 3])
+def test_mfma_backward(shape, causal, segments):
+    B, H, N, D = shape
+    tq, tk, tv, tg = host_case(B, H, N, D, D, "bf16", seed=N + D + segments + 1, scale=1.0 / np.sqrt(D))
+    say(f"mfma backward {shape} causal={causal} segments={segments}")
+    check_backward(tq, tk, tv, tg, causal, "bf16", plan=dict(kernel=2, segments=segments), floor_factor=6.0)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_mfma_backward_unscaled_and_recomputed_den(D):
+    tq, tk, tv, tg = host_case(1, 2, 700, D, D, "bf16", seed=D + 5, scale=1.0)
+    check_backward(tq, tk, tv, tg, True, "bf16", plan=dict(kernel=2), floor_factor=6.0)
+    check_backward(tq, tk, tv, tg, True, "bf16", plan=dict(kernel=2), use_den=False)
+    check_backward(tq, tk, tv, tg, False, "bf16", plan=dict(kernel=2), floor_factor=6.0)
+
+
+def test_mfma_matches_generic_bf16():
+    # two independent kernel families on the same inputs
+    tq, tk, tv, tg = host_case(2, 2, 500, 64, 64, "bf16", seed=42, scale=0.125)
+    o1, d1 = la.forward(tq, tk, tv, return_den=True, plan=dict(kernel=2))
+    o2, d2 = la.forward(tq, tk, tv, return_den=True, plan=dict(kernel=1))
+    g1 = la.backward(tq, tk, tv, o2, tg, den=d2, plan=dict(kernel=2))
+    g2 = la.backward(tq, tk, tv, o2, tg, den=d2, plan=dict(kernel=1))
+    torch.cuda.synchronize()
+    assert rel_l2(f64(o1), f64(o2)) < 5e-3
+    assert rel_l2(f64(d1), f64(d2)) < 1e-3
+    # dq and dk of the two families differ by their own bf16 roundings (the
+    # generic kernels read the rounded forward output; the MFMA kernels round
+    # phi); each is checked against the oracle elsewhere.  dv is well posed.
+    assert rel_l2(f64(g1[2]), f64(g2[2])) < 1e-2
