@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the decode measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
     return ap.parse_args()
 
 
@@ -58,7 +60,13 @@ def kernel_bytes(name: str, B, H, N, D, M, es, P=1):
     """Algorithmic HBM bytes one launch of `name` must move (inputs read once,
     outputs written once), for B*H heads of N tokens."""
     ht = B * H * N
-    base = name.split(".", 1)[-1]
+    family, _, base = name.rpartition(".")
+    if family == "mfma" and base == "bwd_dq":
+        # reads q, k, v, dout; writes dq and the per-row (c, den) pair
+        return ht * (es * (2 * D + 2 * M) + es * D + 8)
+    if family == "mfma" and base == "bwd_dkdv":
+        # reads q, k, v, dout and (c, den); writes dk, dv
+        return ht * (es * (2 * D + 2 * M) + 8 + es * (D + M))
     if base == "forward":
         return ht * (es * (2 * D + M) + es * M + 4)
     if base == "forward_den":
@@ -86,6 +94,10 @@ def main():
 
     import torch
 
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
+
     import kernelized_causal_attention_amd as la
     from workloads import WORKLOADS, device_inputs
 
@@ -110,26 +122,35 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # A short pass with every kernel timed: the per-kernel breakdown, and
+    # which kernel dominates.
+    nbreak = 3
+    la.profile_enable(True)
+    for _ in range(nbreak):
+        step()
+    torch.cuda.synchronize()
+    prof = la.profile_report()
+    kname = max(prof.items(), key=lambda kv: kv[1][1])[0]
 
+    # Timed region: exactly K steps between synchronisations; only the
+    # dominant kernel is bracketed by events (on the stream it runs on).
     stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    la.profile_enable(True)
+    la.profile_enable(True, only=kname)
     torch.cuda.synchronize()
     t0.record(stream)
     for _ in range(args.steps):
         step()
     t1.record(stream)
     torch.cuda.synchronize()
-    prof = la.profile_report()
+    nl, tot_ms = la.profile_report()[kname]
     la.profile_enable(False)
     ms = t0.elapsed_time(t1) / args.steps
     tokens = B * N
     value = tokens / (ms / 1e3)
-    log(f"{ms:.3f} ms/step, {value:.4g} tokens/s; kernels: {prof}")
-
-    # dominant kernel by total time in the timed region
-    kname, (nl, tot_ms) = max(prof.items(), key=lambda kv: kv[1][1])
+    log(f"{ms:.3f} ms/step, {value:.4g} tokens/s; dominant {kname} {tot_ms / nl:.4f} ms; "
+        f"breakdown: {prof}")
     P = plan_b["segments"] if "bwd" in kname or "scan" in kname else plan_f["segments"]
     kb = kernel_bytes(kname, B, H, N, D, M, es, P)
     avg_ms = tot_ms / nl
@@ -138,7 +159,7 @@ def main():
     for name, (n, t) in sorted(prof.items()):
         b = kernel_bytes(name, B, H, N, D, M, es, P)
         avg = t / n
-        kernels[name] = {"launches_per_step": n / args.steps, "avg_ms": round(avg, 4),
+        kernels[name] = {"launches_per_step": n / nbreak, "avg_ms": round(avg, 4),
                          "alg_bytes": b, "GBps": round(b / (avg / 1e3) / 1e9, 1) if b else None}
     result = {
         "metric": "causal linear-attn fwd+bwd tokens/sec",
@@ -157,7 +178,8 @@ def main():
                    "N": N, "D": D, "M": M, "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)",
                    "plan_forward": plan_f, "plan_backward": plan_b},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(kname),
                      "alg_bytes_per_launch": kb, "avg_launch_ms": round(avg_ms, 4)},
         "kernels": kernels,
     }
@@ -169,6 +191,62 @@ def main():
         result["cpu_baseline"] = cpu_baseline(q, k, v, g, B, H, N, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+COPY_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwdbwd_bf16.txt")
+
+
+def calibrate_copy(torch):
+    """A plain device copy of exactly 1 GiB (read) + 1 GiB (write), repeated;
+    run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to get the scale of
+    those counters (bytes moved / counter value)."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": COPY_BYTES, "launches": 5}))
+
+
+def kernel_source_sha():
+    """Hash of the HIP sources: measured traffic is valid only for the
+    kernels it was measured on."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kernelized_causal_attention_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kname):
+    """HBM bytes per launch of `kname` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), or
+    None when it is missing or was taken on different kernel sources."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    sha = None
+    table = {}
+    for line in lines:
+        if line.startswith("source_sha"):
+            sha = line.split()[1]
+        elif line and not line.startswith("#"):
+            parts = line.split()
+            if len(parts) >= 3:
+                try:
+                    table[parts[0]] = int(float(parts[1])) + int(float(parts[2]))
+                except ValueError:
+                    pass
+    if sha != kernel_source_sha():
+        return None
+    return table.get(kname)
 
 
 def bench_decode(la, torch, steps):
@@ -186,7 +264,7 @@ def bench_decode(la, torch, steps):
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    la.profile_enable(True)
+    la.profile_enable(True, only="decode")
     e0.record(stream)
     for t in range(steps):
         la.decode_step(S, Z, sq[t % w.steps], sk[t % w.steps], sv[t % w.steps], out=outs[t])

@@ -163,6 +163,11 @@ la_status la_resolve_plan(int op, int64_t B, int64_t H, int64_t N, int64_t D, in
  * and clears the records.  LA_ERR_INVALID if buf is NULL or too small. */
 la_status la_profile_enable(int on);
 la_status la_profile_report(char* buf, size_t len);
+/* Restrict the timing to the kernels named in `names` (comma-separated,
+ * e.g. "mfma.bwd_dq"); NULL or "" times every kernel.  Each timed launch
+ * adds two event records to its stream, so timing only the kernel of
+ * interest keeps the rest of the stream undisturbed. */
+la_status la_profile_select(const char* names);
 
 const char* la_status_str(int status);
 /* Detail of the last non-OK status returned on this thread ("" if none). */

@@ -74,9 +74,13 @@ def version() -> int:
     return _native.load().la_version()
 
 
-def profile_enable(on: bool = True) -> None:
-    """Start (clearing old records) or stop per-kernel HIP-event timing."""
-    _native.check(_native.load().la_profile_enable(int(bool(on))))
+def profile_enable(on: bool = True, only=None) -> None:
+    """Start (clearing old records) or stop per-kernel HIP-event timing;
+    `only` restricts it to the named kernels (list or comma-separated)."""
+    lib = _native.load()
+    names = "" if only is None else (only if isinstance(only, str) else ",".join(only))
+    _native.check(lib.la_profile_select(names.encode()))
+    _native.check(lib.la_profile_enable(int(bool(on))))
 
 
 def profile_report() -> dict:

@@ -22,6 +22,7 @@ EXPORTS = (
     "la_forward", "la_forward_ex", "la_backward", "la_backward_ex", "la_decode_step",
     "la_prefix_state", "la_workspace_bytes", "la_workspace_bytes_ex", "la_resolve_plan",
     "la_status_str", "la_last_error", "la_version", "la_profile_enable", "la_profile_report",
+    "la_profile_select",
 )
 
 
@@ -73,6 +74,7 @@ def load() -> ctypes.CDLL:
         "la_version": ([], i32),
         "la_profile_enable": ([i32], i32),
         "la_profile_report": ([ctypes.c_char_p, sz], i32),
+        "la_profile_select": ([ctypes.c_char_p], i32),
     }
     for name, (args, res) in sigs.items():
         f = getattr(lib, name)

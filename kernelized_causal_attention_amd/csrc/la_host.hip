@@ -141,9 +141,10 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
   int64_t P = req && req->segments > 0 ? req->segments : 0;
   if (req && req->segments < 0) return fail(LA_ERR_INVALID, "plan.segments=%d", req->segments);
   if (P == 0) {
-    // Enough independent workgroups to cover 256 CUs about twice over,
-    // with segments of at least 4 units.
-    const int64_t want = (512 + BH - 1) / BH;
+    // About 1024 independent workgroups (four per CU on 256 CUs) so that
+    // several segments' loads are in flight per CU, with segments of at
+    // least 4 units; more segments only add scan work.
+    const int64_t want = (1024 + BH - 1) / BH;
     P = std::min<int64_t>(want, std::max<int64_t>(1, nunits / 4));
   }
   P = std::max<int64_t>(1, std::min<int64_t>(P, nunits));
@@ -217,6 +218,13 @@ struct ProfRec {
 
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+std::string g_prof_only;  // comma-separated kernel names to time ("" = all)
+
+bool prof_wanted(const char* name) {
+  if (g_prof_only.empty()) return true;
+  const std::string key = std::string(",") + name + ",";
+  return (std::string(",") + g_prof_only + ",").find(key) != std::string::npos;
+}
 std::vector<ProfRec> g_prof;
 std::vector<hipEvent_t> g_pool;
 
@@ -233,7 +241,7 @@ hipEvent_t pool_get() {
 
 template <typename F>
 hipError_t timed(const char* name, hipStream_t st, F&& f) {
-  if (!g_prof_on) return f();
+  if (!g_prof_on || !prof_wanted(name)) return f();
   hipEvent_t a, b;
   {
     std::lock_guard<std::mutex> lk(g_prof_mu);
@@ -588,6 +596,12 @@ LA_API la_status la_profile_enable(int on) {
   }
   g_prof.clear();
   g_prof_on = on != 0;
+  return ok();
+}
+
+LA_API la_status la_profile_select(const char* names) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_only = names ? names : "";
   return ok();
 }
 

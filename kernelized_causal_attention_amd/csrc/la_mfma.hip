@@ -188,12 +188,11 @@ __global__ __launch_bounds__(NT) void k_fwd_mfma(const bf16_t* __restrict__ q, c
               if (4 * g + u > li) acc[u] = 0.f;
           }
           ahi[t] = pack4(acc);
+          const f32x4_t h = unpack4(ahi[t]);
+          alo[t] = pack4(acc - h);
+          const f32x4_t lo = unpack4(alo[t]);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float h = fb(ahi[t][u]);
-            alo[t][u] = bf(acc[u] - h);
-            rs += h + fb(alo[t][u]);
-          }
+          for (int u = 0; u < 4; ++u) rs += h[u] + lo[u];
         }
       }
       rs = shfl_sum_groups(rs);
@@ -236,13 +235,10 @@ __global__ __launch_bounds__(NT) void k_fwd_mfma(const bf16_t* __restrict__ q, c
     }
     if (i < nrow) {
       if (oh) {
+        const float inv = 1.f / den;
 #pragma unroll
-        for (int n = 0; n < NTL; ++n) {
-          i16x4 ov;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) ov[u] = bf(o[n][u] / den);
-          *reinterpret_cast<i16x4*>(oh + (c0 + i) * DIM + 16 * n + 4 * g) = ov;
-        }
+        for (int n = 0; n < NTL; ++n)
+          *reinterpret_cast<i16x4*>(oh + (c0 + i) * DIM + 16 * n + 4 * g) = pack4(o[n] * inv);
       }
       if (dh && g == 0) dh[c0 + i] = den;
     }

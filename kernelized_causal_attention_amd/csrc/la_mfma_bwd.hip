@@ -38,19 +38,15 @@ constexpr int T = kT;
 // Split a masked fp32 score tile into bf16 hi + lo.
 __device__ __forceinline__ void split(const f32x4_t& acc, i16x4& hi, i16x4& lo) {
   hi = pack4(acc);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) lo[u] = bf(acc[u] - fb(hi[u]));
+  lo = pack4(acc - unpack4(hi));
 }
 
 // c values of tokens 32s + 8g .. +7 as bf16 hi / lo A operands (every row
 // of the operand is the same, so the MFMA result is sum_i c_i X[i][col]).
 __device__ __forceinline__ void c_operand(const float* sC, int s, int g, i16x8& hi, i16x8& lo) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float c = sC[32 * s + 8 * g + e];
-    hi[e] = bf(c);
-    lo[e] = bf(c - fb(hi[e]));
-  }
+  const f32x8_t c = *reinterpret_cast<const f32x8_t*>(sC + 32 * s + 8 * g);
+  hi = pack8(c);
+  lo = pack8(c - unpack8(hi));
 }
 
 // Per-wave state layout used by both kernels: X^T accumulators (X = S or R)
@@ -275,9 +271,7 @@ __global__ __launch_bounds__(NT) void k_bwd_dq_mfma(const bf16_t* __restrict__ q
     i16x8 gq[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const i16x8 hg = __builtin_bit_cast(i16x8, gcur[s]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gq[s][e] = bf(fb(hg[e]) * inv);
+      gq[s] = pack8(unpack8(__builtin_bit_cast(i16x8, gcur[s])) * inv);
       *reinterpret_cast<i16x8*>(sG + i * LD + 8 * g + 32 * s) = gq[s];
     }
     __syncthreads();
@@ -416,13 +410,9 @@ __global__ __launch_bounds__(NT) void k_bwd_dkdv_mfma(const bf16_t* __restrict__
       store_tile<DIM, true>(sQf, qraw, nrow);
       const float inv = j < nrow ? 1.f / dnr : 0.f;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const i16x8 hg = __builtin_bit_cast(i16x8, graw[s]);
-        i16x8 gv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gv[e] = bf(fb(hg[e]) * inv);
-        *reinterpret_cast<i16x8*>(sG + j * LD + 8 * g + 32 * s) = gv;
-      }
+      for (int s = 0; s < KS; ++s)
+        *reinterpret_cast<i16x8*>(sG + j * LD + 8 * g + 32 * s) =
+            pack8(unpack8(__builtin_bit_cast(i16x8, graw[s])) * inv);
       if (g == 0) sC[j] = j < nrow ? cnr : 0.f;
     }
     __syncthreads();

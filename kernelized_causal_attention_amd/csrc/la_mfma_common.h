@@ -44,25 +44,45 @@ __device__ __forceinline__ i16x8 cat(i16x4 a, i16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__device__ __forceinline__ short bf(float x) { return static_cast<short>(f32_to_bf16(x)); }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+
+// fp32 -> bf16 conversions use the hardware round-to-nearest-even packed
+// convert (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ short bf(float x) {
+  const f32x2_t v = {x, 0.f};
+  return __builtin_bit_cast(short, __builtin_convertvector(v, bf16x2_t)[0]);
+}
 __device__ __forceinline__ float fb(short h) { return bf16_to_f32(static_cast<uint16_t>(h)); }
 
 __device__ __forceinline__ i16x4 pack4(f32x4_t v) {
-  i16x4 r;
-  r[0] = bf(v[0]);
-  r[1] = bf(v[1]);
-  r[2] = bf(v[2]);
-  r[3] = bf(v[3]);
-  return r;
+  return __builtin_bit_cast(i16x4, __builtin_convertvector(v, bf16x4_t));
 }
+
+__device__ __forceinline__ i16x8 pack8(f32x8_t v) {
+  return __builtin_bit_cast(i16x8, __builtin_convertvector(v, bf16x8_t));
+}
+
+__device__ __forceinline__ f32x8_t unpack8(i16x8 h) {
+  return __builtin_convertvector(__builtin_bit_cast(bf16x8_t, h), f32x8_t);
+}
+
+__device__ __forceinline__ f32x4_t unpack4(i16x4 h) {
+  return __builtin_convertvector(__builtin_bit_cast(bf16x4_t, h), f32x4_t);
+}
+
+// phi for the bf16 kernels: e^x through the hardware exp2 (its error is far
+// below the bf16 rounding that follows).
+__device__ __forceinline__ float phi_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
 // phi applied to 8 bf16 values (raw 16-byte vector), result rounded to bf16.
 __device__ __forceinline__ i16x8 phi8(i32x4 raw) {
-  const i16x8 h = __builtin_bit_cast(i16x8, raw);
-  i16x8 r;
+  f32x8_t x = unpack8(__builtin_bit_cast(i16x8, raw));
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = bf(phi(fb(h[e])));
-  return r;
+  for (int e = 0; e < 8; ++e) x[e] = phi_fast(x[e]);
+  return pack8(x);
 }
 
 __device__ __forceinline__ float shfl_sum_groups(float x) {
