@@ -103,7 +103,7 @@ __device__ __forceinline__ void init_state(f32x4_t (&Sacc)[Geo<DIM>::DT][Geo<DIM
 
 // ---------------------------------------------------------------------------
 template <int DIM, bool CAUSAL>
-__global__ __launch_bounds__(NT) void k_fwd_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+__global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_fwd_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                  const bf16_t* __restrict__ v, bf16_t* __restrict__ out,
                                                  float* __restrict__ den_out, const float* __restrict__ carry,
                                                  int64_t N, int P, int seg_len) {
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(NT) void k_fwd_mfma(const bf16_t* __restrict__ q, c
 
 // Segment aggregates dS = phi(K)^T V, dZ = colsum phi(K) over one segment.
 template <int DIM>
-__global__ __launch_bounds__(NT) void k_seg_state_mfma(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+__global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_seg_state_mfma(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                                        float* __restrict__ s_out, int64_t s_stride,
                                                        float* __restrict__ z_out, int64_t z_stride, int64_t N,
                                                        int P, int seg_len) {

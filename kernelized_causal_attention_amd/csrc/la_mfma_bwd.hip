@@ -41,12 +41,12 @@ __device__ __forceinline__ void split(const f32x4_t& acc, i16x4& hi, i16x4& lo) 
   lo = pack4(acc - unpack4(hi));
 }
 
-// c values of tokens 32s + 8g .. +7 as bf16 hi / lo A operands (every row
-// of the operand is the same, so the MFMA result is sum_i c_i X[i][col]).
-__device__ __forceinline__ void c_operand(const float* sC, int s, int g, i16x8& hi, i16x8& lo) {
-  const f32x8_t c = *reinterpret_cast<const f32x8_t*>(sC + 32 * s + 8 * g);
-  hi = pack8(c);
-  lo = pack8(c - unpack8(hi));
+// Each row's c as a bf16 hi + lo pair in LDS (sCh[i], sCh[T + i]), written
+// once per chunk by the wave that owns the row.
+__device__ __forceinline__ void put_c(uint16_t* sCh, int i, float c) {
+  const short hi = bf(c);
+  sCh[i] = static_cast<uint16_t>(hi);
+  sCh[kT + i] = static_cast<uint16_t>(bf(c - fb(hi)));
 }
 
 // Per-wave state layout used by both kernels: X^T accumulators (X = S or R)
@@ -101,11 +101,13 @@ __device__ __forceinline__ void store_xt(float* __restrict__ rec, const f32x4_t 
 }
 
 // X^T[m][d] += sum_j A[j][m] B[j][d] over the chunk's 64 tokens, and
-// x[d] += sum_j w_j B[j][d] (w = ones, or c as hi + lo when WC).
+// x[d] += sum_j w_j B[j][d] (w = ones, or c as the hi + lo pair in sCh when
+// WC; every row of that A operand is the same, so the MFMA result is
+// sum_j c_j B[j][col]).
 template <int DIM, bool WC>
 __device__ __forceinline__ void outer_update(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&x)[Geo<DIM>::DT],
-                                             const uint16_t* sA, const uint16_t* sB, const float* sC, int w, int g,
-                                             int li) {
+                                             const uint16_t* sA, const uint16_t* sB, const uint16_t* sCh, int w,
+                                             int g, int li) {
   using G = Geo<DIM>;
   const short one = 0x3f80;
   const i16x8 ones = {one, one, one, one, one, one, one, one};
@@ -114,7 +116,10 @@ __device__ __forceinline__ void outer_update(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>
     const int jr = 32 * s + 8 * g + li / 4;
     const int cc = 4 * (li % 4);
     i16x8 chi = ones, clo = ones;
-    if (WC) c_operand(sC, s, g, chi, clo);
+    if (WC) {
+      chi = lds8(sCh + 32 * s + 8 * g);
+      clo = lds8(sCh + T + 32 * s + 8 * g);
+    }
     i16x8 aop[G::DT];
 #pragma unroll
     for (int a = 0; a < G::DT; ++a) {
@@ -139,29 +144,33 @@ __device__ __forceinline__ void outer_update(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>
 // Forward sweep: dq, the per-row c and den for the reverse sweep, and the
 // segment's (R, r) aggregate when r_agg != null.
 //
-// The normaliser terms are recomputed here in fp32 rather than read from the
-// forward's (rounded) output: grad phi(Q_i) = sum_j phi(K_j) g_i.(V_j - out_i)
-// is a near-cancellation of S g_i against c_i Z, so c_i must be formed from
-// the same rounded g_i the MFMAs use and from an unrounded out_i.  The chunk
-// therefore first repeats the forward computation (num_i, den_i), then sets
-//   g_i = bf16(dout_i / den_i),  c_i = -(g_i . num_i) / den_i.
+// grad phi(Q_i) = sum_j phi(K_j) g_i.(V_j - out_i) is a near-cancellation of
+// S g_i against c_i Z, so c_i must come from the same rounded g_i the MFMAs
+// use and from the same S.  Here g_i = bf16(dout_i / den_i) with den_i
+// recomputed in fp32, and
+//   g_i . num_i = phi(Q_i) . (S g_i) + sum_{j<=i in chunk} A_ij (g_i . V_j),
+// whose two pieces are exactly the MFMA products the chunk needs anyway
+// (the inter term S g_i of grad phi(Q_i), and the tiles g_i . V_j of B), so
+// c_i = -(g_i . num_i) / den_i costs no extra pass over num.  The query,
+// g and c tiles are double-buffered so that the (R, r) aggregate of a chunk
+// can be summed after the chunk's last barrier: two barriers per chunk.
 // ---------------------------------------------------------------------------
 template <int DIM, bool CAUSAL>
-__global__ __launch_bounds__(NT) void k_bwd_dq_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                                                    const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
-                                                    const float* __restrict__ carry_s, bf16_t* __restrict__ dq,
-                                                    float* __restrict__ r_agg, float* __restrict__ c_out,
-                                                    float* __restrict__ den_out, int64_t N, int P, int seg_len) {
+__global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                       const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
+                                                       const float* __restrict__ carry_s, bf16_t* __restrict__ dq,
+                                                       float* __restrict__ r_agg, float* __restrict__ c_out,
+                                                       float* __restrict__ den_out, int64_t N, int P, int seg_len) {
   using G = Geo<DIM>;
   constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* sKf = smem;
   uint16_t* sV = sKf + T * LD;
-  uint16_t* sQf = sV + T * LD;
-  uint16_t* sG = sQf + T * LD;
-  uint16_t* sS = sG + T * LD;
+  uint16_t* sQf2 = sV + T * LD;     // two buffers
+  uint16_t* sG2 = sQf2 + 2 * T * LD;  // two buffers
+  uint16_t* sS = sG2 + 2 * T * LD;
   float* sZ = reinterpret_cast<float*>(sS + DIM * LD);
-  float* sC = sZ + DIM;
+  uint16_t* sCh2 = reinterpret_cast<uint16_t*>(sZ + DIM);  // two buffers of 2*T
 
   // w is made wave-uniform (an SGPR) so that branches on it are scalar: an
   // MFMA under an EXEC-masked branch still writes every lane.
@@ -198,7 +207,11 @@ __global__ __launch_bounds__(NT) void k_bwd_dq_mfma(const bf16_t* __restrict__ q
   };
   fetch(c0, nrow);
 
+  int buf = 0;
   while (c0 < r1) {
+    uint16_t* sQf = sQf2 + buf * T * LD;
+    uint16_t* sG = sG2 + buf * T * LD;
+    uint16_t* sCh = sCh2 + buf * 2 * T;
     if (CAUSAL) {
       store_tile<DIM, true>(sKf, kraw, nrow);
       store_tile<DIM, false>(sV, vraw, nrow);
@@ -213,133 +226,130 @@ __global__ __launch_bounds__(NT) void k_bwd_dq_mfma(const bf16_t* __restrict__ q
     const int nrow1 = c1 < r1 ? static_cast<int>(min(static_cast<int64_t>(T), r1 - c1)) : 0;
     if (nrow1 > 0) fetch(c1, nrow1);
 
-    // --- the forward quantities num_i (fp32) and den_i for this wave's rows
+    // --- den_i: intra-chunk scores A_ij (fp32, masked j <= i) and phi(Q_i).Z
     i16x8 qf[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = lds8(sQf + i * LD + 8 * g + 32 * s);
-    i16x4 ahi[4], alo[4];
+    f32x4_t at[4];
     float rs = 0.f;
     if (CAUSAL) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        ahi[t] = alo[t] = i16x4{0, 0, 0, 0};
+        at[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (t <= w) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < KS; ++s) acc = mfma(lds8(sKf + (16 * t + li) * LD + 8 * g + 32 * s), qf[s], acc);
+          for (int s = 0; s < KS; ++s) at[t] = mfma(lds8(sKf + (16 * t + li) * LD + 8 * g + 32 * s), qf[s], at[t]);
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (t == w && 4 * g + u > li) acc[u] = 0.f;
-          split(acc, ahi[t], alo[t]);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) rs += fb(ahi[t][u]) + fb(alo[t][u]);
-        }
-      }
-      rs = shfl_sum_groups(rs);
-    }
-    float di = 0.f;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) di += fb(qf[s][e]) * sZ[8 * g + 32 * s + e];
-    di = shfl_sum_groups(di);
-    const float den = rs + di;
-    f32x4_t num[NTL];
-#pragma unroll
-    for (int n = 0; n < NTL; ++n) {
-      num[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int dr = 32 * s + 8 * g + li / 4;
-        const i16x8 a = cat(lds_tr(sS + dr * LD + 16 * n + cc), lds_tr(sS + (dr + 4) * LD + 16 * n + cc));
-        num[n] = mfma(a, qf[s], num[n]);
-      }
-      if (CAUSAL) {
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp) {
-          if (2 * tp <= w) {
-            const int jr = 32 * tp + 4 * g + li / 4;
-            const i16x8 a = cat(lds_tr(sV + jr * LD + 16 * n + cc), lds_tr(sV + (jr + 16) * LD + 16 * n + cc));
-            num[n] = mfma(a, cat(ahi[2 * tp], ahi[2 * tp + 1]), num[n]);
-            num[n] = mfma(a, cat(alo[2 * tp], alo[2 * tp + 1]), num[n]);
+          for (int u = 0; u < 4; ++u) {
+            if (t == w && 4 * g + u > li) at[t][u] = 0.f;
+            rs += at[t][u];
           }
         }
       }
     }
-    // --- g_i = bf16(dout_i / den_i) (to registers and sG), then c_i
+    float di = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const f32x8_t qv = unpack8(qf[s]);
+      const f32x8_t zv = *reinterpret_cast<const f32x8_t*>(sZ + 8 * g + 32 * s);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) di += qv[e] * zv[e];
+    }
+    const float den = shfl_sum_groups(rs + di);
     const float inv = valid ? 1.f / den : 0.f;
+    // --- g_i = bf16(dout_i / den_i): registers (B operand) and sG (for R)
     i16x8 gq[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       gq[s] = pack8(unpack8(__builtin_bit_cast(i16x8, gcur[s])) * inv);
       *reinterpret_cast<i16x8*>(sG + i * LD + 8 * g + 32 * s) = gq[s];
     }
-    __syncthreads();
+    // --- S g_i  (dQ^T[d][i] inter term) and Bv^T[j][i] = g_i . V_j
+    f32x4_t o[NTL];
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) {
+      o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) o[n] = mfma(lds8(sS + (16 * n + li) * LD + 8 * g + 32 * s), gq[s], o[n]);
+    }
+    f32x4_t bv[4];
+    if (CAUSAL) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bv[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (t <= w) {
+#pragma unroll
+          for (int s = 0; s < KS; ++s) bv[t] = mfma(lds8(sV + (16 * t + li) * LD + 8 * g + 32 * s), gq[s], bv[t]);
+        }
+      }
+    }
+    // --- c_i = -(phi(Q_i).(S g_i) + sum_j A_ij (g_i . V_j)) / den_i
     float dot = 0.f;
 #pragma unroll
     for (int n = 0; n < NTL; ++n) {
-      const i16x4 gv = *reinterpret_cast<const i16x4*>(sG + i * LD + 16 * n + 4 * g);
+      const f32x4_t qd = unpack4(*reinterpret_cast<const i16x4*>(sQf + i * LD + 16 * n + 4 * g));
 #pragma unroll
-      for (int u = 0; u < 4; ++u) dot += fb(gv[u]) * num[n][u];
+      for (int u = 0; u < 4; ++u) dot += qd[u] * o[n][u];
     }
-    dot = shfl_sum_groups(dot);
-    const float c = -dot * inv;
+    if (CAUSAL) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (t <= w) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) dot += at[t][u] * bv[t][u];
+        }
+    }
+    const float c = -shfl_sum_groups(dot) * inv;
     if (g == 0) {
-      sC[i] = c;
+      put_c(sCh, i, c);
       if (valid) {
         ch[c0 + i] = c;
         dh[c0 + i] = den;
       }
     }
-    __syncthreads();
-
-    // --- B^T[j][i] = g_i.V_j + c_i for key tiles t <= w, masked j <= i
-    i16x4 bhi[4], blo[4];
+    // --- B^T = Bv^T + c_i (centred: g_i.(V_j - out_i)), masked j <= i,
+    // then grad phi(Q)^T += phi(K)^T B^T, + c_i Z[d], times phi'(q)
     if (CAUSAL) {
+      i16x4 bt[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        bhi[t] = blo[t] = i16x4{0, 0, 0, 0};
-        if (t <= w) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t b = bv[t] + c;
 #pragma unroll
-          for (int s = 0; s < KS; ++s) acc = mfma(lds8(sV + (16 * t + li) * LD + 8 * g + 32 * s), gq[s], acc);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) acc[u] = (t == w && 4 * g + u > li) ? 0.f : acc[u] + c;
-          split(acc, bhi[t], blo[t]);
-        }
+        for (int u = 0; u < 4; ++u)
+          if (t > w || (t == w && 4 * g + u > li)) b[u] = 0.f;
+        bt[t] = pack4(b);
       }
-    }
-    // --- grad phi(Q)^T[d][i] = S g_i (+ phi(K)^T B^T) + c_i Z[d]
 #pragma unroll
-    for (int n = 0; n < NTL; ++n) {
-      f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) o = mfma(lds8(sS + (16 * n + li) * LD + 8 * g + 32 * s), gq[s], o);
-      if (CAUSAL) {
+      for (int n = 0; n < NTL; ++n) {
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {
           if (2 * tp <= w) {
             const int jr = 32 * tp + 4 * g + li / 4;
             const i16x8 a = cat(lds_tr(sKf + jr * LD + 16 * n + cc), lds_tr(sKf + (jr + 16) * LD + 16 * n + cc));
-            o = mfma(a, cat(bhi[2 * tp], bhi[2 * tp + 1]), o);
-            o = mfma(a, cat(blo[2 * tp], blo[2 * tp + 1]), o);
+            o[n] = mfma(a, cat(bt[2 * tp], bt[2 * tp + 1]), o[n]);
           }
         }
       }
-      if (valid) {
-        const i16x4 qv = *reinterpret_cast<const i16x4*>(sQf + i * LD + 16 * n + 4 * g);
-        i16x4 r;
+    }
+    if (valid) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) r[u] = bf((o[u] + c * sZ[16 * n + 4 * g + u]) * fminf(fb(qv[u]), 1.f));
-        *reinterpret_cast<i16x4*>(dq + hoff + (c0 + i) * DIM + 16 * n + 4 * g) = r;
+      for (int n = 0; n < NTL; ++n) {
+        const f32x4_t z = *reinterpret_cast<const f32x4_t*>(sZ + 16 * n + 4 * g);
+        const f32x4_t qd = unpack4(*reinterpret_cast<const i16x4*>(sQf + i * LD + 16 * n + 4 * g));
+        f32x4_t r;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u] = (o[n][u] + c * z[u]) * __builtin_amdgcn_fmed3f(qd[u], 0.f, 1.f);
+        *reinterpret_cast<i16x4*>(dq + hoff + (c0 + i) * DIM + 16 * n + 4 * g) = pack4(r);
       }
     }
     if (CAUSAL) outer_update<DIM, false>(Sacc, zacc, sV, sKf, nullptr, w, g, li);
-    if (want_r) outer_update<DIM, true>(Racc, racc, sG, sQf, sC, w, g, li);
     __syncthreads();
+    // this chunk's g, phi(Q) and c rows are complete: sum its (R, r) part
+    if (want_r) outer_update<DIM, true>(Racc, racc, sG, sQf, sCh, w, g, li);
     if (CAUSAL) write_xt<DIM>(sS, sZ, Sacc, zacc, w, g, li);
     c0 = c1;
     nrow = nrow1;
+    buf ^= 1;
   }
   if (want_r) store_xt<DIM>(r_agg + (bh * P + seg) * E, Racc, racc, w, g, li);
 }
@@ -348,7 +358,7 @@ __global__ __launch_bounds__(NT) void k_bwd_dq_mfma(const bf16_t* __restrict__ q
 // Reverse sweep: dk, dv with the suffix state (R, r) carried in.
 // ---------------------------------------------------------------------------
 template <int DIM, bool CAUSAL>
-__global__ __launch_bounds__(NT) void k_bwd_dkdv_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+__global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                       const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
                                                       const float* __restrict__ den_in,
                                                       const float* __restrict__ c_in,
@@ -364,6 +374,7 @@ __global__ __launch_bounds__(NT) void k_bwd_dkdv_mfma(const bf16_t* __restrict__
   uint16_t* sR = sG + T * LD;
   float* sRv = reinterpret_cast<float*>(sR + DIM * LD);
   float* sC = sRv + DIM;
+  uint16_t* sCh = reinterpret_cast<uint16_t*>(sC + T);
 
   // w is made wave-uniform (an SGPR) so that branches on it are scalar: an
   // MFMA under an EXEC-masked branch still writes every lane.
@@ -413,7 +424,11 @@ __global__ __launch_bounds__(NT) void k_bwd_dkdv_mfma(const bf16_t* __restrict__
       for (int s = 0; s < KS; ++s)
         *reinterpret_cast<i16x8*>(sG + j * LD + 8 * g + 32 * s) =
             pack8(unpack8(__builtin_bit_cast(i16x8, graw[s])) * inv);
-      if (g == 0) sC[j] = j < nrow ? cnr : 0.f;
+      if (g == 0) {
+        const float cj = j < nrow ? cnr : 0.f;
+        sC[j] = cj;
+        put_c(sCh, j, cj);
+      }
     }
     __syncthreads();
 
@@ -430,11 +445,11 @@ __global__ __launch_bounds__(NT) void k_bwd_dkdv_mfma(const bf16_t* __restrict__
     }
     // A[i][j] = phi(Q_i).phi(K_j) and Bm[i][j] = g_i.V_j + c_i for query
     // tiles t >= w, masked i >= j, hi + lo
-    i16x4 ahi[4], alo[4], bhi[4], blo[4];
+    i16x4 ahi[4], alo[4], bm[4];
     if (CAUSAL) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        ahi[t] = alo[t] = bhi[t] = blo[t] = i16x4{0, 0, 0, 0};
+        ahi[t] = alo[t] = bm[t] = i16x4{0, 0, 0, 0};
         if (t >= w) {
           f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -449,7 +464,7 @@ __global__ __launch_bounds__(NT) void k_bwd_dkdv_mfma(const bf16_t* __restrict__
             b[u] = keep ? b[u] + sC[16 * t + 4 * g + u] : 0.f;
           }
           split(a, ahi[t], alo[t]);
-          split(b, bhi[t], blo[t]);
+          bm[t] = pack4(b);
         }
       }
     }
@@ -477,8 +492,7 @@ __global__ __launch_bounds__(NT) void k_bwd_dkdv_mfma(const bf16_t* __restrict__
             ov = mfma(ag, cat(ahi[2 * tp], ahi[2 * tp + 1]), ov);
             ov = mfma(ag, cat(alo[2 * tp], alo[2 * tp + 1]), ov);
             const i16x8 aq = cat(lds_tr(sQf + ir * LD + 16 * n + cc), lds_tr(sQf + (ir + 16) * LD + 16 * n + cc));
-            ok = mfma(aq, cat(bhi[2 * tp], bhi[2 * tp + 1]), ok);
-            ok = mfma(aq, cat(blo[2 * tp], blo[2 * tp + 1]), ok);
+            ok = mfma(aq, cat(bm[2 * tp], bm[2 * tp + 1]), ok);
           }
         }
       }
@@ -488,13 +502,13 @@ __global__ __launch_bounds__(NT) void k_bwd_dkdv_mfma(const bf16_t* __restrict__
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           rv[u] = bf(ov[u]);
-          rk[u] = bf((ok[u] + sRv[16 * n + 4 * g + u]) * fminf(fb(kv[u]), 1.f));
+          rk[u] = bf((ok[u] + sRv[16 * n + 4 * g + u]) * __builtin_amdgcn_fmed3f(fb(kv[u]), 0.f, 1.f));
         }
         *reinterpret_cast<i16x4*>(dv + hoff + (c0 + j) * DIM + 16 * n + 4 * g) = rv;
         *reinterpret_cast<i16x4*>(dk + hoff + (c0 + j) * DIM + 16 * n + 4 * g) = rk;
       }
     }
-    if (CAUSAL) outer_update<DIM, true>(Racc, racc, sG, sQf, sC, w, g, li);
+    if (CAUSAL) outer_update<DIM, true>(Racc, racc, sG, sQf, sCh, w, g, li);
     __syncthreads();
     if (CAUSAL) write_xt<DIM>(sR, sRv, Racc, racc, w, g, li);
     --ci;
@@ -504,7 +518,12 @@ __global__ __launch_bounds__(NT) void k_bwd_dkdv_mfma(const bf16_t* __restrict__
 }
 
 size_t lds_bwd(int dim) {
-  return (4 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + (dim + T) * sizeof(float);
+  return (4 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + (dim + T) * sizeof(float) +
+         2 * T * sizeof(uint16_t);
+}
+size_t lds_dq(int dim) {
+  return (6 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + dim * sizeof(float) +
+         4 * T * sizeof(uint16_t);
 }
 
 #define LA_MLAUNCH(kernel, grid, lds, st, ...)                                                              \
@@ -523,7 +542,7 @@ hipError_t launch_bwd_dq_mfma(int causal, const SegGeom& g, const void* q, const
                               float* den_out, hipStream_t st) {
   const int64_t grid = g.BH * g.P;
 #define LA_DQ(D, C)                                                                                          \
-  LA_MLAUNCH((k_bwd_dq_mfma<D, C>), grid, lds_bwd(D), st, static_cast<const bf16_t*>(q),                    \
+  LA_MLAUNCH((k_bwd_dq_mfma<D, C>), grid, lds_dq(D), st, static_cast<const bf16_t*>(q),                    \
              static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), \
              carry_s, static_cast<bf16_t*>(dq), r_agg, c_out, den_out, g.N, g.P, g.seg_len)
   if (g.D == 64) {

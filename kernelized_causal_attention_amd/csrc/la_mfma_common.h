@@ -57,12 +57,20 @@ __device__ __forceinline__ short bf(float x) {
 }
 __device__ __forceinline__ float fb(short h) { return bf16_to_f32(static_cast<uint16_t>(h)); }
 
+// Two fp32 -> one packed pair of bf16 (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ int pack2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(int, __builtin_convertvector(v, bf16x2_t));
+}
+
 __device__ __forceinline__ i16x4 pack4(f32x4_t v) {
-  return __builtin_bit_cast(i16x4, __builtin_convertvector(v, bf16x4_t));
+  const i32x2 r = {pack2(v[0], v[1]), pack2(v[2], v[3])};
+  return __builtin_bit_cast(i16x4, r);
 }
 
 __device__ __forceinline__ i16x8 pack8(f32x8_t v) {
-  return __builtin_bit_cast(i16x8, __builtin_convertvector(v, bf16x8_t));
+  const i32x4 r = {pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+  return __builtin_bit_cast(i16x8, r);
 }
 
 __device__ __forceinline__ f32x8_t unpack8(i16x8 h) {
