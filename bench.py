@@ -3,7 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
 
 A step is one pass of the training hot path over one batch: la_forward
-(causal, keeping the row denominators) followed by la_backward, on the
+(causal, keeping the row denominators and the per-segment prefix states)
+followed by la_backward reading those states, on the
 bf16 workload B=8, H=16, N=8192, D=M=64 (Q, K, V ~ N(0,1)/sqrt(D), dout ~
 N(0,1), synthetic, drawn on the device, resident in HBM before timing).
 The timed region is exactly K steps between two synchronisations, timed with
@@ -113,10 +114,12 @@ def main():
     ws_b = torch.empty(max(1, la.workspace_bytes("backward", B, H, N, D, M, True, "bf16")), dtype=torch.uint8, device=dev)
     out = torch.empty((B, H, N, M), dtype=torch.bfloat16, device=dev)
     den = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    nsaved = la.saved_bytes(B, H, N, D, M, True, "bf16")
+    saved = torch.empty(nsaved, dtype=torch.uint8, device=dev) if nsaved else None
 
     def step():
-        la.forward(q, k, v, causal=True, out=out, den=den, return_den=True, workspace=ws_f)
-        return la.backward(q, k, v, out, g, den=den, causal=True, workspace=ws_b)
+        la.forward(q, k, v, causal=True, out=out, den=den, return_den=True, workspace=ws_f, saved=saved)
+        return la.backward(q, k, v, out, g, den=den, causal=True, workspace=ws_b, saved=saved)
 
     log(f"workload fwdbwd_bf16 B={B} H={H} N={N} D={D} M={M}; plan fwd {plan_f} bwd {plan_b}")
     for _ in range(args.warmup):

@@ -94,11 +94,24 @@ la_status la_forward(const void* q, const void* k, const void* v, void* out,
                      int causal, int dtype, float* den_out,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* As la_forward, with a tuning plan (NULL = automatic) and, when `saved` is
+ * not NULL, the prefix states it computes kept for la_backward_ex: fp32
+ * records of D*M + D floats (S row-major, then Z), the state entering each
+ * segment of the plan for causal != 0 ([B,H,segments], none when the plan
+ * has one segment), or the totals S_N, Z_N for causal == 0 ([B,H]).
+ * `saved_bytes` must be at least la_saved_bytes(); `saved` is 16-byte
+ * aligned and must not overlap any other argument. */
 la_status la_forward_ex(const void* q, const void* k, const void* v, void* out,
                         int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                         int causal, int dtype, float* den_out,
+                        float* saved, size_t saved_bytes,
                         void* workspace, size_t workspace_bytes, hipStream_t stream,
                         const la_plan* plan);
+
+/* Bytes of the `saved` record of la_forward_ex for these sizes and plan (0
+ * when there is nothing to keep: causal with a single segment). */
+size_t la_saved_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                      int causal, int dtype, const la_plan* plan);
 
 /* Backward of L = sum(dout * out) with respect to the RAW q, k, v.
  * Numerator terms: "Transformers are RNNs" walkthrough, section 3.1,
@@ -118,8 +131,16 @@ la_status la_backward(const void* q, const void* k, const void* v, const void* o
                       int causal, int dtype,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* As la_backward, with a tuning plan (NULL = automatic) and `saved`, the
+ * record la_forward_ex left for the same q, k, v, sizes, causal, dtype and
+ * plan, or NULL.  With it the prefix states S, Z are read instead of being
+ * recomputed (a pass over k and v and a scan fewer).  LA_ERR_INVALID if
+ * saved_bytes is short of la_saved_bytes() or the forward and backward
+ * plans cut the sequence differently (e.g. different kernels requested). */
 la_status la_backward_ex(const void* q, const void* k, const void* v, const void* out,
-                         const void* dout, const float* den, void* dq, void* dk, void* dv,
+                         const void* dout, const float* den,
+                         const float* saved, size_t saved_bytes,
+                         void* dq, void* dk, void* dv,
                          int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                          int causal, int dtype,
                          void* workspace, size_t workspace_bytes, hipStream_t stream,

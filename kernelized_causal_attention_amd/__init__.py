@@ -18,7 +18,7 @@ from . import _native
 from ._native import LinAttnError, la_plan  # noqa: F401
 
 __all__ = [
-    "forward", "backward", "decode_step", "prefix_state", "workspace_bytes", "resolve_plan",
+    "forward", "backward", "decode_step", "prefix_state", "workspace_bytes", "saved_bytes", "resolve_plan",
     "LinAttnError", "library_path", "version", "profile_enable", "profile_report",
 ]
 
@@ -119,12 +119,19 @@ def _workspace(nbytes: int, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
+def saved_bytes(B, H, N, D, M, causal=True, dtype="f32", plan=None) -> int:
+    dt = {"f32": _native.LA_F32, "bf16": _native.LA_BF16}[dtype]
+    return int(_native.load().la_saved_bytes(B, H, N, D, M, int(bool(causal)), dt, _plan_ref(_plan(plan))))
+
+
 def forward(q, k, v, causal: bool = True, return_den: bool = False, plan=None, stream=None,
-            out=None, den=None, workspace=None):
+            out=None, den=None, workspace=None, saved=None):
     """V' = phi(Q) S / phi(Q) Z (causal) or phi(Q)(phi(K)^T V) normalised.
 
     q, k: [B,H,N,D]; v: [B,H,N,M]; float32 or bfloat16 (all the same).
-    Returns out [B,H,N,M] (and den [B,H,N] fp32 when return_den).
+    Returns out [B,H,N,M] (and den [B,H,N] fp32 when return_den).  When
+    `saved` is a GPU tensor of at least saved_bytes(...) bytes, the prefix
+    states are also kept there for backward(saved=...).
     """
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -145,15 +152,19 @@ def forward(q, k, v, causal: bool = True, return_den: bool = False, plan=None, s
     need = int(lib.la_workspace_bytes_ex(_native.LA_OP_FORWARD, B, H, N, D, M, int(bool(causal)), dt, _plan_ref(p)))
     ws = workspace if workspace is not None else _workspace(need, q.device)
     wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    ssz = 0 if saved is None else _dev(saved, "saved").numel() * saved.element_size()
     _native.check(lib.la_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, D, M,
-                                    int(bool(causal)), dt, _ptr(den), _ptr(ws), wsz, _stream(stream),
-                                    _plan_ref(p)))
+                                    int(bool(causal)), dt, _ptr(den), _ptr(saved), ssz, _ptr(ws), wsz,
+                                    _stream(stream), _plan_ref(p)))
     return (out, den) if return_den else out
 
 
 def backward(q, k, v, out, dout, den=None, causal: bool = True, plan=None, stream=None,
-             workspace=None) -> Tuple:
-    """Gradients (dq, dk, dv) of sum(dout * out) w.r.t. the raw q, k, v."""
+             workspace=None, saved=None) -> Tuple:
+    """Gradients (dq, dk, dv) of sum(dout * out) w.r.t. the raw q, k, v.
+
+    `saved`: the tensor forward(saved=...) filled for these inputs and the
+    same plan; the prefix states are then read instead of recomputed."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
         _dev(t, n)
@@ -176,9 +187,11 @@ def backward(q, k, v, out, dout, den=None, causal: bool = True, plan=None, strea
     need = int(lib.la_workspace_bytes_ex(_native.LA_OP_BACKWARD, B, H, N, D, M, int(bool(causal)), dt, _plan_ref(p)))
     ws = workspace if workspace is not None else _workspace(need, q.device)
     wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    ssz = 0 if saved is None else _dev(saved, "saved").numel() * saved.element_size()
     _native.check(lib.la_backward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
-                                     _ptr(den), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, M,
-                                     int(bool(causal)), dt, _ptr(ws), wsz, _stream(stream), _plan_ref(p)))
+                                     _ptr(den), _ptr(saved), ssz, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                     B, H, N, D, M, int(bool(causal)), dt, _ptr(ws), wsz, _stream(stream),
+                                     _plan_ref(p)))
     return dq, dk, dv
 
 

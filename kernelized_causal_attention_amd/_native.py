@@ -22,7 +22,7 @@ EXPORTS = (
     "la_forward", "la_forward_ex", "la_backward", "la_backward_ex", "la_decode_step",
     "la_prefix_state", "la_workspace_bytes", "la_workspace_bytes_ex", "la_resolve_plan",
     "la_status_str", "la_last_error", "la_version", "la_profile_enable", "la_profile_report",
-    "la_profile_select",
+    "la_profile_select", "la_saved_bytes",
 )
 
 
@@ -61,9 +61,10 @@ def load() -> ctypes.CDLL:
     bwd = [vp, vp, vp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     sigs = {
         "la_forward": (fwd, i32),
-        "la_forward_ex": (fwd + [plan_p], i32),
+        "la_forward_ex": (fwd[:12] + [fp, sz] + fwd[12:] + [plan_p], i32),
         "la_backward": (bwd, i32),
-        "la_backward_ex": (bwd + [plan_p], i32),
+        "la_backward_ex": (bwd[:6] + [fp, sz] + bwd[6:] + [plan_p], i32),
+        "la_saved_bytes": ([i64, i64, i64, i64, i64, i32, i32, plan_p], sz),
         "la_decode_step": ([fp, fp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp], i32),
         "la_prefix_state": ([vp, vp, fp, fp, i64, i64, i64, i64, i64, i32, vp, sz, vp], i32),
         "la_workspace_bytes": ([i32, i64, i64, i64, i64, i64, i32, i32], sz),

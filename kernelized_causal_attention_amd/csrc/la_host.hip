@@ -20,7 +20,8 @@ int mfma_supported(int op, int64_t D, int64_t M, int dtype);
 hipError_t launch_forward_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
                                void* out, float* den_out, const float* carry, hipStream_t st);
 hipError_t launch_seg_state_mfma(const SegGeom& g, const void* k, const void* v, float* s_out,
-                                 int64_t s_stride, float* z_out, int64_t z_stride, hipStream_t st);
+                                 int64_t s_stride, float* z_out, int64_t z_stride, float* u_out, int64_t u_stride,
+                                 hipStream_t st);
 hipError_t launch_bwd_dq_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
                               const void* dout, const float* carry_s, void* dq, float* r_agg, float* c_out,
                               float* den_out, hipStream_t st);
@@ -178,7 +179,8 @@ struct WsLayout {
 WsLayout layout(int op, int64_t BH, int64_t N, int64_t D, int64_t M, int causal, const Plan& p) {
   WsLayout w;
   Carve c;
-  const size_t E = static_cast<size_t>(D * M + D);
+  const size_t E = static_cast<size_t>(la::state_elems(static_cast<int>(D), static_cast<int>(M)));
+  const size_t ER = static_cast<size_t>(la::suffix_elems(static_cast<int>(D), static_cast<int>(M)));
   const size_t recs = static_cast<size_t>(BH) * p.P * E;
   if (op == LA_OP_FORWARD) {
     if (causal) {
@@ -190,8 +192,8 @@ WsLayout layout(int op, int64_t BH, int64_t N, int64_t D, int64_t M, int causal,
   } else if (op == LA_OP_BACKWARD) {
     w.aggS = c.take(recs);
     w.totS = c.take(static_cast<size_t>(BH) * E);
-    w.aggR = c.take(recs);
-    w.totR = c.take(static_cast<size_t>(BH) * E);
+    w.aggR = c.take(static_cast<size_t>(BH) * p.P * ER);
+    w.totR = c.take(static_cast<size_t>(BH) * ER);
     w.den = c.take(static_cast<size_t>(BH) * N);
     if (p.kernel == LA_KERNEL_MFMA) w.cvec = c.take(static_cast<size_t>(BH) * N);
   } else if (op == LA_OP_PREFIX_STATE) {
@@ -202,6 +204,14 @@ WsLayout layout(int op, int64_t BH, int64_t N, int64_t D, int64_t M, int causal,
 }
 
 float* at(void* ws, size_t off) { return reinterpret_cast<float*>(static_cast<char*>(ws) + off); }
+
+// Prefix states a forward leaves for its backward: the state entering each
+// segment (causal; none with one segment) or the totals (non-causal).
+size_t saved_floats(int64_t BH, int64_t D, int64_t M, int causal, const Plan& p) {
+  const size_t E = static_cast<size_t>(la::state_elems(static_cast<int>(D), static_cast<int>(M)));
+  if (causal) return p.P > 1 ? static_cast<size_t>(BH) * p.P * E : 0;
+  return static_cast<size_t>(BH) * E;
+}
 
 }  // namespace
 
@@ -278,17 +288,20 @@ la::SegGeom geom(int64_t BH, int64_t N, int64_t D, int64_t M, const Plan& p, int
   return g;
 }
 
-// Segment aggregates of (S, Z) into ws records [BH][P][E].
+// Segment aggregates of (S, Z, U) into ws records [BH][P][E].
 hipError_t seg_state(int dtype, const Plan& p, const la::SegGeom& gbase, const void* k, const void* v,
                      float* recs, hipStream_t st) {
   const int64_t E = la::state_elems(gbase.D, gbase.M);
   const int64_t DM = static_cast<int64_t>(gbase.D) * gbase.M;
+  float* z = recs + DM;
+  float* u = z + gbase.D;
   if (p.kernel == LA_KERNEL_MFMA)
-    return timed("mfma.seg_state", st, [&] { return la::launch_seg_state_mfma(gbase, k, v, recs, E, recs + DM, E, st); });
+    return timed("mfma.seg_state", st,
+                 [&] { return la::launch_seg_state_mfma(gbase, k, v, recs, E, z, E, u, E, st); });
   la::SegGeom g = gbase;
   g.chunk = la::generic_chunk_for(g.D, g.M, 1);
   return timed("generic.seg_state", st,
-               [&] { return la::launch_seg_state_generic(dtype, g, k, v, recs, E, recs + DM, E, st); });
+               [&] { return la::launch_seg_state_generic(dtype, g, k, v, recs, E, z, E, u, E, st); });
 }
 
 hipError_t fwd_pass(int dtype, int causal, const Plan& p, const la::SegGeom& gbase, const void* q,
@@ -304,16 +317,21 @@ hipError_t fwd_pass(int dtype, int causal, const Plan& p, const la::SegGeom& gba
                [&] { return la::launch_forward_generic(dtype, causal, g, q, k, v, out, den_out, carry, st); });
 }
 
+// Exclusive scan of prefix-state records (S, Z, U; forward direction) or of
+// suffix records (R, r; reverse).  tot, when given, receives each head's
+// total as a record of the same kind; tot_s/tot_z split it (U dropped).
 hipError_t scan(float* agg, int64_t BH, int P, int D, int M, int reverse, float* tot_s, int64_t ts_stride,
-                float* tot_z, int64_t tz_stride, hipStream_t st) {
+                float* tot_z, int64_t tz_stride, float* tot_u, int64_t tu_stride, hipStream_t st) {
   return timed("seg_scan", st, [&] {
-    return la::launch_seg_scan(agg, BH, P, D, M, reverse, tot_s, ts_stride, tot_z, tz_stride, st);
+    return la::launch_seg_scan(agg, BH, P, D, M, reverse ? 0 : 1, reverse, tot_s, ts_stride, tot_z, tz_stride,
+                               tot_u, tu_stride, st);
   });
 }
 
 la_status do_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H, int64_t N,
-                     int64_t D, int64_t M, int causal, int dtype, float* den_out, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream, const la_plan* plan) {
+                     int64_t D, int64_t M, int causal, int dtype, float* den_out, float* saved,
+                     size_t saved_bytes, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                     const la_plan* plan) {
   la_status s = check_sizes(B, H, N, D, M, dtype);
   if (s != LA_OK) return s;
   causal = causal ? 1 : 0;
@@ -321,14 +339,20 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
       (s = check_ptr(out, "out", dtype)))
     return s;
   if (den_out && (reinterpret_cast<uintptr_t>(den_out) & 3)) return fail(LA_ERR_INVALID, "den_out misaligned");
+  if (saved && (reinterpret_cast<uintptr_t>(saved) & 15)) return fail(LA_ERR_INVALID, "saved must be 16-byte aligned");
   const int64_t BH = B * H;
   const size_t es = dtype_size(dtype);
-  const Span ins[] = {span("q", q, BH * N * D, es), span("k", k, BH * N * D, es), span("v", v, BH * N * M, es),
-                      span("workspace", workspace, workspace ? (int64_t)workspace_bytes : 0, 1)};
-  const Span outs[] = {span("out", out, BH * N * M, es), span("den_out", den_out, den_out ? BH * N : 0, 4)};
-  if ((s = check_disjoint(outs, 2, ins, 4))) return s;
   Plan p;
   if ((s = resolve(LA_OP_FORWARD, B, H, N, D, M, causal, dtype, plan, &p))) return s;
+  const size_t nsaved = saved_floats(BH, D, M, causal, p);
+  if (saved && saved_bytes < nsaved * sizeof(float))
+    return fail(LA_ERR_INVALID, "saved too small: %zu bytes given, %zu needed", saved_bytes, nsaved * sizeof(float));
+  float* sv = nsaved ? saved : nullptr;
+  const Span ins[] = {span("q", q, BH * N * D, es), span("k", k, BH * N * D, es), span("v", v, BH * N * M, es),
+                      span("workspace", workspace, workspace ? (int64_t)workspace_bytes : 0, 1)};
+  const Span outs[] = {span("out", out, BH * N * M, es), span("den_out", den_out, den_out ? BH * N : 0, 4),
+                       span("saved", sv, sv ? static_cast<int64_t>(nsaved) : 0, 4)};
+  if ((s = check_disjoint(outs, 3, ins, 4))) return s;
   const WsLayout w = layout(LA_OP_FORWARD, BH, N, D, M, causal, p);
   if (workspace_bytes < w.bytes)
     return fail(LA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, w.bytes);
@@ -341,27 +365,27 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
   if (causal) {
     const float* carry = nullptr;
     if (p.P > 1) {
-      float* agg = at(workspace, w.aggS);
+      float* agg = sv ? sv : at(workspace, w.aggS);
       if ((e = seg_state(dtype, p, g, k, v, agg, stream))) return dev(e, "segment state");
-      if ((e = scan(agg, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream)))
+      if ((e = scan(agg, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, nullptr, 0, stream)))
         return dev(e, "segment scan");
       carry = agg;
     }
     return dev(fwd_pass(dtype, 1, p, g, q, k, v, out, den_out, carry, stream), "forward");
   }
   float* agg = at(workspace, w.aggS);
-  float* tot = at(workspace, w.totS);
+  float* tot = sv ? sv : at(workspace, w.totS);
   const int64_t E = la::state_elems(g.D, g.M);
   if ((e = seg_state(dtype, p, g, k, v, agg, stream))) return dev(e, "segment state");
-  if ((e = scan(agg, BH, p.P, g.D, g.M, 0, tot, E, tot + D * M, E, stream)))
+  if ((e = scan(agg, BH, p.P, g.D, g.M, 0, tot, E, tot + D * M, E, tot + D * M + D, E, stream)))
     return dev(e, "segment scan");
   return dev(fwd_pass(dtype, 0, p, g, q, k, v, out, den_out, tot, stream), "forward");
 }
 
 la_status do_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                      const float* den, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
-                      int64_t D, int64_t M, int causal, int dtype, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream, const la_plan* plan) {
+                      const float* den, const float* saved, size_t saved_bytes, void* dq, void* dk, void* dv,
+                      int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal, int dtype,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream, const la_plan* plan) {
   la_status s = check_sizes(B, H, N, D, M, dtype);
   if (s != LA_OK) return s;
   causal = causal ? 1 : 0;
@@ -370,17 +394,32 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
       (s = check_ptr(dq, "dq", dtype)) || (s = check_ptr(dk, "dk", dtype)) || (s = check_ptr(dv, "dv", dtype)))
     return s;
   if (den && (reinterpret_cast<uintptr_t>(den) & 3)) return fail(LA_ERR_INVALID, "den misaligned");
+  if (saved && (reinterpret_cast<uintptr_t>(saved) & 15)) return fail(LA_ERR_INVALID, "saved must be 16-byte aligned");
   const int64_t BH = B * H;
   const size_t es = dtype_size(dtype);
+  Plan p;
+  if ((s = resolve(LA_OP_BACKWARD, B, H, N, D, M, causal, dtype, plan, &p))) return s;
+  const size_t nsaved = saved_floats(BH, D, M, causal, p);
+  if (saved) {
+    // the saved states are per segment of the forward's plan
+    Plan pf;
+    if ((s = resolve(LA_OP_FORWARD, B, H, N, D, M, causal, dtype, plan, &pf))) return s;
+    if (pf.P != p.P || pf.seg_len != p.seg_len)
+      return fail(LA_ERR_INVALID, "saved states are cut into %d segments of %d tokens, the backward into %d of %d",
+                  pf.P, pf.seg_len, p.P, p.seg_len);
+    if (saved_bytes < nsaved * sizeof(float))
+      return fail(LA_ERR_INVALID, "saved too small: %zu bytes given, %zu needed", saved_bytes,
+                  nsaved * sizeof(float));
+  }
+  const float* sv = nsaved ? saved : nullptr;
   const Span ins[] = {span("q", q, BH * N * D, es),       span("k", k, BH * N * D, es),
                       span("v", v, BH * N * M, es),       span("out", out, BH * N * M, es),
                       span("dout", dout, BH * N * M, es), span("den", den, den ? BH * N : 0, 4),
+                      span("saved", sv, sv ? static_cast<int64_t>(nsaved) : 0, 4),
                       span("workspace", workspace, workspace ? (int64_t)workspace_bytes : 0, 1)};
   const Span outs[] = {span("dq", dq, BH * N * D, es), span("dk", dk, BH * N * D, es),
                        span("dv", dv, BH * N * M, es)};
-  if ((s = check_disjoint(outs, 3, ins, 7))) return s;
-  Plan p;
-  if ((s = resolve(LA_OP_BACKWARD, B, H, N, D, M, causal, dtype, plan, &p))) return s;
+  if ((s = check_disjoint(outs, 3, ins, 8))) return s;
   const WsLayout w = layout(LA_OP_BACKWARD, BH, N, D, M, causal, p);
   if (workspace_bytes < w.bytes)
     return fail(LA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, w.bytes);
@@ -389,22 +428,25 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
 
   const la::SegGeom g = geom(BH, N, D, M, p, p.chunk);
   const int64_t E = la::state_elems(g.D, g.M);
+  const int64_t ER = la::suffix_elems(g.D, g.M);
   float* aggS = at(workspace, w.aggS);
   float* totS = at(workspace, w.totS);
   float* aggR = at(workspace, w.aggR);
   float* totR = at(workspace, w.totR);
   hipError_t e;
   const float* carry_s = nullptr;
-  if (causal) {
+  if (saved) {
+    carry_s = sv;  // the forward's scanned states (null: one causal segment)
+  } else if (causal) {
     if (p.P > 1) {
       if ((e = seg_state(dtype, p, g, k, v, aggS, stream))) return dev(e, "segment state");
-      if ((e = scan(aggS, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream)))
+      if ((e = scan(aggS, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, nullptr, 0, stream)))
         return dev(e, "segment scan");
       carry_s = aggS;
     }
   } else {
     if ((e = seg_state(dtype, p, g, k, v, aggS, stream))) return dev(e, "segment state");
-    if ((e = scan(aggS, BH, p.P, g.D, g.M, 0, totS, E, totS + D * M, E, stream)))
+    if ((e = scan(aggS, BH, p.P, g.D, g.M, 0, totS, E, totS + D * M, E, totS + D * M + D, E, stream)))
       return dev(e, "segment scan");
     carry_s = totS;
   }
@@ -434,12 +476,12 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
   const float* carry_r = nullptr;
   if (causal) {
     if (p.P > 1) {
-      if ((e = scan(aggR, BH, p.P, g.D, g.M, 1, nullptr, 0, nullptr, 0, stream)))
+      if ((e = scan(aggR, BH, p.P, g.D, g.M, 1, nullptr, 0, nullptr, 0, nullptr, 0, stream)))
         return dev(e, "suffix scan");
       carry_r = aggR;
     }
   } else {
-    if ((e = scan(aggR, BH, p.P, g.D, g.M, 1, totR, E, totR + D * M, E, stream)))
+    if ((e = scan(aggR, BH, p.P, g.D, g.M, 1, totR, ER, totR + D * M, ER, nullptr, 0, stream)))
       return dev(e, "suffix scan");
     carry_r = totR;
   }
@@ -462,33 +504,33 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
 LA_API la_status la_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
                             int64_t N, int64_t D, int64_t M, int causal, int dtype, float* den_out,
                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return do_forward(q, k, v, out, B, H, N, D, M, causal, dtype, den_out, workspace, workspace_bytes, stream,
-                    nullptr);
+  return do_forward(q, k, v, out, B, H, N, D, M, causal, dtype, den_out, nullptr, 0, workspace, workspace_bytes,
+                    stream, nullptr);
 }
 
 LA_API la_status la_forward_ex(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
                                int64_t N, int64_t D, int64_t M, int causal, int dtype, float* den_out,
-                               void* workspace, size_t workspace_bytes, hipStream_t stream,
-                               const la_plan* plan) {
-  return do_forward(q, k, v, out, B, H, N, D, M, causal, dtype, den_out, workspace, workspace_bytes, stream,
-                    plan);
+                               float* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream, const la_plan* plan) {
+  return do_forward(q, k, v, out, B, H, N, D, M, causal, dtype, den_out, saved, saved_bytes, workspace,
+                    workspace_bytes, stream, plan);
 }
 
 LA_API la_status la_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
                              const float* den, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
                              int64_t D, int64_t M, int causal, int dtype, void* workspace,
                              size_t workspace_bytes, hipStream_t stream) {
-  return do_backward(q, k, v, out, dout, den, dq, dk, dv, B, H, N, D, M, causal, dtype, workspace,
+  return do_backward(q, k, v, out, dout, den, nullptr, 0, dq, dk, dv, B, H, N, D, M, causal, dtype, workspace,
                      workspace_bytes, stream, nullptr);
 }
 
 LA_API la_status la_backward_ex(const void* q, const void* k, const void* v, const void* out,
-                                const void* dout, const float* den, void* dq, void* dk, void* dv, int64_t B,
-                                int64_t H, int64_t N, int64_t D, int64_t M, int causal, int dtype,
-                                void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                const la_plan* plan) {
-  return do_backward(q, k, v, out, dout, den, dq, dk, dv, B, H, N, D, M, causal, dtype, workspace,
-                     workspace_bytes, stream, plan);
+                                const void* dout, const float* den, const float* saved, size_t saved_bytes,
+                                void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t D,
+                                int64_t M, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream, const la_plan* plan) {
+  return do_backward(q, k, v, out, dout, den, saved, saved_bytes, dq, dk, dv, B, H, N, D, M, causal, dtype,
+                     workspace, workspace_bytes, stream, plan);
 }
 
 LA_API la_status la_decode_step(float* S, float* Z, const void* q, const void* k, const void* v, void* out,
@@ -533,17 +575,17 @@ LA_API la_status la_prefix_state(const void* k, const void* v, float* S, float* 
   hipError_t e;
   if (p.P == 1) {
     if (p.kernel == LA_KERNEL_MFMA)
-      return dev(timed("mfma.seg_state", stream, [&] { return la::launch_seg_state_mfma(g, k, v, S, D * M, Z, D, stream); }),
+      return dev(timed("mfma.seg_state", stream, [&] { return la::launch_seg_state_mfma(g, k, v, S, D * M, Z, D, nullptr, 0, stream); }),
                  "prefix state");
     la::SegGeom gs = g;
     gs.chunk = la::generic_chunk_for(g.D, g.M, 1);
     return dev(timed("generic.seg_state", stream,
-                     [&] { return la::launch_seg_state_generic(dtype, gs, k, v, S, D * M, Z, D, stream); }),
+                     [&] { return la::launch_seg_state_generic(dtype, gs, k, v, S, D * M, Z, D, nullptr, 0, stream); }),
                "prefix state");
   }
   float* agg = at(workspace, w.aggS);
   if ((e = seg_state(dtype, p, g, k, v, agg, stream))) return dev(e, "prefix state");
-  return dev(scan(agg, BH, p.P, g.D, g.M, 0, S, D * M, Z, D, stream), "prefix scan");
+  return dev(scan(agg, BH, p.P, g.D, g.M, 0, S, D * M, Z, D, nullptr, 0, stream), "prefix scan");
 }
 
 LA_API size_t la_workspace_bytes_ex(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
@@ -554,6 +596,14 @@ LA_API size_t la_workspace_bytes_ex(int op, int64_t B, int64_t H, int64_t N, int
   if (resolve(op, B, H, N, D, M, causal ? 1 : 0, dtype, op == LA_OP_PREFIX_STATE ? nullptr : plan, &p) != LA_OK)
     return 0;
   return layout(op, B * H, N, D, M, causal ? 1 : 0, p).bytes;
+}
+
+LA_API size_t la_saved_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal, int dtype,
+                             const la_plan* plan) {
+  if (check_sizes(B, H, N, D, M, dtype) != LA_OK) return 0;
+  Plan p;
+  if (resolve(LA_OP_FORWARD, B, H, N, D, M, causal ? 1 : 0, dtype, plan, &p) != LA_OK) return 0;
+  return saved_floats(B * H, D, M, causal ? 1 : 0, p) * sizeof(float);
 }
 
 LA_API size_t la_workspace_bytes(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,

@@ -123,7 +123,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_fwd_mfma(const bf16_t
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
   const int64_t r1 = min(N, r0 + seg_len);
-  constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;
+  constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + 2 * DIM;  // S, Z, U record
   const float* cs = carry ? (CAUSAL ? carry + (bh * P + seg) * E : carry + bh * E) : nullptr;
   const bf16_t* qh = q + bh * N * DIM;
   const bf16_t* kh = k + bh * N * DIM;
@@ -251,17 +251,25 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_fwd_mfma(const bf16_t
   }
 }
 
-// Segment aggregates dS = phi(K)^T V, dZ = colsum phi(K) over one segment.
+// Segment aggregates dS = phi(K)^T V, dZ = colsum phi(K) and (when u_out is
+// not null) dU = colsum V over one segment.  phi(K) = 1 + E(K) is split so
+// that the records are as exact as fp32 allows: the MFMAs sum E(K)^T V and
+// colsum E(K) with E = elu carried as bf16 (a rounding relative to E, not to
+// phi ~ 1), and the ones part enters in fp32 as dS = 1 dU^T + E^T V,
+// dZ = count + colsum E.  The backward splits the records again and relies
+// on that precision.
 template <int DIM>
 __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_seg_state_mfma(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                                        float* __restrict__ s_out, int64_t s_stride,
-                                                       float* __restrict__ z_out, int64_t z_stride, int64_t N,
+                                                       float* __restrict__ z_out, int64_t z_stride,
+                                                       float* __restrict__ u_out, int64_t u_stride, int64_t N,
                                                        int P, int seg_len) {
   using G = Geo<DIM>;
   constexpr int LD = G::LD, NTL = G::NTL, PC = G::PC, DT = G::DT;
   extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t* sKf = smem;
-  uint16_t* sV = sKf + T * LD;
+  uint16_t* sKe = smem;
+  uint16_t* sV = sKe + T * LD;
+  float* sRow = reinterpret_cast<float*>(sV + T * LD);  // row sums (unused here)
   // w is made wave-uniform (an SGPR) so that branches on it are scalar: an
   // MFMA under an EXEC-masked branch still writes every lane.
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
@@ -274,14 +282,19 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_seg_state_mfma(const 
   const bf16_t* vh = v + bh * N * DIM;
   f32x4_t Sacc[DT][NTL];
   f32x4_t zacc[DT];
+  f32x4_t uacc[NTL];  // column sums of V: lane holds U[16n + li]
   init_state<DIM>(Sacc, zacc, nullptr, w, g, li);
+#pragma unroll
+  for (int n = 0; n < NTL; ++n) uacc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const short one = 0x3f80;  // bf16 1.0
+  const i16x8 ones = {one, one, one, one, one, one, one, one};
   int64_t c0 = r0;
   int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
   i32x4 kraw[PC], vraw[PC];
   load_tile<DIM>(kraw, kh, c0, nrow);
   load_tile<DIM>(vraw, vh, c0, nrow);
   while (c0 < r1) {
-    store_tile<DIM, true>(sKf, kraw, nrow);
+    store_tile_elu<DIM>(sKe, kraw, nrow, sRow);
     store_tile<DIM, false>(sV, vraw, nrow);
     __syncthreads();
     const int64_t c1 = c0 + T;
@@ -290,12 +303,22 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_seg_state_mfma(const 
       load_tile<DIM>(kraw, kh, c1, nrow1);
       load_tile<DIM>(vraw, vh, c1, nrow1);
     }
-    state_update<DIM>(Sacc, zacc, sKf, sV, w, g, li);
+    state_update<DIM>(Sacc, zacc, sKe, sV, w, g, li);
+#pragma unroll
+    for (int s = 0; s < T / 32; ++s) {
+      const int jr = 32 * s + 8 * g + li / 4;
+      const int cc = 4 * (li % 4);
+#pragma unroll
+      for (int n = 0; n < NTL; ++n)
+        uacc[n] = mfma(ones, cat(lds_tr(sV + jr * LD + 16 * n + cc), lds_tr(sV + (jr + 4) * LD + 16 * n + cc)),
+                       uacc[n]);
+    }
     __syncthreads();
     c0 = c1;
     nrow = nrow1;
   }
   const int64_t rec = bh * P + seg;
+  const float count = static_cast<float>(r1 - r0);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     const int d0 = 16 * (w * DT + dt);
@@ -303,14 +326,18 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_seg_state_mfma(const 
     for (int u = 0; u < 4; ++u) {
       const int d = d0 + 4 * g + u;
 #pragma unroll
-      for (int n = 0; n < NTL; ++n) s_out[rec * s_stride + d * DIM + 16 * n + li] = Sacc[dt][n][u];
-      if (li == 0) z_out[rec * z_stride + d] = zacc[dt][u];
+      for (int n = 0; n < NTL; ++n) s_out[rec * s_stride + d * DIM + 16 * n + li] = Sacc[dt][n][u] + uacc[n][0];
+      if (li == 0) z_out[rec * z_stride + d] = zacc[dt][u] + count;
     }
+  }
+  if (u_out && w == 0 && g == 0) {
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) u_out[rec * u_stride + 16 * n + li] = uacc[n][0];
   }
 }
 
 size_t lds_fwd(int dim) { return (2 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + dim * sizeof(float); }
-size_t lds_seg(int dim) { return 2 * T * (dim + 8) * sizeof(uint16_t); }
+size_t lds_seg(int dim) { return 2 * T * (dim + 8) * sizeof(uint16_t) + T * sizeof(float); }
 
 #define LA_MLAUNCH(kernel, grid, lds, st, ...)                                                          \
   do {                                                                                                  \
@@ -347,14 +374,16 @@ hipError_t launch_forward_mfma(int causal, const SegGeom& g, const void* q, cons
 }
 
 hipError_t launch_seg_state_mfma(const SegGeom& g, const void* k, const void* v, float* s_out, int64_t s_stride,
-                                 float* z_out, int64_t z_stride, hipStream_t st) {
+                                 float* z_out, int64_t z_stride, float* u_out, int64_t u_stride, hipStream_t st) {
   const int64_t grid = g.BH * g.P;
   const bf16_t* K = static_cast<const bf16_t*>(k);
   const bf16_t* V = static_cast<const bf16_t*>(v);
   if (g.D == 64)
-    LA_MLAUNCH((k_seg_state_mfma<64>), grid, lds_seg(64), st, K, V, s_out, s_stride, z_out, z_stride, g.N, g.P, g.seg_len);
+    LA_MLAUNCH((k_seg_state_mfma<64>), grid, lds_seg(64), st, K, V, s_out, s_stride, z_out, z_stride, u_out,
+               u_stride, g.N, g.P, g.seg_len);
   if (g.D == 128)
-    LA_MLAUNCH((k_seg_state_mfma<128>), grid, lds_seg(128), st, K, V, s_out, s_stride, z_out, z_stride, g.N, g.P, g.seg_len);
+    LA_MLAUNCH((k_seg_state_mfma<128>), grid, lds_seg(128), st, K, V, s_out, s_stride, z_out, z_stride, u_out,
+               u_stride, g.N, g.P, g.seg_len);
   return hipErrorNotSupported;
 }
 

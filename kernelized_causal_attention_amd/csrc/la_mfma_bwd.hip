@@ -140,20 +140,119 @@ __device__ __forceinline__ void outer_update(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>
   }
 }
 
+// Variants of the helpers above for the forward sweep, which writes
+// phi = 1 + E (E = elu) and keeps the prefix state split as
+//   S = 1 U^T + S',  Z = n 1 + Z',  U = sum_j V_j,  S' = sum_j E(K_j) V_j^T,
+//   Z' = sum_j E(K_j)
+// (n tokens so far).  y holds, for the wave's column tiles, a vector over m
+// in the X^T accumulator layout: lane holds y[16mt + 4g + u].
+template <int DIM>
+__device__ __forceinline__ void init_split(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&x)[Geo<DIM>::DT],
+                                           f32x4_t (&y)[Geo<DIM>::DT], const float* __restrict__ rec, float n0,
+                                           int w, int g, int li) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int a = 0; a < G::DT; ++a) {
+    const int mt = w * G::DT + a;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) y[a][u] = rec ? rec[DIM * DIM + DIM + 16 * mt + 4 * g + u] : 0.f;
+#pragma unroll
+    for (int n = 0; n < G::NTL; ++n)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) X[a][n][u] = rec ? rec[(16 * n + li) * DIM + 16 * mt + 4 * g + u] - y[a][u] : 0.f;
+    const float z = rec ? rec[DIM * DIM + 16 * mt + li] - n0 : 0.f;
+    x[a] = f32x4_t{z, z, z, z};
+  }
+}
+
+template <int DIM>
+__device__ __forceinline__ void write_y(float* sy, const f32x4_t (&y)[Geo<DIM>::DT], int w, int g, int li) {
+#pragma unroll
+  for (int a = 0; a < Geo<DIM>::DT; ++a)
+    if (li == 0) *reinterpret_cast<f32x4_t*>(sy + 16 * (w * Geo<DIM>::DT + a) + 4 * g) = y[a];
+}
+
+// outer_update plus y[m] += sum_j A[j][m] (column sums of the A side).
+template <int DIM, bool WC>
+__device__ __forceinline__ void outer_update_y(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&x)[Geo<DIM>::DT],
+                                               f32x4_t (&y)[Geo<DIM>::DT], const uint16_t* sA, const uint16_t* sB,
+                                               const uint16_t* sCh, int w, int g, int li) {
+  using G = Geo<DIM>;
+  const short one = 0x3f80;
+  const i16x8 ones = {one, one, one, one, one, one, one, one};
+#pragma unroll
+  for (int s = 0; s < T / 32; ++s) {
+    const int jr = 32 * s + 8 * g + li / 4;
+    const int cc = 4 * (li % 4);
+    i16x8 chi = ones, clo = ones;
+    if (WC) {
+      chi = lds8(sCh + 32 * s + 8 * g);
+      clo = lds8(sCh + T + 32 * s + 8 * g);
+    }
+    i16x8 aop[G::DT];
+#pragma unroll
+    for (int a = 0; a < G::DT; ++a) {
+      const int mt = w * G::DT + a;
+      aop[a] = cat(lds_tr(sA + jr * G::LD + 16 * mt + cc), lds_tr(sA + (jr + 4) * G::LD + 16 * mt + cc));
+      y[a] = mfma(aop[a], ones, y[a]);
+    }
+#pragma unroll
+    for (int n = 0; n < G::NTL; ++n) {
+      const i16x8 b = cat(lds_tr(sB + jr * G::LD + 16 * n + cc), lds_tr(sB + (jr + 4) * G::LD + 16 * n + cc));
+#pragma unroll
+      for (int a = 0; a < G::DT; ++a) X[a][n] = mfma(aop[a], b, X[a][n]);
+      if (n / G::DT == w) {
+        const int b_ = n % G::DT;
+        x[b_] = mfma(chi, b, x[b_]);
+        if (WC) x[b_] = mfma(clo, b, x[b_]);
+      }
+    }
+  }
+}
+
+// Suffix record (R, r) from R = R' + 1 G^T, r = r' + C 1.
+template <int DIM>
+__device__ __forceinline__ void store_r(float* __restrict__ rec, const f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL],
+                                        const f32x4_t (&x)[Geo<DIM>::DT], const f32x4_t (&y)[Geo<DIM>::DT], float C,
+                                        int w, int g, int li) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int a = 0; a < G::DT; ++a) {
+    const int mt = w * G::DT + a;
+#pragma unroll
+    for (int n = 0; n < G::NTL; ++n)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rec[(16 * n + li) * DIM + 16 * mt + 4 * g + u] = X[a][n][u] + y[a][u];
+    if (g == 0) rec[DIM * DIM + 16 * mt + li] = x[a][0] + C;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Forward sweep: dq, the per-row c and den for the reverse sweep, and the
 // segment's (R, r) aggregate when r_agg != null.
 //
-// grad phi(Q_i) = sum_j phi(K_j) g_i.(V_j - out_i) is a near-cancellation of
-// S g_i against c_i Z, so c_i must come from the same rounded g_i the MFMAs
-// use and from the same S.  Here g_i = bf16(dout_i / den_i) with den_i
-// recomputed in fp32, and
-//   g_i . num_i = phi(Q_i) . (S g_i) + sum_{j<=i in chunk} A_ij (g_i . V_j),
-// whose two pieces are exactly the MFMA products the chunk needs anyway
-// (the inter term S g_i of grad phi(Q_i), and the tiles g_i . V_j of B), so
-// c_i = -(g_i . num_i) / den_i costs no extra pass over num.  The query,
-// g and c tiles are double-buffered so that the (R, r) aggregate of a chunk
-// can be summed after the chunk's last barrier: two barriers per chunk.
+// grad phi(Q_i) = sum_{j<=i} phi(K_j) b_ij with b_ij = g_i.V_j + c_i, and
+// sum_{j<=i} A_ij b_ij = 0 exactly (that is what out_i is): the gradient is
+// what is left after the ones direction of phi(K) ~ 1 cancels, a few times
+// smaller than its terms.  Rounding phi(K), S or b to bf16 puts an error
+// into that ones direction which the cancellation then amplifies, so this
+// kernel writes phi(K_j) = 1 + E_j with E = elu carried as bf16 and every
+// ones-direction term in fp32:
+//   grad phi(Q_i) = beta_i 1 + S' g_i + c_i Z' + sum_{j<=i in chunk} E_j b_ij
+//   beta_i = sum_{j<=i} b_ij = g_i.U + n_i c_i + sum_{j in chunk} g_i.V_j
+// with (S', Z', U) the state before the chunk (split as above), n_i the
+// number of keys j <= i, and g_i = bf16(dout_i / den_i).  The same split of
+// phi(Q_i) = 1 + E_i gives the scores and the denominator in fp32 from
+// bf16 E's:
+//   A_ij = D + sum_d E_i + sum_d E_j + E_i.E_j
+//   den_i = sum_{j in chunk} A_ij + n0 (D + sum_d E_i) + sum_d (1 + E_i) Z'
+// and c_i = -(g_i . num_i) / den_i from the same pieces:
+//   g_i . num_i = sum_j A_ij (g_i.V_j) + (D + sum_d E_i)(g_i.U)
+//                 + sum_d (1 + E_i)[d] (S' g_i)[d].
+// The query, g and c tiles are double-buffered so that the (R, r) aggregate
+// of a chunk is summed after the chunk's last barrier: two barriers per
+// chunk.  R and r are accumulated the same way, R = 1 G^T + sum_i E_i g_i^T
+// and r = C 1 + sum_i c_i E_i with G = sum_i g_i, C = sum_i c_i.
 // ---------------------------------------------------------------------------
 template <int DIM, bool CAUSAL>
 __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -164,13 +263,17 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
   using G = Geo<DIM>;
   constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
   extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t* sKf = smem;
-  uint16_t* sV = sKf + T * LD;
-  uint16_t* sQf2 = sV + T * LD;     // two buffers
-  uint16_t* sG2 = sQf2 + 2 * T * LD;  // two buffers
-  uint16_t* sS = sG2 + 2 * T * LD;
-  float* sZ = reinterpret_cast<float*>(sS + DIM * LD);
-  uint16_t* sCh2 = reinterpret_cast<uint16_t*>(sZ + DIM);  // two buffers of 2*T
+  uint16_t* sKe = smem;                // E(K) chunk tile
+  uint16_t* sV = sKe + T * LD;
+  uint16_t* sQe2 = sV + T * LD;        // E(Q), two buffers
+  uint16_t* sG2 = sQe2 + 2 * T * LD;   // g, two buffers
+  uint16_t* sS = sG2 + 2 * T * LD;     // bf16 S'
+  float* sZ = reinterpret_cast<float*>(sS + DIM * LD);  // Z'
+  float* sU = sZ + DIM;                // U
+  float* sSk = sU + DIM;               // sum_d E(K_j) per key
+  float* sSq = sSk + T;                // sum_d E(Q_i) per query
+  float* sRed = sSq + T;               // 4 floats: per-wave sums of c
+  uint16_t* sCh2 = reinterpret_cast<uint16_t*>(sRed + 4);  // c hi/lo, two buffers of 2T
 
   // w is made wave-uniform (an SGPR) so that branches on it are scalar: an
   // MFMA under an EXEC-masked branch still writes every lane.
@@ -180,19 +283,24 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
   const int64_t r1 = min(N, r0 + seg_len);
-  constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;
-  const float* cs = carry_s ? (CAUSAL ? carry_s + (bh * P + seg) * E : carry_s + bh * E) : nullptr;
+  constexpr int64_t ES = static_cast<int64_t>(DIM) * DIM + 2 * DIM;  // S, Z, U record
+  constexpr int64_t ER = static_cast<int64_t>(DIM) * DIM + DIM;      // R, r record
+  const float* cs = carry_s ? (CAUSAL ? carry_s + (bh * P + seg) * ES : carry_s + bh * ES) : nullptr;
   const int64_t hoff = bh * N * DIM;
   float* ch = c_out + bh * N;
   float* dh = den_out + bh * N;
   const bool want_r = r_agg != nullptr;
   const int i = 16 * w + li;
   const int cc = 4 * (li % 4);
+  // tokens before the current chunk (the carried state's count)
+  float n0 = CAUSAL ? static_cast<float>(r0) : static_cast<float>(N);
 
-  f32x4_t Sacc[DT][NTL], zacc[DT], Racc[DT][NTL], racc[DT];
-  init_xt<DIM>(Sacc, zacc, cs, w, g, li);
-  init_xt<DIM>(Racc, racc, nullptr, w, g, li);
+  f32x4_t Sacc[DT][NTL], zacc[DT], uacc[DT], Racc[DT][NTL], racc[DT], gacc[DT];
+  init_split<DIM>(Sacc, zacc, uacc, cs, n0, w, g, li);
+  init_split<DIM>(Racc, racc, gacc, nullptr, 0.f, w, g, li);
   write_xt<DIM>(sS, sZ, Sacc, zacc, w, g, li);
+  write_y<DIM>(sU, uacc, w, g, li);
+  float csum = 0.f;
 
   int64_t c0 = r0;
   int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
@@ -209,14 +317,14 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
 
   int buf = 0;
   while (c0 < r1) {
-    uint16_t* sQf = sQf2 + buf * T * LD;
+    uint16_t* sQe = sQe2 + buf * T * LD;
     uint16_t* sG = sG2 + buf * T * LD;
     uint16_t* sCh = sCh2 + buf * 2 * T;
     if (CAUSAL) {
-      store_tile<DIM, true>(sKf, kraw, nrow);
+      store_tile_elu<DIM>(sKe, kraw, nrow, sSk);
       store_tile<DIM, false>(sV, vraw, nrow);
     }
-    store_tile<DIM, true>(sQf, qraw, nrow);
+    store_tile_elu<DIM>(sQe, qraw, nrow, sSq);
     __syncthreads();
     const bool valid = i < nrow;
     i32x4 gcur[KS];
@@ -226,10 +334,11 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
     const int nrow1 = c1 < r1 ? static_cast<int>(min(static_cast<int64_t>(T), r1 - c1)) : 0;
     if (nrow1 > 0) fetch(c1, nrow1);
 
-    // --- den_i: intra-chunk scores A_ij (fp32, masked j <= i) and phi(Q_i).Z
+    const float dq_i = static_cast<float>(DIM) + sSq[i];  // sum_d phi(Q_i)
+    // --- scores A^T[j][i] = D + sq_i + sk_j + E_j.E_i (masked j <= i), fp32
     i16x8 qf[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = lds8(sQf + i * LD + 8 * g + 32 * s);
+    for (int s = 0; s < KS; ++s) qf[s] = lds8(sQe + i * LD + 8 * g + 32 * s);
     f32x4_t at[4];
     float rs = 0.f;
     if (CAUSAL) {
@@ -238,33 +347,42 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
         at[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (t <= w) {
 #pragma unroll
-          for (int s = 0; s < KS; ++s) at[t] = mfma(lds8(sKf + (16 * t + li) * LD + 8 * g + 32 * s), qf[s], at[t]);
+          for (int s = 0; s < KS; ++s) at[t] = mfma(lds8(sKe + (16 * t + li) * LD + 8 * g + 32 * s), qf[s], at[t]);
+          const f32x4_t sk = *reinterpret_cast<const f32x4_t*>(sSk + 16 * t + 4 * g);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            if (t == w && 4 * g + u > li) at[t][u] = 0.f;
+            at[t][u] = (t == w && 4 * g + u > li) ? 0.f : at[t][u] + dq_i + sk[u];
             rs += at[t][u];
           }
         }
       }
     }
+    // --- den_i = sum_j A_ij + n0 (D + sq_i) + sum_d (1 + E_i)[d] Z'[d]
     float di = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const f32x8_t qv = unpack8(qf[s]);
       const f32x8_t zv = *reinterpret_cast<const f32x8_t*>(sZ + 8 * g + 32 * s);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) di += qv[e] * zv[e];
+      for (int e = 0; e < 8; ++e) di += (1.f + qv[e]) * zv[e];
     }
-    const float den = shfl_sum_groups(rs + di);
+    const float den = shfl_sum_groups(rs + di) + n0 * dq_i;
     const float inv = valid ? 1.f / den : 0.f;
-    // --- g_i = bf16(dout_i / den_i): registers (B operand) and sG (for R)
+    // --- g_i = bf16(dout_i / den_i): registers (B operand) and sG (for R);
+    // g_i . U in fp32
     i16x8 gq[KS];
+    float gu = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       gq[s] = pack8(unpack8(__builtin_bit_cast(i16x8, gcur[s])) * inv);
       *reinterpret_cast<i16x8*>(sG + i * LD + 8 * g + 32 * s) = gq[s];
+      const f32x8_t gv = unpack8(gq[s]);
+      const f32x8_t uv = *reinterpret_cast<const f32x8_t*>(sU + 8 * g + 32 * s);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gu += gv[e] * uv[e];
     }
-    // --- S g_i  (dQ^T[d][i] inter term) and Bv^T[j][i] = g_i . V_j
+    gu = shfl_sum_groups(gu);
+    // --- S' g_i  (dQ^T[d][i] inter term) and Bv^T[j][i] = g_i . V_j
     f32x4_t o[NTL];
 #pragma unroll
     for (int n = 0; n < NTL; ++n) {
@@ -280,26 +398,35 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
         if (t <= w) {
 #pragma unroll
           for (int s = 0; s < KS; ++s) bv[t] = mfma(lds8(sV + (16 * t + li) * LD + 8 * g + 32 * s), gq[s], bv[t]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (t == w && 4 * g + u > li) bv[t][u] = 0.f;
         }
       }
     }
-    // --- c_i = -(phi(Q_i).(S g_i) + sum_j A_ij (g_i . V_j)) / den_i
-    float dot = 0.f;
+    // --- c_i = -(sum_j A_ij bv_ij + (D + sq_i) g.U + sum_d (1 + E_i) (S'g)) / den_i
+    float dot = 0.f, sbv = 0.f;
 #pragma unroll
     for (int n = 0; n < NTL; ++n) {
-      const f32x4_t qd = unpack4(*reinterpret_cast<const i16x4*>(sQf + i * LD + 16 * n + 4 * g));
+      const f32x4_t qd = unpack4(*reinterpret_cast<const i16x4*>(sQe + i * LD + 16 * n + 4 * g));
 #pragma unroll
-      for (int u = 0; u < 4; ++u) dot += qd[u] * o[n][u];
+      for (int u = 0; u < 4; ++u) dot += (1.f + qd[u]) * o[n][u];
     }
     if (CAUSAL) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         if (t <= w) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) dot += at[t][u] * bv[t][u];
+          for (int u = 0; u < 4; ++u) {
+            dot += at[t][u] * bv[t][u];
+            sbv += bv[t][u];
+          }
         }
     }
-    const float c = -shfl_sum_groups(dot) * inv;
+    const float c = -(shfl_sum_groups(dot) + dq_i * gu) * inv;
+    // beta_i = g.U + n_i c_i + sum_{j in chunk} g.V_j, n_i = n0 + (i + 1)
+    const float beta = gu + c * (n0 + (CAUSAL ? static_cast<float>(i + 1) : 0.f)) + shfl_sum_groups(sbv);
+    csum += c;
     if (g == 0) {
       put_c(sCh, i, c);
       if (valid) {
@@ -307,8 +434,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
         dh[c0 + i] = den;
       }
     }
-    // --- B^T = Bv^T + c_i (centred: g_i.(V_j - out_i)), masked j <= i,
-    // then grad phi(Q)^T += phi(K)^T B^T, + c_i Z[d], times phi'(q)
+    // --- grad phi(Q)^T[d][i] = beta + S'g + c Z'[d] + E(K)^T b, times phi'(q)
     if (CAUSAL) {
       i16x4 bt[4];
 #pragma unroll
@@ -325,7 +451,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
         for (int tp = 0; tp < 2; ++tp) {
           if (2 * tp <= w) {
             const int jr = 32 * tp + 4 * g + li / 4;
-            const i16x8 a = cat(lds_tr(sKf + jr * LD + 16 * n + cc), lds_tr(sKf + (jr + 16) * LD + 16 * n + cc));
+            const i16x8 a = cat(lds_tr(sKe + jr * LD + 16 * n + cc), lds_tr(sKe + (jr + 16) * LD + 16 * n + cc));
             o[n] = mfma(a, cat(bt[2 * tp], bt[2 * tp + 1]), o[n]);
           }
         }
@@ -335,23 +461,37 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
 #pragma unroll
       for (int n = 0; n < NTL; ++n) {
         const f32x4_t z = *reinterpret_cast<const f32x4_t*>(sZ + 16 * n + 4 * g);
-        const f32x4_t qd = unpack4(*reinterpret_cast<const i16x4*>(sQf + i * LD + 16 * n + 4 * g));
+        const f32x4_t qd = unpack4(*reinterpret_cast<const i16x4*>(sQe + i * LD + 16 * n + 4 * g));
         f32x4_t r;
+        // phi'(q) = min(phi(q), 1) = 1 + min(E, 0)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) r[u] = (o[n][u] + c * z[u]) * __builtin_amdgcn_fmed3f(qd[u], 0.f, 1.f);
+        for (int u = 0; u < 4; ++u) r[u] = (beta + o[n][u] + c * z[u]) * (1.f + fminf(qd[u], 0.f));
         *reinterpret_cast<i16x4*>(dq + hoff + (c0 + i) * DIM + 16 * n + 4 * g) = pack4(r);
       }
     }
-    if (CAUSAL) outer_update<DIM, false>(Sacc, zacc, sV, sKf, nullptr, w, g, li);
+    if (CAUSAL) outer_update_y<DIM, false>(Sacc, zacc, uacc, sV, sKe, nullptr, w, g, li);
     __syncthreads();
-    // this chunk's g, phi(Q) and c rows are complete: sum its (R, r) part
-    if (want_r) outer_update<DIM, true>(Racc, racc, sG, sQf, sCh, w, g, li);
-    if (CAUSAL) write_xt<DIM>(sS, sZ, Sacc, zacc, w, g, li);
+    // this chunk's g, E(Q) and c rows are complete: sum its (R, r) part
+    if (want_r) outer_update_y<DIM, true>(Racc, racc, gacc, sG, sQe, sCh, w, g, li);
+    if (CAUSAL) {
+      write_xt<DIM>(sS, sZ, Sacc, zacc, w, g, li);
+      write_y<DIM>(sU, uacc, w, g, li);
+    }
+    if (CAUSAL) n0 += static_cast<float>(nrow);
     c0 = c1;
     nrow = nrow1;
     buf ^= 1;
   }
-  if (want_r) store_xt<DIM>(r_agg + (bh * P + seg) * E, Racc, racc, w, g, li);
+  if (want_r) {
+    // C = sum of c over the segment's rows (csum is the same in all four
+    // 16-lane groups of a wave: sum over li, then over the waves)
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) csum += __shfl_xor(csum, off, 64);
+    if (l == 0) sRed[w] = csum;
+    __syncthreads();
+    const float C = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+    store_r<DIM>(r_agg + (bh * P + seg) * ER, Racc, racc, gacc, C, w, g, li);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -522,7 +662,7 @@ size_t lds_bwd(int dim) {
          2 * T * sizeof(uint16_t);
 }
 size_t lds_dq(int dim) {
-  return (6 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + dim * sizeof(float) +
+  return (6 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + (2 * dim + 2 * T + 4) * sizeof(float) +
          4 * T * sizeof(uint16_t);
 }
 

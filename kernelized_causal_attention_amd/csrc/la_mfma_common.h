@@ -85,6 +85,10 @@ __device__ __forceinline__ f32x4_t unpack4(i16x4 h) {
 // below the bf16 rounding that follows).
 __device__ __forceinline__ float phi_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
+// elu(x) = phi(x) - 1 (alpha = 1), for kernels that carry phi = 1 + elu with
+// the ones part in fp32 and only the small elu part as a bf16 operand.
+__device__ __forceinline__ float elu_fast(float x) { return x > 0.f ? x : __expf(x) - 1.f; }
+
 // phi applied to 8 bf16 values (raw 16-byte vector), result rounded to bf16.
 __device__ __forceinline__ i16x8 phi8(i32x4 raw) {
   f32x8_t x = unpack8(__builtin_bit_cast(i16x8, raw));
@@ -139,6 +143,35 @@ __device__ __forceinline__ void store_tile(uint16_t* lds, const i32x4 (&raw)[Geo
     i16x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
     if (j < nrow) val = PHI ? phi8(raw[r]) : __builtin_bit_cast(i16x8, raw[r]);
     *reinterpret_cast<i16x8*>(lds + j * G::LD + c8 * 8) = val;
+  }
+}
+
+// Registers -> LDS as bf16 elu(x), and each row's sum of the rounded values
+// (fp32) into rowsum[j]; rows past nrow are zero.  The ROW8 pieces of a row
+// sit in ROW8 consecutive lanes, so the row sum is a butterfly over them.
+template <int DIM>
+__device__ __forceinline__ void store_tile_elu(uint16_t* lds, const i32x4 (&raw)[Geo<DIM>::PC], int nrow,
+                                               float* rowsum) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int r = 0; r < G::PC; ++r) {
+    const int p = threadIdx.x + kNT * r;
+    const int j = p / G::ROW8, c8 = p % G::ROW8;
+    i16x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
+    float sum = 0.f;
+    if (j < nrow) {
+      f32x8_t x = unpack8(__builtin_bit_cast(i16x8, raw[r]));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = elu_fast(x[e]);
+      val = pack8(x);
+      const f32x8_t xr = unpack8(val);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum += xr[e];
+    }
+    *reinterpret_cast<i16x8*>(lds + j * G::LD + c8 * 8) = val;
+#pragma unroll
+    for (int off = 1; off < G::ROW8; off <<= 1) sum += __shfl_xor(sum, off, 64);
+    if (c8 == 0) rowsum[j] = sum;
   }
 }
 

@@ -151,3 +151,46 @@ def test_binding_requires_built_library_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_native, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         _native.load()
+
+
+def test_saved_bytes(lib):
+    # causal over one segment keeps nothing; several segments keep one record
+    # (S, Z, U: D*M + D + M floats) per segment and head; non-causal keeps the
+    # totals.
+    one = _native.la_plan(0, 1, 1)
+    four = _native.la_plan(0, 4, 1)
+    E = 16 * 8 + 16 + 8
+    assert lib.la_saved_bytes(1, 1, 256, 16, 8, 1, 0, ctypes.byref(one)) == 0
+    assert lib.la_saved_bytes(2, 3, 256, 16, 8, 1, 0, ctypes.byref(four)) == 2 * 3 * 4 * E * 4
+    assert lib.la_saved_bytes(2, 3, 256, 16, 8, 0, 0, ctypes.byref(four)) == 2 * 3 * E * 4
+    assert lib.la_saved_bytes(1, 1, 256, 300, 8, 1, 0, None) == 0  # unsupported -> 0
+
+
+@nogpu
+def test_saved_state_arguments_are_validated(lib):
+    E = 0x50000000
+    F = 0x60000000
+    G = 0x70000000
+    H_ = 0x80000000
+    S = 0xA0000000
+    W = 0xB0000000
+    four = _native.la_plan(0, 4, 1)
+    need = lib.la_saved_bytes(1, 1, 256, 4, 4, 1, 0, ctypes.byref(four))
+    fws = lib.la_workspace_bytes_ex(0, 1, 1, 256, 4, 4, 1, 0, ctypes.byref(four))
+
+    def fwd(saved=S, ssz=need, plan=four):
+        return lib.la_forward_ex(A, Bp, C, Dp, 1, 1, 256, 4, 4, 1, 0, None, saved, ssz, W, fws, None,
+                                 ctypes.byref(plan))
+
+    assert fwd(saved=S + 4) == 1 and b"16-byte" in lib.la_last_error()
+    assert fwd(ssz=need - 4) == 1 and b"saved too small" in lib.la_last_error()
+    assert fwd(saved=C) == 1 and b"saved overlaps input v" in lib.la_last_error()
+
+    bws = lib.la_workspace_bytes_ex(1, 1, 1, 256, 4, 4, 1, 0, ctypes.byref(four))
+
+    def bwd(saved=S, ssz=need, plan=four, dq=F):
+        return lib.la_backward_ex(A, Bp, C, Dp, E, None, saved, ssz, dq, G, H_, 1, 1, 256, 4, 4, 1, 0, W, bws,
+                                  None, ctypes.byref(plan))
+
+    assert bwd(ssz=need - 4) == 1 and b"saved too small" in lib.la_last_error()
+    assert bwd(dq=S) == 1 and b"overlaps input saved" in lib.la_last_error()

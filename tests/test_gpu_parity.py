@@ -81,14 +81,15 @@ def check_backward(tq, tk, tv, tg, causal, dtype, plan=None, heads=None, use_den
     hi = [h for _, h in sel]
     q64, k64, v64, g64 = (f64(t[bi, hi]) for t in (tq, tk, tv, tg))
     rq, rk, rv, _, _ = oracle.backward(q64, k64, v64, g64, causal)
-    # rel-L2, with the denominator floored at 1e-2 * ||dv||: at N = 1 (and
-    # other degenerate inputs) dq and dk are exactly zero, so a plain relative
-    # error would divide rounding noise by zero; dv never degenerates (its
-    # rows sum to the rows of dout).
-    floor = 1e-2 * np.linalg.norm(rv.ravel())
+    # Plain rel-L2 per gradient.  Only where the exact gradient vanishes
+    # identically (every row sees one key, N = 1: out_i = V_i, so dq = dk = 0)
+    # is the error taken against 1e-2 * ||dv|| instead, since a relative error
+    # would divide rounding noise by zero; dv never vanishes.
+    scale = np.linalg.norm(rv.ravel())
 
     def err(x, r):
-        return float(np.linalg.norm((x - r).ravel()) / max(np.linalg.norm(r.ravel()), floor))
+        nr = np.linalg.norm(r.ravel())
+        return float(np.linalg.norm((x - r).ravel()) / (nr if nr > 1e-9 * scale else 1e-2 * scale))
 
     errs = {n: err(f64(t[bi, hi]), r) for n, t, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv))}
     say(f"backward causal={causal} dtype={dtype} shape={tuple(tq.shape)}+{tv.shape[-1]} den={use_den} "
@@ -96,15 +97,14 @@ def check_backward(tq, tk, tv, tg, causal, dtype, plan=None, heads=None, use_den
     for n, e in errs.items():
         assert e < TOL[dtype], (n, e)
     if dtype == "bf16" and floor_factor:
-        # The bf16 kernels feed phi(Q), phi(K) (~1 + x, so rounding to bf16
-        # keeps few bits of x) and g = dout/den to the MFMAs as bf16; an exact
-        # emulation of that arithmetic gives gradient errors of a few times
-        # the rounding of the gradients themselves.  Bar: floor_factor x that
-        # rounding error, or 1e-2 (half the tolerance) where it is tiny.
+        # The bf16 kernels feed elu(Q), elu(K) (or phi), V and g = dout/den to
+        # the MFMAs as bf16; an emulation of that arithmetic gives gradient
+        # errors of about twice the rounding of the gradients themselves.
+        # Bar: floor_factor x that rounding error (5e-3 where it vanishes).
         for n, r in (("dq", rq), ("dk", rk), ("dv", rv)):
             e_round = err(f64(torch.from_numpy(r).float().to(torch.bfloat16)), r)
             say(f"  {n}: bf16 rounding floor {e_round:.2e}")
-            assert errs[n] < max(floor_factor * e_round, 1e-2), (n, errs[n], e_round)
+            assert errs[n] < max(floor_factor * e_round, 5e-3), (n, errs[n], e_round)
     return dq, dk, dv
 
 
@@ -314,15 +314,52 @@ def test_mfma_backward(shape, causal, segments):
     B, H, N, D = shape
     tq, tk, tv, tg = host_case(B, H, N, D, D, "bf16", seed=N + D + segments + 1, scale=1.0 / np.sqrt(D))
     say(f"mfma backward {shape} causal={causal} segments={segments}")
-    check_backward(tq, tk, tv, tg, causal, "bf16", plan=dict(kernel=2, segments=segments), floor_factor=6.0)
+    check_backward(tq, tk, tv, tg, causal, "bf16", plan=dict(kernel=2, segments=segments), floor_factor=4.0)
 
 
 @pytest.mark.parametrize("D", [64, 128])
 def test_mfma_backward_unscaled_and_recomputed_den(D):
     tq, tk, tv, tg = host_case(1, 2, 700, D, D, "bf16", seed=D + 5, scale=1.0)
-    check_backward(tq, tk, tv, tg, True, "bf16", plan=dict(kernel=2), floor_factor=6.0)
+    check_backward(tq, tk, tv, tg, True, "bf16", plan=dict(kernel=2), floor_factor=4.0)
     check_backward(tq, tk, tv, tg, True, "bf16", plan=dict(kernel=2), use_den=False)
-    check_backward(tq, tk, tv, tg, False, "bf16", plan=dict(kernel=2), floor_factor=6.0)
+    check_backward(tq, tk, tv, tg, False, "bf16", plan=dict(kernel=2), floor_factor=4.0)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("kernel,dtype,D", [(1, "f32", 32), (2, "bf16", 64), (2, "bf16", 128)])
+@pytest.mark.parametrize("segments", [1, 3])
+def test_backward_reads_saved_states(causal, kernel, dtype, D, segments):
+    # The forward keeps its scanned prefix states; the backward that reads
+    # them must give bit for bit what it gives when it recomputes them (same
+    # kernels, same inputs, fixed reduction order), and match the oracle.
+    B, H, N = 2, 2, 700
+    tq, tk, tv, tg = host_case(B, H, N, D, D, dtype, seed=D + segments + 17, scale=1.0 / np.sqrt(D))
+    plan = dict(kernel=kernel, segments=segments)
+    nb = la.saved_bytes(B, H, N, D, D, causal, dtype, plan)
+    if causal and segments == 1:
+        assert nb == 0
+    saved = torch.empty(nb, dtype=torch.uint8, device=DEV) if nb else None
+    out, den = la.forward(tq, tk, tv, causal=causal, return_den=True, plan=plan, saved=saved)
+    g_saved = la.backward(tq, tk, tv, out, tg, den=den, causal=causal, plan=plan, saved=saved)
+    g_plain = la.backward(tq, tk, tv, out, tg, den=den, causal=causal, plan=plan)
+    torch.cuda.synchronize()
+    for a, b in zip(g_saved, g_plain):
+        assert torch.equal(a, b)
+    rq, rk, rv, _, _ = oracle.backward(f64(tq), f64(tk), f64(tv), f64(tg), causal)
+    for n, x, r in (("dq", g_saved[0], rq), ("dk", g_saved[1], rk), ("dv", g_saved[2], rv)):
+        e = rel_l2(f64(x), r)
+        say(f"saved states causal={causal} {dtype} D={D} segments={segments} {n}={e:.2e}")
+        assert e < TOL[dtype], (n, e)
+
+
+def test_saved_states_rejected_when_too_small():
+    tq, tk, tv, tg = host_case(1, 1, 256, 64, 64, "bf16", seed=3, scale=0.125)
+    plan = dict(kernel=2, segments=4)
+    nb = la.saved_bytes(1, 1, 256, 64, 64, True, "bf16", plan)
+    assert nb == 4 * (64 * 64 + 64 + 64) * 4
+    small = torch.empty(nb - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(la.LinAttnError, match="saved too small"):
+        la.forward(tq, tk, tv, plan=plan, saved=small)
 
 
 def test_mfma_matches_generic_bf16():
