@@ -270,9 +270,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
   uint16_t* sS = sG2 + 2 * T * LD;     // bf16 S'
   float* sZ = reinterpret_cast<float*>(sS + DIM * LD);  // Z'
   float* sU = sZ + DIM;                // U
-  float* sSk = sU + DIM;               // sum_d E(K_j) per key
-  float* sSq = sSk + T;                // sum_d E(Q_i) per query
-  float* sRed = sSq + T;               // 4 floats: per-wave sums of c
+  float* sRed = sU + DIM;              // 4 floats: per-wave sums of c
   uint16_t* sCh2 = reinterpret_cast<uint16_t*>(sRed + 4);  // c hi/lo, two buffers of 2T
 
   // w is made wave-uniform (an SGPR) so that branches on it are scalar: an
@@ -287,13 +285,26 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
   constexpr int64_t ER = static_cast<int64_t>(DIM) * DIM + DIM;      // R, r record
   const float* cs = carry_s ? (CAUSAL ? carry_s + (bh * P + seg) * ES : carry_s + bh * ES) : nullptr;
   const int64_t hoff = bh * N * DIM;
+  const int64_t hbytes = N * DIM * 2;
+  const rsrc_t rq = make_rsrc(q + hoff, hbytes), rk = make_rsrc(k + hoff, hbytes), rv = make_rsrc(v + hoff, hbytes),
+               rg = make_rsrc(dout + hoff, hbytes), rdq = make_rsrc(dq + hoff, hbytes);
   float* ch = c_out + bh * N;
   float* dh = den_out + bh * N;
   const bool want_r = r_agg != nullptr;
   const int i = 16 * w + li;
   const int cc = 4 * (li % 4);
+  const short one = 0x3f80;  // bf16 1.0
+  const i16x8 ones = {one, one, one, one, one, one, one, one};
   // tokens before the current chunk (the carried state's count)
   float n0 = CAUSAL ? static_cast<float>(r0) : static_cast<float>(N);
+  // causal mask of key j = 16t + 4g + u against query i = 16w + li, as 0 / 1
+  // factors (kept in VGPRs: as per-(t, u) lane masks they would not fit in
+  // the scalar registers)
+  f32x4_t mt[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mt[t][u] = (t < w || (t == w && 4 * g + u <= li)) ? 1.f : 0.f;
 
   f32x4_t Sacc[DT][NTL], zacc[DT], uacc[DT], Racc[DT][NTL], racc[DT], gacc[DT];
   init_split<DIM>(Sacc, zacc, uacc, cs, n0, w, g, li);
@@ -305,15 +316,15 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
   int64_t c0 = r0;
   int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
   i32x4 kraw[PC], vraw[PC], qraw[PC], graw[KS];
-  auto fetch = [&](int64_t cc0, int nr) {
+  auto fetch = [&](int soff) {
     if (CAUSAL) {
-      load_tile<DIM>(kraw, k + hoff, cc0, nr);
-      load_tile<DIM>(vraw, v + hoff, cc0, nr);
+      bload_tile<DIM>(kraw, rk, soff);
+      bload_tile<DIM>(vraw, rv, soff);
     }
-    load_tile<DIM>(qraw, q + hoff, cc0, nr);
-    load_q<DIM>(graw, dout + hoff, cc0, nr, i, g);
+    bload_tile<DIM>(qraw, rq, soff);
+    bload_q<DIM>(graw, rg, soff, i, g);
   };
-  fetch(c0, nrow);
+  fetch(static_cast<int>(c0 * DIM * 2));
 
   int buf = 0;
   while (c0 < r1) {
@@ -321,10 +332,10 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
     uint16_t* sG = sG2 + buf * T * LD;
     uint16_t* sCh = sCh2 + buf * 2 * T;
     if (CAUSAL) {
-      store_tile_elu<DIM>(sKe, kraw, nrow, sSk);
-      store_tile<DIM, false>(sV, vraw, nrow);
+      store_tile_e<DIM>(sKe, kraw);
+      store_tile_v<DIM>(sV, vraw);
     }
-    store_tile_elu<DIM>(sQe, qraw, nrow, sSq);
+    store_tile_e<DIM>(sQe, qraw);
     __syncthreads();
     const bool valid = i < nrow;
     i32x4 gcur[KS];
@@ -332,13 +343,24 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
     for (int s = 0; s < KS; ++s) gcur[s] = graw[s];
     const int64_t c1 = c0 + T;
     const int nrow1 = c1 < r1 ? static_cast<int>(min(static_cast<int64_t>(T), r1 - c1)) : 0;
-    if (nrow1 > 0) fetch(c1, nrow1);
+    if (nrow1 > 0) fetch(static_cast<int>(c1 * DIM * 2));
+    const int soff = static_cast<int>(c0 * DIM * 2);
 
-    const float dq_i = static_cast<float>(DIM) + sSq[i];  // sum_d phi(Q_i)
-    // --- scores A^T[j][i] = D + sq_i + sk_j + E_j.E_i (masked j <= i), fp32
+    // E(Q_i) in the MFMA B layout (features 8g + 32s + e) and, unpacked once,
+    // in the accumulator layout (features 16n + 4g + u)
     i16x8 qf[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = lds8(sQe + i * LD + 8 * g + 32 * s);
+    f32x4_t qd[NTL];
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) qd[n] = unpack4(*reinterpret_cast<const i16x4*>(sQe + i * LD + 16 * n + 4 * g));
+    // sum_d phi(Q_i) = D + sum_d E(Q_i), through the MFMA against ones
+    f32x4_t sq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) sq = mfma(ones, qf[s], sq);
+    const float dq_i = static_cast<float>(DIM) + sq[0];
+    // --- scores A^T[j][i] = (D + sq_i) + sk_j + E_j.E_i, masked j <= i: the
+    // key row sums sk_j come from the same MFMA chain against ones
     f32x4_t at[4];
     float rs = 0.f;
     if (CAUSAL) {
@@ -346,30 +368,31 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
       for (int t = 0; t < 4; ++t) {
         at[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (t <= w) {
+          at[t] = f32x4_t{dq_i, dq_i, dq_i, dq_i};
 #pragma unroll
-          for (int s = 0; s < KS; ++s) at[t] = mfma(lds8(sKe + (16 * t + li) * LD + 8 * g + 32 * s), qf[s], at[t]);
-          const f32x4_t sk = *reinterpret_cast<const f32x4_t*>(sSk + 16 * t + 4 * g);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            at[t][u] = (t == w && 4 * g + u > li) ? 0.f : at[t][u] + dq_i + sk[u];
-            rs += at[t][u];
+          for (int s = 0; s < KS; ++s) {
+            const i16x8 ka = lds8(sKe + (16 * t + li) * LD + 8 * g + 32 * s);
+            at[t] = mfma(ka, ones, at[t]);
+            at[t] = mfma(ka, qf[s], at[t]);
           }
+          at[t] *= mt[t];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) rs += at[t][u];
         }
       }
     }
     // --- den_i = sum_j A_ij + n0 (D + sq_i) + sum_d (1 + E_i)[d] Z'[d]
     float di = 0.f;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const f32x8_t qv = unpack8(qf[s]);
-      const f32x8_t zv = *reinterpret_cast<const f32x8_t*>(sZ + 8 * g + 32 * s);
+    for (int n = 0; n < NTL; ++n) {
+      const f32x4_t z = *reinterpret_cast<const f32x4_t*>(sZ + 16 * n + 4 * g);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) di += (1.f + qv[e]) * zv[e];
+      for (int u = 0; u < 4; ++u) di += (1.f + qd[n][u]) * z[u];
     }
     const float den = shfl_sum_groups(rs + di) + n0 * dq_i;
     const float inv = valid ? 1.f / den : 0.f;
     // --- g_i = bf16(dout_i / den_i): registers (B operand) and sG (for R);
-    // g_i . U in fp32
+    // g_i . U in fp32 from the rounded g
     i16x8 gq[KS];
     float gu = 0.f;
 #pragma unroll
@@ -398,28 +421,23 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
         if (t <= w) {
 #pragma unroll
           for (int s = 0; s < KS; ++s) bv[t] = mfma(lds8(sV + (16 * t + li) * LD + 8 * g + 32 * s), gq[s], bv[t]);
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (t == w && 4 * g + u > li) bv[t][u] = 0.f;
         }
       }
     }
     // --- c_i = -(sum_j A_ij bv_ij + (D + sq_i) g.U + sum_d (1 + E_i) (S'g)) / den_i
     float dot = 0.f, sbv = 0.f;
 #pragma unroll
-    for (int n = 0; n < NTL; ++n) {
-      const f32x4_t qd = unpack4(*reinterpret_cast<const i16x4*>(sQe + i * LD + 16 * n + 4 * g));
+    for (int n = 0; n < NTL; ++n)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) dot += (1.f + qd[u]) * o[n][u];
-    }
+      for (int u = 0; u < 4; ++u) dot += (1.f + qd[n][u]) * o[n][u];
     if (CAUSAL) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         if (t <= w) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            dot += at[t][u] * bv[t][u];
-            sbv += bv[t][u];
+            dot += at[t][u] * bv[t][u];  // at is masked
+            sbv += mt[t][u] * bv[t][u];
           }
         }
     }
@@ -438,13 +456,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
     if (CAUSAL) {
       i16x4 bt[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        f32x4_t b = bv[t] + c;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (t > w || (t == w && 4 * g + u > li)) b[u] = 0.f;
-        bt[t] = pack4(b);
-      }
+      for (int t = 0; t < 4; ++t) bt[t] = pack4((bv[t] + c) * mt[t]);
 #pragma unroll
       for (int n = 0; n < NTL; ++n) {
 #pragma unroll
@@ -457,17 +469,14 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
         }
       }
     }
-    if (valid) {
 #pragma unroll
-      for (int n = 0; n < NTL; ++n) {
-        const f32x4_t z = *reinterpret_cast<const f32x4_t*>(sZ + 16 * n + 4 * g);
-        const f32x4_t qd = unpack4(*reinterpret_cast<const i16x4*>(sQe + i * LD + 16 * n + 4 * g));
-        f32x4_t r;
-        // phi'(q) = min(phi(q), 1) = 1 + min(E, 0)
+    for (int n = 0; n < NTL; ++n) {
+      const f32x4_t z = *reinterpret_cast<const f32x4_t*>(sZ + 16 * n + 4 * g);
+      f32x4_t r;
+      // phi'(q) = min(phi(q), 1) = 1 + min(E, 0)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) r[u] = (beta + o[n][u] + c * z[u]) * (1.f + fminf(qd[u], 0.f));
-        *reinterpret_cast<i16x4*>(dq + hoff + (c0 + i) * DIM + 16 * n + 4 * g) = pack4(r);
-      }
+      for (int u = 0; u < 4; ++u) r[u] = (beta + o[n][u] + c * z[u]) * (1.f + fminf(qd[n][u], 0.f));
+      bstore8(rdq, pack4(r), (i * DIM + 16 * n + 4 * g) * 2, soff);
     }
     if (CAUSAL) outer_update_y<DIM, false>(Sacc, zacc, uacc, sV, sKe, nullptr, w, g, li);
     __syncthreads();
@@ -662,7 +671,7 @@ size_t lds_bwd(int dim) {
          2 * T * sizeof(uint16_t);
 }
 size_t lds_dq(int dim) {
-  return (6 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + (2 * dim + 2 * T + 4) * sizeof(float) +
+  return (6 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + (2 * dim + 4) * sizeof(float) +
          4 * T * sizeof(uint16_t);
 }
 

@@ -106,6 +106,30 @@ __device__ __forceinline__ float shfl_sum_groups(float x) {
 
 __device__ __forceinline__ i32x4 gload16(const bf16_t* p) { return *reinterpret_cast<const i32x4*>(p); }
 
+// Raw buffer access (stride 0) over one head's rows: loads past the range
+// return zero and stores past it are dropped, so a partial last chunk needs
+// no row guards, and addresses are 32-bit offsets (a per-lane constant plus a
+// wave-uniform chunk offset) instead of 64-bit pointers.  The host keeps every
+// head under 2^31 bytes.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer descriptor word 3 (32-bit data format)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           kRsrcWord3);
+}
+__device__ __forceinline__ i32x4 bload16(rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ void bstore8(rsrc_t r, i16x4 v, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, soff, 0);
+}
+__device__ __forceinline__ void bstore4(rsrc_t r, float v, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, voff, soff, 0);
+}
+
 constexpr int kNT = 256;  // threads per workgroup (4 wave64s)
 constexpr int kT = 64;    // tokens per chunk
 
@@ -172,6 +196,49 @@ __device__ __forceinline__ void store_tile_elu(uint16_t* lds, const i32x4 (&raw)
 #pragma unroll
     for (int off = 1; off < G::ROW8; off <<= 1) sum += __shfl_xor(sum, off, 64);
     if (c8 == 0) rowsum[j] = sum;
+  }
+}
+
+// Buffer versions of load_tile / load_q: `soff` is the chunk's first row in
+// bytes; rows past the head's end read as zero.
+template <int DIM>
+__device__ __forceinline__ void bload_tile(i32x4 (&raw)[Geo<DIM>::PC], rsrc_t src, int soff) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int r = 0; r < G::PC; ++r) {
+    const int p = threadIdx.x + kNT * r;
+    raw[r] = bload16(src, ((p / G::ROW8) * DIM + (p % G::ROW8) * 8) * 2, soff);
+  }
+}
+template <int DIM>
+__device__ __forceinline__ void bload_q(i32x4 (&raw)[Geo<DIM>::KS], rsrc_t src, int soff, int i, int g) {
+#pragma unroll
+  for (int s = 0; s < Geo<DIM>::KS; ++s) raw[s] = bload16(src, (i * DIM + 8 * g + 32 * s) * 2, soff);
+}
+
+// Registers -> LDS as bf16 elu(x) for tiles whose rows past the end were
+// loaded as zero (elu(0) = 0, so no row guard is needed).
+template <int DIM>
+__device__ __forceinline__ void store_tile_e(uint16_t* lds, const i32x4 (&raw)[Geo<DIM>::PC]) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int r = 0; r < G::PC; ++r) {
+    const int p = threadIdx.x + kNT * r;
+    f32x8_t x = unpack8(__builtin_bit_cast(i16x8, raw[r]));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = elu_fast(x[e]);
+    *reinterpret_cast<i16x8*>(lds + (p / G::ROW8) * G::LD + (p % G::ROW8) * 8) = pack8(x);
+  }
+}
+
+// Registers -> LDS unchanged (rows past the end already zero).
+template <int DIM>
+__device__ __forceinline__ void store_tile_v(uint16_t* lds, const i32x4 (&raw)[Geo<DIM>::PC]) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int r = 0; r < G::PC; ++r) {
+    const int p = threadIdx.x + kNT * r;
+    *reinterpret_cast<i16x8*>(lds + (p / G::ROW8) * G::LD + (p % G::ROW8) * 8) = __builtin_bit_cast(i16x8, raw[r]);
   }
 }
 
