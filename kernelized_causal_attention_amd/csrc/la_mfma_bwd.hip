@@ -390,7 +390,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
       for (int u = 0; u < 4; ++u) di += (1.f + qd[n][u]) * z[u];
     }
     const float den = shfl_sum_groups(rs + di) + n0 * dq_i;
-    const float inv = valid ? 1.f / den : 0.f;
+    const float inv = valid ? __builtin_amdgcn_rcpf(den) : 0.f;  // the reverse sweep forms the same g
     // --- g_i = bf16(dout_i / den_i): registers (B operand) and sG (for R);
     // g_i . U in fp32 from the rounded g
     i16x8 gq[KS];
@@ -533,12 +533,23 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
   const int64_t r1 = min(N, r0 + seg_len);
-  constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;
+  constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;  // R, r record
   const float* cr = carry_r ? (CAUSAL ? carry_r + (bh * P + seg) * E : carry_r + bh * E) : nullptr;
   const int64_t hoff = bh * N * DIM;
+  const int64_t hbytes = N * DIM * 2;
+  const rsrc_t rq = make_rsrc(q + hoff, hbytes), rk = make_rsrc(k + hoff, hbytes), rv = make_rsrc(v + hoff, hbytes),
+               rg = make_rsrc(dout + hoff, hbytes), rdk = make_rsrc(dk + hoff, hbytes),
+               rdv = make_rsrc(dv + hoff, hbytes);
   const float* denh = den_in + bh * N;
   const float* chh = c_in + bh * N;
   const int j = 16 * w + li;  // this lane's key row (outputs); also its query row for g, c
+  // causal mask of query i = 16t + 4g + u against key j = 16w + li (i >= j)
+  // as 0 / 1 factors
+  f32x4_t mt[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mt[t][u] = (t > w || (t == w && 4 * g + u >= li)) ? 1.f : 0.f;
 
   f32x4_t Racc[DT][NTL], racc[DT];
   init_xt<DIM>(Racc, racc, cr, w, g, li);
@@ -551,11 +562,12 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
   i32x4 kraw[PC], vraw[PC], qraw[PC], graw[KS];
   float dnr = 1.f, cnr = 0.f;
   auto fetch = [&](int64_t cc0, int nr) {
-    load_tile<DIM>(kraw, k + hoff, cc0, nr);
-    load_tile<DIM>(vraw, v + hoff, cc0, nr);
+    const int soff = static_cast<int>(cc0 * DIM * 2);
+    bload_tile<DIM>(kraw, rk, soff);
+    bload_tile<DIM>(vraw, rv, soff);
     if (CAUSAL) {
-      load_tile<DIM>(qraw, q + hoff, cc0, nr);
-      load_q<DIM>(graw, dout + hoff, cc0, nr, j, g);
+      bload_tile<DIM>(qraw, rq, soff);
+      bload_q<DIM>(graw, rg, soff, j, g);
       dnr = j < nr ? denh[cc0 + j] : 1.f;
       cnr = j < nr ? chh[cc0 + j] : 0.f;
     }
@@ -564,28 +576,27 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
 
   while (ci >= 0) {
     store_tile<DIM, true>(sKf, kraw, nrow);
-    store_tile<DIM, false>(sV, vraw, nrow);
+    store_tile_v<DIM>(sV, vraw);
     if (CAUSAL) {
       // the same g_i = bf16(dout_i / den_i) and c_i as the forward sweep used
       store_tile<DIM, true>(sQf, qraw, nrow);
-      const float inv = j < nrow ? 1.f / dnr : 0.f;
+      const float inv = j < nrow ? __builtin_amdgcn_rcpf(dnr) : 0.f;  // as in the forward sweep
 #pragma unroll
       for (int s = 0; s < KS; ++s)
         *reinterpret_cast<i16x8*>(sG + j * LD + 8 * g + 32 * s) =
             pack8(unpack8(__builtin_bit_cast(i16x8, graw[s])) * inv);
       if (g == 0) {
-        const float cj = j < nrow ? cnr : 0.f;
-        sC[j] = cj;
-        put_c(sCh, j, cj);
+        sC[j] = cnr;
+        put_c(sCh, j, cnr);
       }
     }
     __syncthreads();
+    const int soff = static_cast<int>(c0 * DIM * 2);
 
     const int64_t cp = c0 - T;
     const int nrowp = ci > 0 ? T : 0;  // earlier chunks of a segment are always full
     if (ci > 0) fetch(cp, nrowp);
 
-    const bool valid = j < nrow;
     i16x8 kreg[KS], vreg[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -593,7 +604,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
       vreg[s] = lds8(sV + j * LD + 8 * g + 32 * s);
     }
     // A[i][j] = phi(Q_i).phi(K_j) and Bm[i][j] = g_i.V_j + c_i for query
-    // tiles t >= w, masked i >= j, hi + lo
+    // tiles t >= w, masked i >= j; A as hi + lo
     i16x4 ahi[4], alo[4], bm[4];
     if (CAUSAL) {
 #pragma unroll
@@ -606,14 +617,9 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
             a = mfma(lds8(sQf + (16 * t + li) * LD + 8 * g + 32 * s), kreg[s], a);
             b = mfma(lds8(sG + (16 * t + li) * LD + 8 * g + 32 * s), vreg[s], b);
           }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const bool keep = !(t == w && 4 * g + u < li);
-            a[u] = keep ? a[u] : 0.f;
-            b[u] = keep ? b[u] + sC[16 * t + 4 * g + u] : 0.f;
-          }
-          split(a, ahi[t], alo[t]);
-          bm[t] = pack4(b);
+          const f32x4_t cv = *reinterpret_cast<const f32x4_t*>(sC + 16 * t + 4 * g);
+          split(a * mt[t], ahi[t], alo[t]);
+          bm[t] = pack4((b + cv) * mt[t]);
         }
       }
     }
@@ -645,17 +651,14 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
           }
         }
       }
-      if (valid) {
-        i16x4 rv, rk;
-        const i16x4 kv = *reinterpret_cast<const i16x4*>(sKf + j * LD + 16 * n + 4 * g);
+      // rows past the head's end fall outside the buffer range: dropped
+      const f32x4_t kv = unpack4(*reinterpret_cast<const i16x4*>(sKf + j * LD + 16 * n + 4 * g));
+      const f32x4_t rr = *reinterpret_cast<const f32x4_t*>(sRv + 16 * n + 4 * g);
+      f32x4_t rk;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          rv[u] = bf(ov[u]);
-          rk[u] = bf((ok[u] + sRv[16 * n + 4 * g + u]) * __builtin_amdgcn_fmed3f(fb(kv[u]), 0.f, 1.f));
-        }
-        *reinterpret_cast<i16x4*>(dv + hoff + (c0 + j) * DIM + 16 * n + 4 * g) = rv;
-        *reinterpret_cast<i16x4*>(dk + hoff + (c0 + j) * DIM + 16 * n + 4 * g) = rk;
-      }
+      for (int u = 0; u < 4; ++u) rk[u] = (ok[u] + rr[u]) * fminf(kv[u], 1.f);
+      bstore8(rdv, pack4(ov), (j * DIM + 16 * n + 4 * g) * 2, soff);
+      bstore8(rdk, pack4(rk), (j * DIM + 16 * n + 4 * g) * 2, soff);
     }
     if (CAUSAL) outer_update<DIM, true>(Racc, racc, sG, sQf, sCh, w, g, li);
     __syncthreads();
