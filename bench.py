@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the decode measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="seconds of untimed steps before the warmup steps (the GPU raises its clocks "
+                         "over the first few hundred milliseconds of load)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -79,7 +82,7 @@ def kernel_bytes(name: str, B, H, N, D, M, es, P=1):
     if base == "bwd_dkdv":
         return ht * (es * (2 * D + 3 * M) + 4 + es * (D + M))
     if base == "seg_scan":
-        return B * H * (P * 2 + 1) * (D * M + D) * 4
+        return B * H * (P * 2 + 1) * (D * M + D + M) * 4  # prefix records (suffix ones lack the M)
     if base == "decode":
         return B * H * (2 * D * M * 4 + 2 * D * 4 + es * (2 * D + M) + es * M)
     return 0
@@ -122,6 +125,13 @@ def main():
         return la.backward(q, k, v, out, g, den=den, causal=True, workspace=ws_b, saved=saved)
 
     log(f"workload fwdbwd_bf16 B={B} H={H} N={N} D={D} M={M}; plan fwd {plan_f} bwd {plan_b}")
+    # Untimed settling: an idle GPU needs a few hundred milliseconds of load
+    # to reach its steady clocks (the first ~0.3 s of steps run ~5% slower).
+    t_settle = time.time() + args.settle
+    while time.time() < t_settle:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -142,10 +142,14 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
   int64_t P = req && req->segments > 0 ? req->segments : 0;
   if (req && req->segments < 0) return fail(LA_ERR_INVALID, "plan.segments=%d", req->segments);
   if (P == 0) {
-    // About 1024 independent workgroups (four per CU on 256 CUs) so that
-    // several segments' loads are in flight per CU, with segments of at
-    // least 4 units; more segments only add scan work.
-    const int64_t want = (1024 + BH - 1) / BH;
+    // Generic kernels: about 1024 independent workgroups (four per CU on the
+    // 256 CUs of an MI355X) so that several segments' loads are in flight per
+    // CU.  MFMA kernels: about 512, one full round of the backward kernels at
+    // two workgroups per CU (measured best on the B=8, H=16, N=8192, D=64
+    // step: 512 beats 1024, 768 and 2048).  Segments keep at least 4 units;
+    // more segments only add scan work.
+    const int64_t target = kernel == LA_KERNEL_MFMA ? 512 : 1024;
+    const int64_t want = (target + BH - 1) / BH;
     P = std::min<int64_t>(want, std::max<int64_t>(1, nunits / 4));
   }
   P = std::max<int64_t>(1, std::min<int64_t>(P, nunits));
