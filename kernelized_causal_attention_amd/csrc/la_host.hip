@@ -120,10 +120,11 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
   (void)causal;
   int kernel = req ? req->kernel : LA_KERNEL_AUTO;
   if (kernel < LA_KERNEL_AUTO || kernel > LA_KERNEL_MFMA) return fail(LA_ERR_INVALID, "plan.kernel=%d", kernel);
-  const int mfma_ok = la::mfma_supported(op, D, M, dtype);
+  // the MFMA kernels address one head's rows with 32-bit buffer offsets
+  const int mfma_ok = la::mfma_supported(op, D, M, dtype) && N * std::max(D, M) * 2 < (int64_t(1) << 31);
   if (kernel == LA_KERNEL_MFMA && !mfma_ok)
-    return fail(LA_ERR_UNSUPPORTED, "no MFMA kernel for op %d, D=%lld, M=%lld, dtype %d", op, (long long)D,
-                (long long)M, dtype);
+    return fail(LA_ERR_UNSUPPORTED, "no MFMA kernel for op %d, N=%lld, D=%lld, M=%lld, dtype %d", op, (long long)N,
+                (long long)D, (long long)M, dtype);
   if (kernel == LA_KERNEL_AUTO) kernel = mfma_ok ? LA_KERNEL_MFMA : LA_KERNEL_GENERIC;
   const int unit = kernel == LA_KERNEL_MFMA ? 64 : 32;  // segment granularity
   int chunk = req ? req->chunk : 0;

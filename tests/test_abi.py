@@ -84,6 +84,13 @@ def test_resolve_plan(lib):
     assert lib.la_resolve_plan(0, 1, 1, 100, 16, 16, 1, 0, ctypes.byref(bad), ctypes.byref(out)) == 1
     bad = _native.la_plan(0, 0, 7)
     assert lib.la_resolve_plan(0, 1, 1, 100, 16, 16, 1, 0, ctypes.byref(bad), ctypes.byref(out)) == 1
+    # bf16 D = M = 128: MFMA kernels up to 2^31 bytes per head, generic beyond
+    assert lib.la_resolve_plan(0, 1, 1, (1 << 23) - 64, 128, 128, 1, 1, None, ctypes.byref(out)) == 0
+    assert out.kernel == 2
+    assert lib.la_resolve_plan(0, 1, 1, 1 << 23, 128, 128, 1, 1, None, ctypes.byref(out)) == 0
+    assert out.kernel == 1
+    mf = _native.la_plan(0, 0, 2)
+    assert lib.la_resolve_plan(0, 1, 1, 1 << 23, 128, 128, 1, 1, ctypes.byref(mf), ctypes.byref(out)) == 2
 
 
 nogpu = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer validation tests run on hosts without a GPU")
