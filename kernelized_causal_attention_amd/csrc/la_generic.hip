@@ -67,8 +67,7 @@ __device__ __forceinline__ void state_update(float* S, int SP, float* Z, const f
 template <typename TIn, int TC>
 __global__ __launch_bounds__(NT) void k_seg_state(const TIn* __restrict__ k, const TIn* __restrict__ v,
                                                   float* __restrict__ s_out, int64_t s_stride,
-                                                  float* __restrict__ z_out, int64_t z_stride,
-                                                  float* __restrict__ u_out, int64_t u_stride, int64_t N, int D,
+                                                  float* __restrict__ z_out, int64_t z_stride, int64_t N, int D,
                                                   int M, int P, int seg_len) {
   extern __shared__ float sm[];
   const int SP = M + 1, DP = D + 1, MP = M + 1;
@@ -84,7 +83,6 @@ __global__ __launch_bounds__(NT) void k_seg_state(const TIn* __restrict__ k, con
   const TIn* vh = v + bh * N * M;
   for (int e = threadIdx.x; e < D * M; e += NT) S[(e / M) * SP + e % M] = 0.f;
   for (int d = threadIdx.x; d < D; d += NT) Z[d] = 0.f;
-  float u = 0.f;  // thread m < M: sum of V[:, m] over the segment
   for (int64_t c0 = r0; c0 < r1; c0 += TC) {
     const int nrow = static_cast<int>(min(static_cast<int64_t>(TC), r1 - c0));
     __syncthreads();
@@ -92,24 +90,20 @@ __global__ __launch_bounds__(NT) void k_seg_state(const TIn* __restrict__ k, con
     stage<TIn, TC>(V, MP, vh, c0, nrow, M, false);
     __syncthreads();
     state_update(S, SP, Z, Kf, DP, V, MP, nrow, D, M);
-    if (threadIdx.x < M)
-      for (int j = 0; j < nrow; ++j) u += V[j * MP + threadIdx.x];
   }
   __syncthreads();
   const int64_t rec = bh * P + s;
   for (int e = threadIdx.x; e < D * M; e += NT) s_out[rec * s_stride + e] = S[(e / M) * SP + e % M];
   for (int d = threadIdx.x; d < D; d += NT) z_out[rec * z_stride + d] = Z[d];
-  if (u_out && threadIdx.x < M) u_out[rec * u_stride + threadIdx.x] = u;
 }
 
 // ---------------------------------------------------------------------------
 // Exclusive scan of per-segment records along the segment axis, fixed order.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(NT) void k_seg_scan(float* __restrict__ agg, int P, int64_t E, int64_t nb,
-                                                 int reverse, int64_t DM, int D, float* __restrict__ tot_s,
+                                                 int reverse, int64_t DM, float* __restrict__ tot_s,
                                                  int64_t ts_stride, float* __restrict__ tot_z,
-                                                 int64_t tz_stride, float* __restrict__ tot_u,
-                                                 int64_t tu_stride) {
+                                                 int64_t tz_stride) {
   const int64_t bh = blockIdx.x / nb;
   const int64_t e = (blockIdx.x % nb) * NT + threadIdx.x;
   if (e >= E) return;
@@ -124,10 +118,8 @@ __global__ __launch_bounds__(NT) void k_seg_scan(float* __restrict__ agg, int P,
   if (tot_s) {
     if (e < DM)
       tot_s[bh * ts_stride + e] = carry;
-    else if (e < DM + D)
+    else
       tot_z[bh * tz_stride + (e - DM)] = carry;
-    else if (tot_u)
-      tot_u[bh * tu_stride + (e - DM - D)] = carry;
   }
 }
 
@@ -268,7 +260,6 @@ __global__ __launch_bounds__(NT) void k_bwd_dq(const TIn* __restrict__ q, const 
   const int64_t r1 = min(N, r0 + seg_len);
   const int DM = D * M;
   const int64_t E = state_elems(D, M);
-  const int64_t ER = suffix_elems(D, M);
   const float* cs = nullptr;
   if (carry_s) cs = CAUSAL ? carry_s + (bh * P + s) * E : carry_s + bh * E;
   for (int e = t; e < DM; e += NT) S[(e / M) * SP + e % M] = cs ? cs[e] : 0.f;
@@ -334,7 +325,7 @@ __global__ __launch_bounds__(NT) void k_bwd_dq(const TIn* __restrict__ q, const 
     }
   }
   if (r_agg) {
-    float* rec = r_agg + (bh * P + s) * ER;
+    float* rec = r_agg + (bh * P + s) * E;
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
       const int e = t + r * NT;
@@ -377,7 +368,7 @@ __global__ __launch_bounds__(NT) void k_bwd_dkdv(const TIn* __restrict__ q, cons
   const int64_t r0 = static_cast<int64_t>(s) * seg_len;
   const int64_t r1 = min(N, r0 + seg_len);
   const int DM = D * M;
-  const int64_t E = suffix_elems(D, M);
+  const int64_t E = state_elems(D, M);
   const float* cr = nullptr;
   if (carry_r) cr = CAUSAL ? carry_r + (bh * P + s) * E : carry_r + bh * E;
   for (int e = t; e < DM; e += NT) R[(e / M) * SP + e % M] = cr ? cr[e] : 0.f;
@@ -496,13 +487,11 @@ int generic_chunk_for(int D, int M, int which) {
 }
 
 hipError_t launch_seg_state_generic(int dtype, const SegGeom& g, const void* k, const void* v, float* s_out,
-                                    int64_t s_stride, float* z_out, int64_t z_stride, float* u_out,
-                                    int64_t u_stride, hipStream_t st) {
+                                    int64_t s_stride, float* z_out, int64_t z_stride, hipStream_t st) {
   const int64_t grid = g.BH * g.P;
 #define LA_SEG(T, TC)                                                                             \
   LA_LAUNCH((k_seg_state<T, TC>), grid, lds_seg(TC, g.D, g.M), st, static_cast<const T*>(k),     \
-            static_cast<const T*>(v), s_out, s_stride, z_out, z_stride, u_out, u_stride, g.N, g.D, g.M, \
-            g.P, g.seg_len)
+            static_cast<const T*>(v), s_out, s_stride, z_out, z_stride, g.N, g.D, g.M, g.P, g.seg_len)
   if (dtype == 0) {
     if (g.chunk == 32) LA_SEG(float, 32);
     LA_SEG(float, 16);
@@ -513,13 +502,12 @@ hipError_t launch_seg_state_generic(int dtype, const SegGeom& g, const void* k, 
 #undef LA_SEG
 }
 
-hipError_t launch_seg_scan(float* agg, int64_t BH, int P, int D, int M, int with_u, int reverse, float* tot_s,
-                           int64_t ts_stride, float* tot_z, int64_t tz_stride, float* tot_u, int64_t tu_stride,
-                           hipStream_t st) {
-  const int64_t E = with_u ? state_elems(D, M) : suffix_elems(D, M);
+hipError_t launch_seg_scan(float* agg, int64_t BH, int P, int D, int M, int reverse, float* tot_s,
+                           int64_t ts_stride, float* tot_z, int64_t tz_stride, hipStream_t st) {
+  const int64_t E = state_elems(D, M);
   const int64_t nb = (E + NT - 1) / NT;
   hipLaunchKernelGGL(k_seg_scan, dim3(static_cast<unsigned>(BH * nb)), dim3(NT), 0, st, agg, P, E, nb, reverse,
-                     static_cast<int64_t>(D) * M, D, tot_s, ts_stride, tot_z, tz_stride, tot_u, tu_stride);
+                     static_cast<int64_t>(D) * M, tot_s, ts_stride, tot_z, tz_stride);
   return hipGetLastError();
 }
 

@@ -20,8 +20,7 @@ int mfma_supported(int op, int64_t D, int64_t M, int dtype);
 hipError_t launch_forward_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
                                void* out, float* den_out, const float* carry, hipStream_t st);
 hipError_t launch_seg_state_mfma(const SegGeom& g, const void* k, const void* v, float* s_out,
-                                 int64_t s_stride, float* z_out, int64_t z_stride, float* u_out, int64_t u_stride,
-                                 hipStream_t st);
+                                 int64_t s_stride, float* z_out, int64_t z_stride, hipStream_t st);
 hipError_t launch_bwd_dq_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
                               const void* dout, const float* carry_s, void* dq, float* r_agg, float* c_out,
                               float* den_out, hipStream_t st);
@@ -185,7 +184,6 @@ WsLayout layout(int op, int64_t BH, int64_t N, int64_t D, int64_t M, int causal,
   WsLayout w;
   Carve c;
   const size_t E = static_cast<size_t>(la::state_elems(static_cast<int>(D), static_cast<int>(M)));
-  const size_t ER = static_cast<size_t>(la::suffix_elems(static_cast<int>(D), static_cast<int>(M)));
   const size_t recs = static_cast<size_t>(BH) * p.P * E;
   if (op == LA_OP_FORWARD) {
     if (causal) {
@@ -197,8 +195,8 @@ WsLayout layout(int op, int64_t BH, int64_t N, int64_t D, int64_t M, int causal,
   } else if (op == LA_OP_BACKWARD) {
     w.aggS = c.take(recs);
     w.totS = c.take(static_cast<size_t>(BH) * E);
-    w.aggR = c.take(static_cast<size_t>(BH) * p.P * ER);
-    w.totR = c.take(static_cast<size_t>(BH) * ER);
+    w.aggR = c.take(recs);
+    w.totR = c.take(static_cast<size_t>(BH) * E);
     w.den = c.take(static_cast<size_t>(BH) * N);
     if (p.kernel == LA_KERNEL_MFMA) w.cvec = c.take(static_cast<size_t>(BH) * N);
   } else if (op == LA_OP_PREFIX_STATE) {
@@ -293,20 +291,17 @@ la::SegGeom geom(int64_t BH, int64_t N, int64_t D, int64_t M, const Plan& p, int
   return g;
 }
 
-// Segment aggregates of (S, Z, U) into ws records [BH][P][E].
+// Segment aggregates of (S, Z) into ws records [BH][P][E].
 hipError_t seg_state(int dtype, const Plan& p, const la::SegGeom& gbase, const void* k, const void* v,
                      float* recs, hipStream_t st) {
   const int64_t E = la::state_elems(gbase.D, gbase.M);
-  const int64_t DM = static_cast<int64_t>(gbase.D) * gbase.M;
-  float* z = recs + DM;
-  float* u = z + gbase.D;
+  float* z = recs + static_cast<int64_t>(gbase.D) * gbase.M;
   if (p.kernel == LA_KERNEL_MFMA)
-    return timed("mfma.seg_state", st,
-                 [&] { return la::launch_seg_state_mfma(gbase, k, v, recs, E, z, E, u, E, st); });
+    return timed("mfma.seg_state", st, [&] { return la::launch_seg_state_mfma(gbase, k, v, recs, E, z, E, st); });
   la::SegGeom g = gbase;
   g.chunk = la::generic_chunk_for(g.D, g.M, 1);
   return timed("generic.seg_state", st,
-               [&] { return la::launch_seg_state_generic(dtype, g, k, v, recs, E, z, E, u, E, st); });
+               [&] { return la::launch_seg_state_generic(dtype, g, k, v, recs, E, z, E, st); });
 }
 
 hipError_t fwd_pass(int dtype, int causal, const Plan& p, const la::SegGeom& gbase, const void* q,
@@ -322,14 +317,10 @@ hipError_t fwd_pass(int dtype, int causal, const Plan& p, const la::SegGeom& gba
                [&] { return la::launch_forward_generic(dtype, causal, g, q, k, v, out, den_out, carry, st); });
 }
 
-// Exclusive scan of prefix-state records (S, Z, U; forward direction) or of
-// suffix records (R, r; reverse).  tot, when given, receives each head's
-// total as a record of the same kind; tot_s/tot_z split it (U dropped).
 hipError_t scan(float* agg, int64_t BH, int P, int D, int M, int reverse, float* tot_s, int64_t ts_stride,
-                float* tot_z, int64_t tz_stride, float* tot_u, int64_t tu_stride, hipStream_t st) {
+                float* tot_z, int64_t tz_stride, hipStream_t st) {
   return timed("seg_scan", st, [&] {
-    return la::launch_seg_scan(agg, BH, P, D, M, reverse ? 0 : 1, reverse, tot_s, ts_stride, tot_z, tz_stride,
-                               tot_u, tu_stride, st);
+    return la::launch_seg_scan(agg, BH, P, D, M, reverse, tot_s, ts_stride, tot_z, tz_stride, st);
   });
 }
 
@@ -372,7 +363,7 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
     if (p.P > 1) {
       float* agg = sv ? sv : at(workspace, w.aggS);
       if ((e = seg_state(dtype, p, g, k, v, agg, stream))) return dev(e, "segment state");
-      if ((e = scan(agg, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, nullptr, 0, stream)))
+      if ((e = scan(agg, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream)))
         return dev(e, "segment scan");
       carry = agg;
     }
@@ -382,7 +373,7 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
   float* tot = sv ? sv : at(workspace, w.totS);
   const int64_t E = la::state_elems(g.D, g.M);
   if ((e = seg_state(dtype, p, g, k, v, agg, stream))) return dev(e, "segment state");
-  if ((e = scan(agg, BH, p.P, g.D, g.M, 0, tot, E, tot + D * M, E, tot + D * M + D, E, stream)))
+  if ((e = scan(agg, BH, p.P, g.D, g.M, 0, tot, E, tot + D * M, E, stream)))
     return dev(e, "segment scan");
   return dev(fwd_pass(dtype, 0, p, g, q, k, v, out, den_out, tot, stream), "forward");
 }
@@ -433,7 +424,6 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
 
   const la::SegGeom g = geom(BH, N, D, M, p, p.chunk);
   const int64_t E = la::state_elems(g.D, g.M);
-  const int64_t ER = la::suffix_elems(g.D, g.M);
   float* aggS = at(workspace, w.aggS);
   float* totS = at(workspace, w.totS);
   float* aggR = at(workspace, w.aggR);
@@ -445,13 +435,13 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
   } else if (causal) {
     if (p.P > 1) {
       if ((e = seg_state(dtype, p, g, k, v, aggS, stream))) return dev(e, "segment state");
-      if ((e = scan(aggS, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, nullptr, 0, stream)))
+      if ((e = scan(aggS, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream)))
         return dev(e, "segment scan");
       carry_s = aggS;
     }
   } else {
     if ((e = seg_state(dtype, p, g, k, v, aggS, stream))) return dev(e, "segment state");
-    if ((e = scan(aggS, BH, p.P, g.D, g.M, 0, totS, E, totS + D * M, E, totS + D * M + D, E, stream)))
+    if ((e = scan(aggS, BH, p.P, g.D, g.M, 0, totS, E, totS + D * M, E, stream)))
       return dev(e, "segment scan");
     carry_s = totS;
   }
@@ -481,12 +471,12 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
   const float* carry_r = nullptr;
   if (causal) {
     if (p.P > 1) {
-      if ((e = scan(aggR, BH, p.P, g.D, g.M, 1, nullptr, 0, nullptr, 0, nullptr, 0, stream)))
+      if ((e = scan(aggR, BH, p.P, g.D, g.M, 1, nullptr, 0, nullptr, 0, stream)))
         return dev(e, "suffix scan");
       carry_r = aggR;
     }
   } else {
-    if ((e = scan(aggR, BH, p.P, g.D, g.M, 1, totR, ER, totR + D * M, ER, nullptr, 0, stream)))
+    if ((e = scan(aggR, BH, p.P, g.D, g.M, 1, totR, E, totR + D * M, E, stream)))
       return dev(e, "suffix scan");
     carry_r = totR;
   }
@@ -580,17 +570,17 @@ LA_API la_status la_prefix_state(const void* k, const void* v, float* S, float* 
   hipError_t e;
   if (p.P == 1) {
     if (p.kernel == LA_KERNEL_MFMA)
-      return dev(timed("mfma.seg_state", stream, [&] { return la::launch_seg_state_mfma(g, k, v, S, D * M, Z, D, nullptr, 0, stream); }),
+      return dev(timed("mfma.seg_state", stream, [&] { return la::launch_seg_state_mfma(g, k, v, S, D * M, Z, D, stream); }),
                  "prefix state");
     la::SegGeom gs = g;
     gs.chunk = la::generic_chunk_for(g.D, g.M, 1);
     return dev(timed("generic.seg_state", stream,
-                     [&] { return la::launch_seg_state_generic(dtype, gs, k, v, S, D * M, Z, D, nullptr, 0, stream); }),
+                     [&] { return la::launch_seg_state_generic(dtype, gs, k, v, S, D * M, Z, D, stream); }),
                "prefix state");
   }
   float* agg = at(workspace, w.aggS);
   if ((e = seg_state(dtype, p, g, k, v, agg, stream))) return dev(e, "prefix state");
-  return dev(scan(agg, BH, p.P, g.D, g.M, 0, S, D * M, Z, D, nullptr, 0, stream), "prefix scan");
+  return dev(scan(agg, BH, p.P, g.D, g.M, 0, S, D * M, Z, D, stream), "prefix scan");
 }
 
 LA_API size_t la_workspace_bytes_ex(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,

@@ -7,12 +7,10 @@
 
 namespace la {
 
-// Per-head prefix-state record in a workspace: D*M floats of S (row-major
-// [D][M]), then D floats of Z, then M floats of U = sum_j V_j (the column
-// sums that the bf16 backward needs to split S = 1 U^T + sum_j elu(K_j) V_j^T).
-__host__ __device__ inline int64_t state_elems(int D, int M) { return static_cast<int64_t>(D) * M + D + M; }
-// Suffix record of the backward: D*M floats of R, then D floats of r.
-__host__ __device__ inline int64_t suffix_elems(int D, int M) { return static_cast<int64_t>(D) * M + D; }
+// Per-head state record in a workspace: D*M floats of S (row-major [D][M])
+// followed by D floats of Z (or R, r for the backward's suffix records);
+// E = D*M + D.
+__host__ __device__ inline int64_t state_elems(int D, int M) { return static_cast<int64_t>(D) * M + D; }
 
 struct SegGeom {
   int64_t BH;   // B * H independent sequences
@@ -30,21 +28,18 @@ struct SegGeom {
 // (0 forward, 1 segment state, 2 backward dq, 3 backward dk/dv); 0 if none.
 int generic_chunk_for(int D, int M, int which);
 
-// Segment aggregates dS = sum phi(K_j) V_j^T, dZ = sum phi(K_j), dU = sum V_j
-// over each segment, written at s_out + (bh*P + s)*s_stride, z_out + ... and
-// (when u_out is not null) u_out + (bh*P + s)*u_stride.
+// Segment aggregates dS = sum phi(K_j) V_j^T, dZ = sum phi(K_j) over each
+// segment; written at s_out + (bh*P + s)*s_stride and z_out + (bh*P + s)*z_stride.
 hipError_t launch_seg_state_generic(int dtype, const SegGeom& g, const void* k, const void* v, float* s_out,
-                                    int64_t s_stride, float* z_out, int64_t z_stride, float* u_out,
-                                    int64_t u_stride, hipStream_t st);
+                                    int64_t s_stride, float* z_out, int64_t z_stride, hipStream_t st);
 
 // In-place exclusive scan of [BH][P][E] records over the segment axis
-// (reverse = suffix sums), E = D*M + D (+ M when with_u).  When tot_s is not
-// null the inclusive total of each head goes to tot_s + bh*ts_stride (the
-// D*M entries of S or R), tot_z + bh*tz_stride (the D of Z or r) and, when
-// tot_u is not null, tot_u + bh*tu_stride (the M of U).
-hipError_t launch_seg_scan(float* agg, int64_t BH, int P, int D, int M, int with_u, int reverse,
-                           float* tot_s, int64_t ts_stride, float* tot_z, int64_t tz_stride, float* tot_u,
-                           int64_t tu_stride, hipStream_t st);
+// (reverse = suffix sums).  The inclusive total of each head goes to
+// tot_s + bh*ts_stride (first D*M entries) and tot_z + bh*tz_stride (last D),
+// when tot_s is not null.
+hipError_t launch_seg_scan(float* agg, int64_t BH, int P, int D, int M, int reverse,
+                           float* tot_s, int64_t ts_stride, float* tot_z, int64_t tz_stride,
+                           hipStream_t st);
 
 // Chunked forward.  carry: per-(bh, segment) exclusive prefix records
 // (causal) or per-bh totals (non-causal), or null for a zero state (P == 1).

@@ -123,7 +123,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_fwd_mfma(const bf16_t
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
   const int64_t r1 = min(N, r0 + seg_len);
-  constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + 2 * DIM;  // S, Z, U record
+  constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;
   const float* cs = carry ? (CAUSAL ? carry + (bh * P + seg) * E : carry + bh * E) : nullptr;
   const bf16_t* qh = q + bh * N * DIM;
   const bf16_t* kh = k + bh * N * DIM;
@@ -251,18 +251,16 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_fwd_mfma(const bf16_t
   }
 }
 
-// Segment aggregates dS = phi(K)^T V, dZ = colsum phi(K) and (when u_out is
-// not null) dU = colsum V over one segment.  phi(K) = 1 + E(K) is split so
-// that the records are as exact as fp32 allows: the MFMAs sum E(K)^T V and
-// colsum E(K) with E = elu carried as bf16 (a rounding relative to E, not to
-// phi ~ 1), and the ones part enters in fp32 as dS = 1 dU^T + E^T V,
-// dZ = count + colsum E.  The backward splits the records again and relies
-// on that precision.
+// Segment aggregates dS = phi(K)^T V, dZ = colsum phi(K) over one segment.
+// phi(K) = 1 + E(K) is split so that the records are as exact as fp32
+// allows: the MFMAs sum E(K)^T V and colsum E(K) with E = elu carried as
+// bf16 (a rounding relative to E, not to phi ~ 1), and the ones part enters
+// in fp32 as dS = 1 (colsum V)^T + E^T V, dZ = count + colsum E.  The
+// backward splits the carried states again and relies on that precision.
 template <int DIM>
 __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_seg_state_mfma(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                                        float* __restrict__ s_out, int64_t s_stride,
-                                                       float* __restrict__ z_out, int64_t z_stride,
-                                                       float* __restrict__ u_out, int64_t u_stride, int64_t N,
+                                                       float* __restrict__ z_out, int64_t z_stride, int64_t N,
                                                        int P, int seg_len) {
   using G = Geo<DIM>;
   constexpr int LD = G::LD, NTL = G::NTL, PC = G::PC, DT = G::DT;
@@ -330,10 +328,6 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_seg_state_mfma(const 
       if (li == 0) z_out[rec * z_stride + d] = zacc[dt][u] + count;
     }
   }
-  if (u_out && w == 0 && g == 0) {
-#pragma unroll
-    for (int n = 0; n < NTL; ++n) u_out[rec * u_stride + 16 * n + li] = uacc[n][0];
-  }
 }
 
 size_t lds_fwd(int dim) { return (2 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + dim * sizeof(float); }
@@ -374,16 +368,16 @@ hipError_t launch_forward_mfma(int causal, const SegGeom& g, const void* q, cons
 }
 
 hipError_t launch_seg_state_mfma(const SegGeom& g, const void* k, const void* v, float* s_out, int64_t s_stride,
-                                 float* z_out, int64_t z_stride, float* u_out, int64_t u_stride, hipStream_t st) {
+                                 float* z_out, int64_t z_stride, hipStream_t st) {
   const int64_t grid = g.BH * g.P;
   const bf16_t* K = static_cast<const bf16_t*>(k);
   const bf16_t* V = static_cast<const bf16_t*>(v);
   if (g.D == 64)
-    LA_MLAUNCH((k_seg_state_mfma<64>), grid, lds_seg(64), st, K, V, s_out, s_stride, z_out, z_stride, u_out,
-               u_stride, g.N, g.P, g.seg_len);
+    LA_MLAUNCH((k_seg_state_mfma<64>), grid, lds_seg(64), st, K, V, s_out, s_stride, z_out, z_stride, g.N, g.P,
+               g.seg_len);
   if (g.D == 128)
-    LA_MLAUNCH((k_seg_state_mfma<128>), grid, lds_seg(128), st, K, V, s_out, s_stride, z_out, z_stride, u_out,
-               u_stride, g.N, g.P, g.seg_len);
+    LA_MLAUNCH((k_seg_state_mfma<128>), grid, lds_seg(128), st, K, V, s_out, s_stride, z_out, z_stride, g.N,
+               g.P, g.seg_len);
   return hipErrorNotSupported;
 }
 

@@ -142,27 +142,52 @@ __device__ __forceinline__ void outer_update(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>
 
 // Variants of the helpers above for the forward sweep, which writes
 // phi = 1 + E (E = elu) and keeps the prefix state split as
-//   S = 1 U^T + S',  Z = n 1 + Z',  U = sum_j V_j,  S' = sum_j E(K_j) V_j^T,
-//   Z' = sum_j E(K_j)
-// (n tokens so far).  y holds, for the wave's column tiles, a vector over m
-// in the X^T accumulator layout: lane holds y[16mt + 4g + u].
+//   S = 1 U^T + S',  Z = n 1 + Z'.
+// The split is exact for any U and n; it pays when S' and Z' are small, i.e.
+// when U and n carry the ones direction of S and Z.  Within the sweep the
+// kernel keeps U = sum_j V_j, n = number of tokens, S' = sum_j E(K_j) V_j^T,
+// Z' = sum_j E(K_j); for a carried-in state (S, Z) it takes U = mean over d
+// of S[d][:] and n = mean over d of Z[d] (for a state built from tokens these
+// leave S', Z' no larger than the token sums do, and they need nothing but
+// S and Z).  y holds, for the wave's column tiles, a vector over m in the
+// X^T accumulator layout: lane holds y[16mt + 4g + u].
 template <int DIM>
-__device__ __forceinline__ void init_split(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&x)[Geo<DIM>::DT],
-                                           f32x4_t (&y)[Geo<DIM>::DT], const float* __restrict__ rec, float n0,
-                                           int w, int g, int li) {
+__device__ __forceinline__ float init_split(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&x)[Geo<DIM>::DT],
+                                            f32x4_t (&y)[Geo<DIM>::DT], const float* __restrict__ rec, int w, int g,
+                                            int li) {
   using G = Geo<DIM>;
+  // n = mean of Z: every wave sums all D entries (lane l reads Z[l], Z[l + 64])
+  float n = 0.f;
+  if (rec) {
+#pragma unroll
+    for (int d0 = 0; d0 < DIM; d0 += 64) n += rec[DIM * DIM + d0 + (threadIdx.x & 63)];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) n += __shfl_xor(n, off, 64);
+    n *= 1.f / DIM;
+  }
 #pragma unroll
   for (int a = 0; a < G::DT; ++a) {
     const int mt = w * G::DT + a;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) y[a][u] = rec ? rec[DIM * DIM + DIM + 16 * mt + 4 * g + u] : 0.f;
+    for (int n_ = 0; n_ < G::NTL; ++n_)
 #pragma unroll
-    for (int n = 0; n < G::NTL; ++n)
+      for (int u = 0; u < 4; ++u) X[a][n_][u] = rec ? rec[(16 * n_ + li) * DIM + 16 * mt + 4 * g + u] : 0.f;
+    // U[m] = mean over d = 16 n_ + li: in-lane over n_, then over the 16 li
 #pragma unroll
-      for (int u = 0; u < 4; ++u) X[a][n][u] = rec ? rec[(16 * n + li) * DIM + 16 * mt + 4 * g + u] - y[a][u] : 0.f;
-    const float z = rec ? rec[DIM * DIM + 16 * mt + li] - n0 : 0.f;
+    for (int u = 0; u < 4; ++u) {
+      float s = 0.f;
+#pragma unroll
+      for (int n_ = 0; n_ < G::NTL; ++n_) s += X[a][n_][u];
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off, 64);
+      y[a][u] = s * (1.f / DIM);
+#pragma unroll
+      for (int n_ = 0; n_ < G::NTL; ++n_) X[a][n_][u] -= y[a][u];
+    }
+    const float z = rec ? rec[DIM * DIM + 16 * mt + li] - n : 0.f;
     x[a] = f32x4_t{z, z, z, z};
   }
+  return n;
 }
 
 template <int DIM>
@@ -281,9 +306,8 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
   const int64_t r1 = min(N, r0 + seg_len);
-  constexpr int64_t ES = static_cast<int64_t>(DIM) * DIM + 2 * DIM;  // S, Z, U record
-  constexpr int64_t ER = static_cast<int64_t>(DIM) * DIM + DIM;      // R, r record
-  const float* cs = carry_s ? (CAUSAL ? carry_s + (bh * P + seg) * ES : carry_s + bh * ES) : nullptr;
+  constexpr int64_t ER = static_cast<int64_t>(DIM) * DIM + DIM;  // S, Z (or R, r) record
+  const float* cs = carry_s ? (CAUSAL ? carry_s + (bh * P + seg) * ER : carry_s + bh * ER) : nullptr;
   const int64_t hoff = bh * N * DIM;
   const int64_t hbytes = N * DIM * 2;
   const rsrc_t rq = make_rsrc(q + hoff, hbytes), rk = make_rsrc(k + hoff, hbytes), rv = make_rsrc(v + hoff, hbytes),
@@ -295,8 +319,6 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
   const int cc = 4 * (li % 4);
   const short one = 0x3f80;  // bf16 1.0
   const i16x8 ones = {one, one, one, one, one, one, one, one};
-  // tokens before the current chunk (the carried state's count)
-  float n0 = CAUSAL ? static_cast<float>(r0) : static_cast<float>(N);
   // causal mask of key j = 16t + 4g + u against query i = 16w + li, as 0 / 1
   // factors (kept in VGPRs: as per-(t, u) lane masks they would not fit in
   // the scalar registers)
@@ -307,8 +329,9 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
     for (int u = 0; u < 4; ++u) mt[t][u] = (t < w || (t == w && 4 * g + u <= li)) ? 1.f : 0.f;
 
   f32x4_t Sacc[DT][NTL], zacc[DT], uacc[DT], Racc[DT][NTL], racc[DT], gacc[DT];
-  init_split<DIM>(Sacc, zacc, uacc, cs, n0, w, g, li);
-  init_split<DIM>(Racc, racc, gacc, nullptr, 0.f, w, g, li);
+  // n0: the ones-direction count of the state before the current chunk
+  float n0 = init_split<DIM>(Sacc, zacc, uacc, cs, w, g, li);
+  init_split<DIM>(Racc, racc, gacc, nullptr, w, g, li);
   write_xt<DIM>(sS, sZ, Sacc, zacc, w, g, li);
   write_y<DIM>(sU, uacc, w, g, li);
   float csum = 0.f;

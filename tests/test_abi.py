@@ -162,11 +162,10 @@ def test_binding_requires_built_library_loudly(monkeypatch, tmp_path):
 
 def test_saved_bytes(lib):
     # causal over one segment keeps nothing; several segments keep one record
-    # (S, Z, U: D*M + D + M floats) per segment and head; non-causal keeps the
-    # totals.
+    # (S, Z: D*M + D floats) per segment and head; non-causal keeps the totals.
     one = _native.la_plan(0, 1, 1)
     four = _native.la_plan(0, 4, 1)
-    E = 16 * 8 + 16 + 8
+    E = 16 * 8 + 16
     assert lib.la_saved_bytes(1, 1, 256, 16, 8, 1, 0, ctypes.byref(one)) == 0
     assert lib.la_saved_bytes(2, 3, 256, 16, 8, 1, 0, ctypes.byref(four)) == 2 * 3 * 4 * E * 4
     assert lib.la_saved_bytes(2, 3, 256, 16, 8, 0, 0, ctypes.byref(four)) == 2 * 3 * E * 4

@@ -356,7 +356,7 @@ def test_saved_states_rejected_when_too_small():
     tq, tk, tv, tg = host_case(1, 1, 256, 64, 64, "bf16", seed=3, scale=0.125)
     plan = dict(kernel=2, segments=4)
     nb = la.saved_bytes(1, 1, 256, 64, 64, True, "bf16", plan)
-    assert nb == 4 * (64 * 64 + 64 + 64) * 4
+    assert nb == 4 * (64 * 64 + 64) * 4
     small = torch.empty(nb - 256, dtype=torch.uint8, device=DEV)
     with pytest.raises(la.LinAttnError, match="saved too small"):
         la.forward(tq, tk, tv, plan=plan, saved=small)
