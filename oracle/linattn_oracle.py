@@ -67,7 +67,9 @@ __all__ = [
     "decode_step",
     "decode_steps",
     "backward",
+    "backward_state",
     "fd_grad",
+    "fd_grad_state",
 ]
 
 
@@ -95,12 +97,16 @@ def phi_prime(x) -> np.ndarray:
 # Forward, quadratic form: the definition.
 # [W] eq:common with sim(q, k) = phi(q)^T phi(k) (section 2), the causal
 # mask of eq:mask (section 3), and the denominator phi(Q)(phi(K)^T 1) of
-# [X] section 1.
+# [X] section 1.  A state (S0, Z0) carried in from earlier tokens ([W]
+# section 4 starts from s_0 = z_0 = 0; [X] section 4.2 saves and restores a
+# session's state) enters every row as phi(Q_i)^T S0 and phi(Q_i)^T Z0:
+# the earlier tokens' terms of the same masked sum.
 # --------------------------------------------------------------------------
-def forward_quadratic(q, k, v, causal: bool = True):
+def forward_quadratic(q, k, v, causal: bool = True, S0=None, Z0=None):
     """Return (out, den) from the O(N^2) masked-sum definition.
 
     q, k: [..., N, D]; v: [..., N, M].  out: [..., N, M]; den: [..., N].
+    S0 [..., D, M], Z0 [..., D] (optional): the state of earlier tokens.
     """
     qf = phi(q)
     kf = phi(k)
@@ -111,6 +117,9 @@ def forward_quadratic(q, k, v, causal: bool = True):
         w = w * np.tril(np.ones((n, n)))  # keep j <= i
     num = w @ v
     den = w.sum(axis=-1)
+    if S0 is not None:
+        num = num + qf @ _f64(S0)
+        den = den + (qf * _f64(Z0)[..., None, :]).sum(axis=-1)
     return num / den[..., None], den
 
 
@@ -236,6 +245,17 @@ def decode_steps(S, Z, q, k, v):
 # --------------------------------------------------------------------------
 def backward(q, k, v, dout, causal: bool = True):
     """Return (dq, dk, dv, out, den) for the loss L = sum(dout * out)."""
+    dq, dk, dv, _, _, out, den = backward_state(q, k, v, dout, None, None, causal)
+    return dq, dk, dv, out, den
+
+
+# With a carried-in state (S0, Z0) the prefix sweep starts from it (S_i and
+# Z_i include S0, Z0), and since every row reads S0 and Z0:
+#   dL/dS0 = sum_i phi(Q_i) g_i^T = R_1,   dL/dZ0 = sum_i c_i phi(Q_i) = r_1,
+# the full suffix sums (non-causal: R, r over all rows, the same sums).
+def backward_state(q, k, v, dout, S0, Z0, causal: bool = True):
+    """Return (dq, dk, dv, dS0, dZ0, out, den) for L = sum(dout * out) with
+    the state (S0, Z0) carried in (None: zero state; dS0, dZ0 still given)."""
     q = _f64(q)
     k = _f64(k)
     v = _f64(v)
@@ -247,13 +267,13 @@ def backward(q, k, v, dout, causal: bool = True):
     m = v.shape[-1]
 
     # Forward sweep: prefix states S_i, Z_i, the outputs and grad phi(Q).
-    out, den, S_N, Z_N = forward_recurrent(q, k, v, causal)
+    out, den, S_N, Z_N = forward_recurrent(q, k, v, causal, S0, Z0)
     g = G / den[..., None]
     c = -(G * out).sum(axis=-1) / den
     dqf = np.empty(lead + (n, d))
     if causal:
-        S = np.zeros(lead + (d, m))
-        Z = np.zeros(lead + (d,))
+        S = np.zeros(lead + (d, m)) if S0 is None else _f64(S0).copy()
+        Z = np.zeros(lead + (d,)) if Z0 is None else _f64(Z0).copy()
         for i in range(n):
             S += kf[..., i, :, None] * v[..., i, None, :]
             Z += kf[..., i, :]
@@ -282,7 +302,8 @@ def backward(q, k, v, dout, causal: bool = True):
 
     dq = dqf * phi_prime(q)
     dk = dkf * phi_prime(k)
-    return dq, dk, dv, out, den
+    # R and r now hold the sums over all rows
+    return dq, dk, dv, R, r, out, den
 
 
 def fd_grad(q, k, v, dout, causal: bool = True, h: float = 1e-6):
@@ -293,6 +314,34 @@ def fd_grad(q, k, v, dout, causal: bool = True, h: float = 1e-6):
 
     def loss():
         o, _ = forward_quadratic(arrs[0], arrs[1], arrs[2], causal)
+        return float((G * o).sum())
+
+    grads = []
+    for a in arrs:
+        gr = np.zeros_like(a)
+        flat = a.reshape(-1)
+        gflat = gr.reshape(-1)
+        for idx in range(flat.size):
+            x0 = flat[idx]
+            flat[idx] = x0 + h
+            lp = loss()
+            flat[idx] = x0 - h
+            lm = loss()
+            flat[idx] = x0
+            gflat[idx] = (lp - lm) / (2.0 * h)
+        grads.append(gr)
+    return tuple(grads)
+
+
+def fd_grad_state(q, k, v, dout, S0, Z0, causal: bool = True, h: float = 1e-6):
+    """Central finite differences of L = sum(dout * out) through the
+    quadratic definition with a carried-in state; returns
+    (dq, dk, dv, dS0, dZ0).  For tiny inputs only."""
+    arrs = [_f64(q).copy(), _f64(k).copy(), _f64(v).copy(), _f64(S0).copy(), _f64(Z0).copy()]
+    G = _f64(dout)
+
+    def loss():
+        o, _ = forward_quadratic(arrs[0], arrs[1], arrs[2], causal, arrs[3], arrs[4])
         return float((G * o).sum())
 
     grads = []

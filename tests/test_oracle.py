@@ -216,6 +216,79 @@ def test_backward_returns_forward_output():
 
 
 # ------------------------------------------------------ frozen snapshot ---
+# ------------------------------------------------- carried-in state -----
+# A state (S0, Z0) from earlier tokens: the walkthrough's section 4 starts
+# the recurrence from s_0 = z_0 = 0, and "The deep link between Transformer
+# and RNN" (xxqk.cn), section 4.2, saves and restores a session's state.
+# Carrying the state of a prefix must reproduce the plain definition over the
+# concatenated tokens.
+@pytest.mark.parametrize("causal", [True, False])
+def test_state_forms_agree(causal):
+    q, k, v, _ = numpy_inputs(2, 2, 9, 3, 4, seed=31, scale=1.0)
+    S0 = rand((2, 2, 3, 4), 32)
+    Z0 = np.abs(rand((2, 2, 3), 33)) + 0.5  # a valid Z is positive
+    o1, d1 = oracle.forward_quadratic(q, k, v, causal, S0, Z0)
+    o2, d2, S2, Z2 = oracle.forward_recurrent(q, k, v, causal, S0, Z0)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12)
+    np.testing.assert_allclose(d1, d2, rtol=1e-12)
+    Sp, Zp = oracle.prefix_state(k, v)
+    np.testing.assert_allclose(S2, S0 + Sp, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(Z2, Z0 + Zp, rtol=1e-12)
+
+
+def test_state_of_prefix_continues_the_sequence():
+    # rows a..N of the causal definition over N tokens == the rows computed
+    # over tokens a..N alone, starting from the state of tokens 0..a-1
+    q, k, v, _ = numpy_inputs(1, 2, 13, 4, 3, seed=34, scale=1.0)
+    full, dfull = oracle.forward_quadratic(q, k, v, True)
+    for a in (1, 5, 12):
+        S0, Z0 = oracle.prefix_state(k[..., :a, :], v[..., :a, :])
+        part, dpart = oracle.forward_quadratic(q[..., a:, :], k[..., a:, :], v[..., a:, :], True, S0, Z0)
+        np.testing.assert_allclose(part, full[..., a:, :], rtol=1e-12)
+        np.testing.assert_allclose(dpart, dfull[..., a:], rtol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_state_matches_finite_differences(causal):
+    q, k, v, g = numpy_inputs(1, 1, 6, 3, 2, seed=35, scale=1.0)
+    S0 = rand((1, 1, 3, 2), 36)
+    Z0 = np.abs(rand((1, 1, 3), 37)) + 0.5
+    dq, dk, dv, dS0, dZ0, _, _ = oracle.backward_state(q, k, v, g, S0, Z0, causal)
+    fq, fk, fv, fS, fZ = oracle.fd_grad_state(q, k, v, g, S0, Z0, causal)
+    for a, b in ((dq, fq), (dk, fk), (dv, fv), (dS0, fS), (dZ0, fZ)):
+        assert rel_l2(a, b) < 1e-6
+
+
+def test_state_gradients_are_what_the_prefix_tokens_receive():
+    # Over [prefix | rest] with dout = 0 on the prefix rows, a prefix token's
+    # value and key reach the loss only through the rest's state S0, Z0, so
+    # dv_p = dS0^T phi(K_p) and grad phi(K_p) = dS0 v_p + dZ0.
+    q, k, v, g = numpy_inputs(1, 2, 11, 3, 4, seed=38, scale=1.0)
+    a = 4
+    g = g.copy()
+    g[..., :a, :] = 0.0
+    dq, dk, dv, _, _ = oracle.backward(q, k, v, g, True)
+    S0, Z0 = oracle.prefix_state(k[..., :a, :], v[..., :a, :])
+    rest = (x[..., a:, :] for x in (q, k, v, g))
+    rq, rk, rv, dS0, dZ0, _, _ = oracle.backward_state(*rest, S0, Z0, True)
+    np.testing.assert_allclose(rq, dq[..., a:, :], rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(rk, dk[..., a:, :], rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(rv, dv[..., a:, :], rtol=1e-10, atol=1e-14)
+    kf = oracle.phi(k[..., :a, :])
+    np.testing.assert_allclose(dv[..., :a, :], np.einsum("...dm,...pd->...pm", dS0, kf), rtol=1e-10)
+    dkf = np.einsum("...dm,...pm->...pd", dS0, v[..., :a, :]) + dZ0[..., None, :]
+    np.testing.assert_allclose(dk[..., :a, :], dkf * oracle.phi_prime(k[..., :a, :]), rtol=1e-10)
+
+
+def test_backward_state_zero_state_is_backward():
+    q, k, v, g = numpy_inputs(1, 2, 8, 3, 3, seed=39, scale=1.0)
+    for causal in (True, False):
+        a = oracle.backward(q, k, v, g, causal)
+        b = oracle.backward_state(q, k, v, g, np.zeros((1, 2, 3, 3)), np.zeros((1, 2, 3)), causal)
+        for x, y in zip(a[:3], b[:3]):
+            np.testing.assert_allclose(x, y, rtol=1e-13)
+
+
 def test_oracle_matches_frozen_snapshot():
     # tests/golden/oracle_small.json was written by tests/golden/make_golden.py
     # (oracle only); a change here means the oracle's arithmetic changed.

@@ -58,7 +58,22 @@ def pins_pass(o) -> bool:
         _, _, outs = o.decode_steps(S, Z, *(np.moveaxis(x, 2, 0) for x in (q, k, v)))
         if not np.allclose(np.moveaxis(outs, 0, 2), o.forward_quadratic(q, k, v, True)[0], rtol=1e-12):
             return False
+        # carried-in state: the rest of a sequence from its prefix's state,
+        # and the state gradients vs finite differences
+        q, k, v, g = numpy_inputs(1, 1, 7, 3, 2, seed=12, scale=1.0)
+        full, _ = o.forward_quadratic(q, k, v, True)
+        S0, Z0 = o.prefix_state(k[..., :3, :], v[..., :3, :])
+        part, _ = o.forward_recurrent(q[..., 3:, :], k[..., 3:, :], v[..., 3:, :], True, S0, Z0)[:2]
+        if not np.allclose(part, full[..., 3:, :], rtol=1e-12):
+            return False
+        for causal in (True, False):
+            got = o.backward_state(q[..., 3:, :], k[..., 3:, :], v[..., 3:, :], g[..., 3:, :], S0, Z0, causal)
+            fd = o.fd_grad_state(q[..., 3:, :], k[..., 3:, :], v[..., 3:, :], g[..., 3:, :], S0, Z0, causal)
+            for a, b in zip(got[:5], fd):
+                if not rel_l2(a, b) < 1e-6:
+                    return False
         # prefix state vs the recurrence's final state
+        q, k, v, _ = numpy_inputs(1, 1, 6, 3, 2, seed=10, scale=1.0)
         S1, Z1 = o.prefix_state(k, v)
         _, _, S2, Z2 = o.forward_recurrent(q, k, v, False)
         if not (np.allclose(S1, S2, rtol=1e-12) and np.allclose(Z1, Z2, rtol=1e-12)):
@@ -89,6 +104,10 @@ MUTANTS = {
     "decode_update_missing_z": ("    Z = _f64(Z) + kf\n", "    Z = _f64(Z)\n"),
     "prefix_state_drops_feature_map": ("    kf = phi(k)\n    v = _f64(v)\n    S = np.swapaxes",
                                        "    kf = _f64(k)\n    v = _f64(v)\n    S = np.swapaxes"),
+    "state_ignored_in_denominator": ("        den = den + (qf * _f64(Z0)[..., None, :]).sum(axis=-1)\n", ""),
+    "carried_state_dropped_in_prefix_sweep": ("        S = np.zeros(lead + (d, m)) if S0 is None else _f64(S0).copy()\n",
+                                             "        S = np.zeros(lead + (d, m))\n"),
+    "state_gradient_misses_normaliser": ("    return dq, dk, dv, R, r, out, den", "    return dq, dk, dv, R, 0.0 * r, out, den"),
     "noncausal_dq_uses_zero_state": ("dqf = np.einsum(\"...dm,...nm->...nd\", S_N, g) + c[..., :, None] * Z_N[..., None, :]",
                                      "dqf = np.einsum(\"...dm,...nm->...nd\", S_N, g)"),
 }
