@@ -62,7 +62,9 @@ typedef enum la_op {
   LA_OP_FORWARD = 0,
   LA_OP_BACKWARD = 1,
   LA_OP_PREFIX_STATE = 2,
-  LA_OP_DECODE = 3
+  LA_OP_DECODE = 3,
+  LA_OP_FORWARD_STATE = 4,  /* la_forward_state  */
+  LA_OP_BACKWARD_STATE = 5  /* la_backward_state */
 } la_op;
 
 /* Kernel family choice for the *_ex entry points (0 = automatic). */
@@ -145,6 +147,38 @@ la_status la_backward_ex(const void* q, const void* k, const void* v, const void
                          int causal, int dtype,
                          void* workspace, size_t workspace_bytes, hipStream_t stream,
                          const la_plan* plan);
+
+/* Causal forward that carries a state across calls: the N tokens continue
+ * a sequence whose earlier tokens left the state (S0, Z0) (the RNN form of
+ * the walkthrough's section 4 starts from s_0 = z_0 = 0; "The deep link
+ * between Transformer and RNN" (xxqk.cn), section 4.2, keeps one state per
+ * session and saves / restores it):
+ *   out_i = phi(Q_i)^T (S0 + S_i) / phi(Q_i)^T (Z0 + Z_i),
+ * and the state after the N tokens, S0 + S_N and Z0 + Z_N, is written to
+ * S_out, Z_out.  A prefill, a multi-token decode step and the next block of
+ * a long sequence are all this call; its state feeds la_decode_step.
+ *   S0 [B,H,D,M], Z0 [B,H,D] fp32, or both NULL (zero state);
+ *   S_out [B,H,D,M], Z_out [B,H,D] fp32, or both NULL; they may be S0, Z0
+ *     themselves (updated in place) but must not overlap them otherwise;
+ *   q, k, v, out, den_out as in la_forward (causal); workspace from
+ *   la_workspace_bytes(LA_OP_FORWARD_STATE, ...). */
+la_status la_forward_state(const void* q, const void* k, const void* v, void* out,
+                           int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype,
+                           const float* S0, const float* Z0, float* S_out, float* Z_out,
+                           float* den_out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Backward of la_forward_state (L = sum(dout * out)): dq, dk, dv as in
+ * la_backward with the prefix sweep starting from (S0, Z0), and, since every
+ * row reads the carried state, dL/dS0 = sum_i phi(Q_i) g_i^T and
+ * dL/dZ0 = sum_i c_i phi(Q_i) (the full suffix sums R_1, r_1) into dS0
+ * [B,H,D,M] and dZ0 [B,H,D] fp32 (both NULL to skip).  Workspace from
+ * la_workspace_bytes(LA_OP_BACKWARD_STATE, ...). */
+la_status la_backward_state(const void* q, const void* k, const void* v, const void* out,
+                            const void* dout, const float* den, const float* S0, const float* Z0,
+                            void* dq, void* dk, void* dv, float* dS0, float* dZ0,
+                            int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* One RNN decode step per (b,h), in place ("Transformers are RNNs"
  * walkthrough, section 4; the state is updated first, then read):

@@ -18,7 +18,8 @@ from . import _native
 from ._native import LinAttnError, la_plan  # noqa: F401
 
 __all__ = [
-    "forward", "backward", "decode_step", "prefix_state", "workspace_bytes", "saved_bytes", "resolve_plan",
+    "forward", "backward", "forward_state", "backward_state", "decode_step", "prefix_state", "workspace_bytes",
+    "saved_bytes", "resolve_plan",
     "LinAttnError", "library_path", "version", "profile_enable", "profile_report",
 ]
 
@@ -193,6 +194,86 @@ def backward(q, k, v, out, dout, den=None, causal: bool = True, plan=None, strea
                                      B, H, N, D, M, int(bool(causal)), dt, _ptr(ws), wsz, _stream(stream),
                                      _plan_ref(p)))
     return dq, dk, dv
+
+
+def _state_pair(S, Z, B, H, D, M, name):
+    torch = _torch()
+    if (S is None) != (Z is None):
+        raise ValueError(f"{name}: give both S and Z, or neither")
+    if S is None:
+        return None, None
+    for t, n in ((S, "S"), (Z, "Z")):
+        _dev(t, f"{name} {n}")
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} {n} must be float32")
+    if tuple(S.shape) != (B, H, D, M) or tuple(Z.shape) != (B, H, D):
+        raise ValueError(f"{name}: S [B,H,D,M] and Z [B,H,D] expected")
+    return S, Z
+
+
+def forward_state(q, k, v, S0=None, Z0=None, out=None, S_out=None, Z_out=None, return_den=False, stream=None,
+                  workspace=None):
+    """Causal forward continuing from the state (S0, Z0) of earlier tokens
+    (None: zero state).  Returns (out, S_N, Z_N) -- and den when return_den --
+    where S_N, Z_N is the state after these tokens (written into S_out, Z_out
+    when given; pass S_out=S0, Z_out=Z0 to update a session's state in
+    place)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    B, H, N, D = q.shape
+    M = v.shape[3]
+    S0, Z0 = _state_pair(S0, Z0, B, H, D, M, "S0/Z0")
+    if S_out is None:
+        S_out = torch.empty((B, H, D, M), dtype=torch.float32, device=q.device)
+        Z_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    S_out, Z_out = _state_pair(S_out, Z_out, B, H, D, M, "S_out/Z_out")
+    if out is None:
+        out = torch.empty((B, H, N, M), dtype=q.dtype, device=q.device)
+    den = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_den else None
+    lib = _native.load()
+    need = int(lib.la_workspace_bytes(_native.LA_OP_FORWARD_STATE, B, H, N, D, M, 1, _dtype_code(q)))
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    _native.check(lib.la_forward_state(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, D, M,
+                                       _dtype_code(q), _ptr(S0), _ptr(Z0), _ptr(S_out), _ptr(Z_out), _ptr(den),
+                                       _ptr(ws), wsz, _stream(stream)))
+    return (out, S_out, Z_out, den) if return_den else (out, S_out, Z_out)
+
+
+def backward_state(q, k, v, out, dout, S0=None, Z0=None, den=None, stream=None, workspace=None):
+    """Gradients (dq, dk, dv, dS0, dZ0) of sum(dout * out) for forward_state
+    from (S0, Z0) (None: zero state; dS0, dZ0 are still returned)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _dev(t, n)
+    B, H, N, D = q.shape
+    M = v.shape[3]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or out.shape != v.shape or dout.shape != v.shape:
+        raise ValueError("shape mismatch")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise TypeError("q, k, v, out, dout must share one dtype")
+    S0, Z0 = _state_pair(S0, Z0, B, H, D, M, "S0/Z0")
+    if den is not None:
+        _dev(den, "den")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dS0 = torch.empty((B, H, D, M), dtype=torch.float32, device=q.device)
+    dZ0 = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    lib = _native.load()
+    need = int(lib.la_workspace_bytes(_native.LA_OP_BACKWARD_STATE, B, H, N, D, M, 1, _dtype_code(q)))
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    _native.check(lib.la_backward_state(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                                        _ptr(den), _ptr(S0), _ptr(Z0), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                        dS0.data_ptr(), dZ0.data_ptr(), B, H, N, D, M, _dtype_code(q), _ptr(ws), wsz,
+                                        _stream(stream)))
+    return dq, dk, dv, dS0, dZ0
 
 
 def decode_step(S, Z, q, k, v, out=None, stream=None):

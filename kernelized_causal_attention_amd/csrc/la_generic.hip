@@ -101,13 +101,14 @@ __global__ __launch_bounds__(NT) void k_seg_state(const TIn* __restrict__ k, con
 // Exclusive scan of per-segment records along the segment axis, fixed order.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(NT) void k_seg_scan(float* __restrict__ agg, int P, int64_t E, int64_t nb,
-                                                 int reverse, int64_t DM, float* __restrict__ tot_s,
-                                                 int64_t ts_stride, float* __restrict__ tot_z,
-                                                 int64_t tz_stride) {
+                                                 int reverse, int64_t DM, const float* init_s, const float* init_z,
+                                                 float* tot_s, int64_t ts_stride, float* tot_z, int64_t tz_stride) {
   const int64_t bh = blockIdx.x / nb;
   const int64_t e = (blockIdx.x % nb) * NT + threadIdx.x;
   if (e >= E) return;
-  float carry = 0.f;
+  // (init and tot may be the same memory: each element is read here, by the
+  // thread that writes its total below)
+  float carry = init_s ? (e < DM ? init_s[bh * DM + e] : init_z[bh * (E - DM) + (e - DM)]) : 0.f;
   for (int p = 0; p < P; ++p) {
     const int s = reverse ? P - 1 - p : p;
     float* ptr = agg + (bh * P + s) * E + e;
@@ -502,12 +503,13 @@ hipError_t launch_seg_state_generic(int dtype, const SegGeom& g, const void* k, 
 #undef LA_SEG
 }
 
-hipError_t launch_seg_scan(float* agg, int64_t BH, int P, int D, int M, int reverse, float* tot_s,
-                           int64_t ts_stride, float* tot_z, int64_t tz_stride, hipStream_t st) {
+hipError_t launch_seg_scan(float* agg, int64_t BH, int P, int D, int M, int reverse, const float* init_s,
+                           const float* init_z, float* tot_s, int64_t ts_stride, float* tot_z, int64_t tz_stride,
+                           hipStream_t st) {
   const int64_t E = state_elems(D, M);
   const int64_t nb = (E + NT - 1) / NT;
   hipLaunchKernelGGL(k_seg_scan, dim3(static_cast<unsigned>(BH * nb)), dim3(NT), 0, st, agg, P, E, nb, reverse,
-                     static_cast<int64_t>(D) * M, tot_s, ts_stride, tot_z, tz_stride);
+                     static_cast<int64_t>(D) * M, init_s, init_z, tot_s, ts_stride, tot_z, tz_stride);
   return hipGetLastError();
 }
 

@@ -119,6 +119,9 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
   (void)causal;
   int kernel = req ? req->kernel : LA_KERNEL_AUTO;
   if (kernel < LA_KERNEL_AUTO || kernel > LA_KERNEL_MFMA) return fail(LA_ERR_INVALID, "plan.kernel=%d", kernel);
+  // the state-carrying calls run the forward / backward kernels
+  if (op == LA_OP_FORWARD_STATE) op = LA_OP_FORWARD;
+  if (op == LA_OP_BACKWARD_STATE) op = LA_OP_BACKWARD;
   // the MFMA kernels address one head's rows with 32-bit buffer offsets
   const int mfma_ok = la::mfma_supported(op, D, M, dtype) && N * std::max(D, M) * 2 < (int64_t(1) << 31);
   if (kernel == LA_KERNEL_MFMA && !mfma_ok)
@@ -185,14 +188,16 @@ WsLayout layout(int op, int64_t BH, int64_t N, int64_t D, int64_t M, int causal,
   Carve c;
   const size_t E = static_cast<size_t>(la::state_elems(static_cast<int>(D), static_cast<int>(M)));
   const size_t recs = static_cast<size_t>(BH) * p.P * E;
-  if (op == LA_OP_FORWARD) {
+  if (op == LA_OP_FORWARD_STATE) {
+    w.aggS = c.take(recs);
+  } else if (op == LA_OP_FORWARD) {
     if (causal) {
       if (p.P > 1) w.aggS = c.take(recs);
     } else {
       w.aggS = c.take(recs);
       w.totS = c.take(static_cast<size_t>(BH) * E);
     }
-  } else if (op == LA_OP_BACKWARD) {
+  } else if (op == LA_OP_BACKWARD || op == LA_OP_BACKWARD_STATE) {
     w.aggS = c.take(recs);
     w.totS = c.take(static_cast<size_t>(BH) * E);
     w.aggR = c.take(recs);
@@ -318,16 +323,39 @@ hipError_t fwd_pass(int dtype, int causal, const Plan& p, const la::SegGeom& gba
 }
 
 hipError_t scan(float* agg, int64_t BH, int P, int D, int M, int reverse, float* tot_s, int64_t ts_stride,
-                float* tot_z, int64_t tz_stride, hipStream_t st) {
+                float* tot_z, int64_t tz_stride, hipStream_t st, const float* init_s = nullptr,
+                const float* init_z = nullptr) {
   return timed("seg_scan", st, [&] {
-    return la::launch_seg_scan(agg, BH, P, D, M, reverse, tot_s, ts_stride, tot_z, tz_stride, st);
+    return la::launch_seg_scan(agg, BH, P, D, M, reverse, init_s, init_z, tot_s, ts_stride, tot_z, tz_stride, st);
   });
+}
+
+// State-carrying calls (la_forward_state / la_backward_state).
+struct StateArgs {
+  bool on = false;               // the call carries a state (causal only)
+  const float* S0 = nullptr;     // [BH][D][M] state carried in, or null (zero)
+  const float* Z0 = nullptr;     // [BH][D]
+  float* S_out = nullptr;        // forward: state after the N tokens; backward: dL/dS0
+  float* Z_out = nullptr;        // forward: Z after the N tokens; backward: dL/dZ0
+};
+
+la_status check_state(const StateArgs& st, int64_t BH, int64_t D, int64_t M, Span* spans) {
+  if (!st.on) return LA_OK;
+  if ((st.S0 == nullptr) != (st.Z0 == nullptr)) return fail(LA_ERR_INVALID, "S0 and Z0 must both be given or both be NULL");
+  if ((st.S_out == nullptr) != (st.Z_out == nullptr))
+    return fail(LA_ERR_INVALID, "the two state outputs must both be given or both be NULL");
+  for (const void* p : {static_cast<const void*>(st.S0), static_cast<const void*>(st.Z0),
+                        static_cast<const void*>(st.S_out), static_cast<const void*>(st.Z_out)})
+    if (p && (reinterpret_cast<uintptr_t>(p) & 3)) return fail(LA_ERR_INVALID, "state pointers must be 4-byte aligned");
+  spans[0] = span("S0", st.S0, st.S0 ? BH * D * M : 0, 4);
+  spans[1] = span("Z0", st.Z0, st.Z0 ? BH * D : 0, 4);
+  return LA_OK;
 }
 
 la_status do_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H, int64_t N,
                      int64_t D, int64_t M, int causal, int dtype, float* den_out, float* saved,
                      size_t saved_bytes, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                     const la_plan* plan) {
+                     const la_plan* plan, const StateArgs& st = StateArgs()) {
   la_status s = check_sizes(B, H, N, D, M, dtype);
   if (s != LA_OK) return s;
   causal = causal ? 1 : 0;
@@ -344,12 +372,20 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
   if (saved && saved_bytes < nsaved * sizeof(float))
     return fail(LA_ERR_INVALID, "saved too small: %zu bytes given, %zu needed", saved_bytes, nsaved * sizeof(float));
   float* sv = nsaved ? saved : nullptr;
+  Span sspan[2] = {span("S0", nullptr, 0, 4), span("Z0", nullptr, 0, 4)};
+  if ((s = check_state(st, BH, D, M, sspan))) return s;
+  // the state outputs may update S0, Z0 in place (exactly the same memory)
   const Span ins[] = {span("q", q, BH * N * D, es), span("k", k, BH * N * D, es), span("v", v, BH * N * M, es),
-                      span("workspace", workspace, workspace ? (int64_t)workspace_bytes : 0, 1)};
+                      span("workspace", workspace, workspace ? (int64_t)workspace_bytes : 0, 1),
+                      st.S_out == st.S0 ? span("S0", nullptr, 0, 4) : sspan[0],
+                      st.Z_out == st.Z0 ? span("Z0", nullptr, 0, 4) : sspan[1]};
   const Span outs[] = {span("out", out, BH * N * M, es), span("den_out", den_out, den_out ? BH * N : 0, 4),
-                       span("saved", sv, sv ? static_cast<int64_t>(nsaved) : 0, 4)};
-  if ((s = check_disjoint(outs, 3, ins, 4))) return s;
-  const WsLayout w = layout(LA_OP_FORWARD, BH, N, D, M, causal, p);
+                       span("saved", sv, sv ? static_cast<int64_t>(nsaved) : 0, 4),
+                       span("S_out", st.S_out, st.S_out ? BH * D * M : 0, 4),
+                       span("Z_out", st.Z_out, st.Z_out ? BH * D : 0, 4)};
+  if ((s = check_disjoint(outs, 5, ins, 6))) return s;
+  if (st.S_out == st.S0 && st.S0 && (s = check_disjoint(&outs[0], 3, &sspan[0], 2))) return s;
+  const WsLayout w = layout(st.on ? LA_OP_FORWARD_STATE : LA_OP_FORWARD, BH, N, D, M, causal, p);
   if (workspace_bytes < w.bytes)
     return fail(LA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, w.bytes);
   if (w.bytes && !workspace) return fail(LA_ERR_INVALID, "workspace is NULL (%zu bytes needed)", w.bytes);
@@ -358,6 +394,15 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
 
   const la::SegGeom g = geom(BH, N, D, M, p, p.chunk);
   hipError_t e;
+  if (st.on) {
+    // every segment's carry-in (starting from S0, Z0) and the final state
+    // come from the segment aggregates and their scan, as exact as fp32
+    float* agg = sv ? sv : at(workspace, w.aggS);
+    if ((e = seg_state(dtype, p, g, k, v, agg, stream))) return dev(e, "segment state");
+    if ((e = scan(agg, BH, p.P, g.D, g.M, 0, st.S_out, D * M, st.Z_out, D, stream, st.S0, st.Z0)))
+      return dev(e, "segment scan");
+    return dev(fwd_pass(dtype, 1, p, g, q, k, v, out, den_out, agg, stream), "forward");
+  }
   if (causal) {
     const float* carry = nullptr;
     if (p.P > 1) {
@@ -381,7 +426,8 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
 la_status do_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
                       const float* den, const float* saved, size_t saved_bytes, void* dq, void* dk, void* dv,
                       int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal, int dtype,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream, const la_plan* plan) {
+                      void* workspace, size_t workspace_bytes, hipStream_t stream, const la_plan* plan,
+                      const StateArgs& st = StateArgs()) {
   la_status s = check_sizes(B, H, N, D, M, dtype);
   if (s != LA_OK) return s;
   causal = causal ? 1 : 0;
@@ -408,15 +454,19 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
                   nsaved * sizeof(float));
   }
   const float* sv = nsaved ? saved : nullptr;
+  Span sspan[2] = {span("S0", nullptr, 0, 4), span("Z0", nullptr, 0, 4)};
+  if ((s = check_state(st, BH, D, M, sspan))) return s;
   const Span ins[] = {span("q", q, BH * N * D, es),       span("k", k, BH * N * D, es),
                       span("v", v, BH * N * M, es),       span("out", out, BH * N * M, es),
                       span("dout", dout, BH * N * M, es), span("den", den, den ? BH * N : 0, 4),
                       span("saved", sv, sv ? static_cast<int64_t>(nsaved) : 0, 4),
-                      span("workspace", workspace, workspace ? (int64_t)workspace_bytes : 0, 1)};
+                      span("workspace", workspace, workspace ? (int64_t)workspace_bytes : 0, 1),
+                      sspan[0], sspan[1]};
   const Span outs[] = {span("dq", dq, BH * N * D, es), span("dk", dk, BH * N * D, es),
-                       span("dv", dv, BH * N * M, es)};
-  if ((s = check_disjoint(outs, 3, ins, 8))) return s;
-  const WsLayout w = layout(LA_OP_BACKWARD, BH, N, D, M, causal, p);
+                       span("dv", dv, BH * N * M, es), span("dS0", st.S_out, st.S_out ? BH * D * M : 0, 4),
+                       span("dZ0", st.Z_out, st.Z_out ? BH * D : 0, 4)};
+  if ((s = check_disjoint(outs, 5, ins, 10))) return s;
+  const WsLayout w = layout(st.on ? LA_OP_BACKWARD_STATE : LA_OP_BACKWARD, BH, N, D, M, causal, p);
   if (workspace_bytes < w.bytes)
     return fail(LA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, w.bytes);
   if (!workspace) return fail(LA_ERR_INVALID, "workspace is NULL (%zu bytes needed)", w.bytes);
@@ -430,7 +480,13 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
   float* totR = at(workspace, w.totR);
   hipError_t e;
   const float* carry_s = nullptr;
-  if (saved) {
+  if (st.on) {
+    // carry-in from S0, Z0 through the segment scan (any number of segments)
+    if ((e = seg_state(dtype, p, g, k, v, aggS, stream))) return dev(e, "segment state");
+    if ((e = scan(aggS, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream, st.S0, st.Z0)))
+      return dev(e, "segment scan");
+    carry_s = aggS;
+  } else if (saved) {
     carry_s = sv;  // the forward's scanned states (null: one causal segment)
   } else if (causal) {
     if (p.P > 1) {
@@ -445,7 +501,9 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
       return dev(e, "segment scan");
     carry_s = totS;
   }
-  float* r_agg = (causal && p.P == 1) ? nullptr : aggR;
+  // the suffix aggregates are needed across segments, and for dL/dS0, dL/dZ0
+  // (their totals) in a state-carrying call
+  float* r_agg = (causal && p.P == 1 && !st.S_out) ? nullptr : aggR;
   // The MFMA path recomputes num and den in fp32 inside its forward sweep
   // (it reads neither out nor den) and passes den and c to the reverse sweep
   // through the workspace.
@@ -470,10 +528,10 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
   if (e) return dev(e, "backward dq");
   const float* carry_r = nullptr;
   if (causal) {
-    if (p.P > 1) {
-      if ((e = scan(aggR, BH, p.P, g.D, g.M, 1, nullptr, 0, nullptr, 0, stream)))
+    if (p.P > 1 || st.S_out) {
+      if ((e = scan(aggR, BH, p.P, g.D, g.M, 1, st.S_out, D * M, st.Z_out, D, stream)))
         return dev(e, "suffix scan");
-      carry_r = aggR;
+      if (p.P > 1) carry_r = aggR;
     }
   } else {
     if ((e = scan(aggR, BH, p.P, g.D, g.M, 1, totR, E, totR + D * M, E, stream)))
@@ -526,6 +584,35 @@ LA_API la_status la_backward_ex(const void* q, const void* k, const void* v, con
                                 hipStream_t stream, const la_plan* plan) {
   return do_backward(q, k, v, out, dout, den, saved, saved_bytes, dq, dk, dv, B, H, N, D, M, causal, dtype,
                      workspace, workspace_bytes, stream, plan);
+}
+
+LA_API la_status la_forward_state(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
+                                  int64_t N, int64_t D, int64_t M, int dtype, const float* S0, const float* Z0,
+                                  float* S_out, float* Z_out, float* den_out, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  StateArgs st;
+  st.on = true;
+  st.S0 = S0;
+  st.Z0 = Z0;
+  st.S_out = S_out;
+  st.Z_out = Z_out;
+  return do_forward(q, k, v, out, B, H, N, D, M, 1, dtype, den_out, nullptr, 0, workspace, workspace_bytes, stream,
+                    nullptr, st);
+}
+
+LA_API la_status la_backward_state(const void* q, const void* k, const void* v, const void* out,
+                                   const void* dout, const float* den, const float* S0, const float* Z0, void* dq,
+                                   void* dk, void* dv, float* dS0, float* dZ0, int64_t B, int64_t H, int64_t N,
+                                   int64_t D, int64_t M, int dtype, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  StateArgs st;
+  st.on = true;
+  st.S0 = S0;
+  st.Z0 = Z0;
+  st.S_out = dS0;
+  st.Z_out = dZ0;
+  return do_backward(q, k, v, out, dout, den, nullptr, 0, dq, dk, dv, B, H, N, D, M, 1, dtype, workspace,
+                     workspace_bytes, stream, nullptr, st);
 }
 
 LA_API la_status la_decode_step(float* S, float* Z, const void* q, const void* k, const void* v, void* out,

@@ -34,12 +34,14 @@ hipError_t launch_seg_state_generic(int dtype, const SegGeom& g, const void* k, 
                                     int64_t s_stride, float* z_out, int64_t z_stride, hipStream_t st);
 
 // In-place exclusive scan of [BH][P][E] records over the segment axis
-// (reverse = suffix sums).  The inclusive total of each head goes to
+// (reverse = suffix sums), starting from init_s [BH][D*M], init_z [BH][D]
+// when init_s is not null (a state carried in from earlier tokens) and from
+// zero otherwise.  The inclusive total of each head goes to
 // tot_s + bh*ts_stride (first D*M entries) and tot_z + bh*tz_stride (last D),
-// when tot_s is not null.
+// when tot_s is not null; a total may overwrite its init in place.
 hipError_t launch_seg_scan(float* agg, int64_t BH, int P, int D, int M, int reverse,
-                           float* tot_s, int64_t ts_stride, float* tot_z, int64_t tz_stride,
-                           hipStream_t st);
+                           const float* init_s, const float* init_z, float* tot_s, int64_t ts_stride,
+                           float* tot_z, int64_t tz_stride, hipStream_t st);
 
 // Chunked forward.  carry: per-(bh, segment) exclusive prefix records
 // (causal) or per-bh totals (non-causal), or null for a zero state (P == 1).
