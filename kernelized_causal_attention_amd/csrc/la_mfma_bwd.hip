@@ -279,7 +279,10 @@ __device__ __forceinline__ void store_r(float* __restrict__ rec, const f32x4_t (
 // chunk.  R and r are accumulated the same way, R = 1 G^T + sum_i E_i g_i^T
 // and r = C 1 + sum_i c_i E_i with G = sum_i g_i, C = sum_i c_i.
 // ---------------------------------------------------------------------------
-template <int DIM, bool CAUSAL>
+// FUSED_R: the (R, r) aggregate is summed here (D = 64); at D = 128 the two
+// fp32 128 x 128 states do not fit one wave's registers together, and
+// k_bwd_ragg_mfma sums the aggregate in a pass of its own.
+template <int DIM, bool CAUSAL, bool FUSED_R>
 __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                        const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
                                                        const float* __restrict__ carry_s, bf16_t* __restrict__ dq,
@@ -314,7 +317,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
                rg = make_rsrc(dout + hoff, hbytes), rdq = make_rsrc(dq + hoff, hbytes);
   float* ch = c_out + bh * N;
   float* dh = den_out + bh * N;
-  const bool want_r = r_agg != nullptr;
+  const bool want_r = FUSED_R && r_agg != nullptr;
   const int i = 16 * w + li;
   const int cc = 4 * (li % 4);
   const short one = 0x3f80;  // bf16 1.0
@@ -328,10 +331,11 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
 #pragma unroll
     for (int u = 0; u < 4; ++u) mt[t][u] = (t < w || (t == w && 4 * g + u <= li)) ? 1.f : 0.f;
 
-  f32x4_t Sacc[DT][NTL], zacc[DT], uacc[DT], Racc[DT][NTL], racc[DT], gacc[DT];
+  f32x4_t Sacc[DT][NTL], zacc[DT], uacc[DT];
   // n0: the ones-direction count of the state before the current chunk
   float n0 = init_split<DIM>(Sacc, zacc, uacc, cs, w, g, li);
-  init_split<DIM>(Racc, racc, gacc, nullptr, w, g, li);
+  f32x4_t Racc[FUSED_R ? DT : 1][FUSED_R ? NTL : 1], racc[FUSED_R ? DT : 1], gacc[FUSED_R ? DT : 1];
+  if constexpr (FUSED_R) init_split<DIM>(Racc, racc, gacc, nullptr, w, g, li);
   write_xt<DIM>(sS, sZ, Sacc, zacc, w, g, li);
   write_y<DIM>(sU, uacc, w, g, li);
   float csum = 0.f;
@@ -421,7 +425,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       gq[s] = pack8(unpack8(__builtin_bit_cast(i16x8, gcur[s])) * inv);
-      *reinterpret_cast<i16x8*>(sG + i * LD + 8 * g + 32 * s) = gq[s];
+      if constexpr (FUSED_R) *reinterpret_cast<i16x8*>(sG + i * LD + 8 * g + 32 * s) = gq[s];
       const f32x8_t gv = unpack8(gq[s]);
       const f32x8_t uv = *reinterpret_cast<const f32x8_t*>(sU + 8 * g + 32 * s);
 #pragma unroll
@@ -469,7 +473,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
     const float beta = gu + c * (n0 + (CAUSAL ? static_cast<float>(i + 1) : 0.f)) + shfl_sum_groups(sbv);
     csum += c;
     if (g == 0) {
-      put_c(sCh, i, c);
+      if constexpr (FUSED_R) put_c(sCh, i, c);
       if (valid) {
         ch[c0 + i] = c;
         dh[c0 + i] = den;
@@ -504,7 +508,8 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
     if (CAUSAL) outer_update_y<DIM, false>(Sacc, zacc, uacc, sV, sKe, nullptr, w, g, li);
     __syncthreads();
     // this chunk's g, E(Q) and c rows are complete: sum its (R, r) part
-    if (want_r) outer_update_y<DIM, true>(Racc, racc, gacc, sG, sQe, sCh, w, g, li);
+    if constexpr (FUSED_R)
+      if (want_r) outer_update_y<DIM, true>(Racc, racc, gacc, sG, sQe, sCh, w, g, li);
     if (CAUSAL) {
       write_xt<DIM>(sS, sZ, Sacc, zacc, w, g, li);
       write_y<DIM>(sU, uacc, w, g, li);
@@ -514,16 +519,79 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
     nrow = nrow1;
     buf ^= 1;
   }
-  if (want_r) {
-    // C = sum of c over the segment's rows (csum is the same in all four
-    // 16-lane groups of a wave: sum over li, then over the waves)
+  if constexpr (FUSED_R) {
+    if (want_r) {
+      // C = sum of c over the segment's rows (csum is the same in all four
+      // 16-lane groups of a wave: sum over li, then over the waves)
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) csum += __shfl_xor(csum, off, 64);
-    if (l == 0) sRed[w] = csum;
-    __syncthreads();
-    const float C = sRed[0] + sRed[1] + sRed[2] + sRed[3];
-    store_r<DIM>(r_agg + (bh * P + seg) * ER, Racc, racc, gacc, C, w, g, li);
+      for (int off = 1; off < 16; off <<= 1) csum += __shfl_xor(csum, off, 64);
+      if (l == 0) sRed[w] = csum;
+      __syncthreads();
+      const float C = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+      store_r<DIM>(r_agg + (bh * P + seg) * ER, Racc, racc, gacc, C, w, g, li);
+    }
   }
+}
+
+// ---------------------------------------------------------------------------
+// The segment's (R, r) aggregate as its own pass (used at D = 128): the same
+// g_i = bf16(dout_i / den_i) and c_i the forward sweep used (den, c read from
+// its outputs), summed exactly as the fused version sums them, so the
+// aggregate is the same bit for bit.
+// ---------------------------------------------------------------------------
+template <int DIM>
+__global__ __launch_bounds__(NT, 2) void k_bwd_ragg_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout,
+                                                         const float* __restrict__ den_in,
+                                                         const float* __restrict__ c_in, float* __restrict__ r_agg,
+                                                         int64_t N, int P, int seg_len) {
+  using G = Geo<DIM>;
+  constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* sQe = smem;
+  uint16_t* sG = sQe + T * LD;
+  float* sRed = reinterpret_cast<float*>(sG + T * LD);
+  uint16_t* sCh = reinterpret_cast<uint16_t*>(sRed + 4);
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.x / P;
+  const int seg = blockIdx.x % P;
+  const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
+  const int64_t r1 = min(N, r0 + seg_len);
+  constexpr int64_t ER = static_cast<int64_t>(DIM) * DIM + DIM;
+  const int64_t hoff = bh * N * DIM;
+  const int64_t hbytes = N * DIM * 2;
+  const rsrc_t rq = make_rsrc(q + hoff, hbytes), rg = make_rsrc(dout + hoff, hbytes);
+  const float* denh = den_in + bh * N;
+  const float* chh = c_in + bh * N;
+  const int i = 16 * w + li;
+  f32x4_t Racc[DT][NTL], racc[DT], gacc[DT];
+  init_split<DIM>(Racc, racc, gacc, nullptr, w, g, li);
+  float csum = 0.f;
+  for (int64_t c0 = r0; c0 < r1; c0 += T) {
+    const int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
+    const int soff = static_cast<int>(c0 * DIM * 2);
+    i32x4 qraw[PC], graw[KS];
+    bload_tile<DIM>(qraw, rq, soff);
+    bload_q<DIM>(graw, rg, soff, i, g);
+    const bool valid = i < nrow;
+    const float inv = valid ? __builtin_amdgcn_rcpf(denh[c0 + i]) : 0.f;  // as in the forward sweep
+    const float c = valid ? chh[c0 + i] : 0.f;
+    store_tile_e<DIM>(sQe, qraw);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      *reinterpret_cast<i16x8*>(sG + i * LD + 8 * g + 32 * s) = pack8(unpack8(__builtin_bit_cast(i16x8, graw[s])) * inv);
+    if (g == 0) put_c(sCh, i, c);
+    csum += c;
+    __syncthreads();
+    outer_update_y<DIM, true>(Racc, racc, gacc, sG, sQe, sCh, w, g, li);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) csum += __shfl_xor(csum, off, 64);
+  if (l == 0) sRed[w] = csum;
+  __syncthreads();
+  const float C = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+  store_r<DIM>(r_agg + (bh * P + seg) * ER, Racc, racc, gacc, C, w, g, li);
 }
 
 // ---------------------------------------------------------------------------
@@ -696,6 +764,7 @@ size_t lds_bwd(int dim) {
   return (4 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + (dim + T) * sizeof(float) +
          2 * T * sizeof(uint16_t);
 }
+size_t lds_ragg(int dim) { return 2 * T * (dim + 8) * sizeof(uint16_t) + 4 * sizeof(float) + 2 * T * sizeof(uint16_t); }
 size_t lds_dq(int dim) {
   return (6 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + (2 * dim + 4) * sizeof(float) +
          4 * T * sizeof(uint16_t);
@@ -716,20 +785,23 @@ hipError_t launch_bwd_dq_mfma(int causal, const SegGeom& g, const void* q, const
                               const void* dout, const float* carry_s, void* dq, float* r_agg, float* c_out,
                               float* den_out, hipStream_t st) {
   const int64_t grid = g.BH * g.P;
-#define LA_DQ(D, C)                                                                                          \
-  LA_MLAUNCH((k_bwd_dq_mfma<D, C>), grid, lds_dq(D), st, static_cast<const bf16_t*>(q),                    \
+#define LA_DQ(D, C, F)                                                                                       \
+  LA_MLAUNCH((k_bwd_dq_mfma<D, C, F>), grid, lds_dq(D), st, static_cast<const bf16_t*>(q),                 \
              static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), \
              carry_s, static_cast<bf16_t*>(dq), r_agg, c_out, den_out, g.N, g.P, g.seg_len)
   if (g.D == 64) {
-    if (causal) LA_DQ(64, true);
-    LA_DQ(64, false);
+    if (causal) LA_DQ(64, true, true);
+    LA_DQ(64, false, true);
   }
-  if (g.D == 128) {
-    if (causal) LA_DQ(128, true);
-    LA_DQ(128, false);
-  }
+  if (g.D != 128) return hipErrorNotSupported;
+  const hipError_t e = [&]() -> hipError_t {
+    if (causal) LA_DQ(128, true, false);
+    LA_DQ(128, false, false);
+  }();
+  if (e != hipSuccess || !r_agg) return e;
+  LA_MLAUNCH((k_bwd_ragg_mfma<128>), grid, lds_ragg(128), st, static_cast<const bf16_t*>(q),
+             static_cast<const bf16_t*>(dout), den_out, c_out, r_agg, g.N, g.P, g.seg_len);
 #undef LA_DQ
-  return hipErrorNotSupported;
 }
 
 hipError_t launch_bwd_dkdv_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
