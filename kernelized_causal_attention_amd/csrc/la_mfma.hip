@@ -41,11 +41,19 @@ using namespace mf;
 constexpr int NT = kNT;
 constexpr int T = kT;
 
-// S (fp32 accumulators) -> S^T bf16 in LDS, Z -> LDS.
+// Waves per workgroup: 4 at D = 64; 8 at D = 128, where the pairs of waves
+// on one 16-row query tile split the output columns and every wave owns one
+// 16-row slab of the state, so that a wave's registers stay within what
+// two resident waves per SIMD allow.
 template <int DIM>
-__device__ __forceinline__ void write_state(uint16_t* sST, float* sZ, const f32x4_t (&Sacc)[Geo<DIM>::DT][Geo<DIM>::NTL],
-                                            const f32x4_t (&zacc)[Geo<DIM>::DT], int w, int g, int li) {
-  using G = Geo<DIM>;
+constexpr int kFwdWaves = DIM == 128 ? 8 : 4;
+
+// S (fp32 accumulators) -> S^T bf16 in LDS, Z -> LDS.
+template <int DIM, int NW>
+__device__ __forceinline__ void write_state(uint16_t* sST, float* sZ,
+                                            const f32x4_t (&Sacc)[(Geo<DIM, NW>::DT)][(Geo<DIM, NW>::NTL)],
+                                            const f32x4_t (&zacc)[(Geo<DIM, NW>::DT)], int w, int g, int li) {
+  using G = Geo<DIM, NW>;
 #pragma unroll
   for (int dt = 0; dt < G::DT; ++dt) {
     const int d0 = 16 * (w * G::DT + dt);
@@ -60,10 +68,11 @@ __device__ __forceinline__ void write_state(uint16_t* sST, float* sZ, const f32x
 }
 
 // S += phi(K_c)^T V_c and Z += colsum phi(K_c) for this wave's state rows.
-template <int DIM>
-__device__ __forceinline__ void state_update(f32x4_t (&Sacc)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&zacc)[Geo<DIM>::DT],
-                                             const uint16_t* sKf, const uint16_t* sV, int w, int g, int li) {
-  using G = Geo<DIM>;
+template <int DIM, int NW>
+__device__ __forceinline__ void state_update(f32x4_t (&Sacc)[(Geo<DIM, NW>::DT)][(Geo<DIM, NW>::NTL)],
+                                             f32x4_t (&zacc)[(Geo<DIM, NW>::DT)], const uint16_t* sKf,
+                                             const uint16_t* sV, int w, int g, int li) {
+  using G = Geo<DIM, NW>;
   const short one = 0x3f80;  // bf16 1.0
   const i16x8 ones = {one, one, one, one, one, one, one, one};
 #pragma unroll
@@ -84,10 +93,11 @@ __device__ __forceinline__ void state_update(f32x4_t (&Sacc)[Geo<DIM>::DT][Geo<D
   }
 }
 
-template <int DIM>
-__device__ __forceinline__ void init_state(f32x4_t (&Sacc)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&zacc)[Geo<DIM>::DT],
-                                           const float* __restrict__ cs, int w, int g, int li) {
-  using G = Geo<DIM>;
+template <int DIM, int NW>
+__device__ __forceinline__ void init_state(f32x4_t (&Sacc)[(Geo<DIM, NW>::DT)][(Geo<DIM, NW>::NTL)],
+                                           f32x4_t (&zacc)[(Geo<DIM, NW>::DT)], const float* __restrict__ cs, int w,
+                                           int g, int li) {
+  using G = Geo<DIM, NW>;
 #pragma unroll
   for (int dt = 0; dt < G::DT; ++dt) {
     const int d0 = 16 * (w * G::DT + dt);
@@ -103,22 +113,31 @@ __device__ __forceinline__ void init_state(f32x4_t (&Sacc)[Geo<DIM>::DT][Geo<DIM
 
 // ---------------------------------------------------------------------------
 template <int DIM, bool CAUSAL>
-__global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_fwd_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+__global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                  const bf16_t* __restrict__ v, bf16_t* __restrict__ out,
                                                  float* __restrict__ den_out, const float* __restrict__ carry,
                                                  int64_t N, int P, int seg_len) {
-  using G = Geo<DIM>;
+  constexpr int NW = kFwdWaves<DIM>;
+  using G = Geo<DIM, NW>;
   constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
+  constexpr int NCG = NW / 4;       // column groups per query tile
+  constexpr int NTW = NTL / NCG;    // output tiles per wave
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* sKf = smem;
   uint16_t* sV = sKf + T * LD;
   uint16_t* sST = sV + T * LD;
   float* sZ = reinterpret_cast<float*>(sST + DIM * LD);
+  // With two waves per query tile, phi(Q) is staged once in LDS rather than
+  // computed by both waves of a pair from their own loads.
+  constexpr bool kQInLds = NCG > 1;
+  uint16_t* sQf = reinterpret_cast<uint16_t*>(sZ + DIM);
 
   // w is made wave-uniform (an SGPR) so that branches on it are scalar: an
   // MFMA under an EXEC-masked branch still writes every lane.
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rt = w & 3;             // query row tile
+  const int nb = NCG == 1 ? 0 : (w >> 2) * NTW;  // first output tile of this wave
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
@@ -130,44 +149,58 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_fwd_mfma(const bf16_t
   const bf16_t* vh = v + bh * N * DIM;
   bf16_t* oh = out ? out + bh * N * DIM : nullptr;
   float* dh = den_out ? den_out + bh * N : nullptr;
-  const int i = 16 * w + li;  // this lane's query row within the chunk
+  const int i = 16 * rt + li;  // this lane's query row within the chunk
 
   f32x4_t Sacc[DT][NTL];
   f32x4_t zacc[DT];
-  init_state<DIM>(Sacc, zacc, cs, w, g, li);
-  write_state<DIM>(sST, sZ, Sacc, zacc, w, g, li);
+  init_state<DIM, NW>(Sacc, zacc, cs, w, g, li);
+  write_state<DIM, NW>(sST, sZ, Sacc, zacc, w, g, li);
 
   int64_t c0 = r0;
   int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
-  i32x4 kraw[PC], vraw[PC], qraw[KS];
+  constexpr int QN = kQInLds ? PC : KS;  // q pieces held per lane
+  i32x4 kraw[PC], vraw[PC], qraw[QN];
+  auto fetch_q = [&](int64_t cc0, int nr) {
+    if constexpr (kQInLds)
+      load_tile<DIM, NW>(qraw, qh, cc0, nr);
+    else
+      load_q<DIM>(qraw, qh, cc0, nr, i, g);
+  };
   if (CAUSAL) {
-    load_tile<DIM>(kraw, kh, c0, nrow);
-    load_tile<DIM>(vraw, vh, c0, nrow);
+    load_tile<DIM, NW>(kraw, kh, c0, nrow);
+    load_tile<DIM, NW>(vraw, vh, c0, nrow);
   }
-  load_q<DIM>(qraw, qh, c0, nrow, i, g);
+  fetch_q(c0, nrow);
 
   while (c0 < r1) {
     if (CAUSAL) {
-      store_tile<DIM, true>(sKf, kraw, nrow);
-      store_tile<DIM, false>(sV, vraw, nrow);
+      store_tile<DIM, true, NW>(sKf, kraw, nrow);
+      store_tile<DIM, false, NW>(sV, vraw, nrow);
     }
     i16x8 qf[KS];
+    if constexpr (kQInLds) {
+      store_tile<DIM, true, NW>(sQf, qraw, nrow);
+      __syncthreads();
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = i < nrow ? phi8(qraw[s]) : i16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    __syncthreads();
+      for (int s = 0; s < KS; ++s) qf[s] = lds8(sQf + i * LD + 8 * g + 32 * s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[s] = i < nrow ? phi8(qraw[s]) : i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      __syncthreads();
+    }
 
     // prefetch the next chunk while this one computes
     const int64_t c1 = c0 + T;
     const int nrow1 = c1 < r1 ? static_cast<int>(min(static_cast<int64_t>(T), r1 - c1)) : 0;
     if (nrow1 > 0) {
       if (CAUSAL) {
-        load_tile<DIM>(kraw, kh, c1, nrow1);
-        load_tile<DIM>(vraw, vh, c1, nrow1);
+        load_tile<DIM, NW>(kraw, kh, c1, nrow1);
+        load_tile<DIM, NW>(vraw, vh, c1, nrow1);
       }
-      load_q<DIM>(qraw, qh, c1, nrow1, i, g);
+      fetch_q(c1, nrow1);
     }
 
-    // Intra-chunk scores A^T (key tiles t <= w), masked.  With phi ~ 1 + x
+    // Intra-chunk scores A^T (key tiles t <= rt), masked.  With phi ~ 1 + x
     // the scores sit near D with a small spread, so one bf16 rounding would
     // lose most of that spread; each score is carried as hi + lo, two bf16
     // values whose sum keeps ~16 significant bits, and both enter the MFMA.
@@ -178,11 +211,11 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_fwd_mfma(const bf16_t
       for (int t = 0; t < 4; ++t) {
         ahi[t] = i16x4{0, 0, 0, 0};
         alo[t] = i16x4{0, 0, 0, 0};
-        if (t <= w) {
+        if (t <= rt) {
           f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < KS; ++s) acc = mfma(lds8(sKf + (16 * t + li) * LD + 8 * g + 32 * s), qf[s], acc);
-          if (t == w) {
+          if (t == rt) {
 #pragma unroll
             for (int u = 0; u < 4; ++u)
               if (4 * g + u > li) acc[u] = 0.f;
@@ -208,27 +241,28 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_fwd_mfma(const bf16_t
     di = shfl_sum_groups(di);
     const float den = rs + di;
 
-    // O^T = S^T phi(Q)^T (+ V^T A^T)
-    f32x4_t o[NTL];
+    // O^T = S^T phi(Q)^T (+ V^T A^T), this wave's output tiles
+    f32x4_t o[NTW];
 #pragma unroll
-    for (int n = 0; n < NTL; ++n) {
+    for (int n = 0; n < NTW; ++n) {
       o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) o[n] = mfma(lds8(sST + (16 * n + li) * LD + 8 * g + 32 * s), qf[s], o[n]);
+      for (int s = 0; s < KS; ++s) o[n] = mfma(lds8(sST + (16 * (nb + n) + li) * LD + 8 * g + 32 * s), qf[s], o[n]);
     }
     if (CAUSAL) {
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp) {
-        if (2 * tp <= w) {
-          const i16x8 bh = cat(ahi[2 * tp], ahi[2 * tp + 1]);
-          const i16x8 bl = cat(alo[2 * tp], alo[2 * tp + 1]);
+        if (2 * tp <= rt) {
+          const i16x8 bhi = cat(ahi[2 * tp], ahi[2 * tp + 1]);
+          const i16x8 blo = cat(alo[2 * tp], alo[2 * tp + 1]);
           const int jr = 32 * tp + 4 * g + li / 4;
           const int cc = 4 * (li % 4);
 #pragma unroll
-          for (int n = 0; n < NTL; ++n) {
-            const i16x8 a = cat(lds_tr(sV + jr * LD + 16 * n + cc), lds_tr(sV + (jr + 16) * LD + 16 * n + cc));
-            o[n] = mfma(a, bh, o[n]);
-            o[n] = mfma(a, bl, o[n]);
+          for (int n = 0; n < NTW; ++n) {
+            const int m0 = 16 * (nb + n) + cc;
+            const i16x8 a = cat(lds_tr(sV + jr * LD + m0), lds_tr(sV + (jr + 16) * LD + m0));
+            o[n] = mfma(a, bhi, o[n]);
+            o[n] = mfma(a, blo, o[n]);
           }
         }
       }
@@ -237,15 +271,15 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_fwd_mfma(const bf16_t
       if (oh) {
         const float inv = 1.f / den;
 #pragma unroll
-        for (int n = 0; n < NTL; ++n)
-          *reinterpret_cast<i16x4*>(oh + (c0 + i) * DIM + 16 * n + 4 * g) = pack4(o[n] * inv);
+        for (int n = 0; n < NTW; ++n)
+          *reinterpret_cast<i16x4*>(oh + (c0 + i) * DIM + 16 * (nb + n) + 4 * g) = pack4(o[n] * inv);
       }
-      if (dh && g == 0) dh[c0 + i] = den;
+      if (dh && g == 0 && nb == 0) dh[c0 + i] = den;
     }
 
-    if (CAUSAL) state_update<DIM>(Sacc, zacc, sKf, sV, w, g, li);
+    if (CAUSAL) state_update<DIM, NW>(Sacc, zacc, sKf, sV, w, g, li);
     __syncthreads();
-    if (CAUSAL) write_state<DIM>(sST, sZ, Sacc, zacc, w, g, li);
+    if (CAUSAL) write_state<DIM, NW>(sST, sZ, Sacc, zacc, w, g, li);
     c0 = c1;
     nrow = nrow1;
   }
@@ -258,16 +292,16 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_fwd_mfma(const bf16_t
 // in fp32 as dS = 1 (colsum V)^T + E^T V, dZ = count + colsum E.  The
 // backward splits the carried states again and relies on that precision.
 template <int DIM>
-__global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_seg_state_mfma(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+__global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_seg_state_mfma(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                                        float* __restrict__ s_out, int64_t s_stride,
                                                        float* __restrict__ z_out, int64_t z_stride, int64_t N,
                                                        int P, int seg_len) {
-  using G = Geo<DIM>;
+  constexpr int NW = kFwdWaves<DIM>;
+  using G = Geo<DIM, NW>;
   constexpr int LD = G::LD, NTL = G::NTL, PC = G::PC, DT = G::DT;
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* sKe = smem;
   uint16_t* sV = sKe + T * LD;
-  float* sRow = reinterpret_cast<float*>(sV + T * LD);  // row sums (unused here)
   // w is made wave-uniform (an SGPR) so that branches on it are scalar: an
   // MFMA under an EXEC-masked branch still writes every lane.
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
@@ -276,32 +310,29 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_seg_state_mfma(const 
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
   const int64_t r1 = min(N, r0 + seg_len);
-  const bf16_t* kh = k + bh * N * DIM;
-  const bf16_t* vh = v + bh * N * DIM;
+  const int64_t hbytes = N * DIM * 2;
+  const rsrc_t rk = make_rsrc(k + bh * N * DIM, hbytes), rv = make_rsrc(v + bh * N * DIM, hbytes);
   f32x4_t Sacc[DT][NTL];
   f32x4_t zacc[DT];
   f32x4_t uacc[NTL];  // column sums of V: lane holds U[16n + li]
-  init_state<DIM>(Sacc, zacc, nullptr, w, g, li);
+  init_state<DIM, NW>(Sacc, zacc, nullptr, w, g, li);
 #pragma unroll
   for (int n = 0; n < NTL; ++n) uacc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const short one = 0x3f80;  // bf16 1.0
   const i16x8 ones = {one, one, one, one, one, one, one, one};
-  int64_t c0 = r0;
-  int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
   i32x4 kraw[PC], vraw[PC];
-  load_tile<DIM>(kraw, kh, c0, nrow);
-  load_tile<DIM>(vraw, vh, c0, nrow);
-  while (c0 < r1) {
-    store_tile_elu<DIM>(sKe, kraw, nrow, sRow);
-    store_tile<DIM, false>(sV, vraw, nrow);
+  // rows past the head's end load as zero (elu(0) = 0, V = 0)
+  bload_tile<DIM, NW>(kraw, rk, static_cast<int>(r0 * DIM * 2));
+  bload_tile<DIM, NW>(vraw, rv, static_cast<int>(r0 * DIM * 2));
+  for (int64_t c0 = r0; c0 < r1; c0 += T) {
+    store_tile_e<DIM, NW>(sKe, kraw);
+    store_tile_v<DIM, NW>(sV, vraw);
     __syncthreads();
-    const int64_t c1 = c0 + T;
-    const int nrow1 = c1 < r1 ? static_cast<int>(min(static_cast<int64_t>(T), r1 - c1)) : 0;
-    if (nrow1 > 0) {
-      load_tile<DIM>(kraw, kh, c1, nrow1);
-      load_tile<DIM>(vraw, vh, c1, nrow1);
+    if (c0 + T < r1) {
+      bload_tile<DIM, NW>(kraw, rk, static_cast<int>((c0 + T) * DIM * 2));
+      bload_tile<DIM, NW>(vraw, rv, static_cast<int>((c0 + T) * DIM * 2));
     }
-    state_update<DIM>(Sacc, zacc, sKe, sV, w, g, li);
+    state_update<DIM, NW>(Sacc, zacc, sKe, sV, w, g, li);
 #pragma unroll
     for (int s = 0; s < T / 32; ++s) {
       const int jr = 32 * s + 8 * g + li / 4;
@@ -312,8 +343,6 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_seg_state_mfma(const 
                        uacc[n]);
     }
     __syncthreads();
-    c0 = c1;
-    nrow = nrow1;
   }
   const int64_t rec = bh * P + seg;
   const float count = static_cast<float>(r1 - r0);
@@ -330,15 +359,18 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_seg_state_mfma(const 
   }
 }
 
-size_t lds_fwd(int dim) { return (2 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + dim * sizeof(float); }
-size_t lds_seg(int dim) { return 2 * T * (dim + 8) * sizeof(uint16_t) + T * sizeof(float); }
+size_t lds_fwd(int dim) {
+  const int tiles = dim == 128 ? 3 : 2;  // K, V (and phi(Q) with two waves per query tile)
+  return (tiles * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + dim * sizeof(float);
+}
+size_t lds_seg(int dim) { return 2 * T * (dim + 8) * sizeof(uint16_t); }
 
-#define LA_MLAUNCH(kernel, grid, lds, st, ...)                                                          \
+#define LA_MLAUNCH(kernel, nthreads, grid, lds, st, ...)                                                \
   do {                                                                                                  \
     hipError_t e_ = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),                          \
                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)); \
     if (e_ != hipSuccess) return e_;                                                                    \
-    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(NT), lds, st, __VA_ARGS__);      \
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(nthreads), lds, st, __VA_ARGS__); \
     return hipGetLastError();                                                                           \
   } while (0)
 
@@ -357,12 +389,12 @@ hipError_t launch_forward_mfma(int causal, const SegGeom& g, const void* q, cons
   const bf16_t* V = static_cast<const bf16_t*>(v);
   bf16_t* O = static_cast<bf16_t*>(out);
   if (g.D == 64) {
-    if (causal) LA_MLAUNCH((k_fwd_mfma<64, true>), grid, lds_fwd(64), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
-    LA_MLAUNCH((k_fwd_mfma<64, false>), grid, lds_fwd(64), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
+    if (causal) LA_MLAUNCH((k_fwd_mfma<64, true>), 64 * kFwdWaves<64>, grid, lds_fwd(64), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
+    LA_MLAUNCH((k_fwd_mfma<64, false>), 64 * kFwdWaves<64>, grid, lds_fwd(64), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
   }
   if (g.D == 128) {
-    if (causal) LA_MLAUNCH((k_fwd_mfma<128, true>), grid, lds_fwd(128), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
-    LA_MLAUNCH((k_fwd_mfma<128, false>), grid, lds_fwd(128), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
+    if (causal) LA_MLAUNCH((k_fwd_mfma<128, true>), 64 * kFwdWaves<128>, grid, lds_fwd(128), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
+    LA_MLAUNCH((k_fwd_mfma<128, false>), 64 * kFwdWaves<128>, grid, lds_fwd(128), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
   }
   return hipErrorNotSupported;
 }
@@ -373,10 +405,10 @@ hipError_t launch_seg_state_mfma(const SegGeom& g, const void* k, const void* v,
   const bf16_t* K = static_cast<const bf16_t*>(k);
   const bf16_t* V = static_cast<const bf16_t*>(v);
   if (g.D == 64)
-    LA_MLAUNCH((k_seg_state_mfma<64>), grid, lds_seg(64), st, K, V, s_out, s_stride, z_out, z_stride, g.N, g.P,
+    LA_MLAUNCH((k_seg_state_mfma<64>), 64 * kFwdWaves<64>, grid, lds_seg(64), st, K, V, s_out, s_stride, z_out, z_stride, g.N, g.P,
                g.seg_len);
   if (g.D == 128)
-    LA_MLAUNCH((k_seg_state_mfma<128>), grid, lds_seg(128), st, K, V, s_out, s_stride, z_out, z_stride, g.N,
+    LA_MLAUNCH((k_seg_state_mfma<128>), 64 * kFwdWaves<128>, grid, lds_seg(128), st, K, V, s_out, s_stride, z_out, z_stride, g.N,
                g.P, g.seg_len);
   return hipErrorNotSupported;
 }

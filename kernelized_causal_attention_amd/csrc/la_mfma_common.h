@@ -133,36 +133,38 @@ __device__ __forceinline__ void bstore4(rsrc_t r, float v, int voff, int soff) {
 constexpr int kNT = 256;  // threads per workgroup (4 wave64s)
 constexpr int kT = 64;    // tokens per chunk
 
-template <int DIM>
+// NW wave64s per workgroup (4, or 8 for the D = 128 forward kernels).
+template <int DIM, int NW = 4>
 struct Geo {
+  static constexpr int NT = 64 * NW;            // threads per workgroup
   static constexpr int LD = DIM + 8;            // padded LDS row stride (elements)
   static constexpr int NTL = DIM / 16;          // 16-wide tiles along D (= M)
-  static constexpr int KS = DIM / 32;             // 32-deep k-steps along D (= M)
-  static constexpr int PC = kT * DIM / 8 / kNT; // 16-byte pieces per thread per T x DIM tile
-  static constexpr int DT = NTL / 4;            // state row tiles owned by each wave
-  static constexpr int ROW8 = DIM / 8;            // 16-byte pieces per row
+  static constexpr int KS = DIM / 32;           // 32-deep k-steps along D (= M)
+  static constexpr int PC = kT * DIM / 8 / NT;  // 16-byte pieces per thread per T x DIM tile
+  static constexpr int DT = NTL / NW;           // state row tiles owned by each wave
+  static constexpr int ROW8 = DIM / 8;          // 16-byte pieces per row
 };
 
 // Global -> registers: thread's pieces of a T x DIM token-major tile.
-template <int DIM>
-__device__ __forceinline__ void load_tile(i32x4 (&raw)[Geo<DIM>::PC], const bf16_t* __restrict__ src,
+template <int DIM, int NW = 4>
+__device__ __forceinline__ void load_tile(i32x4 (&raw)[(Geo<DIM, NW>::PC)], const bf16_t* __restrict__ src,
                                           int64_t c0, int nrow) {
-  using G = Geo<DIM>;
+  using G = Geo<DIM, NW>;
 #pragma unroll
   for (int r = 0; r < G::PC; ++r) {
-    const int p = threadIdx.x + kNT * r;
+    const int p = threadIdx.x + G::NT * r;
     const int j = p / G::ROW8, c8 = p % G::ROW8;
     raw[r] = j < nrow ? gload16(src + (c0 + j) * DIM + c8 * 8) : i32x4{0, 0, 0, 0};
   }
 }
 
 // Registers -> LDS (phi applied when asked); rows past nrow are zero.
-template <int DIM, bool PHI>
-__device__ __forceinline__ void store_tile(uint16_t* lds, const i32x4 (&raw)[Geo<DIM>::PC], int nrow) {
-  using G = Geo<DIM>;
+template <int DIM, bool PHI, int NW = 4>
+__device__ __forceinline__ void store_tile(uint16_t* lds, const i32x4 (&raw)[(Geo<DIM, NW>::PC)], int nrow) {
+  using G = Geo<DIM, NW>;
 #pragma unroll
   for (int r = 0; r < G::PC; ++r) {
-    const int p = threadIdx.x + kNT * r;
+    const int p = threadIdx.x + G::NT * r;
     const int j = p / G::ROW8, c8 = p % G::ROW8;
     i16x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
     if (j < nrow) val = PHI ? phi8(raw[r]) : __builtin_bit_cast(i16x8, raw[r]);
@@ -201,12 +203,12 @@ __device__ __forceinline__ void store_tile_elu(uint16_t* lds, const i32x4 (&raw)
 
 // Buffer versions of load_tile / load_q: `soff` is the chunk's first row in
 // bytes; rows past the head's end read as zero.
-template <int DIM>
-__device__ __forceinline__ void bload_tile(i32x4 (&raw)[Geo<DIM>::PC], rsrc_t src, int soff) {
-  using G = Geo<DIM>;
+template <int DIM, int NW = 4>
+__device__ __forceinline__ void bload_tile(i32x4 (&raw)[(Geo<DIM, NW>::PC)], rsrc_t src, int soff) {
+  using G = Geo<DIM, NW>;
 #pragma unroll
   for (int r = 0; r < G::PC; ++r) {
-    const int p = threadIdx.x + kNT * r;
+    const int p = threadIdx.x + G::NT * r;
     raw[r] = bload16(src, ((p / G::ROW8) * DIM + (p % G::ROW8) * 8) * 2, soff);
   }
 }
@@ -218,12 +220,12 @@ __device__ __forceinline__ void bload_q(i32x4 (&raw)[Geo<DIM>::KS], rsrc_t src, 
 
 // Registers -> LDS as bf16 elu(x) for tiles whose rows past the end were
 // loaded as zero (elu(0) = 0, so no row guard is needed).
-template <int DIM>
-__device__ __forceinline__ void store_tile_e(uint16_t* lds, const i32x4 (&raw)[Geo<DIM>::PC]) {
-  using G = Geo<DIM>;
+template <int DIM, int NW = 4>
+__device__ __forceinline__ void store_tile_e(uint16_t* lds, const i32x4 (&raw)[(Geo<DIM, NW>::PC)]) {
+  using G = Geo<DIM, NW>;
 #pragma unroll
   for (int r = 0; r < G::PC; ++r) {
-    const int p = threadIdx.x + kNT * r;
+    const int p = threadIdx.x + G::NT * r;
     f32x8_t x = unpack8(__builtin_bit_cast(i16x8, raw[r]));
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = elu_fast(x[e]);
@@ -232,12 +234,12 @@ __device__ __forceinline__ void store_tile_e(uint16_t* lds, const i32x4 (&raw)[G
 }
 
 // Registers -> LDS unchanged (rows past the end already zero).
-template <int DIM>
-__device__ __forceinline__ void store_tile_v(uint16_t* lds, const i32x4 (&raw)[Geo<DIM>::PC]) {
-  using G = Geo<DIM>;
+template <int DIM, int NW = 4>
+__device__ __forceinline__ void store_tile_v(uint16_t* lds, const i32x4 (&raw)[(Geo<DIM, NW>::PC)]) {
+  using G = Geo<DIM, NW>;
 #pragma unroll
   for (int r = 0; r < G::PC; ++r) {
-    const int p = threadIdx.x + kNT * r;
+    const int p = threadIdx.x + G::NT * r;
     *reinterpret_cast<i16x8*>(lds + (p / G::ROW8) * G::LD + (p % G::ROW8) * 8) = __builtin_bit_cast(i16x8, raw[r]);
   }
 }
