@@ -21,6 +21,10 @@ hipError_t launch_forward_mfma(int causal, const SegGeom& g, const void* q, cons
                                void* out, float* den_out, const float* carry, hipStream_t st);
 hipError_t launch_seg_state_mfma(const SegGeom& g, const void* k, const void* v, float* s_out,
                                  int64_t s_stride, float* z_out, int64_t z_stride, hipStream_t st);
+hipError_t launch_forward_f32mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
+                                  void* out, float* den_out, const float* carry, hipStream_t st);
+hipError_t launch_seg_state_f32mfma(const SegGeom& g, const void* k, const void* v, float* s_out,
+                                    int64_t s_stride, float* z_out, int64_t z_stride, hipStream_t st);
 hipError_t launch_bwd_dq_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
                               const void* dout, const float* carry_s, void* dq, float* r_agg, float* c_out,
                               float* den_out, hipStream_t st);
@@ -302,7 +306,10 @@ hipError_t seg_state(int dtype, const Plan& p, const la::SegGeom& gbase, const v
   const int64_t E = la::state_elems(gbase.D, gbase.M);
   float* z = recs + static_cast<int64_t>(gbase.D) * gbase.M;
   if (p.kernel == LA_KERNEL_MFMA)
-    return timed("mfma.seg_state", st, [&] { return la::launch_seg_state_mfma(gbase, k, v, recs, E, z, E, st); });
+    return timed("mfma.seg_state", st, [&] {
+      return dtype == LA_F32 ? la::launch_seg_state_f32mfma(gbase, k, v, recs, E, z, E, st)
+                             : la::launch_seg_state_mfma(gbase, k, v, recs, E, z, E, st);
+    });
   la::SegGeom g = gbase;
   g.chunk = la::generic_chunk_for(g.D, g.M, 1);
   return timed("generic.seg_state", st,
@@ -315,7 +322,10 @@ hipError_t fwd_pass(int dtype, int causal, const Plan& p, const la::SegGeom& gba
   const char* name = out ? kname(p.kernel, "generic.forward", "mfma.forward")
                          : kname(p.kernel, "generic.forward_den", "mfma.forward_den");
   if (p.kernel == LA_KERNEL_MFMA)
-    return timed(name, st, [&] { return la::launch_forward_mfma(causal, gbase, q, k, v, out, den_out, carry, st); });
+    return timed(name, st, [&] {
+      return dtype == LA_F32 ? la::launch_forward_f32mfma(causal, gbase, q, k, v, out, den_out, carry, st)
+                             : la::launch_forward_mfma(causal, gbase, q, k, v, out, den_out, carry, st);
+    });
   la::SegGeom g = gbase;
   g.chunk = std::min(p.chunk, la::generic_chunk_for(g.D, g.M, 0));
   return timed(name, st,
@@ -657,7 +667,10 @@ LA_API la_status la_prefix_state(const void* k, const void* v, float* S, float* 
   hipError_t e;
   if (p.P == 1) {
     if (p.kernel == LA_KERNEL_MFMA)
-      return dev(timed("mfma.seg_state", stream, [&] { return la::launch_seg_state_mfma(g, k, v, S, D * M, Z, D, stream); }),
+      return dev(timed("mfma.seg_state", stream, [&] {
+                   return dtype == LA_F32 ? la::launch_seg_state_f32mfma(g, k, v, S, D * M, Z, D, stream)
+                                          : la::launch_seg_state_mfma(g, k, v, S, D * M, Z, D, stream);
+                 }),
                  "prefix state");
     la::SegGeom gs = g;
     gs.chunk = la::generic_chunk_for(g.D, g.M, 1);

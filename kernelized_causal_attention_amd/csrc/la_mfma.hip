@@ -377,7 +377,10 @@ size_t lds_seg(int dim) { return 2 * T * (dim + 8) * sizeof(uint16_t); }
 }  // namespace
 
 int mfma_supported(int op, int64_t D, int64_t M, int dtype) {
-  if (dtype != 1 || D != M || (D != 64 && D != 128)) return 0;
+  if (D != M) return 0;
+  // fp32 (v_mfma_f32_16x16x4_f32): forward and prefix state at D = M = 64
+  if (dtype == 0) return D == 64 && (op == 0 /* forward */ || op == 2 /* prefix state */);
+  if (dtype != 1 || (D != 64 && D != 128)) return 0;
   return op == 0 /* forward */ || op == 1 /* backward */ || op == 2 /* prefix state */;
 }
 

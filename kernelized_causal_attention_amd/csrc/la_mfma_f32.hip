@@ -1,0 +1,311 @@
+// fp32 MFMA kernels for the chunked forward and the segment states (gfx950),
+// D = M = 64, fp32 inputs and outputs.
+//
+// Same method and schedule as the bf16 kernels ("[Paper walkthrough]
+// Transformers are RNNs", wkq9411.github.io, sections 2 and 3: phi = elu + 1,
+// S_i, Z_i, eq:output; non-causal eq:linear), on v_mfma_f32_16x16x4_f32, so
+// every operand stays fp32 and nothing is rounded to a narrower type.
+// Lane layout (l = lane, g = l / 16, li = l % 16; measured on the hardware):
+//   A operand A[li][g], B operand B[g][li] (one fp32 each),
+//   C / D     C[4g + u][li], u = 0..3.
+// The contraction index of each product is permuted freely (the same on
+// both operands): along D, the MFMA step s and lane group g take feature
+// 16g + s, so a lane's 16 features sit contiguously in LDS; along tokens the
+// scores' accumulator layout (four consecutive keys per lane) is used as is.
+#include "la_internal.h"
+#include "la_mfma_common.h"
+
+namespace la {
+namespace {
+
+using namespace mf;
+
+constexpr int NT = kNT;
+constexpr int T = kT;
+constexpr int DF = 64;        // D = M
+constexpr int LDF = DF + 4;   // fp32 LDS row stride (keeps 16-byte rows aligned)
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+// Global fp32 [T x 64] tile -> LDS (phi applied when asked); rows past nrow
+// are zero.  256 threads, four 16-byte pieces each.
+template <bool PHI>
+__device__ __forceinline__ void stage_f32(float* lds, int nrow, const f32x4 (&raw)[4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int p = threadIdx.x + NT * r;
+    const int j = p / 16, c4 = p % 16;
+    f32x4 x = raw[r];
+    if (j < nrow) {
+      if (PHI) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = phi_f(x[e]);
+      }
+    } else {
+      x = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    *reinterpret_cast<f32x4*>(lds + j * LDF + 4 * c4) = x;
+  }
+}
+
+__device__ __forceinline__ void load_f32(f32x4 (&raw)[4], const float* __restrict__ src, int64_t c0, int nrow) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int p = threadIdx.x + NT * r;
+    const int j = p / 16, c4 = p % 16;
+    raw[r] = j < nrow ? *reinterpret_cast<const f32x4*>(src + (c0 + j) * DF + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// State update for this wave's 16 state rows d = 16w + (row): S[d][m] +=
+// sum_j phi(K_j)[d] V_j[m], Z[d] += sum_j phi(K_j)[d] (64 keys, j = 16g + s).
+// Sacc[n] holds S[16w + 4g + u][16n + li]; zacc holds Z[16w + 4g + u].
+__device__ __forceinline__ void state_update_f32(f32x4_t (&Sacc)[4], f32x4_t& zacc, const float* sKf,
+                                                 const float* sV, int w, int g, int li) {
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int j = 16 * g + s;
+    const float a = sKf[j * LDF + 16 * w + li];
+    zacc = mfma4(a, 1.f, zacc);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) Sacc[n] = mfma4(a, sV[j * LDF + 16 * n + li], Sacc[n]);
+  }
+}
+
+__device__ __forceinline__ void write_state_f32(float* sS, float* sZ, const f32x4_t (&Sacc)[4], const f32x4_t& zacc,
+                                                int w, int g, int li) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int d = 16 * w + 4 * g + u;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) sS[d * LDF + 16 * n + li] = Sacc[n][u];
+    if (li == 0) sZ[d] = zacc[u];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Forward.  Wave w owns query rows 16w .. 16w + 15 of each 64-token chunk.
+// ---------------------------------------------------------------------------
+template <bool CAUSAL>
+__global__ __launch_bounds__(NT, 2) void k_fwd_f32mfma(const float* __restrict__ q, const float* __restrict__ k,
+                                                       const float* __restrict__ v, float* __restrict__ out,
+                                                       float* __restrict__ den_out, const float* __restrict__ carry,
+                                                       int64_t N, int P, int seg_len) {
+  extern __shared__ __align__(16) float smf[];
+  float* sKf = smf;
+  float* sV = sKf + T * LDF;
+  float* sQf = sV + T * LDF;
+  float* sS = sQf + T * LDF;
+  float* sZ = sS + DF * LDF;
+  // w is wave-uniform (an SGPR): an MFMA under an EXEC-masked branch would
+  // still write every lane.
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.x / P;
+  const int seg = blockIdx.x % P;
+  const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
+  const int64_t r1 = min(N, r0 + seg_len);
+  constexpr int64_t E = static_cast<int64_t>(DF) * DF + DF;
+  const float* cs = carry ? (CAUSAL ? carry + (bh * P + seg) * E : carry + bh * E) : nullptr;
+  const float* qh = q + bh * N * DF;
+  const float* kh = k + bh * N * DF;
+  const float* vh = v + bh * N * DF;
+  float* oh = out ? out + bh * N * DF : nullptr;
+  float* dh = den_out ? den_out + bh * N : nullptr;
+  const int i = 16 * w + li;
+
+  f32x4_t Sacc[4], zacc;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int d = 16 * w + 4 * g + u;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) Sacc[n][u] = cs ? cs[d * DF + 16 * n + li] : 0.f;
+    zacc[u] = cs ? cs[DF * DF + d] : 0.f;
+  }
+  write_state_f32(sS, sZ, Sacc, zacc, w, g, li);
+
+  int64_t c0 = r0;
+  int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
+  f32x4 kraw[4], vraw[4], qraw[4];
+  if (CAUSAL) {
+    load_f32(kraw, kh, c0, nrow);
+    load_f32(vraw, vh, c0, nrow);
+  }
+  load_f32(qraw, qh, c0, nrow);
+  while (c0 < r1) {
+    if (CAUSAL) {
+      stage_f32<true>(sKf, nrow, kraw);
+      stage_f32<false>(sV, nrow, vraw);
+    }
+    stage_f32<true>(sQf, nrow, qraw);
+    __syncthreads();
+    const int64_t c1 = c0 + T;
+    const int nrow1 = c1 < r1 ? static_cast<int>(min(static_cast<int64_t>(T), r1 - c1)) : 0;
+    if (nrow1 > 0) {
+      if (CAUSAL) {
+        load_f32(kraw, kh, c1, nrow1);
+        load_f32(vraw, vh, c1, nrow1);
+      }
+      load_f32(qraw, qh, c1, nrow1);
+    }
+    // this lane's phi(Q_i) features 16g .. 16g + 15
+    float qv[16];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(sQf + i * LDF + 16 * g + 4 * s4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[4 * s4 + e] = x[e];
+    }
+    // scores A^T[j][i] for key tiles t <= w, masked j <= i
+    f32x4_t at[4];
+    float rs = 0.f;
+    if (CAUSAL) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        at[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (t <= w) {
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) {
+            const f32x4 kx = *reinterpret_cast<const f32x4*>(sKf + (16 * t + li) * LDF + 16 * g + 4 * s4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) at[t] = mfma4(kx[e], qv[4 * s4 + e], at[t]);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (t == w && 4 * g + u > li) at[t][u] = 0.f;
+            rs += at[t][u];
+          }
+        }
+      }
+    }
+    // den = sum_j A_ij + phi(Q_i) . Z
+    float di = 0.f;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) di += qv[s] * sZ[16 * g + s];
+    const float den = shfl_sum_groups(rs + di);
+    // O^T[m][i] = sum_d S[d][m] phi(Q_i)[d] + sum_j V[j][m] A^T[j][i]
+    f32x4_t o[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 16; ++s) o[n] = mfma4(sS[(16 * g + s) * LDF + 16 * n + li], qv[s], o[n]);
+    }
+    if (CAUSAL) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t <= w) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int j = 16 * t + 4 * g + u;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) o[n] = mfma4(sV[j * LDF + 16 * n + li], at[t][u], o[n]);
+          }
+        }
+      }
+    }
+    if (i < nrow) {
+      if (oh) {
+        const float inv = 1.f / den;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) *reinterpret_cast<f32x4*>(oh + (c0 + i) * DF + 16 * n + 4 * g) = o[n] * inv;
+      }
+      if (dh && g == 0) dh[c0 + i] = den;
+    }
+    if (CAUSAL) state_update_f32(Sacc, zacc, sKf, sV, w, g, li);
+    __syncthreads();
+    if (CAUSAL) write_state_f32(sS, sZ, Sacc, zacc, w, g, li);
+    c0 = c1;
+    nrow = nrow1;
+  }
+}
+
+// Segment aggregates dS = phi(K)^T V, dZ = colsum phi(K) over one segment.
+__global__ __launch_bounds__(NT, 2) void k_seg_state_f32mfma(const float* __restrict__ k, const float* __restrict__ v,
+                                                             float* __restrict__ s_out, int64_t s_stride,
+                                                             float* __restrict__ z_out, int64_t z_stride, int64_t N,
+                                                             int P, int seg_len) {
+  extern __shared__ __align__(16) float smf[];
+  float* sKf = smf;
+  float* sV = sKf + T * LDF;
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.x / P;
+  const int seg = blockIdx.x % P;
+  const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
+  const int64_t r1 = min(N, r0 + seg_len);
+  const float* kh = k + bh * N * DF;
+  const float* vh = v + bh * N * DF;
+  f32x4_t Sacc[4] = {}, zacc = {0.f, 0.f, 0.f, 0.f};
+  int64_t c0 = r0;
+  int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
+  f32x4 kraw[4], vraw[4];
+  load_f32(kraw, kh, c0, nrow);
+  load_f32(vraw, vh, c0, nrow);
+  while (c0 < r1) {
+    stage_f32<true>(sKf, nrow, kraw);
+    stage_f32<false>(sV, nrow, vraw);
+    __syncthreads();
+    const int64_t c1 = c0 + T;
+    const int nrow1 = c1 < r1 ? static_cast<int>(min(static_cast<int64_t>(T), r1 - c1)) : 0;
+    if (nrow1 > 0) {
+      load_f32(kraw, kh, c1, nrow1);
+      load_f32(vraw, vh, c1, nrow1);
+    }
+    state_update_f32(Sacc, zacc, sKf, sV, w, g, li);
+    __syncthreads();
+    c0 = c1;
+    nrow = nrow1;
+  }
+  const int64_t rec = bh * P + seg;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int d = 16 * w + 4 * g + u;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) s_out[rec * s_stride + d * DF + 16 * n + li] = Sacc[n][u];
+    if (li == 0) z_out[rec * z_stride + d] = zacc[u];
+  }
+}
+
+constexpr size_t kLdsFwd = (3 * T * LDF + DF * LDF + DF) * sizeof(float);
+constexpr size_t kLdsSeg = 2 * T * LDF * sizeof(float);
+
+}  // namespace
+
+hipError_t launch_forward_f32mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
+                                  void* out, float* den_out, const float* carry, hipStream_t st) {
+  if (g.D != DF || g.M != DF) return hipErrorNotSupported;
+  const dim3 grid(static_cast<unsigned>(g.BH * g.P));
+  const float* Q = static_cast<const float*>(q);
+  const float* K = static_cast<const float*>(k);
+  const float* V = static_cast<const float*>(v);
+  float* O = static_cast<float*>(out);
+  const void* kern = causal ? reinterpret_cast<const void*>(k_fwd_f32mfma<true>)
+                            : reinterpret_cast<const void*>(k_fwd_f32mfma<false>);
+  const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsFwd));
+  if (e != hipSuccess) return e;
+  if (causal)
+    hipLaunchKernelGGL((k_fwd_f32mfma<true>), grid, dim3(NT), kLdsFwd, st, Q, K, V, O, den_out, carry, g.N, g.P,
+                       g.seg_len);
+  else
+    hipLaunchKernelGGL((k_fwd_f32mfma<false>), grid, dim3(NT), kLdsFwd, st, Q, K, V, O, den_out, carry, g.N, g.P,
+                       g.seg_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_state_f32mfma(const SegGeom& g, const void* k, const void* v, float* s_out, int64_t s_stride,
+                                    float* z_out, int64_t z_stride, hipStream_t st) {
+  if (g.D != DF || g.M != DF) return hipErrorNotSupported;
+  hipLaunchKernelGGL(k_seg_state_f32mfma, dim3(static_cast<unsigned>(g.BH * g.P)), dim3(NT), kLdsSeg, st,
+                     static_cast<const float*>(k), static_cast<const float*>(v), s_out, s_stride, z_out, z_stride,
+                     g.N, g.P, g.seg_len);
+  return hipGetLastError();
+}
+
+}  // namespace la

@@ -362,6 +362,33 @@ def test_saved_states_rejected_when_too_small():
         la.forward(tq, tk, tv, plan=plan, saved=small)
 
 
+F32_MFMA_SHAPES = [(1, 1, 1, 64), (1, 2, 63, 64), (2, 1, 64, 64), (1, 1, 65, 64), (2, 3, 333, 64),
+                   (1, 2, 1000, 64)]
+
+
+@pytest.mark.parametrize("shape", F32_MFMA_SHAPES)
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("segments", [1, 3])
+def test_f32_mfma_forward(shape, causal, segments):
+    # fp32 operands on v_mfma_f32_16x16x4_f32: held to the fp32 tolerance
+    B, H, N, D = shape
+    plan = dict(kernel=2, segments=segments)
+    assert la.resolve_plan("forward", B, H, N, D, D, causal, "f32", plan)["kernel"] == 2
+    tq, tk, tv, _ = host_case(B, H, N, D, D, "f32", seed=N + D + segments + 7, scale=1.0 / np.sqrt(D))
+    check_forward(tq, tk, tv, causal, "f32", plan=plan)
+
+
+def test_f32_mfma_forward_unscaled_and_prefix_state():
+    tq, tk, tv, _ = host_case(2, 2, 700, 64, 64, "f32", seed=71, scale=1.0)
+    check_forward(tq, tk, tv, True, "f32", plan=dict(kernel=2))
+    check_forward(tq, tk, tv, False, "f32", plan=dict(kernel=2))
+    S, Z = la.prefix_state(tk, tv)
+    torch.cuda.synchronize()
+    S0, Z0 = oracle.prefix_state(f64(tk), f64(tv))
+    assert rel_l2(f64(S), S0) < 1e-6
+    assert rel_l2(f64(Z), Z0) < 1e-6
+
+
 def test_mfma_matches_generic_bf16():
     # two independent kernel families on the same inputs
     tq, tk, tv, tg = host_case(2, 2, 500, 64, 64, "bf16", seed=42, scale=0.125)
