@@ -75,7 +75,11 @@ def quadratic(q, k, v, log_gamma, S0=None):
     q, k, v, lg = _f64(q), _f64(k), _f64(v), _f64(log_gamma)
     n = q.shape[-2]
     L = np.cumsum(lg, axis=-1)
-    decay = np.exp(L[..., :, None] - L[..., None, :]) * np.tril(np.ones((n, n)))
+    # only the terms j <= i exist: exp(L_i - L_j) there (an exponent <= 0);
+    # the masked entries are not formed (they would overflow for long gated
+    # sequences and turn 0 * inf into NaN)
+    keep = np.tril(np.ones((n, n), dtype=bool))
+    decay = np.where(keep, np.exp(np.where(keep, L[..., :, None] - L[..., None, :], 0.0)), 0.0)
     w = (q @ np.swapaxes(k, -1, -2)) * decay
     y = w @ v
     if S0 is not None:

@@ -45,6 +45,16 @@ def test_constant_inputs_closed_form():
     np.testing.assert_allclose(y[:, 0], (1 - gam ** (t + 1)) / (1 - gam), rtol=1e-12)
 
 
+def test_long_strongly_gated_sequence_stays_finite():
+    # cumulative log decay far below the exponent range: only the current
+    # and the few latest tokens matter, and the masked sum must not overflow
+    q, k, v, _ = numpy_inputs(1, 1, 3000, 3, 2, seed=66, scale=1.0)
+    lg = np.full((1, 1, 3000), math.log(0.05))
+    y = ret.quadratic(q, k, v, lg)
+    assert np.isfinite(y).all()
+    np.testing.assert_allclose(y, ret.recurrent(q, k, v, lg)[0], rtol=1e-10, atol=1e-12)
+
+
 def test_zero_decay_keeps_only_the_current_token():
     q, k, v, _ = numpy_inputs(1, 2, 9, 4, 3, seed=51, scale=1.0)
     y = ret.recurrent(q, k, v, np.full((1, 2, 9), -800.0))[0]
@@ -142,7 +152,7 @@ RET_MUTANTS = {
     "decay_after_update": (
         "S = np.exp(lg[..., t])[..., None, None] * S + k[..., t, :, None] * v[..., t, None, :]\n        y[",
         "S = np.exp(lg[..., t])[..., None, None] * (S + k[..., t, :, None] * v[..., t, None, :])\n        y["),
-    "decay_exponent_sign": ("np.exp(L[..., :, None] - L[..., None, :])", "np.exp(L[..., None, :] - L[..., :, None])"),
+    "decay_exponent_sign": ("L[..., :, None] - L[..., None, :], 0.0)", "L[..., None, :] - L[..., :, None], 0.0)"),
     "state_not_decayed_in_quadratic": ("y = y + np.exp(L)[..., None] * (q @ _f64(S0))", "y = y + (q @ _f64(S0))"),
     "forward_cumsum_for_gates": ("dlg = np.flip(np.cumsum(np.flip(per_token, -1), -1), -1)",
                                  "dlg = np.cumsum(per_token, -1)"),
