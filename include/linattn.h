@@ -64,7 +64,9 @@ typedef enum la_op {
   LA_OP_PREFIX_STATE = 2,
   LA_OP_DECODE = 3,
   LA_OP_FORWARD_STATE = 4,  /* la_forward_state  */
-  LA_OP_BACKWARD_STATE = 5  /* la_backward_state */
+  LA_OP_BACKWARD_STATE = 5, /* la_backward_state */
+  LA_OP_RETENTION_FORWARD = 6,  /* la_retention_forward  */
+  LA_OP_RETENTION_BACKWARD = 7  /* la_retention_backward */
 } la_op;
 
 /* Kernel family choice for the *_ex entry points (0 = automatic). */
@@ -179,6 +181,28 @@ la_status la_backward_state(const void* q, const void* k, const void* v, const v
                             void* dq, void* dk, void* dv, float* dS0, float* dZ0,
                             int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Decayed / gated linear attention ("retention"): "08 - Transformer and
+ * Variants" (by-xin.github.io), section 1.3.4 -- RetNet's H_t = gamma
+ * H_{t-1} + v_t k_t^T, y_t = H_t q_t, and gated retention with a per-token
+ * gamma_t; no feature map and no normaliser, as printed.  The state is
+ * stored as S = H^T [B,H,D,M] fp32 (S_t = gamma_t S_{t-1} + k_t v_t^T,
+ * y_t = S_t^T q_t), so
+ *   y_i = sum_{j<=i} exp(L_i - L_j) (q_i . k_j) v_j + exp(L_i) S0^T q_i,
+ *   L_i = sum_{l<=i} log gamma_l.
+ *   q, k: [B,H,N,D]; v, y: [B,H,N,M] (bf16, D = M in {64, 128}; other
+ *     shapes and dtypes return LA_ERR_UNSUPPORTED)
+ *   log_gamma: [B,H,N] fp32, log of the decay, <= 0 (RetNet: one value per
+ *     head repeated; gamma = 1 gives the undecayed sum); values below -80
+ *     are taken as -80 (gamma ~ 0, a full reset); NaN propagates
+ *   S0: [B,H,D,M] fp32 state carried in, or NULL (zero);
+ *   S_out: [B,H,D,M] fp32, the state after the N tokens, or NULL; may be S0
+ *     itself (in place).
+ * Workspace from la_workspace_bytes(LA_OP_RETENTION_FORWARD, ...). */
+la_status la_retention_forward(const void* q, const void* k, const void* v, const float* log_gamma,
+                               void* y, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                               int dtype, const float* S0, float* S_out,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* One RNN decode step per (b,h), in place ("Transformers are RNNs"
  * walkthrough, section 4; the state is updated first, then read):

@@ -19,7 +19,7 @@ from ._native import LinAttnError, la_plan  # noqa: F401
 
 __all__ = [
     "forward", "backward", "forward_state", "backward_state", "decode_step", "prefix_state", "workspace_bytes",
-    "saved_bytes", "resolve_plan",
+    "saved_bytes", "resolve_plan", "retention_forward",
     "LinAttnError", "library_path", "version", "profile_enable", "profile_report",
 ]
 
@@ -274,6 +274,38 @@ def backward_state(q, k, v, out, dout, S0=None, Z0=None, den=None, stream=None, 
                                         dS0.data_ptr(), dZ0.data_ptr(), B, H, N, D, M, _dtype_code(q), _ptr(ws), wsz,
                                         _stream(stream)))
     return dq, dk, dv, dS0, dZ0
+
+
+def retention_forward(q, k, v, log_gamma, S0=None, S_out=None, return_state=False, stream=None, workspace=None):
+    """Decayed / gated linear attention: y_t = S_t^T q_t with
+    S_t = gamma_t S_{t-1} + k_t v_t^T (log_gamma [B,H,N] fp32, <= 0; S0 the
+    state carried in or None).  Returns y, and the final state too when
+    return_state (written into S_out when given; S_out=S0 updates in place)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (log_gamma, "log_gamma")):
+        _dev(t, n)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    B, H, N, D = q.shape
+    M = v.shape[3]
+    if log_gamma.dtype != torch.float32 or tuple(log_gamma.shape) != (B, H, N):
+        raise ValueError("log_gamma must be float32 [B,H,N]")
+    for t, n in ((S0, "S0"), (S_out, "S_out")):
+        if t is not None:
+            _dev(t, n)
+            if t.dtype != torch.float32 or tuple(t.shape) != (B, H, D, M):
+                raise ValueError(f"{n} must be float32 [B,H,D,M]")
+    if return_state and S_out is None:
+        S_out = torch.empty((B, H, D, M), dtype=torch.float32, device=q.device)
+    y = torch.empty((B, H, N, M), dtype=q.dtype, device=q.device)
+    lib = _native.load()
+    need = int(lib.la_workspace_bytes(_native.LA_OP_RETENTION_FORWARD, B, H, N, D, M, 1, _dtype_code(q)))
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    _native.check(lib.la_retention_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_gamma.data_ptr(),
+                                           y.data_ptr(), B, H, N, D, M, _dtype_code(q), _ptr(S0), _ptr(S_out),
+                                           _ptr(ws), wsz, _stream(stream)))
+    return (y, S_out) if return_state else y
 
 
 def decode_step(S, Z, q, k, v, out=None, stream=None):

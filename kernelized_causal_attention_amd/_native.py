@@ -16,6 +16,7 @@ LA_OK, LA_ERR_INVALID, LA_ERR_UNSUPPORTED, LA_ERR_DEVICE = 0, 1, 2, 3
 LA_F32, LA_BF16 = 0, 1
 LA_OP_FORWARD, LA_OP_BACKWARD, LA_OP_PREFIX_STATE, LA_OP_DECODE = 0, 1, 2, 3
 LA_OP_FORWARD_STATE, LA_OP_BACKWARD_STATE = 4, 5
+LA_OP_RETENTION_FORWARD, LA_OP_RETENTION_BACKWARD = 6, 7
 LA_KERNEL_AUTO, LA_KERNEL_GENERIC, LA_KERNEL_MFMA = 0, 1, 2
 
 # Every symbol include/linattn.h declares.
@@ -23,7 +24,7 @@ EXPORTS = (
     "la_forward", "la_forward_ex", "la_backward", "la_backward_ex", "la_decode_step",
     "la_prefix_state", "la_workspace_bytes", "la_workspace_bytes_ex", "la_resolve_plan",
     "la_status_str", "la_last_error", "la_version", "la_profile_enable", "la_profile_report",
-    "la_profile_select", "la_saved_bytes", "la_forward_state", "la_backward_state",
+    "la_profile_select", "la_saved_bytes", "la_forward_state", "la_backward_state", "la_retention_forward",
 )
 
 
@@ -67,6 +68,7 @@ def load() -> ctypes.CDLL:
         "la_backward_ex": (bwd[:6] + [fp, sz] + bwd[6:] + [plan_p], i32),
         "la_saved_bytes": ([i64, i64, i64, i64, i64, i32, i32, plan_p], sz),
         "la_forward_state": ([vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, fp, fp, fp, fp, fp, vp, sz, vp], i32),
+        "la_retention_forward": ([vp, vp, vp, fp, vp, i64, i64, i64, i64, i64, i32, fp, fp, vp, sz, vp], i32),
         "la_backward_state": ([vp, vp, vp, vp, vp, fp, fp, fp, vp, vp, vp, fp, fp, i64, i64, i64, i64, i64, i32,
                                vp, sz, vp], i32),
         "la_decode_step": ([fp, fp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp], i32),

@@ -21,6 +21,13 @@ hipError_t launch_forward_mfma(int causal, const SegGeom& g, const void* q, cons
                                void* out, float* den_out, const float* carry, hipStream_t st);
 hipError_t launch_seg_state_mfma(const SegGeom& g, const void* k, const void* v, float* s_out,
                                  int64_t s_stride, float* z_out, int64_t z_stride, hipStream_t st);
+int retention_supported(int64_t D, int64_t M, int dtype);
+hipError_t launch_ret_seg_state(const SegGeom& g, const void* k, const void* v, const float* lg, float* recs,
+                                hipStream_t st);
+hipError_t launch_ret_scan(float* recs, int64_t BH, int P, int D, int M, const float* init, float* tot,
+                           hipStream_t st);
+hipError_t launch_ret_forward(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg, void* y,
+                              const float* carry, hipStream_t st);
 hipError_t launch_forward_f32mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
                                   void* out, float* den_out, const float* carry, hipStream_t st);
 hipError_t launch_seg_state_f32mfma(const SegGeom& g, const void* k, const void* v, float* s_out,
@@ -123,8 +130,9 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
   (void)causal;
   int kernel = req ? req->kernel : LA_KERNEL_AUTO;
   if (kernel < LA_KERNEL_AUTO || kernel > LA_KERNEL_MFMA) return fail(LA_ERR_INVALID, "plan.kernel=%d", kernel);
-  // the state-carrying calls run the forward / backward kernels
-  if (op == LA_OP_FORWARD_STATE) op = LA_OP_FORWARD;
+  // the state-carrying and retention calls use the forward / backward plans
+  if (op == LA_OP_FORWARD_STATE || op == LA_OP_RETENTION_FORWARD) op = LA_OP_FORWARD;
+  if (op == LA_OP_RETENTION_BACKWARD) op = LA_OP_BACKWARD;
   if (op == LA_OP_BACKWARD_STATE) op = LA_OP_BACKWARD;
   // the MFMA kernels address one head's rows with 32-bit buffer offsets
   const int mfma_ok = la::mfma_supported(op, D, M, dtype) && N * std::max(D, M) * 2 < (int64_t(1) << 31);
@@ -192,7 +200,7 @@ WsLayout layout(int op, int64_t BH, int64_t N, int64_t D, int64_t M, int causal,
   Carve c;
   const size_t E = static_cast<size_t>(la::state_elems(static_cast<int>(D), static_cast<int>(M)));
   const size_t recs = static_cast<size_t>(BH) * p.P * E;
-  if (op == LA_OP_FORWARD_STATE) {
+  if (op == LA_OP_FORWARD_STATE || op == LA_OP_RETENTION_FORWARD) {
     w.aggS = c.take(recs);
   } else if (op == LA_OP_FORWARD) {
     if (causal) {
@@ -623,6 +631,58 @@ LA_API la_status la_backward_state(const void* q, const void* k, const void* v, 
   st.Z_out = dZ0;
   return do_backward(q, k, v, out, dout, den, nullptr, 0, dq, dk, dv, B, H, N, D, M, 1, dtype, workspace,
                      workspace_bytes, stream, nullptr, st);
+}
+
+LA_API la_status la_retention_forward(const void* q, const void* k, const void* v, const float* log_gamma,
+                                      void* y, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype,
+                                      const float* S0, float* S_out, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  la_status s = check_sizes(B, H, N, D, M, dtype);
+  if (s != LA_OK) return s;
+  if ((s = check_ptr(q, "q", dtype)) || (s = check_ptr(k, "k", dtype)) || (s = check_ptr(v, "v", dtype)) ||
+      (s = check_ptr(y, "y", dtype)) || (s = check_ptr(log_gamma, "log_gamma", LA_F32)))
+    return s;
+  for (const void* p : {static_cast<const void*>(S0), static_cast<const void*>(S_out)})
+    if (p && (reinterpret_cast<uintptr_t>(p) & 3)) return fail(LA_ERR_INVALID, "state pointers must be 4-byte aligned");
+  if (!la::retention_supported(D, M, dtype))
+    return fail(LA_ERR_UNSUPPORTED, "retention kernels take bf16 with D = M in {64, 128} (D=%lld, M=%lld, dtype %d)",
+                (long long)D, (long long)M, dtype);
+  const int64_t BH = B * H;
+  const size_t es = dtype_size(dtype);
+  Plan p;
+  if ((s = resolve(LA_OP_RETENTION_FORWARD, B, H, N, D, M, 1, dtype, nullptr, &p))) return s;
+  if (p.kernel != LA_KERNEL_MFMA) return fail(LA_ERR_UNSUPPORTED, "sequence too long for the retention kernels");
+  const Span ins[] = {span("q", q, BH * N * D, es), span("k", k, BH * N * D, es), span("v", v, BH * N * M, es),
+                      span("log_gamma", log_gamma, BH * N, 4),
+                      span("workspace", workspace, workspace ? (int64_t)workspace_bytes : 0, 1),
+                      S_out == S0 ? span("S0", nullptr, 0, 4) : span("S0", S0, S0 ? BH * D * M : 0, 4)};
+  const Span outs[] = {span("y", y, BH * N * M, es), span("S_out", S_out, S_out ? BH * D * M : 0, 4)};
+  if ((s = check_disjoint(outs, 2, ins, 6))) return s;
+  if (S_out && S_out == S0) {
+    const Span s0[] = {span("S0", S0, BH * D * M, 4)};
+    if ((s = check_disjoint(outs, 1, s0, 1))) return s;
+  }
+  const WsLayout w = layout(LA_OP_RETENTION_FORWARD, BH, N, D, M, 1, p);
+  if (workspace_bytes < w.bytes)
+    return fail(LA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, w.bytes);
+  if (!workspace) return fail(LA_ERR_INVALID, "workspace is NULL (%zu bytes needed)", w.bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 15) return fail(LA_ERR_INVALID, "workspace must be 16-byte aligned");
+  const la::SegGeom g = geom(BH, N, D, M, p, p.chunk);
+  const float* carry = nullptr;
+  hipError_t e;
+  if (p.P > 1 || S0 || S_out) {
+    // segment aggregates and their decayed scan from S0; the total is the
+    // state after the N tokens
+    float* recs = at(workspace, w.aggS);
+    if ((e = timed("ret.seg_state", stream, [&] { return la::launch_ret_seg_state(g, k, v, log_gamma, recs, stream); })))
+      return dev(e, "retention segment state");
+    if ((e = timed("ret.scan", stream, [&] { return la::launch_ret_scan(recs, BH, p.P, g.D, g.M, S0, S_out, stream); })))
+      return dev(e, "retention scan");
+    carry = recs;
+  }
+  return dev(timed("ret.forward", stream,
+                   [&] { return la::launch_ret_forward(g, q, k, v, log_gamma, y, carry, stream); }),
+             "retention forward");
 }
 
 LA_API la_status la_decode_step(float* S, float* Z, const void* q, const void* k, const void* v, void* out,
