@@ -204,6 +204,20 @@ la_status la_retention_forward(const void* q, const void* k, const void* v, cons
                                int dtype, const float* S0, float* S_out,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Backward of la_retention_forward for L = sum(dy * y), by the chain rule
+ * through the recurrence (the page gives no gradients):
+ *   dq_i = S_i dy_i;  R_j = sum_{i>=j} exp(L_i - L_j) q_i dy_i^T;
+ *   dk_j = R_j v_j;  dv_j = R_j^T k_j;  dS0 = gamma_1 R_1;
+ *   dlog_gamma_t = sum_{m>=t} (q_m . dq_m - k_m . dk_m).
+ *   dq, dk: [B,H,N,D], dv: [B,H,N,M] (dtype); dlog_gamma: [B,H,N] fp32;
+ *   dS0: [B,H,D,M] fp32 or NULL; S0 as given to the forward (or NULL).
+ * Workspace from la_workspace_bytes(LA_OP_RETENTION_BACKWARD, ...). */
+la_status la_retention_backward(const void* q, const void* k, const void* v, const float* log_gamma,
+                                const void* dy, const float* S0, void* dq, void* dk, void* dv,
+                                float* dlog_gamma, float* dS0, int64_t B, int64_t H, int64_t N,
+                                int64_t D, int64_t M, int dtype, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
 /* One RNN decode step per (b,h), in place ("Transformers are RNNs"
  * walkthrough, section 4; the state is updated first, then read):
  *   S <- S + phi(k) v^T;  Z <- Z + phi(k);  out = phi(q)^T S / phi(q)^T Z.

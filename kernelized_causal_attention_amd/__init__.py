@@ -19,7 +19,7 @@ from ._native import LinAttnError, la_plan  # noqa: F401
 
 __all__ = [
     "forward", "backward", "forward_state", "backward_state", "decode_step", "prefix_state", "workspace_bytes",
-    "saved_bytes", "resolve_plan", "retention_forward",
+    "saved_bytes", "resolve_plan", "retention_forward", "retention_backward",
     "LinAttnError", "library_path", "version", "profile_enable", "profile_report",
 ]
 
@@ -105,7 +105,8 @@ def workspace_bytes(op: str, B, H, N, D, M, causal=True, dtype="f32", plan=None)
 
 def resolve_plan(op: str, B, H, N, D, M, causal=True, dtype="f32", plan=None) -> dict:
     ops = {"forward": _native.LA_OP_FORWARD, "backward": _native.LA_OP_BACKWARD,
-           "prefix_state": _native.LA_OP_PREFIX_STATE}
+           "prefix_state": _native.LA_OP_PREFIX_STATE, "retention_forward": _native.LA_OP_RETENTION_FORWARD,
+           "retention_backward": _native.LA_OP_RETENTION_BACKWARD}
     dt = {"f32": _native.LA_F32, "bf16": _native.LA_BF16}[dtype]
     out = la_plan()
     _native.check(_native.load().la_resolve_plan(ops[op], B, H, N, D, M, int(bool(causal)), dt,
@@ -306,6 +307,40 @@ def retention_forward(q, k, v, log_gamma, S0=None, S_out=None, return_state=Fals
                                            y.data_ptr(), B, H, N, D, M, _dtype_code(q), _ptr(S0), _ptr(S_out),
                                            _ptr(ws), wsz, _stream(stream)))
     return (y, S_out) if return_state else y
+
+
+def retention_backward(q, k, v, log_gamma, dy, S0=None, stream=None, workspace=None):
+    """Gradients (dq, dk, dv, dlog_gamma, dS0) of sum(dy * y) for
+    retention_forward (dS0 is returned whether or not S0 was given)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (log_gamma, "log_gamma"), (dy, "dy")):
+        _dev(t, n)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    B, H, N, D = q.shape
+    M = v.shape[3]
+    if dy.shape != v.shape or dy.dtype != q.dtype:
+        raise ValueError("dy must match v")
+    if log_gamma.dtype != torch.float32 or tuple(log_gamma.shape) != (B, H, N):
+        raise ValueError("log_gamma must be float32 [B,H,N]")
+    if S0 is not None:
+        _dev(S0, "S0")
+        if S0.dtype != torch.float32 or tuple(S0.shape) != (B, H, D, M):
+            raise ValueError("S0 must be float32 [B,H,D,M]")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dlg = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    dS0 = torch.empty((B, H, D, M), dtype=torch.float32, device=q.device)
+    lib = _native.load()
+    need = int(lib.la_workspace_bytes(_native.LA_OP_RETENTION_BACKWARD, B, H, N, D, M, 1, _dtype_code(q)))
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    _native.check(lib.la_retention_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_gamma.data_ptr(),
+                                            dy.data_ptr(), _ptr(S0), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                            dlg.data_ptr(), dS0.data_ptr(), B, H, N, D, M, _dtype_code(q), _ptr(ws),
+                                            wsz, _stream(stream)))
+    return dq, dk, dv, dlg, dS0
 
 
 def decode_step(S, Z, q, k, v, out=None, stream=None):

@@ -28,6 +28,9 @@ hipError_t launch_ret_scan(float* recs, int64_t BH, int P, int D, int M, const f
                            hipStream_t st);
 hipError_t launch_ret_forward(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg, void* y,
                               const float* carry, hipStream_t st);
+hipError_t launch_ret_backward(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg,
+                               const void* dy, const float* carry_s, float* r_agg, void* dq, void* dk, void* dv,
+                               float* a, float* dlg, float* dS0, hipStream_t st);
 hipError_t launch_forward_f32mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
                                   void* out, float* den_out, const float* carry, hipStream_t st);
 hipError_t launch_seg_state_f32mfma(const SegGeom& g, const void* k, const void* v, float* s_out,
@@ -131,6 +134,7 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
   int kernel = req ? req->kernel : LA_KERNEL_AUTO;
   if (kernel < LA_KERNEL_AUTO || kernel > LA_KERNEL_MFMA) return fail(LA_ERR_INVALID, "plan.kernel=%d", kernel);
   // the state-carrying and retention calls use the forward / backward plans
+  const int op_in = op;
   if (op == LA_OP_FORWARD_STATE || op == LA_OP_RETENTION_FORWARD) op = LA_OP_FORWARD;
   if (op == LA_OP_RETENTION_BACKWARD) op = LA_OP_BACKWARD;
   if (op == LA_OP_BACKWARD_STATE) op = LA_OP_BACKWARD;
@@ -166,6 +170,10 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
     const int64_t target = kernel == LA_KERNEL_MFMA ? 512 : 1024;
     const int64_t want = (target + BH - 1) / BH;
     P = std::min<int64_t>(want, std::max<int64_t>(1, nunits / 4));
+    // The retention backward anchors its gate gradients at every segment
+    // end; between anchors the rounding of the chunk-crossing terms adds up
+    // like a random walk, so its segments stay within 16 units.
+    if (op_in == LA_OP_RETENTION_BACKWARD) P = std::max<int64_t>(P, (nunits + 15) / 16);
   }
   P = std::max<int64_t>(1, std::min<int64_t>(P, nunits));
   const int64_t seg_units = (nunits + P - 1) / P;
@@ -209,6 +217,10 @@ WsLayout layout(int op, int64_t BH, int64_t N, int64_t D, int64_t M, int causal,
       w.aggS = c.take(recs);
       w.totS = c.take(static_cast<size_t>(BH) * E);
     }
+  } else if (op == LA_OP_RETENTION_BACKWARD) {
+    w.aggS = c.take(recs);
+    w.aggR = c.take(recs);
+    w.den = c.take(static_cast<size_t>(BH) * N);  // per-token q.dq - k.dk
   } else if (op == LA_OP_BACKWARD || op == LA_OP_BACKWARD_STATE) {
     w.aggS = c.take(recs);
     w.totS = c.take(static_cast<size_t>(BH) * E);
@@ -683,6 +695,58 @@ LA_API la_status la_retention_forward(const void* q, const void* k, const void* 
   return dev(timed("ret.forward", stream,
                    [&] { return la::launch_ret_forward(g, q, k, v, log_gamma, y, carry, stream); }),
              "retention forward");
+}
+
+LA_API la_status la_retention_backward(const void* q, const void* k, const void* v, const float* log_gamma,
+                                       const void* dy, const float* S0, void* dq, void* dk, void* dv,
+                                       float* dlog_gamma, float* dS0, int64_t B, int64_t H, int64_t N, int64_t D,
+                                       int64_t M, int dtype, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  la_status s = check_sizes(B, H, N, D, M, dtype);
+  if (s != LA_OK) return s;
+  if ((s = check_ptr(q, "q", dtype)) || (s = check_ptr(k, "k", dtype)) || (s = check_ptr(v, "v", dtype)) ||
+      (s = check_ptr(dy, "dy", dtype)) || (s = check_ptr(log_gamma, "log_gamma", LA_F32)) ||
+      (s = check_ptr(dq, "dq", dtype)) || (s = check_ptr(dk, "dk", dtype)) || (s = check_ptr(dv, "dv", dtype)) ||
+      (s = check_ptr(dlog_gamma, "dlog_gamma", LA_F32)))
+    return s;
+  for (const void* p : {static_cast<const void*>(S0), static_cast<const void*>(dS0)})
+    if (p && (reinterpret_cast<uintptr_t>(p) & 3)) return fail(LA_ERR_INVALID, "state pointers must be 4-byte aligned");
+  if (!la::retention_supported(D, M, dtype))
+    return fail(LA_ERR_UNSUPPORTED, "retention kernels take bf16 with D = M in {64, 128} (D=%lld, M=%lld, dtype %d)",
+                (long long)D, (long long)M, dtype);
+  const int64_t BH = B * H;
+  const size_t es = dtype_size(dtype);
+  Plan p;
+  if ((s = resolve(LA_OP_RETENTION_BACKWARD, B, H, N, D, M, 1, dtype, nullptr, &p))) return s;
+  if (p.kernel != LA_KERNEL_MFMA) return fail(LA_ERR_UNSUPPORTED, "sequence too long for the retention kernels");
+  const Span ins[] = {span("q", q, BH * N * D, es), span("k", k, BH * N * D, es), span("v", v, BH * N * M, es),
+                      span("log_gamma", log_gamma, BH * N, 4), span("dy", dy, BH * N * M, es),
+                      span("S0", S0, S0 ? BH * D * M : 0, 4),
+                      span("workspace", workspace, workspace ? (int64_t)workspace_bytes : 0, 1)};
+  const Span outs[] = {span("dq", dq, BH * N * D, es), span("dk", dk, BH * N * D, es), span("dv", dv, BH * N * M, es),
+                       span("dlog_gamma", dlog_gamma, BH * N, 4), span("dS0", dS0, dS0 ? BH * D * M : 0, 4)};
+  if ((s = check_disjoint(outs, 5, ins, 7))) return s;
+  const WsLayout w = layout(LA_OP_RETENTION_BACKWARD, BH, N, D, M, 1, p);
+  if (workspace_bytes < w.bytes)
+    return fail(LA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, w.bytes);
+  if (!workspace) return fail(LA_ERR_INVALID, "workspace is NULL (%zu bytes needed)", w.bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 15) return fail(LA_ERR_INVALID, "workspace must be 16-byte aligned");
+  const la::SegGeom g = geom(BH, N, D, M, p, p.chunk);
+  float* recs = at(workspace, w.aggS);
+  float* rrec = at(workspace, w.aggR);
+  float* a = at(workspace, w.den);
+  hipError_t e;
+  // the prefix states entering each segment, from S0 (as the forward)
+  if ((e = timed("ret.seg_state", stream, [&] { return la::launch_ret_seg_state(g, k, v, log_gamma, recs, stream); })))
+    return dev(e, "retention segment state");
+  if ((e = timed("ret.scan", stream, [&] { return la::launch_ret_scan(recs, BH, p.P, g.D, g.M, S0, nullptr, stream); })))
+    return dev(e, "retention scan");
+  return dev(timed("ret.backward", stream,
+                   [&] {
+                     return la::launch_ret_backward(g, q, k, v, log_gamma, dy, recs, rrec, dq, dk, dv, a, dlog_gamma,
+                                                    dS0, stream);
+                   }),
+             "retention backward");
 }
 
 LA_API la_status la_decode_step(float* S, float* Z, const void* q, const void* k, const void* v, void* out,

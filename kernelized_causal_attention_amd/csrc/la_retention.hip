@@ -62,6 +62,19 @@ __device__ __forceinline__ void store_tile_scaled(uint16_t* lds, const i32x4 (&r
   }
 }
 
+// Registers -> LDS with row j times exp(b_j) (<= 1).
+template <int DIM>
+__device__ __forceinline__ void store_tile_decay(uint16_t* lds, const i32x4 (&raw)[Geo<DIM>::PC], float b) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int r = 0; r < G::PC; ++r) {
+    const int p = threadIdx.x + NT * r;
+    const int j = p / G::ROW8, c8 = p % G::ROW8;
+    const float s = __expf(__shfl(b, j, 64));
+    *reinterpret_cast<i16x8*>(lds + j * G::LD + c8 * 8) = pack8(unpack8(__builtin_bit_cast(i16x8, raw[r])) * s);
+  }
+}
+
 // S (fp32, this wave's DT row tiles of the state) and its bf16 S^T copy.
 template <int DIM>
 __device__ __forceinline__ void write_st(uint16_t* sST, const f32x4_t (&Sacc)[Geo<DIM>::DT][Geo<DIM>::NTL], int w,
@@ -307,8 +320,495 @@ __global__ __launch_bounds__(NT) void k_ret_scan(float* __restrict__ recs, int P
   if (tot) tot[bh * DM + e] = carry;
 }
 
+// ===========================================================================
+// Backward of L = sum(dy * y), by the chain rule through the recurrence:
+//   dq_i = S_i dy_i,  R_j = sum_{i>=j} exp(L_i - L_j) q_i dy_i^T,
+//   dk_j = R_j v_j,   dv_j = R_j^T k_j,   dS0 = the suffix sum decayed to
+//   before the first token,  d log gamma_t = sum_{m>=t} (q_m.dq_m - k_m.dk_m)
+// (L_m enters row m's terms with + and column m's with -).  Chunked:
+//   dq_i = exp(b_i) S dy_i + sum_{j<=i} exp(b_i - b_j)(dy_i.v_j) k_j
+//   dk_j = exp(b_T - b_j) R v_j + sum_{i>=j} exp(b_i - b_j)(dy_i.v_j) q_i
+//   dv_j = exp(b_T - b_j) R^T k_j + sum_{i>=j} exp(b_i - b_j)(q_i.k_j) dy_i
+//   R (passed to the previous chunk) = exp(b_T) R + sum_i exp(b_i) q_i dy_i^T
+// with S the state before the chunk and R the suffix state decayed to the
+// chunk's last token.
+//
+// d log gamma_t is the sum of the pair terms w_ij = exp(L_i - L_j)(q_i.k_j)
+// (dy_i.v_j) over the pairs i >= t > j that straddle t.  Summing
+// q.dq - k.dk over all later tokens would cancel long runs of large terms
+// computed through different bf16 roundings, so it is formed as
+//   d log gamma_t = Y + sum_{t <= m < segment end} a_m,
+//   a_m = p_m + rowsum_m - colsum_m - r_m,
+// Y = <S, R> at the segment's end (the straddling pairs there, from the fp32
+// state records), p_m = exp(b_m) q_m^T S dy_m (pairs into the chunk from
+// before it), r_m = exp(b_T - b_m) k_m^T R v_m (pairs out of the chunk), and
+// the in-chunk pairs' row and column sums from fp32 w_ij.
+// ===========================================================================
+
+// X^T layout for the suffix state (as in the linear-attention backward):
+// lane holds X[d = 16n + li][m = 16mt + 4g + u], mt = w DT + a.
+// X^T[m][d] += sum_j A[j][m] B[j][d] over the chunk's 64 tokens.
+template <int DIM>
+__device__ __forceinline__ void outer_xt(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], const uint16_t* sA,
+                                         const uint16_t* sB, int w, int g, int li) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int s = 0; s < T / 32; ++s) {
+    const int jr = 32 * s + 8 * g + li / 4;
+    const int cc = 4 * (li % 4);
+    i16x8 aop[G::DT];
+#pragma unroll
+    for (int a = 0; a < G::DT; ++a) {
+      const int mt = w * G::DT + a;
+      aop[a] = cat(lds_tr(sA + jr * G::LD + 16 * mt + cc), lds_tr(sA + (jr + 4) * G::LD + 16 * mt + cc));
+    }
+#pragma unroll
+    for (int n = 0; n < G::NTL; ++n) {
+      const i16x8 b = cat(lds_tr(sB + jr * G::LD + 16 * n + cc), lds_tr(sB + (jr + 4) * G::LD + 16 * n + cc));
+#pragma unroll
+      for (int a = 0; a < G::DT; ++a) X[a][n] = mfma(aop[a], b, X[a][n]);
+    }
+  }
+}
+
+// bf16 row-major X[d][m] into LDS from the X^T accumulators.
+template <int DIM>
+__device__ __forceinline__ void write_x(uint16_t* sX, const f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], int w, int g,
+                                        int li) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int a = 0; a < G::DT; ++a)
+#pragma unroll
+    for (int n = 0; n < G::NTL; ++n)
+      *reinterpret_cast<i16x4*>(sX + (16 * n + li) * G::LD + 16 * (w * G::DT + a) + 4 * g) = pack4(X[a][n]);
+}
+
+template <int DIM>
+__device__ __forceinline__ void init_x(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], const float* __restrict__ src,
+                                       int w, int g, int li) {
+  using G = Geo<DIM>;
+#pragma unroll
+  for (int a = 0; a < G::DT; ++a)
+#pragma unroll
+    for (int n = 0; n < G::NTL; ++n)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        X[a][n][u] = src ? src[(16 * n + li) * DIM + 16 * (w * G::DT + a) + 4 * g + u] : 0.f;
+}
+
+// Own-row tile writes (row i of the chunk, features 8g + 32s + e), scaled.
+template <int DIM>
+__device__ __forceinline__ void put_row(uint16_t* lds, const i32x4 (&raw)[Geo<DIM>::KS], int i, int g, float sc) {
+#pragma unroll
+  for (int s = 0; s < Geo<DIM>::KS; ++s)
+    *reinterpret_cast<i16x8*>(lds + i * Geo<DIM>::LD + 8 * g + 32 * s) =
+        sc == 1.f ? __builtin_bit_cast(i16x8, raw[s]) : pack8(unpack8(__builtin_bit_cast(i16x8, raw[s])) * sc);
+}
+
+// ---------------------------------------------------------------------------
+// Forward sweep: dq, p_i per token (into qdq), and the segment's
+// suffix aggregate dR = sum_i exp(B_i) q_i dy_i^T (B_i: log decay from the
+// segment start through token i) with Lambda in the record's first Z slot.
+// ---------------------------------------------------------------------------
+template <int DIM>
+__global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                 const bf16_t* __restrict__ v, const float* __restrict__ lg,
+                                                 const bf16_t* __restrict__ dy, const float* __restrict__ carry,
+                                                 bf16_t* __restrict__ dq, float* __restrict__ qdq,
+                                                 float* __restrict__ r_agg, int64_t N, int P, int seg_len) {
+  using G = Geo<DIM>;
+  constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* sK = smem;
+  uint16_t* sKs = sK + T * LD;
+  uint16_t* sV = sKs + T * LD;
+  uint16_t* sQ = sV + T * LD;
+  uint16_t* sQs = sQ + T * LD;
+  uint16_t* sG = sQs + T * LD;
+  uint16_t* sS = sG + T * LD;  // bf16 S, row-major [d][m]
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.x / P;
+  const int seg = blockIdx.x % P;
+  const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
+  const int64_t r1 = min(N, r0 + seg_len);
+  constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;
+  const float* cs = carry ? carry + (bh * P + seg) * E : nullptr;
+  const int64_t hoff = bh * N * DIM;
+  const int64_t hbytes = N * DIM * 2;
+  const rsrc_t rq = make_rsrc(q + hoff, hbytes), rk = make_rsrc(k + hoff, hbytes), rv = make_rsrc(v + hoff, hbytes),
+               rg = make_rsrc(dy + hoff, hbytes), rdq = make_rsrc(dq + hoff, hbytes),
+               rl = make_rsrc(lg + bh * N, N * 4);
+  float* qdqh = qdq + bh * N;
+  const int i = 16 * w + li;
+  const int cc = 4 * (li % 4);
+  f32x4_t mt[4];  // causal mask (key j = 16t + 4g + u <= query i) as 0 / 1
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mt[t][u] = (t < w || (t == w && 4 * g + u <= li)) ? 1.f : 0.f;
+
+  f32x4_t Sacc[DT][NTL], Racc[DT][NTL];
+  init_s<DIM>(Sacc, cs, w, g, li);
+  init_x<DIM>(Racc, nullptr, w, g, li);
+  // bf16 S row-major for the S dy product: element (d, m) from the S layout
+  // Sacc[dt][n] = S[16(w DT + dt) + 4g + u][16n + li]
+  auto write_s = [&]() {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int n = 0; n < NTL; ++n)
+          sS[(16 * (w * DT + dt) + 4 * g + u) * LD + 16 * n + li] = static_cast<uint16_t>(bf(Sacc[dt][n][u]));
+  };
+  write_s();
+
+  i32x4 kraw[PC], vraw[PC], qraw[KS], graw[KS];
+  float lgv;
+  auto fetch = [&](int64_t cc0) {
+    const int soff = static_cast<int>(cc0 * DIM * 2);
+    bload_tile<DIM>(kraw, rk, soff);
+    bload_tile<DIM>(vraw, rv, soff);
+    bload_q<DIM>(qraw, rq, soff, i, g);
+    bload_q<DIM>(graw, rg, soff, i, g);
+    lgv = gate(rl, l, cc0);
+  };
+  fetch(r0);
+  float Bc = 0.f;  // log decay from the segment start to before this chunk
+  for (int64_t c0 = r0; c0 < r1; c0 += T) {
+    const float b = wave_incl_scan(lgv);
+    const float bT = __shfl(b, 63, 64);
+    const float bi = __shfl(b, i, 64);
+    store_tile_v<DIM>(sK, kraw);
+    store_tile_scaled<DIM>(sKs, kraw, b, bT);
+    store_tile_v<DIM>(sV, vraw);
+    put_row<DIM>(sQ, qraw, i, g, 1.f);
+    put_row<DIM>(sQs, qraw, i, g, __expf(Bc + bi));
+    put_row<DIM>(sG, graw, i, g, 1.f);
+    i16x8 gq[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) gq[s] = __builtin_bit_cast(i16x8, graw[s]);
+    __syncthreads();
+    const int soff = static_cast<int>(c0 * DIM * 2);
+    const int64_t nrow = min(static_cast<int64_t>(T), r1 - c0);
+    if (c0 + T < r1) fetch(c0 + T);
+
+    // dQ^T[d][i] = exp(b_i) (S dy_i)[d] + sum_j K^T B^T
+    f32x4_t o[NTL];
+    const float di = __expf(bi);
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) {
+      o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) o[n] = mfma(lds8(sS + (16 * n + li) * LD + 8 * g + 32 * s), gq[s], o[n]);
+      o[n] *= di;
+    }
+    // p_i = q_i . exp(b_i) S dy_i (fp32)
+    float qd = 0.f;
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) {
+      const f32x4_t qv = unpack4(*reinterpret_cast<const i16x4*>(sQ + i * LD + 16 * n + 4 * g));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) qd += qv[u] * o[n][u];
+    }
+    qd = shfl_sum_groups(qd);
+    // B^T[j][i] = (v_j . dy_i) exp(b_i - b_j), masked j <= i
+    i16x4 bt[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      if (t <= w) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = mfma(lds8(sV + (16 * t + li) * LD + 8 * g + 32 * s), gq[s], acc);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] *= __expf(fminf(bi - __shfl(b, 16 * t + 4 * g + u, 64), 0.f)) * mt[t][u];
+      }
+      bt[t] = pack4(acc);
+    }
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) {
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp) {
+        if (2 * tp <= w) {
+          const int jr = 32 * tp + 4 * g + li / 4;
+          const i16x8 a = cat(lds_tr(sK + jr * LD + 16 * n + cc), lds_tr(sK + (jr + 16) * LD + 16 * n + cc));
+          o[n] = mfma(a, cat(bt[2 * tp], bt[2 * tp + 1]), o[n]);
+        }
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) bstore8(rdq, pack4(o[n]), (i * DIM + 16 * n + 4 * g) * 2, soff);
+    if (g == 0 && i < nrow) qdqh[c0 + i] = qd;
+    // state and suffix aggregate
+    decay_update<DIM>(Sacc, bT, sKs, sV, w, g, li);
+    outer_xt<DIM>(Racc, sG, sQs, w, g, li);
+    Bc += bT;
+    __syncthreads();
+    write_s();
+  }
+  if (r_agg) {
+    float* rec = r_agg + (bh * P + seg) * E;
+#pragma unroll
+    for (int a = 0; a < DT; ++a)
+#pragma unroll
+      for (int n = 0; n < NTL; ++n)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rec[(16 * n + li) * DIM + 16 * (w * DT + a) + 4 * g + u] = Racc[a][n][u];
+    if (tid == 0) rec[DIM * DIM] = Bc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Reverse sweep: dk, dv; completes a_j = p_j + rowsum_j - colsum_j - r_j in
+// place in qdq.
+// carry_r: the suffix state decayed to the segment's last token (or null).
+// ---------------------------------------------------------------------------
+template <int DIM>
+__global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                   const bf16_t* __restrict__ v, const float* __restrict__ lg,
+                                                   const bf16_t* __restrict__ dy, const float* __restrict__ carry_r,
+                                                   bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
+                                                   float* __restrict__ qdq, int64_t N, int P, int seg_len) {
+  using G = Geo<DIM>;
+  constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* sK = smem;
+  uint16_t* sV = sK + T * LD;
+  uint16_t* sQ = sV + T * LD;
+  uint16_t* sQs = sQ + T * LD;
+  uint16_t* sG = sQs + T * LD;
+  uint16_t* sR = sG + T * LD;  // bf16 R, row-major [d][m]
+  float* sRow = reinterpret_cast<float*>(sR + DIM * LD);  // [wave][row] partial row sums of w
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.x / P;
+  const int seg = blockIdx.x % P;
+  const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
+  const int64_t r1 = min(N, r0 + seg_len);
+  constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;
+  const float* cr = carry_r ? carry_r + (bh * P + seg) * E : nullptr;
+  const int64_t hoff = bh * N * DIM;
+  const int64_t hbytes = N * DIM * 2;
+  const rsrc_t rq = make_rsrc(q + hoff, hbytes), rk = make_rsrc(k + hoff, hbytes), rv = make_rsrc(v + hoff, hbytes),
+               rg = make_rsrc(dy + hoff, hbytes), rdk = make_rsrc(dk + hoff, hbytes),
+               rdv = make_rsrc(dv + hoff, hbytes), rl = make_rsrc(lg + bh * N, N * 4);
+  float* qdqh = qdq + bh * N;
+  const int j = 16 * w + li;  // this lane's key row
+  const int cc = 4 * (li % 4);
+  f32x4_t mt[4];  // causal mask (query i = 16t + 4g + u >= key j) as 0 / 1
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mt[t][u] = (t > w || (t == w && 4 * g + u >= li)) ? 1.f : 0.f;
+
+  f32x4_t Racc[DT][NTL];
+  init_x<DIM>(Racc, cr, w, g, li);
+  write_x<DIM>(sR, Racc, w, g, li);
+
+  const int64_t nch = (r1 - r0 + T - 1) / T;
+  i32x4 kraw[PC], vraw[PC], qraw[PC], graw[PC];
+  float lgv;
+  auto fetch = [&](int64_t cc0) {
+    const int soff = static_cast<int>(cc0 * DIM * 2);
+    bload_tile<DIM>(kraw, rk, soff);
+    bload_tile<DIM>(vraw, rv, soff);
+    bload_tile<DIM>(qraw, rq, soff);
+    bload_tile<DIM>(graw, rg, soff);
+    lgv = gate(rl, l, cc0);
+  };
+  fetch(r0 + (nch - 1) * T);
+  for (int64_t ci = nch - 1; ci >= 0; --ci) {
+    const int64_t c0 = r0 + ci * T;
+    const float b = wave_incl_scan(lgv);
+    const float bT = __shfl(b, 63, 64);
+    store_tile_v<DIM>(sK, kraw);
+    store_tile_v<DIM>(sV, vraw);
+    store_tile_v<DIM>(sQ, qraw);
+    store_tile_decay<DIM>(sQs, qraw, b);  // row i times exp(b_i)
+    store_tile_v<DIM>(sG, graw);
+    __syncthreads();
+    const int soff = static_cast<int>(c0 * DIM * 2);
+    const int64_t nrow = min(static_cast<int64_t>(T), r1 - c0);
+    if (ci > 0) fetch(c0 - T);
+
+    const float bj = __shfl(b, j, 64);
+    i16x8 kreg[KS], vreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      kreg[s] = lds8(sK + j * LD + 8 * g + 32 * s);
+      vreg[s] = lds8(sV + j * LD + 8 * g + 32 * s);
+    }
+    // A[i][j] = (q_i . k_j) exp(b_i - b_j), Bm[i][j] = (dy_i . v_j) exp(b_i - b_j),
+    // query tiles t >= w, masked i >= j; wv: the pair terms w_ij in fp32
+    i16x4 am[4], bm[4];
+    float wv[16];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4_t a = {0.f, 0.f, 0.f, 0.f}, bb = {0.f, 0.f, 0.f, 0.f};
+      if (t >= w) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          a = mfma(lds8(sQ + (16 * t + li) * LD + 8 * g + 32 * s), kreg[s], a);
+          bb = mfma(lds8(sG + (16 * t + li) * LD + 8 * g + 32 * s), vreg[s], bb);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float dec = __expf(fminf(__shfl(b, 16 * t + 4 * g + u, 64) - bj, 0.f)) * mt[t][u];
+          wv[4 * t + u] = a[u] * bb[u] * dec;
+          a[u] *= dec;
+          bb[u] *= dec;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) wv[4 * t + u] = 0.f;
+      }
+      am[t] = pack4(a);
+      bm[t] = pack4(bb);
+    }
+    // column sum (key j): over this lane's 16 rows, then the four groups
+    float colsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) colsum += wv[r];
+    colsum = shfl_sum_groups(colsum);
+    // row sums over this wave's 16 keys: halve the 16 values across lanes
+    // li ^ 8, ^ 4, ^ 2, ^ 1; lane li keeps row r = li, i.e. query
+    // i = 16 (li / 4) + 4g + li % 4
+    {
+      float h8[8], h4[4], h2[2];
+      const bool b3 = li & 8, b2 = li & 4, b1 = li & 2, b0 = li & 1;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) h8[x] = (b3 ? wv[x + 8] : wv[x]) + __shfl_xor(b3 ? wv[x] : wv[x + 8], 8, 64);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) h4[x] = (b2 ? h8[x + 4] : h8[x]) + __shfl_xor(b2 ? h8[x] : h8[x + 4], 4, 64);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) h2[x] = (b1 ? h4[x + 2] : h4[x]) + __shfl_xor(b1 ? h4[x] : h4[x + 2], 2, 64);
+      const float h1 = (b0 ? h2[1] : h2[0]) + __shfl_xor(b0 ? h2[0] : h2[1], 1, 64);
+      sRow[w * T + 16 * (li >> 2) + 4 * g + (li & 3)] = h1;
+    }
+    const float dj = __expf(bT - bj);
+    float kd = 0.f;
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) {
+      // dv^T[m][j] = exp(b_T - b_j) R^T k_j + sum_i dy^T A
+      f32x4_t ov = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int dr = 32 * s + 8 * g + li / 4;
+        ov = mfma(cat(lds_tr(sR + dr * LD + 16 * n + cc), lds_tr(sR + (dr + 4) * LD + 16 * n + cc)), kreg[s], ov);
+      }
+      ov *= dj;
+      // dk^T[d][j] = exp(b_T - b_j) R v_j + sum_i q^T Bm
+      f32x4_t ok = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) ok = mfma(lds8(sR + (16 * n + li) * LD + 8 * g + 32 * s), vreg[s], ok);
+      ok *= dj;
+      // r_j = k_j . exp(b_T - b_j) R v_j (fp32)
+      const f32x4_t kv = unpack4(*reinterpret_cast<const i16x4*>(sK + j * LD + 16 * n + 4 * g));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kd += kv[u] * ok[u];
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp) {
+        if (2 * tp + 1 >= w) {
+          const int ir = 32 * tp + 4 * g + li / 4;
+          ov = mfma(cat(lds_tr(sG + ir * LD + 16 * n + cc), lds_tr(sG + (ir + 16) * LD + 16 * n + cc)),
+                    cat(am[2 * tp], am[2 * tp + 1]), ov);
+          ok = mfma(cat(lds_tr(sQ + ir * LD + 16 * n + cc), lds_tr(sQ + (ir + 16) * LD + 16 * n + cc)),
+                    cat(bm[2 * tp], bm[2 * tp + 1]), ok);
+        }
+      }
+      bstore8(rdv, pack4(ov), (j * DIM + 16 * n + 4 * g) * 2, soff);
+      bstore8(rdk, pack4(ok), (j * DIM + 16 * n + 4 * g) * 2, soff);
+    }
+    kd = shfl_sum_groups(kd);
+    // R for the previous chunk: exp(b_T) R + sum_i exp(b_i) q_i dy_i^T
+    const float dT = __expf(bT);
+#pragma unroll
+    for (int a = 0; a < DT; ++a)
+#pragma unroll
+      for (int n = 0; n < NTL; ++n) Racc[a][n] *= dT;
+    outer_xt<DIM>(Racc, sG, sQs, w, g, li);
+    __syncthreads();
+    write_x<DIM>(sR, Racc, w, g, li);
+    if (g == 0 && j < nrow) {
+      const float rowsum = sRow[j] + sRow[T + j] + sRow[2 * T + j] + sRow[3 * T + j];
+      qdqh[c0 + j] += rowsum - colsum - kd;
+    }
+  }
+}
+
+// Reverse decayed exclusive scan of the suffix aggregates: record p receives
+// the suffix state decayed to segment p's last token,
+// C_{P-1} = 0, C_{p-1} = dR_p + exp(Lambda_p) C_p; the total (dS0) goes to tot.
+__global__ __launch_bounds__(NT) void k_ret_rscan(float* __restrict__ recs, int P, int64_t E, int64_t DM, int64_t nb,
+                                                  float* tot) {
+  const int64_t bh = blockIdx.x / nb;
+  const int64_t e = (blockIdx.x % nb) * NT + threadIdx.x;
+  if (e >= DM) return;
+  float carry = 0.f;
+  for (int p = P - 1; p >= 0; --p) {
+    float* rec = recs + (bh * P + p) * E;
+    const float x = rec[e];
+    const float lam = rec[DM];
+    rec[e] = carry;
+    carry = x + __expf(lam) * carry;
+  }
+  if (tot) tot[bh * DM + e] = carry;
+}
+
+// d log gamma_t = Y_p + sum_{t <= m < r1} a_m over segment p = [r0, r1), one
+// block per (head, segment).  Y_p = <S, R> at the segment's end: S the
+// state after its last token (the next segment's carry record), R the suffix
+// state decayed to that token (its own reverse-scan record); zero for the
+// last segment.
+__global__ __launch_bounds__(NT) void k_ret_dlg(const float* __restrict__ a, const float* __restrict__ srecs,
+                                                const float* __restrict__ rrecs, float* __restrict__ dlg, int64_t N,
+                                                int P, int seg_len, int64_t E, int64_t DM) {
+  __shared__ float wsum[4];
+  const int64_t bh = blockIdx.x / P;
+  const int p = blockIdx.x % P;
+  const int64_t r0 = static_cast<int64_t>(p) * seg_len;
+  const int64_t r1 = min(N, r0 + seg_len);
+  const float* ah = a + bh * N;
+  float* oh = dlg + bh * N;
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  float y = 0.f;
+  if (p + 1 < P) {
+    const float* s = srecs + (bh * P + p + 1) * E;
+    const float* r = rrecs + (bh * P + p) * E;
+    for (int64_t e = tid; e < DM; e += NT) y += s[e] * r[e];
+  }
+  y += __shfl_xor(y, 1, 64);
+  y += __shfl_xor(y, 2, 64);
+  y += __shfl_xor(y, 4, 64);
+  y += __shfl_xor(y, 8, 64);
+  y += __shfl_xor(y, 16, 64);
+  y += __shfl_xor(y, 32, 64);
+  if (l == 0) wsum[w] = y;
+  __syncthreads();
+  float carry = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  for (int64_t hi = r1; hi > r0; hi -= NT) {
+    // thread tid takes position hi - 1 - tid: a forward scan over the
+    // threads is then a reverse scan over positions
+    const int64_t t = hi - 1 - tid;
+    float x = t >= r0 ? ah[t] : 0.f;
+    x = wave_incl_scan(x);
+    if (l == 63) wsum[w] = x;
+    __syncthreads();
+    float before = carry;
+    for (int u = 0; u < w; ++u) before += wsum[u];
+    if (t >= r0) oh[t] = before + x;
+    const float total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    carry += total;
+  }
+}
+
 size_t lds_ret_fwd(int dim) { return (3 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t); }
 size_t lds_ret_seg(int dim) { return 2 * T * (dim + 8) * sizeof(uint16_t); }
+size_t lds_ret_dq(int dim) { return (6 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t); }
+size_t lds_ret_dkdv(int dim) { return (5 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + 4 * T * sizeof(float); }
 
 #define LA_RLAUNCH(kernel, grid, lds, st, ...)                                                               \
   do {                                                                                                       \
@@ -353,6 +853,42 @@ hipError_t launch_ret_forward(const SegGeom& g, const void* q, const void* k, co
   if (g.D == 128)
     LA_RLAUNCH((k_ret_fwd_mfma<128>), grid, lds_ret_fwd(128), st, Q, K, V, lg, Y, carry, g.N, g.P, g.seg_len);
   return hipErrorNotSupported;
+}
+
+hipError_t launch_ret_backward(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg,
+                               const void* dy, const float* carry_s, float* r_agg, void* dq, void* dk, void* dv,
+                               float* a, float* dlg, float* dS0, hipStream_t st) {
+  const int64_t grid = g.BH * g.P;
+  const bf16_t* Q = static_cast<const bf16_t*>(q);
+  const bf16_t* K = static_cast<const bf16_t*>(k);
+  const bf16_t* V = static_cast<const bf16_t*>(v);
+  const bf16_t* Gy = static_cast<const bf16_t*>(dy);
+  bf16_t* dQ = static_cast<bf16_t*>(dq);
+  bf16_t* dK = static_cast<bf16_t*>(dk);
+  bf16_t* dV = static_cast<bf16_t*>(dv);
+  auto dq_pass = [&]() -> hipError_t {
+    if (g.D == 64)
+      LA_RLAUNCH((k_ret_dq<64>), grid, lds_ret_dq(64), st, Q, K, V, lg, Gy, carry_s, dQ, a, r_agg, g.N, g.P, g.seg_len);
+    LA_RLAUNCH((k_ret_dq<128>), grid, lds_ret_dq(128), st, Q, K, V, lg, Gy, carry_s, dQ, a, r_agg, g.N, g.P,
+               g.seg_len);
+  };
+  hipError_t e = dq_pass();
+  if (e != hipSuccess) return e;
+  const int64_t DM = static_cast<int64_t>(g.D) * g.M;
+  const int64_t nb = (DM + NT - 1) / NT;
+  hipLaunchKernelGGL(k_ret_rscan, dim3(static_cast<unsigned>(g.BH * nb)), dim3(NT), 0, st, r_agg, g.P,
+                     state_elems(g.D, g.M), DM, nb, dS0);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  auto kv_pass = [&]() -> hipError_t {
+    if (g.D == 64)
+      LA_RLAUNCH((k_ret_dkdv<64>), grid, lds_ret_dkdv(64), st, Q, K, V, lg, Gy, r_agg, dK, dV, a, g.N, g.P, g.seg_len);
+    LA_RLAUNCH((k_ret_dkdv<128>), grid, lds_ret_dkdv(128), st, Q, K, V, lg, Gy, r_agg, dK, dV, a, g.N, g.P,
+               g.seg_len);
+  };
+  if ((e = kv_pass()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_ret_dlg, dim3(static_cast<unsigned>(g.BH * g.P)), dim3(NT), 0, st, a, carry_s, r_agg, dlg, g.N,
+                     g.P, g.seg_len, state_elems(g.D, g.M), DM);
+  return hipGetLastError();
 }
 
 }  // namespace la

@@ -93,6 +93,22 @@ def test_resolve_plan(lib):
     assert lib.la_resolve_plan(0, 1, 1, 1 << 23, 128, 128, 1, 1, ctypes.byref(mf), ctypes.byref(out)) == 2
 
 
+def test_retention_backward_segments_are_capped(lib):
+    # 512 heads fill the chip with one segment each; the retention backward
+    # still cuts each head into segments of at most 1024 tokens (its gate
+    # gradients are anchored at every segment end), the forward does not
+    out = _native.la_plan()
+    assert lib.la_resolve_plan(_native.LA_OP_RETENTION_FORWARD, 4, 128, 8192, 64, 64, 1, 1, None,
+                               ctypes.byref(out)) == 0
+    assert out.segments == 1
+    assert lib.la_resolve_plan(_native.LA_OP_RETENTION_BACKWARD, 4, 128, 8192, 64, 64, 1, 1, None,
+                               ctypes.byref(out)) == 0
+    assert out.segments == 8 and out.kernel == 2
+    assert lib.la_resolve_plan(_native.LA_OP_RETENTION_BACKWARD, 4, 128, 8000, 64, 64, 1, 1, None,
+                               ctypes.byref(out)) == 0
+    assert out.segments == 8  # 125 units -> 8 segments of 16 units (the last 13)
+
+
 nogpu = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer validation tests run on hosts without a GPU")
 
 A = 0x10000000  # fake, 256-byte aligned "device" addresses, far apart

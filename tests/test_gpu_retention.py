@@ -113,3 +113,119 @@ def test_retention_rejects_unsupported():
     tq, tk, tv, _, tl = case(1, 1, 64, 64, seed=1)
     with pytest.raises(la.LinAttnError, match="UNSUPPORTED"):
         la.retention_forward(tq.float(), tk.float(), tv.float(), tl)
+
+
+# ------------------------------------------------------------ backward ----
+# Gradients of L = sum(dy * y) against the oracle's chain rule through the
+# recurrence (pinned there by finite differences).  dq, dk, dv are bf16 and
+# take the forward's bound; dlog_gamma and dS0 are fp32 outputs built from bf16
+# operands and take the bf16 tolerance 2e-2.
+def bwd_case(B, H, N, D, seed, lo=0.6, hi=1.0, with_state=False):
+    tq, tk, tv, tg, tl = case(B, H, N, D, seed, lo, hi)
+    S0 = np.random.default_rng(seed + 7).standard_normal((B, H, D, D)) * 0.3 if with_state else None
+    tS0 = None if S0 is None else torch.tensor(S0, dtype=torch.float32, device=DEV)
+    return tq, tk, tv, tg, tl, S0, tS0
+
+
+def check_grads(got, want, what, q=None):
+    """dlog_gamma is a reverse sum of q.dq - k.dk; where the exact sum is 0
+    (one token and no carried state: the only decay multiplies a zero state)
+    its error is taken relative to the size of the q.dq terms instead."""
+    names = ("dq", "dk", "dv", "dlog_gamma", "dS0")
+    for name, a, b in zip(names, got, want):
+        if name in ("dq", "dk", "dv"):
+            check(a, b, f"{what} {name}")
+        else:
+            e_abs = np.linalg.norm((f64(a) - b).ravel())
+            nb = np.linalg.norm(b.ravel())
+            s = np.linalg.norm((f64(q) * want[0]).sum(-1).ravel()) if (name == "dlog_gamma" and q is not None) else 0
+            e = e_abs / nb if nb > 1e-9 * s else e_abs / s
+            say(f"{what} {name}: rel-L2 {e:.2e}")
+            assert np.isfinite(f64(a)).all()
+            assert e < 2e-2, (name, e)
+
+
+@pytest.mark.parametrize("shape", RET_SHAPES)
+@pytest.mark.parametrize("with_state", [False, True])
+def test_retention_backward_matches_oracle(shape, with_state):
+    B, H, N, D = shape
+    tq, tk, tv, tg, tl, S0, tS0 = bwd_case(B, H, N, D, seed=N + D + 5, with_state=with_state)
+    say(f"backward {shape} state={with_state}")
+    got = la.retention_backward(tq, tk, tv, tl, tg, S0=tS0)
+    torch.cuda.synchronize()
+    want = ret.backward(f64(tq), f64(tk), f64(tv), f64(tl), f64(tg), S0)
+    check_grads(got, want, f"backward {shape} state={with_state}", q=tq)
+
+
+@pytest.mark.parametrize("lo,hi", [(1.0, 1.0), (0.01, 0.2), (0.999, 1.0)])
+def test_retention_backward_gate_regimes(lo, hi):
+    tq, tk, tv, tg, tl, _, _ = bwd_case(2, 2, 2000, 64, seed=29, lo=lo, hi=hi)
+    say(f"backward gates in [{lo}, {hi}]")
+    got = la.retention_backward(tq, tk, tv, tl, tg)
+    torch.cuda.synchronize()
+    want = ret.backward(f64(tq), f64(tk), f64(tv), f64(tl), f64(tg))
+    check_grads(got, want, f"backward gates in [{lo}, {hi}]", q=tq)
+
+
+def test_retention_backward_full_reset_gates():
+    # below -80 a gate is taken as -80 in both passes; the gradient returned
+    # there is the one at -80 (where gamma ~ 0 makes it ~ 0 anyway)
+    tq, tk, tv, tg, tl, _, _ = bwd_case(1, 2, 300, 64, seed=31)
+    tl[:, :, 100] = -1e30
+    tl[:, :, 250] = -200.0
+    got = la.retention_backward(tq, tk, tv, tl, tg)
+    torch.cuda.synchronize()
+    lg = np.maximum(f64(tl), -80.0)
+    want = ret.backward(f64(tq), f64(tk), f64(tv), lg, f64(tg))
+    check_grads(got, want, "backward with full resets", q=tq)
+
+
+def test_retention_backward_split_sequence_chains_state_gradients():
+    # gradients of a sequence cut in two, with the state carried: the second
+    # half's dS0 is the gradient the first half receives through S_out; the
+    # first half's own dy plus that carried gradient reproduce the gradients
+    # of the whole sequence.  Checks dS0 as a seam, against the oracle.
+    B, H, N, D, a = 1, 2, 700, 64, 301
+    tq, tk, tv, tg, tl, _, _ = bwd_case(B, H, N, D, seed=37)
+    sl1, sl2 = slice(0, a), slice(a, N)
+    part = lambda t, s: t[:, :, s].contiguous()
+    S = torch.zeros(B, H, D, D, device=DEV)
+    la.retention_forward(part(tq, sl1), part(tk, sl1), part(tv, sl1), part(tl, sl1), S0=S, S_out=S)
+    g2 = la.retention_backward(part(tq, sl2), part(tk, sl2), part(tv, sl2), part(tl, sl2), part(tg, sl2), S0=S)
+    torch.cuda.synchronize()
+    want = ret.backward(f64(tq), f64(tk), f64(tv), f64(tl), f64(tg))
+    for name, got_t, full_t in zip(("dq", "dk", "dv"), g2[:3], want[:3]):
+        check(got_t, full_t[:, :, a:], f"second half {name}")
+    # the oracle's second half from the oracle's state gives the same dS0
+    _, S_a = ret.recurrent(f64(tq)[:, :, :a], f64(tk)[:, :, :a], f64(tv)[:, :, :a], f64(tl)[:, :, :a])
+    w2 = ret.backward(f64(tq)[:, :, a:], f64(tk)[:, :, a:], f64(tv)[:, :, a:], f64(tl)[:, :, a:], f64(tg)[:, :, a:],
+                      S_a)
+    assert rel_l2(f64(g2[4]), w2[4]) < 2e-2
+    assert rel_l2(f64(g2[3]), w2[3]) < 2e-2
+
+
+def test_retention_backward_rejects_unsupported():
+    tq, tk, tv, tg, tl, _, _ = bwd_case(1, 1, 64, 64, seed=2)
+    with pytest.raises(la.LinAttnError, match="UNSUPPORTED"):
+        la.retention_backward(tq.float(), tk.float(), tv.float(), tl, tg.float())
+
+
+@pytest.mark.parametrize("lo,hi", [(0.01, 0.2), (0.95, 1.0)])
+def test_retention_backward_many_heads(lo, hi):
+    # 512 heads: the plan gives one segment per head for the forward and
+    # caps the backward's at 1024 tokens; heads are independent, so the
+    # oracle checks four of them (both ends of the batch)
+    B, H, N, D = 4, 128, 4096, 64
+    plan = la.resolve_plan("retention_backward", B, H, N, D, D, True, "bf16")
+    assert plan["segments"] == 4
+    gen = torch.Generator(device=DEV).manual_seed(41)
+    mk = lambda: (torch.randn(B, H, N, D, device=DEV, generator=gen) / np.sqrt(D)).to(torch.bfloat16)
+    tq, tk, tv, tg = mk(), mk(), mk(), mk()
+    tl = torch.log(torch.rand(B, H, N, device=DEV, generator=gen) * (hi - lo) + lo).float()
+    say(f"backward B={B} H={H} N={N} gates in [{lo}, {hi}]")
+    got = la.retention_backward(tq, tk, tv, tl, tg)
+    torch.cuda.synchronize()
+    for b, hs in ((0, slice(0, 2)), (3, slice(126, 128))):
+        want = ret.backward(f64(tq[b, hs]), f64(tk[b, hs]), f64(tv[b, hs]), f64(tl[b, hs]), f64(tg[b, hs]))
+        check_grads([t[b, hs] for t in got], want, f"many heads, batch {b} heads {hs.start}..{hs.stop - 1}",
+                    q=tq[b, hs])
