@@ -218,6 +218,18 @@ la_status la_retention_backward(const void* q, const void* k, const void* v, con
                                 int64_t D, int64_t M, int dtype, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
+/* One decayed recurrent step per (b,h), in place ("08 - Transformer and
+ * Variants", section 1.3.4, the recurrence itself):
+ *   S <- gamma S + k v^T,  y = S^T q,  gamma = exp(log_gamma[b,h]).
+ *   S: [B,H,D,M] fp32, read and written (owned by the caller; a state from
+ *   la_retention_forward's S_out continues that sequence);
+ *   q, k: [B,H,D], v, y: [B,H,M] (dtype, fp32 or bf16); log_gamma: [B,H]
+ *   fp32 (below -80 taken as -80).  Any D, M <= 256.  Inputs must not
+ *   overlap S or y; no workspace. */
+la_status la_retention_decode_step(float* S, const void* q, const void* k, const void* v,
+                                   const float* log_gamma, void* y, int64_t B, int64_t H, int64_t D,
+                                   int64_t M, int dtype, hipStream_t stream);
+
 /* One RNN decode step per (b,h), in place ("Transformers are RNNs"
  * walkthrough, section 4; the state is updated first, then read):
  *   S <- S + phi(k) v^T;  Z <- Z + phi(k);  out = phi(q)^T S / phi(q)^T Z.

@@ -19,7 +19,7 @@ from ._native import LinAttnError, la_plan  # noqa: F401
 
 __all__ = [
     "forward", "backward", "forward_state", "backward_state", "decode_step", "prefix_state", "workspace_bytes",
-    "saved_bytes", "resolve_plan", "retention_forward", "retention_backward",
+    "saved_bytes", "resolve_plan", "retention_forward", "retention_backward", "retention_decode_step",
     "LinAttnError", "library_path", "version", "profile_enable", "profile_report",
 ]
 
@@ -341,6 +341,29 @@ def retention_backward(q, k, v, log_gamma, dy, S0=None, stream=None, workspace=N
                                             dlg.data_ptr(), dS0.data_ptr(), B, H, N, D, M, _dtype_code(q), _ptr(ws),
                                             wsz, _stream(stream)))
     return dq, dk, dv, dlg, dS0
+
+
+def retention_decode_step(S, q, k, v, log_gamma, out=None, stream=None):
+    """One decayed recurrent step in place: S <- gamma S + k v^T, returns
+    y = S^T q (q, k [B,H,D], v [B,H,M], log_gamma [B,H] fp32, S fp32
+    [B,H,D,M])."""
+    torch = _torch()
+    for t, n in ((S, "S"), (q, "q"), (k, "k"), (v, "v"), (log_gamma, "log_gamma")):
+        _dev(t, n)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    B, H, D = q.shape
+    M = v.shape[2]
+    if S.dtype != torch.float32 or tuple(S.shape) != (B, H, D, M):
+        raise ValueError("S must be float32 [B,H,D,M]")
+    if log_gamma.dtype != torch.float32 or tuple(log_gamma.shape) != (B, H):
+        raise ValueError("log_gamma must be float32 [B,H]")
+    y = out if out is not None else torch.empty((B, H, M), dtype=q.dtype, device=q.device)
+    lib = _native.load()
+    _native.check(lib.la_retention_decode_step(S.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                               log_gamma.data_ptr(), y.data_ptr(), B, H, D, M, _dtype_code(q),
+                                               _stream(stream)))
+    return y
 
 
 def decode_step(S, Z, q, k, v, out=None, stream=None):

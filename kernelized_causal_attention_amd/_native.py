@@ -26,6 +26,7 @@ EXPORTS = (
     "la_status_str", "la_last_error", "la_version", "la_profile_enable", "la_profile_report",
     "la_profile_select", "la_saved_bytes", "la_forward_state", "la_backward_state", "la_retention_forward",
     "la_retention_backward",
+    "la_retention_decode_step",
 )
 
 
@@ -70,6 +71,7 @@ def load() -> ctypes.CDLL:
         "la_saved_bytes": ([i64, i64, i64, i64, i64, i32, i32, plan_p], sz),
         "la_forward_state": ([vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, fp, fp, fp, fp, fp, vp, sz, vp], i32),
         "la_retention_forward": ([vp, vp, vp, fp, vp, i64, i64, i64, i64, i64, i32, fp, fp, vp, sz, vp], i32),
+        "la_retention_decode_step": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp], i32),
         "la_retention_backward": ([vp, vp, vp, fp, vp, fp, vp, vp, vp, fp, fp, i64, i64, i64, i64, i64, i32, vp, sz,
                                    vp], i32),
         "la_backward_state": ([vp, vp, vp, vp, vp, fp, fp, fp, vp, vp, vp, fp, fp, i64, i64, i64, i64, i64, i32,

@@ -767,6 +767,29 @@ LA_API la_status la_decode_step(float* S, float* Z, const void* q, const void* k
              "decode step");
 }
 
+LA_API la_status la_retention_decode_step(float* S, const void* q, const void* k, const void* v,
+                                          const float* log_gamma, void* y, int64_t B, int64_t H, int64_t D,
+                                          int64_t M, int dtype, hipStream_t stream) {
+  la_status s = check_sizes(B, H, 1, D, M, dtype);
+  if (s != LA_OK) return s;
+  if ((s = check_ptr(S, "S", LA_F32)) || (s = check_ptr(q, "q", dtype)) || (s = check_ptr(k, "k", dtype)) ||
+      (s = check_ptr(v, "v", dtype)) || (s = check_ptr(log_gamma, "log_gamma", LA_F32)) ||
+      (s = check_ptr(y, "y", dtype)))
+    return s;
+  const int64_t BH = B * H;
+  const size_t es = dtype_size(dtype);
+  const Span ins[] = {span("q", q, BH * D, es), span("k", k, BH * D, es), span("v", v, BH * M, es),
+                      span("log_gamma", log_gamma, BH, 4)};
+  const Span outs[] = {span("S", S, BH * D * M, 4), span("y", y, BH * M, es)};
+  if ((s = check_disjoint(outs, 2, ins, 4))) return s;
+  if (BH > 0xffffffffLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
+  return dev(timed("ret.decode", stream,
+                   [&] {
+                     return la::launch_ret_decode_step(dtype, BH, (int)D, (int)M, S, q, k, v, log_gamma, y, stream);
+                   }),
+             "retention decode step");
+}
+
 LA_API la_status la_prefix_state(const void* k, const void* v, float* S, float* Z, int64_t B, int64_t H,
                                  int64_t N, int64_t D, int64_t M, int dtype, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {

@@ -229,3 +229,60 @@ def test_retention_backward_many_heads(lo, hi):
         want = ret.backward(f64(tq[b, hs]), f64(tk[b, hs]), f64(tv[b, hs]), f64(tl[b, hs]), f64(tg[b, hs]))
         check_grads([t[b, hs] for t in got], want, f"many heads, batch {b} heads {hs.start}..{hs.stop - 1}",
                     q=tq[b, hs])
+
+
+# -------------------------------------------------------------- decode ----
+DEC_SHAPES = [(2, 3, 64, 64), (1, 2, 128, 128), (2, 1, 48, 40), (1, 1, 256, 64), (1, 2, 7, 1)]
+
+
+@pytest.mark.parametrize("shape", DEC_SHAPES)
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_retention_decode_steps_match_recurrence(shape, dt):
+    # token-by-token steps from a random state reproduce the recurrence
+    B, H, D, M = shape
+    N = 12
+    q, k, v, _ = numpy_inputs(B, H, N, D, M, seed=D + M, scale=1.0 / np.sqrt(D))
+    tq, tk, tv = (to_torch(x, dt, DEV) for x in (q, k, v))
+    lg = np.log(np.random.default_rng(D).uniform(0.5, 1.0, (B, H, N)))
+    tl = torch.tensor(lg, dtype=torch.float32, device=DEV)
+    S0 = np.random.default_rng(M).standard_normal((B, H, D, M)) * 0.2
+    S = torch.tensor(S0, dtype=torch.float32, device=DEV)
+    say(f"decode {shape} {dt}")
+    ys = [la.retention_decode_step(S, tq[:, :, t].contiguous(), tk[:, :, t].contiguous(), tv[:, :, t].contiguous(),
+                                   tl[:, :, t].contiguous()) for t in range(N)]
+    torch.cuda.synchronize()
+    ref, rS = ret.recurrent(f64(tq), f64(tk), f64(tv), f64(tl), S0)
+    y = torch.stack(ys, dim=2)
+    if dt == "f32":
+        assert rel_l2(f64(y), ref) < 1e-4
+    else:
+        check(y, ref, f"decode {shape} bf16")
+    assert rel_l2(f64(S), rS) < 1e-5
+
+
+def test_retention_prefill_then_decode():
+    # the forward's final state continues the sequence in decode steps
+    B, H, N, D, a = 2, 2, 300, 64, 257
+    tq, tk, tv, _, tl = case(B, H, N, D, seed=43)
+    S = torch.empty(B, H, D, D, device=DEV)
+    y1 = la.retention_forward(tq[:, :, :a].contiguous(), tk[:, :, :a].contiguous(), tv[:, :, :a].contiguous(),
+                              tl[:, :, :a].contiguous(), S_out=S)
+    ys = [la.retention_decode_step(S, tq[:, :, t].contiguous(), tk[:, :, t].contiguous(), tv[:, :, t].contiguous(),
+                                   tl[:, :, t].contiguous()) for t in range(a, N)]
+    torch.cuda.synchronize()
+    ref, rS = ret.recurrent(f64(tq), f64(tk), f64(tv), f64(tl))
+    check(torch.cat([y1, torch.stack(ys, dim=2)], dim=2), ref, "prefill then decode")
+    assert rel_l2(f64(S), rS) < 2e-3
+
+
+def test_retention_decode_full_reset():
+    # log gamma = -1e30 (taken as -80): the old state is forgotten
+    B, H, D, M = 1, 2, 64, 64
+    q, k, v, _ = numpy_inputs(B, H, 1, D, M, seed=3, scale=1.0)
+    tq, tk, tv = (to_torch(x[:, :, 0], "f32", DEV) for x in (q, k, v))
+    S = torch.randn(B, H, D, M, device=DEV)
+    y = la.retention_decode_step(S, tq, tk, tv, torch.full((B, H), -1e30, device=DEV))
+    torch.cuda.synchronize()
+    want_S = f64(tk)[..., :, None] * f64(tv)[..., None, :]
+    np.testing.assert_allclose(f64(S), want_S, rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(f64(y), np.einsum("bhd,bhdm->bhm", f64(tq), want_S), rtol=1e-5, atol=1e-5)
