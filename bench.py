@@ -20,6 +20,9 @@ Extra fields:
   decode        -- the batched decode step (B=256, H=32, D=M=128, fp32 state,
                    1024 consecutive steps after a 512-token prefix): steps/s
                    and HBM GB/s.
+  retention     -- decayed / gated linear attention forward+backward on the
+                   same shape (gates gamma_t ~ U(0.6, 1)): tokens/s and the
+                   dominant kernel's HBM roofline.
 """
 
 from __future__ import annotations
@@ -51,6 +54,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the decode measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--retention-only", action="store_true",
+                    help="run only the retention forward+backward measurement (for profiling) and print it")
     ap.add_argument("--settle", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps (the GPU raises its clocks "
                          "over the first few hundred milliseconds of load)")
@@ -65,6 +70,20 @@ def kernel_bytes(name: str, B, H, N, D, M, es, P=1):
     outputs written once), for B*H heads of N tokens."""
     ht = B * H * N
     family, _, base = name.rpartition(".")
+    if family == "ret":
+        # decayed / gated linear attention; the log gammas are 4 bytes a token
+        if base == "seg_state":
+            return ht * (es * (D + M) + 4)
+        if base in ("scan", "rscan"):
+            return B * H * (P * 2 + 1) * D * M * 4
+        if base == "forward":
+            return ht * (es * (2 * D + M) + 4 + es * M)
+        if base == "bwd_dq":  # reads q, k, v, dy, gates; writes dq and a
+            return ht * (es * (2 * D + 2 * M) + 4 + es * D + 4)
+        if base == "bwd_dkdv":  # reads q, k, v, dy, gates, a; writes dk, dv, a
+            return ht * (es * (2 * D + 2 * M) + 4 + 8 + es * (D + M))
+        if base == "dlg":  # reads a and the segment-end states S, R; writes d log gamma
+            return ht * 8 + B * H * (P - 1) * 2 * D * M * 4
     if family == "mfma" and base == "bwd_dq":
         # reads q, k, v, dout; writes dq and the per-row (c, den) pair
         return ht * (es * (2 * D + 2 * M) + es * D + 8)
@@ -104,6 +123,11 @@ def main():
 
     import kernelized_causal_attention_amd as la
     from workloads import WORKLOADS, device_inputs
+
+    if args.retention_only:
+        torch.cuda.set_device(0)
+        print(json.dumps(bench_retention(la, torch, args.steps, args.warmup)), flush=True)
+        return
 
     w = WORKLOADS["fwdbwd_bf16"]
     B, H, N, D, M = w.B, w.H, w.N, w.D, w.M
@@ -199,6 +223,7 @@ def main():
 
     if not args.no_extra:
         result["decode"] = bench_decode(la, torch, args.decode_steps)
+        result["retention"] = bench_retention(la, torch, args.steps, args.warmup)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(q, k, v, g, B, H, N, args.cpu_seconds)
@@ -208,6 +233,7 @@ def main():
 
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwdbwd_bf16.txt")
+TRAFFIC_FILE_RET = os.path.join(ROOT, "profiles", "traffic_retention_fwdbwd_bf16.txt")
 
 
 def calibrate_copy(torch):
@@ -237,12 +263,12 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kname):
+def measured_traffic(kname, path=TRAFFIC_FILE):
     """HBM bytes per launch of `kname` from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), or
     None when it is missing or was taken on different kernel sources."""
     try:
-        lines = open(TRAFFIC_FILE).read().splitlines()
+        lines = open(path).read().splitlines()
     except OSError:
         return None
     sha = None
@@ -297,6 +323,76 @@ def bench_decode(la, torch, steps):
             "roofline": {"bound": "hbm", "kernel": "decode", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                          "alg_bytes_per_launch": b, "avg_launch_ms": round(kavg, 5)}}
+
+
+def bench_retention(la, torch, steps, warmup):
+    """Decayed / gated linear attention forward + backward on the same bf16
+    shape as the main step (gates gamma_t ~ U(0.6, 1) per token; the
+    backward reads the forward's segment states): tokens/s and the dominant
+    kernel's HBM roofline."""
+    from workloads import WORKLOADS, device_inputs
+
+    w = WORKLOADS["fwdbwd_bf16"]
+    B, H, N, D, M = w.B, w.H, w.N, w.D, w.M
+    dev = "cuda"
+    q, k, v, g = device_inputs(B, H, N, D, M, "bf16", seed=1, scale=1.0 / D ** 0.5, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(2)
+    lg = torch.log(torch.rand(B, H, N, device=dev, generator=gen) * 0.4 + 0.6)
+    ws_f = torch.empty(max(1, la.workspace_bytes("retention_forward", B, H, N, D, M, True, "bf16")),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(1, la.workspace_bytes("retention_backward", B, H, N, D, M, True, "bf16")),
+                       dtype=torch.uint8, device=dev)
+    plan_f = la.resolve_plan("retention_forward", B, H, N, D, M, True, "bf16")
+    plan_b = la.resolve_plan("retention_backward", B, H, N, D, M, True, "bf16")
+    saved = torch.empty(la.retention_saved_bytes(B, H, N, D, M), dtype=torch.uint8, device=dev)
+
+    def step():
+        la.retention_forward(q, k, v, lg, workspace=ws_f, saved=saved)
+        return la.retention_backward(q, k, v, lg, g, workspace=ws_b, saved=saved)
+
+    for _ in range(warmup + 3):
+        step()
+    torch.cuda.synchronize()
+    la.profile_enable(True)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    prof = la.profile_report()
+    kname = max(prof.items(), key=lambda kv: kv[1][1])[0]
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    la.profile_enable(True, only=kname)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    nl, tot_ms = la.profile_report()[kname]
+    la.profile_enable(False)
+    ms = e0.elapsed_time(e1) / steps
+    kernels = {}
+    for name, (n, t) in sorted(prof.items()):
+        P = plan_b["segments"] if name in ("ret.bwd_dq", "ret.rscan", "ret.bwd_dkdv", "ret.dlg") else plan_f["segments"]
+        b = kernel_bytes(name, B, H, N, D, M, 2, P)
+        avg = t / n
+        kernels[name] = {"launches_per_step": n / 3, "avg_ms": round(avg, 4), "alg_bytes": b,
+                         "GBps": round(b / (avg / 1e3) / 1e9, 1) if b else None}
+    avg_ms = tot_ms / nl
+    kb = kernels[kname]["alg_bytes"]
+    gbs = kb / (avg_ms / 1e3) / 1e9
+    log(f"retention: {ms:.3f} ms/step, {B * N / (ms / 1e3):.4g} tokens/s; dominant {kname} {avg_ms:.4f} ms "
+        f"{gbs:.0f} GB/s; breakdown {prof}")
+    return {"metric": "decayed linear-attn (retention) fwd+bwd tokens/sec", "value": round(B * N / (ms / 1e3), 1),
+            "unit": "tokens/s", "ms_per_step": round(ms, 4),
+            "config": {"workload": "retention forward+backward, bf16 in / fp32 accumulate, gamma_t ~ U(0.6, 1)",
+                       "B": B, "H": H, "N": N, "D": D, "M": M, "plan_forward": plan_f, "plan_backward": plan_b},
+            "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic(kname, TRAFFIC_FILE_RET),
+                         "alg_bytes_per_launch": kb, "avg_launch_ms": round(avg_ms, 4)},
+            "kernels": kernels}
 
 
 def cpu_baseline(q, k, v, g, B, H, N, budget_s):

@@ -201,8 +201,17 @@ la_status la_backward_state(const void* q, const void* k, const void* v, const v
  * Workspace from la_workspace_bytes(LA_OP_RETENTION_FORWARD, ...). */
 la_status la_retention_forward(const void* q, const void* k, const void* v, const float* log_gamma,
                                void* y, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
-                               int dtype, const float* S0, float* S_out,
-                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+                               int dtype, const float* S0, float* S_out, float* saved,
+                               size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Bytes of la_retention_forward's `saved` record for these sizes: the state
+ * entering each segment of its plan ([B,H,segments] records of D*M + D
+ * floats, S row-major, then the segment's summed log gamma), which
+ * la_retention_backward reads instead of recomputing them.  `saved` is
+ * 16-byte aligned, caller-owned, and must not overlap any other argument;
+ * NULL keeps nothing.  0 for unsupported sizes. */
+size_t la_retention_saved_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype);
 
 /* Backward of la_retention_forward for L = sum(dy * y), by the chain rule
  * through the recurrence (the page gives no gradients):
@@ -210,10 +219,14 @@ la_status la_retention_forward(const void* q, const void* k, const void* v, cons
  *   dk_j = R_j v_j;  dv_j = R_j^T k_j;  dS0 = gamma_1 R_1;
  *   dlog_gamma_t = sum_{m>=t} (q_m . dq_m - k_m . dk_m).
  *   dq, dk: [B,H,N,D], dv: [B,H,N,M] (dtype); dlog_gamma: [B,H,N] fp32;
- *   dS0: [B,H,D,M] fp32 or NULL; S0 as given to the forward (or NULL).
+ *   dS0: [B,H,D,M] fp32 or NULL; S0 as given to the forward (or NULL);
+ *   saved: the record la_retention_forward kept for the same q, k, v,
+ *     log_gamma, S0 and sizes, or NULL (then the states are recomputed);
+ *     LA_ERR_INVALID when saved_bytes is short of la_retention_saved_bytes().
  * Workspace from la_workspace_bytes(LA_OP_RETENTION_BACKWARD, ...). */
 la_status la_retention_backward(const void* q, const void* k, const void* v, const float* log_gamma,
-                                const void* dy, const float* S0, void* dq, void* dk, void* dv,
+                                const void* dy, const float* S0, const float* saved,
+                                size_t saved_bytes, void* dq, void* dk, void* dv,
                                 float* dlog_gamma, float* dS0, int64_t B, int64_t H, int64_t N,
                                 int64_t D, int64_t M, int dtype, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);

@@ -20,6 +20,7 @@ from ._native import LinAttnError, la_plan  # noqa: F401
 __all__ = [
     "forward", "backward", "forward_state", "backward_state", "decode_step", "prefix_state", "workspace_bytes",
     "saved_bytes", "resolve_plan", "retention_forward", "retention_backward", "retention_decode_step",
+    "retention_saved_bytes",
     "LinAttnError", "library_path", "version", "profile_enable", "profile_report",
 ]
 
@@ -95,21 +96,23 @@ def profile_report() -> dict:
     return out
 
 
+_OPS = {"forward": _native.LA_OP_FORWARD, "backward": _native.LA_OP_BACKWARD,
+        "prefix_state": _native.LA_OP_PREFIX_STATE, "decode": _native.LA_OP_DECODE,
+        "forward_state": _native.LA_OP_FORWARD_STATE, "backward_state": _native.LA_OP_BACKWARD_STATE,
+        "retention_forward": _native.LA_OP_RETENTION_FORWARD,
+        "retention_backward": _native.LA_OP_RETENTION_BACKWARD}
+
+
 def workspace_bytes(op: str, B, H, N, D, M, causal=True, dtype="f32", plan=None) -> int:
-    ops = {"forward": _native.LA_OP_FORWARD, "backward": _native.LA_OP_BACKWARD,
-           "prefix_state": _native.LA_OP_PREFIX_STATE, "decode": _native.LA_OP_DECODE}
     dt = {"f32": _native.LA_F32, "bf16": _native.LA_BF16}[dtype]
     p = _plan(plan)
-    return int(_native.load().la_workspace_bytes_ex(ops[op], B, H, N, D, M, int(bool(causal)), dt, _plan_ref(p)))
+    return int(_native.load().la_workspace_bytes_ex(_OPS[op], B, H, N, D, M, int(bool(causal)), dt, _plan_ref(p)))
 
 
 def resolve_plan(op: str, B, H, N, D, M, causal=True, dtype="f32", plan=None) -> dict:
-    ops = {"forward": _native.LA_OP_FORWARD, "backward": _native.LA_OP_BACKWARD,
-           "prefix_state": _native.LA_OP_PREFIX_STATE, "retention_forward": _native.LA_OP_RETENTION_FORWARD,
-           "retention_backward": _native.LA_OP_RETENTION_BACKWARD}
     dt = {"f32": _native.LA_F32, "bf16": _native.LA_BF16}[dtype]
     out = la_plan()
-    _native.check(_native.load().la_resolve_plan(ops[op], B, H, N, D, M, int(bool(causal)), dt,
+    _native.check(_native.load().la_resolve_plan(_OPS[op], B, H, N, D, M, int(bool(causal)), dt,
                                                  _plan_ref(_plan(plan)), ctypes.byref(out)))
     return {"chunk": out.chunk, "segments": out.segments, "kernel": out.kernel}
 
@@ -277,11 +280,20 @@ def backward_state(q, k, v, out, dout, S0=None, Z0=None, den=None, stream=None, 
     return dq, dk, dv, dS0, dZ0
 
 
-def retention_forward(q, k, v, log_gamma, S0=None, S_out=None, return_state=False, stream=None, workspace=None):
+def retention_saved_bytes(B, H, N, D, M, dtype="bf16") -> int:
+    """Bytes of retention_forward's `saved` record (0 when unsupported)."""
+    dt = {"f32": _native.LA_F32, "bf16": _native.LA_BF16}[dtype]
+    return int(_native.load().la_retention_saved_bytes(B, H, N, D, M, dt))
+
+
+def retention_forward(q, k, v, log_gamma, S0=None, S_out=None, return_state=False, stream=None, workspace=None,
+                      saved=None):
     """Decayed / gated linear attention: y_t = S_t^T q_t with
     S_t = gamma_t S_{t-1} + k_t v_t^T (log_gamma [B,H,N] fp32, <= 0; S0 the
     state carried in or None).  Returns y, and the final state too when
-    return_state (written into S_out when given; S_out=S0 updates in place)."""
+    return_state (written into S_out when given; S_out=S0 updates in place).
+    `saved` (a device buffer of retention_saved_bytes()) keeps the segment
+    states for retention_backward."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (log_gamma, "log_gamma")):
         _dev(t, n)
@@ -303,15 +315,19 @@ def retention_forward(q, k, v, log_gamma, S0=None, S_out=None, return_state=Fals
     need = int(lib.la_workspace_bytes(_native.LA_OP_RETENTION_FORWARD, B, H, N, D, M, 1, _dtype_code(q)))
     ws = workspace if workspace is not None else _workspace(need, q.device)
     wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    if saved is not None:
+        _dev(saved, "saved")
+    ssz = 0 if saved is None else saved.numel() * saved.element_size()
     _native.check(lib.la_retention_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_gamma.data_ptr(),
                                            y.data_ptr(), B, H, N, D, M, _dtype_code(q), _ptr(S0), _ptr(S_out),
-                                           _ptr(ws), wsz, _stream(stream)))
+                                           _ptr(saved), ssz, _ptr(ws), wsz, _stream(stream)))
     return (y, S_out) if return_state else y
 
 
-def retention_backward(q, k, v, log_gamma, dy, S0=None, stream=None, workspace=None):
+def retention_backward(q, k, v, log_gamma, dy, S0=None, stream=None, workspace=None, saved=None):
     """Gradients (dq, dk, dv, dlog_gamma, dS0) of sum(dy * y) for
-    retention_forward (dS0 is returned whether or not S0 was given)."""
+    retention_forward (dS0 is returned whether or not S0 was given).
+    `saved`: the record retention_forward kept for the same inputs, or None."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (log_gamma, "log_gamma"), (dy, "dy")):
         _dev(t, n)
@@ -336,8 +352,12 @@ def retention_backward(q, k, v, log_gamma, dy, S0=None, stream=None, workspace=N
     need = int(lib.la_workspace_bytes(_native.LA_OP_RETENTION_BACKWARD, B, H, N, D, M, 1, _dtype_code(q)))
     ws = workspace if workspace is not None else _workspace(need, q.device)
     wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    if saved is not None:
+        _dev(saved, "saved")
+    ssz = 0 if saved is None else saved.numel() * saved.element_size()
     _native.check(lib.la_retention_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_gamma.data_ptr(),
-                                            dy.data_ptr(), _ptr(S0), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                            dy.data_ptr(), _ptr(S0), _ptr(saved), ssz, dq.data_ptr(),
+                                            dk.data_ptr(), dv.data_ptr(),
                                             dlg.data_ptr(), dS0.data_ptr(), B, H, N, D, M, _dtype_code(q), _ptr(ws),
                                             wsz, _stream(stream)))
     return dq, dk, dv, dlg, dS0

@@ -27,6 +27,7 @@ EXPORTS = (
     "la_profile_select", "la_saved_bytes", "la_forward_state", "la_backward_state", "la_retention_forward",
     "la_retention_backward",
     "la_retention_decode_step",
+    "la_retention_saved_bytes",
 )
 
 
@@ -70,10 +71,12 @@ def load() -> ctypes.CDLL:
         "la_backward_ex": (bwd[:6] + [fp, sz] + bwd[6:] + [plan_p], i32),
         "la_saved_bytes": ([i64, i64, i64, i64, i64, i32, i32, plan_p], sz),
         "la_forward_state": ([vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, fp, fp, fp, fp, fp, vp, sz, vp], i32),
-        "la_retention_forward": ([vp, vp, vp, fp, vp, i64, i64, i64, i64, i64, i32, fp, fp, vp, sz, vp], i32),
+        "la_retention_forward": ([vp, vp, vp, fp, vp, i64, i64, i64, i64, i64, i32, fp, fp, fp, sz, vp, sz, vp],
+                                 i32),
+        "la_retention_saved_bytes": ([i64, i64, i64, i64, i64, i32], sz),
         "la_retention_decode_step": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp], i32),
-        "la_retention_backward": ([vp, vp, vp, fp, vp, fp, vp, vp, vp, fp, fp, i64, i64, i64, i64, i64, i32, vp, sz,
-                                   vp], i32),
+        "la_retention_backward": ([vp, vp, vp, fp, vp, fp, fp, sz, vp, vp, vp, fp, fp, i64, i64, i64, i64, i64, i32,
+                                   vp, sz, vp], i32),
         "la_backward_state": ([vp, vp, vp, vp, vp, fp, fp, fp, vp, vp, vp, fp, fp, i64, i64, i64, i64, i64, i32,
                                vp, sz, vp], i32),
         "la_decode_step": ([fp, fp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp], i32),

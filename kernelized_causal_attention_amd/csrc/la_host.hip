@@ -28,9 +28,13 @@ hipError_t launch_ret_scan(float* recs, int64_t BH, int P, int D, int M, const f
                            hipStream_t st);
 hipError_t launch_ret_forward(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg, void* y,
                               const float* carry, hipStream_t st);
-hipError_t launch_ret_backward(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg,
-                               const void* dy, const float* carry_s, float* r_agg, void* dq, void* dk, void* dv,
-                               float* a, float* dlg, float* dS0, hipStream_t st);
+hipError_t launch_ret_bwd_dq(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg,
+                             const void* dy, const float* carry_s, float* r_agg, void* dq, float* a, hipStream_t st);
+hipError_t launch_ret_rscan(const SegGeom& g, float* r_agg, float* dS0, hipStream_t st);
+hipError_t launch_ret_bwd_dkdv(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg,
+                               const void* dy, const float* r_agg, void* dk, void* dv, float* a, hipStream_t st);
+hipError_t launch_ret_dlg(const SegGeom& g, const float* a, const float* carry_s, const float* r_agg, float* dlg,
+                          hipStream_t st);
 hipError_t launch_forward_f32mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
                                   void* out, float* den_out, const float* carry, hipStream_t st);
 hipError_t launch_seg_state_f32mfma(const SegGeom& g, const void* k, const void* v, float* s_out,
@@ -172,8 +176,11 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
     P = std::min<int64_t>(want, std::max<int64_t>(1, nunits / 4));
     // The retention backward anchors its gate gradients at every segment
     // end; between anchors the rounding of the chunk-crossing terms adds up
-    // like a random walk, so its segments stay within 16 units.
-    if (op_in == LA_OP_RETENTION_BACKWARD) P = std::max<int64_t>(P, (nunits + 15) / 16);
+    // like a random walk, so its segments stay within 16 units.  The
+    // forward cuts the sequence the same way, so that its segment states can
+    // be handed to the backward.
+    if (op_in == LA_OP_RETENTION_BACKWARD || op_in == LA_OP_RETENTION_FORWARD)
+      P = std::max<int64_t>(P, (nunits + 15) / 16);
   }
   P = std::max<int64_t>(1, std::min<int64_t>(P, nunits));
   const int64_t seg_units = (nunits + P - 1) / P;
@@ -645,10 +652,17 @@ LA_API la_status la_backward_state(const void* q, const void* k, const void* v, 
                      workspace_bytes, stream, nullptr, st);
 }
 
+LA_API size_t la_retention_saved_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype) {
+  if (check_sizes(B, H, N, D, M, dtype) != LA_OK || !la::retention_supported(D, M, dtype)) return 0;
+  Plan p;
+  if (resolve(LA_OP_RETENTION_FORWARD, B, H, N, D, M, 1, dtype, nullptr, &p) != LA_OK) return 0;
+  return static_cast<size_t>(B * H) * p.P * la::state_elems(static_cast<int>(D), static_cast<int>(M)) * sizeof(float);
+}
+
 LA_API la_status la_retention_forward(const void* q, const void* k, const void* v, const float* log_gamma,
                                       void* y, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype,
-                                      const float* S0, float* S_out, void* workspace, size_t workspace_bytes,
-                                      hipStream_t stream) {
+                                      const float* S0, float* S_out, float* saved, size_t saved_bytes,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   la_status s = check_sizes(B, H, N, D, M, dtype);
   if (s != LA_OK) return s;
   if ((s = check_ptr(q, "q", dtype)) || (s = check_ptr(k, "k", dtype)) || (s = check_ptr(v, "v", dtype)) ||
@@ -664,12 +678,17 @@ LA_API la_status la_retention_forward(const void* q, const void* k, const void* 
   Plan p;
   if ((s = resolve(LA_OP_RETENTION_FORWARD, B, H, N, D, M, 1, dtype, nullptr, &p))) return s;
   if (p.kernel != LA_KERNEL_MFMA) return fail(LA_ERR_UNSUPPORTED, "sequence too long for the retention kernels");
+  const size_t nsaved = static_cast<size_t>(BH) * p.P * la::state_elems(static_cast<int>(D), static_cast<int>(M));
+  if (saved && saved_bytes < nsaved * sizeof(float))
+    return fail(LA_ERR_INVALID, "saved too small: %zu bytes given, %zu needed", saved_bytes, nsaved * sizeof(float));
+  if (saved && (reinterpret_cast<uintptr_t>(saved) & 15)) return fail(LA_ERR_INVALID, "saved must be 16-byte aligned");
   const Span ins[] = {span("q", q, BH * N * D, es), span("k", k, BH * N * D, es), span("v", v, BH * N * M, es),
                       span("log_gamma", log_gamma, BH * N, 4),
                       span("workspace", workspace, workspace ? (int64_t)workspace_bytes : 0, 1),
                       S_out == S0 ? span("S0", nullptr, 0, 4) : span("S0", S0, S0 ? BH * D * M : 0, 4)};
-  const Span outs[] = {span("y", y, BH * N * M, es), span("S_out", S_out, S_out ? BH * D * M : 0, 4)};
-  if ((s = check_disjoint(outs, 2, ins, 6))) return s;
+  const Span outs[] = {span("y", y, BH * N * M, es), span("S_out", S_out, S_out ? BH * D * M : 0, 4),
+                       span("saved", saved, saved ? static_cast<int64_t>(nsaved) : 0, 4)};
+  if ((s = check_disjoint(outs, 3, ins, 6))) return s;
   if (S_out && S_out == S0) {
     const Span s0[] = {span("S0", S0, BH * D * M, 4)};
     if ((s = check_disjoint(outs, 1, s0, 1))) return s;
@@ -682,10 +701,10 @@ LA_API la_status la_retention_forward(const void* q, const void* k, const void* 
   const la::SegGeom g = geom(BH, N, D, M, p, p.chunk);
   const float* carry = nullptr;
   hipError_t e;
-  if (p.P > 1 || S0 || S_out) {
+  if (p.P > 1 || S0 || S_out || saved) {
     // segment aggregates and their decayed scan from S0; the total is the
-    // state after the N tokens
-    float* recs = at(workspace, w.aggS);
+    // state after the N tokens; kept in `saved` when given
+    float* recs = saved ? saved : at(workspace, w.aggS);
     if ((e = timed("ret.seg_state", stream, [&] { return la::launch_ret_seg_state(g, k, v, log_gamma, recs, stream); })))
       return dev(e, "retention segment state");
     if ((e = timed("ret.scan", stream, [&] { return la::launch_ret_scan(recs, BH, p.P, g.D, g.M, S0, S_out, stream); })))
@@ -698,10 +717,10 @@ LA_API la_status la_retention_forward(const void* q, const void* k, const void* 
 }
 
 LA_API la_status la_retention_backward(const void* q, const void* k, const void* v, const float* log_gamma,
-                                       const void* dy, const float* S0, void* dq, void* dk, void* dv,
-                                       float* dlog_gamma, float* dS0, int64_t B, int64_t H, int64_t N, int64_t D,
-                                       int64_t M, int dtype, void* workspace, size_t workspace_bytes,
-                                       hipStream_t stream) {
+                                       const void* dy, const float* S0, const float* saved, size_t saved_bytes,
+                                       void* dq, void* dk, void* dv, float* dlog_gamma, float* dS0, int64_t B,
+                                       int64_t H, int64_t N, int64_t D, int64_t M, int dtype, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
   la_status s = check_sizes(B, H, N, D, M, dtype);
   if (s != LA_OK) return s;
   if ((s = check_ptr(q, "q", dtype)) || (s = check_ptr(k, "k", dtype)) || (s = check_ptr(v, "v", dtype)) ||
@@ -719,34 +738,51 @@ LA_API la_status la_retention_backward(const void* q, const void* k, const void*
   Plan p;
   if ((s = resolve(LA_OP_RETENTION_BACKWARD, B, H, N, D, M, 1, dtype, nullptr, &p))) return s;
   if (p.kernel != LA_KERNEL_MFMA) return fail(LA_ERR_UNSUPPORTED, "sequence too long for the retention kernels");
+  const size_t nsaved = static_cast<size_t>(BH) * p.P * la::state_elems(static_cast<int>(D), static_cast<int>(M));
+  if (saved && saved_bytes < nsaved * sizeof(float))
+    return fail(LA_ERR_INVALID, "saved too small: %zu bytes given, %zu needed", saved_bytes, nsaved * sizeof(float));
+  if (saved && (reinterpret_cast<uintptr_t>(saved) & 15)) return fail(LA_ERR_INVALID, "saved must be 16-byte aligned");
   const Span ins[] = {span("q", q, BH * N * D, es), span("k", k, BH * N * D, es), span("v", v, BH * N * M, es),
                       span("log_gamma", log_gamma, BH * N, 4), span("dy", dy, BH * N * M, es),
                       span("S0", S0, S0 ? BH * D * M : 0, 4),
-                      span("workspace", workspace, workspace ? (int64_t)workspace_bytes : 0, 1)};
+                      span("workspace", workspace, workspace ? (int64_t)workspace_bytes : 0, 1),
+                      span("saved", saved, saved ? static_cast<int64_t>(nsaved) : 0, 4)};
   const Span outs[] = {span("dq", dq, BH * N * D, es), span("dk", dk, BH * N * D, es), span("dv", dv, BH * N * M, es),
                        span("dlog_gamma", dlog_gamma, BH * N, 4), span("dS0", dS0, dS0 ? BH * D * M : 0, 4)};
-  if ((s = check_disjoint(outs, 5, ins, 7))) return s;
+  if ((s = check_disjoint(outs, 5, ins, 8))) return s;
   const WsLayout w = layout(LA_OP_RETENTION_BACKWARD, BH, N, D, M, 1, p);
   if (workspace_bytes < w.bytes)
     return fail(LA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, w.bytes);
   if (!workspace) return fail(LA_ERR_INVALID, "workspace is NULL (%zu bytes needed)", w.bytes);
   if (reinterpret_cast<uintptr_t>(workspace) & 15) return fail(LA_ERR_INVALID, "workspace must be 16-byte aligned");
   const la::SegGeom g = geom(BH, N, D, M, p, p.chunk);
-  float* recs = at(workspace, w.aggS);
   float* rrec = at(workspace, w.aggR);
   float* a = at(workspace, w.den);
   hipError_t e;
-  // the prefix states entering each segment, from S0 (as the forward)
-  if ((e = timed("ret.seg_state", stream, [&] { return la::launch_ret_seg_state(g, k, v, log_gamma, recs, stream); })))
-    return dev(e, "retention segment state");
-  if ((e = timed("ret.scan", stream, [&] { return la::launch_ret_scan(recs, BH, p.P, g.D, g.M, S0, nullptr, stream); })))
-    return dev(e, "retention scan");
-  return dev(timed("ret.backward", stream,
-                   [&] {
-                     return la::launch_ret_backward(g, q, k, v, log_gamma, dy, recs, rrec, dq, dk, dv, a, dlog_gamma,
-                                                    dS0, stream);
-                   }),
-             "retention backward");
+  // the states entering each segment: the forward's, or recomputed from S0
+  const float* recs = saved;
+  if (!saved) {
+    float* r = at(workspace, w.aggS);
+    if ((e = timed("ret.seg_state", stream, [&] { return la::launch_ret_seg_state(g, k, v, log_gamma, r, stream); })))
+      return dev(e, "retention segment state");
+    if ((e = timed("ret.scan", stream, [&] { return la::launch_ret_scan(r, BH, p.P, g.D, g.M, S0, nullptr, stream); })))
+      return dev(e, "retention scan");
+    recs = r;
+  }
+  // forward sweep (dq, p, suffix aggregates), reverse scan of the
+  // aggregates (total = dS0), reverse sweep (dk, dv, a), gate gradients
+  if ((e = timed("ret.bwd_dq", stream, [&] {
+         return la::launch_ret_bwd_dq(g, q, k, v, log_gamma, dy, recs, rrec, dq, a, stream);
+       })))
+    return dev(e, "retention backward (dq)");
+  if ((e = timed("ret.rscan", stream, [&] { return la::launch_ret_rscan(g, rrec, dS0, stream); })))
+    return dev(e, "retention backward (suffix scan)");
+  if ((e = timed("ret.bwd_dkdv", stream, [&] {
+         return la::launch_ret_bwd_dkdv(g, q, k, v, log_gamma, dy, rrec, dk, dv, a, stream);
+       })))
+    return dev(e, "retention backward (dk, dv)");
+  return dev(timed("ret.dlg", stream, [&] { return la::launch_ret_dlg(g, a, recs, rrec, dlog_gamma, stream); }),
+             "retention backward (d log gamma)");
 }
 
 LA_API la_status la_decode_step(float* S, float* Z, const void* q, const void* k, const void* v, void* out,

@@ -855,39 +855,51 @@ hipError_t launch_ret_forward(const SegGeom& g, const void* q, const void* k, co
   return hipErrorNotSupported;
 }
 
-hipError_t launch_ret_backward(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg,
-                               const void* dy, const float* carry_s, float* r_agg, void* dq, void* dk, void* dv,
-                               float* a, float* dlg, float* dS0, hipStream_t st) {
+hipError_t launch_ret_bwd_dq(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg,
+                             const void* dy, const float* carry_s, float* r_agg, void* dq, float* a, hipStream_t st) {
   const int64_t grid = g.BH * g.P;
   const bf16_t* Q = static_cast<const bf16_t*>(q);
   const bf16_t* K = static_cast<const bf16_t*>(k);
   const bf16_t* V = static_cast<const bf16_t*>(v);
   const bf16_t* Gy = static_cast<const bf16_t*>(dy);
   bf16_t* dQ = static_cast<bf16_t*>(dq);
-  bf16_t* dK = static_cast<bf16_t*>(dk);
-  bf16_t* dV = static_cast<bf16_t*>(dv);
-  auto dq_pass = [&]() -> hipError_t {
-    if (g.D == 64)
-      LA_RLAUNCH((k_ret_dq<64>), grid, lds_ret_dq(64), st, Q, K, V, lg, Gy, carry_s, dQ, a, r_agg, g.N, g.P, g.seg_len);
+  if (g.D == 64)
+    LA_RLAUNCH((k_ret_dq<64>), grid, lds_ret_dq(64), st, Q, K, V, lg, Gy, carry_s, dQ, a, r_agg, g.N, g.P, g.seg_len);
+  if (g.D == 128)
     LA_RLAUNCH((k_ret_dq<128>), grid, lds_ret_dq(128), st, Q, K, V, lg, Gy, carry_s, dQ, a, r_agg, g.N, g.P,
                g.seg_len);
-  };
-  hipError_t e = dq_pass();
-  if (e != hipSuccess) return e;
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_ret_rscan(const SegGeom& g, float* r_agg, float* dS0, hipStream_t st) {
   const int64_t DM = static_cast<int64_t>(g.D) * g.M;
   const int64_t nb = (DM + NT - 1) / NT;
   hipLaunchKernelGGL(k_ret_rscan, dim3(static_cast<unsigned>(g.BH * nb)), dim3(NT), 0, st, r_agg, g.P,
                      state_elems(g.D, g.M), DM, nb, dS0);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  auto kv_pass = [&]() -> hipError_t {
-    if (g.D == 64)
-      LA_RLAUNCH((k_ret_dkdv<64>), grid, lds_ret_dkdv(64), st, Q, K, V, lg, Gy, r_agg, dK, dV, a, g.N, g.P, g.seg_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_ret_bwd_dkdv(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg,
+                               const void* dy, const float* r_agg, void* dk, void* dv, float* a, hipStream_t st) {
+  const int64_t grid = g.BH * g.P;
+  const bf16_t* Q = static_cast<const bf16_t*>(q);
+  const bf16_t* K = static_cast<const bf16_t*>(k);
+  const bf16_t* V = static_cast<const bf16_t*>(v);
+  const bf16_t* Gy = static_cast<const bf16_t*>(dy);
+  bf16_t* dK = static_cast<bf16_t*>(dk);
+  bf16_t* dV = static_cast<bf16_t*>(dv);
+  if (g.D == 64)
+    LA_RLAUNCH((k_ret_dkdv<64>), grid, lds_ret_dkdv(64), st, Q, K, V, lg, Gy, r_agg, dK, dV, a, g.N, g.P, g.seg_len);
+  if (g.D == 128)
     LA_RLAUNCH((k_ret_dkdv<128>), grid, lds_ret_dkdv(128), st, Q, K, V, lg, Gy, r_agg, dK, dV, a, g.N, g.P,
                g.seg_len);
-  };
-  if ((e = kv_pass()) != hipSuccess) return e;
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_ret_dlg(const SegGeom& g, const float* a, const float* carry_s, const float* r_agg, float* dlg,
+                          hipStream_t st) {
   hipLaunchKernelGGL(k_ret_dlg, dim3(static_cast<unsigned>(g.BH * g.P)), dim3(NT), 0, st, a, carry_s, r_agg, dlg, g.N,
-                     g.P, g.seg_len, state_elems(g.D, g.M), DM);
+                     g.P, g.seg_len, state_elems(g.D, g.M), static_cast<int64_t>(g.D) * g.M);
   return hipGetLastError();
 }
 

@@ -93,20 +93,23 @@ def test_resolve_plan(lib):
     assert lib.la_resolve_plan(0, 1, 1, 1 << 23, 128, 128, 1, 1, ctypes.byref(mf), ctypes.byref(out)) == 2
 
 
-def test_retention_backward_segments_are_capped(lib):
-    # 512 heads fill the chip with one segment each; the retention backward
-    # still cuts each head into segments of at most 1024 tokens (its gate
-    # gradients are anchored at every segment end), the forward does not
+def test_retention_segments_are_capped(lib):
+    # 512 heads fill the chip with one segment each; the retention calls
+    # still cut each head into segments of at most 1024 tokens (the
+    # backward's gate gradients are anchored at every segment end, and the
+    # forward cuts the same way so that its states can be handed over)
     out = _native.la_plan()
-    assert lib.la_resolve_plan(_native.LA_OP_RETENTION_FORWARD, 4, 128, 8192, 64, 64, 1, 1, None,
-                               ctypes.byref(out)) == 0
+    for op in (_native.LA_OP_RETENTION_FORWARD, _native.LA_OP_RETENTION_BACKWARD):
+        assert lib.la_resolve_plan(op, 4, 128, 8192, 64, 64, 1, 1, None, ctypes.byref(out)) == 0
+        assert out.segments == 8 and out.kernel == 2
+        assert lib.la_resolve_plan(op, 4, 128, 8000, 64, 64, 1, 1, None, ctypes.byref(out)) == 0
+        assert out.segments == 8  # 125 units -> 8 segments of 16 units (the last 13)
+    # the linear-attention forward is not capped
+    assert lib.la_resolve_plan(_native.LA_OP_FORWARD, 4, 128, 8192, 64, 64, 1, 1, None, ctypes.byref(out)) == 0
     assert out.segments == 1
-    assert lib.la_resolve_plan(_native.LA_OP_RETENTION_BACKWARD, 4, 128, 8192, 64, 64, 1, 1, None,
-                               ctypes.byref(out)) == 0
-    assert out.segments == 8 and out.kernel == 2
-    assert lib.la_resolve_plan(_native.LA_OP_RETENTION_BACKWARD, 4, 128, 8000, 64, 64, 1, 1, None,
-                               ctypes.byref(out)) == 0
-    assert out.segments == 8  # 125 units -> 8 segments of 16 units (the last 13)
+    # the saved record: one state (D*M + D floats) per segment
+    assert lib.la_retention_saved_bytes(4, 128, 8192, 64, 64, 1) == 512 * 8 * (64 * 64 + 64) * 4
+    assert lib.la_retention_saved_bytes(4, 128, 8192, 64, 64, 0) == 0  # fp32: no retention kernels
 
 
 nogpu = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer validation tests run on hosts without a GPU")

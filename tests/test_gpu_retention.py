@@ -286,3 +286,30 @@ def test_retention_decode_full_reset():
     want_S = f64(tk)[..., :, None] * f64(tv)[..., None, :]
     np.testing.assert_allclose(f64(S), want_S, rtol=1e-6, atol=1e-6)
     np.testing.assert_allclose(f64(y), np.einsum("bhd,bhdm->bhm", f64(tq), want_S), rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("shape,with_state", [((2, 3, 333, 64), True), ((1, 2, 3000, 64), False),
+                                              ((1, 2, 1100, 128), True), ((1, 1, 1, 64), False)])
+def test_retention_backward_reads_saved_states(shape, with_state):
+    # the forward's segment states, handed to the backward, give the same
+    # gradients bit for bit as the backward recomputing them
+    B, H, N, D = shape
+    tq, tk, tv, tg, tl, S0, tS0 = bwd_case(B, H, N, D, seed=N + 11, with_state=with_state)
+    saved = torch.empty(la.retention_saved_bytes(B, H, N, D, D), dtype=torch.uint8, device=DEV)
+    y = la.retention_forward(tq, tk, tv, tl, S0=tS0, saved=saved)
+    with_saved = la.retention_backward(tq, tk, tv, tl, tg, S0=tS0, saved=saved)
+    recomputed = la.retention_backward(tq, tk, tv, tl, tg, S0=tS0)
+    torch.cuda.synchronize()
+    for a, b in zip(with_saved, recomputed):
+        assert torch.equal(a, b)
+    check(y, ret.recurrent(f64(tq), f64(tk), f64(tv), f64(tl), S0)[0], f"forward keeping states {shape}")
+
+
+def test_retention_saved_too_small_is_rejected():
+    tq, tk, tv, tg, tl, _, _ = bwd_case(1, 2, 3000, 64, seed=5)
+    n = la.retention_saved_bytes(1, 2, 3000, 64, 64)
+    short = torch.empty(n - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(la.LinAttnError, match="INVALID"):
+        la.retention_forward(tq, tk, tv, tl, saved=short)
+    with pytest.raises(la.LinAttnError, match="INVALID"):
+        la.retention_backward(tq, tk, tv, tl, tg, saved=short)
