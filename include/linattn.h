@@ -243,6 +243,19 @@ la_status la_retention_decode_step(float* S, const void* q, const void* k, const
                                    const float* log_gamma, void* y, int64_t B, int64_t H, int64_t D,
                                    int64_t M, int dtype, hipStream_t stream);
 
+/* Linear attention with the degree-2 polynomial kernel ("[Paper
+ * walkthrough] Transformers are RNNs", section 2, "feature map and
+ * computation cost", item (3): sim(q, k) = (q^T k)^2, C = D^2 features),
+ * in eq:common form, causal per eq:mask when causal != 0:
+ *   out_i = sum_{j<=i} (q_i . k_j)^2 v_j / den_i,  den_i = sum_{j<=i} (q_i . k_j)^2,
+ * with out_i = 0 where den_i = 0 (no epsilon; every weight is then 0).
+ *   q, k: [B,H,N,D], v, out: [B,H,N,M] (bf16, D = M in {64, 128});
+ *   den_out: [B,H,N] fp32 or NULL (kept for la_poly_backward).
+ * No workspace.  LA_ERR_UNSUPPORTED for other dtypes or sizes. */
+la_status la_poly_forward(const void* q, const void* k, const void* v, void* out, float* den_out,
+                          int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
+                          int dtype, hipStream_t stream);
+
 /* One RNN decode step per (b,h), in place ("Transformers are RNNs"
  * walkthrough, section 4; the state is updated first, then read):
  *   S <- S + phi(k) v^T;  Z <- Z + phi(k);  out = phi(q)^T S / phi(q)^T Z.

@@ -20,7 +20,7 @@ from ._native import LinAttnError, la_plan  # noqa: F401
 __all__ = [
     "forward", "backward", "forward_state", "backward_state", "decode_step", "prefix_state", "workspace_bytes",
     "saved_bytes", "resolve_plan", "retention_forward", "retention_backward", "retention_decode_step",
-    "retention_saved_bytes",
+    "retention_saved_bytes", "poly_forward",
     "LinAttnError", "library_path", "version", "profile_enable", "profile_report",
 ]
 
@@ -384,6 +384,26 @@ def retention_decode_step(S, q, k, v, log_gamma, out=None, stream=None):
                                                log_gamma.data_ptr(), y.data_ptr(), B, H, D, M, _dtype_code(q),
                                                _stream(stream)))
     return y
+
+
+def poly_forward(q, k, v, causal=True, out=None, den=None, return_den=False, stream=None):
+    """Degree-2 polynomial-kernel attention: out_i = sum_j (q_i.k_j)^2 v_j /
+    sum_j (q_i.k_j)^2 over j <= i (causal) or all j (0 where every weight is
+    0).  bf16, D = M in {64, 128}.  Returns out (and den when return_den)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    B, H, N, D = q.shape
+    M = v.shape[3]
+    if out is None:
+        out = torch.empty((B, H, N, M), dtype=q.dtype, device=q.device)
+    if return_den and den is None:
+        den = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _native.check(_native.load().la_poly_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _ptr(den),
+                                                 B, H, N, D, M, int(bool(causal)), _dtype_code(q), _stream(stream)))
+    return (out, den) if return_den else out
 
 
 def decode_step(S, Z, q, k, v, out=None, stream=None):

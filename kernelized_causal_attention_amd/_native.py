@@ -28,6 +28,7 @@ EXPORTS = (
     "la_retention_backward",
     "la_retention_decode_step",
     "la_retention_saved_bytes",
+    "la_poly_forward",
 )
 
 
@@ -74,6 +75,7 @@ def load() -> ctypes.CDLL:
         "la_retention_forward": ([vp, vp, vp, fp, vp, i64, i64, i64, i64, i64, i32, fp, fp, fp, sz, vp, sz, vp],
                                  i32),
         "la_retention_saved_bytes": ([i64, i64, i64, i64, i64, i32], sz),
+        "la_poly_forward": ([vp, vp, vp, vp, fp, i64, i64, i64, i64, i64, i32, i32, vp], i32),
         "la_retention_decode_step": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp], i32),
         "la_retention_backward": ([vp, vp, vp, fp, vp, fp, fp, sz, vp, vp, vp, fp, fp, i64, i64, i64, i64, i64, i32,
                                    vp, sz, vp], i32),

@@ -28,6 +28,9 @@ hipError_t launch_ret_scan(float* recs, int64_t BH, int P, int D, int M, const f
                            hipStream_t st);
 hipError_t launch_ret_forward(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg, void* y,
                               const float* carry, hipStream_t st);
+int poly_supported(int64_t D, int64_t M, int dtype);
+hipError_t launch_poly_forward(int64_t BH, int64_t N, int D, const void* q, const void* k, const void* v, void* out,
+                               float* den, int causal, hipStream_t st);
 hipError_t launch_ret_bwd_dq(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg,
                              const void* dy, const float* carry_s, float* r_agg, void* dq, float* a, hipStream_t st);
 hipError_t launch_ret_rscan(const SegGeom& g, float* r_agg, float* dS0, hipStream_t st);
@@ -783,6 +786,30 @@ LA_API la_status la_retention_backward(const void* q, const void* k, const void*
     return dev(e, "retention backward (dk, dv)");
   return dev(timed("ret.dlg", stream, [&] { return la::launch_ret_dlg(g, a, recs, rrec, dlog_gamma, stream); }),
              "retention backward (d log gamma)");
+}
+
+LA_API la_status la_poly_forward(const void* q, const void* k, const void* v, void* out, float* den_out, int64_t B,
+                                 int64_t H, int64_t N, int64_t D, int64_t M, int causal, int dtype,
+                                 hipStream_t stream) {
+  la_status s = check_sizes(B, H, N, D, M, dtype);
+  if (s != LA_OK) return s;
+  if ((s = check_ptr(q, "q", dtype)) || (s = check_ptr(k, "k", dtype)) || (s = check_ptr(v, "v", dtype)) ||
+      (s = check_ptr(out, "out", dtype)))
+    return s;
+  if (den_out && (reinterpret_cast<uintptr_t>(den_out) & 3)) return fail(LA_ERR_INVALID, "den_out misaligned");
+  if (!la::poly_supported(D, M, dtype))
+    return fail(LA_ERR_UNSUPPORTED, "polynomial kernels take bf16 with D = M in {64, 128} (D=%lld, M=%lld, dtype %d)",
+                (long long)D, (long long)M, dtype);
+  if (N * D * 2 >= (int64_t(1) << 31)) return fail(LA_ERR_UNSUPPORTED, "head too large for 32-bit offsets");
+  const int64_t BH = B * H;
+  if (BH * ((N + 127) / 128) > 0xffffffffLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
+  const size_t es = dtype_size(dtype);
+  const Span ins[] = {span("q", q, BH * N * D, es), span("k", k, BH * N * D, es), span("v", v, BH * N * M, es)};
+  const Span outs[] = {span("out", out, BH * N * M, es), span("den_out", den_out, den_out ? BH * N : 0, 4)};
+  if ((s = check_disjoint(outs, 2, ins, 3))) return s;
+  return dev(timed("poly.forward", stream,
+                   [&] { return la::launch_poly_forward(BH, N, (int)D, q, k, v, out, den_out, causal ? 1 : 0, stream); }),
+             "polynomial forward");
 }
 
 LA_API la_status la_decode_step(float* S, float* Z, const void* q, const void* k, const void* v, void* out,
