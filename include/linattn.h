@@ -66,7 +66,8 @@ typedef enum la_op {
   LA_OP_FORWARD_STATE = 4,  /* la_forward_state  */
   LA_OP_BACKWARD_STATE = 5, /* la_backward_state */
   LA_OP_RETENTION_FORWARD = 6,  /* la_retention_forward  */
-  LA_OP_RETENTION_BACKWARD = 7  /* la_retention_backward */
+  LA_OP_RETENTION_BACKWARD = 7, /* la_retention_backward */
+  LA_OP_POLY_BACKWARD = 8       /* la_poly_backward      */
 } la_op;
 
 /* Kernel family choice for the *_ex entry points (0 = automatic). */
@@ -251,10 +252,28 @@ la_status la_retention_decode_step(float* S, const void* q, const void* k, const
  * with out_i = 0 where den_i = 0 (no epsilon; every weight is then 0).
  *   q, k: [B,H,N,D], v, out: [B,H,N,M] (bf16, D = M in {64, 128});
  *   den_out: [B,H,N] fp32 or NULL (kept for la_poly_backward).
+ * The weights enter the numerator rounded to bf16 and out is normalised by
+ * their sum (an exact convex combination of the values); den_out is the sum
+ * of the fp32 weights.
  * No workspace.  LA_ERR_UNSUPPORTED for other dtypes or sizes. */
 la_status la_poly_forward(const void* q, const void* k, const void* v, void* out, float* den_out,
                           int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
                           int dtype, hipStream_t stream);
+
+/* Backward of la_poly_forward for L = sum(dout * out), by the chain rule
+ * through the masked sum (the page gives no gradients); with
+ * s_ij = q_i . k_j, g_i = dout_i / den_i, c_i = -(dout_i . out_i) / den_i:
+ *   dS_ij = 2 s_ij (g_i . v_j + c_i) over the masked pairs,
+ *   dq_i = sum_j dS_ij k_j,  dk_j = sum_i dS_ij q_i,  dv_j = sum_i s_ij^2 g_i,
+ * and g_i = c_i = 0 where den_i = 0.
+ *   out, den: la_poly_forward's outputs for the same q, k, v and causal
+ *   (den required); dout: [B,H,N,M]; dq, dk: [B,H,N,D], dv: [B,H,N,M].
+ * Workspace from la_workspace_bytes(LA_OP_POLY_BACKWARD, ...) (B*H*N
+ * floats). */
+la_status la_poly_backward(const void* q, const void* k, const void* v, const void* out,
+                           const void* dout, const float* den, void* dq, void* dk, void* dv,
+                           int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
+                           int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* One RNN decode step per (b,h), in place ("Transformers are RNNs"
  * walkthrough, section 4; the state is updated first, then read):

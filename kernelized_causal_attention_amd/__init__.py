@@ -20,7 +20,7 @@ from ._native import LinAttnError, la_plan  # noqa: F401
 __all__ = [
     "forward", "backward", "forward_state", "backward_state", "decode_step", "prefix_state", "workspace_bytes",
     "saved_bytes", "resolve_plan", "retention_forward", "retention_backward", "retention_decode_step",
-    "retention_saved_bytes", "poly_forward",
+    "retention_saved_bytes", "poly_forward", "poly_backward",
     "LinAttnError", "library_path", "version", "profile_enable", "profile_report",
 ]
 
@@ -100,7 +100,7 @@ _OPS = {"forward": _native.LA_OP_FORWARD, "backward": _native.LA_OP_BACKWARD,
         "prefix_state": _native.LA_OP_PREFIX_STATE, "decode": _native.LA_OP_DECODE,
         "forward_state": _native.LA_OP_FORWARD_STATE, "backward_state": _native.LA_OP_BACKWARD_STATE,
         "retention_forward": _native.LA_OP_RETENTION_FORWARD,
-        "retention_backward": _native.LA_OP_RETENTION_BACKWARD}
+        "retention_backward": _native.LA_OP_RETENTION_BACKWARD, "poly_backward": _native.LA_OP_POLY_BACKWARD}
 
 
 def workspace_bytes(op: str, B, H, N, D, M, causal=True, dtype="f32", plan=None) -> int:
@@ -404,6 +404,29 @@ def poly_forward(q, k, v, causal=True, out=None, den=None, return_den=False, str
     _native.check(_native.load().la_poly_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _ptr(den),
                                                  B, H, N, D, M, int(bool(causal)), _dtype_code(q), _stream(stream)))
     return (out, den) if return_den else out
+
+
+def poly_backward(q, k, v, out, dout, den, causal=True, stream=None, workspace=None):
+    """Gradients (dq, dk, dv) of sum(dout * out) for poly_forward, given its
+    out and den."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"), (den, "den")):
+        _dev(t, n)
+    B, H, N, D = q.shape
+    M = v.shape[3]
+    if out.shape != v.shape or dout.shape != v.shape or tuple(den.shape) != (B, H, N) or den.dtype != torch.float32:
+        raise ValueError("out, dout must match v; den must be float32 [B,H,N]")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    lib = _native.load()
+    need = int(lib.la_workspace_bytes(_native.LA_OP_POLY_BACKWARD, B, H, N, D, M, int(bool(causal)), _dtype_code(q)))
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    _native.check(lib.la_poly_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                                       den.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, M,
+                                       int(bool(causal)), _dtype_code(q), _ptr(ws), wsz, _stream(stream)))
+    return dq, dk, dv
 
 
 def decode_step(S, Z, q, k, v, out=None, stream=None):

@@ -17,6 +17,7 @@ LA_F32, LA_BF16 = 0, 1
 LA_OP_FORWARD, LA_OP_BACKWARD, LA_OP_PREFIX_STATE, LA_OP_DECODE = 0, 1, 2, 3
 LA_OP_FORWARD_STATE, LA_OP_BACKWARD_STATE = 4, 5
 LA_OP_RETENTION_FORWARD, LA_OP_RETENTION_BACKWARD = 6, 7
+LA_OP_POLY_BACKWARD = 8
 LA_KERNEL_AUTO, LA_KERNEL_GENERIC, LA_KERNEL_MFMA = 0, 1, 2
 
 # Every symbol include/linattn.h declares.
@@ -29,6 +30,7 @@ EXPORTS = (
     "la_retention_decode_step",
     "la_retention_saved_bytes",
     "la_poly_forward",
+    "la_poly_backward",
 )
 
 
@@ -76,6 +78,7 @@ def load() -> ctypes.CDLL:
                                  i32),
         "la_retention_saved_bytes": ([i64, i64, i64, i64, i64, i32], sz),
         "la_poly_forward": ([vp, vp, vp, vp, fp, i64, i64, i64, i64, i64, i32, i32, vp], i32),
+        "la_poly_backward": ([vp, vp, vp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp, sz, vp], i32),
         "la_retention_decode_step": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp], i32),
         "la_retention_backward": ([vp, vp, vp, fp, vp, fp, fp, sz, vp, vp, vp, fp, fp, i64, i64, i64, i64, i64, i32,
                                    vp, sz, vp], i32),

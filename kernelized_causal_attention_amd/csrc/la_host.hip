@@ -31,6 +31,9 @@ hipError_t launch_ret_forward(const SegGeom& g, const void* q, const void* k, co
 int poly_supported(int64_t D, int64_t M, int dtype);
 hipError_t launch_poly_forward(int64_t BH, int64_t N, int D, const void* q, const void* k, const void* v, void* out,
                                float* den, int causal, hipStream_t st);
+hipError_t launch_poly_backward(int64_t BH, int64_t N, int D, const void* q, const void* k, const void* v,
+                                const void* out, const void* dout, const float* den, void* dq, void* dk, void* dv,
+                                float* cvec, int causal, hipStream_t st);
 hipError_t launch_ret_bwd_dq(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg,
                              const void* dy, const float* carry_s, float* r_agg, void* dq, float* a, hipStream_t st);
 hipError_t launch_ret_rscan(const SegGeom& g, float* r_agg, float* dS0, hipStream_t st);
@@ -812,6 +815,42 @@ LA_API la_status la_poly_forward(const void* q, const void* k, const void* v, vo
              "polynomial forward");
 }
 
+LA_API la_status la_poly_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                  const float* den, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
+                                  int64_t D, int64_t M, int causal, int dtype, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  la_status s = check_sizes(B, H, N, D, M, dtype);
+  if (s != LA_OK) return s;
+  if ((s = check_ptr(q, "q", dtype)) || (s = check_ptr(k, "k", dtype)) || (s = check_ptr(v, "v", dtype)) ||
+      (s = check_ptr(out, "out", dtype)) || (s = check_ptr(dout, "dout", dtype)) ||
+      (s = check_ptr(den, "den", LA_F32)) || (s = check_ptr(dq, "dq", dtype)) || (s = check_ptr(dk, "dk", dtype)) ||
+      (s = check_ptr(dv, "dv", dtype)))
+    return s;
+  if (!la::poly_supported(D, M, dtype))
+    return fail(LA_ERR_UNSUPPORTED, "polynomial kernels take bf16 with D = M in {64, 128} (D=%lld, M=%lld, dtype %d)",
+                (long long)D, (long long)M, dtype);
+  if (N * D * 2 >= (int64_t(1) << 31)) return fail(LA_ERR_UNSUPPORTED, "head too large for 32-bit offsets");
+  const int64_t BH = B * H;
+  if (BH * ((N + 63) / 64) > 0xffffffffLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
+  const size_t need = la_workspace_bytes(LA_OP_POLY_BACKWARD, B, H, N, D, M, causal, dtype);
+  if (workspace_bytes < need)
+    return fail(LA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  if (!workspace) return fail(LA_ERR_INVALID, "workspace is NULL (%zu bytes needed)", need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 15) return fail(LA_ERR_INVALID, "workspace must be 16-byte aligned");
+  const size_t es = dtype_size(dtype);
+  const Span ins[] = {span("q", q, BH * N * D, es), span("k", k, BH * N * D, es), span("v", v, BH * N * M, es),
+                      span("out", out, BH * N * M, es), span("dout", dout, BH * N * M, es), span("den", den, BH * N, 4),
+                      span("workspace", workspace, (int64_t)workspace_bytes, 1)};
+  const Span outs[] = {span("dq", dq, BH * N * D, es), span("dk", dk, BH * N * D, es), span("dv", dv, BH * N * M, es)};
+  if ((s = check_disjoint(outs, 3, ins, 7))) return s;
+  return dev(timed("poly.backward", stream,
+                   [&] {
+                     return la::launch_poly_backward(BH, N, (int)D, q, k, v, out, dout, den, dq, dk, dv,
+                                                     static_cast<float*>(workspace), causal ? 1 : 0, stream);
+                   }),
+             "polynomial backward");
+}
+
 LA_API la_status la_decode_step(float* S, float* Z, const void* q, const void* k, const void* v, void* out,
                                 int64_t B, int64_t H, int64_t D, int64_t M, int dtype, hipStream_t stream) {
   la_status s = check_sizes(B, H, 1, D, M, dtype);
@@ -897,6 +936,9 @@ LA_API size_t la_workspace_bytes_ex(int op, int64_t B, int64_t H, int64_t N, int
                                     int dtype, const la_plan* plan) {
   if (op == LA_OP_DECODE) return 0;
   if (check_sizes(B, H, N, D, M, dtype) != LA_OK) return 0;
+  if (op == LA_OP_POLY_BACKWARD)
+    return la::poly_supported(D, M, dtype) ? (static_cast<size_t>(B * H * N) * sizeof(float) + kAlign - 1) / kAlign * kAlign
+                                           : 0;
   Plan p;
   if (resolve(op, B, H, N, D, M, causal ? 1 : 0, dtype, op == LA_OP_PREFIX_STATE ? nullptr : plan, &p) != LA_OK)
     return 0;

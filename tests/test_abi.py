@@ -93,6 +93,14 @@ def test_resolve_plan(lib):
     assert lib.la_resolve_plan(0, 1, 1, 1 << 23, 128, 128, 1, 1, ctypes.byref(mf), ctypes.byref(out)) == 2
 
 
+def test_poly_workspace_and_support(lib):
+    # the polynomial backward keeps one float per row (c_i); other dtypes or
+    # sizes are unsupported (0 bytes)
+    assert lib.la_workspace_bytes(_native.LA_OP_POLY_BACKWARD, 2, 3, 100, 64, 64, 1, 1) >= 2 * 3 * 100 * 4
+    assert lib.la_workspace_bytes(_native.LA_OP_POLY_BACKWARD, 2, 3, 100, 64, 64, 1, 0) == 0
+    assert lib.la_workspace_bytes(_native.LA_OP_POLY_BACKWARD, 2, 3, 100, 32, 32, 1, 1) == 0
+
+
 def test_retention_segments_are_capped(lib):
     # 512 heads fill the chip with one segment each; the retention calls
     # still cut each head into segments of at most 1024 tokens (the
