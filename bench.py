@@ -23,6 +23,9 @@ Extra fields:
   retention     -- decayed / gated linear attention forward+backward on the
                    same shape (gates gamma_t ~ U(0.6, 1)): tokens/s and the
                    dominant kernel's HBM roofline.
+  poly          -- degree-2 polynomial-kernel attention forward+backward on
+                   the same shape: tokens/s and the dominant kernel's MFMA
+                   roofline (TFLOP/s against the dense bf16 peak).
 """
 
 from __future__ import annotations
@@ -39,6 +42,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 
 def log(*a):
@@ -56,6 +60,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--retention-only", action="store_true",
                     help="run only the retention forward+backward measurement (for profiling) and print it")
+    ap.add_argument("--poly-only", action="store_true",
+                    help="run only the polynomial-kernel forward+backward measurement (for profiling) and print it")
     ap.add_argument("--settle", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps (the GPU raises its clocks "
                          "over the first few hundred milliseconds of load)")
@@ -107,6 +113,16 @@ def kernel_bytes(name: str, B, H, N, D, M, es, P=1):
     return 0
 
 
+def kernel_flops(name: str, B, H, N, D, M, causal=True):
+    """Matrix-product flops one launch of a polynomial-kernel pass performs
+    over the query-key pairs it must visit (N (N + 1) / 2 per head causal):
+    forward s = q.k and P V (2D + 2M per pair); dq sweep s, g.v and dS K
+    (4D + 2M); dk / dv sweep s, g.v, P^T g and dS^T q (4D + 4M)."""
+    pairs = B * H * (N * (N + 1) // 2 if causal else N * N)
+    per = {"poly.forward": 2 * D + 2 * M, "poly.bwd_dq": 4 * D + 2 * M, "poly.bwd_dkdv": 4 * D + 4 * M}
+    return pairs * per.get(name, 0)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -127,6 +143,10 @@ def main():
     if args.retention_only:
         torch.cuda.set_device(0)
         print(json.dumps(bench_retention(la, torch, args.steps, args.warmup)), flush=True)
+        return
+    if args.poly_only:
+        torch.cuda.set_device(0)
+        print(json.dumps(bench_poly(la, torch, args.steps, args.warmup)), flush=True)
         return
 
     w = WORKLOADS["fwdbwd_bf16"]
@@ -224,6 +244,7 @@ def main():
     if not args.no_extra:
         result["decode"] = bench_decode(la, torch, args.decode_steps)
         result["retention"] = bench_retention(la, torch, args.steps, args.warmup)
+        result["poly"] = bench_poly(la, torch, args.steps, args.warmup)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(q, k, v, g, B, H, N, args.cpu_seconds)
@@ -392,6 +413,71 @@ def bench_retention(la, torch, steps, warmup):
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": measured_traffic(kname, TRAFFIC_FILE_RET),
                          "alg_bytes_per_launch": kb, "avg_launch_ms": round(avg_ms, 4)},
+            "kernels": kernels}
+
+
+def bench_poly(la, torch, steps, warmup):
+    """Degree-2 polynomial-kernel attention forward + backward on the same
+    bf16 shape as the main step: tokens/s and the dominant kernel's MFMA
+    roofline (matrix-product flops over its time, against the dense bf16
+    peak)."""
+    from workloads import WORKLOADS, device_inputs
+
+    w = WORKLOADS["fwdbwd_bf16"]
+    B, H, N, D, M = w.B, w.H, w.N, w.D, w.M
+    dev = "cuda"
+    q, k, v, g = device_inputs(B, H, N, D, M, "bf16", seed=3, scale=1.0 / D ** 0.5, device=dev)
+    out = torch.empty((B, H, N, M), dtype=torch.bfloat16, device=dev)
+    den = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, la.workspace_bytes("poly_backward", B, H, N, D, M, True, "bf16")), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        la.poly_forward(q, k, v, out=out, den=den)
+        return la.poly_backward(q, k, v, out, g, den, workspace=ws)
+
+    for _ in range(warmup + 3):
+        step()
+    torch.cuda.synchronize()
+    la.profile_enable(True)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    prof = la.profile_report()
+    kname = max(prof.items(), key=lambda kv: kv[1][1])[0]
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    la.profile_enable(True, only=kname)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    nl, tot_ms = la.profile_report()[kname]
+    la.profile_enable(False)
+    ms = e0.elapsed_time(e1) / steps
+    kernels = {}
+    for name, (n, t) in sorted(prof.items()):
+        f = kernel_flops(name, B, H, N, D, M)
+        avg = t / n
+        kernels[name] = {"launches_per_step": n / 3, "avg_ms": round(avg, 4), "flops": f,
+                         "TFLOPs": round(f / (avg / 1e3) / 1e12, 1)}
+    avg_ms = tot_ms / nl
+    kf = kernels[kname]["flops"]
+    tf = kf / (avg_ms / 1e3) / 1e12
+    step_tf = sum(v["flops"] for v in kernels.values()) / (ms / 1e3) / 1e12
+    log(f"poly: {ms:.3f} ms/step, {B * N / (ms / 1e3):.4g} tokens/s, {step_tf:.0f} TFLOP/s over the step; dominant "
+        f"{kname} {avg_ms:.4f} ms {tf:.0f} TFLOP/s; breakdown {prof}")
+    return {"metric": "polynomial-kernel (degree-2) causal attention fwd+bwd tokens/sec",
+            "value": round(B * N / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+            "step_tflops": round(step_tf, 1),
+            "config": {"workload": "(q.k)^2 causal attention forward+backward, bf16 in / fp32 accumulate",
+                       "B": B, "H": H, "N": N, "D": D, "M": M},
+            "roofline": {"bound": "mfma", "kernel": kname, "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                         "flops_per_launch": kf, "avg_launch_ms": round(avg_ms, 4)},
             "kernels": kernels}
 
 

@@ -31,9 +31,9 @@ hipError_t launch_ret_forward(const SegGeom& g, const void* q, const void* k, co
 int poly_supported(int64_t D, int64_t M, int dtype);
 hipError_t launch_poly_forward(int64_t BH, int64_t N, int D, const void* q, const void* k, const void* v, void* out,
                                float* den, int causal, hipStream_t st);
-hipError_t launch_poly_backward(int64_t BH, int64_t N, int D, const void* q, const void* k, const void* v,
-                                const void* out, const void* dout, const float* den, void* dq, void* dk, void* dv,
-                                float* cvec, int causal, hipStream_t st);
+hipError_t launch_poly_bwd(int pass, int64_t BH, int64_t N, int D, const void* q, const void* k, const void* v,
+                           const void* out, const void* dout, const float* den, void* dq, void* dk, void* dv,
+                           float* cvec, int causal, hipStream_t st);
 hipError_t launch_ret_bwd_dq(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg,
                              const void* dy, const float* carry_s, float* r_agg, void* dq, float* a, hipStream_t st);
 hipError_t launch_ret_rscan(const SegGeom& g, float* r_agg, float* dS0, hipStream_t st);
@@ -843,12 +843,19 @@ LA_API la_status la_poly_backward(const void* q, const void* k, const void* v, c
                       span("workspace", workspace, (int64_t)workspace_bytes, 1)};
   const Span outs[] = {span("dq", dq, BH * N * D, es), span("dk", dk, BH * N * D, es), span("dv", dv, BH * N * M, es)};
   if ((s = check_disjoint(outs, 3, ins, 7))) return s;
-  return dev(timed("poly.backward", stream,
+  float* cvec = static_cast<float*>(workspace);
+  hipError_t e;
+  if ((e = timed("poly.bwd_dq", stream, [&] {
+         return la::launch_poly_bwd(0, BH, N, (int)D, q, k, v, out, dout, den, dq, dk, dv, cvec, causal ? 1 : 0,
+                                    stream);
+       })))
+    return dev(e, "polynomial backward (dq)");
+  return dev(timed("poly.bwd_dkdv", stream,
                    [&] {
-                     return la::launch_poly_backward(BH, N, (int)D, q, k, v, out, dout, den, dq, dk, dv,
-                                                     static_cast<float*>(workspace), causal ? 1 : 0, stream);
+                     return la::launch_poly_bwd(1, BH, N, (int)D, q, k, v, out, dout, den, dq, dk, dv, cvec,
+                                                causal ? 1 : 0, stream);
                    }),
-             "polynomial backward");
+             "polynomial backward (dk, dv)");
 }
 
 LA_API la_status la_decode_step(float* S, float* Z, const void* q, const void* k, const void* v, void* out,

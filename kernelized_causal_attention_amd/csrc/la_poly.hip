@@ -469,13 +469,13 @@ hipError_t launch_poly_forward(int64_t BH, int64_t N, int D, const void* q, cons
 
 namespace la {
 
-hipError_t launch_poly_backward(int64_t BH, int64_t N, int D, const void* q, const void* k, const void* v,
-                                const void* out, const void* dout, const float* den, void* dq, void* dk, void* dv,
-                                float* cvec, int causal, hipStream_t st) {
+hipError_t launch_poly_bwd(int pass, int64_t BH, int64_t N, int D, const void* q, const void* k, const void* v,
+                           const void* out, const void* dout, const float* den, void* dq, void* dk, void* dv,
+                           float* cvec, int causal, hipStream_t st) {
+  // pass 0: the dq sweep (also writes c); pass 1: the dk / dv sweep
   const int bq = 64 * poly_bwd_tiles(D);
-  const int nqb = static_cast<int>((N + bq - 1) / bq);
-  const int nkb = nqb;
-  const dim3 gq(static_cast<unsigned>(BH * nqb)), gk(static_cast<unsigned>(BH * nkb)), block(NT);
+  const int nb = static_cast<int>((N + bq - 1) / bq);
+  const dim3 grid(static_cast<unsigned>(BH * nb)), block(NT);
   const bf16_t* Q = static_cast<const bf16_t*>(q);
   const bf16_t* K = static_cast<const bf16_t*>(k);
   const bf16_t* V = static_cast<const bf16_t*>(v);
@@ -484,11 +484,12 @@ hipError_t launch_poly_backward(int64_t BH, int64_t N, int D, const void* q, con
   bf16_t* dQ = static_cast<bf16_t*>(dq);
   bf16_t* dK = static_cast<bf16_t*>(dk);
   bf16_t* dV = static_cast<bf16_t*>(dv);
-#define LA_PBWD(DIMV, C)                                                                                       \
-  do {                                                                                                         \
-    hipLaunchKernelGGL((k_poly_dq<DIMV, C>), gq, block, 0, st, Q, K, V, O, dO, den, dQ, cvec, N, nqb, BH);     \
-    if (hipError_t e_ = hipGetLastError()) return e_;                                                          \
-    hipLaunchKernelGGL((k_poly_dkdv<DIMV, C>), gk, block, 0, st, Q, K, V, dO, den, cvec, dK, dV, N, BH);      \
+#define LA_PBWD(DIMV, C)                                                                                     \
+  do {                                                                                                       \
+    if (pass == 0)                                                                                           \
+      hipLaunchKernelGGL((k_poly_dq<DIMV, C>), grid, block, 0, st, Q, K, V, O, dO, den, dQ, cvec, N, nb, BH); \
+    else                                                                                                     \
+      hipLaunchKernelGGL((k_poly_dkdv<DIMV, C>), grid, block, 0, st, Q, K, V, dO, den, cvec, dK, dV, N, BH); \
   } while (0)
   if (D == 64) {
     if (causal) LA_PBWD(64, true); else LA_PBWD(64, false);
