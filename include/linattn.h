@@ -275,6 +275,29 @@ la_status la_poly_backward(const void* q, const void* k, const void* v, const vo
                            int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
                            int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The polynomial map's linear-form state after N tokens ("[Paper
+ * walkthrough] Transformers are RNNs", section 2, item (3), with eq:mask's
+ * S, Z): S[c][m] = sum_t phi(k_t)_c v_t[m], Z[c] = sum_t phi(k_t)_c, with
+ * phi(k)_{a D + b} = k_a k_b (C = D^2 rows).
+ *   k: [B,H,N,D], v: [B,H,N,M] (bf16, D = M in {64, 128});
+ *   S: [B,H,D*D,M] fp32, Z: [B,H,D*D] fp32 (outputs, overwritten).
+ * The products enter the state rounded to bf16 once; Z sums them in fp32.
+ * No workspace. */
+la_status la_poly_prefix_state(const void* k, const void* v, float* S, float* Z, int64_t B,
+                               int64_t H, int64_t N, int64_t D, int64_t M, int dtype,
+                               hipStream_t stream);
+
+/* One recurrent step of the polynomial map per (b,h), in place (the
+ * section 4 loop with phi(x)_{a D + b} = x_a x_b):
+ *   S <- S + phi(k) v^T,  Z <- Z + phi(k),  out = phi(q)^T S / phi(q)^T Z
+ * (0 where the denominator is 0).
+ *   S: [B,H,D*D,M], Z: [B,H,D*D] fp32 (read and written, caller-owned);
+ *   q, k: [B,H,D], v, out: [B,H,M] (fp32 or bf16); D a power of two <= 128,
+ *   M <= 256.  No workspace. */
+la_status la_poly_decode_step(float* S, float* Z, const void* q, const void* k, const void* v,
+                              void* out, int64_t B, int64_t H, int64_t D, int64_t M, int dtype,
+                              hipStream_t stream);
+
 /* One RNN decode step per (b,h), in place ("Transformers are RNNs"
  * walkthrough, section 4; the state is updated first, then read):
  *   S <- S + phi(k) v^T;  Z <- Z + phi(k);  out = phi(q)^T S / phi(q)^T Z.

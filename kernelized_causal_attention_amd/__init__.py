@@ -20,7 +20,7 @@ from ._native import LinAttnError, la_plan  # noqa: F401
 __all__ = [
     "forward", "backward", "forward_state", "backward_state", "decode_step", "prefix_state", "workspace_bytes",
     "saved_bytes", "resolve_plan", "retention_forward", "retention_backward", "retention_decode_step",
-    "retention_saved_bytes", "poly_forward", "poly_backward",
+    "retention_saved_bytes", "poly_forward", "poly_backward", "poly_prefix_state", "poly_decode_step",
     "LinAttnError", "library_path", "version", "profile_enable", "profile_report",
 ]
 
@@ -427,6 +427,39 @@ def poly_backward(q, k, v, out, dout, den, causal=True, stream=None, workspace=N
                                        den.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, M,
                                        int(bool(causal)), _dtype_code(q), _ptr(ws), wsz, _stream(stream)))
     return dq, dk, dv
+
+
+def poly_prefix_state(k, v, stream=None):
+    """(S, Z) of the polynomial map after the given tokens: S [B,H,D*D,M],
+    Z [B,H,D*D] fp32 (bf16 k, v; D = M in {64, 128})."""
+    torch = _torch()
+    _dev(k, "k")
+    _dev(v, "v")
+    B, H, N, D = k.shape
+    M = v.shape[3]
+    S = torch.empty((B, H, D * D, M), dtype=torch.float32, device=k.device)
+    Z = torch.empty((B, H, D * D), dtype=torch.float32, device=k.device)
+    _native.check(_native.load().la_poly_prefix_state(k.data_ptr(), v.data_ptr(), S.data_ptr(), Z.data_ptr(), B, H, N,
+                                                      D, M, _dtype_code(k), _stream(stream)))
+    return S, Z
+
+
+def poly_decode_step(S, Z, q, k, v, out=None, stream=None):
+    """One polynomial-map recurrent step in place: S += phi(k) v^T,
+    Z += phi(k); returns phi(q)^T S / phi(q)^T Z (q, k [B,H,D], v [B,H,M])."""
+    torch = _torch()
+    for t, n in ((S, "S"), (Z, "Z"), (q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    B, H, D = q.shape
+    M = v.shape[2]
+    if tuple(S.shape) != (B, H, D * D, M) or tuple(Z.shape) != (B, H, D * D):
+        raise ValueError("S must be [B,H,D*D,M] and Z [B,H,D*D] (float32)")
+    if out is None:
+        out = torch.empty((B, H, M), dtype=q.dtype, device=q.device)
+    _native.check(_native.load().la_poly_decode_step(S.data_ptr(), Z.data_ptr(), q.data_ptr(), k.data_ptr(),
+                                                     v.data_ptr(), out.data_ptr(), B, H, D, M, _dtype_code(q),
+                                                     _stream(stream)))
+    return out
 
 
 def decode_step(S, Z, q, k, v, out=None, stream=None):

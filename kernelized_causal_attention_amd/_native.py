@@ -31,6 +31,8 @@ EXPORTS = (
     "la_retention_saved_bytes",
     "la_poly_forward",
     "la_poly_backward",
+    "la_poly_prefix_state",
+    "la_poly_decode_step",
 )
 
 
@@ -77,6 +79,8 @@ def load() -> ctypes.CDLL:
         "la_retention_forward": ([vp, vp, vp, fp, vp, i64, i64, i64, i64, i64, i32, fp, fp, fp, sz, vp, sz, vp],
                                  i32),
         "la_retention_saved_bytes": ([i64, i64, i64, i64, i64, i32], sz),
+        "la_poly_prefix_state": ([vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp], i32),
+        "la_poly_decode_step": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp], i32),
         "la_poly_forward": ([vp, vp, vp, vp, fp, i64, i64, i64, i64, i64, i32, i32, vp], i32),
         "la_poly_backward": ([vp, vp, vp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp, sz, vp], i32),
         "la_retention_decode_step": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp], i32),

@@ -15,11 +15,17 @@
 // partials, which an LDS pass reduces in a fixed order.  The denominator
 // phi(q)^T Z is a wavefront reduction.
 //
-// The same kernels take the decayed recurrence ("08 - Transformer and
-// Variants", by-xin.github.io, section 1.3.4) when RET is set: S <- gamma S +
-// k v^T and y = S^T q, with no feature map and no normaliser, gamma =
-// exp(log gamma) per (b,h) (log gamma below -80 taken as -80, as in the
-// chunked kernels; NaN passes through).
+// The same kernels take two more recurrences (MODE):
+// * kRet, the decayed recurrence ("08 - Transformer and Variants",
+//   by-xin.github.io, section 1.3.4): S <- gamma S + k v^T and y = S^T q,
+//   with no feature map and no normaliser, gamma = exp(log gamma) per (b,h)
+//   (log gamma below -80 taken as -80, as in the chunked kernels; NaN passes
+//   through);
+// * kPoly, the degree-2 polynomial feature map ("[Paper walkthrough]
+//   Transformers are RNNs", section 2, "feature map and computation cost",
+//   item (3)): C = D^2 state rows, phi(x)[a D + b] = x_a x_b formed on the fly
+//   from the D raw values in LDS (D a power of two), and out = 0 where the
+//   denominator is 0.
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -27,6 +33,15 @@ namespace la {
 namespace {
 
 constexpr int NT = 256;
+constexpr int kLin = 0, kRet = 1, kPoly = 2;
+
+// Feature c of the row: phi(x)_c from LDS (kLin: phi stored; kRet: x stored;
+// kPoly: x stored, c = a D + b -> x_a x_b).
+template <int MODE>
+__device__ __forceinline__ float feat(const float* f_s, int c, int lgD) {
+  if (MODE == kPoly) return f_s[c >> lgD] * f_s[c & ((1 << lgD) - 1)];
+  return f_s[c];
+}
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -34,32 +49,40 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Phase 1, shared by both kernels: phi(q), phi(k) and v into LDS, Z updated
-// in place, and den = phi(q)^T Z' (fixed-order reduction).  RET: q, k as
-// given, no Z, den = 1.
-template <bool RET, typename TIn>
+// Phase 1, shared by both kernels: phi(q), phi(k) (kLin) or q, k (kRet,
+// kPoly) and v into LDS, Z updated in place over the C state rows, and
+// den = phi(q)^T Z' (fixed-order reduction; 1 for kRet, which has no Z).
+template <int MODE, typename TIn>
 __device__ __forceinline__ float decode_prologue(float* qf_s, float* kf_s, float* v_s, float* wden,
                                                  float* __restrict__ Z, const TIn* __restrict__ q,
                                                  const TIn* __restrict__ k, const TIn* __restrict__ v,
-                                                 int64_t bh, int D, int M) {
+                                                 int64_t bh, int D, int C, int lgD, int M) {
   const int t = threadIdx.x;
-  float part = 0.f;
   for (int d = t; d < D; d += NT) {
-    const float kf = RET ? ld(k, bh * D + d) : phi(ld(k, bh * D + d));
-    const float qf = RET ? ld(q, bh * D + d) : phi(ld(q, bh * D + d));
-    kf_s[d] = kf;
-    qf_s[d] = qf;
-    if (!RET) {
-      const float z = Z[bh * D + d] + kf;
-      Z[bh * D + d] = z;
-      part += qf * z;
-    }
+    kf_s[d] = MODE == kLin ? phi(ld(k, bh * D + d)) : ld(k, bh * D + d);
+    qf_s[d] = MODE == kLin ? phi(ld(q, bh * D + d)) : ld(q, bh * D + d);
   }
   for (int m = t; m < M; m += NT) v_s[m] = ld(v, bh * M + m);
+  if (MODE == kPoly) __syncthreads();  // the features read other threads' entries
+  float part = 0.f;
+  if (MODE != kRet) {
+    for (int c = t; c < C; c += NT) {
+      const float z = Z[bh * C + c] + feat<MODE>(kf_s, c, lgD);
+      Z[bh * C + c] = z;
+      part += feat<MODE>(qf_s, c, lgD) * z;
+    }
+  }
   part = wave_sum(part);
   if ((t & 63) == 0) wden[t >> 6] = part;
   __syncthreads();
-  return RET ? 1.f : ((wden[0] + wden[1]) + wden[2]) + wden[3];
+  return MODE == kRet ? 1.f : ((wden[0] + wden[1]) + wden[2]) + wden[3];
+}
+
+template <int MODE>
+__device__ __forceinline__ float readout(float o, float den) {
+  if (MODE == kRet) return o;
+  if (MODE == kPoly) return den > 0.f ? o / den : 0.f;
+  return o / den;
 }
 
 __device__ __forceinline__ float decay_of(const float* __restrict__ lg, int64_t bh) {
@@ -68,11 +91,11 @@ __device__ __forceinline__ float decay_of(const float* __restrict__ lg, int64_t 
 }
 
 // Vector path: M/4 threads per row, NT/(M/4) rows per pass, U rows in flight.
-template <typename TIn, int TPR, bool RET>
+template <typename TIn, int TPR, int MODE>
 __global__ __launch_bounds__(NT) void k_decode_vec(float* __restrict__ S, float* __restrict__ Z,
                                                    const TIn* __restrict__ q, const TIn* __restrict__ k,
                                                    const TIn* __restrict__ v, const float* __restrict__ lg,
-                                                   TIn* __restrict__ out, int D) {
+                                                   TIn* __restrict__ out, int D, int C, int lgD) {
   constexpr int M = TPR * 4;
   constexpr int RPI = NT / TPR;
   constexpr int U = 16;
@@ -80,26 +103,26 @@ __global__ __launch_bounds__(NT) void k_decode_vec(float* __restrict__ S, float*
   __shared__ float red[RPI * M];
   const int64_t bh = blockIdx.x;
   const int t = threadIdx.x;
-  const float den = decode_prologue<RET>(qf_s, kf_s, v_s, wden, Z, q, k, v, bh, D, M);
-  const float gam = RET ? decay_of(lg, bh) : 1.f;
+  const float den = decode_prologue<MODE>(qf_s, kf_s, v_s, wden, Z, q, k, v, bh, D, C, lgD, M);
+  const float gam = MODE == kRet ? decay_of(lg, bh) : 1.f;
   const int c4 = t % TPR, rg = t / TPR;
   const f32x4 vv = {v_s[4 * c4], v_s[4 * c4 + 1], v_s[4 * c4 + 2], v_s[4 * c4 + 3]};
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  f32x4* Sh = reinterpret_cast<f32x4*>(S + bh * static_cast<int64_t>(D) * M) + c4;
-  for (int d0 = rg; d0 < D; d0 += RPI * U) {
+  f32x4* Sh = reinterpret_cast<f32x4*>(S + bh * static_cast<int64_t>(C) * M) + c4;
+  for (int d0 = rg; d0 < C; d0 += RPI * U) {
     f32x4 sv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int d = d0 + u * RPI;
-      if (d < D) sv[u] = __builtin_nontemporal_load(Sh + static_cast<int64_t>(d) * TPR);
+      if (d < C) sv[u] = __builtin_nontemporal_load(Sh + static_cast<int64_t>(d) * TPR);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int d = d0 + u * RPI;
-      if (d < D) {
-        const f32x4 s = (RET ? gam * sv[u] : sv[u]) + kf_s[d] * vv;
+      if (d < C) {
+        const f32x4 s = (MODE == kRet ? gam * sv[u] : sv[u]) + feat<MODE>(kf_s, d, lgD) * vv;
         __builtin_nontemporal_store(s, Sh + static_cast<int64_t>(d) * TPR);
-        acc += qf_s[d] * s;
+        acc += feat<MODE>(qf_s, d, lgD) * s;
       }
     }
   }
@@ -112,33 +135,33 @@ __global__ __launch_bounds__(NT) void k_decode_vec(float* __restrict__ S, float*
     float o = 0.f;
 #pragma unroll
     for (int r = 0; r < RPI; ++r) o += red[r * M + m];
-    st(out, bh * M + m, RET ? o : o / den);
+    st(out, bh * M + m, readout<MODE>(o, den));
   }
 }
 
 // Scalar path for any M <= 256: one thread per column, NT/M rows per pass.
-template <typename TIn, bool RET>
+template <typename TIn, int MODE>
 __global__ __launch_bounds__(NT) void k_decode_scalar(float* __restrict__ S, float* __restrict__ Z,
                                                       const TIn* __restrict__ q, const TIn* __restrict__ k,
                                                       const TIn* __restrict__ v, const float* __restrict__ lg,
-                                                      TIn* __restrict__ out, int D, int M) {
+                                                      TIn* __restrict__ out, int D, int C, int lgD, int M) {
   __shared__ float qf_s[256], kf_s[256], v_s[256], wden[4];
   __shared__ float red[NT];
   const int64_t bh = blockIdx.x;
   const int t = threadIdx.x;
-  const float den = decode_prologue<RET>(qf_s, kf_s, v_s, wden, Z, q, k, v, bh, D, M);
-  const float gam = RET ? decay_of(lg, bh) : 1.f;
+  const float den = decode_prologue<MODE>(qf_s, kf_s, v_s, wden, Z, q, k, v, bh, D, C, lgD, M);
+  const float gam = MODE == kRet ? decay_of(lg, bh) : 1.f;
   const int rpi = NT / M;
   const int m = t % M, rg = t / M;
   float acc = 0.f;
   if (rg < rpi) {
-    float* Sh = S + bh * static_cast<int64_t>(D) * M + m;
+    float* Sh = S + bh * static_cast<int64_t>(C) * M + m;
     const float vm = v_s[m];
-    for (int d = rg; d < D; d += rpi) {
+    for (int d = rg; d < C; d += rpi) {
       const float s0 = Sh[static_cast<int64_t>(d) * M];
-      const float s = (RET ? gam * s0 : s0) + kf_s[d] * vm;
+      const float s = (MODE == kRet ? gam * s0 : s0) + feat<MODE>(kf_s, d, lgD) * vm;
       Sh[static_cast<int64_t>(d) * M] = s;
-      acc += qf_s[d] * s;
+      acc += feat<MODE>(qf_s, d, lgD) * s;
     }
     red[rg * M + m] = acc;
   }
@@ -146,18 +169,21 @@ __global__ __launch_bounds__(NT) void k_decode_scalar(float* __restrict__ S, flo
   for (int mm = t; mm < M; mm += NT) {
     float o = 0.f;
     for (int r = 0; r < rpi; ++r) o += red[r * M + mm];
-    st(out, bh * M + mm, RET ? o : o / den);
+    st(out, bh * M + mm, readout<MODE>(o, den));
   }
 }
 
-template <bool RET>
+template <int MODE>
 hipError_t launch_decode(int dtype, int64_t BH, int D, int M, float* S, float* Z, const void* q, const void* k,
                          const void* v, const float* lg, void* out, hipStream_t st) {
+  int lgD = 0;
+  while ((1 << lgD) < D) ++lgD;
+  const int C = MODE == kPoly ? D * D : D;
   const dim3 grid(static_cast<unsigned>(BH)), block(NT);
   const bool aligned = (reinterpret_cast<uintptr_t>(S) & 15u) == 0;
 #define LA_DEC_VEC(T, TPR)                                                                              \
-  hipLaunchKernelGGL((k_decode_vec<T, TPR, RET>), grid, block, 0, st, S, Z, static_cast<const T*>(q),   \
-                     static_cast<const T*>(k), static_cast<const T*>(v), lg, static_cast<T*>(out), D); \
+  hipLaunchKernelGGL((k_decode_vec<T, TPR, MODE>), grid, block, 0, st, S, Z, static_cast<const T*>(q),  \
+                     static_cast<const T*>(k), static_cast<const T*>(v), lg, static_cast<T*>(out), D, C, lgD); \
   return hipGetLastError()
 #define LA_DEC(T)                                                                                        \
   if (aligned && M % 4 == 0) {                                                                           \
@@ -172,8 +198,8 @@ hipError_t launch_decode(int dtype, int64_t BH, int D, int M, float* S, float* Z
       default: break;                                                                                    \
     }                                                                                                    \
   }                                                                                                      \
-  hipLaunchKernelGGL((k_decode_scalar<T, RET>), grid, block, 0, st, S, Z, static_cast<const T*>(q),      \
-                     static_cast<const T*>(k), static_cast<const T*>(v), lg, static_cast<T*>(out), D, M); \
+  hipLaunchKernelGGL((k_decode_scalar<T, MODE>), grid, block, 0, st, S, Z, static_cast<const T*>(q),     \
+                     static_cast<const T*>(k), static_cast<const T*>(v), lg, static_cast<T*>(out), D, C, lgD, M); \
   return hipGetLastError()
   if (dtype == 0) {
     LA_DEC(float);
@@ -188,12 +214,17 @@ hipError_t launch_decode(int dtype, int64_t BH, int D, int M, float* S, float* Z
 
 hipError_t launch_decode_step(int dtype, int64_t BH, int D, int M, float* S, float* Z, const void* q,
                               const void* k, const void* v, void* out, hipStream_t st) {
-  return launch_decode<false>(dtype, BH, D, M, S, Z, q, k, v, nullptr, out, st);
+  return launch_decode<kLin>(dtype, BH, D, M, S, Z, q, k, v, nullptr, out, st);
 }
 
 hipError_t launch_ret_decode_step(int dtype, int64_t BH, int D, int M, float* S, const void* q, const void* k,
                                   const void* v, const float* lg, void* y, hipStream_t st) {
-  return launch_decode<true>(dtype, BH, D, M, S, nullptr, q, k, v, lg, y, st);
+  return launch_decode<kRet>(dtype, BH, D, M, S, nullptr, q, k, v, lg, y, st);
+}
+
+hipError_t launch_poly_decode_step(int dtype, int64_t BH, int D, int M, float* S, float* Z, const void* q,
+                                   const void* k, const void* v, void* out, hipStream_t st) {
+  return launch_decode<kPoly>(dtype, BH, D, M, S, Z, q, k, v, nullptr, out, st);
 }
 
 }  // namespace la

@@ -31,6 +31,8 @@ hipError_t launch_ret_forward(const SegGeom& g, const void* q, const void* k, co
 int poly_supported(int64_t D, int64_t M, int dtype);
 hipError_t launch_poly_forward(int64_t BH, int64_t N, int D, const void* q, const void* k, const void* v, void* out,
                                float* den, int causal, hipStream_t st);
+hipError_t launch_poly_state(int64_t BH, int64_t N, int D, const void* k, const void* v, float* S, float* Z,
+                             hipStream_t st);
 hipError_t launch_poly_bwd(int pass, int64_t BH, int64_t N, int D, const void* q, const void* k, const void* v,
                            const void* out, const void* dout, const float* den, void* dq, void* dk, void* dv,
                            float* cvec, int causal, hipStream_t st);
@@ -856,6 +858,47 @@ LA_API la_status la_poly_backward(const void* q, const void* k, const void* v, c
                                                 causal ? 1 : 0, stream);
                    }),
              "polynomial backward (dk, dv)");
+}
+
+LA_API la_status la_poly_prefix_state(const void* k, const void* v, float* S, float* Z, int64_t B, int64_t H,
+                                      int64_t N, int64_t D, int64_t M, int dtype, hipStream_t stream) {
+  la_status s = check_sizes(B, H, N, D, M, dtype);
+  if (s != LA_OK) return s;
+  if ((s = check_ptr(k, "k", dtype)) || (s = check_ptr(v, "v", dtype)) || (s = check_ptr(S, "S", LA_F32)) ||
+      (s = check_ptr(Z, "Z", LA_F32)))
+    return s;
+  if (!la::poly_supported(D, M, dtype))
+    return fail(LA_ERR_UNSUPPORTED, "polynomial kernels take bf16 with D = M in {64, 128} (D=%lld, M=%lld, dtype %d)",
+                (long long)D, (long long)M, dtype);
+  if (N * D * 2 >= (int64_t(1) << 31)) return fail(LA_ERR_UNSUPPORTED, "head too large for 32-bit offsets");
+  const int64_t BH = B * H;
+  if (BH * D * (D / 64) > 0xffffffffLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
+  const size_t es = dtype_size(dtype);
+  const Span ins[] = {span("k", k, BH * N * D, es), span("v", v, BH * N * M, es)};
+  const Span outs[] = {span("S", S, BH * D * D * M, 4), span("Z", Z, BH * D * D, 4)};
+  if ((s = check_disjoint(outs, 2, ins, 2))) return s;
+  return dev(timed("poly.state", stream, [&] { return la::launch_poly_state(BH, N, (int)D, k, v, S, Z, stream); }),
+             "polynomial prefix state");
+}
+
+LA_API la_status la_poly_decode_step(float* S, float* Z, const void* q, const void* k, const void* v, void* out,
+                                     int64_t B, int64_t H, int64_t D, int64_t M, int dtype, hipStream_t stream) {
+  la_status s = check_sizes(B, H, 1, D, M, dtype);
+  if (s != LA_OK) return s;
+  if ((s = check_ptr(S, "S", LA_F32)) || (s = check_ptr(Z, "Z", LA_F32)) || (s = check_ptr(q, "q", dtype)) ||
+      (s = check_ptr(k, "k", dtype)) || (s = check_ptr(v, "v", dtype)) || (s = check_ptr(out, "out", dtype)))
+    return s;
+  if (D > 128 || (D & (D - 1)))
+    return fail(LA_ERR_UNSUPPORTED, "polynomial decode takes D a power of two <= 128 (D=%lld)", (long long)D);
+  const int64_t BH = B * H;
+  const size_t es = dtype_size(dtype);
+  const Span ins[] = {span("q", q, BH * D, es), span("k", k, BH * D, es), span("v", v, BH * M, es)};
+  const Span outs[] = {span("S", S, BH * D * D * M, 4), span("Z", Z, BH * D * D, 4), span("out", out, BH * M, es)};
+  if ((s = check_disjoint(outs, 3, ins, 3))) return s;
+  if (BH > 0xffffffffLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
+  return dev(timed("poly.decode", stream,
+                   [&] { return la::launch_poly_decode_step(dtype, BH, (int)D, (int)M, S, Z, q, k, v, out, stream); }),
+             "polynomial decode step");
 }
 
 LA_API la_status la_decode_step(float* S, float* Z, const void* q, const void* k, const void* v, void* out,

@@ -63,6 +63,8 @@ hipError_t launch_bwd_dkdv_generic(int dtype, int causal, const SegGeom& g, cons
                                    const float* carry_r, void* dk, void* dv, hipStream_t st);
 
 // ---- decode ----
+hipError_t launch_poly_decode_step(int dtype, int64_t BH, int D, int M, float* S, float* Z, const void* q,
+                                   const void* k, const void* v, void* out, hipStream_t st);
 hipError_t launch_ret_decode_step(int dtype, int64_t BH, int D, int M, float* S, const void* q, const void* k,
                                   const void* v, const float* lg, void* y, hipStream_t st);
 hipError_t launch_decode_step(int dtype, int64_t BH, int D, int M, float* S, float* Z, const void* q,

@@ -441,6 +441,85 @@ __global__ __launch_bounds__(NT, 2) void k_poly_dkdv(const bf16_t* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------------------
+// The linear form's state after a prefix: S[c][m] = sum_t phi(k_t)_c v_t[m],
+// Z[c] = sum_t phi(k_t)_c, c = a D + b, phi(k)_c = k_a k_b (D^2 x M fp32 per
+// head, the recurrence's S_N, Z_N).  A workgroup owns the 64 rows
+// c = a D + b0 .. a D + b0 + 63 (wave w: 16 of them) for all M columns; per
+// 64-token chunk the A operand phi(K)^T[c][t] is the transposed K fragment
+// of columns b scaled by k_t[a] (one bf16 rounding), V the B operand; Z sums
+// the same products in fp32.
+// ---------------------------------------------------------------------------
+template <int DIM>
+__global__ __launch_bounds__(NT, 2) void k_poly_state(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                                                      float* __restrict__ S, float* __restrict__ Z, int64_t N) {
+  using G = Geo<DIM>;
+  constexpr int LD = G::LD, NTL = G::NTL, PC = G::PC;
+  constexpr int NB = DIM / 64;  // workgroups per value of a
+  __shared__ __align__(16) uint16_t sK[T * LD];
+  __shared__ __align__(16) uint16_t sV[T * LD];
+  __shared__ __align__(16) float sKa[T];
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.x / (DIM * NB);
+  const int rem = static_cast<int>(blockIdx.x % (DIM * NB));
+  const int a = rem / NB, b0 = (rem % NB) * 64;
+  const int64_t hbytes = N * DIM * 2;
+  const rsrc_t rk = make_rsrc(k + bh * N * DIM, hbytes), rv = make_rsrc(v + bh * N * DIM, hbytes);
+  f32x4_t acc[NTL];
+#pragma unroll
+  for (int n = 0; n < NTL; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float zacc = 0.f;
+  const int nch = static_cast<int>((N + T - 1) / T);
+  i32x4 kraw[PC], vraw[PC];
+  auto fetch = [&](int c) {
+    bload_tile<DIM>(kraw, rk, c * T * DIM * 2);
+    bload_tile<DIM>(vraw, rv, c * T * DIM * 2);
+  };
+  fetch(0);
+  const int cc = 4 * (li % 4);
+  for (int c = 0; c < nch; ++c) {
+    store_tile_v<DIM>(sK, kraw);
+    store_tile_v<DIM>(sV, vraw);
+    __syncthreads();
+    if (tid < T) sKa[tid] = fb(static_cast<short>(sK[tid * LD + a]));
+    if (c + 1 < nch) fetch(c + 1);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < T / 32; ++s) {
+      const int jr = 32 * s + 8 * g + li / 4;
+      const int col = b0 + 16 * w + cc;
+      const f32x8_t kt = unpack8(cat(lds_tr(sK + jr * LD + col), lds_tr(sK + (jr + 4) * LD + col)));
+      const f32x4_t ka0 = *reinterpret_cast<const f32x4_t*>(sKa + 32 * s + 8 * g);
+      const f32x4_t ka1 = *reinterpret_cast<const f32x4_t*>(sKa + 32 * s + 8 * g + 4);
+      f32x8_t ph;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ph[e] = kt[e] * ka0[e];
+        ph[e + 4] = kt[e + 4] * ka1[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zacc += ph[e];
+      const i16x8 af = pack8(ph);
+#pragma unroll
+      for (int n = 0; n < NTL; ++n) {
+        const i16x8 bb = cat(lds_tr(sV + jr * LD + 16 * n + cc), lds_tr(sV + (jr + 4) * LD + 16 * n + cc));
+        acc[n] = mfma(af, bb, acc[n]);
+      }
+    }
+    __syncthreads();
+  }
+  const int64_t C = static_cast<int64_t>(DIM) * DIM;
+  float* Sh = S + bh * C * DIM;
+  const int64_t crow = static_cast<int64_t>(a) * DIM + b0 + 16 * w;
+#pragma unroll
+  for (int n = 0; n < NTL; ++n)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) Sh[(crow + 4 * g + u) * DIM + 16 * n + li] = acc[n][u];
+  zacc = shfl_sum_groups(zacc);
+  if (g == 0) Z[bh * C + crow + li] = zacc;
+}
+
 }  // namespace
 
 int poly_supported(int64_t D, int64_t M, int dtype) { return dtype == 1 && D == M && (D == 64 || D == 128); }
@@ -468,6 +547,20 @@ hipError_t launch_poly_forward(int64_t BH, int64_t N, int D, const void* q, cons
 }  // namespace la
 
 namespace la {
+
+hipError_t launch_poly_state(int64_t BH, int64_t N, int D, const void* k, const void* v, float* S, float* Z,
+                             hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(BH * D * (D / 64))), block(NT);
+  const bf16_t* K = static_cast<const bf16_t*>(k);
+  const bf16_t* V = static_cast<const bf16_t*>(v);
+  if (D == 64)
+    hipLaunchKernelGGL((k_poly_state<64>), grid, block, 0, st, K, V, S, Z, N);
+  else if (D == 128)
+    hipLaunchKernelGGL((k_poly_state<128>), grid, block, 0, st, K, V, S, Z, N);
+  else
+    return hipErrorNotSupported;
+  return hipGetLastError();
+}
 
 hipError_t launch_poly_bwd(int pass, int64_t BH, int64_t N, int D, const void* q, const void* k, const void* v,
                            const void* out, const void* dout, const float* den, void* dq, void* dk, void* dv,

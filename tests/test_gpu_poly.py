@@ -146,3 +146,74 @@ def test_poly_backward_workload_sampled_heads():
     for b, h in ((0, 0), (7, 15)):
         want = po.backward(f64(tq[b, h]), f64(tk[b, h]), f64(tv[b, h]), f64(tg[b, h]))[:3]
         check_grads([t[b, h] for t in got], want, f"workload head ({b}, {h})")
+
+
+# ------------------------------------------- linear form: state, decode ----
+@pytest.mark.parametrize("shape", [(1, 2, 200, 64), (2, 1, 65, 64), (1, 1, 130, 128)])
+def test_poly_prefix_state_matches_oracle(shape):
+    # S = sum_t phi(k_t) v_t^T over the D^2 features (one bf16 rounding of
+    # each product), Z = sum_t phi(k_t) in fp32
+    B, H, N, D = shape
+    _, tk, tv, _ = case(B, H, N, D, seed=N + 21)
+    S, Z = la.poly_prefix_state(tk, tv)
+    torch.cuda.synchronize()
+    rS, rZ = po.prefix_state(f64(tk), f64(tv))
+    eS, eZ = rel_l2(f64(S), rS), rel_l2(f64(Z), rZ)
+    say(f"prefix state {shape}: S rel-L2 {eS:.2e}, Z rel-L2 {eZ:.2e}")
+    assert eS < 2e-3
+    assert eZ < 1e-5
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_poly_prefill_then_decode(D):
+    # the prefix state continues the sequence in decode steps; rows equal the
+    # masked quadratic form over all the tokens
+    B, H, N, a = 2, 2, 220, 200
+    tq, tk, tv, _ = case(B, H, N, D, seed=D + 5)
+    S, Z = la.poly_prefix_state(tk[:, :, :a].contiguous(), tv[:, :, :a].contiguous())
+    outs = [la.poly_decode_step(S, Z, tq[:, :, t].contiguous(), tk[:, :, t].contiguous(), tv[:, :, t].contiguous())
+            for t in range(a, N)]
+    torch.cuda.synchronize()
+    ref = po.forward_quadratic(f64(tq), f64(tk), f64(tv))[0][:, :, a:]
+    check(torch.stack(outs, dim=2), ref, f"prefill then decode D={D}")
+
+
+@pytest.mark.parametrize("dm", [(16, 8), (32, 40), (64, 64), (8, 1)])
+def test_poly_decode_steps_fp32_match_oracle(dm):
+    # fp32 steps from an fp32 state built by the oracle (vector and scalar
+    # kernel paths)
+    D, M = dm
+    B, H, N = 2, 3, 10
+    q, k, v, _ = numpy_inputs(B, H, N, D, M, seed=D * M, scale=1.0 / np.sqrt(D))
+    S0, Z0 = po.prefix_state(k[:, :, :4], v[:, :, :4])
+    S = torch.tensor(S0, dtype=torch.float32, device=DEV)
+    Z = torch.tensor(Z0, dtype=torch.float32, device=DEV)
+    tq, tk, tv = (to_torch(x, "f32", DEV) for x in (q, k, v))
+    rS, rZ = S0, Z0
+    for t in range(4, N):
+        o = la.poly_decode_step(S, Z, tq[:, :, t].contiguous(), tk[:, :, t].contiguous(), tv[:, :, t].contiguous())
+        rS, rZ, ro = po.decode_step(rS, rZ, f64(tq[:, :, t]), f64(tk[:, :, t]), f64(tv[:, :, t]))
+        torch.cuda.synchronize()
+        assert rel_l2(f64(o), ro) < 1e-5
+    assert rel_l2(f64(S), rS) < 1e-6
+    assert rel_l2(f64(Z), rZ) < 1e-6
+
+
+def test_poly_decode_zero_query_reads_zero():
+    B, H, D, M = 1, 2, 16, 8
+    S = torch.zeros(B, H, D * D, M, device=DEV)
+    Z = torch.zeros(B, H, D * D, device=DEV)
+    k = torch.randn(B, H, D, device=DEV)
+    v = torch.randn(B, H, M, device=DEV)
+    o = la.poly_decode_step(S, Z, torch.zeros(B, H, D, device=DEV), k, v)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0)
+
+
+def test_poly_decode_rejects_non_power_of_two():
+    B, H, D, M = 1, 1, 48, 8
+    S = torch.zeros(B, H, D * D, M, device=DEV)
+    Z = torch.zeros(B, H, D * D, device=DEV)
+    x = torch.randn(B, H, D, device=DEV)
+    with pytest.raises(la.LinAttnError, match="UNSUPPORTED"):
+        la.poly_decode_step(S, Z, x, x.clone(), torch.randn(B, H, M, device=DEV))
