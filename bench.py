@@ -478,7 +478,47 @@ def bench_poly(la, torch, steps, warmup):
             "roofline": {"bound": "mfma", "kernel": kname, "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                          "flops_per_launch": kf, "avg_launch_ms": round(avg_ms, 4)},
-            "kernels": kernels}
+            "kernels": kernels, "decode": bench_poly_decode(la, torch)}
+
+
+def bench_poly_decode(la, torch, steps=256, B=16, H=32, D=64, M=64, prefix=512):
+    """The polynomial map's recurrent decode step (the linear form: a
+    D^2 x M fp32 state per head, 1 MB at D = M = 64) after a bf16 prefix:
+    steps/s and HBM GB/s."""
+    dev = "cuda"
+    gen = torch.Generator(device=dev).manual_seed(4)
+    pk = (torch.randn(B, H, prefix, D, device=dev, generator=gen) / D ** 0.5).to(torch.bfloat16)
+    pv = (torch.randn(B, H, prefix, M, device=dev, generator=gen) / D ** 0.5).to(torch.bfloat16)
+    S, Z = la.poly_prefix_state(pk, pv)
+    sq, sk, sv = ((torch.randn(steps, B, H, n, device=dev, generator=gen) / D ** 0.5).to(torch.bfloat16)
+                  for n in (D, D, M))
+    outs = torch.empty((steps, B, H, M), dtype=torch.bfloat16, device=dev)
+    for t in range(4):
+        la.poly_decode_step(S.clone(), Z.clone(), sq[t], sk[t], sv[t])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    la.profile_enable(True, only="poly.decode")
+    e0.record(stream)
+    for t in range(steps):
+        la.poly_decode_step(S, Z, sq[t], sk[t], sv[t], out=outs[t])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    n, kms = la.profile_report().get("poly.decode", (steps, e0.elapsed_time(e1)))
+    la.profile_enable(False)
+    ms = e0.elapsed_time(e1)
+    C = D * D
+    b = B * H * (2 * C * M * 4 + 2 * C * 4 + 2 * (2 * D + M) + 2 * M)
+    kavg = kms / n
+    gbs = b / (kavg / 1e3) / 1e9
+    log(f"poly decode: {steps} steps in {ms:.2f} ms, kernel avg {kavg * 1e3:.1f} us, {gbs:.0f} GB/s")
+    return {"metric": "polynomial-map decode steps/sec", "value": round(steps / (ms / 1e3), 1), "unit": "steps/s",
+            "config": {"workload": "degree-2 polynomial map recurrent decode step, fp32 D^2 x M state, bf16 tokens",
+                       "B": B, "H": H, "D": D, "M": M, "prefix": prefix, "steps": steps},
+            "roofline": {"bound": "hbm", "kernel": "poly.decode", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "alg_bytes_per_launch": b, "avg_launch_ms": round(kavg, 5)}}
 
 
 def cpu_baseline(q, k, v, g, B, H, N, budget_s):
