@@ -298,6 +298,29 @@ la_status la_poly_decode_step(float* S, float* Z, const void* q, const void* k, 
                               void* out, int64_t B, int64_t H, int64_t D, int64_t M, int dtype,
                               hipStream_t stream);
 
+/* Softmax attention, the comparison baseline ("[Paper walkthrough]
+ * Transformers are RNNs", section 1, eq:softmax; causal per eq:mask),
+ * computed blockwise with the running maximum / denominator / weighted sum
+ * update of "Transformer study notes (4)", section "FlashAttention":
+ *   out = softmax(Q K^T / sqrt(D)) V,  lse_i = log sum_j exp(q_i.k_j / sqrt(D)).
+ *   q, k: [B,H,N,D], v, out: [B,H,N,M] (bf16, D = M in {64, 128});
+ *   lse: [B,H,N] fp32 or NULL.  No workspace. */
+la_status la_softmax_forward(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
+                             int dtype, hipStream_t stream);
+
+/* One KV-cache decode step per (b,h) ("The deep link between Transformer and
+ * RNN", section 3): append (k, v) at position L of the caches, then
+ *   out = softmax(q . K[0..L] / sqrt(D)) V[0..L].
+ *   k_cache: [B,H,capacity,D], v_cache: [B,H,capacity,M] (dtype; caller-owned,
+ *   positions 0 .. L-1 filled, position L written), 0 <= L < capacity;
+ *   q, k: [B,H,D], v, out: [B,H,M]; fp32 or bf16, D = M in {64, 128}.
+ *   The caller advances L.  No workspace. */
+la_status la_softmax_decode_step(void* k_cache, void* v_cache, const void* q, const void* k,
+                                 const void* v, void* out, int64_t B, int64_t H, int64_t L,
+                                 int64_t capacity, int64_t D, int64_t M, int dtype,
+                                 hipStream_t stream);
+
 /* One RNN decode step per (b,h), in place ("Transformers are RNNs"
  * walkthrough, section 4; the state is updated first, then read):
  *   S <- S + phi(k) v^T;  Z <- Z + phi(k);  out = phi(q)^T S / phi(q)^T Z.

@@ -21,6 +21,7 @@ __all__ = [
     "forward", "backward", "forward_state", "backward_state", "decode_step", "prefix_state", "workspace_bytes",
     "saved_bytes", "resolve_plan", "retention_forward", "retention_backward", "retention_decode_step",
     "retention_saved_bytes", "poly_forward", "poly_backward", "poly_prefix_state", "poly_decode_step",
+    "softmax_forward", "softmax_decode_step",
     "LinAttnError", "library_path", "version", "profile_enable", "profile_report",
 ]
 
@@ -459,6 +460,43 @@ def poly_decode_step(S, Z, q, k, v, out=None, stream=None):
     _native.check(_native.load().la_poly_decode_step(S.data_ptr(), Z.data_ptr(), q.data_ptr(), k.data_ptr(),
                                                      v.data_ptr(), out.data_ptr(), B, H, D, M, _dtype_code(q),
                                                      _stream(stream)))
+    return out
+
+
+def softmax_forward(q, k, v, causal=True, out=None, lse=None, return_lse=False, stream=None):
+    """Softmax attention softmax(q k^T / sqrt(D)) v, causal or not (bf16,
+    D = M in {64, 128}).  Returns out (and lse when return_lse)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    B, H, N, D = q.shape
+    M = v.shape[3]
+    if out is None:
+        out = torch.empty((B, H, N, M), dtype=q.dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _native.check(_native.load().la_softmax_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                                    _ptr(lse), B, H, N, D, M, int(bool(causal)), _dtype_code(q),
+                                                    _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def softmax_decode_step(k_cache, v_cache, L, q, k, v, out=None, stream=None):
+    """One KV-cache step: writes (k, v) at position L of the caches
+    ([B,H,capacity,D] / [B,H,capacity,M]) and returns the attention of q over
+    positions 0..L.  The caller advances L."""
+    torch = _torch()
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    B, H, cap, D = k_cache.shape
+    M = v_cache.shape[3]
+    if out is None:
+        out = torch.empty((B, H, M), dtype=q.dtype, device=q.device)
+    _native.check(_native.load().la_softmax_decode_step(k_cache.data_ptr(), v_cache.data_ptr(), q.data_ptr(),
+                                                        k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, L, cap, D,
+                                                        M, _dtype_code(q), _stream(stream)))
     return out
 
 

@@ -33,6 +33,8 @@ EXPORTS = (
     "la_poly_backward",
     "la_poly_prefix_state",
     "la_poly_decode_step",
+    "la_softmax_forward",
+    "la_softmax_decode_step",
 )
 
 
@@ -81,6 +83,8 @@ def load() -> ctypes.CDLL:
         "la_retention_saved_bytes": ([i64, i64, i64, i64, i64, i32], sz),
         "la_poly_prefix_state": ([vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp], i32),
         "la_poly_decode_step": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp], i32),
+        "la_softmax_forward": ([vp, vp, vp, vp, fp, i64, i64, i64, i64, i64, i32, i32, vp], i32),
+        "la_softmax_decode_step": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp], i32),
         "la_poly_forward": ([vp, vp, vp, vp, fp, i64, i64, i64, i64, i64, i32, i32, vp], i32),
         "la_poly_backward": ([vp, vp, vp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp, sz, vp], i32),
         "la_retention_decode_step": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp], i32),

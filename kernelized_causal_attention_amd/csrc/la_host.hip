@@ -31,6 +31,11 @@ hipError_t launch_ret_forward(const SegGeom& g, const void* q, const void* k, co
 int poly_supported(int64_t D, int64_t M, int dtype);
 hipError_t launch_poly_forward(int64_t BH, int64_t N, int D, const void* q, const void* k, const void* v, void* out,
                                float* den, int causal, hipStream_t st);
+int softmax_supported(int64_t D, int64_t M, int dtype);
+hipError_t launch_softmax_forward(int64_t BH, int64_t N, int D, const void* q, const void* k, const void* v,
+                                  void* out, float* lse, int causal, hipStream_t st);
+hipError_t launch_softmax_decode(int dtype, int64_t BH, int D, void* kc, void* vc, const void* q, const void* k,
+                                 const void* v, void* out, int64_t L, int64_t cap, hipStream_t st);
 hipError_t launch_poly_state(int64_t BH, int64_t N, int D, const void* k, const void* v, float* S, float* Z,
                              hipStream_t st);
 hipError_t launch_poly_bwd(int pass, int64_t BH, int64_t N, int D, const void* q, const void* k, const void* v,
@@ -899,6 +904,61 @@ LA_API la_status la_poly_decode_step(float* S, float* Z, const void* q, const vo
   return dev(timed("poly.decode", stream,
                    [&] { return la::launch_poly_decode_step(dtype, BH, (int)D, (int)M, S, Z, q, k, v, out, stream); }),
              "polynomial decode step");
+}
+
+LA_API la_status la_softmax_forward(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                                    int64_t H, int64_t N, int64_t D, int64_t M, int causal, int dtype,
+                                    hipStream_t stream) {
+  la_status s = check_sizes(B, H, N, D, M, dtype);
+  if (s != LA_OK) return s;
+  if ((s = check_ptr(q, "q", dtype)) || (s = check_ptr(k, "k", dtype)) || (s = check_ptr(v, "v", dtype)) ||
+      (s = check_ptr(out, "out", dtype)))
+    return s;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return fail(LA_ERR_INVALID, "lse misaligned");
+  if (!la::softmax_supported(D, M, dtype))
+    return fail(LA_ERR_UNSUPPORTED, "softmax kernels take bf16 with D = M in {64, 128} (D=%lld, M=%lld, dtype %d)",
+                (long long)D, (long long)M, dtype);
+  if (N * D * 2 >= (int64_t(1) << 31)) return fail(LA_ERR_UNSUPPORTED, "head too large for 32-bit offsets");
+  const int64_t BH = B * H;
+  if (BH * ((N + 127) / 128) > 0xffffffffLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
+  const size_t es = dtype_size(dtype);
+  const Span ins[] = {span("q", q, BH * N * D, es), span("k", k, BH * N * D, es), span("v", v, BH * N * M, es)};
+  const Span outs[] = {span("out", out, BH * N * M, es), span("lse", lse, lse ? BH * N : 0, 4)};
+  if ((s = check_disjoint(outs, 2, ins, 3))) return s;
+  return dev(timed("softmax.forward", stream,
+                   [&] { return la::launch_softmax_forward(BH, N, (int)D, q, k, v, out, lse, causal ? 1 : 0, stream); }),
+             "softmax forward");
+}
+
+LA_API la_status la_softmax_decode_step(void* k_cache, void* v_cache, const void* q, const void* k, const void* v,
+                                        void* out, int64_t B, int64_t H, int64_t L, int64_t capacity, int64_t D,
+                                        int64_t M, int dtype, hipStream_t stream) {
+  la_status s = check_sizes(B, H, 1, D, M, dtype);
+  if (s != LA_OK) return s;
+  if ((s = check_ptr(k_cache, "k_cache", dtype)) || (s = check_ptr(v_cache, "v_cache", dtype)) ||
+      (s = check_ptr(q, "q", dtype)) || (s = check_ptr(k, "k", dtype)) || (s = check_ptr(v, "v", dtype)) ||
+      (s = check_ptr(out, "out", dtype)))
+    return s;
+  if (D != M || (D != 64 && D != 128))
+    return fail(LA_ERR_UNSUPPORTED, "the KV-cache step takes D = M in {64, 128} (D=%lld, M=%lld)", (long long)D,
+                (long long)M);
+  if (L < 0 || L >= capacity)
+    return fail(LA_ERR_INVALID, "cache length %lld must be in [0, capacity %lld)", (long long)L, (long long)capacity);
+  for (const void* p : {k_cache, v_cache})
+    if (reinterpret_cast<uintptr_t>(p) & 15) return fail(LA_ERR_INVALID, "caches must be 16-byte aligned");
+  const int64_t BH = B * H;
+  if (BH > 0xffffffffLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
+  const size_t es = dtype_size(dtype);
+  const Span ins[] = {span("q", q, BH * D, es), span("k", k, BH * D, es), span("v", v, BH * M, es)};
+  const Span outs[] = {span("k_cache", k_cache, BH * capacity * D, es), span("v_cache", v_cache, BH * capacity * M, es),
+                       span("out", out, BH * M, es)};
+  if ((s = check_disjoint(outs, 3, ins, 3))) return s;
+  return dev(timed("softmax.decode", stream,
+                   [&] {
+                     return la::launch_softmax_decode(dtype, BH, (int)D, k_cache, v_cache, q, k, v, out, L, capacity,
+                                                      stream);
+                   }),
+             "softmax KV-cache decode step");
 }
 
 LA_API la_status la_decode_step(float* S, float* Z, const void* q, const void* k, const void* v, void* out,
