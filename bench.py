@@ -26,6 +26,10 @@ Extra fields:
   poly          -- degree-2 polynomial-kernel attention forward+backward on
                    the same shape: tokens/s and the dominant kernel's MFMA
                    roofline (TFLOP/s against the dense bf16 peak).
+  softmax       -- the softmax baseline's causal forward on the same shape,
+                   beside the linear-attention forward on the same inputs;
+                   the decode field adds the softmax KV-cache step on the
+                   decode workload's tokens and the linear decode's speedup.
 """
 
 from __future__ import annotations
@@ -245,6 +249,7 @@ def main():
         result["decode"] = bench_decode(la, torch, args.decode_steps)
         result["retention"] = bench_retention(la, torch, args.steps, args.warmup)
         result["poly"] = bench_poly(la, torch, args.steps, args.warmup)
+        result["softmax"] = bench_softmax(la, torch, args.steps, args.warmup)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(q, k, v, g, B, H, N, args.cpu_seconds)
@@ -338,7 +343,37 @@ def bench_decode(la, torch, steps):
     kavg = kms / n
     gbs = b / (kavg / 1e3) / 1e9
     log(f"decode: {steps} steps in {ms:.2f} ms, kernel avg {kavg * 1e3:.1f} us, {gbs:.0f} GB/s")
+    # the softmax baseline on the same tokens: a KV cache filled with the
+    # prefix, then the same steps (append, attend over every cached position)
+    del S, Z
+    cap = w.prefix + steps
+    kc = torch.empty((w.B, w.H, cap, w.D), dtype=torch.float32, device=dev)
+    vc = torch.empty((w.B, w.H, cap, w.M), dtype=torch.float32, device=dev)
+    kc[:, :, :w.prefix] = pk
+    vc[:, :, :w.prefix] = pv
+    del pk, pv
+    torch.cuda.synchronize()
+    la.profile_enable(True, only="softmax.decode")
+    e0.record(stream)
+    for t in range(steps):
+        la.softmax_decode_step(kc, vc, w.prefix + t, sq[t % w.steps], sk[t % w.steps], sv[t % w.steps], out=outs[t])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sprof = la.profile_report()
+    la.profile_enable(False)
+    sms = e0.elapsed_time(e1)
+    sn, skms = sprof.get("softmax.decode", (steps, sms))
+    sb = sum(w.B * w.H * ((w.prefix + t + 1) * (w.D + w.M) * 4 + (2 * w.D + 2 * w.M) * 4) for t in range(steps))
+    sgbs = sb / (skms / 1e3) / 1e9
+    log(f"softmax KV-cache decode: {steps} steps in {sms:.2f} ms ({sms / steps * 1e3:.1f} us/step, cache "
+        f"{w.prefix}..{w.prefix + steps - 1} tokens), {sgbs:.0f} GB/s; linear decode is {sms / ms:.1f}x faster")
+    del kc, vc
+    softmax = {"metric": "softmax KV-cache decode steps/sec", "value": round(steps / (sms / 1e3), 1),
+               "unit": "steps/s", "avg_step_ms": round(sms / steps, 5),
+               "cache_tokens": [w.prefix, w.prefix + steps - 1], "achieved_GBps": round(sgbs, 1),
+               "frac": round(sgbs / PEAK_HBM_GBS, 4), "linear_decode_speedup": round(sms / ms, 2)}
     return {"metric": "decode steps/sec", "value": round(steps / (ms / 1e3), 1), "unit": "steps/s",
+            "softmax_kv_cache": softmax,
             "config": {"workload": "batched RNN decode step, fp32 state", "B": w.B, "H": w.H, "D": w.D,
                        "M": w.M, "prefix": w.prefix, "steps": steps},
             "roofline": {"bound": "hbm", "kernel": "decode", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
@@ -479,6 +514,49 @@ def bench_poly(la, torch, steps, warmup):
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                          "flops_per_launch": kf, "avg_launch_ms": round(avg_ms, 4)},
             "kernels": kernels, "decode": bench_poly_decode(la, torch)}
+
+
+def bench_softmax(la, torch, steps, warmup):
+    """The softmax baseline's causal forward on the main step's shape against
+    the linear-attention forward on the same inputs (the pages' speed claim
+    as a kernel ratio on one GPU)."""
+    from workloads import WORKLOADS, device_inputs
+
+    w = WORKLOADS["fwdbwd_bf16"]
+    B, H, N, D, M = w.B, w.H, w.N, w.D, w.M
+    q, k, v, _ = device_inputs(B, H, N, D, M, "bf16", seed=5, scale=1.0 / D ** 0.5, device="cuda")
+    out = torch.empty((B, H, N, M), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(1, la.workspace_bytes("forward", B, H, N, D, M, True, "bf16")), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(warmup + 3):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    sm_ms = timed(lambda: la.softmax_forward(q, k, v, out=out))
+    la_ms = timed(lambda: la.forward(q, k, v, causal=True, out=out, workspace=ws))
+    flops = B * H * (N * (N + 1) // 2) * (2 * D + 2 * M)
+    tf = flops / (sm_ms / 1e3) / 1e12
+    log(f"softmax forward: {sm_ms:.3f} ms ({tf:.0f} TFLOP/s); linear-attention forward {la_ms:.3f} ms "
+        f"({sm_ms / la_ms:.1f}x)")
+    return {"metric": "softmax causal attention forward tokens/sec", "value": round(B * N / (sm_ms / 1e3), 1),
+            "unit": "tokens/s", "ms": round(sm_ms, 4),
+            "config": {"workload": "softmax(QK^T/sqrt(D))V causal forward, bf16 in / fp32 accumulate", "B": B,
+                       "H": H, "N": N, "D": D, "M": M},
+            "roofline": {"bound": "mfma", "kernel": "softmax.forward", "achieved": round(tf, 1),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None, "flops_per_launch": flops, "avg_launch_ms": round(sm_ms, 4)},
+            "linear_forward_ms": round(la_ms, 4), "linear_forward_speedup": round(sm_ms / la_ms, 2)}
 
 
 def bench_poly_decode(la, torch, steps=256, B=16, H=32, D=64, M=64, prefix=512):
