@@ -12,11 +12,15 @@
 //
 // Forward: the same blocking as the polynomial-kernel forward (128 queries
 // per workgroup, two 16-row tiles per wave, 64-key blocks in LDS, transposed
-// scores feeding O^T += V^T P^T).  Scores are kept in the log2 domain
-// (s log2(e) / sqrt(D)) so that each weight is one exp2; a lane holds four
-// consecutive keys of one query per tile, so a row's block maximum is an
-// in-lane max over its 16 entries and two cross-lane steps, and the
-// rescale r multiplies that lane's output column directly.
+// scores feeding O^T += V^T P^T).  A lane holds four consecutive keys of one
+// query per tile, so a row's block maximum is an in-lane max over its 16
+// raw scores and two cross-lane steps, and the rescale multiplies that
+// lane's output column directly.  Each weight is one FMA and one hardware
+// exp2: exp2((s - m) log2(e) / sqrt(D)).  The reference maximum m of a row
+// moves only when a block raises it by more than kSlack (in log2 units):
+// the weights then stay <= 2^kSlack, harmless in bf16 and fp32, and the
+// rescale of the output (a wave-uniform decision) is skipped for most
+// blocks.  Any common reference gives the same quotient a / l.
 #include "la_device.h"
 #include "la_internal.h"
 #include "la_mfma_common.h"
@@ -31,6 +35,11 @@ constexpr int T = kT;
 constexpr int QT = 2;
 constexpr int BQ = 128;
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kSlack = 8.f;  // log2 of the largest weight allowed before m moves
+
+// 2^x on the hardware unit (no denormal range reduction: every argument here
+// is <= kSlack, and results below 2^-126 are weights that do not matter).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float max_groups(float x) {
   x = fmaxf(x, __shfl_xor(x, 16, 64));
@@ -90,7 +99,7 @@ __global__ __launch_bounds__(NT, 2) void k_sm_fwd(const bf16_t* __restrict__ q, 
     __syncthreads();
     if (kb + 1 < nkb) fetch(kb + 1);
     const int64_t k0 = static_cast<int64_t>(kb) * T;
-    // log2-domain scores s^T[j][i], masked entries -inf
+    // raw scores s^T[j][i], masked entries -inf
     f32x4_t sc[QT][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -111,7 +120,7 @@ __global__ __launch_bounds__(NT, 2) void k_sm_fwd(const bf16_t* __restrict__ q, 
           for (int u = 0; u < 4; ++u) {
             const int64_t j = k0 + 16 * t + 4 * g + u;
             const bool keep = (!diag || j <= r0 + li) && (!tail || j < N);
-            acc[u] = keep ? x[u] * scale2 : kNegInf;
+            acc[u] = keep ? x[u] : kNegInf;
           }
         }
         sc[qt][t] = acc;
@@ -124,25 +133,29 @@ __global__ __launch_bounds__(NT, 2) void k_sm_fwd(const bf16_t* __restrict__ q, 
       float mb = kNegInf;
 #pragma unroll
       for (int t = 0; t < 4; ++t) mb = fmaxf(mb, fmaxf(fmaxf(sc[qt][t][0], sc[qt][t][1]), fmaxf(sc[qt][t][2], sc[qt][t][3])));
-      const float mnew = fmaxf(mrow[qt], max_groups(mb));
-      // a row whose keys so far are all masked keeps m = -inf (never -inf - -inf)
-      const float msub = mnew == kNegInf ? 0.f : mnew;
-      const float r = exp2f(mrow[qt] - msub);
-      mrow[qt] = mnew;
+      const float mcand = fmaxf(mrow[qt], max_groups(mb));
+      // move the reference only when some row of the wave outgrows it
+      if (__any((mcand - mrow[qt]) * scale2 > kSlack)) {
+        // a row whose keys so far are all masked keeps m = -inf and r = 0
+        const float r = mcand == kNegInf ? 1.f : exp2_hw((mrow[qt] - mcand) * scale2);
+        mrow[qt] = mcand;
+        lsum[qt] *= r;
+#pragma unroll
+        for (int n = 0; n < NTL; ++n) o[qt][n] *= r;
+      }
+      const float msc = mrow[qt] == kNegInf ? 0.f : -mrow[qt] * scale2;
       float ps = 0.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         f32x4_t p;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          p[u] = exp2f(sc[qt][t][u] - msub);
+          p[u] = exp2_hw(__builtin_fmaf(sc[qt][t][u], scale2, msc));
           ps += p[u];
         }
         pt[qt][t] = pack4(p);
       }
-      lsum[qt] = lsum[qt] * r + ps;
-#pragma unroll
-      for (int n = 0; n < NTL; ++n) o[qt][n] *= r;
+      lsum[qt] += ps;
     }
     // O^T += V^T P^T
 #pragma unroll
@@ -167,7 +180,8 @@ __global__ __launch_bounds__(NT, 2) void k_sm_fwd(const bf16_t* __restrict__ q, 
     const int row = 32 * w + 16 * qt + li;
 #pragma unroll
     for (int n = 0; n < NTL; ++n) bstore8(ro, pack4(o[qt][n] * inv), (row * DIM + 16 * n + 4 * g) * 2, qoff);
-    if (lse && g == 0 && q0 + row < N) lse[bh * N + q0 + row] = mrow[qt] * 0.69314718055994531f + __logf(lt);
+    if (lse && g == 0 && q0 + row < N)
+      lse[bh * N + q0 + row] = mrow[qt] * scale2 * 0.69314718055994531f + __logf(lt);
   }
 }
 
@@ -257,8 +271,8 @@ __global__ __launch_bounds__(NT) void k_sm_decode(TIn* __restrict__ kc, TIn* __r
 #pragma unroll
     for (int off = 4; off < 64; off <<= 1) mb = fmaxf(mb, __shfl_xor(mb, off, 64));
     const float mnew = fmaxf(m, mb);  // finite: key j0 is live
-    const float r = exp2f(m - mnew);
-    const float p = exp2f(s2 - mnew);
+    const float r = exp2_hw(m - mnew);
+    const float p = exp2_hw(s2 - mnew);
     float psum = p;
 #pragma unroll
     for (int off = 4; off < 64; off <<= 1) psum += __shfl_xor(psum, off, 64);
@@ -292,13 +306,13 @@ __global__ __launch_bounds__(NT) void k_sm_decode(TIn* __restrict__ kc, TIn* __r
     for (int off = 32; off >= 1; off >>= 1) sn += __shfl_xor(sn, off, 64);
     const float s2n = sn * scale2;
     const float mt = fmaxf(fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3])), s2n);
-    float f[4], lt = exp2f(s2n - mt);
+    float f[4], lt = exp2_hw(s2n - mt);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      f[u] = exp2f(wm[u] - mt);
+      f[u] = exp2_hw(wm[u] - mt);
       lt += f[u] * wl[u];
     }
-    const float inv = 1.f / lt, fn = exp2f(s2n - mt);
+    const float inv = 1.f / lt, fn = exp2_hw(s2n - mt);
     for (int c = l; c < DIM; c += 64) {
       const float a = ((f[0] * wa[0][c] + f[1] * wa[1][c]) + (f[2] * wa[2][c] + f[3] * wa[3][c])) + fn * sv[c];
       st(out, bh * DIM + c, a * inv);
