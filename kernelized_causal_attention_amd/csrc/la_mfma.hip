@@ -361,9 +361,9 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_seg_state_mfma(const
 
 size_t lds_fwd(int dim) {
   const int tiles = dim == 128 ? 3 : 2;  // K, V (and phi(Q) with two waves per query tile)
-  return (tiles * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + dim * sizeof(float);
+  return (tiles * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t) + dim * sizeof(float);
 }
-size_t lds_seg(int dim) { return 2 * T * (dim + 8) * sizeof(uint16_t); }
+size_t lds_seg(int dim) { return 2 * T * (dim + kLdsPad) * sizeof(uint16_t); }
 
 #define LA_MLAUNCH(kernel, nthreads, grid, lds, st, ...)                                                \
   do {                                                                                                  \

@@ -761,12 +761,12 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
 }
 
 size_t lds_bwd(int dim) {
-  return (4 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + (dim + T) * sizeof(float) +
+  return (4 * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t) + (dim + T) * sizeof(float) +
          2 * T * sizeof(uint16_t);
 }
-size_t lds_ragg(int dim) { return 2 * T * (dim + 8) * sizeof(uint16_t) + 4 * sizeof(float) + 2 * T * sizeof(uint16_t); }
+size_t lds_ragg(int dim) { return 2 * T * (dim + kLdsPad) * sizeof(uint16_t) + 4 * sizeof(float) + 2 * T * sizeof(uint16_t); }
 size_t lds_dq(int dim) {
-  return (6 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + (2 * dim + 4) * sizeof(float) +
+  return (6 * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t) + (2 * dim + 4) * sizeof(float) +
          4 * T * sizeof(uint16_t);
 }
 

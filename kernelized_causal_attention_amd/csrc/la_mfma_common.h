@@ -132,12 +132,16 @@ __device__ __forceinline__ void bstore4(rsrc_t r, float v, int voff, int soff) {
 
 constexpr int kNT = 256;  // threads per workgroup (4 wave64s)
 constexpr int kT = 64;    // tokens per chunk
+// LDS row padding (elements): a row of a T x DIM tile starts 16 bytes after
+// a multiple of 128, so the 16-byte row reads of eight consecutive rows hit
+// distinct banks.
+constexpr int kLdsPad = 8;
 
 // NW wave64s per workgroup (4, or 8 for the D = 128 forward kernels).
 template <int DIM, int NW = 4>
 struct Geo {
   static constexpr int NT = 64 * NW;            // threads per workgroup
-  static constexpr int LD = DIM + 8;            // padded LDS row stride (elements)
+  static constexpr int LD = DIM + kLdsPad;      // padded LDS row stride (elements)
   static constexpr int NTL = DIM / 16;          // 16-wide tiles along D (= M)
   static constexpr int KS = DIM / 32;           // 32-deep k-steps along D (= M)
   static constexpr int PC = kT * DIM / 8 / NT;  // 16-byte pieces per thread per T x DIM tile

@@ -805,10 +805,10 @@ __global__ __launch_bounds__(NT) void k_ret_dlg(const float* __restrict__ a, con
   }
 }
 
-size_t lds_ret_fwd(int dim) { return (3 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t); }
-size_t lds_ret_seg(int dim) { return 2 * T * (dim + 8) * sizeof(uint16_t); }
-size_t lds_ret_dq(int dim) { return (6 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t); }
-size_t lds_ret_dkdv(int dim) { return (5 * T * (dim + 8) + dim * (dim + 8)) * sizeof(uint16_t) + 4 * T * sizeof(float); }
+size_t lds_ret_fwd(int dim) { return (3 * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t); }
+size_t lds_ret_seg(int dim) { return 2 * T * (dim + kLdsPad) * sizeof(uint16_t); }
+size_t lds_ret_dq(int dim) { return (6 * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t); }
+size_t lds_ret_dkdv(int dim) { return (5 * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t) + 4 * T * sizeof(float); }
 
 #define LA_RLAUNCH(kernel, grid, lds, st, ...)                                                               \
   do {                                                                                                       \
