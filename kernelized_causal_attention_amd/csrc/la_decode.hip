@@ -28,12 +28,17 @@
 //   denominator is 0.
 #include "la_device.h"
 #include "la_internal.h"
+#include "la_mfma_common.h"
 
 namespace la {
 namespace {
 
 constexpr int NT = 256;
 constexpr int kLin = 0, kRet = 1, kPoly = 2;
+constexpr int kNonTemporal = 2;  // buffer cache-policy bits: non-temporal
+using mf::make_rsrc;
+using mf::rsrc_t;
+using mf::u32x4;
 
 // Feature c of the row: phi(x)_c from LDS (kLin: phi stored; kRet: x stored;
 // kPoly: x stored, c = a D + b -> x_a x_b).
@@ -90,7 +95,58 @@ __device__ __forceinline__ float decay_of(const float* __restrict__ lg, int64_t 
   return __expf(x < -80.f ? -80.f : x);
 }
 
+// Prologue of the vector path for kLin / kRet (D, M <= NT): thread t holds
+// entry t of q, k, v and Z.  Split from its use so that the S fetch can be
+// issued between the two halves and overlap the prologue's dependent steps.
+struct RawIn {
+  float q, k, v, z;
+};
+
+template <int MODE, typename TIn>
+__device__ __forceinline__ RawIn load_raw(const float* __restrict__ Z, const TIn* __restrict__ q,
+                                          const TIn* __restrict__ k, const TIn* __restrict__ v, int64_t bh, int D,
+                                          int M) {
+  const int t = threadIdx.x;
+  RawIn r = {0.f, 0.f, 0.f, 0.f};
+  if (t < D) {
+    r.q = ld(q, bh * D + t);
+    r.k = ld(k, bh * D + t);
+    if (MODE == kLin) r.z = Z[bh * D + t];
+  }
+  if (t < M) r.v = ld(v, bh * M + t);
+  return r;
+}
+
+// Second half: features into LDS, Z' = Z + phi(k) stored, den = phi(q)^T Z'
+// (same fixed-order reduction as decode_prologue).
+template <int MODE>
+__device__ __forceinline__ float finish_raw(const RawIn& r, float* qf_s, float* kf_s, float* v_s, float* wden,
+                                            float* __restrict__ Z, int64_t bh, int D, int M) {
+  const int t = threadIdx.x;
+  float part = 0.f;
+  if (t < D) {
+    const float kf = MODE == kLin ? phi(r.k) : r.k;
+    const float qf = MODE == kLin ? phi(r.q) : r.q;
+    kf_s[t] = kf;
+    qf_s[t] = qf;
+    if (MODE == kLin) {
+      const float z = r.z + kf;
+      Z[bh * D + t] = z;
+      part = qf * z;
+    }
+  }
+  if (t < M) v_s[t] = r.v;
+  part = wave_sum(part);
+  if ((t & 63) == 0) wden[t >> 6] = part;
+  __syncthreads();
+  return MODE == kRet ? 1.f : ((wden[0] + wden[1]) + wden[2]) + wden[3];
+}
+
 // Vector path: M/4 threads per row, NT/(M/4) rows per pass, U rows in flight.
+// The first U rows of each thread are requested before the prologue's
+// features and Z update (kLin / kRet after their raw loads, so that waiting
+// for those does not wait for S), and each later batch right after the
+// previous one is consumed.
 template <typename TIn, int TPR, int MODE>
 __global__ __launch_bounds__(NT) void k_decode_vec(float* __restrict__ S, float* __restrict__ Z,
                                                    const TIn* __restrict__ q, const TIn* __restrict__ k,
@@ -103,28 +159,50 @@ __global__ __launch_bounds__(NT) void k_decode_vec(float* __restrict__ S, float*
   __shared__ float red[RPI * M];
   const int64_t bh = blockIdx.x;
   const int t = threadIdx.x;
-  const float den = decode_prologue<MODE>(qf_s, kf_s, v_s, wden, Z, q, k, v, bh, D, C, lgD, M);
-  const float gam = MODE == kRet ? decay_of(lg, bh) : 1.f;
   const int c4 = t % TPR, rg = t / TPR;
+  // Buffer access over this head's C x M state: per-lane offset plus a
+  // wave-uniform row offset, non-temporal (the state is far larger than the
+  // caches and is not reused within a step).  Rows past C read as zero and
+  // their stores are dropped by the range check.
+  const rsrc_t Sr = make_rsrc(S + bh * static_cast<int64_t>(C) * M, static_cast<int64_t>(C) * M * 4);
+  const int voff = (rg * M + 4 * c4) * 4;
+  f32x4 sv[U];
+  // Always U loads, so the count of loads in flight is fixed and waiting for
+  // the prologue's own loads does not wait for S.
+  auto fetch = [&](int r0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      sv[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(Sr, voff, (r0 + u * RPI) * M * 4, kNonTemporal));
+  };
+  float den;
+  if (MODE == kPoly) {
+    fetch(0);
+    den = decode_prologue<MODE>(qf_s, kf_s, v_s, wden, Z, q, k, v, bh, D, C, lgD, M);
+  } else {
+    const RawIn r = load_raw<MODE>(Z, q, k, v, bh, D, M);
+    fetch(0);
+    den = finish_raw<MODE>(r, qf_s, kf_s, v_s, wden, Z, bh, D, M);
+  }
+  const float gam = MODE == kRet ? decay_of(lg, bh) : 1.f;
   const f32x4 vv = {v_s[4 * c4], v_s[4 * c4 + 1], v_s[4 * c4 + 2], v_s[4 * c4 + 3]};
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  f32x4* Sh = reinterpret_cast<f32x4*>(S + bh * static_cast<int64_t>(C) * M) + c4;
-  for (int d0 = rg; d0 < C; d0 += RPI * U) {
-    f32x4 sv[U];
+  auto consume = [&](int r0, bool guard) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int d = d0 + u * RPI;
-      if (d < C) sv[u] = __builtin_nontemporal_load(Sh + static_cast<int64_t>(d) * TPR);
+      const int d = r0 + rg + u * RPI;
+      const int dc = guard ? min(d, C - 1) : d;
+      const f32x4 s = (MODE == kRet ? gam * sv[u] : sv[u]) + feat<MODE>(kf_s, dc, lgD) * vv;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s), Sr, voff, (r0 + u * RPI) * M * 4,
+                                             kNonTemporal);
+      if (!guard || d < C) acc += feat<MODE>(qf_s, dc, lgD) * s;
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int d = d0 + u * RPI;
-      if (d < C) {
-        const f32x4 s = (MODE == kRet ? gam * sv[u] : sv[u]) + feat<MODE>(kf_s, d, lgD) * vv;
-        __builtin_nontemporal_store(s, Sh + static_cast<int64_t>(d) * TPR);
-        acc += feat<MODE>(qf_s, d, lgD) * s;
-      }
-    }
+  };
+  for (int r0 = 0; r0 < C; r0 += RPI * U) {
+    if (r0) fetch(r0);
+    if (r0 + RPI * U <= C)  // wave-uniform: every row of the batch exists
+      consume(r0, false);
+    else
+      consume(r0, true);
   }
   red[rg * M + 4 * c4 + 0] = acc.x;
   red[rg * M + 4 * c4 + 1] = acc.y;

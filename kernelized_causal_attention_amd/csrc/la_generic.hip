@@ -48,11 +48,41 @@ __device__ __forceinline__ void stage(float* dst, int stride, const TIn* __restr
 // S[d][m] += sum_j Kf[j][d] V[j][m];  Z[d] += sum_j Kf[j][d]
 __device__ __forceinline__ void state_update(float* S, int SP, float* Z, const float* Kf, int DP,
                                              const float* V, int MP, int nrow, int D, int M) {
-  for (int e = threadIdx.x; e < D * M; e += NT) {
-    const int d = e / M, m = e - d * M;
-    float acc = S[d * SP + m];
-    for (int j = 0; j < nrow; ++j) acc += Kf[j * DP + d] * V[j * MP + m];
-    S[d * SP + m] = acc;
+  if ((D & 3) == 0 && (M & 3) == 0) {
+    // 4 x 4 register tiles: thread tile (dt, mt) holds S[dt + a D/4][mt + b M/4],
+    // a, b < 4, for the whole chunk -- 16 FMAs per 8 LDS reads; consecutive
+    // threads take consecutive mt (conflict-free V reads, broadcast K reads)
+    const int D4 = D >> 2, M4 = M >> 2;
+    for (int t = threadIdx.x; t < D4 * M4; t += NT) {
+      const int dt = t / M4, mt = t - dt * M4;
+      float acc[4][4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = S[(dt + a * D4) * SP + mt + b * M4];
+      for (int j = 0; j < nrow; ++j) {
+        float kk[4], vv[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) kk[a] = Kf[j * DP + dt + a * D4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) vv[b] = V[j * MP + mt + b * M4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[a][b] += kk[a] * vv[b];
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) S[(dt + a * D4) * SP + mt + b * M4] = acc[a][b];
+    }
+  } else {
+    for (int e = threadIdx.x; e < D * M; e += NT) {
+      const int d = e / M, m = e - d * M;
+      float acc = S[d * SP + m];
+      for (int j = 0; j < nrow; ++j) acc += Kf[j * DP + d] * V[j * MP + m];
+      S[d * SP + m] = acc;
+    }
   }
   for (int d = threadIdx.x; d < D; d += NT) {
     float z = Z[d];
