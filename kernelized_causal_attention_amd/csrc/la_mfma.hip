@@ -131,6 +131,9 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_
   // computed by both waves of a pair from their own loads.
   constexpr bool kQInLds = NCG > 1;
   uint16_t* sQf = reinterpret_cast<uint16_t*>(sZ + DIM);
+  // per-wave output staging: 16 rows x NTW * 16 columns
+  constexpr int OC = NTW * 16;
+  uint16_t* sOut = sQf + (kQInLds ? T * LD : 0);
 
   // w is made wave-uniform (an SGPR) so that branches on it are scalar: an
   // MFMA under an EXEC-masked branch still writes every lane.
@@ -147,9 +150,10 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_
   const bf16_t* qh = q + bh * N * DIM;
   const bf16_t* kh = k + bh * N * DIM;
   const bf16_t* vh = v + bh * N * DIM;
-  bf16_t* oh = out ? out + bh * N * DIM : nullptr;
+  const rsrc_t ro = make_rsrc(out ? out + bh * N * DIM : nullptr, out ? N * DIM * 2 : 0);
   float* dh = den_out ? den_out + bh * N : nullptr;
   const int i = 16 * rt + li;  // this lane's query row within the chunk
+  uint16_t* sO = sOut + w * 16 * (OC + kLdsPad);
 
   f32x4_t Sacc[DT][NTL];
   f32x4_t zacc[DT];
@@ -267,15 +271,15 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_
         }
       }
     }
-    if (i < nrow) {
-      if (oh) {
-        const float inv = 1.f / den;
+    if (out) {
+      // rows past the head's end (den may be 0 there) are dropped by the
+      // store's range check
+      const float inv = 1.f / den;
 #pragma unroll
-        for (int n = 0; n < NTW; ++n)
-          *reinterpret_cast<i16x4*>(oh + (c0 + i) * DIM + 16 * (nb + n) + 4 * g) = pack4(o[n] * inv);
-      }
-      if (dh && g == 0 && nb == 0) dh[c0 + i] = den;
+      for (int n = 0; n < NTW; ++n) stage_piece<OC>(sO, pack4(o[n] * inv), li, g, n);
+      store_staged<OC, DIM>(sO, ro, 16 * rt, 16 * nb, static_cast<int>(c0 * DIM * 2));
     }
+    if (i < nrow && dh && g == 0 && nb == 0) dh[c0 + i] = den;
 
     if (CAUSAL) state_update<DIM, NW>(Sacc, zacc, sKf, sV, w, g, li);
     __syncthreads();
@@ -359,11 +363,140 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_seg_state_mfma(const
   }
 }
 
+// The same aggregates at D = 64 with wave-private chunks: wave w of the
+// workgroup sums chunks w, w + 4, w + 8, ... of the segment into a full
+// 64 x 64 partial of its own (16 fp32 accumulator tiles), staging each chunk
+// in a private LDS tile, so the chunk loop has no workgroup barrier and
+// every staged element is read from LDS once (the A and B operands of all
+// sixteen tiles are held in registers).  The four partials are added in
+// wave order at the end.  Same split as above: dS = 1 U^T + E^T V,
+// dZ = count + colsum E.
+__global__ __launch_bounds__(256, 2) void k_seg_state_wave64(const bf16_t* __restrict__ k,
+                                                             const bf16_t* __restrict__ v, float* __restrict__ s_out,
+                                                             int64_t s_stride, float* __restrict__ z_out,
+                                                             int64_t z_stride, int64_t N, int P, int seg_len) {
+  constexpr int DIM = 64, LD = DIM + kLdsPad;
+  constexpr int PW = T * DIM / 8 / 64;  // 16-byte pieces per lane per chunk tile
+  constexpr int RP = DIM + 4;           // fp32 row stride of the partials in LDS
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint16_t* sK = smem + w * 2 * T * LD;
+  uint16_t* sV = sK + T * LD;
+  const int64_t bh = blockIdx.x / P;
+  const int seg = blockIdx.x % P;
+  const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
+  const int64_t r1 = min(N, r0 + seg_len);
+  const int64_t hbytes = N * DIM * 2;
+  const rsrc_t rk = make_rsrc(k + bh * N * DIM, hbytes), rv = make_rsrc(v + bh * N * DIM, hbytes);
+  const int nch = static_cast<int>((r1 - r0 + T - 1) / T);
+  const short one = 0x3f80;  // bf16 1.0
+  const i16x8 ones = {one, one, one, one, one, one, one, one};
+  f32x4_t S[4][4], zacc[4], uacc[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    zacc[a] = uacc[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) S[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // piece p of lane l: row (64 p + l) / 8, features 8 ((64 p + l) % 8) ..
+  i32x4 kr[PW], vr[PW];
+  auto fetch = [&](int c) {
+    const int soff = static_cast<int>((r0 + static_cast<int64_t>(c) * T) * DIM * 2);
+#pragma unroll
+    for (int p = 0; p < PW; ++p) {
+      kr[p] = bload16(rk, (64 * p + l) * 16, soff);
+      vr[p] = bload16(rv, (64 * p + l) * 16, soff);
+    }
+  };
+  if (w < nch) fetch(w);
+  for (int c = w; c < nch; c += 4) {
+    // rows past the head's end loaded as zero: elu(0) = 0, V = 0
+#pragma unroll
+    for (int p = 0; p < PW; ++p) {
+      const int e = 64 * p + l;
+      f32x8_t x = unpack8(__builtin_bit_cast(i16x8, kr[p]));
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x[q] = elu_fast(x[q]);
+      *reinterpret_cast<i16x8*>(sK + (e >> 3) * LD + (e & 7) * 8) = pack8(x);
+      *reinterpret_cast<i16x8*>(sV + (e >> 3) * LD + (e & 7) * 8) = __builtin_bit_cast(i16x8, vr[p]);
+    }
+    if (c + 4 < nch) fetch(c + 4);
+    // the tiles are private to this wave: its LDS operations complete in
+    // order, so only the compiler has to be kept from reordering them
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int s = 0; s < T / 32; ++s) {
+      const int jr = 32 * s + 8 * g + li / 4;
+      const int cc = 4 * (li % 4);
+      i16x8 a[4], b[4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        a[n] = cat(lds_tr(sK + jr * LD + 16 * n + cc), lds_tr(sK + (jr + 4) * LD + 16 * n + cc));
+        b[n] = cat(lds_tr(sV + jr * LD + 16 * n + cc), lds_tr(sV + (jr + 4) * LD + 16 * n + cc));
+      }
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        zacc[n] = mfma(a[n], ones, zacc[n]);
+        uacc[n] = mfma(ones, b[n], uacc[n]);
+      }
+#pragma unroll
+      for (int dn = 0; dn < 4; ++dn)
+#pragma unroll
+        for (int mn = 0; mn < 4; ++mn) S[dn][mn] = mfma(a[dn], b[mn], S[dn][mn]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  // partials to LDS: Sp[w][d][m] (rows padded to RP floats), Zp[w][d], Up[w][m]
+  __syncthreads();
+  float* Sp = reinterpret_cast<float*>(smem);
+  float* Zp = Sp + 4 * DIM * RP;
+  float* Up = Zp + 4 * DIM;
+#pragma unroll
+  for (int dn = 0; dn < 4; ++dn)
+#pragma unroll
+    for (int mn = 0; mn < 4; ++mn)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Sp[(w * DIM + 16 * dn + 4 * g + u) * RP + 16 * mn + li] = S[dn][mn][u];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    if (li == 0)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Zp[w * DIM + 16 * n + 4 * g + u] = zacc[n][u];
+    if (g == 0) Up[w * DIM + 16 * n + li] = uacc[n][0];
+  }
+  __syncthreads();
+  const int64_t rec = bh * P + seg;
+  const float count = static_cast<float>(r1 - r0);
+  const int m = tid & 63;
+  const float um = ((Up[m] + Up[DIM + m]) + Up[2 * DIM + m]) + Up[3 * DIM + m];
+  for (int d = tid >> 6; d < DIM; d += 4) {
+    const float sum = ((Sp[d * RP + m] + Sp[(DIM + d) * RP + m]) + Sp[(2 * DIM + d) * RP + m]) +
+                      Sp[(3 * DIM + d) * RP + m];
+    s_out[rec * s_stride + d * DIM + m] = sum + um;
+  }
+  if (tid < DIM)
+    z_out[rec * z_stride + tid] =
+        (((Zp[tid] + Zp[DIM + tid]) + Zp[2 * DIM + tid]) + Zp[3 * DIM + tid]) + count;
+}
+
 size_t lds_fwd(int dim) {
   const int tiles = dim == 128 ? 3 : 2;  // K, V (and phi(Q) with two waves per query tile)
-  return (tiles * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t) + dim * sizeof(float);
+  const int waves = dim == 128 ? 8 : 4;  // each with a 16 x 64 output staging tile
+  return (tiles * T * (dim + kLdsPad) + dim * (dim + kLdsPad) + waves * 16 * (64 + kLdsPad)) * sizeof(uint16_t) +
+         dim * sizeof(float);
 }
 size_t lds_seg(int dim) { return 2 * T * (dim + kLdsPad) * sizeof(uint16_t); }
+// four wave-private K / V tile pairs; the partials reuse the space at the end
+size_t lds_seg_wave64() {
+  const size_t tiles = 4 * 2 * T * (64 + kLdsPad) * sizeof(uint16_t);
+  const size_t parts = (4 * 64 * (64 + 4) + 2 * 4 * 64) * sizeof(float);
+  return tiles > parts ? tiles : parts;
+}
 
 #define LA_MLAUNCH(kernel, nthreads, grid, lds, st, ...)                                                \
   do {                                                                                                  \
@@ -408,7 +541,7 @@ hipError_t launch_seg_state_mfma(const SegGeom& g, const void* k, const void* v,
   const bf16_t* K = static_cast<const bf16_t*>(k);
   const bf16_t* V = static_cast<const bf16_t*>(v);
   if (g.D == 64)
-    LA_MLAUNCH((k_seg_state_mfma<64>), 64 * kFwdWaves<64>, grid, lds_seg(64), st, K, V, s_out, s_stride, z_out, z_stride, g.N, g.P,
+    LA_MLAUNCH(k_seg_state_wave64, 256, grid, lds_seg_wave64(), st, K, V, s_out, s_stride, z_out, z_stride, g.N, g.P,
                g.seg_len);
   if (g.D == 128)
     LA_MLAUNCH((k_seg_state_mfma<128>), 64 * kFwdWaves<128>, grid, lds_seg(128), st, K, V, s_out, s_stride, z_out, z_stride, g.N,

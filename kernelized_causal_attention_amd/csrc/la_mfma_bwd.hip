@@ -620,6 +620,9 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
   // MFMA under an EXEC-masked branch still writes every lane.
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // this wave's staging tiles for its dv and dk rows
+  uint16_t* sDV = sCh + 2 * T + w * 2 * 16 * LD;
+  uint16_t* sDK = sDV + 16 * LD;
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
@@ -748,9 +751,11 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
       f32x4_t rk;
 #pragma unroll
       for (int u = 0; u < 4; ++u) rk[u] = (ok[u] + rr[u]) * fminf(kv[u], 1.f);
-      bstore8(rdv, pack4(ov), (j * DIM + 16 * n + 4 * g) * 2, soff);
-      bstore8(rdk, pack4(rk), (j * DIM + 16 * n + 4 * g) * 2, soff);
+      stage_piece<DIM>(sDV, pack4(ov), li, g, n);
+      stage_piece<DIM>(sDK, pack4(rk), li, g, n);
     }
+    store_staged<DIM, DIM>(sDV, rdv, 16 * w, 0, soff);
+    store_staged<DIM, DIM>(sDK, rdk, 16 * w, 0, soff);
     if (CAUSAL) outer_update<DIM, true>(Racc, racc, sG, sQf, sCh, w, g, li);
     __syncthreads();
     if (CAUSAL) write_xt<DIM>(sR, sRv, Racc, racc, w, g, li);
@@ -762,7 +767,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
 
 size_t lds_bwd(int dim) {
   return (4 * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t) + (dim + T) * sizeof(float) +
-         2 * T * sizeof(uint16_t);
+         2 * T * sizeof(uint16_t) + 4 * 2 * 16 * (dim + kLdsPad) * sizeof(uint16_t);  // + output staging
 }
 size_t lds_ragg(int dim) { return 2 * T * (dim + kLdsPad) * sizeof(uint16_t) + 4 * sizeof(float) + 2 * T * sizeof(uint16_t); }
 size_t lds_dq(int dim) {

@@ -205,6 +205,42 @@ __device__ __forceinline__ void store_tile_elu(uint16_t* lds, const i32x4 (&raw)
   }
 }
 
+// Coalesced output rows.  An MFMA accumulator tile gives lane (li, g) four
+// consecutive columns of row li, so storing straight from it writes 16 rows
+// in 8-byte pieces per instruction, which the memory system takes well
+// below its streaming rate.  Instead each wave puts its pieces into a
+// private LDS tile of 16 rows x COLS bf16 (row stride COLS + kLdsPad) and
+// reads it back in 16-byte pieces, so every store instruction writes whole
+// runs of consecutive row bytes.
+__device__ __forceinline__ void wave_lds_sync() {
+  // a wave's LDS operations complete in order: only the compiler has to be
+  // kept from moving them across this point
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+template <int COLS>
+__device__ __forceinline__ void stage_piece(uint16_t* stage, i16x4 v, int li, int g, int n) {
+  *reinterpret_cast<i16x4*>(stage + li * (COLS + kLdsPad) + 16 * n + 4 * g) = v;
+}
+// Rows row0 .. row0 + 15 of a row-major [*, ROWLEN] bf16 tensor, columns
+// col0 .. col0 + COLS - 1, from the staged tile; `soff` is the chunk's byte
+// offset.  Rows past the buffer's range are dropped by the hardware check.
+template <int COLS, int ROWLEN>
+__device__ __forceinline__ void store_staged(const uint16_t* stage, rsrc_t dst, int row0, int col0, int soff) {
+  constexpr int PR = COLS / 8;  // 16-byte pieces per row
+  const int l = threadIdx.x & 63;
+  wave_lds_sync();
+#pragma unroll
+  for (int k = 0; k < 16 * PR / 64; ++k) {
+    const int p = 64 * k + l, r = p / PR, c8 = p % PR;
+    const i16x8 v = *reinterpret_cast<const i16x8*>(stage + r * (COLS + kLdsPad) + 8 * c8);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), dst,
+                                           ((row0 + r) * ROWLEN + col0 + 8 * c8) * 2, soff, 0);
+  }
+  wave_lds_sync();
+}
+
 // Buffer versions of load_tile / load_q: `soff` is the chunk's first row in
 // bytes; rows past the head's end read as zero.
 template <int DIM, int NW = 4>
