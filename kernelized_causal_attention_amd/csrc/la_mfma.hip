@@ -139,7 +139,10 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_
   // MFMA under an EXEC-masked branch still writes every lane.
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rt = w & 3;             // query row tile
+  // query row tile; the triangular intra-chunk work grows with it, so odd
+  // workgroups take the tiles in reverse and two workgroups sharing a CU
+  // give every SIMD the same total
+  const int rt = (blockIdx.x & 1) ? 3 - (w & 3) : (w & 3);
   const int nb = NCG == 1 ? 0 : (w >> 2) * NTW;  // first output tile of this wave
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;

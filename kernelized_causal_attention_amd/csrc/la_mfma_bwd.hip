@@ -305,6 +305,10 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
   // MFMA under an EXEC-masked branch still writes every lane.
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // The triangular intra-chunk work grows with a wave's row tile (tile t
+  // does t + 1 key tiles); odd workgroups map wave w to tile 3 - w, so two
+  // workgroups sharing a CU give every SIMD the same total.
+  const int rw = (blockIdx.x & 1) ? 3 - w : w;
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
@@ -318,7 +322,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
   float* ch = c_out + bh * N;
   float* dh = den_out + bh * N;
   const bool want_r = FUSED_R && r_agg != nullptr;
-  const int i = 16 * w + li;
+  const int i = 16 * rw + li;
   const int cc = 4 * (li % 4);
   const short one = 0x3f80;  // bf16 1.0
   const i16x8 ones = {one, one, one, one, one, one, one, one};
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) mt[t][u] = (t < w || (t == w && 4 * g + u <= li)) ? 1.f : 0.f;
+    for (int u = 0; u < 4; ++u) mt[t][u] = (t < rw || (t == rw && 4 * g + u <= li)) ? 1.f : 0.f;
 
   f32x4_t Sacc[DT][NTL], zacc[DT], uacc[DT];
   // n0: the ones-direction count of the state before the current chunk
@@ -394,7 +398,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         at[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (t <= w) {
+        if (t <= rw) {
           at[t] = f32x4_t{dq_i, dq_i, dq_i, dq_i};
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
@@ -445,7 +449,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         bv[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (t <= w) {
+        if (t <= rw) {
 #pragma unroll
           for (int s = 0; s < KS; ++s) bv[t] = mfma(lds8(sV + (16 * t + li) * LD + 8 * g + 32 * s), gq[s], bv[t]);
         }
@@ -460,7 +464,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
     if (CAUSAL) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        if (t <= w) {
+        if (t <= rw) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             dot += at[t][u] * bv[t][u];  // at is masked
@@ -488,7 +492,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
       for (int n = 0; n < NTL; ++n) {
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {
-          if (2 * tp <= w) {
+          if (2 * tp <= rw) {
             const int jr = 32 * tp + 4 * g + li / 4;
             const i16x8 a = cat(lds_tr(sKe + jr * LD + 16 * n + cc), lds_tr(sKe + (jr + 16) * LD + 16 * n + cc));
             o[n] = mfma(a, cat(bt[2 * tp], bt[2 * tp + 1]), o[n]);
@@ -620,6 +624,10 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
   // MFMA under an EXEC-masked branch still writes every lane.
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // The triangular intra-chunk work grows with a wave's row tile (tile t
+  // does t + 1 key tiles); odd workgroups map wave w to tile 3 - w, so two
+  // workgroups sharing a CU give every SIMD the same total.
+  const int rw = (blockIdx.x & 1) ? 3 - w : w;
   // this wave's staging tiles for its dv and dk rows
   uint16_t* sDV = sCh + 2 * T + w * 2 * 16 * LD;
   uint16_t* sDK = sDV + 16 * LD;
@@ -636,14 +644,14 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
                rdv = make_rsrc(dv + hoff, hbytes);
   const float* denh = den_in + bh * N;
   const float* chh = c_in + bh * N;
-  const int j = 16 * w + li;  // this lane's key row (outputs); also its query row for g, c
+  const int j = 16 * rw + li;  // this lane's key row (outputs); also its query row for g, c
   // causal mask of query i = 16t + 4g + u against key j = 16w + li (i >= j)
   // as 0 / 1 factors
   f32x4_t mt[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) mt[t][u] = (t > w || (t == w && 4 * g + u >= li)) ? 1.f : 0.f;
+    for (int u = 0; u < 4; ++u) mt[t][u] = (t > rw || (t == rw && 4 * g + u >= li)) ? 1.f : 0.f;
 
   f32x4_t Racc[DT][NTL], racc[DT];
   init_xt<DIM>(Racc, racc, cr, w, g, li);
@@ -704,7 +712,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         ahi[t] = alo[t] = bm[t] = i16x4{0, 0, 0, 0};
-        if (t >= w) {
+        if (t >= rw) {
           f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
@@ -735,7 +743,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
       if (CAUSAL) {
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {
-          if (2 * tp + 1 >= w) {
+          if (2 * tp + 1 >= rw) {
             const int ir = 32 * tp + 4 * g + li / 4;
             const i16x8 ag = cat(lds_tr(sG + ir * LD + 16 * n + cc), lds_tr(sG + (ir + 16) * LD + 16 * n + cc));
             ov = mfma(ag, cat(ahi[2 * tp], ahi[2 * tp + 1]), ov);
@@ -754,8 +762,8 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
       stage_piece<DIM>(sDV, pack4(ov), li, g, n);
       stage_piece<DIM>(sDK, pack4(rk), li, g, n);
     }
-    store_staged<DIM, DIM>(sDV, rdv, 16 * w, 0, soff);
-    store_staged<DIM, DIM>(sDK, rdk, 16 * w, 0, soff);
+    store_staged<DIM, DIM>(sDV, rdv, 16 * rw, 0, soff);
+    store_staged<DIM, DIM>(sDK, rdk, 16 * rw, 0, soff);
     if (CAUSAL) outer_update<DIM, true>(Racc, racc, sG, sQf, sCh, w, g, li);
     __syncthreads();
     if (CAUSAL) write_xt<DIM>(sR, sRv, Racc, racc, w, g, li);
