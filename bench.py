@@ -71,7 +71,36 @@ def parse():
                          "over the first few hundred milliseconds of load)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only run the streaming-bandwidth microbenchmark and print its lines")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-bandwidth microbenchmark (e.g. under a profiler)")
     return ap.parse_args()
+
+
+CEILING_EXE = os.path.join(ROOT, "kernelized_causal_attention_amd", "_lib", "hbm_ceiling")
+# the traffic mix of each kernel (tensors read / written), for its practical ceiling
+KERNEL_MIX = {"mfma.seg_state": "r2", "mfma.forward": "r3w1", "mfma.bwd_dq": "r4w1", "mfma.bwd_dkdv": "r4w2",
+              "decode": "r1w1"}
+
+
+def hbm_ceilings():
+    """Streaming rates of plain 16-byte-vector kernels for each traffic mix,
+    measured on this GPU by a child process (the parent has not touched the
+    GPU yet).  Returns {mix: GB/s}, or None when the program is missing."""
+    if not os.path.exists(CEILING_EXE):
+        log(f"{CEILING_EXE} missing (build first): no practical ceilings")
+        return None
+    r = subprocess.run([CEILING_EXE], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        log(f"hbm_ceiling failed ({r.returncode}): {r.stderr.strip()[-300:]}")
+        return None
+    mixes = {}
+    for line in r.stdout.splitlines():
+        d = json.loads(line)
+        mixes[d["mix"]] = d["GBps"]
+    log("streaming ceilings (GB/s): " + ", ".join(f"{k} {v:.0f}" for k, v in mixes.items()))
+    return mixes
 
 
 # ---------------------------------------------------------------- bytes ----
@@ -130,10 +159,16 @@ def kernel_flops(name: str, B, H, N, D, M, causal=True):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(every (b,h) head is independent; multi-GPU sharding is described in the design notes, "
               "not run).", file=sys.stderr)
         sys.exit(2)
+    if args.ceilings:
+        r = subprocess.run([CEILING_EXE])
+        sys.exit(r.returncode)
+    ceil = None
+    if not (args.no_ceiling or args.calibrate_copy or args.retention_only or args.poly_only):
+        ceil = hbm_ceilings()
 
     import torch
 
@@ -222,6 +257,10 @@ def main():
         avg = t / n
         kernels[name] = {"launches_per_step": n / nbreak, "avg_ms": round(avg, 4),
                          "alg_bytes": b, "GBps": round(b / (avg / 1e3) / 1e9, 1) if b else None}
+        mix = KERNEL_MIX.get(name)
+        if ceil and mix in ceil and b:
+            kernels[name]["ceiling_mix"] = mix
+            kernels[name]["frac_of_ceiling"] = round(b / (avg / 1e3) / 1e9 / ceil[mix], 4)
     result = {
         "metric": "causal linear-attn fwd+bwd tokens/sec",
         "value": round(value, 1),
@@ -244,9 +283,19 @@ def main():
                      "alg_bytes_per_launch": kb, "avg_launch_ms": round(avg_ms, 4)},
         "kernels": kernels,
     }
+    if ceil:
+        mix = KERNEL_MIX.get(kname)
+        result["hbm_ceiling"] = {
+            "source": "streaming microbenchmark on this GPU (kernelized_causal_attention_amd/_lib/hbm_ceiling): "
+                      "plain 16-byte-vector kernels over 134 MB tensors, GB/s per traffic mix",
+            "mixes": ceil, "dominant_mix": mix,
+            "dominant_frac_of_ceiling": round(achieved / ceil[mix], 4) if mix in ceil else None}
 
     if not args.no_extra:
         result["decode"] = bench_decode(la, torch, args.decode_steps)
+        if ceil and "r1w1" in ceil:
+            result["decode"]["roofline"]["frac_of_ceiling"] = round(
+                result["decode"]["roofline"]["achieved"] / ceil["r1w1"], 4)
         result["retention"] = bench_retention(la, torch, args.steps, args.warmup)
         result["poly"] = bench_poly(la, torch, args.steps, args.warmup)
         result["softmax"] = bench_softmax(la, torch, args.steps, args.warmup)

@@ -4,7 +4,9 @@ Usage:  python -m kernelized_causal_attention_amd.build   (from the repo root)
 
 Every source under ``csrc/`` is compiled on its own (in parallel) and the
 objects are linked into one shared library that exports the C ABI declared in
-``include/linattn.h``.  Packed-fp32 instruction forms are disabled for all
+``include/linattn.h``.  ``ceiling/hbm_ceiling.hip`` becomes the executable
+``_lib/hbm_ceiling``, the streaming-bandwidth microbenchmark that
+``bench.py --ceilings`` runs.  Packed-fp32 instruction forms are disabled for all
 device code (``-packed-fp32-ops``).
 """
 
@@ -23,6 +25,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "liblinattn.so")
+# streaming-bandwidth microbenchmark (measurement only; not part of the library)
+CEILING_SRC = os.path.join(PKG, "ceiling", "hbm_ceiling.hip")
+CEILING_EXE = os.path.join(OUT_DIR, "hbm_ceiling")
 OBJ_DIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
@@ -70,8 +75,13 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    cmd = [hipcc(), *COMMON, "-o", CEILING_EXE + ".tmp", CEILING_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {CEILING_SRC}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(CEILING_EXE + ".tmp", CEILING_EXE)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
+        print(f"built {LIB} and {CEILING_EXE}", file=sys.stderr)
     return LIB
 
 
