@@ -300,6 +300,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
   float* sU = sZ + DIM;                // U
   float* sRed = sU + DIM;              // 4 floats: per-wave sums of c
   uint16_t* sCh2 = reinterpret_cast<uint16_t*>(sRed + 4);  // c hi/lo, two buffers of 2T
+  uint16_t* sStage = sCh2 + 4 * T;     // per-wave dq staging, 16 x LD each
 
   // w is made wave-uniform (an SGPR) so that branches on it are scalar: an
   // MFMA under an EXEC-masked branch still writes every lane.
@@ -324,6 +325,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
   const bool want_r = FUSED_R && r_agg != nullptr;
   const int i = 16 * rw + li;
   const int cc = 4 * (li % 4);
+  uint16_t* sDQ = sStage + w * 16 * LD;
   const short one = 0x3f80;  // bf16 1.0
   const i16x8 ones = {one, one, one, one, one, one, one, one};
   // causal mask of key j = 16t + 4g + u against query i = 16w + li, as 0 / 1
@@ -507,8 +509,9 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
       // phi'(q) = min(phi(q), 1) = 1 + min(E, 0)
 #pragma unroll
       for (int u = 0; u < 4; ++u) r[u] = (beta + o[n][u] + c * z[u]) * (1.f + fminf(qd[n][u], 0.f));
-      bstore8(rdq, pack4(r), (i * DIM + 16 * n + 4 * g) * 2, soff);
+      stage_piece<DIM>(sDQ, pack4(r), li, g, n);
     }
+    store_staged<DIM, DIM>(sDQ, rdq, 16 * rw, 0, soff);
     if (CAUSAL) outer_update_y<DIM, false>(Sacc, zacc, uacc, sV, sKe, nullptr, w, g, li);
     __syncthreads();
     // this chunk's g, E(Q) and c rows are complete: sum its (R, r) part
@@ -780,7 +783,7 @@ size_t lds_bwd(int dim) {
 size_t lds_ragg(int dim) { return 2 * T * (dim + kLdsPad) * sizeof(uint16_t) + 4 * sizeof(float) + 2 * T * sizeof(uint16_t); }
 size_t lds_dq(int dim) {
   return (6 * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t) + (2 * dim + 4) * sizeof(float) +
-         4 * T * sizeof(uint16_t);
+         4 * T * sizeof(uint16_t) + 4 * 16 * (dim + kLdsPad) * sizeof(uint16_t);  // + output staging
 }
 
 #define LA_MLAUNCH(kernel, grid, lds, st, ...)                                                              \
