@@ -153,6 +153,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_fwd_mfma(const bf
   // under an EXEC-masked branch still writes every lane.
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint16_t* sOut = sST + DIM * LD + w * 16 * LD;  // this wave's output staging tile
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
@@ -239,7 +240,8 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_fwd_mfma(const bf
     }
     // rows past the head's end fall outside the buffer range: dropped
 #pragma unroll
-    for (int n = 0; n < NTL; ++n) bstore8(ry, pack4(o[n]), (i * DIM + 16 * n + 4 * g) * 2, soff);
+    for (int n = 0; n < NTL; ++n) stage_piece<DIM>(sOut, pack4(o[n]), li, g, n);
+    store_staged<DIM, DIM>(sOut, ry, 16 * w, 0, soff);
     decay_update<DIM>(Sacc, bT, sKs, sV, w, g, li);
     __syncthreads();
     write_st<DIM>(sST, Sacc, w, g, li);
@@ -428,6 +430,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
   uint16_t* sS = sG + T * LD;  // bf16 S, row-major [d][m]
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint16_t* sOut = sS + DIM * LD + w * 16 * LD;  // this wave's output staging tile
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
@@ -538,7 +541,8 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
       }
     }
 #pragma unroll
-    for (int n = 0; n < NTL; ++n) bstore8(rdq, pack4(o[n]), (i * DIM + 16 * n + 4 * g) * 2, soff);
+    for (int n = 0; n < NTL; ++n) stage_piece<DIM>(sOut, pack4(o[n]), li, g, n);
+    store_staged<DIM, DIM>(sOut, rdq, 16 * w, 0, soff);
     if (g == 0 && i < nrow) qdqh[c0 + i] = qd;
     // state and suffix aggregate
     decay_update<DIM>(Sacc, bT, sKs, sV, w, g, li);
@@ -582,6 +586,8 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
   float* sRow = reinterpret_cast<float*>(sR + DIM * LD);  // [wave][row] partial row sums of w
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint16_t* sDV = reinterpret_cast<uint16_t*>(sRow + 4 * T) + w * 2 * 16 * LD;  // this wave's dv, dk staging
+  uint16_t* sDK = sDV + 16 * LD;
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
@@ -717,9 +723,11 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
                     cat(bm[2 * tp], bm[2 * tp + 1]), ok);
         }
       }
-      bstore8(rdv, pack4(ov), (j * DIM + 16 * n + 4 * g) * 2, soff);
-      bstore8(rdk, pack4(ok), (j * DIM + 16 * n + 4 * g) * 2, soff);
+      stage_piece<DIM>(sDV, pack4(ov), li, g, n);
+      stage_piece<DIM>(sDK, pack4(ok), li, g, n);
     }
+    store_staged<DIM, DIM>(sDV, rdv, 16 * w, 0, soff);
+    store_staged<DIM, DIM>(sDK, rdk, 16 * w, 0, soff);
     kd = shfl_sum_groups(kd);
     // R for the previous chunk: exp(b_T) R + sum_i exp(b_i) q_i dy_i^T
     const float dT = __expf(bT);
@@ -805,10 +813,14 @@ __global__ __launch_bounds__(NT) void k_ret_dlg(const float* __restrict__ a, con
   }
 }
 
-size_t lds_ret_fwd(int dim) { return (3 * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t); }
+// each also holds a 16-row output staging tile per wave (two in the dk / dv sweep)
+size_t lds_ret_fwd(int dim) { return (3 * T * (dim + kLdsPad) + dim * (dim + kLdsPad) + 4 * 16 * (dim + kLdsPad)) * sizeof(uint16_t); }
 size_t lds_ret_seg(int dim) { return 2 * T * (dim + kLdsPad) * sizeof(uint16_t); }
-size_t lds_ret_dq(int dim) { return (6 * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t); }
-size_t lds_ret_dkdv(int dim) { return (5 * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t) + 4 * T * sizeof(float); }
+size_t lds_ret_dq(int dim) { return (6 * T * (dim + kLdsPad) + dim * (dim + kLdsPad) + 4 * 16 * (dim + kLdsPad)) * sizeof(uint16_t); }
+size_t lds_ret_dkdv(int dim) {
+  return (5 * T * (dim + kLdsPad) + dim * (dim + kLdsPad) + 4 * 2 * 16 * (dim + kLdsPad)) * sizeof(uint16_t) +
+         4 * T * sizeof(float);
+}
 
 #define LA_RLAUNCH(kernel, grid, lds, st, ...)                                                               \
   do {                                                                                                       \
