@@ -282,12 +282,15 @@ __device__ __forceinline__ void store_r(float* __restrict__ rec, const f32x4_t (
 // FUSED_R: the (R, r) aggregate is summed here (D = 64); at D = 128 the two
 // fp32 128 x 128 states do not fit one wave's registers together, and
 // k_bwd_ragg_mfma sums the aggregate in a pass of its own.
-template <int DIM, bool CAUSAL, bool FUSED_R>
-__global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                                                       const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
-                                                       const float* __restrict__ carry_s, bf16_t* __restrict__ dq,
-                                                       float* __restrict__ r_agg, float* __restrict__ c_out,
-                                                       float* __restrict__ den_out, int64_t N, int P, int seg_len) {
+// The sweep for one query row tile RW of the chunk: every branch on the
+// row tile (the triangle of key tiles) resolves at compile time, and the
+// chunk body becomes one stretch of code to schedule (the dq sweep is
+// bound by its instruction issue; 162 -> 153 us at B=8 H=16 N=8192 D=64).
+template <int DIM, bool CAUSAL, bool FUSED_R, int RW>
+__device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                                        const bf16_t* __restrict__ dout, const float* __restrict__ carry_s,
+                                        bf16_t* __restrict__ dq, float* __restrict__ r_agg, float* __restrict__ c_out,
+                                        float* __restrict__ den_out, int64_t N, int P, int seg_len) {
   using G = Geo<DIM>;
   constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -306,10 +309,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
   // MFMA under an EXEC-masked branch still writes every lane.
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // The triangular intra-chunk work grows with a wave's row tile (tile t
-  // does t + 1 key tiles); odd workgroups map wave w to tile 3 - w, so two
-  // workgroups sharing a CU give every SIMD the same total.
-  const int rw = (blockIdx.x & 1) ? 3 - w : w;
+  constexpr int rw = RW;  // query row tile (chosen by k_bwd_dq_mfma)
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
@@ -537,6 +537,27 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
       const float C = sRed[0] + sRed[1] + sRed[2] + sRed[3];
       store_r<DIM>(r_agg + (bh * P + seg) * ER, Racc, racc, gacc, C, w, g, li);
     }
+  }
+}
+
+template <int DIM, bool CAUSAL, bool FUSED_R>
+__global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                       const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
+                                                       const float* __restrict__ carry_s, bf16_t* __restrict__ dq,
+                                                       float* __restrict__ r_agg, float* __restrict__ c_out,
+                                                       float* __restrict__ den_out, int64_t N, int P, int seg_len) {
+  // The triangular intra-chunk work grows with a wave's row tile (tile t
+  // does t + 1 key tiles); odd workgroups map wave w to tile 3 - w, so two
+  // workgroups sharing a CU give every SIMD the same total.
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  switch ((blockIdx.x & 1) ? 3 - w : w) {
+#define LA_DQ_BODY(RW_) \
+  case RW_: dq_body<DIM, CAUSAL, FUSED_R, RW_>(q, k, v, dout, carry_s, dq, r_agg, c_out, den_out, N, P, seg_len); break
+    LA_DQ_BODY(0);
+    LA_DQ_BODY(1);
+    LA_DQ_BODY(2);
+    LA_DQ_BODY(3);
+#undef LA_DQ_BODY
   }
 }
 
