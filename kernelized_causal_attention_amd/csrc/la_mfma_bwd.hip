@@ -387,6 +387,11 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
     f32x4_t qd[NTL];
 #pragma unroll
     for (int n = 0; n < NTL; ++n) qd[n] = unpack4(*reinterpret_cast<const i16x4*>(sQe + i * LD + 16 * n + 4 * g));
+    // phi(Q_i) = 1 + E in the accumulator layout (an arithmetic result, so
+    // the min below needs no NaN canonicalisation)
+    f32x4_t pq[NTL];
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) pq[n] = 1.f + qd[n];
     // sum_d phi(Q_i) = D + sum_d E(Q_i), through the MFMA against ones
     f32x4_t sq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -420,7 +425,7 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
     for (int n = 0; n < NTL; ++n) {
       const f32x4_t z = *reinterpret_cast<const f32x4_t*>(sZ + 16 * n + 4 * g);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) di += (1.f + qd[n][u]) * z[u];
+      for (int u = 0; u < 4; ++u) di += pq[n][u] * z[u];
     }
     const float den = shfl_sum_groups(rs + di) + n0 * dq_i;
     const float inv = valid ? __builtin_amdgcn_rcpf(den) : 0.f;  // the reverse sweep forms the same g
@@ -462,7 +467,7 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
 #pragma unroll
     for (int n = 0; n < NTL; ++n)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) dot += (1.f + qd[n][u]) * o[n][u];
+      for (int u = 0; u < 4; ++u) dot += pq[n][u] * o[n][u];
     if (CAUSAL) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -506,9 +511,9 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
     for (int n = 0; n < NTL; ++n) {
       const f32x4_t z = *reinterpret_cast<const f32x4_t*>(sZ + 16 * n + 4 * g);
       f32x4_t r;
-      // phi'(q) = min(phi(q), 1) = 1 + min(E, 0)
+      // phi'(q) = min(phi(q), 1)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) r[u] = (beta + o[n][u] + c * z[u]) * (1.f + fminf(qd[n][u], 0.f));
+      for (int u = 0; u < 4; ++u) r[u] = (beta + o[n][u] + c * z[u]) * fminf(pq[n][u], 1.f);
       stage_piece<DIM>(sDQ, pack4(r), li, g, n);
     }
     store_staged<DIM, DIM>(sDQ, rdq, 16 * rw, 0, soff);
