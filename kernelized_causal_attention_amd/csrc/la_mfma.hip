@@ -514,8 +514,8 @@ size_t lds_seg_wave64() {
 
 int mfma_supported(int op, int64_t D, int64_t M, int dtype) {
   if (D != M) return 0;
-  // fp32 (v_mfma_f32_16x16x4_f32): forward and prefix state at D = M = 64
-  if (dtype == 0) return D == 64 && (op == 0 /* forward */ || op == 2 /* prefix state */);
+  // fp32 (v_mfma_f32_16x16x4_f32): forward at D = M = 64, prefix state at 64 and 128
+  if (dtype == 0) return (D == 64 && op == 0 /* forward */) || ((D == 64 || D == 128) && op == 2 /* prefix state */);
   if (dtype != 1 || (D != 64 && D != 128)) return 0;
   return op == 0 /* forward */ || op == 1 /* backward */ || op == 2 /* prefix state */;
 }

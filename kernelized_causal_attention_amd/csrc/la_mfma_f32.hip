@@ -1,5 +1,6 @@
 // fp32 MFMA kernels for the chunked forward and the segment states (gfx950),
-// D = M = 64, fp32 inputs and outputs.
+// D = M = 64 (forward and segment states) and D = M = 128 (segment states),
+// fp32 inputs and outputs.
 //
 // Same method and schedule as the bf16 kernels ("[Paper walkthrough]
 // Transformers are RNNs", wkq9411.github.io, sections 2 and 3: phi = elu + 1,
@@ -226,55 +227,110 @@ __global__ __launch_bounds__(NT, 2) void k_fwd_f32mfma(const float* __restrict__
   }
 }
 
-// Segment aggregates dS = phi(K)^T V, dZ = colsum phi(K) over one segment.
+// Segment aggregates dS = phi(K)^T V, dZ = colsum phi(K) over one segment,
+// at D = M = DIM (64 or 128).  Wave w owns the RT = DIM / 64 state row tiles
+// 16 (RT w + rt) .. + 15 and every column tile; the chunk's phi(K) and V
+// rows are staged in LDS (row stride DIM + 4 floats).
+template <int DIM>
 __global__ __launch_bounds__(NT, 2) void k_seg_state_f32mfma(const float* __restrict__ k, const float* __restrict__ v,
                                                              float* __restrict__ s_out, int64_t s_stride,
                                                              float* __restrict__ z_out, int64_t z_stride, int64_t N,
                                                              int P, int seg_len) {
+  constexpr int LDD = DIM + 4;
+  constexpr int RT = DIM / 64;     // 16-row state tiles per wave
+  constexpr int CT = DIM / 16;     // 16-column state tiles
+  constexpr int PR = DIM / 4;      // 16-byte pieces per token row
+  constexpr int PC = T * PR / NT;  // pieces per thread per chunk tile
   extern __shared__ __align__(16) float smf[];
   float* sKf = smf;
-  float* sV = sKf + T * LDF;
+  float* sV = sKf + T * LDD;
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
   const int64_t r1 = min(N, r0 + seg_len);
-  const float* kh = k + bh * N * DF;
-  const float* vh = v + bh * N * DF;
-  f32x4_t Sacc[4] = {}, zacc = {0.f, 0.f, 0.f, 0.f};
+  const float* kh = k + bh * N * DIM;
+  const float* vh = v + bh * N * DIM;
+  f32x4_t Sacc[RT][CT], zacc[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    zacc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < CT; ++n) Sacc[rt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // piece p of a T x DIM tile: row p / PR, features 4 (p % PR) .. + 3
+  auto load = [&](f32x4 (&raw)[PC], const float* __restrict__ src, int64_t c0, int nrow) {
+#pragma unroll
+    for (int r = 0; r < PC; ++r) {
+      const int p = tid + NT * r, j = p / PR, c4 = p % PR;
+      raw[r] = j < nrow ? *reinterpret_cast<const f32x4*>(src + (c0 + j) * DIM + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  // rows past nrow were loaded as zero; phi is applied to the valid rows only
+  auto stage = [&](float* lds, const f32x4 (&raw)[PC], int nrow, bool phi) {
+#pragma unroll
+    for (int r = 0; r < PC; ++r) {
+      const int p = tid + NT * r, j = p / PR, c4 = p % PR;
+      f32x4 x = raw[r];
+      if (phi && j < nrow) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = phi_f(x[e]);
+      }
+      *reinterpret_cast<f32x4*>(lds + j * LDD + 4 * c4) = x;
+    }
+  };
   int64_t c0 = r0;
   int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
-  f32x4 kraw[4], vraw[4];
-  load_f32(kraw, kh, c0, nrow);
-  load_f32(vraw, vh, c0, nrow);
+  f32x4 kraw[PC], vraw[PC];
+  load(kraw, kh, c0, nrow);
+  load(vraw, vh, c0, nrow);
   while (c0 < r1) {
-    stage_f32<true>(sKf, nrow, kraw);
-    stage_f32<false>(sV, nrow, vraw);
+    stage(sKf, kraw, nrow, true);
+    stage(sV, vraw, nrow, false);
     __syncthreads();
     const int64_t c1 = c0 + T;
     const int nrow1 = c1 < r1 ? static_cast<int>(min(static_cast<int64_t>(T), r1 - c1)) : 0;
     if (nrow1 > 0) {
-      load_f32(kraw, kh, c1, nrow1);
-      load_f32(vraw, vh, c1, nrow1);
+      load(kraw, kh, c1, nrow1);
+      load(vraw, vh, c1, nrow1);
     }
-    state_update_f32(Sacc, zacc, sKf, sV, w, g, li);
+    // S[d][m] += sum_j phi(K_j)[d] V_j[m], Z[d] += sum_j phi(K_j)[d] over the
+    // chunk's 64 keys (step s, lane group g: key 16 g + s)
+#pragma unroll
+    for (int s_ = 0; s_ < 16; ++s_) {
+      const int j = 16 * g + s_;
+      float a[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        a[rt] = sKf[j * LDD + 16 * (RT * w + rt) + li];
+        zacc[rt] = mfma4(a[rt], 1.f, zacc[rt]);
+      }
+#pragma unroll
+      for (int n = 0; n < CT; ++n) {
+        const float b = sV[j * LDD + 16 * n + li];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) Sacc[rt][n] = mfma4(a[rt], b, Sacc[rt][n]);
+      }
+    }
     __syncthreads();
     c0 = c1;
     nrow = nrow1;
   }
   const int64_t rec = bh * P + seg;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int d = 16 * w + 4 * g + u;
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) s_out[rec * s_stride + d * DF + 16 * n + li] = Sacc[n][u];
-    if (li == 0) z_out[rec * z_stride + d] = zacc[u];
-  }
+    for (int u = 0; u < 4; ++u) {
+      const int d = 16 * (RT * w + rt) + 4 * g + u;
+#pragma unroll
+      for (int n = 0; n < CT; ++n) s_out[rec * s_stride + d * DIM + 16 * n + li] = Sacc[rt][n][u];
+      if (li == 0) z_out[rec * z_stride + d] = zacc[rt][u];
+    }
 }
 
 constexpr size_t kLdsFwd = (3 * T * LDF + DF * LDF + DF) * sizeof(float);
-constexpr size_t kLdsSeg = 2 * T * LDF * sizeof(float);
+constexpr size_t lds_seg_f32(int dim) { return 2 * T * (dim + 4) * sizeof(float); }
 
 }  // namespace
 
@@ -301,10 +357,21 @@ hipError_t launch_forward_f32mfma(int causal, const SegGeom& g, const void* q, c
 
 hipError_t launch_seg_state_f32mfma(const SegGeom& g, const void* k, const void* v, float* s_out, int64_t s_stride,
                                     float* z_out, int64_t z_stride, hipStream_t st) {
-  if (g.D != DF || g.M != DF) return hipErrorNotSupported;
-  hipLaunchKernelGGL(k_seg_state_f32mfma, dim3(static_cast<unsigned>(g.BH * g.P)), dim3(NT), kLdsSeg, st,
-                     static_cast<const float*>(k), static_cast<const float*>(v), s_out, s_stride, z_out, z_stride,
-                     g.N, g.P, g.seg_len);
+  if (g.D != g.M || (g.D != 64 && g.D != 128)) return hipErrorNotSupported;
+  const dim3 grid(static_cast<unsigned>(g.BH * g.P));
+  const float* K = static_cast<const float*>(k);
+  const float* V = static_cast<const float*>(v);
+  if (g.D == 64) {
+    hipLaunchKernelGGL((k_seg_state_f32mfma<64>), grid, dim3(NT), lds_seg_f32(64), st, K, V, s_out, s_stride, z_out,
+                       z_stride, g.N, g.P, g.seg_len);
+    return hipGetLastError();
+  }
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_seg_state_f32mfma<128>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(lds_seg_f32(128)));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_seg_state_f32mfma<128>), grid, dim3(NT), lds_seg_f32(128), st, K, V, s_out, s_stride, z_out,
+                     z_stride, g.N, g.P, g.seg_len);
   return hipGetLastError();
 }
 

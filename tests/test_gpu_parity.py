@@ -389,6 +389,21 @@ def test_f32_mfma_forward_unscaled_and_prefix_state():
     assert rel_l2(f64(Z), Z0) < 1e-6
 
 
+@pytest.mark.parametrize("N", [333, 2000])
+@pytest.mark.parametrize("scale", [1.0 / np.sqrt(128), 1.0])
+def test_f32_prefix_state_d128(N, scale):
+    # fp32 D = M = 128 on the fp32 MFMA segment kernel: one segment at N = 333
+    # (a ragged last chunk), eight segments and the scan at N = 2000
+    assert la.resolve_plan("prefix_state", 2, 3, N, 128, 128, True, "f32")["kernel"] == 2
+    tq, tk, tv, _ = host_case(2, 3, N, 128, 128, "f32", seed=29, scale=scale)
+    S, Z = la.prefix_state(tk, tv)
+    torch.cuda.synchronize()
+    S0, Z0 = oracle.prefix_state(f64(tk), f64(tv))
+    say(f"f32 prefix state D=128 N={N} scale={scale:.3f}: S {rel_l2(f64(S), S0):.2e} Z {rel_l2(f64(Z), Z0):.2e}")
+    assert rel_l2(f64(S), S0) < 1e-6
+    assert rel_l2(f64(Z), Z0) < 1e-6
+
+
 def test_mfma_matches_generic_bf16():
     # two independent kernel families on the same inputs
     tq, tk, tv, tg = host_case(2, 2, 500, 64, 64, "bf16", seed=42, scale=0.125)
