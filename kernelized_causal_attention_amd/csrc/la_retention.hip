@@ -153,6 +153,10 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_fwd_mfma(const bf
   // under an EXEC-masked branch still writes every lane.
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // query (key) row tile of this wave; odd workgroups take the tiles in
+  // reverse so that two workgroups on a CU give each SIMD the same
+  // triangular intra-chunk work
+  const int rw = (blockIdx.x & 1) ? 3 - w : w;
   uint16_t* sOut = sST + DIM * LD + w * 16 * LD;  // this wave's output staging tile
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
@@ -164,13 +168,13 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_fwd_mfma(const bf
   const int64_t hbytes = N * DIM * 2;
   const rsrc_t rq = make_rsrc(q + hoff, hbytes), rk = make_rsrc(k + hoff, hbytes), rv = make_rsrc(v + hoff, hbytes),
                ry = make_rsrc(y + hoff, hbytes), rl = make_rsrc(lg + bh * N, N * 4);
-  const int i = 16 * w + li;
+  const int i = 16 * rw + li;
   // causal mask of key j = 16t + 4g + u against query i, as 0 / 1 factors
   f32x4_t mt[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) mt[t][u] = (t < w || (t == w && 4 * g + u <= li)) ? 1.f : 0.f;
+    for (int u = 0; u < 4; ++u) mt[t][u] = (t < rw || (t == rw && 4 * g + u <= li)) ? 1.f : 0.f;
 
   f32x4_t Sacc[DT][NTL];
   init_s<DIM>(Sacc, cs, w, g, li);
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_fwd_mfma(const bf
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       at[t] = i16x4{0, 0, 0, 0};
-      if (t <= w) {
+      if (t <= rw) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) acc = mfma(lds8(sK + (16 * t + li) * LD + 8 * g + 32 * s), qf[s], acc);
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_fwd_mfma(const bf
     }
 #pragma unroll
     for (int tp = 0; tp < 2; ++tp) {
-      if (2 * tp <= w) {
+      if (2 * tp <= rw) {
         const i16x8 bb = cat(at[2 * tp], at[2 * tp + 1]);
         const int jr = 32 * tp + 4 * g + li / 4;
         const int cc = 4 * (li % 4);
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_fwd_mfma(const bf
     // rows past the head's end fall outside the buffer range: dropped
 #pragma unroll
     for (int n = 0; n < NTL; ++n) stage_piece<DIM>(sOut, pack4(o[n]), li, g, n);
-    store_staged<DIM, DIM>(sOut, ry, 16 * w, 0, soff);
+    store_staged<DIM, DIM>(sOut, ry, 16 * rw, 0, soff);
     decay_update<DIM>(Sacc, bT, sKs, sV, w, g, li);
     __syncthreads();
     write_st<DIM>(sST, Sacc, w, g, li);
@@ -430,6 +434,10 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
   uint16_t* sS = sG + T * LD;  // bf16 S, row-major [d][m]
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // query (key) row tile of this wave; odd workgroups take the tiles in
+  // reverse so that two workgroups on a CU give each SIMD the same
+  // triangular intra-chunk work
+  const int rw = (blockIdx.x & 1) ? 3 - w : w;
   uint16_t* sOut = sS + DIM * LD + w * 16 * LD;  // this wave's output staging tile
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
@@ -443,13 +451,13 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
                rg = make_rsrc(dy + hoff, hbytes), rdq = make_rsrc(dq + hoff, hbytes),
                rl = make_rsrc(lg + bh * N, N * 4);
   float* qdqh = qdq + bh * N;
-  const int i = 16 * w + li;
+  const int i = 16 * rw + li;
   const int cc = 4 * (li % 4);
   f32x4_t mt[4];  // causal mask (key j = 16t + 4g + u <= query i) as 0 / 1
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) mt[t][u] = (t < w || (t == w && 4 * g + u <= li)) ? 1.f : 0.f;
+    for (int u = 0; u < 4; ++u) mt[t][u] = (t < rw || (t == rw && 4 * g + u <= li)) ? 1.f : 0.f;
 
   f32x4_t Sacc[DT][NTL], Racc[DT][NTL];
   init_s<DIM>(Sacc, cs, w, g, li);
@@ -521,7 +529,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      if (t <= w) {
+      if (t <= rw) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) acc = mfma(lds8(sV + (16 * t + li) * LD + 8 * g + 32 * s), gq[s], acc);
 #pragma unroll
@@ -533,7 +541,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
     for (int n = 0; n < NTL; ++n) {
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp) {
-        if (2 * tp <= w) {
+        if (2 * tp <= rw) {
           const int jr = 32 * tp + 4 * g + li / 4;
           const i16x8 a = cat(lds_tr(sK + jr * LD + 16 * n + cc), lds_tr(sK + (jr + 16) * LD + 16 * n + cc));
           o[n] = mfma(a, cat(bt[2 * tp], bt[2 * tp + 1]), o[n]);
@@ -542,7 +550,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
     }
 #pragma unroll
     for (int n = 0; n < NTL; ++n) stage_piece<DIM>(sOut, pack4(o[n]), li, g, n);
-    store_staged<DIM, DIM>(sOut, rdq, 16 * w, 0, soff);
+    store_staged<DIM, DIM>(sOut, rdq, 16 * rw, 0, soff);
     if (g == 0 && i < nrow) qdqh[c0 + i] = qd;
     // state and suffix aggregate
     decay_update<DIM>(Sacc, bT, sKs, sV, w, g, li);
@@ -586,6 +594,10 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
   float* sRow = reinterpret_cast<float*>(sR + DIM * LD);  // [wave][row] partial row sums of w
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // query (key) row tile of this wave; odd workgroups take the tiles in
+  // reverse so that two workgroups on a CU give each SIMD the same
+  // triangular intra-chunk work
+  const int rw = (blockIdx.x & 1) ? 3 - w : w;
   uint16_t* sDV = reinterpret_cast<uint16_t*>(sRow + 4 * T) + w * 2 * 16 * LD;  // this wave's dv, dk staging
   uint16_t* sDK = sDV + 16 * LD;
   const int64_t bh = blockIdx.x / P;
@@ -600,13 +612,13 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
                rg = make_rsrc(dy + hoff, hbytes), rdk = make_rsrc(dk + hoff, hbytes),
                rdv = make_rsrc(dv + hoff, hbytes), rl = make_rsrc(lg + bh * N, N * 4);
   float* qdqh = qdq + bh * N;
-  const int j = 16 * w + li;  // this lane's key row
+  const int j = 16 * rw + li;  // this lane's key row
   const int cc = 4 * (li % 4);
   f32x4_t mt[4];  // causal mask (query i = 16t + 4g + u >= key j) as 0 / 1
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) mt[t][u] = (t > w || (t == w && 4 * g + u >= li)) ? 1.f : 0.f;
+    for (int u = 0; u < 4; ++u) mt[t][u] = (t > rw || (t == rw && 4 * g + u >= li)) ? 1.f : 0.f;
 
   f32x4_t Racc[DT][NTL];
   init_x<DIM>(Racc, cr, w, g, li);
@@ -652,7 +664,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       f32x4_t a = {0.f, 0.f, 0.f, 0.f}, bb = {0.f, 0.f, 0.f, 0.f};
-      if (t >= w) {
+      if (t >= rw) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           a = mfma(lds8(sQ + (16 * t + li) * LD + 8 * g + 32 * s), kreg[s], a);
@@ -715,7 +727,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
       for (int u = 0; u < 4; ++u) kd += kv[u] * ok[u];
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp) {
-        if (2 * tp + 1 >= w) {
+        if (2 * tp + 1 >= rw) {
           const int ir = 32 * tp + 4 * g + li / 4;
           ov = mfma(cat(lds_tr(sG + ir * LD + 16 * n + cc), lds_tr(sG + (ir + 16) * LD + 16 * n + cc)),
                     cat(am[2 * tp], am[2 * tp + 1]), ov);
@@ -726,8 +738,8 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
       stage_piece<DIM>(sDV, pack4(ov), li, g, n);
       stage_piece<DIM>(sDK, pack4(ok), li, g, n);
     }
-    store_staged<DIM, DIM>(sDV, rdv, 16 * w, 0, soff);
-    store_staged<DIM, DIM>(sDK, rdk, 16 * w, 0, soff);
+    store_staged<DIM, DIM>(sDV, rdv, 16 * rw, 0, soff);
+    store_staged<DIM, DIM>(sDK, rdk, 16 * rw, 0, soff);
     kd = shfl_sum_groups(kd);
     // R for the previous chunk: exp(b_T) R + sum_i exp(b_i) q_i dy_i^T
     const float dT = __expf(bT);
