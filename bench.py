@@ -91,7 +91,11 @@ def hbm_ceilings():
     if not os.path.exists(CEILING_EXE):
         log(f"{CEILING_EXE} missing (build first): no practical ceilings")
         return None
-    r = subprocess.run([CEILING_EXE], capture_output=True, text=True, timeout=120)
+    try:
+        r = subprocess.run([CEILING_EXE], capture_output=True, text=True, timeout=120)
+    except (OSError, subprocess.TimeoutExpired) as e:
+        log(f"hbm_ceiling did not run: {e}")
+        return None
     if r.returncode != 0:
         log(f"hbm_ceiling failed ({r.returncode}): {r.stderr.strip()[-300:]}")
         return None
