@@ -66,14 +66,20 @@ __global__ __launch_bounds__(NT, 2) void k_poly_fwd(const bf16_t* __restrict__ q
       qf[qt][s] = __builtin_bit_cast(i16x8, bload16(rq, ((32 * w + 16 * qt + li) * DIM + 8 * g + 32 * s) * 2, qoff));
 
   f32x4_t o[QT][NTL];
-  float dacc[QT], racc[QT];  // sums of the fp32 and of the bf16-rounded weights
+  // sums of the fp32 weights (lane partials) and of the bf16-rounded ones
+  // (an MFMA against ones beside O^T: every row of rsum[qt] holds the sum
+  // for query li)
+  float dacc[QT];
+  f32x4_t rsum[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     dacc[qt] = 0.f;
-    racc[qt] = 0.f;
+    rsum[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int n = 0; n < NTL; ++n) o[qt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  const short one = 0x3f80;  // bf16 1.0
+  const i16x8 ones = {one, one, one, one, one, one, one, one};
 
   const int64_t kend = CAUSAL ? min(N, q0 + BQ) : N;
   const int nkb = static_cast<int>((kend + T - 1) / T);
@@ -107,17 +113,18 @@ __global__ __launch_bounds__(NT, 2) void k_poly_fwd(const bf16_t* __restrict__ q
 #pragma unroll
           for (int s = 0; s < KS; ++s) acc = mfma(ka[s], qf[qt][s], acc);
           const bool diag = CAUSAL && k0 + 16 * t + 15 > r0;
+          // key 16t + 4g + u of the block against query li of the tile, in
+          // 32 bits relative to the (wave-uniform) row offset
+          const int rel = static_cast<int>(r0 - k0) - 16 * t;
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             float p = acc[u] * acc[u];
-            if (diag) p = (k0 + 16 * t + 4 * g + u <= r0 + li) ? p : 0.f;
+            if (diag) p = (4 * g + u - li <= rel) ? p : 0.f;
             acc[u] = p;
             dacc[qt] += p;
           }
         }
         pt[qt][t] = pack4(acc);
-        const f32x4_t pr = unpack4(pt[qt][t]);
-        racc[qt] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
       }
     }
     // O^T += V^T P^T
@@ -133,6 +140,11 @@ __global__ __launch_bounds__(NT, 2) void k_poly_fwd(const bf16_t* __restrict__ q
           if (!CAUSAL || k0 + 32 * tp <= r0 + 15) o[qt][n] = mfma(a, cat(pt[qt][2 * tp], pt[qt][2 * tp + 1]), o[qt][n]);
         }
       }
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const int64_t r0 = q0 + 32 * w + 16 * qt;
+        if (!CAUSAL || k0 + 32 * tp <= r0 + 15) rsum[qt] = mfma(ones, cat(pt[qt][2 * tp], pt[qt][2 * tp + 1]), rsum[qt]);
+      }
     }
     __syncthreads();
   }
@@ -141,7 +153,7 @@ __global__ __launch_bounds__(NT, 2) void k_poly_fwd(const bf16_t* __restrict__ q
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float d = shfl_sum_groups(dacc[qt]);
-    const float dr = shfl_sum_groups(racc[qt]);
+    const float dr = rsum[qt][0];
     const float inv = dr > 0.f ? 1.f / dr : 0.f;
     const int row = 32 * w + 16 * qt + li;
 #pragma unroll
