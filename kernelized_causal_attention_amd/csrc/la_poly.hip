@@ -276,10 +276,11 @@ __global__ __launch_bounds__(NT, 2) void k_poly_dq(const bf16_t* __restrict__ q,
             dp = mfma(va[s], gf[qt][s], dp);
           }
           const bool diag = CAUSAL && k0 + 16 * t + 15 > r0;
+          const int rel = static_cast<int>(r0 - k0) - 16 * t;  // 32-bit mask test, as in k_poly_fwd
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             float x = 2.f * sc[u] * (dp[u] + cq[qt]);
-            if (diag) x = (k0 + 16 * t + 4 * g + u <= r0 + li) ? x : 0.f;
+            if (diag) x = (4 * g + u - li <= rel) ? x : 0.f;
             sc[u] = x;
           }
         }
@@ -406,11 +407,14 @@ __global__ __launch_bounds__(NT, 2) void k_poly_dkdv(const bf16_t* __restrict__ 
             dp = mfma(ga[s], vf[kt][s], dp);
           }
           const bool diag = CAUSAL && i0 + 16 * t < j0 + 15;
+          // query 16t + 4g + u of the block against key li of the tile, in
+          // 32 bits relative to the (wave-uniform) offset
+          const int rel = static_cast<int>(j0 - i0) - 16 * t;
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             float pw = sc[u] * sc[u];
             float x = 2.f * sc[u] * (dp[u] + cv[u]);
-            if (diag && i0 + 16 * t + 4 * g + u < j0 + li) {
+            if (diag && 4 * g + u - li < rel) {
               pw = 0.f;
               x = 0.f;
             }
