@@ -116,10 +116,14 @@ __global__ __launch_bounds__(NT, 2) void k_sm_fwd(const bf16_t* __restrict__ q, 
           for (int s = 0; s < KS; ++s) x = mfma(ka[s], qf[qt][s], x);
           const bool diag = CAUSAL && k0 + 16 * t + 15 > r0;
           const bool tail = !CAUSAL && k0 + 16 * t + 15 >= N;
+          // key 16t + 4g + u of the block, tested in 32 bits against the
+          // (wave-uniform) query offset and the keys left in the head
+          const int rd = static_cast<int>(r0 - k0);
+          const int rn = static_cast<int>(min(N - k0, static_cast<int64_t>(1) << 30));
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const int64_t j = k0 + 16 * t + 4 * g + u;
-            const bool keep = (!diag || j <= r0 + li) && (!tail || j < N);
+            const int jr = 16 * t + 4 * g + u;
+            const bool keep = (!diag || jr <= rd + li) && (!tail || jr < rn);
             acc[u] = keep ? x[u] : kNegInf;
           }
         }
