@@ -55,9 +55,11 @@ hipError_t launch_seg_state_f32mfma(const SegGeom& g, const void* k, const void*
 hipError_t launch_bwd_dq_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
                               const void* dout, const float* carry_s, void* dq, float* r_agg, float* c_out,
                               float* den_out, hipStream_t st);
+// carry_raw: carry_r holds the raw suffix aggregates (summed in the kernel)
+// rather than their reverse exclusive scan.
 hipError_t launch_bwd_dkdv_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
                                 const void* dout, const float* den, const float* c, const float* carry_r,
-                                void* dk, void* dv, hipStream_t st);
+                                void* dk, void* dv, hipStream_t st, int carry_raw = 0);
 }  // namespace la
 
 namespace {
@@ -456,6 +458,10 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
   if (causal) {
     const float* carry = nullptr;
     if (p.P > 1) {
+      // (summing the carry from the raw aggregates inside the forward kernel,
+      // as the dk/dv sweep does, measured slower here: the forward must also
+      // write the prefix records for the backward, and that prologue cost
+      // more than the scan launch)
       float* agg = sv ? sv : at(workspace, w.aggS);
       if ((e = seg_state(dtype, p, g, k, v, agg, stream))) return dev(e, "segment state");
       if ((e = scan(agg, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream)))
@@ -577,8 +583,13 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
   }
   if (e) return dev(e, "backward dq");
   const float* carry_r = nullptr;
+  int carry_raw = 0;
   if (causal) {
-    if (p.P > 1 || st.S_out) {
+    if (p.kernel == LA_KERNEL_MFMA && p.P > 1 && !st.S_out) {
+      // the MFMA dk/dv sweep sums its suffix carry from the raw aggregates
+      carry_r = aggR;
+      carry_raw = 1;
+    } else if (p.P > 1 || st.S_out) {
       if ((e = scan(aggR, BH, p.P, g.D, g.M, 1, st.S_out, D * M, st.Z_out, D, stream)))
         return dev(e, "suffix scan");
       if (p.P > 1) carry_r = aggR;
@@ -590,7 +601,10 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
   }
   if (p.kernel == LA_KERNEL_MFMA) {
     e = timed("mfma.bwd_dkdv", stream,
-              [&] { return la::launch_bwd_dkdv_mfma(causal, g, q, k, v, dout, den, cw, carry_r, dk, dv, stream); });
+              [&] {
+                return la::launch_bwd_dkdv_mfma(causal, g, q, k, v, dout, den, cw, carry_r, dk, dv, stream,
+                                                carry_raw);
+              });
   } else {
     la::SegGeom gk = g;
     gk.chunk = std::min(p.chunk, la::generic_chunk_for(g.D, g.M, 3));

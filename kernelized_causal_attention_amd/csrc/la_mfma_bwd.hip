@@ -70,6 +70,38 @@ __device__ __forceinline__ void init_xt(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL
   }
 }
 
+// The suffix state entering segment `seg` (of P) from the later segments'
+// aggregate records recs[P - 1], recs[P - 2], ..., recs[seg + 1] -- summed in
+// that order from zero, as the reverse exclusive scan of the records forms
+// it -- in the layout of init_xt.
+template <int DIM>
+__device__ __forceinline__ void init_xt_suffix(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&x)[Geo<DIM>::DT],
+                                               const float* __restrict__ recs, int seg, int P, int w, int g,
+                                               int li) {
+  using G = Geo<DIM>;
+  constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;
+#pragma unroll
+  for (int a = 0; a < G::DT; ++a) {
+    x[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < G::NTL; ++n) X[a][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int p = P - 1; p > seg; --p) {
+    const float* rec = recs + p * E;
+#pragma unroll
+    for (int a = 0; a < G::DT; ++a) {
+      const int mt = w * G::DT + a;
+#pragma unroll
+      for (int n = 0; n < G::NTL; ++n)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) X[a][n][u] += rec[(16 * n + li) * DIM + 16 * mt + 4 * g + u];
+      const float z = rec[DIM * DIM + 16 * mt + li];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[a][u] += z;
+    }
+  }
+}
+
 // bf16 row-major copy X[d][m] and fp32 vector x[d] into LDS.
 template <int DIM>
 __device__ __forceinline__ void write_xt(uint16_t* sX, float* sx, const f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL],
@@ -636,7 +668,8 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
                                                       const float* __restrict__ den_in,
                                                       const float* __restrict__ c_in,
                                                       const float* __restrict__ carry_r, bf16_t* __restrict__ dk,
-                                                      bf16_t* __restrict__ dv, int64_t N, int P, int seg_len) {
+                                                      bf16_t* __restrict__ dv, int64_t N, int P, int seg_len,
+                                                      int carry_raw) {
   using G = Geo<DIM>;
   constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -683,7 +716,12 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
     for (int u = 0; u < 4; ++u) mt[t][u] = (t > rw || (t == rw && 4 * g + u >= li)) ? 1.f : 0.f;
 
   f32x4_t Racc[DT][NTL], racc[DT];
-  init_xt<DIM>(Racc, racc, cr, w, g, li);
+  if (CAUSAL && carry_raw && carry_r)
+    // carry_r holds the raw suffix aggregates: the carry is summed here (no
+    // separate scan launch)
+    init_xt_suffix<DIM>(Racc, racc, carry_r + bh * P * E, seg, P, w, g, li);
+  else
+    init_xt<DIM>(Racc, racc, cr, w, g, li);
   write_xt<DIM>(sR, sRv, Racc, racc, w, g, li);
 
   const int64_t nch = (r1 - r0 + T - 1) / T;
@@ -848,12 +886,12 @@ hipError_t launch_bwd_dq_mfma(int causal, const SegGeom& g, const void* q, const
 
 hipError_t launch_bwd_dkdv_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
                                 const void* dout, const float* den, const float* c, const float* carry_r,
-                                void* dk, void* dv, hipStream_t st) {
+                                void* dk, void* dv, hipStream_t st, int carry_raw) {
   const int64_t grid = g.BH * g.P;
 #define LA_KV(D, C)                                                                                          \
   LA_MLAUNCH((k_bwd_dkdv_mfma<D, C>), grid, lds_bwd(D), st, static_cast<const bf16_t*>(q),                  \
              static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), \
-             den, c, carry_r, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), g.N, g.P, g.seg_len)
+             den, c, carry_r, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), g.N, g.P, g.seg_len, carry_raw)
   if (g.D == 64) {
     if (causal) LA_KV(64, true);
     LA_KV(64, false);
