@@ -48,9 +48,11 @@ constexpr int T = kT;
 template <int DIM>
 constexpr int kFwdWaves = DIM == 128 ? 8 : 4;
 
-// S (fp32 accumulators) -> S^T bf16 in LDS, Z -> LDS.
+// S (fp32 accumulators) -> S^T bf16 in LDS; Z -> LDS as a bf16 pair
+// (hi at sZ[d], the rounding remainder lo at sZ[DIM + d]), the operand of the
+// denominator's MFMA.
 template <int DIM, int NW>
-__device__ __forceinline__ void write_state(uint16_t* sST, float* sZ,
+__device__ __forceinline__ void write_state(uint16_t* sST, uint16_t* sZ,
                                             const f32x4_t (&Sacc)[(Geo<DIM, NW>::DT)][(Geo<DIM, NW>::NTL)],
                                             const f32x4_t (&zacc)[(Geo<DIM, NW>::DT)], int w, int g, int li) {
   using G = Geo<DIM, NW>;
@@ -62,7 +64,11 @@ __device__ __forceinline__ void write_state(uint16_t* sST, float* sZ,
       *reinterpret_cast<i16x4*>(sST + (16 * n + li) * G::LD + d0 + 4 * g) = pack4(Sacc[dt][n]);
     if (li == 0) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) sZ[d0 + 4 * g + u] = zacc[dt][u];
+      for (int u = 0; u < 4; ++u) {
+        const short hi = bf(zacc[dt][u]);
+        sZ[d0 + 4 * g + u] = static_cast<uint16_t>(hi);
+        sZ[DIM + d0 + 4 * g + u] = static_cast<uint16_t>(bf(zacc[dt][u] - fb(hi)));
+      }
     }
   }
 }
@@ -126,11 +132,11 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_
   uint16_t* sKf = smem;
   uint16_t* sV = sKf + T * LD;
   uint16_t* sST = sV + T * LD;
-  float* sZ = reinterpret_cast<float*>(sST + DIM * LD);
+  uint16_t* sZ = sST + DIM * LD;  // Z as bf16 hi [DIM], lo [DIM]
   // With two waves per query tile, phi(Q) is staged once in LDS rather than
   // computed by both waves of a pair from their own loads.
   constexpr bool kQInLds = NCG > 1;
-  uint16_t* sQf = reinterpret_cast<uint16_t*>(sZ + DIM);
+  uint16_t* sQf = sZ + 2 * DIM;
   // per-wave output staging: 16 rows x NTW * 16 columns
   constexpr int OC = NTW * 16;
   uint16_t* sOut = sQf + (kQInLds ? T * LD : 0);
@@ -237,15 +243,16 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_
       }
       rs = shfl_sum_groups(rs);
     }
-    // inter-chunk denominator phi(Q_i)^T Z (fp32)
-    float di = 0.f;
+    // inter-chunk denominator phi(Q_i)^T Z on the MFMA: every row of the A
+    // operand is Z (as its bf16 hi and lo parts, ~16 significant bits), so
+    // each row of the result holds the dot product for query li
+    f32x4_t dz = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const float* zp = sZ + 8 * g + 32 * s;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) di += fb(qf[s][e]) * zp[e];
+      dz = mfma(lds8(sZ + 8 * g + 32 * s), qf[s], dz);
+      dz = mfma(lds8(sZ + DIM + 8 * g + 32 * s), qf[s], dz);
     }
-    di = shfl_sum_groups(di);
+    const float di = dz[0];
     const float den = rs + di;
 
     // O^T = S^T phi(Q)^T (+ V^T A^T), this wave's output tiles
