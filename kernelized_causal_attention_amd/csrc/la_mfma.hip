@@ -162,6 +162,8 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_
   const rsrc_t ro = make_rsrc(out ? out + bh * N * DIM : nullptr, out ? N * DIM * 2 : 0);
   float* dh = den_out ? den_out + bh * N : nullptr;
   const int i = 16 * rt + li;  // this lane's query row within the chunk
+  const short one = 0x3f80;  // bf16 1.0
+  const i16x8 ones = {one, one, one, one, one, one, one, one};
   uint16_t* sO = sOut + w * 16 * (OC + kLdsPad);
 
   f32x4_t Sacc[DT][NTL];
@@ -218,7 +220,6 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_
     // lose most of that spread; each score is carried as hi + lo, two bf16
     // values whose sum keeps ~16 significant bits, and both enter the MFMA.
     i16x4 ahi[4], alo[4];
-    float rs = 0.f;
     if (CAUSAL) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -234,26 +235,21 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_
               if (4 * g + u > li) acc[u] = 0.f;
           }
           ahi[t] = pack4(acc);
-          const f32x4_t h = unpack4(ahi[t]);
-          alo[t] = pack4(acc - h);
-          const f32x4_t lo = unpack4(alo[t]);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) rs += h[u] + lo[u];
+          alo[t] = pack4(acc - unpack4(ahi[t]));
         }
       }
-      rs = shfl_sum_groups(rs);
     }
-    // inter-chunk denominator phi(Q_i)^T Z on the MFMA: every row of the A
-    // operand is Z (as its bf16 hi and lo parts, ~16 significant bits), so
-    // each row of the result holds the dot product for query li
+    // The denominator on the MFMA: the inter-chunk part phi(Q_i)^T Z with
+    // every row of the A operand equal to Z (as its bf16 hi and lo parts, ~16
+    // significant bits), and below the intra-chunk part, the sum of the same
+    // hi + lo scores the numerator uses, against a ones operand.  Every row
+    // of dz ends up holding den for query li.
     f32x4_t dz = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       dz = mfma(lds8(sZ + 8 * g + 32 * s), qf[s], dz);
       dz = mfma(lds8(sZ + DIM + 8 * g + 32 * s), qf[s], dz);
     }
-    const float di = dz[0];
-    const float den = rs + di;
 
     // O^T = S^T phi(Q)^T (+ V^T A^T), this wave's output tiles
     f32x4_t o[NTW];
@@ -269,6 +265,8 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_
         if (2 * tp <= rt) {
           const i16x8 bhi = cat(ahi[2 * tp], ahi[2 * tp + 1]);
           const i16x8 blo = cat(alo[2 * tp], alo[2 * tp + 1]);
+          dz = mfma(ones, bhi, dz);
+          dz = mfma(ones, blo, dz);
           const int jr = 32 * tp + 4 * g + li / 4;
           const int cc = 4 * (li % 4);
 #pragma unroll
@@ -281,6 +279,7 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_
         }
       }
     }
+    const float den = dz[0];
     if (out) {
       // rows past the head's end (den may be 0 there) are dropped by the
       // store's range check
