@@ -47,6 +47,14 @@ __device__ __forceinline__ float gate(rsrc_t rl, int l, int64_t cc0) {
   return x < -80.f ? -80.f : x;
 }
 
+// The kernels keep a chunk's running log decay in base-2 units
+// (b = sum of log2 gamma = sum of log gamma / ln 2), so that every decay
+// factor is a single hardware 2^x; sums handed to other passes (Lambda) are
+// converted back to natural log.
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kLn2 = 0.693147180559945309f;
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Registers -> LDS with each row scaled: row j of the tile times f(j), where
 // the staging thread gets b_j from its own wave's scan (lanes hold b_0..b_63).
 template <int DIM>
@@ -57,12 +65,12 @@ __device__ __forceinline__ void store_tile_scaled(uint16_t* lds, const i32x4 (&r
   for (int r = 0; r < G::PC; ++r) {
     const int p = threadIdx.x + NT * r;
     const int j = p / G::ROW8, c8 = p % G::ROW8;
-    const float s = __expf(bT - __shfl(b, j, 64));
+    const float s = ex2(bT - __shfl(b, j, 64));
     *reinterpret_cast<i16x8*>(lds + j * G::LD + c8 * 8) = pack8(unpack8(__builtin_bit_cast(i16x8, raw[r])) * s);
   }
 }
 
-// Registers -> LDS with row j times exp(b_j) (<= 1).
+// Registers -> LDS with row j times 2^(b_j) (<= 1).
 template <int DIM>
 __device__ __forceinline__ void store_tile_decay(uint16_t* lds, const i32x4 (&raw)[Geo<DIM>::PC], float b) {
   using G = Geo<DIM>;
@@ -70,7 +78,7 @@ __device__ __forceinline__ void store_tile_decay(uint16_t* lds, const i32x4 (&ra
   for (int r = 0; r < G::PC; ++r) {
     const int p = threadIdx.x + NT * r;
     const int j = p / G::ROW8, c8 = p % G::ROW8;
-    const float s = __expf(__shfl(b, j, 64));
+    const float s = ex2(__shfl(b, j, 64));
     *reinterpret_cast<i16x8*>(lds + j * G::LD + c8 * 8) = pack8(unpack8(__builtin_bit_cast(i16x8, raw[r])) * s);
   }
 }
@@ -104,13 +112,13 @@ __device__ __forceinline__ void init_s(f32x4_t (&Sacc)[Geo<DIM>::DT][Geo<DIM>::N
     }
 }
 
-// S <- exp(bT) S + Ks^T V  (Ks: the chunk's keys already scaled by
-// exp(bT - b_j)).
+// S <- 2^(bT) S + Ks^T V  (Ks: the chunk's keys already scaled by
+// 2^(bT - b_j)).
 template <int DIM>
 __device__ __forceinline__ void decay_update(f32x4_t (&Sacc)[Geo<DIM>::DT][Geo<DIM>::NTL], float bT,
                                              const uint16_t* sKs, const uint16_t* sV, int w, int g, int li) {
   using G = Geo<DIM>;
-  const float dk = __expf(bT);
+  const float dk = ex2(bT);
 #pragma unroll
   for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
@@ -158,6 +166,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_fwd_mfma(const bf
   // triangular intra-chunk work
   const int rw = (blockIdx.x & 1) ? 3 - w : w;
   uint16_t* sOut = sST + DIM * LD + w * 16 * LD;  // this wave's output staging tile
+  float* sB = reinterpret_cast<float*>(sST + DIM * LD + 4 * 16 * LD) + 64 * w;  // this wave's copy of b
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
@@ -169,12 +178,6 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_fwd_mfma(const bf
   const rsrc_t rq = make_rsrc(q + hoff, hbytes), rk = make_rsrc(k + hoff, hbytes), rv = make_rsrc(v + hoff, hbytes),
                ry = make_rsrc(y + hoff, hbytes), rl = make_rsrc(lg + bh * N, N * 4);
   const int i = 16 * rw + li;
-  // causal mask of key j = 16t + 4g + u against query i, as 0 / 1 factors
-  f32x4_t mt[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) mt[t][u] = (t < rw || (t == rw && 4 * g + u <= li)) ? 1.f : 0.f;
 
   f32x4_t Sacc[DT][NTL];
   init_s<DIM>(Sacc, cs, w, g, li);
@@ -192,8 +195,9 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_fwd_mfma(const bf
   };
   fetch(r0);
   for (int64_t c0 = r0; c0 < r1; c0 += T) {
-    const float b = wave_incl_scan(lgv);  // lane l: b_l
+    const float b = wave_incl_scan(lgv * kLog2e);  // lane l: b_l
     const float bT = __shfl(b, 63, 64);
+    sB[l] = b;
     store_tile_v<DIM>(sK, kraw);
     store_tile_v<DIM>(sV, vraw);
     store_tile_scaled<DIM>(sKs, kraw, b, bT);
@@ -205,7 +209,9 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_fwd_mfma(const bf
     if (c0 + T < r1) fetch(c0 + T);
 
     const float bi = __shfl(b, i, 64);
-    // scores A^T[j][i] = (k_j . q_i) exp(b_i - b_j), key tiles t <= w, masked
+    // scores A^T[j][i] = (k_j . q_i) 2^(b_i - b_j) over key tiles t <= rw;
+    // below the diagonal tile every key precedes the query (b_i - b_j <= 0),
+    // on it keys j > i are selected away (their 2^x may be +inf)
     i16x4 at[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -214,13 +220,19 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_fwd_mfma(const bf
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) acc = mfma(lds8(sK + (16 * t + li) * LD + 8 * g + 32 * s), qf[s], acc);
+        const f32x4_t bj = *reinterpret_cast<const f32x4_t*>(sB + 16 * t + 4 * g);
+        if (t < rw) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u] *= __expf(fminf(bi - __shfl(b, 16 * t + 4 * g + u, 64), 0.f)) * mt[t][u];
+          for (int u = 0; u < 4; ++u) acc[u] *= ex2(bi - bj[u]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[u] = 4 * g + u <= li ? acc[u] * ex2(bi - bj[u]) : 0.f;
+        }
         at[t] = pack4(acc);
       }
     }
-    // Y^T = exp(b_i) S^T q_i + V^T A^T
-    const float di = __expf(bi);
+    // Y^T = 2^(b_i) S^T q_i + V^T A^T
+    const float di = ex2(bi);
     f32x4_t o[NTL];
 #pragma unroll
     for (int n = 0; n < NTL; ++n) {
@@ -284,7 +296,7 @@ __global__ __launch_bounds__(NT, 2) void k_ret_seg_state(const bf16_t* __restric
   };
   fetch(r0);
   for (int64_t c0 = r0; c0 < r1; c0 += T) {
-    const float b = wave_incl_scan(lgv);
+    const float b = wave_incl_scan(lgv * kLog2e);
     const float bT = __shfl(b, 63, 64);
     lam += bT;
     store_tile_v<DIM>(sV, vraw);
@@ -304,7 +316,7 @@ __global__ __launch_bounds__(NT, 2) void k_ret_seg_state(const bf16_t* __restric
 #pragma unroll
       for (int n = 0; n < NTL; ++n) rec[d * DIM + 16 * n + li] = Sacc[dt][n][u];
     }
-  if (tid == 0) rec[DIM * DIM] = lam;
+  if (tid == 0) rec[DIM * DIM] = lam * kLn2;
 }
 
 // Decayed exclusive scan over segments, in place on the S part of the
@@ -439,6 +451,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
   // triangular intra-chunk work
   const int rw = (blockIdx.x & 1) ? 3 - w : w;
   uint16_t* sOut = sS + DIM * LD + w * 16 * LD;  // this wave's output staging tile
+  float* sB = reinterpret_cast<float*>(sS + DIM * LD + 4 * 16 * LD) + 64 * w;  // this wave's copy of b
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
@@ -453,11 +466,6 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
   float* qdqh = qdq + bh * N;
   const int i = 16 * rw + li;
   const int cc = 4 * (li % 4);
-  f32x4_t mt[4];  // causal mask (key j = 16t + 4g + u <= query i) as 0 / 1
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) mt[t][u] = (t < rw || (t == rw && 4 * g + u <= li)) ? 1.f : 0.f;
 
   f32x4_t Sacc[DT][NTL], Racc[DT][NTL];
   init_s<DIM>(Sacc, cs, w, g, li);
@@ -486,16 +494,17 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
     lgv = gate(rl, l, cc0);
   };
   fetch(r0);
-  float Bc = 0.f;  // log decay from the segment start to before this chunk
+  float Bc = 0.f;  // log2 decay from the segment start to before this chunk
   for (int64_t c0 = r0; c0 < r1; c0 += T) {
-    const float b = wave_incl_scan(lgv);
+    const float b = wave_incl_scan(lgv * kLog2e);
     const float bT = __shfl(b, 63, 64);
     const float bi = __shfl(b, i, 64);
+    sB[l] = b;
     store_tile_v<DIM>(sK, kraw);
     store_tile_scaled<DIM>(sKs, kraw, b, bT);
     store_tile_v<DIM>(sV, vraw);
     put_row<DIM>(sQ, qraw, i, g, 1.f);
-    put_row<DIM>(sQs, qraw, i, g, __expf(Bc + bi));
+    put_row<DIM>(sQs, qraw, i, g, ex2(Bc + bi));
     put_row<DIM>(sG, graw, i, g, 1.f);
     i16x8 gq[KS];
 #pragma unroll
@@ -505,9 +514,9 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
     const int64_t nrow = min(static_cast<int64_t>(T), r1 - c0);
     if (c0 + T < r1) fetch(c0 + T);
 
-    // dQ^T[d][i] = exp(b_i) (S dy_i)[d] + sum_j K^T B^T
+    // dQ^T[d][i] = 2^(b_i) (S dy_i)[d] + sum_j K^T B^T
     f32x4_t o[NTL];
-    const float di = __expf(bi);
+    const float di = ex2(bi);
 #pragma unroll
     for (int n = 0; n < NTL; ++n) {
       o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -515,7 +524,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
       for (int s = 0; s < KS; ++s) o[n] = mfma(lds8(sS + (16 * n + li) * LD + 8 * g + 32 * s), gq[s], o[n]);
       o[n] *= di;
     }
-    // p_i = q_i . exp(b_i) S dy_i (fp32)
+    // p_i = q_i . 2^(b_i) S dy_i (fp32)
     float qd = 0.f;
 #pragma unroll
     for (int n = 0; n < NTL; ++n) {
@@ -524,7 +533,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
       for (int u = 0; u < 4; ++u) qd += qv[u] * o[n][u];
     }
     qd = shfl_sum_groups(qd);
-    // B^T[j][i] = (v_j . dy_i) exp(b_i - b_j), masked j <= i
+    // B^T[j][i] = (v_j . dy_i) 2^(b_i - b_j), j <= i (as in the forward)
     i16x4 bt[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -532,8 +541,14 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
       if (t <= rw) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) acc = mfma(lds8(sV + (16 * t + li) * LD + 8 * g + 32 * s), gq[s], acc);
+        const f32x4_t bj = *reinterpret_cast<const f32x4_t*>(sB + 16 * t + 4 * g);
+        if (t < rw) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u] *= __expf(fminf(bi - __shfl(b, 16 * t + 4 * g + u, 64), 0.f)) * mt[t][u];
+          for (int u = 0; u < 4; ++u) acc[u] *= ex2(bi - bj[u]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[u] = 4 * g + u <= li ? acc[u] * ex2(bi - bj[u]) : 0.f;
+        }
       }
       bt[t] = pack4(acc);
     }
@@ -567,7 +582,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
       for (int n = 0; n < NTL; ++n)
 #pragma unroll
         for (int u = 0; u < 4; ++u) rec[(16 * n + li) * DIM + 16 * (w * DT + a) + 4 * g + u] = Racc[a][n][u];
-    if (tid == 0) rec[DIM * DIM] = Bc;
+    if (tid == 0) rec[DIM * DIM] = Bc * kLn2;
   }
 }
 
@@ -600,6 +615,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
   const int rw = (blockIdx.x & 1) ? 3 - w : w;
   uint16_t* sDV = reinterpret_cast<uint16_t*>(sRow + 4 * T) + w * 2 * 16 * LD;  // this wave's dv, dk staging
   uint16_t* sDK = sDV + 16 * LD;
+  float* sB = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(sRow + 4 * T) + 4 * 2 * 16 * LD) + 64 * w;
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
@@ -614,11 +630,6 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
   float* qdqh = qdq + bh * N;
   const int j = 16 * rw + li;  // this lane's key row
   const int cc = 4 * (li % 4);
-  f32x4_t mt[4];  // causal mask (query i = 16t + 4g + u >= key j) as 0 / 1
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) mt[t][u] = (t > rw || (t == rw && 4 * g + u >= li)) ? 1.f : 0.f;
 
   f32x4_t Racc[DT][NTL];
   init_x<DIM>(Racc, cr, w, g, li);
@@ -638,12 +649,13 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
   fetch(r0 + (nch - 1) * T);
   for (int64_t ci = nch - 1; ci >= 0; --ci) {
     const int64_t c0 = r0 + ci * T;
-    const float b = wave_incl_scan(lgv);
+    const float b = wave_incl_scan(lgv * kLog2e);
     const float bT = __shfl(b, 63, 64);
+    sB[l] = b;
     store_tile_v<DIM>(sK, kraw);
     store_tile_v<DIM>(sV, vraw);
     store_tile_v<DIM>(sQ, qraw);
-    store_tile_decay<DIM>(sQs, qraw, b);  // row i times exp(b_i)
+    store_tile_decay<DIM>(sQs, qraw, b);  // row i times 2^(b_i)
     store_tile_v<DIM>(sG, graw);
     __syncthreads();
     const int soff = static_cast<int>(c0 * DIM * 2);
@@ -657,8 +669,10 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
       kreg[s] = lds8(sK + j * LD + 8 * g + 32 * s);
       vreg[s] = lds8(sV + j * LD + 8 * g + 32 * s);
     }
-    // A[i][j] = (q_i . k_j) exp(b_i - b_j), Bm[i][j] = (dy_i . v_j) exp(b_i - b_j),
-    // query tiles t >= w, masked i >= j; wv: the pair terms w_ij in fp32
+    // A[i][j] = (q_i . k_j) 2^(b_i - b_j), Bm[i][j] = (dy_i . v_j) 2^(b_i - b_j),
+    // query tiles t >= rw; above the diagonal tile every query follows the
+    // key, on it queries i < j are selected away; wv: the pair terms w_ij in
+    // fp32
     i16x4 am[4], bm[4];
     float wv[16];
 #pragma unroll
@@ -670,11 +684,13 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
           a = mfma(lds8(sQ + (16 * t + li) * LD + 8 * g + 32 * s), kreg[s], a);
           bb = mfma(lds8(sG + (16 * t + li) * LD + 8 * g + 32 * s), vreg[s], bb);
         }
+        const f32x4_t bq = *reinterpret_cast<const f32x4_t*>(sB + 16 * t + 4 * g);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float dec = __expf(fminf(__shfl(b, 16 * t + 4 * g + u, 64) - bj, 0.f)) * mt[t][u];
-          wv[4 * t + u] = a[u] * bb[u] * dec;
+          float dec = ex2(bq[u] - bj);
+          if (t == rw) dec = 4 * g + u >= li ? dec : 0.f;
           a[u] *= dec;
+          wv[4 * t + u] = a[u] * bb[u];
           bb[u] *= dec;
         }
       } else {
@@ -704,11 +720,11 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
       const float h1 = (b0 ? h2[1] : h2[0]) + __shfl_xor(b0 ? h2[0] : h2[1], 1, 64);
       sRow[w * T + 16 * (li >> 2) + 4 * g + (li & 3)] = h1;
     }
-    const float dj = __expf(bT - bj);
+    const float dj = ex2(bT - bj);
     float kd = 0.f;
 #pragma unroll
     for (int n = 0; n < NTL; ++n) {
-      // dv^T[m][j] = exp(b_T - b_j) R^T k_j + sum_i dy^T A
+      // dv^T[m][j] = 2^(b_T - b_j) R^T k_j + sum_i dy^T A
       f32x4_t ov = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -716,12 +732,12 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
         ov = mfma(cat(lds_tr(sR + dr * LD + 16 * n + cc), lds_tr(sR + (dr + 4) * LD + 16 * n + cc)), kreg[s], ov);
       }
       ov *= dj;
-      // dk^T[d][j] = exp(b_T - b_j) R v_j + sum_i q^T Bm
+      // dk^T[d][j] = 2^(b_T - b_j) R v_j + sum_i q^T Bm
       f32x4_t ok = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) ok = mfma(lds8(sR + (16 * n + li) * LD + 8 * g + 32 * s), vreg[s], ok);
       ok *= dj;
-      // r_j = k_j . exp(b_T - b_j) R v_j (fp32)
+      // r_j = k_j . 2^(b_T - b_j) R v_j (fp32)
       const f32x4_t kv = unpack4(*reinterpret_cast<const i16x4*>(sK + j * LD + 16 * n + 4 * g));
 #pragma unroll
       for (int u = 0; u < 4; ++u) kd += kv[u] * ok[u];
@@ -741,8 +757,8 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
     store_staged<DIM, DIM>(sDV, rdv, 16 * rw, 0, soff);
     store_staged<DIM, DIM>(sDK, rdk, 16 * rw, 0, soff);
     kd = shfl_sum_groups(kd);
-    // R for the previous chunk: exp(b_T) R + sum_i exp(b_i) q_i dy_i^T
-    const float dT = __expf(bT);
+    // R for the previous chunk: 2^(b_T) R + sum_i 2^(b_i) q_i dy_i^T
+    const float dT = ex2(bT);
 #pragma unroll
     for (int a = 0; a < DT; ++a)
 #pragma unroll
@@ -825,13 +841,20 @@ __global__ __launch_bounds__(NT) void k_ret_dlg(const float* __restrict__ a, con
   }
 }
 
-// each also holds a 16-row output staging tile per wave (two in the dk / dv sweep)
-size_t lds_ret_fwd(int dim) { return (3 * T * (dim + kLdsPad) + dim * (dim + kLdsPad) + 4 * 16 * (dim + kLdsPad)) * sizeof(uint16_t); }
+// each also holds a 16-row output staging tile per wave (two in the dk / dv
+// sweep) and each wave's 64-float copy of the chunk's b
+size_t lds_ret_fwd(int dim) {
+  return (3 * T * (dim + kLdsPad) + dim * (dim + kLdsPad) + 4 * 16 * (dim + kLdsPad)) * sizeof(uint16_t) +
+         4 * T * sizeof(float);
+}
 size_t lds_ret_seg(int dim) { return 2 * T * (dim + kLdsPad) * sizeof(uint16_t); }
-size_t lds_ret_dq(int dim) { return (6 * T * (dim + kLdsPad) + dim * (dim + kLdsPad) + 4 * 16 * (dim + kLdsPad)) * sizeof(uint16_t); }
+size_t lds_ret_dq(int dim) {
+  return (6 * T * (dim + kLdsPad) + dim * (dim + kLdsPad) + 4 * 16 * (dim + kLdsPad)) * sizeof(uint16_t) +
+         4 * T * sizeof(float);
+}
 size_t lds_ret_dkdv(int dim) {
   return (5 * T * (dim + kLdsPad) + dim * (dim + kLdsPad) + 4 * 2 * 16 * (dim + kLdsPad)) * sizeof(uint16_t) +
-         4 * T * sizeof(float);
+         2 * 4 * T * sizeof(float);
 }
 
 #define LA_RLAUNCH(kernel, grid, lds, st, ...)                                                               \
