@@ -142,7 +142,9 @@ __global__ __launch_bounds__(NT) void k_seg_scan(float* __restrict__ agg, int P,
   for (int p = 0; p < P; ++p) {
     const int s = reverse ? P - 1 - p : p;
     float* ptr = agg + (bh * P + s) * E + e;
-    const float x = *ptr;
+    // without a total the last record's aggregate is never needed (and may
+    // not have been computed): it is not read
+    const float x = (tot_s || p + 1 < P) ? *ptr : 0.f;
     *ptr = carry;
     carry += x;
   }

@@ -462,8 +462,13 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
       // as the dk/dv sweep does, measured slower here: the forward must also
       // write the prefix records for the backward, and that prologue cost
       // more than the scan launch)
+      // the last segment's aggregate would only feed the total, which is not
+      // asked for: the segment-state pass skips that segment, and the scan
+      // reads its (unset) record only into the discarded total
       float* agg = sv ? sv : at(workspace, w.aggS);
-      if ((e = seg_state(dtype, p, g, k, v, agg, stream))) return dev(e, "segment state");
+      la::SegGeom gs = g;
+      gs.nseg = p.P - 1;
+      if ((e = seg_state(dtype, p, gs, k, v, agg, stream))) return dev(e, "segment state");
       if ((e = scan(agg, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream)))
         return dev(e, "segment scan");
       carry = agg;

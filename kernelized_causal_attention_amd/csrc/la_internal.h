@@ -19,6 +19,10 @@ struct SegGeom {
   int P;        // segments per sequence
   int seg_len;  // tokens per segment (a multiple of the chunk)
   int chunk;    // tokens per intra-chunk tile
+  // segment-state passes: aggregates of segments 0 .. nseg - 1 only (0: all
+  // P).  A causal forward that returns no final state never reads the last
+  // segment's aggregate (the exclusive scan only hands it to the total).
+  int nseg = 0;
 };
 
 // ---- generic kernels (any D, M with D*M <= 16384, fp32 or bf16 inputs) ----

@@ -308,7 +308,7 @@ template <int DIM>
 __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_seg_state_mfma(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                                        float* __restrict__ s_out, int64_t s_stride,
                                                        float* __restrict__ z_out, int64_t z_stride, int64_t N,
-                                                       int P, int seg_len) {
+                                                       int P, int nseg, int seg_len) {
   constexpr int NW = kFwdWaves<DIM>;
   using G = Geo<DIM, NW>;
   constexpr int LD = G::LD, NTL = G::NTL, PC = G::PC, DT = G::DT;
@@ -319,8 +319,8 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_seg_state_mfma(const
   // MFMA under an EXEC-masked branch still writes every lane.
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t bh = blockIdx.x / P;
-  const int seg = blockIdx.x % P;
+  const int64_t bh = blockIdx.x / nseg;
+  const int seg = blockIdx.x % nseg;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
   const int64_t r1 = min(N, r0 + seg_len);
   const int64_t hbytes = N * DIM * 2;
@@ -383,7 +383,8 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_seg_state_mfma(const
 __global__ __launch_bounds__(256, 2) void k_seg_state_wave64(const bf16_t* __restrict__ k,
                                                              const bf16_t* __restrict__ v, float* __restrict__ s_out,
                                                              int64_t s_stride, float* __restrict__ z_out,
-                                                             int64_t z_stride, int64_t N, int P, int seg_len) {
+                                                             int64_t z_stride, int64_t N, int P, int nseg,
+                                                             int seg_len) {
   constexpr int DIM = 64, LD = DIM + kLdsPad;
   constexpr int PW = T * DIM / 8 / 64;  // 16-byte pieces per lane per chunk tile
   constexpr int RP = DIM + 4;           // fp32 row stride of the partials in LDS
@@ -392,8 +393,8 @@ __global__ __launch_bounds__(256, 2) void k_seg_state_wave64(const bf16_t* __res
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint16_t* sK = smem + w * 2 * T * LD;
   uint16_t* sV = sK + T * LD;
-  const int64_t bh = blockIdx.x / P;
-  const int seg = blockIdx.x % P;
+  const int64_t bh = blockIdx.x / nseg;
+  const int seg = blockIdx.x % nseg;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
   const int64_t r1 = min(N, r0 + seg_len);
   const int64_t hbytes = N * DIM * 2;
@@ -546,15 +547,16 @@ hipError_t launch_forward_mfma(int causal, const SegGeom& g, const void* q, cons
 
 hipError_t launch_seg_state_mfma(const SegGeom& g, const void* k, const void* v, float* s_out, int64_t s_stride,
                                  float* z_out, int64_t z_stride, hipStream_t st) {
-  const int64_t grid = g.BH * g.P;
+  const int nseg = g.nseg > 0 ? g.nseg : g.P;
+  const int64_t grid = g.BH * nseg;
   const bf16_t* K = static_cast<const bf16_t*>(k);
   const bf16_t* V = static_cast<const bf16_t*>(v);
   if (g.D == 64)
     LA_MLAUNCH(k_seg_state_wave64, 256, grid, lds_seg_wave64(), st, K, V, s_out, s_stride, z_out, z_stride, g.N, g.P,
-               g.seg_len);
+               nseg, g.seg_len);
   if (g.D == 128)
     LA_MLAUNCH((k_seg_state_mfma<128>), 64 * kFwdWaves<128>, grid, lds_seg(128), st, K, V, s_out, s_stride, z_out, z_stride, g.N,
-               g.P, g.seg_len);
+               g.P, nseg, g.seg_len);
   return hipErrorNotSupported;
 }
 

@@ -235,7 +235,7 @@ template <int DIM>
 __global__ __launch_bounds__(NT, 2) void k_seg_state_f32mfma(const float* __restrict__ k, const float* __restrict__ v,
                                                              float* __restrict__ s_out, int64_t s_stride,
                                                              float* __restrict__ z_out, int64_t z_stride, int64_t N,
-                                                             int P, int seg_len) {
+                                                             int P, int nseg, int seg_len) {
   constexpr int LDD = DIM + 4;
   constexpr int RT = DIM / 64;     // 16-row state tiles per wave
   constexpr int CT = DIM / 16;     // 16-column state tiles
@@ -246,8 +246,8 @@ __global__ __launch_bounds__(NT, 2) void k_seg_state_f32mfma(const float* __rest
   float* sV = sKf + T * LDD;
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t bh = blockIdx.x / P;
-  const int seg = blockIdx.x % P;
+  const int64_t bh = blockIdx.x / nseg;
+  const int seg = blockIdx.x % nseg;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
   const int64_t r1 = min(N, r0 + seg_len);
   const float* kh = k + bh * N * DIM;
@@ -358,12 +358,13 @@ hipError_t launch_forward_f32mfma(int causal, const SegGeom& g, const void* q, c
 hipError_t launch_seg_state_f32mfma(const SegGeom& g, const void* k, const void* v, float* s_out, int64_t s_stride,
                                     float* z_out, int64_t z_stride, hipStream_t st) {
   if (g.D != g.M || (g.D != 64 && g.D != 128)) return hipErrorNotSupported;
-  const dim3 grid(static_cast<unsigned>(g.BH * g.P));
+  const int nseg = g.nseg > 0 ? g.nseg : g.P;
+  const dim3 grid(static_cast<unsigned>(g.BH * nseg));
   const float* K = static_cast<const float*>(k);
   const float* V = static_cast<const float*>(v);
   if (g.D == 64) {
     hipLaunchKernelGGL((k_seg_state_f32mfma<64>), grid, dim3(NT), lds_seg_f32(64), st, K, V, s_out, s_stride, z_out,
-                       z_stride, g.N, g.P, g.seg_len);
+                       z_stride, g.N, g.P, nseg, g.seg_len);
     return hipGetLastError();
   }
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_seg_state_f32mfma<128>),
@@ -371,7 +372,7 @@ hipError_t launch_seg_state_f32mfma(const SegGeom& g, const void* k, const void*
                                            static_cast<int>(lds_seg_f32(128)));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_seg_state_f32mfma<128>), grid, dim3(NT), lds_seg_f32(128), st, K, V, s_out, s_stride, z_out,
-                     z_stride, g.N, g.P, g.seg_len);
+                     z_stride, g.N, g.P, nseg, g.seg_len);
   return hipGetLastError();
 }
 
