@@ -208,7 +208,7 @@ la_status la_retention_forward(const void* q, const void* k, const void* v, cons
 
 /* Bytes of la_retention_forward's `saved` record for these sizes: the state
  * entering each segment of its plan ([B,H,segments] records of D*M + D
- * floats, S row-major, then the segment's summed log gamma), which
+ * floats: S row-major, then D floats the library uses internally), which
  * la_retention_backward reads instead of recomputing them.  `saved` is
  * 16-byte aligned, caller-owned, and must not overlap any other argument;
  * NULL keeps nothing.  0 for unsupported sizes. */

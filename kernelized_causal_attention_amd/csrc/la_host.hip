@@ -737,7 +737,10 @@ LA_API la_status la_retention_forward(const void* q, const void* k, const void* 
     // segment aggregates and their decayed scan from S0; the total is the
     // state after the N tokens; kept in `saved` when given
     float* recs = saved ? saved : at(workspace, w.aggS);
-    if ((e = timed("ret.seg_state", stream, [&] { return la::launch_ret_seg_state(g, k, v, log_gamma, recs, stream); })))
+    // without S_out the last segment's aggregate would only feed the total
+    la::SegGeom gs = g;
+    if (!S_out && p.P > 1) gs.nseg = p.P - 1;
+    if ((e = timed("ret.seg_state", stream, [&] { return la::launch_ret_seg_state(gs, k, v, log_gamma, recs, stream); })))
       return dev(e, "retention segment state");
     if ((e = timed("ret.scan", stream, [&] { return la::launch_ret_scan(recs, BH, p.P, g.D, g.M, S0, S_out, stream); })))
       return dev(e, "retention scan");

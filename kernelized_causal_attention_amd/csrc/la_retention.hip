@@ -269,7 +269,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_fwd_mfma(const bf
 template <int DIM>
 __global__ __launch_bounds__(NT, 2) void k_ret_seg_state(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                                          const float* __restrict__ lg, float* __restrict__ recs,
-                                                         int64_t N, int P, int seg_len) {
+                                                         int64_t N, int P, int nseg, int seg_len) {
   using G = Geo<DIM>;
   constexpr int LD = G::LD, NTL = G::NTL, PC = G::PC, DT = G::DT;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -277,8 +277,8 @@ __global__ __launch_bounds__(NT, 2) void k_ret_seg_state(const bf16_t* __restric
   uint16_t* sV = sKs + T * LD;
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t bh = blockIdx.x / P;
-  const int seg = blockIdx.x % P;
+  const int64_t bh = blockIdx.x / nseg;  // segments 0 .. nseg - 1 of each head
+  const int seg = blockIdx.x % nseg;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
   const int64_t r1 = min(N, r0 + seg_len);
   const int64_t hbytes = N * DIM * 2;
@@ -330,6 +330,12 @@ __global__ __launch_bounds__(NT) void k_ret_scan(float* __restrict__ recs, int P
   float carry = init ? init[bh * DM + e] : 0.f;
   for (int p = 0; p < P; ++p) {
     float* rec = recs + (bh * P + p) * E;
+    // without a total the last record's aggregate is never needed (and may
+    // not have been computed): it is not read
+    if (p + 1 == P && !tot) {
+      rec[e] = carry;
+      break;
+    }
     const float x = rec[e];
     const float lam = rec[DM];
     rec[e] = carry;
@@ -872,11 +878,13 @@ int retention_supported(int64_t D, int64_t M, int dtype) { return dtype == 1 && 
 
 hipError_t launch_ret_seg_state(const SegGeom& g, const void* k, const void* v, const float* lg, float* recs,
                                 hipStream_t st) {
-  const int64_t grid = g.BH * g.P;
+  const int nseg = g.nseg > 0 ? g.nseg : g.P;
+  const int64_t grid = g.BH * nseg;
   const bf16_t* K = static_cast<const bf16_t*>(k);
   const bf16_t* V = static_cast<const bf16_t*>(v);
-  if (g.D == 64) LA_RLAUNCH((k_ret_seg_state<64>), grid, lds_ret_seg(64), st, K, V, lg, recs, g.N, g.P, g.seg_len);
-  if (g.D == 128) LA_RLAUNCH((k_ret_seg_state<128>), grid, lds_ret_seg(128), st, K, V, lg, recs, g.N, g.P, g.seg_len);
+  if (g.D == 64) LA_RLAUNCH((k_ret_seg_state<64>), grid, lds_ret_seg(64), st, K, V, lg, recs, g.N, g.P, nseg, g.seg_len);
+  if (g.D == 128)
+    LA_RLAUNCH((k_ret_seg_state<128>), grid, lds_ret_seg(128), st, K, V, lg, recs, g.N, g.P, nseg, g.seg_len);
   return hipErrorNotSupported;
 }
 
