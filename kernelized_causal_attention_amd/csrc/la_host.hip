@@ -342,6 +342,14 @@ la::SegGeom geom(int64_t BH, int64_t N, int64_t D, int64_t M, const Plan& p, int
   return g;
 }
 
+// The geometry for a segment-state pass whose scan produces no total: the
+// last segment's aggregate would only feed that total, so it is skipped.
+la::SegGeom without_last(const la::SegGeom& g) {
+  la::SegGeom r = g;
+  if (g.P > 1) r.nseg = g.P - 1;
+  return r;
+}
+
 // Segment aggregates of (S, Z) into ws records [BH][P][E].
 hipError_t seg_state(int dtype, const Plan& p, const la::SegGeom& gbase, const void* k, const void* v,
                      float* recs, hipStream_t st) {
@@ -450,7 +458,7 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
     // every segment's carry-in (starting from S0, Z0) and the final state
     // come from the segment aggregates and their scan, as exact as fp32
     float* agg = sv ? sv : at(workspace, w.aggS);
-    if ((e = seg_state(dtype, p, g, k, v, agg, stream))) return dev(e, "segment state");
+    if ((e = seg_state(dtype, p, st.S_out ? g : without_last(g), k, v, agg, stream))) return dev(e, "segment state");
     if ((e = scan(agg, BH, p.P, g.D, g.M, 0, st.S_out, D * M, st.Z_out, D, stream, st.S0, st.Z0)))
       return dev(e, "segment scan");
     return dev(fwd_pass(dtype, 1, p, g, q, k, v, out, den_out, agg, stream), "forward");
@@ -466,9 +474,7 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
       // asked for: the segment-state pass skips that segment, and the scan
       // reads its (unset) record only into the discarded total
       float* agg = sv ? sv : at(workspace, w.aggS);
-      la::SegGeom gs = g;
-      gs.nseg = p.P - 1;
-      if ((e = seg_state(dtype, p, gs, k, v, agg, stream))) return dev(e, "segment state");
+      if ((e = seg_state(dtype, p, without_last(g), k, v, agg, stream))) return dev(e, "segment state");
       if ((e = scan(agg, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream)))
         return dev(e, "segment scan");
       carry = agg;
@@ -543,7 +549,7 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
   const float* carry_s = nullptr;
   if (st.on) {
     // carry-in from S0, Z0 through the segment scan (any number of segments)
-    if ((e = seg_state(dtype, p, g, k, v, aggS, stream))) return dev(e, "segment state");
+    if ((e = seg_state(dtype, p, without_last(g), k, v, aggS, stream))) return dev(e, "segment state");
     if ((e = scan(aggS, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream, st.S0, st.Z0)))
       return dev(e, "segment scan");
     carry_s = aggS;
@@ -551,7 +557,7 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
     carry_s = sv;  // the forward's scanned states (null: one causal segment)
   } else if (causal) {
     if (p.P > 1) {
-      if ((e = seg_state(dtype, p, g, k, v, aggS, stream))) return dev(e, "segment state");
+      if ((e = seg_state(dtype, p, without_last(g), k, v, aggS, stream))) return dev(e, "segment state");
       if ((e = scan(aggS, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream)))
         return dev(e, "segment scan");
       carry_s = aggS;
@@ -738,8 +744,7 @@ LA_API la_status la_retention_forward(const void* q, const void* k, const void* 
     // state after the N tokens; kept in `saved` when given
     float* recs = saved ? saved : at(workspace, w.aggS);
     // without S_out the last segment's aggregate would only feed the total
-    la::SegGeom gs = g;
-    if (!S_out && p.P > 1) gs.nseg = p.P - 1;
+    const la::SegGeom gs = S_out ? g : without_last(g);
     if ((e = timed("ret.seg_state", stream, [&] { return la::launch_ret_seg_state(gs, k, v, log_gamma, recs, stream); })))
       return dev(e, "retention segment state");
     if ((e = timed("ret.scan", stream, [&] { return la::launch_ret_scan(recs, BH, p.P, g.D, g.M, S0, S_out, stream); })))
@@ -798,7 +803,8 @@ LA_API la_status la_retention_backward(const void* q, const void* k, const void*
   const float* recs = saved;
   if (!saved) {
     float* r = at(workspace, w.aggS);
-    if ((e = timed("ret.seg_state", stream, [&] { return la::launch_ret_seg_state(g, k, v, log_gamma, r, stream); })))
+    const la::SegGeom gs = without_last(g);  // the scan below keeps no total
+    if ((e = timed("ret.seg_state", stream, [&] { return la::launch_ret_seg_state(gs, k, v, log_gamma, r, stream); })))
       return dev(e, "retention segment state");
     if ((e = timed("ret.scan", stream, [&] { return la::launch_ret_scan(r, BH, p.P, g.D, g.M, S0, nullptr, stream); })))
       return dev(e, "retention scan");
