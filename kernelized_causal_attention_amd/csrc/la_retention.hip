@@ -644,6 +644,9 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
   const int64_t nch = (r1 - r0 + T - 1) / T;
   i32x4 kraw[PC], vraw[PC], qraw[PC], graw[PC];
   float lgv;
+  // p_j from the forward sweep, loaded with the chunk's tiles so that the
+  // update of a_j at the end of the chunk waits on no load
+  float pj = 0.f;
   auto fetch = [&](int64_t cc0) {
     const int soff = static_cast<int>(cc0 * DIM * 2);
     bload_tile<DIM>(kraw, rk, soff);
@@ -651,6 +654,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
     bload_tile<DIM>(qraw, rq, soff);
     bload_tile<DIM>(graw, rg, soff);
     lgv = gate(rl, l, cc0);
+    if (g == 0 && cc0 + j < r1) pj = qdqh[cc0 + j];
   };
   fetch(r0 + (nch - 1) * T);
   for (int64_t ci = nch - 1; ci >= 0; --ci) {
@@ -666,6 +670,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
     __syncthreads();
     const int soff = static_cast<int>(c0 * DIM * 2);
     const int64_t nrow = min(static_cast<int64_t>(T), r1 - c0);
+    const float pcur = pj;
     if (ci > 0) fetch(c0 - T);
 
     const float bj = __shfl(b, j, 64);
@@ -774,7 +779,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
     write_x<DIM>(sR, Racc, w, g, li);
     if (g == 0 && j < nrow) {
       const float rowsum = sRow[j] + sRow[T + j] + sRow[2 * T + j] + sRow[3 * T + j];
-      qdqh[c0 + j] += rowsum - colsum - kd;
+      qdqh[c0 + j] = pcur + (rowsum - colsum - kd);
     }
   }
 }
