@@ -28,15 +28,30 @@ using namespace mf;
 constexpr int NT = kNT;
 constexpr int T = kT;
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// x moved across lanes by a DPP control (CTRL), into the rows of ROW_MASK;
+// lanes with no source, and rows outside the mask, receive 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS
+// round trips): shifts by 1, 2, 4, 8 within each 16-lane row, then row 0's
+// total into row 1 and row 2's into row 3 (row_bcast:15), then the total of
+// rows 0-1 into rows 2 and 3 (row_bcast:31).
 __device__ __forceinline__ float wave_incl_scan(float x) {
-  const int l = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(x, off, 64);
-    if (l >= off) x += y;
-  }
+  x += dpp_or_zero<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_or_zero<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_or_zero<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_or_zero<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_or_zero<0x142, 0xa>(x);  // row_bcast:15
+  x += dpp_or_zero<0x143, 0xc>(x);  // row_bcast:31
   return x;
+}
+
+// Lane 63's value (the chunk's total log decay), wave-uniform.
+__device__ __forceinline__ float last_lane(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
 // log gamma of token cc0 + l (zero past the head's end: no decay there);
@@ -196,7 +211,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_fwd_mfma(const bf
   fetch(r0);
   for (int64_t c0 = r0; c0 < r1; c0 += T) {
     const float b = wave_incl_scan(lgv * kLog2e);  // lane l: b_l
-    const float bT = __shfl(b, 63, 64);
+    const float bT = last_lane(b);
     sB[l] = b;
     store_tile_v<DIM>(sK, kraw);
     store_tile_v<DIM>(sV, vraw);
@@ -297,7 +312,7 @@ __global__ __launch_bounds__(NT, 2) void k_ret_seg_state(const bf16_t* __restric
   fetch(r0);
   for (int64_t c0 = r0; c0 < r1; c0 += T) {
     const float b = wave_incl_scan(lgv * kLog2e);
-    const float bT = __shfl(b, 63, 64);
+    const float bT = last_lane(b);
     lam += bT;
     store_tile_v<DIM>(sV, vraw);
     store_tile_scaled<DIM>(sKs, kraw, b, bT);
@@ -503,7 +518,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
   float Bc = 0.f;  // log2 decay from the segment start to before this chunk
   for (int64_t c0 = r0; c0 < r1; c0 += T) {
     const float b = wave_incl_scan(lgv * kLog2e);
-    const float bT = __shfl(b, 63, 64);
+    const float bT = last_lane(b);
     const float bi = __shfl(b, i, 64);
     sB[l] = b;
     store_tile_v<DIM>(sK, kraw);
@@ -660,7 +675,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
   for (int64_t ci = nch - 1; ci >= 0; --ci) {
     const int64_t c0 = r0 + ci * T;
     const float b = wave_incl_scan(lgv * kLog2e);
-    const float bT = __shfl(b, 63, 64);
+    const float bT = last_lane(b);
     sB[l] = b;
     store_tile_v<DIM>(sK, kraw);
     store_tile_v<DIM>(sV, vraw);
