@@ -104,6 +104,17 @@ __device__ __forceinline__ float shfl_sum_groups(float x) {
   return x;
 }
 
+// x from another lane of the same 16-lane row by a DPP control whose every
+// lane has a source (row_ror, row_half_mirror, quad_perm).
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor8 = 0x128;         // row_ror:8 = lane ^ 8 within a row
+constexpr int kDppXor7 = 0x141;         // row_half_mirror = lane ^ 7
+constexpr int kDppXor2 = 0x4e;          // quad_perm [2, 3, 0, 1]
+constexpr int kDppXor1 = 0xb1;          // quad_perm [1, 0, 3, 2]
+
 __device__ __forceinline__ i32x4 gload16(const bf16_t* p) { return *reinterpret_cast<const i32x4*>(p); }
 
 // Raw buffer access (stride 0) over one head's rows: loads past the range

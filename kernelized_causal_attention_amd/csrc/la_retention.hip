@@ -731,19 +731,21 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
 #pragma unroll
     for (int r = 0; r < 16; ++r) colsum += wv[r];
     colsum = shfl_sum_groups(colsum);
-    // row sums over this wave's 16 keys: halve the 16 values across lanes
-    // li ^ 8, ^ 4, ^ 2, ^ 1; lane li keeps row r = li, i.e. query
+    // row sums over this wave's 16 keys: halve the 16 values across the
+    // lanes of the row in four DPP exchanges, each with a partner whose bit
+    // 3, 2, 1, 0 differs (li ^ 8, ^ 7, ^ 2, ^ 1: every lane of the row is
+    // counted once); lane li keeps row r = li, i.e. query
     // i = 16 (li / 4) + 4g + li % 4
     {
       float h8[8], h4[4], h2[2];
       const bool b3 = li & 8, b2 = li & 4, b1 = li & 2, b0 = li & 1;
 #pragma unroll
-      for (int x = 0; x < 8; ++x) h8[x] = (b3 ? wv[x + 8] : wv[x]) + __shfl_xor(b3 ? wv[x] : wv[x + 8], 8, 64);
+      for (int x = 0; x < 8; ++x) h8[x] = (b3 ? wv[x + 8] : wv[x]) + dpp_row<kDppXor8>(b3 ? wv[x] : wv[x + 8]);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) h4[x] = (b2 ? h8[x + 4] : h8[x]) + __shfl_xor(b2 ? h8[x] : h8[x + 4], 4, 64);
+      for (int x = 0; x < 4; ++x) h4[x] = (b2 ? h8[x + 4] : h8[x]) + dpp_row<kDppXor7>(b2 ? h8[x] : h8[x + 4]);
 #pragma unroll
-      for (int x = 0; x < 2; ++x) h2[x] = (b1 ? h4[x + 2] : h4[x]) + __shfl_xor(b1 ? h4[x] : h4[x + 2], 2, 64);
-      const float h1 = (b0 ? h2[1] : h2[0]) + __shfl_xor(b0 ? h2[0] : h2[1], 1, 64);
+      for (int x = 0; x < 2; ++x) h2[x] = (b1 ? h4[x + 2] : h4[x]) + dpp_row<kDppXor2>(b1 ? h4[x] : h4[x + 2]);
+      const float h1 = (b0 ? h2[1] : h2[0]) + dpp_row<kDppXor1>(b0 ? h2[0] : h2[1]);
       sRow[w * T + 16 * (li >> 2) + 4 * g + (li & 3)] = h1;
     }
     const float dj = ex2(bT - bj);
