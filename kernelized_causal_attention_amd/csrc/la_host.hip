@@ -42,12 +42,14 @@ hipError_t launch_poly_bwd(int pass, int64_t BH, int64_t N, int D, const void* q
                            const void* out, const void* dout, const float* den, void* dq, void* dk, void* dv,
                            float* cvec, int causal, hipStream_t st);
 hipError_t launch_ret_bwd_dq(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg,
-                             const void* dy, const float* carry_s, float* r_agg, void* dq, float* a, hipStream_t st);
+                             const void* dy, const float* carry_s, float* r_agg, void* dq, float* a, float* anch_s,
+                             hipStream_t st);
 hipError_t launch_ret_rscan(const SegGeom& g, float* r_agg, float* dS0, hipStream_t st);
 hipError_t launch_ret_bwd_dkdv(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg,
-                               const void* dy, const float* r_agg, void* dk, void* dv, float* a, hipStream_t st);
-hipError_t launch_ret_dlg(const SegGeom& g, const float* a, const float* carry_s, const float* r_agg, float* dlg,
-                          hipStream_t st);
+                               const void* dy, const float* r_agg, void* dk, void* dv, float* a, const float* anch_s,
+                               float* anch_y, hipStream_t st);
+hipError_t launch_ret_dlg(const SegGeom& g, const float* a, const float* carry_s, const float* r_agg,
+                          const float* anch_y, float* dlg, hipStream_t st);
 hipError_t launch_forward_f32mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
                                   void* out, float* den_out, const float* carry, hipStream_t st);
 hipError_t launch_seg_state_f32mfma(const SegGeom& g, const void* k, const void* v, float* s_out,
@@ -189,13 +191,9 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
     const int64_t target = kernel == LA_KERNEL_MFMA ? 512 : 1024;
     const int64_t want = (target + BH - 1) / BH;
     P = std::min<int64_t>(want, std::max<int64_t>(1, nunits / 4));
-    // The retention backward anchors its gate gradients at every segment
-    // end; between anchors the rounding of the chunk-crossing terms adds up
-    // like a random walk, so its segments stay within 16 units.  The
-    // forward cuts the sequence the same way, so that its segment states can
-    // be handed to the backward.
-    if (op_in == LA_OP_RETENTION_BACKWARD || op_in == LA_OP_RETENTION_FORWARD)
-      P = std::max<int64_t>(P, (nunits + 15) / 16);
+    // (the retention backward anchors its gate gradients every kRetAnchor
+    // tokens inside a segment as well as at its end, so its segments need no
+    // cap of their own)
   }
   P = std::max<int64_t>(1, std::min<int64_t>(P, nunits));
   const int64_t seg_units = (nunits + P - 1) / P;
@@ -222,6 +220,7 @@ struct Carve {
 
 struct WsLayout {
   size_t aggS = 0, totS = 0, aggR = 0, totR = 0, den = 0, cvec = 0;
+  size_t anchS = 0, anchY = 0;  // retention backward: states and <S, R> at the inner anchors
   size_t bytes = 0;
 };
 
@@ -243,6 +242,11 @@ WsLayout layout(int op, int64_t BH, int64_t N, int64_t D, int64_t M, int causal,
     w.aggS = c.take(recs);
     w.aggR = c.take(recs);
     w.den = c.take(static_cast<size_t>(BH) * N);  // per-token q.dq - k.dk
+    const size_t na = static_cast<size_t>(la::ret_anchors(p.seg_len));
+    if (na) {
+      w.anchS = c.take(static_cast<size_t>(BH) * p.P * na * D * M);
+      w.anchY = c.take(static_cast<size_t>(BH) * p.P * na);
+    }
   } else if (op == LA_OP_BACKWARD || op == LA_OP_BACKWARD_STATE) {
     w.aggS = c.take(recs);
     w.totS = c.take(static_cast<size_t>(BH) * E);
@@ -798,6 +802,8 @@ LA_API la_status la_retention_backward(const void* q, const void* k, const void*
   const la::SegGeom g = geom(BH, N, D, M, p, p.chunk);
   float* rrec = at(workspace, w.aggR);
   float* a = at(workspace, w.den);
+  float* anch_s = w.anchS ? at(workspace, w.anchS) : nullptr;
+  float* anch_y = w.anchY ? at(workspace, w.anchY) : nullptr;
   hipError_t e;
   // the states entering each segment: the forward's, or recomputed from S0
   const float* recs = saved;
@@ -813,16 +819,17 @@ LA_API la_status la_retention_backward(const void* q, const void* k, const void*
   // forward sweep (dq, p, suffix aggregates), reverse scan of the
   // aggregates (total = dS0), reverse sweep (dk, dv, a), gate gradients
   if ((e = timed("ret.bwd_dq", stream, [&] {
-         return la::launch_ret_bwd_dq(g, q, k, v, log_gamma, dy, recs, rrec, dq, a, stream);
+         return la::launch_ret_bwd_dq(g, q, k, v, log_gamma, dy, recs, rrec, dq, a, anch_s, stream);
        })))
     return dev(e, "retention backward (dq)");
   if ((e = timed("ret.rscan", stream, [&] { return la::launch_ret_rscan(g, rrec, dS0, stream); })))
     return dev(e, "retention backward (suffix scan)");
   if ((e = timed("ret.bwd_dkdv", stream, [&] {
-         return la::launch_ret_bwd_dkdv(g, q, k, v, log_gamma, dy, rrec, dk, dv, a, stream);
+         return la::launch_ret_bwd_dkdv(g, q, k, v, log_gamma, dy, rrec, dk, dv, a, anch_s, anch_y, stream);
        })))
     return dev(e, "retention backward (dk, dv)");
-  return dev(timed("ret.dlg", stream, [&] { return la::launch_ret_dlg(g, a, recs, rrec, dlog_gamma, stream); }),
+  return dev(timed("ret.dlg", stream,
+                   [&] { return la::launch_ret_dlg(g, a, recs, rrec, anch_y, dlog_gamma, stream); }),
              "retention backward (d log gamma)");
 }
 

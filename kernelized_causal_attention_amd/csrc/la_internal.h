@@ -12,6 +12,15 @@ namespace la {
 // E = D*M + D.
 __host__ __device__ inline int64_t state_elems(int D, int M) { return static_cast<int64_t>(D) * M + D; }
 
+// Retention backward: the gate gradients are anchored every kRetAnchor tokens
+// inside a segment (as well as at its end).  Anchor k of a segment starting
+// at r0 sits at token r0 + k kRetAnchor (k >= 1, strictly inside the
+// segment); a segment of seg_len tokens has at most ret_anchors(seg_len).
+constexpr int kRetAnchor = 1024;
+__host__ __device__ inline int ret_anchors(int64_t seg_len) {
+  return seg_len > 0 ? static_cast<int>((seg_len - 1) / kRetAnchor) : 0;
+}
+
 struct SegGeom {
   int64_t BH;   // B * H independent sequences
   int64_t N;    // tokens per sequence

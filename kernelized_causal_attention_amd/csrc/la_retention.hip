@@ -454,7 +454,8 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
                                                  const bf16_t* __restrict__ v, const float* __restrict__ lg,
                                                  const bf16_t* __restrict__ dy, const float* __restrict__ carry,
                                                  bf16_t* __restrict__ dq, float* __restrict__ qdq,
-                                                 float* __restrict__ r_agg, int64_t N, int P, int seg_len) {
+                                                 float* __restrict__ r_agg, float* __restrict__ anch_s, int64_t N,
+                                                 int P, int seg_len) {
   using G = Geo<DIM>;
   constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -516,7 +517,19 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
   };
   fetch(r0);
   float Bc = 0.f;  // log2 decay from the segment start to before this chunk
+  const int na = ret_anchors(seg_len);
   for (int64_t c0 = r0; c0 < r1; c0 += T) {
+    // at an inner anchor, the state entering this chunk (S[d][m] row-major)
+    // for the dk/dv sweep's <S, R> there
+    if (anch_s && c0 > r0 && (c0 - r0) % kRetAnchor == 0) {
+      float* dst = anch_s + ((bh * P + seg) * na + (c0 - r0) / kRetAnchor - 1) * (DIM * DIM);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int n = 0; n < NTL; ++n) dst[(16 * (w * DT + dt) + 4 * g + u) * DIM + 16 * n + li] = Sacc[dt][n][u];
+    }
     const float b = wave_incl_scan(lgv * kLog2e);
     const float bT = last_lane(b);
     const float bi = __shfl(b, i, 64);
@@ -617,7 +630,8 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
                                                    const bf16_t* __restrict__ v, const float* __restrict__ lg,
                                                    const bf16_t* __restrict__ dy, const float* __restrict__ carry_r,
                                                    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
-                                                   float* __restrict__ qdq, int64_t N, int P, int seg_len) {
+                                                   float* __restrict__ qdq, const float* __restrict__ anch_s,
+                                                   float* __restrict__ anch_y, int64_t N, int P, int seg_len) {
   using G = Geo<DIM>;
   constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -636,7 +650,9 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
   const int rw = (blockIdx.x & 1) ? 3 - w : w;
   uint16_t* sDV = reinterpret_cast<uint16_t*>(sRow + 4 * T) + w * 2 * 16 * LD;  // this wave's dv, dk staging
   uint16_t* sDK = sDV + 16 * LD;
-  float* sB = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(sRow + 4 * T) + 4 * 2 * 16 * LD) + 64 * w;
+  float* sB0 = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(sRow + 4 * T) + 4 * 2 * 16 * LD);
+  float* sB = sB0 + 64 * w;  // this wave's copy of b
+  float* sY = sB0 + 4 * 64;  // per-wave parts of <S, R> at an inner anchor
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
@@ -672,8 +688,30 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
     if (g == 0 && cc0 + j < r1) pj = qdqh[cc0 + j];
   };
   fetch(r0 + (nch - 1) * T);
+  const int na = ret_anchors(seg_len);
   for (int64_t ci = nch - 1; ci >= 0; --ci) {
     const int64_t c0 = r0 + ci * T;
+    // an inner anchor at the end of this chunk: <S, R> there, with R the
+    // suffix state decayed to the chunk's last token (Racc before this
+    // chunk) and S the state the dq sweep kept for the anchor
+    int yk = -1;
+    if (anch_s && c0 + T < r1 && (c0 + T - r0) % kRetAnchor == 0) {
+      yk = static_cast<int>((c0 + T - r0) / kRetAnchor) - 1;
+      const float* src = anch_s + ((bh * P + seg) * na + yk) * (DIM * DIM);
+      float part = 0.f;
+#pragma unroll
+      for (int a = 0; a < DT; ++a)
+#pragma unroll
+        for (int n = 0; n < NTL; ++n) {
+          const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(src + (16 * n + li) * DIM + 16 * (w * DT + a) + 4 * g);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) part += Racc[a][n][u] * sv[u];
+        }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off, 64);
+      part = shfl_sum_groups(part);
+      if (l == 0) sY[w] = part;
+    }
     const float b = wave_incl_scan(lgv * kLog2e);
     const float bT = last_lane(b);
     sB[l] = b;
@@ -683,6 +721,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dkdv(const bf16_t
     store_tile_decay<DIM>(sQs, qraw, b);  // row i times 2^(b_i)
     store_tile_v<DIM>(sG, graw);
     __syncthreads();
+    if (yk >= 0 && tid == 0) anch_y[(bh * P + seg) * na + yk] = sY[0] + sY[1] + sY[2] + sY[3];
     const int soff = static_cast<int>(c0 * DIM * 2);
     const int64_t nrow = min(static_cast<int64_t>(T), r1 - c0);
     const float pcur = pj;
@@ -820,14 +859,18 @@ __global__ __launch_bounds__(NT) void k_ret_rscan(float* __restrict__ recs, int 
   if (tot) tot[bh * DM + e] = carry;
 }
 
-// d log gamma_t = Y_p + sum_{t <= m < r1} a_m over segment p = [r0, r1), one
-// block per (head, segment).  Y_p = <S, R> at the segment's end: S the
-// state after its last token (the next segment's carry record), R the suffix
-// state decayed to that token (its own reverse-scan record); zero for the
-// last segment.
+// d log gamma_t over segment p = [r0, r1), one block per (head, segment),
+// from its anchors: for t in [b_k, b_{k+1}) (b_0 = r0, b_k = r0 + k
+// kRetAnchor the inner anchors, the last interval ending at r1)
+//   d log gamma_t = Y(b_{k+1}) + sum_{t <= m < b_{k+1}} a_m,
+// Y at an inner anchor from the dk/dv sweep (anch_y), Y at the segment's end
+// = <S, R> there: S the state after its last token (the next segment's carry
+// record), R the suffix state decayed to that token (its own reverse-scan
+// record); zero for the last segment.
 __global__ __launch_bounds__(NT) void k_ret_dlg(const float* __restrict__ a, const float* __restrict__ srecs,
-                                                const float* __restrict__ rrecs, float* __restrict__ dlg, int64_t N,
-                                                int P, int seg_len, int64_t E, int64_t DM) {
+                                                const float* __restrict__ rrecs, const float* __restrict__ anch_y,
+                                                float* __restrict__ dlg, int64_t N, int P, int seg_len, int64_t E,
+                                                int64_t DM) {
   __shared__ float wsum[4];
   const int64_t bh = blockIdx.x / P;
   const int p = blockIdx.x % P;
@@ -852,20 +895,29 @@ __global__ __launch_bounds__(NT) void k_ret_dlg(const float* __restrict__ a, con
   __syncthreads();
   float carry = wsum[0] + wsum[1] + wsum[2] + wsum[3];
   __syncthreads();
-  for (int64_t hi = r1; hi > r0; hi -= NT) {
-    // thread tid takes position hi - 1 - tid: a forward scan over the
-    // threads is then a reverse scan over positions
-    const int64_t t = hi - 1 - tid;
-    float x = t >= r0 ? ah[t] : 0.f;
-    x = wave_incl_scan(x);
-    if (l == 63) wsum[w] = x;
-    __syncthreads();
-    float before = carry;
-    for (int u = 0; u < w; ++u) before += wsum[u];
-    if (t >= r0) oh[t] = before + x;
-    const float total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
-    carry += total;
+  // inner anchors of this segment: b_k < r1 for k = 1 .. K
+  const int na = ret_anchors(seg_len);
+  const int K = static_cast<int>((r1 - r0 - 1) / kRetAnchor);
+  int64_t top = r1;
+  for (int kk = K; kk >= 0; --kk) {
+    const int64_t lo = r0 + static_cast<int64_t>(kk) * kRetAnchor;
+    for (int64_t hi = top; hi > lo; hi -= NT) {
+      // thread tid takes position hi - 1 - tid: a forward scan over the
+      // threads is then a reverse scan over positions
+      const int64_t t = hi - 1 - tid;
+      float x = t >= lo ? ah[t] : 0.f;
+      x = wave_incl_scan(x);
+      if (l == 63) wsum[w] = x;
+      __syncthreads();
+      float before = carry;
+      for (int u = 0; u < w; ++u) before += wsum[u];
+      if (t >= lo) oh[t] = before + x;
+      const float total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+      __syncthreads();
+      carry += total;
+    }
+    if (kk > 0) carry = anch_y[(bh * P + p) * na + kk - 1];
+    top = lo;
   }
 }
 
@@ -882,7 +934,7 @@ size_t lds_ret_dq(int dim) {
 }
 size_t lds_ret_dkdv(int dim) {
   return (5 * T * (dim + kLdsPad) + dim * (dim + kLdsPad) + 4 * 2 * 16 * (dim + kLdsPad)) * sizeof(uint16_t) +
-         2 * 4 * T * sizeof(float);
+         2 * 4 * T * sizeof(float) + 4 * sizeof(float);
 }
 
 #define LA_RLAUNCH(kernel, grid, lds, st, ...)                                                               \
@@ -933,7 +985,8 @@ hipError_t launch_ret_forward(const SegGeom& g, const void* q, const void* k, co
 }
 
 hipError_t launch_ret_bwd_dq(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg,
-                             const void* dy, const float* carry_s, float* r_agg, void* dq, float* a, hipStream_t st) {
+                             const void* dy, const float* carry_s, float* r_agg, void* dq, float* a, float* anch_s,
+                             hipStream_t st) {
   const int64_t grid = g.BH * g.P;
   const bf16_t* Q = static_cast<const bf16_t*>(q);
   const bf16_t* K = static_cast<const bf16_t*>(k);
@@ -941,10 +994,11 @@ hipError_t launch_ret_bwd_dq(const SegGeom& g, const void* q, const void* k, con
   const bf16_t* Gy = static_cast<const bf16_t*>(dy);
   bf16_t* dQ = static_cast<bf16_t*>(dq);
   if (g.D == 64)
-    LA_RLAUNCH((k_ret_dq<64>), grid, lds_ret_dq(64), st, Q, K, V, lg, Gy, carry_s, dQ, a, r_agg, g.N, g.P, g.seg_len);
-  if (g.D == 128)
-    LA_RLAUNCH((k_ret_dq<128>), grid, lds_ret_dq(128), st, Q, K, V, lg, Gy, carry_s, dQ, a, r_agg, g.N, g.P,
+    LA_RLAUNCH((k_ret_dq<64>), grid, lds_ret_dq(64), st, Q, K, V, lg, Gy, carry_s, dQ, a, r_agg, anch_s, g.N, g.P,
                g.seg_len);
+  if (g.D == 128)
+    LA_RLAUNCH((k_ret_dq<128>), grid, lds_ret_dq(128), st, Q, K, V, lg, Gy, carry_s, dQ, a, r_agg, anch_s, g.N,
+               g.P, g.seg_len);
   return hipErrorNotSupported;
 }
 
@@ -957,7 +1011,8 @@ hipError_t launch_ret_rscan(const SegGeom& g, float* r_agg, float* dS0, hipStrea
 }
 
 hipError_t launch_ret_bwd_dkdv(const SegGeom& g, const void* q, const void* k, const void* v, const float* lg,
-                               const void* dy, const float* r_agg, void* dk, void* dv, float* a, hipStream_t st) {
+                               const void* dy, const float* r_agg, void* dk, void* dv, float* a, const float* anch_s,
+                               float* anch_y, hipStream_t st) {
   const int64_t grid = g.BH * g.P;
   const bf16_t* Q = static_cast<const bf16_t*>(q);
   const bf16_t* K = static_cast<const bf16_t*>(k);
@@ -966,16 +1021,17 @@ hipError_t launch_ret_bwd_dkdv(const SegGeom& g, const void* q, const void* k, c
   bf16_t* dK = static_cast<bf16_t*>(dk);
   bf16_t* dV = static_cast<bf16_t*>(dv);
   if (g.D == 64)
-    LA_RLAUNCH((k_ret_dkdv<64>), grid, lds_ret_dkdv(64), st, Q, K, V, lg, Gy, r_agg, dK, dV, a, g.N, g.P, g.seg_len);
+    LA_RLAUNCH((k_ret_dkdv<64>), grid, lds_ret_dkdv(64), st, Q, K, V, lg, Gy, r_agg, dK, dV, a, anch_s, anch_y, g.N,
+               g.P, g.seg_len);
   if (g.D == 128)
-    LA_RLAUNCH((k_ret_dkdv<128>), grid, lds_ret_dkdv(128), st, Q, K, V, lg, Gy, r_agg, dK, dV, a, g.N, g.P,
-               g.seg_len);
+    LA_RLAUNCH((k_ret_dkdv<128>), grid, lds_ret_dkdv(128), st, Q, K, V, lg, Gy, r_agg, dK, dV, a, anch_s, anch_y,
+               g.N, g.P, g.seg_len);
   return hipErrorNotSupported;
 }
 
-hipError_t launch_ret_dlg(const SegGeom& g, const float* a, const float* carry_s, const float* r_agg, float* dlg,
-                          hipStream_t st) {
-  hipLaunchKernelGGL(k_ret_dlg, dim3(static_cast<unsigned>(g.BH * g.P)), dim3(NT), 0, st, a, carry_s, r_agg, dlg, g.N,
+hipError_t launch_ret_dlg(const SegGeom& g, const float* a, const float* carry_s, const float* r_agg,
+                          const float* anch_y, float* dlg, hipStream_t st) {
+  hipLaunchKernelGGL(k_ret_dlg, dim3(static_cast<unsigned>(g.BH * g.P)), dim3(NT), 0, st, a, carry_s, r_agg, anch_y, dlg, g.N,
                      g.P, g.seg_len, state_elems(g.D, g.M), static_cast<int64_t>(g.D) * g.M);
   return hipGetLastError();
 }

@@ -212,12 +212,13 @@ def test_retention_backward_rejects_unsupported():
 
 @pytest.mark.parametrize("lo,hi", [(0.01, 0.2), (0.95, 1.0)])
 def test_retention_backward_many_heads(lo, hi):
-    # 512 heads: the plan gives one segment per head for the forward and
-    # caps the backward's at 1024 tokens; heads are independent, so the
-    # oracle checks four of them (both ends of the batch)
+    # 512 heads: the plan gives one 4096-token segment per head, whose gate
+    # gradients are anchored at its three inner anchors (every 1024 tokens)
+    # and at its end; heads are independent, so the oracle checks four of
+    # them (both ends of the batch)
     B, H, N, D = 4, 128, 4096, 64
     plan = la.resolve_plan("retention_backward", B, H, N, D, D, True, "bf16")
-    assert plan["segments"] == 4
+    assert plan["segments"] == 1
     gen = torch.Generator(device=DEV).manual_seed(41)
     mk = lambda: (torch.randn(B, H, N, D, device=DEV, generator=gen) / np.sqrt(D)).to(torch.bfloat16)
     tq, tk, tv, tg = mk(), mk(), mk(), mk()
@@ -228,6 +229,35 @@ def test_retention_backward_many_heads(lo, hi):
     for b, hs in ((0, slice(0, 2)), (3, slice(126, 128))):
         want = ret.backward(f64(tq[b, hs]), f64(tk[b, hs]), f64(tv[b, hs]), f64(tl[b, hs]), f64(tg[b, hs]))
         check_grads([t[b, hs] for t in got], want, f"many heads, batch {b} heads {hs.start}..{hs.stop - 1}",
+                    q=tq[b, hs])
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_retention_backward_inner_anchors_ragged(with_state):
+    # 256 heads of 2500 tokens: two segments per head (0..1279, 1280..2499),
+    # each with one inner anchor (1024 and 2304), the second segment ragged;
+    # the oracle checks two heads at each end of the batch, with the
+    # forward's saved states and without
+    B, H, N, D = 2, 128, 2500, 64
+    plan = la.resolve_plan("retention_backward", B, H, N, D, D, True, "bf16")
+    assert plan["segments"] == 2  # of ceil(40 / 2) = 20 chunks = 1280 tokens
+    gen = torch.Generator(device=DEV).manual_seed(43)
+    mk = lambda: (torch.randn(B, H, N, D, device=DEV, generator=gen) / np.sqrt(D)).to(torch.bfloat16)
+    tq, tk, tv, tg = mk(), mk(), mk(), mk()
+    tl = torch.log(torch.rand(B, H, N, device=DEV, generator=gen) * 0.4 + 0.6).float()
+    tS0 = (torch.randn(B, H, D, D, device=DEV, generator=gen) * 0.3) if with_state else None
+    say(f"backward B={B} H={H} N={N} inner anchors, state={with_state}")
+    saved = torch.empty(la.retention_saved_bytes(B, H, N, D, D), dtype=torch.uint8, device=DEV)
+    la.retention_forward(tq, tk, tv, tl, S0=tS0, saved=saved)
+    with_saved = la.retention_backward(tq, tk, tv, tl, tg, S0=tS0, saved=saved)
+    got = la.retention_backward(tq, tk, tv, tl, tg, S0=tS0)
+    torch.cuda.synchronize()
+    for a, b in zip(with_saved, got):
+        assert torch.equal(a, b)
+    for b, hs in ((0, slice(0, 2)), (1, slice(126, 128))):
+        S0 = None if tS0 is None else f64(tS0[b, hs])
+        want = ret.backward(f64(tq[b, hs]), f64(tk[b, hs]), f64(tv[b, hs]), f64(tl[b, hs]), f64(tg[b, hs]), S0)
+        check_grads([t[b, hs] for t in got], want, f"inner anchors, batch {b} heads {hs.start}..{hs.stop - 1}",
                     q=tq[b, hs])
 
 
