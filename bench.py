@@ -112,19 +112,27 @@ def kernel_bytes(name: str, B, H, N, D, M, es, P=1):
     """Algorithmic HBM bytes one launch of `name` must move (inputs read once,
     outputs written once), for B*H heads of N tokens."""
     ht = B * H * N
+    # the causal forward's segment-state pass reads the first P - 1 segments
+    # (the last one's aggregate would only feed the total), and its scan reads
+    # P - 1 records and writes P
+    ht_agg = ht * (P - 1) // P if P > 1 else ht
+    seg_len = -(-(-(-N // 64)) // P) * 64
+    anchors = B * H * P * ((seg_len - 1) // 1024)  # retention backward's inner anchors
     family, _, base = name.rpartition(".")
     if family == "ret":
         # decayed / gated linear attention; the log gammas are 4 bytes a token
         if base == "seg_state":
-            return ht * (es * (D + M) + 4)
-        if base in ("scan", "rscan"):
+            return ht_agg * (es * (D + M) + 4)
+        if base == "scan":
+            return B * H * (P * 2 - 1) * D * M * 4
+        if base == "rscan":
             return B * H * (P * 2 + 1) * D * M * 4
         if base == "forward":
             return ht * (es * (2 * D + M) + 4 + es * M)
-        if base == "bwd_dq":  # reads q, k, v, dy, gates; writes dq and a
-            return ht * (es * (2 * D + 2 * M) + 4 + es * D + 4)
-        if base == "bwd_dkdv":  # reads q, k, v, dy, gates, a; writes dk, dv, a
-            return ht * (es * (2 * D + 2 * M) + 4 + 8 + es * (D + M))
+        if base == "bwd_dq":  # reads q, k, v, dy, gates; writes dq, a and the anchor states
+            return ht * (es * (2 * D + 2 * M) + 4 + es * D + 4) + anchors * D * M * 4
+        if base == "bwd_dkdv":  # reads q, k, v, dy, gates, a and the anchor states; writes dk, dv, a
+            return ht * (es * (2 * D + 2 * M) + 4 + 8 + es * (D + M)) + anchors * D * M * 4
         if base == "dlg":  # reads a and the segment-end states S, R; writes d log gamma
             return ht * 8 + B * H * (P - 1) * 2 * D * M * 4
     if family == "mfma" and base == "bwd_dq":
@@ -138,13 +146,13 @@ def kernel_bytes(name: str, B, H, N, D, M, es, P=1):
     if base == "forward_den":
         return ht * (es * (2 * D + M) + 4)
     if base == "seg_state":
-        return ht * es * (D + M)
+        return ht_agg * es * (D + M)
     if base == "bwd_dq":
         return ht * (es * (2 * D + 3 * M) + 4 + es * D)
     if base == "bwd_dkdv":
         return ht * (es * (2 * D + 3 * M) + 4 + es * (D + M))
     if base == "seg_scan":
-        return B * H * (P * 2 + 1) * (D * M + D + M) * 4  # prefix records (suffix ones lack the M)
+        return B * H * (P * 2 - 1) * (D * M + D) * 4
     if base == "decode":
         return B * H * (2 * D * M * 4 + 2 * D * 4 + es * (2 * D + M) + es * M)
     return 0
