@@ -232,13 +232,13 @@ def test_retention_backward_many_heads(lo, hi):
                     q=tq[b, hs])
 
 
-@pytest.mark.parametrize("with_state", [False, True])
-def test_retention_backward_inner_anchors_ragged(with_state):
+@pytest.mark.parametrize("D,with_state", [(64, False), (64, True), (128, True)])
+def test_retention_backward_inner_anchors_ragged(D, with_state):
     # 256 heads of 2500 tokens: two segments per head (0..1279, 1280..2499),
     # each with one inner anchor (1024 and 2304), the second segment ragged;
     # the oracle checks two heads at each end of the batch, with the
     # forward's saved states and without
-    B, H, N, D = 2, 128, 2500, 64
+    B, H, N = 2, 128, 2500
     plan = la.resolve_plan("retention_backward", B, H, N, D, D, True, "bf16")
     assert plan["segments"] == 2  # of ceil(40 / 2) = 20 chunks = 1280 tokens
     gen = torch.Generator(device=DEV).manual_seed(43)
@@ -246,7 +246,7 @@ def test_retention_backward_inner_anchors_ragged(with_state):
     tq, tk, tv, tg = mk(), mk(), mk(), mk()
     tl = torch.log(torch.rand(B, H, N, device=DEV, generator=gen) * 0.4 + 0.6).float()
     tS0 = (torch.randn(B, H, D, D, device=DEV, generator=gen) * 0.3) if with_state else None
-    say(f"backward B={B} H={H} N={N} inner anchors, state={with_state}")
+    say(f"backward B={B} H={H} N={N} D={D} inner anchors, state={with_state}")
     saved = torch.empty(la.retention_saved_bytes(B, H, N, D, D), dtype=torch.uint8, device=DEV)
     la.retention_forward(tq, tk, tv, tl, S0=tS0, saved=saved)
     with_saved = la.retention_backward(tq, tk, tv, tl, tg, S0=tS0, saved=saved)
