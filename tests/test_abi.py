@@ -101,23 +101,29 @@ def test_poly_workspace_and_support(lib):
     assert lib.la_workspace_bytes(_native.LA_OP_POLY_BACKWARD, 2, 3, 100, 32, 32, 1, 1) == 0
 
 
-def test_retention_segments_are_capped(lib):
-    # 512 heads fill the chip with one segment each; the retention calls
-    # still cut each head into segments of at most 1024 tokens (the
-    # backward's gate gradients are anchored at every segment end, and the
-    # forward cuts the same way so that its states can be handed over)
+def test_retention_plan_and_anchor_workspace(lib):
+    # the retention calls take the linear-attention plan (512 heads fill the
+    # chip with one segment each); the backward anchors its gate gradients
+    # every 1024 tokens inside a segment as well, keeping one fp32 D x M
+    # state and one scalar per inner anchor in its workspace
     out = _native.la_plan()
-    for op in (_native.LA_OP_RETENTION_FORWARD, _native.LA_OP_RETENTION_BACKWARD):
+    for op in (_native.LA_OP_RETENTION_FORWARD, _native.LA_OP_RETENTION_BACKWARD, _native.LA_OP_FORWARD):
         assert lib.la_resolve_plan(op, 4, 128, 8192, 64, 64, 1, 1, None, ctypes.byref(out)) == 0
-        assert out.segments == 8 and out.kernel == 2
-        assert lib.la_resolve_plan(op, 4, 128, 8000, 64, 64, 1, 1, None, ctypes.byref(out)) == 0
-        assert out.segments == 8  # 125 units -> 8 segments of 16 units (the last 13)
-    # the linear-attention forward is not capped
-    assert lib.la_resolve_plan(_native.LA_OP_FORWARD, 4, 128, 8192, 64, 64, 1, 1, None, ctypes.byref(out)) == 0
-    assert out.segments == 1
+        assert out.segments == 1 and out.kernel == 2
+        assert lib.la_resolve_plan(op, 8, 16, 8192, 64, 64, 1, 1, None, ctypes.byref(out)) == 0
+        assert out.segments == 4
     # the saved record: one state (D*M + D floats) per segment
-    assert lib.la_retention_saved_bytes(4, 128, 8192, 64, 64, 1) == 512 * 8 * (64 * 64 + 64) * 4
+    assert lib.la_retention_saved_bytes(4, 128, 8192, 64, 64, 1) == 512 * 1 * (64 * 64 + 64) * 4
+    assert lib.la_retention_saved_bytes(8, 16, 8192, 64, 64, 1) == 128 * 4 * (64 * 64 + 64) * 4
     assert lib.la_retention_saved_bytes(4, 128, 8192, 64, 64, 0) == 0  # fp32: no retention kernels
+    # backward workspace (regions of 256-byte multiples): segment and suffix
+    # records, the per-token a, and at 8192 tokens per segment 7 inner anchors
+    rec = 512 * 1 * (64 * 64 + 64) * 4
+    want = 2 * rec + 512 * 8192 * 4 + 512 * 7 * 64 * 64 * 4 + 512 * 7 * 4
+    assert lib.la_workspace_bytes(_native.LA_OP_RETENTION_BACKWARD, 4, 128, 8192, 64, 64, 1, 1) == want
+    # 1024-token segments have no inner anchor
+    want = 2 * rec + 512 * 1024 * 4
+    assert lib.la_workspace_bytes(_native.LA_OP_RETENTION_BACKWARD, 4, 128, 1024, 64, 64, 1, 1) == want
 
 
 nogpu = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer validation tests run on hosts without a GPU")
