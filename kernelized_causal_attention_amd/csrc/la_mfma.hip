@@ -325,12 +325,13 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_seg_state_mfma(const
   const int64_t r1 = min(N, r0 + seg_len);
   const int64_t hbytes = N * DIM * 2;
   const rsrc_t rk = make_rsrc(k + bh * N * DIM, hbytes), rv = make_rsrc(v + bh * N * DIM, hbytes);
+  static_assert(NTL == NW, "one column tile of U per wave");
   f32x4_t Sacc[DT][NTL];
   f32x4_t zacc[DT];
-  f32x4_t uacc[NTL];  // column sums of V: lane holds U[16n + li]
+  // column sums of V, this wave's tile: lane holds U[16w + li] (the waves
+  // share the tiles through LDS at the end)
+  f32x4_t uacc = {0.f, 0.f, 0.f, 0.f};
   init_state<DIM, NW>(Sacc, zacc, nullptr, w, g, li);
-#pragma unroll
-  for (int n = 0; n < NTL; ++n) uacc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const short one = 0x3f80;  // bf16 1.0
   const i16x8 ones = {one, one, one, one, one, one, one, one};
   i32x4 kraw[PC], vraw[PC];
@@ -350,13 +351,14 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_seg_state_mfma(const
     for (int s = 0; s < T / 32; ++s) {
       const int jr = 32 * s + 8 * g + li / 4;
       const int cc = 4 * (li % 4);
-#pragma unroll
-      for (int n = 0; n < NTL; ++n)
-        uacc[n] = mfma(ones, cat(lds_tr(sV + jr * LD + 16 * n + cc), lds_tr(sV + (jr + 4) * LD + 16 * n + cc)),
-                       uacc[n]);
+      uacc = mfma(ones, cat(lds_tr(sV + jr * LD + 16 * w + cc), lds_tr(sV + (jr + 4) * LD + 16 * w + cc)), uacc);
     }
     __syncthreads();
   }
+  // every wave's U tile to LDS (over the K tile, free after the last barrier)
+  float* sU = reinterpret_cast<float*>(sKe);
+  if (g == 0) sU[16 * w + li] = uacc[0];
+  __syncthreads();
   const int64_t rec = bh * P + seg;
   const float count = static_cast<float>(r1 - r0);
 #pragma unroll
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_seg_state_mfma(const
     for (int u = 0; u < 4; ++u) {
       const int d = d0 + 4 * g + u;
 #pragma unroll
-      for (int n = 0; n < NTL; ++n) s_out[rec * s_stride + d * DIM + 16 * n + li] = Sacc[dt][n][u] + uacc[n][0];
+      for (int n = 0; n < NTL; ++n) s_out[rec * s_stride + d * DIM + 16 * n + li] = Sacc[dt][n][u] + sU[16 * n + li];
       if (li == 0) z_out[rec * z_stride + d] = zacc[dt][u] + count;
     }
   }
