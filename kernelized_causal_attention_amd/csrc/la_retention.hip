@@ -445,9 +445,11 @@ __device__ __forceinline__ void put_row(uint16_t* lds, const i32x4 (&raw)[Geo<DI
 }
 
 // ---------------------------------------------------------------------------
-// Forward sweep: dq, p_i per token (into qdq), and the segment's
-// suffix aggregate dR = sum_i exp(B_i) q_i dy_i^T (B_i: log decay from the
-// segment start through token i) with Lambda in the record's first Z slot.
+// Forward sweep: dq, p_i per token (into qdq), the segment's suffix
+// aggregate dR = sum_i exp(B_i) q_i dy_i^T (B_i: log decay from the segment
+// start through token i) with Lambda in the record's first Z slot, and at
+// each inner anchor the state entering it (anch_s, null when the segments
+// have no inner anchor).
 // ---------------------------------------------------------------------------
 template <int DIM>
 __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -622,7 +624,8 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_ret_dq(const bf16_t* 
 
 // ---------------------------------------------------------------------------
 // Reverse sweep: dk, dv; completes a_j = p_j + rowsum_j - colsum_j - r_j in
-// place in qdq.
+// place in qdq, and forms Y = <S, R> at each inner anchor (anch_y) from the
+// states the forward sweep kept there (anch_s).
 // carry_r: the suffix state decayed to the segment's last token (or null).
 // ---------------------------------------------------------------------------
 template <int DIM>
