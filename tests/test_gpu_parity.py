@@ -199,6 +199,47 @@ def test_long_bf16_workload():
     check_forward(tq, tk, tv, True, "bf16", heads=[(0, 0), (0, 11)], null_guard=True)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_forward_largest_mfma_head(D):
+    # The largest head the bf16 MFMA kernels take (2^31 bytes per tensor per
+    # head: their buffer offsets are 32-bit), N = 2^31 / (2 D) - 64 tokens in
+    # 512 segments.  With k = 0 (phi = 1 for every key) the exact output is
+    # the prefix mean of v whatever q is (the "Transformers are RNNs"
+    # walkthrough, section 3, eq:output with equal weights):
+    # out_i[m] = #{j <= i : (j + m) % 5 == 0} / (i + 1) for the 0/1 v used
+    # here, checked row by row on sampled rows across the whole head.
+    B, H = 1, 1
+    N = (1 << 31) // (2 * D) - 64
+    plan = la.resolve_plan("forward", B, H, N, D, D, True, "bf16")
+    assert plan["kernel"] == 2 and plan["segments"] == 512
+    say(f"largest MFMA head: D={D} N={N}")
+    gen = torch.Generator(device=DEV).manual_seed(47)
+    q = (torch.randn(B, H, N, D, device=DEV, generator=gen) * 0.5).to(torch.bfloat16)
+    k = torch.zeros(B, H, N, D, device=DEV, dtype=torch.bfloat16)
+    j = torch.arange(N, device=DEV, dtype=torch.int32)[:, None]
+    m = torch.arange(D, device=DEV, dtype=torch.int32)[None, :]
+    v = ((j + m) % 5 == 0).to(torch.bfloat16).reshape(B, H, N, D)
+    del j, m
+    out = la.forward(q, k, v)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 65, 16383, 16384, N // 2, N - 65, N - 64, N - 2, N - 1],
+                                     rng.integers(0, N, 40)]))
+    got = out[0, 0, torch.as_tensor(rows, device=DEV)].double().cpu().numpy()
+    mm = np.arange(D)
+    r0 = (5 - mm % 5) % 5  # first j with (j + m) % 5 == 0
+    worst = 0.0
+    for row, g in zip(rows, got):
+        count = np.where(row >= r0, (row - r0) // 5 + 1, 0)
+        want = count / (row + 1.0)
+        e = np.linalg.norm(g - want) / np.linalg.norm(want)
+        worst = max(worst, e)
+        assert e < TOL["bf16"], (int(row), e)
+    say(f"largest MFMA head D={D}: worst row rel-L2 {worst:.2e} over {len(rows)} rows")
+    del q, k, v, out
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------- decode -----
 def test_decode_workload_against_parallel_form():
     from workloads import decode_inputs
