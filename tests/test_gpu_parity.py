@@ -240,6 +240,53 @@ def test_forward_largest_mfma_head(D):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_largest_mfma_head(D):
+    # The backward at the largest head of the MFMA kernels (as above), with
+    # q = k = 0 so that every gradient has a closed form (chain rule of
+    # eq:output with phi = 1, den_i = D (i + 1), A_ij = D; dout_i = e_0):
+    #   dv_j[m] = [m = 0] sum_{i >= j} 1 / (i + 1),
+    #   dk_j[d] = (v_j[0] sum_{i >= j} 1 / (i + 1) - sum_{i >= j} out_i[0] / (i + 1)) / D,
+    #   dq_i = 0 (q enters num and den alike), with out_i[0] = (i // 5 + 1) / (i + 1).
+    B, H = 1, 1
+    N = (1 << 31) // (2 * D) - 64
+    say(f"largest MFMA head backward: D={D} N={N}")
+    z = torch.zeros(B, H, N, D, device=DEV, dtype=torch.bfloat16)
+    j = torch.arange(N, device=DEV, dtype=torch.int32)[:, None]
+    m = torch.arange(D, device=DEV, dtype=torch.int32)[None, :]
+    v = ((j + m) % 5 == 0).to(torch.bfloat16).reshape(B, H, N, D)
+    del j, m
+    dout = torch.zeros(B, H, N, D, device=DEV, dtype=torch.bfloat16)
+    dout[..., 0] = 1.0
+    out = la.forward(z, z, v)
+    dq, dk, dv = la.backward(z, z, v, out, dout)
+    torch.cuda.synchronize()
+    i1 = np.arange(1, N + 1, dtype=np.float64)
+    tail_h = np.cumsum((1.0 / i1)[::-1])[::-1]                      # sum_{i >= j} 1 / (i + 1)
+    out0 = (np.arange(N) // 5 + 1) / i1
+    tail_o = np.cumsum((out0 / i1)[::-1])[::-1]                     # sum_{i >= j} out_i[0] / (i + 1)
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, 1, 4, 5, 63, 64, 65, N // 2, N - 65, N - 64, N - 2, N - 1],
+                                     rng.integers(0, N, 40)]))
+    idx = torch.as_tensor(rows, device=DEV)
+    g_dq, g_dk, g_dv = (t[0, 0, idx].double().cpu().numpy() for t in (dq, dk, dv))
+    worst = 0.0
+    for n_, row in enumerate(rows):
+        want_dv = np.zeros(D)
+        want_dv[0] = tail_h[row]
+        want_dk = np.full(D, ((row % 5 == 0) * tail_h[row] - tail_o[row]) / D)
+        for name, g, w in (("dv", g_dv[n_], want_dv), ("dk", g_dk[n_], want_dk)):
+            e = np.linalg.norm(g - w) / np.linalg.norm(w)
+            worst = max(worst, e)
+            assert e < TOL["bf16"], (name, int(row), e)
+        # dq: the two cancelling terms are (i // 5 + 1) / den_i each
+        scale = (row // 5 + 1) / (D * (row + 1.0)) * np.sqrt(D)
+        assert np.linalg.norm(g_dq[n_]) < TOL["bf16"] * scale, (int(row), np.linalg.norm(g_dq[n_]), scale)
+    say(f"largest MFMA head backward D={D}: worst row rel-L2 {worst:.2e} over {len(rows)} rows")
+    del z, v, dout, out, dq, dk, dv
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------- decode -----
 def test_decode_workload_against_parallel_form():
     from workloads import decode_inputs
