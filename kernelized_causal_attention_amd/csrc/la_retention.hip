@@ -886,6 +886,9 @@ __global__ __launch_bounds__(NT) void k_ret_dlg(const float* __restrict__ a, con
   if (p + 1 < P) {
     const float* s = srecs + (bh * P + p + 1) * E;
     const float* r = rrecs + (bh * P + p) * E;
+    // unrolled so that eight pairs of loads are in flight at once (the sum
+    // keeps its order)
+#pragma unroll 8
     for (int64_t e = tid; e < DM; e += NT) y += s[e] * r[e];
   }
   y += __shfl_xor(y, 1, 64);
