@@ -904,20 +904,32 @@ __global__ __launch_bounds__(NT) void k_ret_dlg(const float* __restrict__ a, con
   // inner anchors of this segment: b_k < r1 for k = 1 .. K
   const int na = ret_anchors(seg_len);
   const int K = static_cast<int>((r1 - r0 - 1) / kRetAnchor);
+  // Each interval is walked from its top in blocks of NT * kDlgPer tokens
+  // (kRetAnchor = one block): thread tid holds the kDlgPer consecutive tokens
+  // ending kDlgPer * tid below the block's top, so a block's suffix sums are
+  // each thread's own suffix sums plus an exclusive scan of the thread
+  // totals over the threads.
+  constexpr int kDlgPer = 4;
   int64_t top = r1;
   for (int kk = K; kk >= 0; --kk) {
     const int64_t lo = r0 + static_cast<int64_t>(kk) * kRetAnchor;
-    for (int64_t hi = top; hi > lo; hi -= NT) {
-      // thread tid takes position hi - 1 - tid: a forward scan over the
-      // threads is then a reverse scan over positions
-      const int64_t t = hi - 1 - tid;
-      float x = t >= lo ? ah[t] : 0.f;
-      x = wave_incl_scan(x);
-      if (l == 63) wsum[w] = x;
+    for (int64_t hi = top; hi > lo; hi -= NT * kDlgPer) {
+      const int64_t t0 = hi - static_cast<int64_t>(kDlgPer) * (tid + 1);
+      float x[kDlgPer];
+#pragma unroll
+      for (int u = 0; u < kDlgPer; ++u) x[u] = t0 + u >= lo ? ah[t0 + u] : 0.f;
+#pragma unroll
+      for (int u = kDlgPer - 2; u >= 0; --u) x[u] += x[u + 1];
+      const float incl = wave_incl_scan(x[0]);
+      if (l == 63) wsum[w] = incl;
+      const float up = __shfl_up(incl, 1, 64);
       __syncthreads();
       float before = carry;
       for (int u = 0; u < w; ++u) before += wsum[u];
-      if (t >= lo) oh[t] = before + x;
+      if (l > 0) before += up;  // the totals of this wave's earlier lanes
+#pragma unroll
+      for (int u = 0; u < kDlgPer; ++u)
+        if (t0 + u >= lo) oh[t0 + u] = before + x[u];
       const float total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
       __syncthreads();
       carry += total;
