@@ -334,6 +334,138 @@ __global__ __launch_bounds__(NT, 2) void k_ret_seg_state(const bf16_t* __restric
   if (tid == 0) rec[DIM * DIM] = lam * kLn2;
 }
 
+// Segment aggregates at D = 64 with wave-private chunks (the layout of the
+// linear-attention segment pass).  The workgroup first sums the log decay
+// (base 2) of every chunk of the segment and scans those totals from the
+// end, so that each key can be weighted when staged by its decay to the
+// segment's end, 2^(Lambda - L_j) = 2^((b_T - b_j) + later) <= 1 (b the
+// in-chunk scan, later the summed decay of the chunks after it); wave w
+// then sums chunks w, w + 4, ... into a 64 x 64 partial of its own with no
+// rescaling between chunks, and the four partials are added in wave order.
+// Segments of more than kRetSegWaveChunks chunks use k_ret_seg_state.
+constexpr int kRetSegWaveChunks = NT;
+__global__ __launch_bounds__(NT, 2) void k_ret_seg_wave64(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                                                         const float* __restrict__ lg, float* __restrict__ recs,
+                                                         int64_t N, int P, int nseg, int seg_len) {
+  constexpr int DIM = 64, LD = DIM + kLdsPad;
+  constexpr int PW = T * DIM / 8 / 64;  // 16-byte pieces per lane per chunk tile
+  constexpr int RP = DIM + 4;           // fp32 row stride of the partials in LDS
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint16_t* sK = smem + w * 2 * T * LD;
+  uint16_t* sV = sK + T * LD;
+  float* sLater = reinterpret_cast<float*>(smem + 4 * 2 * T * LD);  // [chunk]: decay of the later chunks
+  float* sW = sLater + kRetSegWaveChunks + 4 + 64 * w;              // this wave's key weights
+  float* wsum = sLater + kRetSegWaveChunks;                         // 4 floats
+  const int64_t bh = blockIdx.x / nseg;
+  const int seg = blockIdx.x % nseg;
+  const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
+  const int64_t r1 = min(N, r0 + seg_len);
+  const int nch = static_cast<int>((r1 - r0 + T - 1) / T);
+  const int64_t hbytes = N * DIM * 2;
+  const rsrc_t rk = make_rsrc(k + bh * N * DIM, hbytes), rv = make_rsrc(v + bh * N * DIM, hbytes),
+               rl = make_rsrc(lg + bh * N, N * 4);
+  // chunk totals (tokens past the head's end read 0: no decay), then their
+  // exclusive suffix sums: thread tid holds chunk nch - 1 - tid, so a scan
+  // over the threads runs from the segment's end
+  for (int c = w; c < nch; c += 4) {
+    float x = gate(rl, l, r0 + static_cast<int64_t>(c) * T) * kLog2e;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+    if (l == 0) sLater[c] = x;
+  }
+  __syncthreads();
+  float lam = 0.f;  // the segment's log2 decay (all chunks)
+  {
+    const int c = nch - 1 - tid;
+    const float t = c >= 0 ? sLater[c] : 0.f;
+    const float incl = wave_incl_scan(t);
+    if (l == 63) wsum[w] = incl;
+    const float up = __shfl_up(incl, 1, 64);
+    __syncthreads();
+    float before = 0.f;
+    for (int u = 0; u < w; ++u) before += wsum[u];
+    if (l > 0) before += up;
+    lam = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    if (c >= 0) sLater[c] = before;
+  }
+  __syncthreads();
+
+  f32x4_t S[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) S[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // piece p of lane l: row (64 p + l) / 8, features 8 ((64 p + l) % 8) ..
+  i32x4 kr[PW], vr[PW];
+  float lgv = 0.f;
+  auto fetch = [&](int c) {
+    const int64_t cc0 = r0 + static_cast<int64_t>(c) * T;
+    const int soff = static_cast<int>(cc0 * DIM * 2);
+#pragma unroll
+    for (int p = 0; p < PW; ++p) {
+      kr[p] = bload16(rk, (64 * p + l) * 16, soff);
+      vr[p] = bload16(rv, (64 * p + l) * 16, soff);
+    }
+    lgv = gate(rl, l, cc0);
+  };
+  if (w < nch) fetch(w);
+  for (int c = w; c < nch; c += 4) {
+    // weight of key l of this chunk: 2^((b_T - b_l) + later)
+    const float b = wave_incl_scan(lgv * kLog2e);
+    sW[l] = ex2(last_lane(b) - b + sLater[c]);
+    wave_lds_sync();
+    // rows past the head's end loaded as zero
+#pragma unroll
+    for (int p = 0; p < PW; ++p) {
+      const int e = 64 * p + l;
+      const float wt = sW[e >> 3];
+      *reinterpret_cast<i16x8*>(sK + (e >> 3) * LD + (e & 7) * 8) =
+          pack8(unpack8(__builtin_bit_cast(i16x8, kr[p])) * wt);
+      *reinterpret_cast<i16x8*>(sV + (e >> 3) * LD + (e & 7) * 8) = __builtin_bit_cast(i16x8, vr[p]);
+    }
+    if (c + 4 < nch) fetch(c + 4);
+    // the tiles are private to this wave: its LDS operations complete in
+    // order, so only the compiler has to be kept from reordering them
+    wave_lds_sync();
+#pragma unroll
+    for (int s = 0; s < T / 32; ++s) {
+      const int jr = 32 * s + 8 * g + li / 4;
+      const int cc = 4 * (li % 4);
+      i16x8 a[4], bb[4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        a[n] = cat(lds_tr(sK + jr * LD + 16 * n + cc), lds_tr(sK + (jr + 4) * LD + 16 * n + cc));
+        bb[n] = cat(lds_tr(sV + jr * LD + 16 * n + cc), lds_tr(sV + (jr + 4) * LD + 16 * n + cc));
+      }
+#pragma unroll
+      for (int dn = 0; dn < 4; ++dn)
+#pragma unroll
+        for (int mn = 0; mn < 4; ++mn) S[dn][mn] = mfma(a[dn], bb[mn], S[dn][mn]);
+    }
+    wave_lds_sync();
+  }
+  // partials to LDS (over the chunk tiles): Sp[w][d][m], rows padded to RP
+  __syncthreads();
+  float* Sp = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int dn = 0; dn < 4; ++dn)
+#pragma unroll
+    for (int mn = 0; mn < 4; ++mn)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Sp[(w * DIM + 16 * dn + 4 * g + u) * RP + 16 * mn + li] = S[dn][mn][u];
+  __syncthreads();
+  constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;
+  float* rec = recs + (bh * P + seg) * E;
+  const int m = tid & 63;
+  for (int d = tid >> 6; d < DIM; d += 4)
+    rec[d * DIM + m] = ((Sp[d * RP + m] + Sp[(DIM + d) * RP + m]) + Sp[(2 * DIM + d) * RP + m]) +
+                       Sp[(3 * DIM + d) * RP + m];
+  if (tid == 0) rec[DIM * DIM] = lam * kLn2;
+}
+
 // Decayed exclusive scan over segments, in place on the S part of the
 // records: C_0 = S0 (or 0), C_{p+1} = exp(Lambda_p) C_p + dS_p; record p
 // receives C_p; the total C_P goes to tot (when not null; tot may be S0).
@@ -946,6 +1078,11 @@ size_t lds_ret_fwd(int dim) {
          4 * T * sizeof(float);
 }
 size_t lds_ret_seg(int dim) { return 2 * T * (dim + kLdsPad) * sizeof(uint16_t); }
+size_t lds_ret_seg_wave64() {
+  const size_t tiles = 4 * 2 * T * (64 + kLdsPad) * sizeof(uint16_t);
+  const size_t parts = 4 * 64 * (64 + 4) * sizeof(float);
+  return (tiles > parts ? tiles : parts) + (kRetSegWaveChunks + 4 + 4 * 64) * sizeof(float);
+}
 size_t lds_ret_dq(int dim) {
   return (6 * T * (dim + kLdsPad) + dim * (dim + kLdsPad) + 4 * 16 * (dim + kLdsPad)) * sizeof(uint16_t) +
          4 * T * sizeof(float);
@@ -974,6 +1111,8 @@ hipError_t launch_ret_seg_state(const SegGeom& g, const void* k, const void* v, 
   const int64_t grid = g.BH * nseg;
   const bf16_t* K = static_cast<const bf16_t*>(k);
   const bf16_t* V = static_cast<const bf16_t*>(v);
+  if (g.D == 64 && (g.seg_len + T - 1) / T <= kRetSegWaveChunks)
+    LA_RLAUNCH(k_ret_seg_wave64, grid, lds_ret_seg_wave64(), st, K, V, lg, recs, g.N, g.P, nseg, g.seg_len);
   if (g.D == 64) LA_RLAUNCH((k_ret_seg_state<64>), grid, lds_ret_seg(64), st, K, V, lg, recs, g.N, g.P, nseg, g.seg_len);
   if (g.D == 128)
     LA_RLAUNCH((k_ret_seg_state<128>), grid, lds_ret_seg(128), st, K, V, lg, recs, g.N, g.P, nseg, g.seg_len);
