@@ -159,6 +159,30 @@ def test_state_updated_in_place_and_decode_handoff():
     assert rel_l2(f64(S), ref[2]) < 1e-5 and rel_l2(f64(Z), ref[3]) < 1e-5
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_state_without_state_outputs(dtype):
+    # la_forward_state with S_out = Z_out = NULL: the segment pass then skips
+    # the last segment (its aggregate would only feed the total); the output
+    # must equal the call that also returns the state, bit for bit
+    B, H, N, D, M = 2, 3, 2000, 64, 64
+    tq, tk, tv, _, S0, Z0 = case(B, H, N, D, M, dtype, seed=9, prefix=100)
+    tS0 = torch.tensor(S0, dtype=torch.float32, device=DEV)
+    tZ0 = torch.tensor(Z0, dtype=torch.float32, device=DEV)
+    assert la.resolve_plan("forward_state", B, H, N, D, M, True, dtype)["segments"] > 1
+    want, _, _ = la.forward_state(tq, tk, tv, tS0, tZ0)
+    lib = la._native.load()
+    out = torch.empty_like(tv)
+    nws = la.workspace_bytes("forward_state", B, H, N, D, M, True, dtype)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=DEV)
+    dt = {"f32": la._native.LA_F32, "bf16": la._native.LA_BF16}[dtype]
+    st = lib.la_forward_state(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), B, H, N, D, M, dt,
+                              tS0.data_ptr(), tZ0.data_ptr(), None, None, None, ws.data_ptr(), nws,
+                              torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0, lib.la_last_error()
+    assert torch.equal(out, want)
+
+
 def test_state_arguments_are_validated():
     tq, tk, tv, _, S0, Z0 = case(1, 1, 64, 16, 16, "f32", seed=1, prefix=10)
     tS0 = torch.tensor(S0, dtype=torch.float32, device=DEV)
