@@ -25,8 +25,20 @@
  *    accumulation is fp32; den, S and Z are always fp32.  bf16 results are
  *    rounded to nearest even.
  *  - Sizes: B, H, N >= 1; 1 <= D, M <= 256 (LA_ERR_UNSUPPORTED otherwise).
- *    bf16 tensors need 4-byte alignment, fp32 tensors 4-byte alignment;
- *    16-byte alignment enables the vectorised fast paths.
+ *  - Alignment: every tensor pointer must be aligned to its element size
+ *    (2 bytes bf16, 4 bytes fp32; LA_ERR_INVALID otherwise); workspace and
+ *    saved records must be 16-byte aligned.  The MFMA kernels move tensors in
+ *    16-byte vectors, so they run only when every q, k, v, out, dout, dq,
+ *    dk, dv pointer of the call is 16-byte aligned (any pointer from
+ *    hipMalloc or torch's allocator is).  A call on the automatic plan
+ *    with a pointer that is only element-aligned runs the generic kernels
+ *    instead, cut into the same segments (so the sizes la_workspace_bytes
+ *    and la_saved_bytes report still suffice); a plan that asks for the
+ *    MFMA kernels is then refused with LA_ERR_UNSUPPORTED.  The retention,
+ *    polynomial and softmax calls, which have no generic kernels, return
+ *    LA_ERR_UNSUPPORTED unless their tensor pointers are 16-byte aligned
+ *    (state pointers S, Z, S0, dS0 and the fp32 outputs den_out, lse,
+ *    dlog_gamma need 4 bytes).
  *  - Outputs must not overlap inputs (LA_ERR_INVALID), except the decode
  *    state S, Z, which is updated in place by design.
  *  - Validation runs before any HIP call: null pointers, sizes < 1, unknown

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <map>
 #include <mutex>
 #include <string>
@@ -128,6 +129,23 @@ la_status check_ptr(const void* p, const char* name, int dtype) {
   return LA_OK;
 }
 
+// The MFMA kernels move q, k, v, out, dout, dq, dk, dv (and, in the families
+// that have no generic kernels, every other per-token tensor) in 16-byte
+// vectors through buffer loads and stores; a tensor that is only
+// dtype-aligned goes to the generic kernels (element accesses) or, where
+// there are none, is refused.
+bool vec16(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (p && (reinterpret_cast<uintptr_t>(p) & 15)) return false;
+  return true;
+}
+
+la_status need_vec16(std::initializer_list<const void*> ptrs, const char* what) {
+  if (vec16(ptrs)) return LA_OK;
+  return fail(LA_ERR_UNSUPPORTED, "%s: every tensor pointer must be 16-byte aligned (these kernels have no "
+              "element-wise fallback)", what);
+}
+
 la_status check_disjoint(const Span* outs, int nout, const Span* ins, int nin) {
   for (int i = 0; i < nout; ++i) {
     if (!outs[i].lo) continue;
@@ -149,8 +167,14 @@ struct Plan {
   int chunk;     // chunk used by the forward-type kernels (informational)
 };
 
+// vec_ok: every tensor pointer of the call is 16-byte aligned (the sizing
+// queries, which see no pointers, assume so).  When it is not, the automatic
+// plan keeps the segmentation the MFMA kernels would use -- so workspace and
+// saved-state sizes stay what la_workspace_bytes / la_saved_bytes report --
+// but runs the generic kernels; a plan that asks for the MFMA kernels is
+// refused.
 la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal, int dtype,
-                  const la_plan* req, Plan* out) {
+                  const la_plan* req, Plan* out, bool vec_ok = true) {
   (void)causal;
   int kernel = req ? req->kernel : LA_KERNEL_AUTO;
   if (kernel < LA_KERNEL_AUTO || kernel > LA_KERNEL_MFMA) return fail(LA_ERR_INVALID, "plan.kernel=%d", kernel);
@@ -164,9 +188,17 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
   if (kernel == LA_KERNEL_MFMA && !mfma_ok)
     return fail(LA_ERR_UNSUPPORTED, "no MFMA kernel for op %d, N=%lld, D=%lld, M=%lld, dtype %d", op, (long long)N,
                 (long long)D, (long long)M, dtype);
+  if (kernel == LA_KERNEL_MFMA && !vec_ok)
+    return fail(LA_ERR_UNSUPPORTED, "the MFMA kernels need 16-byte aligned tensor pointers");
   if (kernel == LA_KERNEL_AUTO) kernel = mfma_ok ? LA_KERNEL_MFMA : LA_KERNEL_GENERIC;
+  // a misaligned call on the automatic plan: MFMA segmentation, generic kernels
+  const bool demoted = kernel == LA_KERNEL_MFMA && !vec_ok;
   const int unit = kernel == LA_KERNEL_MFMA ? 64 : 32;  // segment granularity
   int chunk = req ? req->chunk : 0;
+  if (demoted) {
+    kernel = LA_KERNEL_GENERIC;
+    chunk = 0;
+  }
   if (kernel == LA_KERNEL_GENERIC) {
     if (chunk != 0 && chunk != 16 && chunk != 32)
       return fail(LA_ERR_INVALID, "plan.chunk=%d (generic kernels take 16 or 32)", chunk);
@@ -188,7 +220,7 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
     // two workgroups per CU (measured best on the B=8, H=16, N=8192, D=64
     // step: 512 beats 1024, 768 and 2048).  Segments keep at least 4 units;
     // more segments only add scan work.
-    const int64_t target = kernel == LA_KERNEL_MFMA ? 512 : 1024;
+    const int64_t target = (kernel == LA_KERNEL_MFMA || demoted) ? 512 : 1024;
     const int64_t want = (target + BH - 1) / BH;
     P = std::min<int64_t>(want, std::max<int64_t>(1, nunits / 4));
     // (the retention backward anchors its gate gradients every kRetAnchor
@@ -348,6 +380,8 @@ la::SegGeom geom(int64_t BH, int64_t N, int64_t D, int64_t M, const Plan& p, int
 
 // The geometry for a segment-state pass whose scan produces no total: the
 // last segment's aggregate would only feed that total, so it is skipped.
+// With one segment there is nothing left to sum: callers skip the pass (the
+// scan then writes the initial state into the record).
 la::SegGeom without_last(const la::SegGeom& g) {
   la::SegGeom r = g;
   if (g.P > 1) r.nseg = g.P - 1;
@@ -431,7 +465,7 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
   const int64_t BH = B * H;
   const size_t es = dtype_size(dtype);
   Plan p;
-  if ((s = resolve(LA_OP_FORWARD, B, H, N, D, M, causal, dtype, plan, &p))) return s;
+  if ((s = resolve(LA_OP_FORWARD, B, H, N, D, M, causal, dtype, plan, &p, vec16({q, k, v, out})))) return s;
   const size_t nsaved = saved_floats(BH, D, M, causal, p);
   if (saved && saved_bytes < nsaved * sizeof(float))
     return fail(LA_ERR_INVALID, "saved too small: %zu bytes given, %zu needed", saved_bytes, nsaved * sizeof(float));
@@ -462,7 +496,11 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
     // every segment's carry-in (starting from S0, Z0) and the final state
     // come from the segment aggregates and their scan, as exact as fp32
     float* agg = sv ? sv : at(workspace, w.aggS);
-    if ((e = seg_state(dtype, p, st.S_out ? g : without_last(g), k, v, agg, stream))) return dev(e, "segment state");
+    // (with one segment and no final state the scan only writes S0, Z0 into
+    // the first record: there is no aggregate to compute)
+    if ((st.S_out || p.P > 1) &&
+        (e = seg_state(dtype, p, st.S_out ? g : without_last(g), k, v, agg, stream)))
+      return dev(e, "segment state");
     if ((e = scan(agg, BH, p.P, g.D, g.M, 0, st.S_out, D * M, st.Z_out, D, stream, st.S0, st.Z0)))
       return dev(e, "segment scan");
     return dev(fwd_pass(dtype, 1, p, g, q, k, v, out, den_out, agg, stream), "forward");
@@ -511,7 +549,9 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
   const int64_t BH = B * H;
   const size_t es = dtype_size(dtype);
   Plan p;
-  if ((s = resolve(LA_OP_BACKWARD, B, H, N, D, M, causal, dtype, plan, &p))) return s;
+  if ((s = resolve(LA_OP_BACKWARD, B, H, N, D, M, causal, dtype, plan, &p,
+                   vec16({q, k, v, out, dout, dq, dk, dv}))))
+    return s;
   const size_t nsaved = saved_floats(BH, D, M, causal, p);
   if (saved) {
     // the saved states are per segment of the forward's plan
@@ -552,8 +592,9 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
   hipError_t e;
   const float* carry_s = nullptr;
   if (st.on) {
-    // carry-in from S0, Z0 through the segment scan (any number of segments)
-    if ((e = seg_state(dtype, p, without_last(g), k, v, aggS, stream))) return dev(e, "segment state");
+    // carry-in from S0, Z0 through the segment scan (any number of segments;
+    // with one, the scan only writes S0, Z0 into its record)
+    if (p.P > 1 && (e = seg_state(dtype, p, without_last(g), k, v, aggS, stream))) return dev(e, "segment state");
     if ((e = scan(aggS, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream, st.S0, st.Z0)))
       return dev(e, "segment scan");
     carry_s = aggS;
@@ -715,6 +756,7 @@ LA_API la_status la_retention_forward(const void* q, const void* k, const void* 
   if (!la::retention_supported(D, M, dtype))
     return fail(LA_ERR_UNSUPPORTED, "retention kernels take bf16 with D = M in {64, 128} (D=%lld, M=%lld, dtype %d)",
                 (long long)D, (long long)M, dtype);
+  if ((s = need_vec16({q, k, v, y, log_gamma}, "retention forward"))) return s;
   const int64_t BH = B * H;
   const size_t es = dtype_size(dtype);
   Plan p;
@@ -749,7 +791,9 @@ LA_API la_status la_retention_forward(const void* q, const void* k, const void* 
     float* recs = saved ? saved : at(workspace, w.aggS);
     // without S_out the last segment's aggregate would only feed the total
     const la::SegGeom gs = S_out ? g : without_last(g);
-    if ((e = timed("ret.seg_state", stream, [&] { return la::launch_ret_seg_state(gs, k, v, log_gamma, recs, stream); })))
+    // (with one segment and no S_out the scan only writes S0 into the record)
+    if ((S_out || p.P > 1) &&
+        (e = timed("ret.seg_state", stream, [&] { return la::launch_ret_seg_state(gs, k, v, log_gamma, recs, stream); })))
       return dev(e, "retention segment state");
     if ((e = timed("ret.scan", stream, [&] { return la::launch_ret_scan(recs, BH, p.P, g.D, g.M, S0, S_out, stream); })))
       return dev(e, "retention scan");
@@ -777,6 +821,7 @@ LA_API la_status la_retention_backward(const void* q, const void* k, const void*
   if (!la::retention_supported(D, M, dtype))
     return fail(LA_ERR_UNSUPPORTED, "retention kernels take bf16 with D = M in {64, 128} (D=%lld, M=%lld, dtype %d)",
                 (long long)D, (long long)M, dtype);
+  if ((s = need_vec16({q, k, v, dy, log_gamma, dq, dk, dv}, "retention backward"))) return s;
   const int64_t BH = B * H;
   const size_t es = dtype_size(dtype);
   Plan p;
@@ -810,7 +855,8 @@ LA_API la_status la_retention_backward(const void* q, const void* k, const void*
   if (!saved) {
     float* r = at(workspace, w.aggS);
     const la::SegGeom gs = without_last(g);  // the scan below keeps no total
-    if ((e = timed("ret.seg_state", stream, [&] { return la::launch_ret_seg_state(gs, k, v, log_gamma, r, stream); })))
+    if (p.P > 1 &&
+        (e = timed("ret.seg_state", stream, [&] { return la::launch_ret_seg_state(gs, k, v, log_gamma, r, stream); })))
       return dev(e, "retention segment state");
     if ((e = timed("ret.scan", stream, [&] { return la::launch_ret_scan(r, BH, p.P, g.D, g.M, S0, nullptr, stream); })))
       return dev(e, "retention scan");
@@ -845,6 +891,7 @@ LA_API la_status la_poly_forward(const void* q, const void* k, const void* v, vo
   if (!la::poly_supported(D, M, dtype))
     return fail(LA_ERR_UNSUPPORTED, "polynomial kernels take bf16 with D = M in {64, 128} (D=%lld, M=%lld, dtype %d)",
                 (long long)D, (long long)M, dtype);
+  if ((s = need_vec16({q, k, v, out}, "polynomial forward"))) return s;
   if (N * D * 2 >= (int64_t(1) << 31)) return fail(LA_ERR_UNSUPPORTED, "head too large for 32-bit offsets");
   const int64_t BH = B * H;
   if (BH * ((N + 127) / 128) > 0xffffffffLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
@@ -871,6 +918,7 @@ LA_API la_status la_poly_backward(const void* q, const void* k, const void* v, c
   if (!la::poly_supported(D, M, dtype))
     return fail(LA_ERR_UNSUPPORTED, "polynomial kernels take bf16 with D = M in {64, 128} (D=%lld, M=%lld, dtype %d)",
                 (long long)D, (long long)M, dtype);
+  if ((s = need_vec16({q, k, v, out, dout, den, dq, dk, dv}, "polynomial backward"))) return s;
   if (N * D * 2 >= (int64_t(1) << 31)) return fail(LA_ERR_UNSUPPORTED, "head too large for 32-bit offsets");
   const int64_t BH = B * H;
   if (BH * ((N + 63) / 64) > 0xffffffffLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
@@ -910,6 +958,7 @@ LA_API la_status la_poly_prefix_state(const void* k, const void* v, float* S, fl
   if (!la::poly_supported(D, M, dtype))
     return fail(LA_ERR_UNSUPPORTED, "polynomial kernels take bf16 with D = M in {64, 128} (D=%lld, M=%lld, dtype %d)",
                 (long long)D, (long long)M, dtype);
+  if ((s = need_vec16({k, v}, "polynomial prefix state"))) return s;
   if (N * D * 2 >= (int64_t(1) << 31)) return fail(LA_ERR_UNSUPPORTED, "head too large for 32-bit offsets");
   const int64_t BH = B * H;
   if (BH * D * (D / 64) > 0xffffffffLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
@@ -953,6 +1002,7 @@ LA_API la_status la_softmax_forward(const void* q, const void* k, const void* v,
   if (!la::softmax_supported(D, M, dtype))
     return fail(LA_ERR_UNSUPPORTED, "softmax kernels take bf16 with D = M in {64, 128} (D=%lld, M=%lld, dtype %d)",
                 (long long)D, (long long)M, dtype);
+  if ((s = need_vec16({q, k, v, out}, "softmax forward"))) return s;
   if (N * D * 2 >= (int64_t(1) << 31)) return fail(LA_ERR_UNSUPPORTED, "head too large for 32-bit offsets");
   const int64_t BH = B * H;
   if (BH * ((N + 127) / 128) > 0xffffffffLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
@@ -1052,7 +1102,7 @@ LA_API la_status la_prefix_state(const void* k, const void* v, float* S, float* 
   const Span outs[] = {span("S", S, BH * D * M, 4), span("Z", Z, BH * D, 4)};
   if ((s = check_disjoint(outs, 2, ins, 3))) return s;
   Plan p;
-  if ((s = resolve(LA_OP_PREFIX_STATE, B, H, N, D, M, 1, dtype, nullptr, &p))) return s;
+  if ((s = resolve(LA_OP_PREFIX_STATE, B, H, N, D, M, 1, dtype, nullptr, &p, vec16({k, v})))) return s;
   const WsLayout w = layout(LA_OP_PREFIX_STATE, BH, N, D, M, 1, p);
   if (workspace_bytes < w.bytes)
     return fail(LA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, w.bytes);

@@ -233,3 +233,61 @@ def test_saved_state_arguments_are_validated(lib):
 
     assert bwd(ssz=need - 4) == 1 and b"saved too small" in lib.la_last_error()
     assert bwd(dq=S) == 1 and b"overlaps input saved" in lib.la_last_error()
+
+
+@nogpu
+def test_misaligned_tensors_leave_the_mfma_kernels(lib):
+    # The MFMA kernels move q, k, v, out, dout, dq, dk, dv in 16-byte vectors.
+    # A bf16 pointer that is only 2-byte aligned is valid, but on the
+    # automatic plan it must run the generic kernels (cut into the same
+    # segments), and a plan that forces the MFMA kernels is refused.  The
+    # routing shows in the workspace a backward asks for: the MFMA sweeps also
+    # pass c_i between them (one float per row), the generic ones do not.
+    E = 0x50000000
+    F = 0x60000000
+    G = 0x70000000
+    H_ = 0x80000000
+    W = 0xB0000000
+    N = 256
+    mf = lib.la_workspace_bytes(1, 1, 1, N, 64, 64, 1, 1)  # sizes assume aligned pointers: MFMA
+    generic_need = mf - N * 4
+
+    def bwd(q=A, dv=H_, plan=None):
+        return lib.la_backward_ex(q, Bp, C, Dp, E, None, None, 0, F, G, dv, 1, 1, N, 64, 64, 1, 1, W, 64,
+                                  None, None if plan is None else ctypes.byref(plan))
+
+    assert bwd() == 1 and f"{mf} needed".encode() in lib.la_last_error()
+    assert bwd(q=A + 2) == 1 and f"{generic_need} needed".encode() in lib.la_last_error()
+    assert bwd(dv=H_ + 8) == 1 and f"{generic_need} needed".encode() in lib.la_last_error()
+    # the workspace the sizing query reports covers the routed call too
+    assert generic_need <= mf
+    forced = _native.la_plan(0, 0, 2)
+    assert bwd(q=A + 2, plan=forced) == 2 and b"16-byte" in lib.la_last_error()
+
+    def fwd(q=A, out=Dp, plan=None):
+        return lib.la_forward_ex(q, Bp, C, out, 1, 1, N, 64, 64, 1, 1, None, None, 0, None, 0, None,
+                                 None if plan is None else ctypes.byref(plan))
+
+    assert fwd(out=Dp + 2, plan=forced) == 2 and b"16-byte" in lib.la_last_error()
+    # odd addresses stay invalid for bf16 (element alignment)
+    assert fwd(q=A + 1) == 1 and b"aligned" in lib.la_last_error()
+
+
+@nogpu
+def test_families_without_generic_kernels_need_16_byte_alignment(lib):
+    E = 0x50000000
+    F = 0x60000000
+    G = 0x70000000
+    H_ = 0x80000000
+    L = 0x90000000
+    N = 256
+    assert lib.la_poly_forward(A + 2, Bp, C, Dp, None, 1, 1, N, 64, 64, 1, 1, None) == 2
+    assert b"16-byte" in lib.la_last_error()
+    assert lib.la_softmax_forward(A, Bp, C, Dp + 2, None, 1, 1, N, 64, 64, 1, 1, None) == 2
+    assert b"16-byte" in lib.la_last_error()
+    assert lib.la_retention_forward(A, Bp + 2, C, L, Dp, 1, 1, N, 64, 64, 1, None, None, None, 0, None, 0,
+                                    None) == 2
+    assert b"16-byte" in lib.la_last_error()
+    assert lib.la_poly_backward(A, Bp, C, Dp, E, L, F + 2, G, H_, 1, 1, N, 64, 64, 1, 1, 0xB0000000, 1 << 20,
+                                None) == 2
+    assert b"16-byte" in lib.la_last_error()

@@ -92,6 +92,24 @@ def test_retention_full_reset_gates():
     check(y, ref, "full resets")
 
 
+@pytest.mark.parametrize("N", [300, 3000])
+def test_retention_forward_without_state_output(N):
+    # S0 given, no S_out: the segment pass skips the last segment, and with a
+    # single segment it is not launched (the scan writes S0 into the record);
+    # the output must equal the call that also returns the state, bit for bit
+    B, H, D = 1, 2, 64
+    tq, tk, tv, _, tl = case(B, H, N, D, seed=N + 7)
+    assert (la.resolve_plan("retention_forward", B, H, N, D, D, True, "bf16")["segments"] == 1) == (N == 300)
+    S0 = torch.tensor(np.random.default_rng(N).standard_normal((B, H, D, D)) * 0.3, dtype=torch.float32,
+                      device=DEV)
+    want, _ = la.retention_forward(tq, tk, tv, tl, S0=S0, return_state=True)
+    got = la.retention_forward(tq, tk, tv, tl, S0=S0)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    ref, _ = ret.recurrent(f64(tq), f64(tk), f64(tv), f64(tl), f64(S0))
+    check(got, ref, f"forward without S_out N={N}")
+
+
 def test_retention_state_continues_and_updates_in_place():
     tq, tk, tv, _, tl = case(2, 2, 900, 64, seed=23)
     a = 371

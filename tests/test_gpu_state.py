@@ -160,15 +160,18 @@ def test_state_updated_in_place_and_decode_handoff():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_forward_state_without_state_outputs(dtype):
+@pytest.mark.parametrize("N,one_segment", [(2000, False), (200, True)])
+def test_forward_state_without_state_outputs(dtype, N, one_segment):
     # la_forward_state with S_out = Z_out = NULL: the segment pass then skips
-    # the last segment (its aggregate would only feed the total); the output
-    # must equal the call that also returns the state, bit for bit
-    B, H, N, D, M = 2, 3, 2000, 64, 64
+    # the last segment (its aggregate would only feed the total), and with a
+    # single segment it is not launched at all (the scan writes S0, Z0 into
+    # the record); the output must equal the call that also returns the
+    # state, bit for bit
+    B, H, D, M = 2, 3, 64, 64
     tq, tk, tv, _, S0, Z0 = case(B, H, N, D, M, dtype, seed=9, prefix=100)
     tS0 = torch.tensor(S0, dtype=torch.float32, device=DEV)
     tZ0 = torch.tensor(Z0, dtype=torch.float32, device=DEV)
-    assert la.resolve_plan("forward_state", B, H, N, D, M, True, dtype)["segments"] > 1
+    assert (la.resolve_plan("forward_state", B, H, N, D, M, True, dtype)["segments"] == 1) == one_segment
     want, _, _ = la.forward_state(tq, tk, tv, tS0, tZ0)
     lib = la._native.load()
     out = torch.empty_like(tv)
