@@ -184,8 +184,8 @@ def test_fwd_f32_workload():
 
 def boundary_rows(N, seg_len, chunk=64):
     """Rows on either side of every segment boundary and of a spread of chunk
-    boundaries (where the carried state changes hands), plus the ends."""
-    rows = {0, 1, N - 2, N - 1}
+    boundaries, where the carried state changes hands."""
+    rows = set()
     for b in range(seg_len, N, seg_len):
         rows.update((b - 2, b - 1, b, b + 1))
     for b in range(chunk, N, max(chunk, N // 24 // chunk * chunk)):
@@ -194,18 +194,24 @@ def boundary_rows(N, seg_len, chunk=64):
 
 
 def check_rows(name, got, ref, rows, bar):
-    """Per-row rel-L2 on the given rows of [heads, N, F] arrays: each row
-    within `bar`, and their mean within 4x the mean bf16 rounding of the
-    exact rows (the full-tensor bound, applied where a bug in the hand-over
-    of a carried state would concentrate)."""
-    g, r = got[:, rows], ref[:, rows]
-    nr = np.linalg.norm(r, axis=-1)
-    e = np.linalg.norm(g - r, axis=-1) / nr
-    rr = torch.from_numpy(r).float().to(torch.bfloat16).double().numpy()
-    f = np.linalg.norm(rr - r, axis=-1) / nr
-    say(f"  {name}: {e.size} boundary rows, worst {e.max():.2e} mean {e.mean():.2e} (bf16 rounding mean {f.mean():.2e})")
-    assert e.max() < bar, (name, float(e.max()))
-    assert e.mean() < 4.0 * f.mean(), (name, float(e.mean()), float(f.mean()))
+    """Rows next to segment and chunk boundaries, where a mistake in handing
+    over a carried state would concentrate, against the other rows of the
+    same heads.  A row's error is taken relative to its own norm, floored at
+    a quarter of the head's RMS row norm (rows whose exact value happens to
+    be small are not inflated).  The boundary rows' mean error must be
+    within 1.5x the other rows' mean, and their worst within 2x the other
+    rows' worst (or `bar`): one wrong row per segment already moves the
+    mean over a few hundred boundary rows past that."""
+    rms = np.sqrt(np.mean(np.sum(ref * ref, axis=-1), axis=-1, keepdims=True))
+    nr = np.maximum(np.linalg.norm(ref, axis=-1), 0.25 * rms)
+    e_all = np.linalg.norm(got - ref, axis=-1) / nr
+    inner = np.ones(ref.shape[-2], dtype=bool)
+    inner[rows] = False
+    e, e_in = e_all[:, rows], e_all[:, inner]
+    say(f"  {name}: {e.size} boundary rows, mean {e.mean():.2e} worst {e.max():.2e}; other rows mean "
+        f"{e_in.mean():.2e} worst {e_in.max():.2e}")
+    assert e.mean() < 1.5 * e_in.mean(), (name, float(e.mean()), float(e_in.mean()))
+    assert e.max() < max(bar, 2.0 * e_in.max()), (name, float(e.max()), float(e_in.max()))
 
 
 def test_fwdbwd_bf16_workload():
