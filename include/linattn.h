@@ -125,6 +125,27 @@ la_status la_forward_ex(const void* q, const void* k, const void* v, void* out,
                         void* workspace, size_t workspace_bytes, hipStream_t stream,
                         const la_plan* plan);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): la_forward
+ * with no workspace argument.  The segment records it needs live in a static
+ * device array of the library, 64 MiB (67108864 bytes) per GPU, held from the
+ * first call on that GPU until the process ends; the call allocates nothing
+ * and calls no allocating routine.  Same arguments, plan, kernels and results
+ * (bit for bit) as la_forward; the scratch it needs is la_workspace_bytes
+ * (LA_OP_FORWARD, ...) bytes, and a call needing more than 64 MiB returns
+ * LA_ERR_UNSUPPORTED before any HIP call (with the automatic plan a causal
+ * call needs at most about 34 MB: 512 segment records of D*M + D floats).
+ * Nothing in the scratch needs to start at zero.  All calls on one GPU share
+ * its array and it keeps the last call's contents: calls that overlap on one
+ * GPU (concurrent streams, or several host threads) race and must be
+ * serialised by the caller.  `stream` must belong to the calling thread's
+ * current device (LA_ERR_DEVICE otherwise); the array's address on a device
+ * is looked up once, on that device's first call (a call that is being
+ * captured into a graph should not be a device's first). */
+la_status la_forward_noalloc(const void* q, const void* k, const void* v, void* out,
+                             int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                             int causal, int dtype, float* den_out, hipStream_t stream);
+
 /* Bytes of the `saved` record of la_forward_ex for these sizes and plan (0
  * when there is nothing to keep: causal with a single segment). */
 size_t la_saved_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,

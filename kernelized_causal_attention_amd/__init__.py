@@ -18,7 +18,7 @@ from . import _native
 from ._native import LinAttnError, la_plan  # noqa: F401
 
 __all__ = [
-    "forward", "backward", "forward_state", "backward_state", "decode_step", "prefix_state", "workspace_bytes",
+    "forward", "forward_noalloc", "backward", "forward_state", "backward_state", "decode_step", "prefix_state", "workspace_bytes",
     "saved_bytes", "resolve_plan", "retention_forward", "retention_backward", "retention_decode_step",
     "retention_saved_bytes", "poly_forward", "poly_backward", "poly_prefix_state", "poly_decode_step",
     "softmax_forward", "softmax_decode_step",
@@ -163,6 +163,29 @@ def forward(q, k, v, causal: bool = True, return_den: bool = False, plan=None, s
                                     int(bool(causal)), dt, _ptr(den), _ptr(saved), ssz, _ptr(ws), wsz,
                                     _stream(stream), _plan_ref(p)))
     return (out, den) if return_den else out
+
+
+def forward_noalloc(q, k, v, causal: bool = True, out=None, den=None, stream=None):
+    """forward() through la_forward_noalloc: the library's static device
+    scratch replaces the workspace.  `out` (and `den`, when the row
+    denominators are wanted) must be given: nothing is allocated, here or in
+    the library.  Calls that overlap on one GPU share the scratch and race."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        if t is None:
+            raise ValueError(f"{n} must be given")
+        _dev(t, n)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3] or out.shape != v.shape:
+        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)} out{tuple(out.shape)}")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype):
+        raise TypeError("q, k, v, out must share one dtype")
+    B, H, N, D = q.shape
+    M = v.shape[3]
+    if den is not None:
+        _dev(den, "den")
+    _native.check(_native.load().la_forward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B,
+                                                    H, N, D, M, int(bool(causal)), _dtype_code(q), _ptr(den),
+                                                    _stream(stream)))
+    return out
 
 
 def backward(q, k, v, out, dout, den=None, causal: bool = True, plan=None, stream=None,

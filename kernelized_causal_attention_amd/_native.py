@@ -35,6 +35,7 @@ EXPORTS = (
     "la_poly_decode_step",
     "la_softmax_forward",
     "la_softmax_decode_step",
+    "la_forward_noalloc",
 )
 
 
@@ -74,6 +75,7 @@ def load() -> ctypes.CDLL:
     sigs = {
         "la_forward": (fwd, i32),
         "la_forward_ex": (fwd[:12] + [fp, sz] + fwd[12:] + [plan_p], i32),
+        "la_forward_noalloc": (fwd[:12] + [vp], i32),
         "la_backward": (bwd, i32),
         "la_backward_ex": (bwd[:6] + [fp, sz] + bwd[6:] + [plan_p], i32),
         "la_saved_bytes": ([i64, i64, i64, i64, i64, i32, i32, plan_p], sz),

@@ -363,6 +363,48 @@ const char* kname(int kernel, const char* generic_name, const char* mfma_name) {
 
 }  // namespace
 
+// ======================================================= static scratch ====
+// For callers that cannot allocate (graph capture, tight serving loops):
+// la_forward_noalloc keeps its segment records in this file-scope device
+// array instead of a caller workspace.  Every GPU the library runs on holds
+// its own copy until the process ends; its address on each device is taken
+// once, with that device current, and kept.  In host code `scratch` names a
+// host-side stand-in, never the device memory: only the kept address is
+// passed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// The scratch address on the device `stream` runs on (which must be the
+// calling thread's current device).
+hipError_t scratch_for_stream(hipStream_t stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  if (stream) {
+    hipDevice_t sd = 0;
+    if ((e = hipStreamGetDevice(stream, &sd)) != hipSuccess) return e;
+    if (sd != cur) return hipErrorInvalidDevice;
+  }
+  if (cur < 0 || cur >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_addr[cur]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[cur] = p;
+  }
+  *out = g_scratch_addr[cur];
+  return hipSuccess;
+}
+
+}  // namespace
+
 // ============================================================ dispatch ====
 namespace {
 
@@ -453,7 +495,7 @@ la_status check_state(const StateArgs& st, int64_t BH, int64_t D, int64_t M, Spa
 la_status do_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H, int64_t N,
                      int64_t D, int64_t M, int causal, int dtype, float* den_out, float* saved,
                      size_t saved_bytes, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                     const la_plan* plan, const StateArgs& st = StateArgs()) {
+                     const la_plan* plan, const StateArgs& st = StateArgs(), bool static_scratch = false) {
   la_status s = check_sizes(B, H, N, D, M, dtype);
   if (s != LA_OK) return s;
   causal = causal ? 1 : 0;
@@ -484,6 +526,18 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
   if ((s = check_disjoint(outs, 5, ins, 6))) return s;
   if (st.S_out == st.S0 && st.S0 && (s = check_disjoint(&outs[0], 3, &sspan[0], 2))) return s;
   const WsLayout w = layout(st.on ? LA_OP_FORWARD_STATE : LA_OP_FORWARD, BH, N, D, M, causal, p);
+  if (static_scratch) {
+    // the library's static device scratch stands in for the workspace
+    if (w.bytes > kScratchBytes)
+      return fail(LA_ERR_UNSUPPORTED,
+                  "this call needs %zu bytes of scratch; the static scratch holds %zu (call la_forward with a "
+                  "workspace instead)", w.bytes, kScratchBytes);
+    if (w.bytes) {
+      hipError_t e0 = scratch_for_stream(stream, &workspace);
+      if (e0 != hipSuccess) return dev(e0, "static scratch");
+      workspace_bytes = kScratchBytes;
+    }
+  }
   if (workspace_bytes < w.bytes)
     return fail(LA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, w.bytes);
   if (w.bytes && !workspace) return fail(LA_ERR_INVALID, "workspace is NULL (%zu bytes needed)", w.bytes);
@@ -687,6 +741,13 @@ LA_API la_status la_forward_ex(const void* q, const void* k, const void* v, void
                                hipStream_t stream, const la_plan* plan) {
   return do_forward(q, k, v, out, B, H, N, D, M, causal, dtype, den_out, saved, saved_bytes, workspace,
                     workspace_bytes, stream, plan);
+}
+
+LA_API la_status la_forward_noalloc(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
+                                    int64_t N, int64_t D, int64_t M, int causal, int dtype, float* den_out,
+                                    hipStream_t stream) {
+  return do_forward(q, k, v, out, B, H, N, D, M, causal, dtype, den_out, nullptr, 0, nullptr, 0, stream, nullptr,
+                    StateArgs(), true);
 }
 
 LA_API la_status la_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,

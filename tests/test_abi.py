@@ -291,3 +291,14 @@ def test_families_without_generic_kernels_need_16_byte_alignment(lib):
     assert lib.la_poly_backward(A, Bp, C, Dp, E, L, F + 2, G, H_, 1, 1, N, 64, 64, 1, 1, 0xB0000000, 1 << 20,
                                 None) == 2
     assert b"16-byte" in lib.la_last_error()
+
+
+@nogpu
+def test_noalloc_forward_rejects_calls_beyond_its_scratch(lib):
+    # la_forward_noalloc keeps its segment records in a 64 MiB static device
+    # array; a call that needs more is refused before any HIP call
+    B, H, N, D = 4, 256, 64, 128
+    assert lib.la_workspace_bytes(0, B, H, N, D, D, 0, 1) > 64 << 20
+    st = lib.la_forward_noalloc(A, Bp, C, Dp, B, H, N, D, D, 0, 1, None, None)
+    assert st == 2 and b"static scratch" in lib.la_last_error()
+    assert lib.la_forward_noalloc(None, Bp, C, Dp, 1, 1, 8, 4, 4, 1, 0, None, None) == 1
