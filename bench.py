@@ -98,6 +98,9 @@ def parse():
     ap.add_argument("--pmc-calib", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="with --pmc-summary: FETCH_SIZE / WRITE_SIZE of --calibrate-copy, to scale those "
                          "counters to bytes")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="summarise a rocprofv3 --kernel-trace kernel_trace CSV: per library kernel and grid "
+                         "size, calls, average / min / max duration and the kernel's registers and LDS, then exit")
     ap.add_argument("--pmc-out", help="with --pmc-summary: write the table here (default: stdout)")
     ap.add_argument("--pmc-title", default="", help="with --pmc-summary: the table's first comment line")
     ap.add_argument("--pmc-command", action="append", default=[],
@@ -330,6 +333,9 @@ def main():
         sys.exit(2)
     if args.pmc_summary:
         pmc_summary(args)
+        return
+    if args.trace_summary:
+        trace_summary(args)
         return
     if args.ceilings:
         r = subprocess.run([CEILING_EXE])
@@ -629,6 +635,34 @@ def launch_name(kernel_symbol):
         if kernel_symbol.startswith(sym):
             return name
     return None
+
+
+def trace_summary(args):
+    """Markdown table of the library's kernels in a rocprofv3 kernel trace:
+    one row per kernel template instance and grid size (the grid tells the
+    workloads apart), with durations in microseconds and the resources the
+    trace records per dispatch (VGPRs, accumulation VGPRs, LDS bytes)."""
+    import collections
+    import csv
+    import re
+
+    rows = collections.defaultdict(list)
+    res = {}
+    for r in csv.DictReader(open(args.trace_summary)):
+        m = re.search(r"(?<![A-Za-z0-9_])(k_[A-Za-z0-9_]+(<[^()]*>)?)", r["Kernel_Name"])
+        if not m:
+            continue
+        key = (m.group(1), int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]), int(r["Workgroup_Size_X"]))
+        rows[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        res[key] = (r.get("VGPR_Count", ""), r.get("Accum_VGPR_Count", ""), r.get("LDS_Block_Size", ""))
+    out = ["| kernel | workgroups x threads | calls | average (us) | min (us) | max (us) | VGPR | AGPR | LDS (bytes) |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for key in sorted(rows, key=lambda k: -sum(rows[k])):
+        v = rows[key]
+        vg, ag, lds = res[key]
+        out.append(f"| {key[0]} | {key[1]} x {key[2]} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | "
+                   f"{max(v):.1f} | {vg} | {ag} | {lds} |")
+    print("\n".join(out))
 
 
 def pmc_summary(args):
