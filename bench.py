@@ -168,6 +168,10 @@ def kernel_bytes(name: str, B, H, N, D, M, es, P=1):
     if family == "mfma" and base == "bwd_dq":
         # reads q, k, v, dout; writes dq and the per-row (c, den) pair
         return ht * (es * (2 * D + 2 * M) + es * D + 8)
+    if family == "mfma" and base == "bwd_fused":
+        # reads q, k, v, dout once (the reverse sweep's re-reads are the same
+        # tensors); writes dq, dk, dv; writes and reads back (c, den)
+        return ht * (es * (2 * D + 2 * M) + es * (2 * D + M) + 16)
     if family == "mfma" and base == "bwd_dkdv":
         # reads q, k, v, dout and (c, den); writes dk, dv
         return ht * (es * (2 * D + 2 * M) + 8 + es * (D + M))
@@ -553,7 +557,7 @@ COUNTERS_FILE_F32 = os.path.join(PROFILES, "counters_fwd_f32.txt")
 
 # HIP kernel symbols -> the library's launch names (la_profile_* names)
 KERNEL_SYMBOLS = [
-    ("k_bwd_dkdv_mfma", "mfma.bwd_dkdv"), ("k_bwd_dq_mfma", "mfma.bwd_dq"), ("k_bwd_ragg_mfma", "mfma.bwd_dq"),
+    ("k_bwd_fused_mfma", "mfma.bwd_fused"), ("k_fill_u32", "mfma.bwd_fused"), ("k_bwd_dkdv_mfma", "mfma.bwd_dkdv"), ("k_bwd_dq_mfma", "mfma.bwd_dq"), ("k_bwd_ragg_mfma", "mfma.bwd_dq"),
     ("k_fwd_f32mfma", "mfma.forward"), ("k_fwd_mfma", "mfma.forward"), ("k_seg_state_wave64", "mfma.seg_state"),
     ("k_seg_state_f32mfma", "mfma.seg_state"), ("k_seg_state_mfma", "mfma.seg_state"), ("k_seg_scan", "seg_scan"),
     ("k_decode_vec", "decode"), ("k_ret_fwd_mfma", "ret.forward"), ("k_ret_seg_wave64", "ret.seg_state"),

@@ -82,8 +82,16 @@ typedef enum la_op {
   LA_OP_POLY_BACKWARD = 8       /* la_poly_backward      */
 } la_op;
 
-/* Kernel family choice for the *_ex entry points (0 = automatic). */
-typedef enum la_kernel { LA_KERNEL_AUTO = 0, LA_KERNEL_GENERIC = 1, LA_KERNEL_MFMA = 2 } la_kernel;
+/* Kernel family choice for the *_ex entry points (0 = automatic).
+ * LA_KERNEL_MFMA_ONE_LAUNCH: the MFMA kernels, with the causal bf16
+ * backward at D = M = 64 as one launch (see la_backward_ex); elsewhere the
+ * same as LA_KERNEL_MFMA. */
+typedef enum la_kernel {
+  LA_KERNEL_AUTO = 0,
+  LA_KERNEL_GENERIC = 1,
+  LA_KERNEL_MFMA = 2,
+  LA_KERNEL_MFMA_ONE_LAUNCH = 3
+} la_kernel;
 
 /* Tuning plan.  Every field 0 means "let the library choose".
  *   chunk    -- tokens per intra-chunk tile (generic: 16/32/64; MFMA: 64)
@@ -169,8 +177,16 @@ la_status la_backward(const void* q, const void* k, const void* v, const void* o
                       int causal, int dtype,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* As la_backward, with a tuning plan (NULL = automatic) and `saved`, the
- * record la_forward_ex left for the same q, k, v, sizes, causal, dtype and
+/* As la_backward, with a tuning plan (NULL = automatic) and `saved` (below).
+ * With plan kernel LA_KERNEL_MFMA_ONE_LAUNCH the causal bf16 MFMA backward at
+ * D = M = 64 runs as one launch when its grid fits on the device at once:
+ * each workgroup sweeps its segment forwards (dq), hands its suffix
+ * aggregate to the workgroups of the earlier segments through flags in the
+ * workspace and sweeps the same segment backwards (dk, dv) from the later
+ * segments' aggregates; results are those of the default two launches, bit
+ * for bit (measured slower on MI355X: the default stays two launches).  A
+ * hand-off that times out is reported by la_device_error.
+ * `saved`: the record la_forward_ex left for the same q, k, v, sizes, causal, dtype and
  * plan, or NULL.  With it the prefix states S, Z are read instead of being
  * recomputed (a pass over k and v and a scan fewer).  LA_ERR_INVALID if
  * saved_bytes is short of la_saved_bytes() or the forward and backward
@@ -401,6 +417,16 @@ la_status la_profile_select(const char* names);
 const char* la_status_str(int status);
 /* Detail of the last non-OK status returned on this thread ("" if none). */
 const char* la_last_error(void);
+
+/* Synchronises `stream` and reports (then clears) an error a kernel of this
+ * library recorded on the stream's device: LA_ERR_DEVICE when a bounded wait
+ * of one workgroup for another's result ran out.  The one kernel that waits
+ * so, the one-launch causal backward (see la_backward), is launched only
+ * when its whole grid fits on the device at once, and every workgroup only
+ * waits for workgroups dispatched before it; should a wait still run out
+ * (after 0.5 s), that workgroup writes NaN into its dk, dv rows, sets the
+ * error and finishes normally. */
+la_status la_device_error(hipStream_t stream);
 /* Library version, major * 10000 + minor * 100 + patch. */
 int la_version(void);
 

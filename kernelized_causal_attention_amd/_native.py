@@ -18,7 +18,7 @@ LA_OP_FORWARD, LA_OP_BACKWARD, LA_OP_PREFIX_STATE, LA_OP_DECODE = 0, 1, 2, 3
 LA_OP_FORWARD_STATE, LA_OP_BACKWARD_STATE = 4, 5
 LA_OP_RETENTION_FORWARD, LA_OP_RETENTION_BACKWARD = 6, 7
 LA_OP_POLY_BACKWARD = 8
-LA_KERNEL_AUTO, LA_KERNEL_GENERIC, LA_KERNEL_MFMA = 0, 1, 2
+LA_KERNEL_AUTO, LA_KERNEL_GENERIC, LA_KERNEL_MFMA, LA_KERNEL_MFMA_ONE_LAUNCH = 0, 1, 2, 3
 
 # Every symbol include/linattn.h declares.
 EXPORTS = (
@@ -36,6 +36,7 @@ EXPORTS = (
     "la_softmax_forward",
     "la_softmax_decode_step",
     "la_forward_noalloc",
+    "la_device_error",
 )
 
 
@@ -101,6 +102,7 @@ def load() -> ctypes.CDLL:
         "la_resolve_plan": ([i32, i64, i64, i64, i64, i64, i32, i32, plan_p, plan_p], i32),
         "la_status_str": ([i32], ctypes.c_char_p),
         "la_last_error": ([], ctypes.c_char_p),
+        "la_device_error": ([vp], i32),
         "la_version": ([], i32),
         "la_profile_enable": ([i32], i32),
         "la_profile_report": ([ctypes.c_char_p, sz], i32),

@@ -58,6 +58,12 @@ hipError_t launch_seg_state_f32mfma(const SegGeom& g, const void* k, const void*
 hipError_t launch_bwd_dq_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
                               const void* dout, const float* carry_s, void* dq, float* r_agg, float* c_out,
                               float* den_out, hipStream_t st);
+int bwd_fused_supported(int causal, int D);
+int64_t bwd_fused_resident(int dim);
+hipError_t launch_bwd_fused_mfma(const SegGeom& g, const void* q, const void* k, const void* v, const void* dout,
+                                 const float* carry_s, void* dq, void* dk, void* dv, float* r_agg, float* c_ws,
+                                 float* den_ws, unsigned* flags, unsigned* err, unsigned want, long long spin_ticks,
+                                 hipStream_t st);
 // carry_raw: carry_r holds the raw suffix aggregates (summed in the kernel)
 // rather than their reverse exclusive scan.
 hipError_t launch_bwd_dkdv_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
@@ -165,6 +171,7 @@ struct Plan {
   int P;         // segments
   int seg_len;   // tokens per segment
   int chunk;     // chunk used by the forward-type kernels (informational)
+  bool one_launch = false;  // the causal MFMA backward as one launch where it can
 };
 
 // vec_ok: every tensor pointer of the call is 16-byte aligned (the sizing
@@ -177,7 +184,10 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                   const la_plan* req, Plan* out, bool vec_ok = true) {
   (void)causal;
   int kernel = req ? req->kernel : LA_KERNEL_AUTO;
-  if (kernel < LA_KERNEL_AUTO || kernel > LA_KERNEL_MFMA) return fail(LA_ERR_INVALID, "plan.kernel=%d", kernel);
+  if (kernel < LA_KERNEL_AUTO || kernel > LA_KERNEL_MFMA_ONE_LAUNCH)
+    return fail(LA_ERR_INVALID, "plan.kernel=%d", kernel);
+  const bool one_launch = kernel == LA_KERNEL_MFMA_ONE_LAUNCH;
+  if (one_launch) kernel = LA_KERNEL_MFMA;
   // the state-carrying and retention calls use the forward / backward plans
   const int op_in = op;
   if (op == LA_OP_FORWARD_STATE || op == LA_OP_RETENTION_FORWARD) op = LA_OP_FORWARD;
@@ -234,6 +244,7 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
   if (BH * P > 0xffffffffLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
   if (seg_len > 0x7fffffffLL) return fail(LA_ERR_UNSUPPORTED, "segment too long");
   out->kernel = kernel;
+  out->one_launch = one_launch;
   out->P = static_cast<int>(P);
   out->seg_len = static_cast<int>(seg_len);
   out->chunk = chunk;
@@ -252,6 +263,7 @@ struct Carve {
 
 struct WsLayout {
   size_t aggS = 0, totS = 0, aggR = 0, totR = 0, den = 0, cvec = 0;
+  size_t flags = 0;             // MFMA backward: one hand-off flag per segment
   size_t anchS = 0, anchY = 0;  // retention backward: states and <S, R> at the inner anchors
   size_t bytes = 0;
 };
@@ -285,7 +297,10 @@ WsLayout layout(int op, int64_t BH, int64_t N, int64_t D, int64_t M, int causal,
     w.aggR = c.take(recs);
     w.totR = c.take(static_cast<size_t>(BH) * E);
     w.den = c.take(static_cast<size_t>(BH) * N);
-    if (p.kernel == LA_KERNEL_MFMA) w.cvec = c.take(static_cast<size_t>(BH) * N);
+    if (p.kernel == LA_KERNEL_MFMA) {
+      w.cvec = c.take(static_cast<size_t>(BH) * N);
+      w.flags = c.take(static_cast<size_t>(BH) * p.P);
+    }
   } else if (op == LA_OP_PREFIX_STATE) {
     if (p.P > 1) w.aggS = c.take(recs);
   }
@@ -379,10 +394,19 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_addr[kMaxDevices] = {};
+void* g_err_addr[kMaxDevices] = {};
 
-// The scratch address on the device `stream` runs on (which must be the
-// calling thread's current device).
-hipError_t scratch_for_stream(hipStream_t stream, void** out) {
+}  // namespace
+
+// Set by a kernel whose bounded cross-workgroup wait ran out (the fused
+// backward's hand-off); read and cleared by la_device_error.  As with
+// `scratch`, host code uses only the address taken on each device.
+static __device__ __align__(16) unsigned int dev_err_word[4];
+
+namespace {
+
+// The device `stream` runs on, which must be the calling thread's current one.
+hipError_t stream_device(hipStream_t stream, int* out) {
   int cur = 0;
   hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return e;
@@ -392,6 +416,15 @@ hipError_t scratch_for_stream(hipStream_t stream, void** out) {
     if (sd != cur) return hipErrorInvalidDevice;
   }
   if (cur < 0 || cur >= kMaxDevices) return hipErrorInvalidDevice;
+  *out = cur;
+  return hipSuccess;
+}
+
+// The scratch address on the device `stream` runs on.
+hipError_t scratch_for_stream(hipStream_t stream, void** out) {
+  int cur = 0;
+  hipError_t e = stream_device(stream, &cur);
+  if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lk(g_scratch_mu);
   if (!g_scratch_addr[cur]) {
     void* p = nullptr;
@@ -401,6 +434,42 @@ hipError_t scratch_for_stream(hipStream_t stream, void** out) {
   }
   *out = g_scratch_addr[cur];
   return hipSuccess;
+}
+
+// The device error word's address on the device `stream` runs on.
+hipError_t err_word_for_stream(hipStream_t stream, unsigned** out) {
+  int cur = 0;
+  hipError_t e = stream_device(stream, &cur);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_err_addr[cur]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(dev_err_word))) != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_err_addr[cur] = p;
+  }
+  *out = static_cast<unsigned*>(g_err_addr[cur]);
+  return hipSuccess;
+}
+
+// Bound of a cross-workgroup wait in the device's real-time counter ticks
+// (0.5 s; the counter rate is queried once per device).  LA_HANDOFF_TEST=1
+// in the environment makes the fused backward wait for a flag value that is
+// never published, with a 20 us bound, so that tests can exercise the
+// timeout path (every workgroup still runs to its end).
+long long handoff_ticks(int dev, bool test_mode) {
+  static int rate_khz[kMaxDevices] = {};
+  int r = rate_khz[dev];
+  if (r <= 0) {
+    if (hipDeviceGetAttribute(&r, hipDeviceAttributeWallClockRate, dev) != hipSuccess || r <= 0) r = 100000;
+    rate_khz[dev] = r;
+  }
+  return test_mode ? static_cast<long long>(r) / 50 : static_cast<long long>(r) * 500;
+}
+
+bool handoff_test_mode() {
+  const char* v = getenv("LA_HANDOFF_TEST");
+  return v && v[0] == '1';
 }
 
 }  // namespace
@@ -674,6 +743,31 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
   // (it reads neither out nor den) and passes den and c to the reverse sweep
   // through the workspace.
   float* cw = at(workspace, w.cvec);
+  if (p.kernel == LA_KERNEL_MFMA && p.one_launch && causal && !st.on && dtype == LA_BF16 &&
+      la::bwd_fused_supported(causal, D)) {
+    // one launch: the forward sweep, the hand-off of the suffix aggregates
+    // and the reverse sweep (bit for bit the two-launch result), when every
+    // workgroup of the grid can be resident at once.  Not the default: on
+    // the B=8 H=16 N=8192 D=64 step it measured 0.33-0.36 ms against
+    // 0.30 ms for the two launches (the agent-scope fences of the hand-off
+    // cost more than the reverse sweep saves by re-reading from the cache).
+    const int64_t resident = la::bwd_fused_resident(static_cast<int>(D));
+    if (resident >= BH * p.P) {
+      int devno = 0;
+      unsigned* errw = nullptr;
+      if ((e = stream_device(stream, &devno)) || (e = err_word_for_stream(stream, &errw)))
+        return dev(e, "backward hand-off set-up");
+      const bool test = handoff_test_mode();
+      float* dw = at(workspace, w.den);
+      return dev(timed("mfma.bwd_fused", stream,
+                       [&] {
+                         return la::launch_bwd_fused_mfma(g, q, k, v, dout, carry_s, dq, dk, dv, aggR, cw, dw,
+                                                          reinterpret_cast<unsigned*>(at(workspace, w.flags)), errw,
+                                                          test ? 2u : 1u, handoff_ticks(devno, test), stream);
+                       }),
+                 "backward (one launch)");
+    }
+  }
   if (p.kernel == LA_KERNEL_MFMA) {
     float* dw = at(workspace, w.den);
     e = timed("mfma.bwd_dq", stream,
@@ -1238,6 +1332,20 @@ LA_API const char* la_status_str(int status) {
 }
 
 LA_API const char* la_last_error(void) { return g_err.c_str(); }
+
+LA_API la_status la_device_error(hipStream_t stream) {
+  unsigned* addr = nullptr;
+  hipError_t e = err_word_for_stream(stream, &addr);
+  if (e != hipSuccess) return dev(e, "device error word");
+  if ((e = hipStreamSynchronize(stream)) != hipSuccess) return dev(e, "stream synchronize");
+  unsigned word = 0;
+  if ((e = hipMemcpy(&word, addr, sizeof word, hipMemcpyDeviceToHost)) != hipSuccess) return dev(e, "read error word");
+  if (!word) return ok();
+  const unsigned zero = 0;
+  if ((e = hipMemcpy(addr, &zero, sizeof zero, hipMemcpyHostToDevice)) != hipSuccess) return dev(e, "clear error word");
+  return fail(LA_ERR_DEVICE, "a workgroup's bounded wait for another workgroup's result ran out; the outputs "
+              "of that call hold NaN where it gave up");
+}
 
 LA_API int la_version(void) { return 100; }
 

@@ -24,6 +24,8 @@
 // other operand, read with LDS transpose loads), scores are carried as bf16
 // hi + lo pairs, and Z and r are accumulated in fp32 through MFMAs against a
 // ones / c operand.
+#include <algorithm>
+
 #include "la_internal.h"
 #include "la_mfma_common.h"
 
@@ -322,7 +324,8 @@ template <int DIM, bool CAUSAL, bool FUSED_R, int RW>
 __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                         const bf16_t* __restrict__ dout, const float* __restrict__ carry_s,
                                         bf16_t* __restrict__ dq, float* __restrict__ r_agg, float* __restrict__ c_out,
-                                        float* __restrict__ den_out, int64_t N, int P, int seg_len) {
+                                        float* __restrict__ den_out, int64_t N, int P, int seg_len, int64_t bh,
+                                        int seg) {
   using G = Geo<DIM>;
   constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -341,9 +344,7 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
   // MFMA under an EXEC-masked branch still writes every lane.
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int rw = RW;  // query row tile (chosen by k_bwd_dq_mfma)
-  const int64_t bh = blockIdx.x / P;
-  const int seg = blockIdx.x % P;
+  constexpr int rw = RW;  // query row tile (chosen by the calling kernel)
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
   const int64_t r1 = min(N, r0 + seg_len);
   constexpr int64_t ER = static_cast<int64_t>(DIM) * DIM + DIM;  // S, Z (or R, r) record
@@ -572,10 +573,11 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
   if constexpr (FUSED_R) {
     if (want_r) {
       // C = sum of c over the segment's rows (csum is the same in all four
-      // 16-lane groups of a wave: sum over li, then over the waves)
+      // 16-lane groups of a wave: sum over li, then over the row tiles in
+      // their order, whichever wave holds which)
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) csum += __shfl_xor(csum, off, 64);
-      if (l == 0) sRed[w] = csum;
+      if (l == 0) sRed[rw] = csum;
       __syncthreads();
       const float C = sRed[0] + sRed[1] + sRed[2] + sRed[3];
       store_r<DIM>(r_agg + (bh * P + seg) * ER, Racc, racc, gacc, C, w, g, li);
@@ -595,7 +597,10 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   switch ((blockIdx.x & 1) ? 3 - w : w) {
 #define LA_DQ_BODY(RW_) \
-  case RW_: dq_body<DIM, CAUSAL, FUSED_R, RW_>(q, k, v, dout, carry_s, dq, r_agg, c_out, den_out, N, P, seg_len); break
+  case RW_:                                                                                              \
+    dq_body<DIM, CAUSAL, FUSED_R, RW_>(q, k, v, dout, carry_s, dq, r_agg, c_out, den_out, N, P, seg_len,   \
+                                       blockIdx.x / P, static_cast<int>(blockIdx.x % P));                 \
+    break
     LA_DQ_BODY(0);
     LA_DQ_BODY(1);
     LA_DQ_BODY(2);
@@ -668,14 +673,15 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_ragg_mfma(const bf16_t* __restric
 // ---------------------------------------------------------------------------
 // Reverse sweep: dk, dv with the suffix state (R, r) carried in.
 // ---------------------------------------------------------------------------
+// poison: the suffix carry could not be formed (a hand-off that timed out in
+// the fused kernel): the carry is NaN, so every dk, dv row of the segment is.
 template <int DIM, bool CAUSAL>
-__global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                                                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
-                                                      const float* __restrict__ den_in,
-                                                      const float* __restrict__ c_in,
-                                                      const float* __restrict__ carry_r, bf16_t* __restrict__ dk,
-                                                      bf16_t* __restrict__ dv, int64_t N, int P, int seg_len,
-                                                      int carry_raw) {
+__device__ __forceinline__ void dkdv_body(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                          const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
+                                          const float* __restrict__ den_in, const float* __restrict__ c_in,
+                                          const float* __restrict__ carry_r, bf16_t* __restrict__ dk,
+                                          bf16_t* __restrict__ dv, int64_t N, int P, int seg_len, int carry_raw,
+                                          int64_t bh, int seg, int rw, bool poison) {
   using G = Geo<DIM>;
   constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -692,15 +698,10 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
   // MFMA under an EXEC-masked branch still writes every lane.
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // The triangular intra-chunk work grows with a wave's row tile (tile t
-  // does t + 1 key tiles); odd workgroups map wave w to tile 3 - w, so two
-  // workgroups sharing a CU give every SIMD the same total.
-  const int rw = (blockIdx.x & 1) ? 3 - w : w;
+  (void)l;
   // this wave's staging tiles for its dv and dk rows
   uint16_t* sDV = sCh + 2 * T + w * 2 * 16 * LD;
   uint16_t* sDK = sDV + 16 * LD;
-  const int64_t bh = blockIdx.x / P;
-  const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
   const int64_t r1 = min(N, r0 + seg_len);
   constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;  // R, r record
@@ -728,6 +729,15 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
     init_xt_suffix<DIM>(Racc, racc, carry_r + bh * P * E, seg, P, w, g, li);
   else
     init_xt<DIM>(Racc, racc, cr, w, g, li);
+  if (poison) {
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int a = 0; a < DT; ++a) {
+      racc[a] = f32x4_t{nan, nan, nan, nan};
+#pragma unroll
+      for (int n = 0; n < NTL; ++n) Racc[a][n] = racc[a];
+    }
+  }
   write_xt<DIM>(sR, sRv, Racc, racc, w, g, li);
 
   const int64_t nch = (r1 - r0 + T - 1) / T;
@@ -846,6 +856,106 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
   }
 }
 
+template <int DIM, bool CAUSAL>
+__global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
+                                                      const float* __restrict__ den_in,
+                                                      const float* __restrict__ c_in,
+                                                      const float* __restrict__ carry_r, bf16_t* __restrict__ dk,
+                                                      bf16_t* __restrict__ dv, int64_t N, int P, int seg_len,
+                                                      int carry_raw) {
+  // The triangular intra-chunk work grows with a wave's row tile (tile t
+  // does t + 1 key tiles); odd workgroups map wave w to tile 3 - w, so two
+  // workgroups sharing a CU give every SIMD the same total.
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  dkdv_body<DIM, CAUSAL>(q, k, v, dout, den_in, c_in, carry_r, dk, dv, N, P, seg_len, carry_raw, blockIdx.x / P,
+                         static_cast<int>(blockIdx.x % P), (blockIdx.x & 1) ? 3 - w : w, false);
+}
+
+// ---------------------------------------------------------------------------
+// The causal backward in one launch (D = 64): each workgroup runs the
+// forward sweep over its segment (dq, c, den and the segment's (R, r)
+// aggregate), publishes the aggregate, waits for the aggregates of every
+// later segment of its sequence, sums them into its suffix carry (in the
+// reverse-scan order, as the split sweeps do) and runs the reverse sweep
+// over the same segment (dk, dv).  The reverse sweep re-reads the tokens the
+// forward sweep has just read, last chunk first, so most of those reads
+// come from the last-level cache instead of HBM.  Results are bit for bit
+// those of k_bwd_dq_mfma followed by k_bwd_dkdv_mfma.
+//
+// Hand-off.  Workgroup b serves sequence b / P, segment P - 1 - b % P: the
+// later segments of a sequence have the lower workgroup indices, so a
+// workgroup only ever waits for workgroups dispatched before it (which hold
+// their slots and finish without waiting on anything later), and the host
+// launches it only when every workgroup of the grid can be resident at once
+// besides.  flags[bh * P + seg] (cleared before the launch) becomes `want`
+// once the aggregate is in memory: every thread's stores are released at
+// agent scope (written back past this XCD's L2) before a barrier, after which
+// one thread sets the flag with a vector atomic store.  The waiting thread
+// polls the flags with agent-scope atomic loads (sleeping between polls),
+// then every thread acquires at agent scope before reading the records.
+// Each wait is bounded by `spin_ticks` of the 100 MHz real-time counter; a
+// workgroup whose wait runs out sets *err (la_device_error reports it),
+// poisons its dk, dv with NaN and still runs to its end, so the grid always
+// drains.
+// ---------------------------------------------------------------------------
+template <int DIM>
+__global__ __launch_bounds__(NT, 2) void k_bwd_fused_mfma(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, const float* __restrict__ carry_s, bf16_t* __restrict__ dq,
+    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ r_agg, float* __restrict__ c_ws,
+    float* __restrict__ den_ws, unsigned* __restrict__ flags, unsigned* __restrict__ err, unsigned want,
+    long long spin_ticks, int64_t N, int P, int seg_len) {
+  __shared__ int s_ok;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t bh = blockIdx.x / P;
+  const int seg = P - 1 - static_cast<int>(blockIdx.x % P);
+  const int rw = (blockIdx.x & 1) ? 3 - w : w;
+  // segment 0's aggregate would only feed the total, which is not needed
+  float* ragg = seg > 0 ? r_agg : nullptr;
+  switch (rw) {
+#define LA_FUSED_DQ(RW_)                                                                                     \
+  case RW_:                                                                                                  \
+    dq_body<DIM, true, true, RW_>(q, k, v, dout, carry_s, dq, ragg, c_ws, den_ws, N, P, seg_len, bh, seg); \
+    break
+    LA_FUSED_DQ(0);
+    LA_FUSED_DQ(1);
+    LA_FUSED_DQ(2);
+    LA_FUSED_DQ(3);
+#undef LA_FUSED_DQ
+  }
+  // publish this segment's aggregate (and make c, den visible)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (seg > 0) __hip_atomic_store(flags + bh * P + seg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int ok = 1;
+    if (seg + 1 < P) {
+      const long long t0 = static_cast<long long>(wall_clock64());
+      for (int p = P - 1; p > seg && ok; --p) {
+        while (__hip_atomic_load(flags + bh * P + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
+          if (static_cast<long long>(wall_clock64()) - t0 > spin_ticks) {
+            ok = 0;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(4);
+        }
+      }
+      if (!ok) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    s_ok = ok;
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  dkdv_body<DIM, true>(q, k, v, dout, den_ws, c_ws, r_agg, dk, dv, N, P, seg_len, 1, bh, seg, rw, s_ok == 0);
+}
+
+__global__ __launch_bounds__(256) void k_fill_u32(unsigned* __restrict__ p, int64_t n, unsigned val) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = val;
+}
+
 size_t lds_bwd(int dim) {
   return (4 * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t) + (dim + T) * sizeof(float) +
          2 * T * sizeof(uint16_t) + 4 * 2 * 16 * (dim + kLdsPad) * sizeof(uint16_t);  // + output staging
@@ -888,6 +998,45 @@ hipError_t launch_bwd_dq_mfma(int causal, const SegGeom& g, const void* q, const
   LA_MLAUNCH((k_bwd_ragg_mfma<128>), grid, lds_ragg(128), st, static_cast<const bf16_t*>(q),
              static_cast<const bf16_t*>(dout), den_out, c_out, r_agg, g.N, g.P, g.seg_len);
 #undef LA_DQ
+}
+
+int bwd_fused_supported(int causal, int D) { return causal && D == 64; }
+
+size_t lds_bwd_fused(int dim) { return lds_dq(dim) > lds_bwd(dim) ? lds_dq(dim) : lds_bwd(dim); }
+
+// Workgroups of the fused kernel that can be resident at once on this
+// device (0 on error).
+int64_t bwd_fused_resident(int dim) {
+  static int64_t cached[64] = {};  // per device; the answer does not change
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dim != 64) return 0;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_fused_mfma<64>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_bwd_fused(64))) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_bwd_fused_mfma<64>, NT, lds_bwd_fused(64)) != hipSuccess)
+    return 0;
+  const int64_t n = static_cast<int64_t>(per) * cus;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  return n;
+}
+
+hipError_t launch_bwd_fused_mfma(const SegGeom& g, const void* q, const void* k, const void* v, const void* dout,
+                                 const float* carry_s, void* dq, void* dk, void* dv, float* r_agg, float* c_ws,
+                                 float* den_ws, unsigned* flags, unsigned* err, unsigned want, long long spin_ticks,
+                                 hipStream_t st) {
+  if (g.D != 64) return hipErrorNotSupported;
+  const int64_t nflags = g.BH * g.P;
+  hipLaunchKernelGGL(k_fill_u32, dim3(static_cast<unsigned>(std::min<int64_t>((nflags + 255) / 256, 1024))),
+                     dim3(256), 0, st, flags, nflags, 0u);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  LA_MLAUNCH((k_bwd_fused_mfma<64>), g.BH * g.P, lds_bwd_fused(64), st, static_cast<const bf16_t*>(q),
+             static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout),
+             carry_s, static_cast<bf16_t*>(dq), static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), r_agg, c_ws,
+             den_ws, flags, err, want, spin_ticks, g.N, g.P, g.seg_len);
 }
 
 hipError_t launch_bwd_dkdv_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,

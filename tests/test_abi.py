@@ -242,7 +242,8 @@ def test_misaligned_tensors_leave_the_mfma_kernels(lib):
     # automatic plan it must run the generic kernels (cut into the same
     # segments), and a plan that forces the MFMA kernels is refused.  The
     # routing shows in the workspace a backward asks for: the MFMA sweeps also
-    # pass c_i between them (one float per row), the generic ones do not.
+    # pass c_i between them (one float per row) and keep hand-off flags, the
+    # generic ones do not.
     E = 0x50000000
     F = 0x60000000
     G = 0x70000000
@@ -250,7 +251,11 @@ def test_misaligned_tensors_leave_the_mfma_kernels(lib):
     W = 0xB0000000
     N = 256
     mf = lib.la_workspace_bytes(1, 1, 1, N, 64, 64, 1, 1)  # sizes assume aligned pointers: MFMA
-    generic_need = mf - N * 4
+    out = _native.la_plan()
+    assert lib.la_resolve_plan(1, 1, 1, N, 64, 64, 1, 1, None, ctypes.byref(out)) == 0 and out.kernel == 2
+    generic = _native.la_plan(0, out.segments, 1)
+    generic_need = lib.la_workspace_bytes_ex(1, 1, 1, N, 64, 64, 1, 1, ctypes.byref(generic))
+    assert generic_need < mf
 
     def bwd(q=A, dv=H_, plan=None):
         return lib.la_backward_ex(q, Bp, C, Dp, E, None, None, 0, F, G, dv, 1, 1, N, 64, 64, 1, 1, W, 64,

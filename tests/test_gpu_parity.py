@@ -625,3 +625,97 @@ def test_mfma_backward_negative_mean_inputs(D):
     tq, tk, tv, tg = (to_torch(x, "bf16", DEV) for x in (q, k, v, g))
     check_forward(tq, tk, tv, True, "bf16", null_guard=True)
     check_backward(tq, tk, tv, tg, True, "bf16")
+
+
+# ------------------------------------------- one-launch causal backward ---
+FUSED_CASES = [
+    # (B, H, N, segments): one segment (no hand-off), ragged tails, many
+    # segments per sequence, and the benchmark's workload with saved states
+    (2, 3, 1000, 1),
+    (1, 2, 3000, 3),
+    (2, 2, 2113, 7),
+    (1, 1, 8192, 64),
+    (4, 8, 2048, 0),
+]
+
+
+@pytest.mark.parametrize("B,H,N,segments", FUSED_CASES)
+def test_fused_backward_matches_two_launches(B, H, N, segments):
+    # The causal bf16 backward at D = 64 as one launch (forward sweep,
+    # hand-off of the suffix aggregates between the segments' workgroups,
+    # reverse sweep; plan kernel 3) must give the bits of the default two
+    # launches, and both the oracle's gradients.
+    D = 64
+    tq, tk, tv, tg = host_case(B, H, N, D, D, "bf16", seed=N + segments, scale=1.0 / np.sqrt(D))
+    plan = dict(segments=segments) if segments else None
+    one = dict(kernel=3, segments=segments) if segments else dict(kernel=3)
+    out, den = la.forward(tq, tk, tv, return_den=True, plan=plan)
+    la.profile_enable(True)
+    fused = la.backward(tq, tk, tv, out, tg, den=den, plan=one)
+    torch.cuda.synchronize()
+    ran = la.profile_report()
+    la.profile_enable(False)
+    assert "mfma.bwd_fused" in ran and "mfma.bwd_dkdv" not in ran, ran
+    two = la.backward(tq, tk, tv, out, tg, den=den, plan=plan)
+    torch.cuda.synchronize()
+    assert la._native.load().la_device_error(torch.cuda.current_stream().cuda_stream) == 0
+    for n, a, b in zip(("dq", "dk", "dv"), fused, two):
+        assert torch.equal(a, b), n
+    q64, k64, v64, g64 = (f64(t) for t in (tq, tk, tv, tg))
+    rq, rk, rv, _, _ = oracle.backward(q64, k64, v64, g64, True)
+    errs = {n: rel_l2(f64(t), r) for n, t, r in (("dq", fused[0], rq), ("dk", fused[1], rk), ("dv", fused[2], rv))}
+    say(f"one-launch backward {(B, H, N)} P={segments or 'auto'}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e < TOL["bf16"], (n, e)
+
+
+def test_fused_backward_reads_saved_states():
+    # the training step's form: the forward keeps its prefix states and the
+    # one-launch backward reads them; same bits as without them and as the
+    # two launches
+    B, H, N, D = 2, 4, 4096, 64
+    tq, tk, tv, tg = host_case(B, H, N, D, D, "bf16", seed=71, scale=1.0 / np.sqrt(D))
+    nsaved = la.saved_bytes(B, H, N, D, D, True, "bf16")
+    assert nsaved > 0
+    saved = torch.empty(nsaved, dtype=torch.uint8, device=DEV)
+    out, den = la.forward(tq, tk, tv, return_den=True, saved=saved)
+    a = la.backward(tq, tk, tv, out, tg, den=den, saved=saved, plan=dict(kernel=3))
+    b = la.backward(tq, tk, tv, out, tg, den=den, plan=dict(kernel=3))
+    c = la.backward(tq, tk, tv, out, tg, den=den, saved=saved)
+    torch.cuda.synchronize()
+    for x, y, z in zip(a, b, c):
+        assert torch.equal(x, y) and torch.equal(x, z)
+
+
+def test_fused_backward_timeout_path(monkeypatch):
+    # With LA_HANDOFF_TEST=1 every wait of the one-launch backward (plan
+    # kernel 3) is for a flag value nobody publishes, bounded at 20 us: each
+    # workgroup that waits gives up, writes NaN into its dk, dv rows and
+    # finishes; the library reports LA_ERR_DEVICE through la_device_error.
+    # The last
+    # segment of each sequence waits for nothing and is exact, as is dq.
+    B, H, N, D, P = 1, 2, 1024, 64, 4
+    tq, tk, tv, tg = host_case(B, H, N, D, D, "bf16", seed=73, scale=1.0 / np.sqrt(D))
+    plan = dict(segments=P, kernel=3)
+    out, den = la.forward(tq, tk, tv, return_den=True, plan=plan)
+    good = la.backward(tq, tk, tv, out, tg, den=den, plan=plan)
+    torch.cuda.synchronize()
+    lib = la._native.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    assert lib.la_device_error(stream) == 0
+    monkeypatch.setenv("LA_HANDOFF_TEST", "1")
+    bad = la.backward(tq, tk, tv, out, tg, den=den, plan=plan)
+    st = lib.la_device_error(stream)
+    monkeypatch.delenv("LA_HANDOFF_TEST")
+    assert st == la._native.LA_ERR_DEVICE and b"bounded wait" in lib.la_last_error()
+    assert lib.la_device_error(stream) == 0  # cleared
+    seg = N // P
+    assert torch.equal(bad[0], good[0])  # dq comes before the hand-off
+    for t, ref in ((bad[1], good[1]), (bad[2], good[2])):
+        assert torch.isnan(t[:, :, : N - seg]).all()
+        assert torch.equal(t[:, :, N - seg:], ref[:, :, N - seg:])
+    again = la.backward(tq, tk, tv, out, tg, den=den, plan=plan)
+    torch.cuda.synchronize()
+    assert lib.la_device_error(stream) == 0
+    for x, y in zip(again, good):
+        assert torch.equal(x, y)
