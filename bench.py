@@ -971,7 +971,56 @@ def bench_poly(la, torch, steps, warmup):
             "roofline": {"bound": "mfma", "kernel": kname, "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                          "flops_per_launch": kf, "avg_launch_ms": round(avg_ms, 4)},
-            "kernels": kernels, "decode": bench_poly_decode(la, torch)}
+            "kernels": kernels, "decode": bench_poly_decode(la, torch), "crossover": bench_poly_crossover(la, torch)}
+
+
+def bench_poly_crossover(la, torch, B=1, H=16, D=64, M=64):
+    """The degree-2 map's two evaluation orders across sequence lengths (the
+    walkthrough's section 2, 'feature map and computation cost', item (3):
+    the linear form costs N D^2 M, the masked sum N^2 D, so the linear form
+    wins once N is large against D^2).  Timed per call on 16 heads: the
+    masked-sum causal forward (la_poly_forward) and the linear form's state
+    accumulation S = phi(K)^T V over the D^2 features (la_poly_prefix_state);
+    a causal linear-form forward does that accumulation plus a read-out of
+    the same flop count (phi(Q_i)^T S_i), so twice the accumulation's time
+    stands for it (a chunked linear-form forward is not built)."""
+    from workloads import device_inputs
+
+    rows = []
+    cross = None
+    for N in (1024, 2048, 4096, 8192, 16384, 32768):
+        q, k, v, _ = device_inputs(B, H, N, D, M, "bf16", seed=6, scale=1.0 / D ** 0.5, device="cuda",
+                                   with_dout=False)
+        out = torch.empty_like(v)
+
+        def tm(fn, n=5):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+
+        ms_masked = tm(lambda: la.poly_forward(q, k, v, out=out))
+        ms_state = tm(lambda: la.poly_prefix_state(k, v))
+        rows.append({"N": N, "masked_sum_ms": round(ms_masked, 4), "linear_state_ms": round(ms_state, 4),
+                     "linear_form_estimate_ms": round(2 * ms_state, 4)})
+        if cross is None and ms_masked > 2 * ms_state:
+            cross = N
+        del q, k, v, out
+    log("poly crossover: " + ", ".join(f"N={r['N']} masked {r['masked_sum_ms']:.3f} ms vs linear ~"
+                                       f"{r['linear_form_estimate_ms']:.3f} ms" for r in rows))
+    return {"config": {"B": B, "H": H, "D": D, "M": M, "dtype": "bf16"}, "rows": rows,
+            "first_N_where_linear_form_is_faster": cross,
+            "flop_crossover_N": 4 * D * D * M // (D + M),
+            "note": "linear form = 2 x the D^2-feature state accumulation (update + read-out of equal flops); the "
+                    "pages put the crossover at N > D^2 = %d; counting the causal constants, at 4 D^2 M / (D + M)"
+                    % (D * D)}
 
 
 def bench_softmax(la, torch, steps, warmup):
