@@ -112,8 +112,8 @@ typedef struct la_plan {
  * eq:linear).  No scale and no epsilon are applied.
  *   q, k: [B,H,N,D]; v: [B,H,N,M]  (inputs, dtype)
  *   out:  [B,H,N,M]                 (output, dtype)
- *   den_out: [B,H,N] fp32 row denominators phi(Q_i)^T Z_i, or NULL.  Keep it
- *            for la_backward, which can then skip recomputing it. */
+ *   den_out: [B,H,N] fp32 row denominators phi(Q_i)^T Z_i, or NULL (the
+ *            backward does not need it: it forms den itself in fp32). */
 la_status la_forward(const void* q, const void* k, const void* v, void* out,
                      int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                      int causal, int dtype, float* den_out,
@@ -169,8 +169,23 @@ size_t la_saved_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
  * with R_i = sum_{j>=i} phi(Q_j) g_j^T, r_i = sum_{j>=i} c_j phi(Q_j); then
  * dq = grad phi(Q) * phi'(q), dk = grad phi(K) * phi'(k), dv = grad V.
  *   q, k, v: forward inputs; out: the forward's output; dout: upstream grad
- *   den: [B,H,N] fp32 from la_forward, or NULL (then it is recomputed)
- *   dq, dk: [B,H,N,D]; dv: [B,H,N,M] (outputs, dtype) */
+ *   den: [B,H,N] fp32 from la_forward, or NULL
+ *   dq, dk: [B,H,N,D]; dv: [B,H,N,M] (outputs, dtype)
+ * out and den are checked (size, alignment, no overlap with the outputs) but
+ * not read: the first sweep forms num_i and den_i of every row in fp32 from
+ * the prefix state, as the forward does, and takes c_i = -(dout_i . num_i) /
+ * den_i^2 from them.  A c_i from the stored bf16 out would carry out's 2^-9
+ * rounding, and for phi ~ 1 the two terms of grad phi(Q) cancel in the
+ * all-ones direction several times over, so dq would lose about a decimal
+ * digit.
+ * Precision (bf16): the MFMA kernels feed bf16 phi or elu, V and g to the
+ * matrix cores with fp32 accumulation; against the fp64 result the
+ * gradients' relative L2 error measures ~3e-3 for q, k ~ N(0, 1/D) or
+ * N(0, 1) and v, dout ~ N(0, 1).  Where most features sit far below zero
+ * (phi = e^x small), the dq sweep's phi = 1 + elu split holds phi to an
+ * absolute rather than a relative 2^-9: with q, k ~ N(-3, 1) dq measures
+ * 1.9e-2 (dk, dv 3e-3 to 6e-3), and it grows as the features move further
+ * down.  fp32 inputs: ~1e-6. */
 la_status la_backward(const void* q, const void* k, const void* v, const void* out,
                       const void* dout, const float* den, void* dq, void* dk, void* dv,
                       int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,

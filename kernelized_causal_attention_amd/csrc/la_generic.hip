@@ -236,22 +236,18 @@ __global__ __launch_bounds__(NT) void k_forward(const TIn* __restrict__ q, const
   }
 }
 
-// Stage the per-row backward inputs of one chunk and form
-//   g_i = dout_i / den_i and c_i = -(dout_i . out_i) / den_i
-// (the chain rule through out = num / den).  G holds g afterwards; W is
-// scratch that held the out tile.
+// Stage the per-row backward inputs of one chunk for the reverse sweep:
+//   g_i = dout_i / den_i, with den_i and c_i = -(dout_i . out_i) / den_i as
+// the forward sweep formed them (from the fp32 numerator, not the stored out).
+// G holds g afterwards.
 template <typename TIn, int TC>
-__device__ __forceinline__ void stage_grad_rows(float* G, float* W, int MP, float* cvec, float* dn,
-                                                const TIn* __restrict__ oh, const TIn* __restrict__ gh,
-                                                const float* __restrict__ denh, int64_t c0, int nrow, int M) {
+__device__ __forceinline__ void stage_grad_rows(float* G, int MP, float* cvec, float* dn,
+                                                const TIn* __restrict__ gh, const float* __restrict__ denh,
+                                                const float* __restrict__ ch, int64_t c0, int nrow, int M) {
   stage<TIn, TC>(G, MP, gh, c0, nrow, M, false);
-  stage<TIn, TC>(W, MP, oh, c0, nrow, M, false);
-  for (int i = threadIdx.x; i < TC; i += NT) dn[i] = i < nrow ? denh[c0 + i] : 1.f;
-  __syncthreads();
   for (int i = threadIdx.x; i < TC; i += NT) {
-    float dot = 0.f;
-    for (int m = 0; m < M; ++m) dot += G[i * MP + m] * W[i * MP + m];
-    cvec[i] = i < nrow ? -dot / dn[i] : 0.f;
+    dn[i] = i < nrow ? denh[c0 + i] : 1.f;
+    cvec[i] = i < nrow ? ch[c0 + i] : 0.f;
   }
   __syncthreads();
   for (int e = threadIdx.x; e < TC * M; e += NT) {
@@ -264,15 +260,22 @@ __device__ __forceinline__ void stage_grad_rows(float* G, float* W, int MP, floa
 // Backward, forward sweep:
 //   grad phi(Q_i) = S_i g_i + c_i Z_i
 // chunked as  sum_{j<=i in chunk} (g_i.V_j + c_i) phi(K_j) + S g_i + c_i Z,
-// then dq = grad phi(Q) * phi'(q).  The same pass accumulates the segment's
-// suffix aggregates R = sum phi(Q_i) g_i^T, r = sum c_i phi(Q_i).
+// then dq = grad phi(Q) * phi'(q).  The sweep first forms num_i and den_i of
+// its rows in fp32, exactly as the forward does, and takes
+//   g_i = dout_i / den_i,  c_i = -(dout_i . num_i) / den_i^2
+// from them: the bf16-rounded out would do for c only up to its 2^-9
+// rounding, and with phi ~ 1 the two terms of grad phi(Q) cancel in the
+// all-ones direction, which multiplies that rounding several times over.
+// den and c go to the reverse sweep (den_out, c_out).  The same pass
+// accumulates the segment's suffix aggregates R = sum phi(Q_i) g_i^T,
+// r = sum c_i phi(Q_i).
 // ---------------------------------------------------------------------------
 template <typename TIn, int TC, bool CAUSAL, int RPT>
 __global__ __launch_bounds__(NT) void k_bwd_dq(const TIn* __restrict__ q, const TIn* __restrict__ k,
-                                               const TIn* __restrict__ v, const TIn* __restrict__ out,
-                                               const TIn* __restrict__ dout, const float* __restrict__ den_in,
+                                               const TIn* __restrict__ v, const TIn* __restrict__ dout,
                                                const float* __restrict__ carry_s, TIn* __restrict__ dq,
-                                               float* __restrict__ r_agg, int64_t N, int D, int M, int P,
+                                               float* __restrict__ r_agg, float* __restrict__ c_out,
+                                               float* __restrict__ den_out, int64_t N, int D, int M, int P,
                                                int seg_len) {
   extern __shared__ float sm[];
   const int SP = M + 1, DP = D + 1, MP = M + 1, AP = TC + 1;
@@ -284,7 +287,8 @@ __global__ __launch_bounds__(NT) void k_bwd_dq(const TIn* __restrict__ q, const 
   float* V = Kf + TC * DP;
   float* G = V + TC * MP;
   float* W = G + TC * MP;
-  float* cvec = W + WSZ;
+  float* A = W + WSZ;
+  float* cvec = A + TC * AP;
   float* dn = cvec + TC;
   const int t = threadIdx.x;
   const int64_t bh = blockIdx.x / P;
@@ -300,10 +304,10 @@ __global__ __launch_bounds__(NT) void k_bwd_dq(const TIn* __restrict__ q, const 
   const TIn* qh = q + bh * N * D;
   const TIn* kh = k + bh * N * D;
   const TIn* vh = v + bh * N * M;
-  const TIn* oh = out + bh * N * M;
   const TIn* gh = dout + bh * N * M;
-  const float* denh = den_in + bh * N;
   TIn* dqh = dq + bh * N * D;
+  float* ch = c_out + bh * N;
+  float* dh = den_out + bh * N;
   float racc[RPT];
 #pragma unroll
   for (int r = 0; r < RPT; ++r) racc[r] = 0.f;
@@ -315,7 +319,56 @@ __global__ __launch_bounds__(NT) void k_bwd_dq(const TIn* __restrict__ q, const 
     stage<TIn, TC>(Qf, DP, qh, c0, nrow, D, true);
     if (CAUSAL) stage<TIn, TC>(Kf, DP, kh, c0, nrow, D, true);
     if (CAUSAL) stage<TIn, TC>(V, MP, vh, c0, nrow, M, false);
-    stage_grad_rows<TIn, TC>(G, W, MP, cvec, dn, oh, gh, denh, c0, nrow, M);
+    stage<TIn, TC>(G, MP, gh, c0, nrow, M, false);
+    __syncthreads();
+    if (CAUSAL) {
+      // masked scores A_ij = phi(Q_i).phi(K_j), j <= i
+      for (int e = t; e < TC * TC; e += NT) {
+        const int i = e / TC, j = e - i * TC;
+        float a = 0.f;
+        if (j <= i && i < nrow)
+          for (int d = 0; d < D; ++d) a += Qf[i * DP + d] * Kf[j * DP + d];
+        A[i * AP + j] = a;
+      }
+      __syncthreads();
+    }
+    // num_i into W, den_i into dn (rows past nrow: num 0, den 1)
+    for (int e = t; e < TC * M; e += NT) {
+      const int i = e / M, m = e - i * M;
+      float num = 0.f;
+      if (i < nrow) {
+        for (int d = 0; d < D; ++d) num += Qf[i * DP + d] * S[d * SP + m];
+        if (CAUSAL)
+          for (int j = 0; j <= i; ++j) num += A[i * AP + j] * V[j * MP + m];
+      }
+      W[i * MP + m] = num;
+    }
+    if (t < TC) {
+      float dd = 1.f;
+      if (t < nrow) {
+        dd = 0.f;
+        for (int d = 0; d < D; ++d) dd += Qf[t * DP + d] * Z[d];
+        if (CAUSAL)
+          for (int j = 0; j <= t; ++j) dd += A[t * AP + j];
+      }
+      dn[t] = dd;
+    }
+    __syncthreads();
+    if (t < TC) {
+      float dot = 0.f;
+      for (int m = 0; m < M; ++m) dot += G[t * MP + m] * W[t * MP + m];
+      const float c = t < nrow ? -(dot / dn[t]) / dn[t] : 0.f;
+      cvec[t] = c;
+      if (t < nrow) {
+        ch[c0 + t] = c;
+        dh[c0 + t] = dn[t];
+      }
+    }
+    __syncthreads();
+    for (int e = t; e < TC * M; e += NT) {
+      const int i = e / M, m = e - i * M;
+      G[i * MP + m] = G[i * MP + m] / dn[i];
+    }
     __syncthreads();
     if (CAUSAL) {
       // B_ij = g_i.V_j + c_i for j <= i (W now holds B)
@@ -377,8 +430,8 @@ __global__ __launch_bounds__(NT) void k_bwd_dq(const TIn* __restrict__ q, const 
 // ---------------------------------------------------------------------------
 template <typename TIn, int TC, bool CAUSAL>
 __global__ __launch_bounds__(NT) void k_bwd_dkdv(const TIn* __restrict__ q, const TIn* __restrict__ k,
-                                                 const TIn* __restrict__ v, const TIn* __restrict__ out,
-                                                 const TIn* __restrict__ dout, const float* __restrict__ den_in,
+                                                 const TIn* __restrict__ v, const TIn* __restrict__ dout,
+                                                 const float* __restrict__ den_in, const float* __restrict__ c_in,
                                                  const float* __restrict__ carry_r, TIn* __restrict__ dk,
                                                  TIn* __restrict__ dv, int64_t N, int D, int M, int P,
                                                  int seg_len) {
@@ -409,9 +462,9 @@ __global__ __launch_bounds__(NT) void k_bwd_dkdv(const TIn* __restrict__ q, cons
   const TIn* qh = q + bh * N * D;
   const TIn* kh = k + bh * N * D;
   const TIn* vh = v + bh * N * M;
-  const TIn* oh = out + bh * N * M;
   const TIn* gh = dout + bh * N * M;
   const float* denh = den_in + bh * N;
+  const float* chh = c_in + bh * N;
   TIn* dkh = dk + bh * N * D;
   TIn* dvh = dv + bh * N * M;
   const int64_t nch = (r1 - r0 + TC - 1) / TC;
@@ -423,7 +476,7 @@ __global__ __launch_bounds__(NT) void k_bwd_dkdv(const TIn* __restrict__ q, cons
     stage<TIn, TC>(Kf, DP, kh, c0, nrow, D, true);
     stage<TIn, TC>(V, MP, vh, c0, nrow, M, false);
     if (CAUSAL) stage<TIn, TC>(Qf, DP, qh, c0, nrow, D, true);
-    if (CAUSAL) stage_grad_rows<TIn, TC>(G, W, MP, cvec, dn, oh, gh, denh, c0, nrow, M);
+    if (CAUSAL) stage_grad_rows<TIn, TC>(G, MP, cvec, dn, gh, denh, chh, c0, nrow, M);
     __syncthreads();
     if (CAUSAL) {
       for (int e = t; e < TC * TC; e += NT) {
@@ -485,7 +538,7 @@ size_t lds_seg(int TC, int D, int M) {
 size_t lds_bwd_dq(int TC, int D, int M) {
   const size_t wsz = std::max<size_t>(TC * (M + 1), TC * (TC + 1));
   return sizeof(float) * (static_cast<size_t>(D) * (M + 1) + D + 2 * TC * (D + 1) + 2 * TC * (M + 1) +
-                          wsz + 2 * TC);
+                          wsz + TC * (TC + 1) + 2 * TC);
 }
 size_t lds_bwd_dkdv(int TC, int D, int M) {
   const size_t wsz = std::max<size_t>(TC * (M + 1), TC * (TC + 1));
@@ -568,15 +621,14 @@ hipError_t launch_forward_generic(int dtype, int causal, const SegGeom& g, const
 }
 
 hipError_t launch_bwd_dq_generic(int dtype, int causal, const SegGeom& g, const void* q, const void* k,
-                                 const void* v, const void* out, const void* dout, const float* den,
-                                 const float* carry_s, void* dq, float* r_agg, hipStream_t st) {
+                                 const void* v, const void* dout, const float* carry_s, void* dq, float* r_agg,
+                                 float* c_out, float* den_out, hipStream_t st) {
   const int64_t grid = g.BH * g.P;
   const bool big = g.D * g.M > 16 * NT;
 #define LA_DQ(T, TC, C, R)                                                                        \
   LA_LAUNCH((k_bwd_dq<T, TC, C, R>), grid, lds_bwd_dq(TC, g.D, g.M), st, static_cast<const T*>(q), \
-            static_cast<const T*>(k), static_cast<const T*>(v), static_cast<const T*>(out),        \
-            static_cast<const T*>(dout), den, carry_s, static_cast<T*>(dq), r_agg, g.N, g.D, g.M,  \
-            g.P, g.seg_len)
+            static_cast<const T*>(k), static_cast<const T*>(v), static_cast<const T*>(dout),       \
+            carry_s, static_cast<T*>(dq), r_agg, c_out, den_out, g.N, g.D, g.M, g.P, g.seg_len)
 #define LA_DQ_R(T, TC, C) \
   if (big) LA_DQ(T, TC, C, 64); \
   LA_DQ(T, TC, C, 16)
@@ -596,14 +648,14 @@ hipError_t launch_bwd_dq_generic(int dtype, int causal, const SegGeom& g, const 
 }
 
 hipError_t launch_bwd_dkdv_generic(int dtype, int causal, const SegGeom& g, const void* q, const void* k,
-                                   const void* v, const void* out, const void* dout, const float* den,
+                                   const void* v, const void* dout, const float* den, const float* c,
                                    const float* carry_r, void* dk, void* dv, hipStream_t st) {
   const int64_t grid = g.BH * g.P;
 #define LA_KV(T, TC, C)                                                                           \
   LA_LAUNCH((k_bwd_dkdv<T, TC, C>), grid, lds_bwd_dkdv(TC, g.D, g.M), st, static_cast<const T*>(q), \
-            static_cast<const T*>(k), static_cast<const T*>(v), static_cast<const T*>(out),        \
-            static_cast<const T*>(dout), den, carry_r, static_cast<T*>(dk), static_cast<T*>(dv),   \
-            g.N, g.D, g.M, g.P, g.seg_len)
+            static_cast<const T*>(k), static_cast<const T*>(v), static_cast<const T*>(dout),       \
+            den, c, carry_r, static_cast<T*>(dk), static_cast<T*>(dv), g.N, g.D, g.M, g.P,         \
+            g.seg_len)
 #define LA_KV_C(T, TC) \
   if (causal) LA_KV(T, TC, true); \
   LA_KV(T, TC, false)

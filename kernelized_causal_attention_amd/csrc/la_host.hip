@@ -297,10 +297,8 @@ WsLayout layout(int op, int64_t BH, int64_t N, int64_t D, int64_t M, int causal,
     w.aggR = c.take(recs);
     w.totR = c.take(static_cast<size_t>(BH) * E);
     w.den = c.take(static_cast<size_t>(BH) * N);
-    if (p.kernel == LA_KERNEL_MFMA) {
-      w.cvec = c.take(static_cast<size_t>(BH) * N);
-      w.flags = c.take(static_cast<size_t>(BH) * p.P);
-    }
+    w.cvec = c.take(static_cast<size_t>(BH) * N);
+    if (p.kernel == LA_KERNEL_MFMA) w.flags = c.take(static_cast<size_t>(BH) * p.P);
   } else if (op == LA_OP_PREFIX_STATE) {
     if (p.P > 1) w.aggS = c.take(recs);
   }
@@ -739,10 +737,11 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
   // the suffix aggregates are needed across segments, and for dL/dS0, dL/dZ0
   // (their totals) in a state-carrying call
   float* r_agg = (causal && p.P == 1 && !st.S_out) ? nullptr : aggR;
-  // The MFMA path recomputes num and den in fp32 inside its forward sweep
-  // (it reads neither out nor den) and passes den and c to the reverse sweep
+  // Both kernel families recompute num and den in fp32 inside the forward
+  // sweep (neither reads out or den) and pass den and c to the reverse sweep
   // through the workspace.
   float* cw = at(workspace, w.cvec);
+  float* dw = at(workspace, w.den);
   if (p.kernel == LA_KERNEL_MFMA && p.one_launch && causal && !st.on && dtype == LA_BF16 &&
       la::bwd_fused_supported(causal, D)) {
     // one launch: the forward sweep, the hand-off of the suffix aggregates
@@ -758,7 +757,6 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
       if ((e = stream_device(stream, &devno)) || (e = err_word_for_stream(stream, &errw)))
         return dev(e, "backward hand-off set-up");
       const bool test = handoff_test_mode();
-      float* dw = at(workspace, w.den);
       return dev(timed("mfma.bwd_fused", stream,
                        [&] {
                          return la::launch_bwd_fused_mfma(g, q, k, v, dout, carry_s, dq, dk, dv, aggR, cw, dw,
@@ -769,20 +767,13 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
     }
   }
   if (p.kernel == LA_KERNEL_MFMA) {
-    float* dw = at(workspace, w.den);
     e = timed("mfma.bwd_dq", stream,
               [&] { return la::launch_bwd_dq_mfma(causal, g, q, k, v, dout, carry_s, dq, r_agg, cw, dw, stream); });
-    den = dw;
   } else {
-    if (!den) {
-      float* dw = at(workspace, w.den);
-      if ((e = fwd_pass(dtype, causal, p, g, q, k, v, nullptr, dw, carry_s, stream))) return dev(e, "denominator");
-      den = dw;
-    }
     la::SegGeom gd = g;
     gd.chunk = std::min(p.chunk, la::generic_chunk_for(g.D, g.M, 2));
     e = timed("generic.bwd_dq", stream, [&] {
-      return la::launch_bwd_dq_generic(dtype, causal, gd, q, k, v, out, dout, den, carry_s, dq, r_agg, stream);
+      return la::launch_bwd_dq_generic(dtype, causal, gd, q, k, v, dout, carry_s, dq, r_agg, cw, dw, stream);
     });
   }
   if (e) return dev(e, "backward dq");
@@ -806,14 +797,14 @@ la_status do_backward(const void* q, const void* k, const void* v, const void* o
   if (p.kernel == LA_KERNEL_MFMA) {
     e = timed("mfma.bwd_dkdv", stream,
               [&] {
-                return la::launch_bwd_dkdv_mfma(causal, g, q, k, v, dout, den, cw, carry_r, dk, dv, stream,
+                return la::launch_bwd_dkdv_mfma(causal, g, q, k, v, dout, dw, cw, carry_r, dk, dv, stream,
                                                 carry_raw);
               });
   } else {
     la::SegGeom gk = g;
     gk.chunk = std::min(p.chunk, la::generic_chunk_for(g.D, g.M, 3));
     e = timed("generic.bwd_dkdv", stream, [&] {
-      return la::launch_bwd_dkdv_generic(dtype, causal, gk, q, k, v, out, dout, den, carry_r, dk, dv, stream);
+      return la::launch_bwd_dkdv_generic(dtype, causal, gk, q, k, v, dout, dw, cw, carry_r, dk, dv, stream);
     });
   }
   return dev(e, "backward dk/dv");

@@ -63,16 +63,19 @@ hipError_t launch_forward_generic(int dtype, int causal, const SegGeom& g, const
                                   const void* v, void* out, float* den_out, const float* carry,
                                   hipStream_t st);
 
-// Backward, forward sweep: dq and, as a by-product, the per-segment suffix
-// aggregates (R, r) written to r_agg [BH][P][E].
+// Backward, forward sweep: dq, the per-row c and den [BH][N] (formed in fp32
+// from the carried state; the stored out and den are not read) and, as a
+// by-product, the per-segment suffix aggregates (R, r) written to r_agg
+// [BH][P][E].
 hipError_t launch_bwd_dq_generic(int dtype, int causal, const SegGeom& g, const void* q, const void* k,
-                                 const void* v, const void* out, const void* dout, const float* den,
-                                 const float* carry_s, void* dq, float* r_agg, hipStream_t st);
+                                 const void* v, const void* dout, const float* carry_s, void* dq, float* r_agg,
+                                 float* c_out, float* den_out, hipStream_t st);
 
 // Backward, reverse sweep: dk, dv from the suffix carry (exclusive suffix
-// records for causal, per-bh totals for non-causal).
+// records for causal, per-bh totals for non-causal) and the forward sweep's
+// den and c.
 hipError_t launch_bwd_dkdv_generic(int dtype, int causal, const SegGeom& g, const void* q, const void* k,
-                                   const void* v, const void* out, const void* dout, const float* den,
+                                   const void* v, const void* dout, const float* den, const float* c,
                                    const float* carry_r, void* dk, void* dv, hipStream_t st);
 
 // ---- decode ----
