@@ -88,7 +88,7 @@ def parse():
                     help="only run the streaming-bandwidth microbenchmark and print its lines")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-bandwidth microbenchmark (e.g. under a profiler)")
-    ap.add_argument("--only", choices=["fwdbwd_bf16", "long_bf16", "fwd_f32", "decode_f32"],
+    ap.add_argument("--only", choices=["fwdbwd_bf16", "long_bf16", "fwd_f32", "decode_f32", "chunk128"],
                     help="run only this workload's measurement (for profiling) and print it")
     ap.add_argument("--cpu-workers", type=int, default=0,
                     help="oracle baseline worker processes (0: the cores this process may run on, at most 16)")
@@ -110,8 +110,8 @@ def parse():
 
 CEILING_EXE = os.path.join(ROOT, "kernelized_causal_attention_amd", "_lib", "hbm_ceiling")
 # the traffic mix of each kernel (tensors read / written), for its practical ceiling
-KERNEL_MIX = {"mfma.seg_state": "r2", "mfma.forward": "r3w1", "mfma.bwd_dq": "r4w1", "mfma.bwd_dkdv": "r4w2",
-              "decode": "r1w1"}
+KERNEL_MIX = {"mfma.seg_state": "r2", "mfma.forward": "r3w1", "mfma.forward_t128": "r3w1", "mfma.bwd_dq": "r4w1",
+              "mfma.bwd_dkdv": "r4w2", "decode": "r1w1"}
 
 
 def hbm_ceilings():
@@ -175,7 +175,7 @@ def kernel_bytes(name: str, B, H, N, D, M, es, P=1):
     if family == "mfma" and base == "bwd_dkdv":
         # reads q, k, v, dout and (c, den); writes dk, dv
         return ht * (es * (2 * D + 2 * M) + 8 + es * (D + M))
-    if base == "forward":
+    if base in ("forward", "forward_t128"):
         return ht * (es * (2 * D + M) + es * M + 4)
     if base == "forward_den":
         return ht * (es * (2 * D + M) + 4)
@@ -373,7 +373,8 @@ def main():
         fn = {"fwdbwd_bf16": lambda: bench_fwdbwd(la, torch, args, None),
               "long_bf16": lambda: bench_long(la, torch, args.steps, args.warmup, None),
               "fwd_f32": lambda: bench_fwd_f32(la, torch, args.steps, args.warmup, None),
-              "decode_f32": lambda: bench_decode(la, torch, args.decode_steps)}[args.only]
+              "decode_f32": lambda: bench_decode(la, torch, args.decode_steps),
+              "chunk128": lambda: bench_chunk128(la, torch, args.steps, args.warmup)}[args.only]
         print(json.dumps(fn()), flush=True)
         return
 
@@ -381,6 +382,7 @@ def main():
     if not args.no_extra:
         result["long_bf16"] = bench_long(la, torch, args.steps, args.warmup, ceil)
         result["fwd_f32"] = bench_fwd_f32(la, torch, args.steps, args.warmup, ceil)
+        result["chunk_128"] = bench_chunk128(la, torch, args.steps, args.warmup)
         result["decode"] = bench_decode(la, torch, args.decode_steps)
         if ceil and "r1w1" in ceil:
             result["decode"]["roofline"]["frac_of_ceiling"] = round(
@@ -462,6 +464,52 @@ def bench_fwdbwd(la, torch, args, ceil):
                       "plain 16-byte-vector kernels over 134 MB tensors, GB/s per traffic mix",
             "mixes": ceil, "dominant_mix": mix}
     return result
+
+
+def bench_chunk128(la, torch, steps, warmup):
+    """Chunk length 64 against 128 on the fwd+bwd workload (B=8 H=16 N=8192
+    D=M=64, bf16): the causal forward alone (keeping den and the prefix
+    states) under each plan, and the whole step with the 128-token forward
+    (the backward kernels take 64-token chunks over the same segments)."""
+    from workloads import WORKLOADS, device_inputs
+
+    w = WORKLOADS["fwdbwd_bf16"]
+    B, H, N, D, M = w.B, w.H, w.N, w.D, w.M
+    dev = torch.device("cuda:0")
+    q, k, v, g = device_inputs(B, H, N, D, M, "bf16", seed=0, scale=1.0 / D ** 0.5, device="cuda")
+    out = torch.empty((B, H, N, M), dtype=torch.bfloat16, device=dev)
+    den = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    res = {"workload": f"causal forward (and fwd+bwd step), bf16, B={B} H={H} N={N} D=M={D}",
+           "note": "two rounds, alternating the chunk lengths; forward_kernel_ms is the forward kernel's "
+                   "average over the timed steps (HIP events around its launches)"}
+    runs = {64: [], 128: []}
+    for _ in range(2):
+        for T in (64, 128):
+            plan = la.resolve_plan("forward", B, H, N, D, M, True, "bf16", dict(chunk=T))
+            ws_f = torch.empty(max(1, la.workspace_bytes("forward", B, H, N, D, M, True, "bf16", plan)),
+                               dtype=torch.uint8, device=dev)
+            ws_b = torch.empty(max(1, la.workspace_bytes("backward", B, H, N, D, M, True, "bf16", plan)),
+                               dtype=torch.uint8, device=dev)
+            nsaved = la.saved_bytes(B, H, N, D, M, True, "bf16", plan)
+            saved = torch.empty(nsaved, dtype=torch.uint8, device=dev) if nsaved else None
+
+            def fwd():
+                la.forward(q, k, v, causal=True, out=out, den=den, return_den=True, workspace=ws_f, saved=saved,
+                           plan=plan)
+
+            def step():
+                fwd()
+                return la.backward(q, k, v, out, g, den=den, causal=True, workspace=ws_b, saved=saved, plan=plan)
+
+            ms_f, prof_f, kname, avg_f = timed_steps(la, torch, fwd, steps, warmup, settle=0.5)
+            ms_s, _, _, _ = timed_steps(la, torch, step, steps, warmup, settle=0.5)
+            runs[T].append({"plan": plan, "forward_ms": round(ms_f, 4), "forward_kernel": kname,
+                            "forward_kernel_ms": round(avg_f, 4), "step_ms": round(ms_s, 4),
+                            "forward_breakdown_ms": {kk: round(tt / nn, 4) for kk, (nn, tt) in sorted(prof_f.items())}})
+            log(f"chunk {T}: forward {ms_f:.4f} ms ({kname} {avg_f:.4f} ms), step {ms_s:.4f} ms")
+    for T in (64, 128):
+        res[f"T{T}"] = runs[T]
+    return res
 
 
 def bench_long(la, torch, steps, warmup, ceil):
@@ -558,7 +606,7 @@ COUNTERS_FILE_F32 = os.path.join(PROFILES, "counters_fwd_f32.txt")
 # HIP kernel symbols -> the library's launch names (la_profile_* names)
 KERNEL_SYMBOLS = [
     ("k_bwd_fused_mfma", "mfma.bwd_fused"), ("k_fill_u32", "mfma.bwd_fused"), ("k_bwd_dkdv_mfma", "mfma.bwd_dkdv"), ("k_bwd_dq_mfma", "mfma.bwd_dq"), ("k_bwd_ragg_mfma", "mfma.bwd_dq"),
-    ("k_fwd_f32mfma", "mfma.forward"), ("k_fwd_mfma", "mfma.forward"), ("k_seg_state_wave64", "mfma.seg_state"),
+    ("k_fwd_f32mfma", "mfma.forward"), ("k_fwd_mfma_t128", "mfma.forward_t128"), ("k_fwd_mfma", "mfma.forward"), ("k_seg_state_wave64", "mfma.seg_state"),
     ("k_seg_state_f32mfma", "mfma.seg_state"), ("k_seg_state_mfma", "mfma.seg_state"), ("k_seg_scan", "seg_scan"),
     ("k_decode_vec", "decode"), ("k_ret_fwd_mfma", "ret.forward"), ("k_ret_seg_wave64", "ret.seg_state"),
     ("k_ret_seg_state", "ret.seg_state"), ("k_ret_scan", "ret.scan"), ("k_ret_dq", "ret.bwd_dq"),

@@ -94,7 +94,10 @@ typedef enum la_kernel {
 } la_kernel;
 
 /* Tuning plan.  Every field 0 means "let the library choose".
- *   chunk    -- tokens per intra-chunk tile (generic: 16/32/64; MFMA: 64)
+ *   chunk    -- tokens per intra-chunk tile (generic: 16 or 32; MFMA: 64,
+ *               or 128 for the bf16 forward at D = M = 64: segments are then
+ *               whole 128-token chunks, and the other kernels of a call with
+ *               this plan keep 64-token chunks over those segments)
  *   segments -- how many independent pieces each sequence is cut into along
  *               N; each piece's state is carried in by an exclusive scan of
  *               the pieces before it (the prefix sums split exactly by

@@ -203,8 +203,14 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
   if (kernel == LA_KERNEL_AUTO) kernel = mfma_ok ? LA_KERNEL_MFMA : LA_KERNEL_GENERIC;
   // a misaligned call on the automatic plan: MFMA segmentation, generic kernels
   const bool demoted = kernel == LA_KERNEL_MFMA && !vec_ok;
-  const int unit = kernel == LA_KERNEL_MFMA ? 64 : 32;  // segment granularity
   int chunk = req ? req->chunk : 0;
+  // chunk 128 (bf16, D = M = 64): the forward runs 128-token chunks and every
+  // segment is a whole number of them; the other kernels keep 64-token
+  // chunks over the same segments, so records stay interchangeable between
+  // calls with this plan
+  if (chunk == 128 && !(kernel == LA_KERNEL_MFMA && dtype == LA_BF16 && D == 64 && M == 64))
+    return fail(LA_ERR_INVALID, "plan.chunk=128 is the bf16 MFMA forward at D = M = 64 only");
+  const int unit = kernel == LA_KERNEL_MFMA ? (chunk == 128 ? 128 : 64) : 32;  // segment granularity
   if (demoted) {
     kernel = LA_KERNEL_GENERIC;
     chunk = 0;
@@ -216,8 +222,9 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
     if (tc == 0) return fail(LA_ERR_UNSUPPORTED, "D=%lld, M=%lld do not fit in LDS", (long long)D, (long long)M);
     if (chunk == 0 || chunk > tc) chunk = tc;
   } else {
-    if (chunk != 0 && chunk != 64) return fail(LA_ERR_INVALID, "plan.chunk=%d (MFMA kernels take 64)", chunk);
-    chunk = 64;
+    if (chunk != 0 && chunk != 64 && chunk != 128)
+      return fail(LA_ERR_INVALID, "plan.chunk=%d (MFMA kernels take 64, or 128 for the D = 64 bf16 forward)", chunk);
+    if (chunk == 0) chunk = 64;
   }
   const int64_t nunits = (N + unit - 1) / unit;
   const int64_t BH = B * H;
@@ -516,8 +523,10 @@ hipError_t seg_state(int dtype, const Plan& p, const la::SegGeom& gbase, const v
 hipError_t fwd_pass(int dtype, int causal, const Plan& p, const la::SegGeom& gbase, const void* q,
                     const void* k, const void* v, void* out, float* den_out, const float* carry,
                     hipStream_t st) {
-  const char* name = out ? kname(p.kernel, "generic.forward", "mfma.forward")
-                         : kname(p.kernel, "generic.forward_den", "mfma.forward_den");
+  const bool t128 = p.kernel == LA_KERNEL_MFMA && gbase.chunk == 128;
+  const char* name = t128 ? (out ? "mfma.forward_t128" : "mfma.forward_t128_den")
+                     : out ? kname(p.kernel, "generic.forward", "mfma.forward")
+                           : kname(p.kernel, "generic.forward_den", "mfma.forward_den");
   if (p.kernel == LA_KERNEL_MFMA)
     return timed(name, st, [&] {
       return dtype == LA_F32 ? la::launch_forward_f32mfma(causal, gbase, q, k, v, out, den_out, carry, st)

@@ -73,8 +73,9 @@ __device__ __forceinline__ void write_state(uint16_t* sST, uint16_t* sZ,
   }
 }
 
-// S += phi(K_c)^T V_c and Z += colsum phi(K_c) for this wave's state rows.
-template <int DIM, int NW>
+// S += phi(K_c)^T V_c and Z += colsum phi(K_c) for this wave's state rows
+// (TT-token chunk tiles).
+template <int DIM, int NW, int TT = T>
 __device__ __forceinline__ void state_update(f32x4_t (&Sacc)[(Geo<DIM, NW>::DT)][(Geo<DIM, NW>::NTL)],
                                              f32x4_t (&zacc)[(Geo<DIM, NW>::DT)], const uint16_t* sKf,
                                              const uint16_t* sV, int w, int g, int li) {
@@ -85,7 +86,7 @@ __device__ __forceinline__ void state_update(f32x4_t (&Sacc)[(Geo<DIM, NW>::DT)]
   for (int dt = 0; dt < G::DT; ++dt) {
     const int d0 = 16 * (w * G::DT + dt);
 #pragma unroll
-    for (int s = 0; s < T / 32; ++s) {
+    for (int s = 0; s < TT / 32; ++s) {
       const int jr = 32 * s + 8 * g + li / 4;
       const int cc = 4 * (li % 4);
       const i16x8 a = cat(lds_tr(sKf + jr * G::LD + d0 + cc), lds_tr(sKf + (jr + 4) * G::LD + d0 + cc));
@@ -298,6 +299,188 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_
   }
 }
 
+// ---------------------------------------------------------------------------
+// The D = 64 forward with 128-token chunks (plan chunk 128).  Same
+// arithmetic as k_fwd_mfma (hi + lo scores, S^T in LDS as bf16, fp32 state in
+// MFMA accumulators), over chunks twice as long: the inter-chunk product and
+// the state read-out run once per 128 tokens instead of per 64, and the
+// masked triangle doubles.  Four waves; wave w takes query row tiles w and
+// 7 - w of each chunk, so every wave does the same triangular work (9 key
+// tiles), and owns state rows 16w .. 16w + 15.  Segments are whole numbers
+// of 128-token chunks (the host cuts them so), so the only partial chunk is
+// a sequence's last, whose rows past the end the stores' range check drops.
+// ---------------------------------------------------------------------------
+constexpr int T2 = 128;
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void k_fwd_mfma_t128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                          const bf16_t* __restrict__ v, bf16_t* __restrict__ out,
+                                                          float* __restrict__ den_out, const float* __restrict__ carry,
+                                                          int64_t N, int P, int seg_len) {
+  constexpr int DIM = 64, NW = 4;
+  using G = Geo<DIM, NW>;
+  constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS;
+  constexpr int PC2 = T2 * DIM / 8 / 256;  // 16-byte pieces per thread per 128 x 64 tile
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* sKf = smem;
+  uint16_t* sV = sKf + T2 * LD;
+  uint16_t* sST = sV + T2 * LD;
+  uint16_t* sZ = sST + DIM * LD;  // Z as bf16 hi [DIM], lo [DIM]
+  uint16_t* sOut = sZ + 2 * DIM;  // per-wave output staging, 16 x DIM
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.x / P;
+  const int seg = blockIdx.x % P;
+  const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
+  const int64_t r1 = min(N, r0 + seg_len);
+  constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;
+  const float* cs = carry ? (CAUSAL ? carry + (bh * P + seg) * E : carry + bh * E) : nullptr;
+  const bf16_t* qh = q + bh * N * DIM;
+  const bf16_t* kh = k + bh * N * DIM;
+  const bf16_t* vh = v + bh * N * DIM;
+  const rsrc_t ro = make_rsrc(out ? out + bh * N * DIM : nullptr, out ? N * DIM * 2 : 0);
+  float* dh = den_out ? den_out + bh * N : nullptr;
+  const short one = 0x3f80;  // bf16 1.0
+  const i16x8 ones = {one, one, one, one, one, one, one, one};
+  uint16_t* sO = sOut + w * 16 * (DIM + kLdsPad);
+  const int rts[2] = {w, 7 - w};  // wave-uniform query row tiles
+
+  f32x4_t Sacc[G::DT][NTL];
+  f32x4_t zacc[G::DT];
+  init_state<DIM, NW>(Sacc, zacc, cs, w, g, li);
+  write_state<DIM, NW>(sST, sZ, Sacc, zacc, w, g, li);
+
+  auto load_kv = [&](i32x4 (&raw)[PC2], const bf16_t* src, int64_t cc0, int nr) {
+#pragma unroll
+    for (int r = 0; r < PC2; ++r) {
+      const int p = tid + 256 * r;
+      const int j = p / G::ROW8, c8 = p % G::ROW8;
+      raw[r] = j < nr ? gload16(src + (cc0 + j) * DIM + c8 * 8) : i32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_kv = [&](uint16_t* lds, const i32x4 (&raw)[PC2], int nr, bool apply_phi) {
+#pragma unroll
+    for (int r = 0; r < PC2; ++r) {
+      const int p = tid + 256 * r;
+      const int j = p / G::ROW8, c8 = p % G::ROW8;
+      i16x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (j < nr) val = apply_phi ? phi8(raw[r]) : __builtin_bit_cast(i16x8, raw[r]);
+      *reinterpret_cast<i16x8*>(lds + j * LD + c8 * 8) = val;
+    }
+  };
+
+  int64_t c0 = r0;
+  int nrow = static_cast<int>(min(static_cast<int64_t>(T2), r1 - c0));
+  i32x4 kraw[PC2], vraw[PC2], qraw[2][KS];
+  if (CAUSAL) {
+    load_kv(kraw, kh, c0, nrow);
+    load_kv(vraw, vh, c0, nrow);
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x) load_q<DIM>(qraw[x], qh, c0, nrow, 16 * rts[x] + li, g);
+
+  while (c0 < r1) {
+    if (CAUSAL) {
+      store_kv(sKf, kraw, nrow, true);
+      store_kv(sV, vraw, nrow, false);
+    }
+    i16x8 qf[2][KS];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        qf[x][s] = 16 * rts[x] + li < nrow ? phi8(qraw[x][s]) : i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    __syncthreads();
+
+    // prefetch the next chunk while this one computes
+    const int64_t c1 = c0 + T2;
+    const int nrow1 = c1 < r1 ? static_cast<int>(min(static_cast<int64_t>(T2), r1 - c1)) : 0;
+    if (nrow1 > 0) {
+      if (CAUSAL) {
+        load_kv(kraw, kh, c1, nrow1);
+        load_kv(vraw, vh, c1, nrow1);
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x) load_q<DIM>(qraw[x], qh, c1, nrow1, 16 * rts[x] + li, g);
+    }
+
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int rt = rts[x];
+      const int i = 16 * rt + li;
+      // intra-chunk scores A^T for key tiles t <= rt, masked, as hi + lo
+      i16x4 ahi[T2 / 16], alo[T2 / 16];
+      if (CAUSAL) {
+#pragma unroll
+        for (int t = 0; t < T2 / 16; ++t) {
+          ahi[t] = i16x4{0, 0, 0, 0};
+          alo[t] = i16x4{0, 0, 0, 0};
+          if (t <= rt) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) acc = mfma(lds8(sKf + (16 * t + li) * LD + 8 * g + 32 * s), qf[x][s], acc);
+            if (t == rt) {
+#pragma unroll
+              for (int u = 0; u < 4; ++u)
+                if (4 * g + u > li) acc[u] = 0.f;
+            }
+            ahi[t] = pack4(acc);
+            alo[t] = pack4(acc - unpack4(ahi[t]));
+          }
+        }
+      }
+      // denominator: phi(Q_i)^T Z (Z as hi + lo) and the intra-chunk scores
+      f32x4_t dz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        dz = mfma(lds8(sZ + 8 * g + 32 * s), qf[x][s], dz);
+        dz = mfma(lds8(sZ + DIM + 8 * g + 32 * s), qf[x][s], dz);
+      }
+      // O^T = S^T phi(Q)^T (+ V^T A^T)
+      f32x4_t o[NTL];
+#pragma unroll
+      for (int n = 0; n < NTL; ++n) {
+        o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) o[n] = mfma(lds8(sST + (16 * n + li) * LD + 8 * g + 32 * s), qf[x][s], o[n]);
+      }
+      if (CAUSAL) {
+#pragma unroll
+        for (int tp = 0; tp < T2 / 32; ++tp) {
+          if (2 * tp <= rt) {
+            const i16x8 bhi = cat(ahi[2 * tp], ahi[2 * tp + 1]);
+            const i16x8 blo = cat(alo[2 * tp], alo[2 * tp + 1]);
+            dz = mfma(ones, bhi, dz);
+            dz = mfma(ones, blo, dz);
+            const int jr = 32 * tp + 4 * g + li / 4;
+            const int cc = 4 * (li % 4);
+#pragma unroll
+            for (int n = 0; n < NTL; ++n) {
+              const i16x8 a = cat(lds_tr(sV + jr * LD + 16 * n + cc), lds_tr(sV + (jr + 16) * LD + 16 * n + cc));
+              o[n] = mfma(a, bhi, o[n]);
+              o[n] = mfma(a, blo, o[n]);
+            }
+          }
+        }
+      }
+      const float den = dz[0];
+      if (out) {
+        const float inv = 1.f / den;
+#pragma unroll
+        for (int n = 0; n < NTL; ++n) stage_piece<DIM>(sO, pack4(o[n] * inv), li, g, n);
+        store_staged<DIM, DIM>(sO, ro, 16 * rt, 0, static_cast<int>(c0 * DIM * 2));
+      }
+      if (i < nrow && dh && g == 0) dh[c0 + i] = den;
+    }
+
+    if (CAUSAL) state_update<DIM, NW, T2>(Sacc, zacc, sKf, sV, w, g, li);
+    __syncthreads();
+    if (CAUSAL) write_state<DIM, NW>(sST, sZ, Sacc, zacc, w, g, li);
+    c0 = c1;
+    nrow = nrow1;
+  }
+}
+
 // Segment aggregates dS = phi(K)^T V, dZ = colsum phi(K) over one segment.
 // phi(K) = 1 + E(K) is split so that the records are as exact as fp32
 // allows: the MFMAs sum E(K)^T V and colsum E(K) with E = elu carried as
@@ -502,6 +685,9 @@ size_t lds_fwd(int dim) {
   return (tiles * T * (dim + kLdsPad) + dim * (dim + kLdsPad) + waves * 16 * (64 + kLdsPad)) * sizeof(uint16_t) +
          dim * sizeof(float);
 }
+size_t lds_fwd_t128() {
+  return (2 * T2 * (64 + kLdsPad) + 64 * (64 + kLdsPad) + 2 * 64 + 4 * 16 * (64 + kLdsPad)) * sizeof(uint16_t);
+}
 size_t lds_seg(int dim) { return 2 * T * (dim + kLdsPad) * sizeof(uint16_t); }
 // four wave-private K / V tile pairs; the partials reuse the space at the end
 size_t lds_seg_wave64() {
@@ -536,6 +722,10 @@ hipError_t launch_forward_mfma(int causal, const SegGeom& g, const void* q, cons
   const bf16_t* K = static_cast<const bf16_t*>(k);
   const bf16_t* V = static_cast<const bf16_t*>(v);
   bf16_t* O = static_cast<bf16_t*>(out);
+  if (g.D == 64 && g.chunk == T2) {
+    if (causal) LA_MLAUNCH((k_fwd_mfma_t128<true>), 256, grid, lds_fwd_t128(), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
+    LA_MLAUNCH((k_fwd_mfma_t128<false>), 256, grid, lds_fwd_t128(), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
+  }
   if (g.D == 64) {
     if (causal) LA_MLAUNCH((k_fwd_mfma<64, true>), 64 * kFwdWaves<64>, grid, lds_fwd(64), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
     LA_MLAUNCH((k_fwd_mfma<64, false>), 64 * kFwdWaves<64>, grid, lds_fwd(64), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);

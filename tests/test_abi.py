@@ -93,6 +93,32 @@ def test_resolve_plan(lib):
     assert lib.la_resolve_plan(0, 1, 1, 1 << 23, 128, 128, 1, 1, ctypes.byref(mf), ctypes.byref(out)) == 2
 
 
+def test_resolve_plan_chunk_128(lib):
+    # 128-token chunks: the bf16 MFMA forward at D = M = 64 only; segments are
+    # whole 128-token chunks (for every op of a call with that plan, so the
+    # backward cuts the sequence as the forward did)
+    out = _native.la_plan()
+    for op in (0, 1):
+        for N in (1000, 8192, 300, 129):
+            for segs in (0, 3, 6):
+                req = _native.la_plan(128, segs, 0)
+                assert lib.la_resolve_plan(op, 2, 4, N, 64, 64, 1, 1, ctypes.byref(req), ctypes.byref(out)) == 0
+                assert out.chunk == 128 and out.kernel == 2
+                assert out.segments <= -(-N // 128)
+    req = _native.la_plan(128, 6, 0)
+    base = _native.la_plan(64, 6, 0)
+    o128, o64 = _native.la_plan(), _native.la_plan()
+    assert lib.la_resolve_plan(0, 1, 1, 1000, 64, 64, 1, 1, ctypes.byref(req), ctypes.byref(o128)) == 0
+    assert lib.la_resolve_plan(0, 1, 1, 1000, 64, 64, 1, 1, ctypes.byref(base), ctypes.byref(o64)) == 0
+    # 1000 tokens in six pieces: 192-token segments (6) in 64-token units, 256 (4) in 128-token units
+    assert (o64.segments, o128.segments) == (6, 4)
+    for bad_args in ((0, 1, 1, 1000, 128, 128, 1, 1), (0, 1, 1, 1000, 64, 64, 1, 0),
+                     (0, 1, 1, 1000, 32, 32, 1, 1)):
+        assert lib.la_resolve_plan(*bad_args, ctypes.byref(req), ctypes.byref(out)) == 1
+    gen = _native.la_plan(128, 0, 1)
+    assert lib.la_resolve_plan(0, 1, 1, 1000, 64, 64, 1, 1, ctypes.byref(gen), ctypes.byref(out)) == 1
+
+
 def test_poly_workspace_and_support(lib):
     # the polynomial backward keeps one float per row (c_i); other dtypes or
     # sizes are unsupported (0 bytes)

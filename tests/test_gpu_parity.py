@@ -505,6 +505,53 @@ def test_saved_states_rejected_when_too_small():
         la.forward(tq, tk, tv, plan=plan, saved=small)
 
 
+# ------------------------------------------- 128-token chunks (D = 64) ----
+CHUNK128_SHAPES = [(1, 1, 1), (1, 2, 127), (2, 1, 128), (1, 1, 129), (2, 3, 333), (1, 2, 1000), (1, 1, 2500)]
+
+
+@pytest.mark.parametrize("shape", CHUNK128_SHAPES)
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("segments", [1, 3])
+def test_mfma_forward_chunk_128(shape, causal, segments):
+    # plan chunk 128: the D = 64 forward over 128-token chunks (ragged tails,
+    # one and several segments), against the oracle with the bf16 guards
+    B, H, N = shape
+    D = 64
+    tq, tk, tv, _ = host_case(B, H, N, D, D, "bf16", seed=N + segments + 128, scale=1.0 / np.sqrt(D))
+    plan = dict(kernel=2, segments=segments, chunk=128)
+    la.profile_enable(True)
+    check_forward(tq, tk, tv, causal, "bf16", plan=plan, null_guard=N >= 64)
+    ran = la.profile_report()
+    la.profile_enable(False)
+    assert "mfma.forward_t128" in ran and "mfma.forward" not in ran, ran
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_chunk_128_forward_feeds_the_backward(causal):
+    # a training step with plan chunk 128: the forward's saved segment states
+    # (segments of whole 128-token chunks) feed the 64-token backward kernels
+    # over the same segments; bit for bit the backward that recomputes them,
+    # and the oracle's gradients
+    B, H, N, D = 2, 2, 1000, 64
+    tq, tk, tv, tg = host_case(B, H, N, D, D, "bf16", seed=1280 + causal, scale=1.0 / np.sqrt(D))
+    plan = dict(kernel=2, segments=3, chunk=128)
+    nb = la.saved_bytes(B, H, N, D, D, causal, "bf16", plan)
+    saved = torch.empty(nb, dtype=torch.uint8, device=DEV) if nb else None
+    out, den = la.forward(tq, tk, tv, causal=causal, return_den=True, plan=plan, saved=saved)
+    g_saved = la.backward(tq, tk, tv, out, tg, den=den, causal=causal, plan=plan, saved=saved)
+    g_plain = la.backward(tq, tk, tv, out, tg, causal=causal, plan=plan)
+    torch.cuda.synchronize()
+    for a, b in zip(g_saved, g_plain):
+        assert torch.equal(a, b)
+    rq, rk, rv, rout, _ = oracle.backward(f64(tq), f64(tk), f64(tv), f64(tg), causal)
+    assert rel_l2(f64(out), rout) < TOL["bf16"]
+    for n, x, r in (("dq", g_saved[0], rq), ("dk", g_saved[1], rk), ("dv", g_saved[2], rv)):
+        e = rel_l2(f64(x), r)
+        say(f"chunk 128 step causal={causal} {n}={e:.2e}")
+        e_round = rel_l2(f64(torch.from_numpy(r).float().to(torch.bfloat16)), r)
+        assert e < max(4.0 * e_round, 5e-3), (n, e, e_round)
+
+
 F32_MFMA_SHAPES = [(1, 1, 1, 64), (1, 2, 63, 64), (2, 1, 64, 64), (1, 1, 65, 64), (2, 3, 333, 64),
                    (1, 2, 1000, 64)]
 
