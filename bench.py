@@ -132,9 +132,27 @@ def hbm_ceilings():
     mixes = {}
     for line in r.stdout.splitlines():
         d = json.loads(line)
-        mixes[d["mix"]] = d["GBps"]
+        if "mix" in d:
+            mixes[d["mix"]] = d["GBps"]
+        elif "mfma" in d:
+            MFMA_CEIL[d["mfma"]] = d["TFLOPs"]
     log("streaming ceilings (GB/s): " + ", ".join(f"{k} {v:.0f}" for k, v in mixes.items()))
+    if MFMA_CEIL:
+        log("matrix-core ceilings (TFLOP/s): " + ", ".join(f"{k} {v:.0f}" for k, v in MFMA_CEIL.items()))
     return mixes
+
+
+# measured register-only MFMA loop rates, filled by hbm_ceilings()
+MFMA_CEIL = {}
+
+
+def with_mfma_ceiling(roof, key="bf16_16x16x32"):
+    """Adds the measured matrix-core ceiling to an MFMA-bound roofline."""
+    c = MFMA_CEIL.get(key)
+    if c:
+        roof["measured_ceiling"] = c
+        roof["frac_of_measured_ceiling"] = round(roof["achieved"] / c, 4)
+    return roof
 
 
 # ---------------------------------------------------------------- bytes ----
@@ -306,6 +324,10 @@ def step_roofline(kind, B, H, N, D, M, es, ms, kernels, traffic_file, counters_f
                                                        ai * PEAK_HBM_GBS / 1e3), 1),
             "note": "every pass is HBM-bound at this shape (intensity far below the ridge point), so the "
                     "binding roofline is HBM bandwidth"}
+    mc = MFMA_CEIL.get("bf16_16x16x32" if es == 2 else "f32_16x16x4")
+    if mc:
+        mfma["measured_ceiling"] = mc
+        mfma["frac_of_measured_ceiling"] = {c: round(v / mc, 4) for c, v in tfl.items()}
     ct = read_profile_table(counters_file, cols=None)
     if ct is not None:
         per = {}
@@ -463,6 +485,10 @@ def bench_fwdbwd(la, torch, args, ceil):
             "source": "streaming microbenchmark on this GPU (kernelized_causal_attention_amd/_lib/hbm_ceiling): "
                       "plain 16-byte-vector kernels over 134 MB tensors, GB/s per traffic mix",
             "mixes": ceil, "dominant_mix": mix}
+    if MFMA_CEIL:
+        result["mfma_ceiling"] = {
+            "source": "register-only loop of independent MFMAs over the whole chip (same program), TFLOP/s",
+            "TFLOPs": dict(MFMA_CEIL), "spec": {"bf16_16x16x32": PEAK_BF16_TFLOPS, "f32_16x16x4": PEAK_F32_TFLOPS}}
     return result
 
 
@@ -1016,9 +1042,10 @@ def bench_poly(la, torch, steps, warmup):
             "step_tflops": round(step_tf, 1),
             "config": {"workload": "(q.k)^2 causal attention forward+backward, bf16 in / fp32 accumulate",
                        "B": B, "H": H, "N": N, "D": D, "M": M},
-            "roofline": {"bound": "mfma", "kernel": kname, "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                         "flops_per_launch": kf, "avg_launch_ms": round(avg_ms, 4)},
+            "roofline": with_mfma_ceiling(
+                {"bound": "mfma", "kernel": kname, "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                 "flops_per_launch": kf, "avg_launch_ms": round(avg_ms, 4)}),
             "kernels": kernels, "decode": bench_poly_decode(la, torch), "crossover": bench_poly_crossover(la, torch)}
 
 
@@ -1108,9 +1135,10 @@ def bench_softmax(la, torch, steps, warmup):
             "unit": "tokens/s", "ms": round(sm_ms, 4),
             "config": {"workload": "softmax(QK^T/sqrt(D))V causal forward, bf16 in / fp32 accumulate", "B": B,
                        "H": H, "N": N, "D": D, "M": M},
-            "roofline": {"bound": "mfma", "kernel": "softmax.forward", "achieved": round(tf, 1),
-                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": None, "flops_per_launch": flops, "avg_launch_ms": round(sm_ms, 4)},
+            "roofline": with_mfma_ceiling(
+                {"bound": "mfma", "kernel": "softmax.forward", "achieved": round(tf, 1),
+                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                 "traffic": None, "flops_per_launch": flops, "avg_launch_ms": round(sm_ms, 4)}),
             "linear_forward_ms": round(la_ms, 4), "linear_forward_speedup": round(sm_ms / la_ms, 2),
             "speedup_caveat": f"ratio against this library's online-softmax forward, which runs at "
                               f"{tf / PEAK_BF16_TFLOPS:.2f} of the dense bf16 MFMA peak; at the full peak the "

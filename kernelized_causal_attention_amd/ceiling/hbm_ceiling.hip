@@ -9,6 +9,12 @@
 // r3w1 (forward), r4w1 (dq sweep), r4w2 (dk/dv sweep); and r4w2 with the
 // stores issued from an MFMA accumulator layout (8-byte pieces, 16 rows per
 // instruction) to show what that store layout costs.
+//
+// Then the matrix-core ceilings: a register-only loop of independent
+// v_mfma_f32_16x16x32_bf16 (and v_mfma_f32_16x16x4_f32) over the whole chip,
+// the rate an MFMA-bound kernel can be held against next to the 2.5 PFLOP/s
+// (157.3 TFLOP/s fp32) specification.  One JSON object per line as well,
+// keyed "mfma".
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -89,6 +95,76 @@ __global__ __launch_bounds__(256) void k_rowstore(Ptrs p, long nblk) {
   }
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ACC chains of `iters` MFMAs per wave, operands from the thread index so
+// nothing folds; the sum is stored (per lane) only when it takes a value it
+// never takes, which keeps the loop alive.  A wave needs about 16
+// independent 16x16 accumulators before the dependent-issue latency stops
+// limiting it (bf16 at four waves per SIMD: 8 chains ~1.3 PFLOP/s, 16
+// chains ~2.1), so the loops run 16 (16x16 shapes) or 4 (32x32).
+template <int ACC>
+__global__ __launch_bounds__(256) void k_mfma_bf16(int iters, float* sink) {
+  bf16x8_t a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = static_cast<__bf16>(1.0f + 0.001f * static_cast<float>((threadIdx.x + e) & 63));
+    b[e] = static_cast<__bf16>(0.5f - 0.001f * static_cast<float>((threadIdx.x * 3 + e) & 63));
+  }
+  f32x4_t c[ACC];
+#pragma unroll
+  for (int j = 0; j < ACC; ++j) c[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it)
+#pragma unroll
+    for (int j = 0; j < ACC; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[j], 0, 0, 0);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < ACC; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+  if (s == -1.0f) sink[threadIdx.x] = s;
+}
+
+template <int ACC>
+__global__ __launch_bounds__(256) void k_mfma_bf16_32(int iters, float* sink) {
+  bf16x8_t a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = static_cast<__bf16>(1.0f + 0.001f * static_cast<float>((threadIdx.x + e) & 63));
+    b[e] = static_cast<__bf16>(0.5f - 0.001f * static_cast<float>((threadIdx.x * 3 + e) & 63));
+  }
+  f32x16_t c[ACC];
+#pragma unroll
+  for (int j = 0; j < ACC; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) c[j][e] = 0.f;
+  for (int it = 0; it < iters; ++it)
+#pragma unroll
+    for (int j = 0; j < ACC; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[j], 0, 0, 0);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < ACC; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += c[j][e];
+  if (s == -1.0f) sink[threadIdx.x] = s;
+}
+
+template <int ACC>
+__global__ __launch_bounds__(256) void k_mfma_f32(int iters, float* sink) {
+  const float a = 1.0f + 0.001f * static_cast<float>(threadIdx.x & 63);
+  const float b = 0.5f - 0.001f * static_cast<float>((threadIdx.x * 3) & 63);
+  f32x4_t c[ACC];
+#pragma unroll
+  for (int j = 0; j < ACC; ++j) c[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it)
+#pragma unroll
+    for (int j = 0; j < ACC; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c[j], 0, 0, 0);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < ACC; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+  if (s == -1.0f) sink[threadIdx.x] = s;
+}
+
 template <typename F>
 float best_us(F launch) {
   hipEvent_t e0, e1;
@@ -158,6 +234,30 @@ int main() {
   std::printf("{\"mix\": \"r4w2_rowstore\", \"read_bytes\": %.0f, \"write_bytes\": %.0f, \"us\": %.1f, \"GBps\": %.0f}\n",
               4.0 * kBytes, 2.0 * kBytes, best, 6.0 * kBytes / best / 1e3);
   for (auto& b : buf) CHECK(hipFree(b));
+  // matrix cores: 16 wave64s per CU (4 per SIMD), 256 CUs
+  float* fsink = nullptr;
+  CHECK(hipMalloc(&fsink, 256 * sizeof(float)));
+  int dev = 0, ncu = 0;
+  CHECK(hipGetDevice(&dev));
+  CHECK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+  const int grid = 4 * ncu;
+  struct MfmaCase {
+    const char* name;
+    void (*kern)(int, float*);
+    int iters;
+    double flops_per_iter;  // per wave
+  };
+  const MfmaCase cases[] = {{"bf16_16x16x32", k_mfma_bf16<16>, 2048, 16 * (16.0 * 16 * 32 * 2)},
+                            {"bf16_32x32x16", k_mfma_bf16_32<4>, 2048, 4 * (32.0 * 32 * 16 * 2)},
+                            {"f32_16x16x4", k_mfma_f32<16>, 512, 16 * (16.0 * 16 * 4 * 2)}};
+  for (const auto& c : cases) {
+    const float us = best_us([&] { hipLaunchKernelGGL(c.kern, dim3(grid), dim3(256), 0, 0, c.iters, fsink); });
+    CHECK(hipGetLastError());
+    const double flops = static_cast<double>(grid) * 4 * c.iters * c.flops_per_iter;
+    std::printf("{\"mfma\": \"%s\", \"flops\": %.0f, \"us\": %.1f, \"TFLOPs\": %.1f, \"grid\": %d}\n", c.name,
+                flops, us, flops / us / 1e6, grid);
+  }
+  CHECK(hipFree(fsink));
   CHECK(hipFree(sink));
   return 0;
 }
