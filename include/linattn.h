@@ -181,14 +181,16 @@ size_t la_saved_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
  * rounding, and for phi ~ 1 the two terms of grad phi(Q) cancel in the
  * all-ones direction several times over, so dq would lose about a decimal
  * digit.
- * Precision (bf16): the MFMA kernels feed bf16 phi or elu, V and g to the
- * matrix cores with fp32 accumulation; against the fp64 result the
- * gradients' relative L2 error measures ~3e-3 for q, k ~ N(0, 1/D) or
- * N(0, 1) and v, dout ~ N(0, 1).  Where most features sit far below zero
- * (phi = e^x small), the dq sweep's phi = 1 + elu split holds phi to an
- * absolute rather than a relative 2^-9: with q, k ~ N(-3, 1) dq measures
- * 1.9e-2 (dk, dv 3e-3 to 6e-3), and it grows as the features move further
- * down.  fp32 inputs: ~1e-6. */
+ * Precision (bf16): the MFMA kernels feed bf16 operands to the matrix cores
+ * with fp32 accumulation; where a sum would cancel along the all-ones
+ * direction of phi ~ 1 they split phi = mu + E per feature (mu = 1 where a
+ * segment's keys have phi ~ 1, 0 where phi << 1) and keep the mu part in
+ * fp32.  Against the fp64 result the gradients' relative L2 error measures
+ * 2e-3 to 4e-3 for q, k ~ N(0, 1/D) or N(0, 1), for q, k ~ N(-3, 1), with
+ * every other feature shifted to -3, and with only the keys shifted
+ * (v ~ N(0, 1/D) or N(0, 1), dout ~ N(0, 1)); features below about -12,
+ * where phi < 1e-5 is held to fp32's absolute rounding, are not covered.
+ * fp32 inputs: ~1e-6. */
 la_status la_backward(const void* q, const void* k, const void* v, const void* out,
                       const void* dout, const float* den, void* dq, void* dk, void* dv,
                       int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,

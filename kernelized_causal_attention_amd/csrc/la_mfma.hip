@@ -482,11 +482,13 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mfma_t128(const bf16_t* __restri
 }
 
 // Segment aggregates dS = phi(K)^T V, dZ = colsum phi(K) over one segment.
-// phi(K) = 1 + E(K) is split so that the records are as exact as fp32
-// allows: the MFMAs sum E(K)^T V and colsum E(K) with E = elu carried as
-// bf16 (a rounding relative to E, not to phi ~ 1), and the ones part enters
-// in fp32 as dS = 1 (colsum V)^T + E^T V, dZ = count + colsum E.  The
-// backward splits the carried states again and relies on that precision.
+// phi(K) = mu + E(K) is split (mu in {0, 1} per feature, from the segment's
+// first chunk: decide_mu) so that the records are as exact as fp32 allows:
+// the MFMAs sum E(K)^T V and colsum E(K) with E carried as bf16 (elu where
+// phi ~ 1, a rounding relative to E rather than to 1; phi itself where
+// phi << 1), and the mu part enters in fp32 as dS = mu (colsum V)^T + E^T V,
+// dZ = mu count + colsum E.  The backward splits the carried states again
+// and relies on that precision.
 template <int DIM>
 __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_seg_state_mfma(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                                        float* __restrict__ s_out, int64_t s_stride,
@@ -498,6 +500,8 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_seg_state_mfma(const
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* sKe = smem;
   uint16_t* sV = sKe + T * LD;
+  float* sMuF = reinterpret_cast<float*>(sV + T * LD);
+  uint16_t* sMuB = reinterpret_cast<uint16_t*>(sMuF + DIM);
   // w is made wave-uniform (an SGPR) so that branches on it are scalar: an
   // MFMA under an EXEC-masked branch still writes every lane.
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
@@ -518,11 +522,16 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_seg_state_mfma(const
   const short one = 0x3f80;  // bf16 1.0
   const i16x8 ones = {one, one, one, one, one, one, one, one};
   i32x4 kraw[PC], vraw[PC];
-  // rows past the head's end load as zero (elu(0) = 0, V = 0)
+  // rows past the head's end load as zero (V = 0; E is zeroed past nrow)
   bload_tile<DIM, NW>(kraw, rk, static_cast<int>(r0 * DIM * 2));
   bload_tile<DIM, NW>(vraw, rv, static_cast<int>(r0 * DIM * 2));
+  store_tile_e<DIM, NW>(sKe, kraw);
+  __syncthreads();
+  decide_mu<DIM, LD>(sKe, static_cast<int>(min(static_cast<int64_t>(T), r1 - r0)), sMuF, sMuB);
+  __syncthreads();
+  const MuOff moff = mu_offsets<DIM, NW>(sMuF);
   for (int64_t c0 = r0; c0 < r1; c0 += T) {
-    store_tile_e<DIM, NW>(sKe, kraw);
+    store_tile_emu<DIM, NW>(sKe, kraw, static_cast<int>(min(static_cast<int64_t>(T), r1 - c0)), moff);
     store_tile_v<DIM, NW>(sV, vraw);
     __syncthreads();
     if (c0 + T < r1) {
@@ -550,9 +559,11 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_seg_state_mfma(const
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int d = d0 + 4 * g + u;
+      const float mu = sMuF[d];
 #pragma unroll
-      for (int n = 0; n < NTL; ++n) s_out[rec * s_stride + d * DIM + 16 * n + li] = Sacc[dt][n][u] + sU[16 * n + li];
-      if (li == 0) z_out[rec * z_stride + d] = zacc[dt][u] + count;
+      for (int n = 0; n < NTL; ++n)
+        s_out[rec * s_stride + d * DIM + 16 * n + li] = Sacc[dt][n][u] + mu * sU[16 * n + li];
+      if (li == 0) z_out[rec * z_stride + d] = zacc[dt][u] + mu * count;
     }
   }
 }
@@ -563,8 +574,8 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_seg_state_mfma(const
 // in a private LDS tile, so the chunk loop has no workgroup barrier and
 // every staged element is read from LDS once (the A and B operands of all
 // sixteen tiles are held in registers).  The four partials are added in
-// wave order at the end.  Same split as above: dS = 1 U^T + E^T V,
-// dZ = count + colsum E.
+// wave order at the end.  Same split as above: dS = mu U^T + E^T V,
+// dZ = mu count + colsum E, with mu chosen from the segment's first chunk.
 __global__ __launch_bounds__(256, 2) void k_seg_state_wave64(const bf16_t* __restrict__ k,
                                                              const bf16_t* __restrict__ v, float* __restrict__ s_out,
                                                              int64_t s_stride, float* __restrict__ z_out,
@@ -605,8 +616,11 @@ __global__ __launch_bounds__(256, 2) void k_seg_state_wave64(const bf16_t* __res
     }
   };
   if (w < nch) fetch(w);
-  for (int c = w; c < nch; c += 4) {
-    // rows past the head's end loaded as zero: elu(0) = 0, V = 0
+  // the split constant mu: wave 0 stages the segment's first chunk as elu
+  // (rows past the head's end load as zero, elu(0) = 0) for decide_mu
+  float* sMuF = reinterpret_cast<float*>(smem + 4 * 2 * T * LD);
+  uint16_t* sMuB = reinterpret_cast<uint16_t*>(sMuF + DIM);
+  if (w == 0) {
 #pragma unroll
     for (int p = 0; p < PW; ++p) {
       const int e = 64 * p + l;
@@ -614,6 +628,21 @@ __global__ __launch_bounds__(256, 2) void k_seg_state_wave64(const bf16_t* __res
 #pragma unroll
       for (int q = 0; q < 8; ++q) x[q] = elu_fast(x[q]);
       *reinterpret_cast<i16x8*>(sK + (e >> 3) * LD + (e & 7) * 8) = pack8(x);
+    }
+  }
+  __syncthreads();
+  decide_mu<DIM, LD>(smem, static_cast<int>(min(static_cast<int64_t>(T), r1 - r0)), sMuF, sMuB);
+  __syncthreads();
+  const MuOff moff = mu_offsets<DIM>(sMuF);
+  for (int c = w; c < nch; c += 4) {
+    // rows past the head's end: V loaded as zero, E stored as zero
+    const int nr = static_cast<int>(min(static_cast<int64_t>(T), r1 - r0 - static_cast<int64_t>(c) * T));
+#pragma unroll
+    for (int p = 0; p < PW; ++p) {
+      const int e = 64 * p + l;
+      const i16x8 ke = emu8(kr[p], moff);
+      *reinterpret_cast<i16x8*>(sK + (e >> 3) * LD + (e & 7) * 8) =
+          (e >> 3) < nr ? ke : i16x8{0, 0, 0, 0, 0, 0, 0, 0};
       *reinterpret_cast<i16x8*>(sV + (e >> 3) * LD + (e & 7) * 8) = __builtin_bit_cast(i16x8, vr[p]);
     }
     if (c + 4 < nch) fetch(c + 4);
@@ -672,11 +701,11 @@ __global__ __launch_bounds__(256, 2) void k_seg_state_wave64(const bf16_t* __res
   for (int d = tid >> 6; d < DIM; d += 4) {
     const float sum = ((Sp[d * RP + m] + Sp[(DIM + d) * RP + m]) + Sp[(2 * DIM + d) * RP + m]) +
                       Sp[(3 * DIM + d) * RP + m];
-    s_out[rec * s_stride + d * DIM + m] = sum + um;
+    s_out[rec * s_stride + d * DIM + m] = sum + sMuF[d] * um;
   }
   if (tid < DIM)
     z_out[rec * z_stride + tid] =
-        (((Zp[tid] + Zp[DIM + tid]) + Zp[2 * DIM + tid]) + Zp[3 * DIM + tid]) + count;
+        (((Zp[tid] + Zp[DIM + tid]) + Zp[2 * DIM + tid]) + Zp[3 * DIM + tid]) + sMuF[tid] * count;
 }
 
 size_t lds_fwd(int dim) {
@@ -688,12 +717,16 @@ size_t lds_fwd(int dim) {
 size_t lds_fwd_t128() {
   return (2 * T2 * (64 + kLdsPad) + 64 * (64 + kLdsPad) + 2 * 64 + 4 * 16 * (64 + kLdsPad)) * sizeof(uint16_t);
 }
-size_t lds_seg(int dim) { return 2 * T * (dim + kLdsPad) * sizeof(uint16_t); }
-// four wave-private K / V tile pairs; the partials reuse the space at the end
+// (each + the split constant mu as fp32 and bf16)
+size_t lds_seg(int dim) { return 2 * T * (dim + kLdsPad) * sizeof(uint16_t) + dim * (sizeof(float) + sizeof(uint16_t)); }
+// four wave-private K / V tile pairs (the partials reuse the space at the
+// end), then mu
 size_t lds_seg_wave64() {
   const size_t tiles = 4 * 2 * T * (64 + kLdsPad) * sizeof(uint16_t);
   const size_t parts = (4 * 64 * (64 + 4) + 2 * 4 * 64) * sizeof(float);
-  return tiles > parts ? tiles : parts;
+  static_assert((4 * 64 * (64 + 4) + 2 * 4 * 64) * sizeof(float) <= 4 * 2 * T * (64 + kLdsPad) * sizeof(uint16_t),
+                "the partials fit below mu");
+  return (tiles > parts ? tiles : parts) + 64 * (sizeof(float) + sizeof(uint16_t));
 }
 
 #define LA_MLAUNCH(kernel, nthreads, grid, lds, st, ...)                                                \

@@ -175,30 +175,37 @@ __device__ __forceinline__ void outer_update(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>
 }
 
 // Variants of the helpers above for the forward sweep, which writes
-// phi = 1 + E (E = elu) and keeps the prefix state split as
-//   S = 1 U^T + S',  Z = n 1 + Z'.
+// phi = mu + E (mu in {0, 1} per feature, chosen per segment: decide_mu)
+// and keeps the prefix state split as
+//   S = mu U^T + S',  Z = n mu + Z'.
 // The split is exact for any U and n; it pays when S' and Z' are small, i.e.
-// when U and n carry the ones direction of S and Z.  Within the sweep the
+// when U and n carry the mu direction of S and Z.  Within the sweep the
 // kernel keeps U = sum_j V_j, n = number of tokens, S' = sum_j E(K_j) V_j^T,
-// Z' = sum_j E(K_j); for a carried-in state (S, Z) it takes U = mean over d
-// of S[d][:] and n = mean over d of Z[d] (for a state built from tokens these
-// leave S', Z' no larger than the token sums do, and they need nothing but
-// S and Z).  y holds, for the wave's column tiles, a vector over m in the
-// X^T accumulator layout: lane holds y[16mt + 4g + u].
+// Z' = sum_j E(K_j); for a carried-in state (S, Z) it takes U = mean of
+// S[d][:] and n = mean of Z[d] over the features with mu_d = 1 (for a state
+// built from tokens these leave S', Z' no larger than the token sums do, and
+// they need nothing but S and Z; with no such feature U = 0, n = 0).  y
+// holds, for the wave's column tiles, a vector over m in the X^T accumulator
+// layout: lane holds y[16mt + 4g + u].  smu = sum of mu.
 template <int DIM>
 __device__ __forceinline__ float init_split(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&x)[Geo<DIM>::DT],
-                                            f32x4_t (&y)[Geo<DIM>::DT], const float* __restrict__ rec, int w, int g,
-                                            int li) {
+                                            f32x4_t (&y)[Geo<DIM>::DT], const float* __restrict__ rec,
+                                            const float* sMuF, float smu, int w, int g, int li) {
   using G = Geo<DIM>;
-  // n = mean of Z: every wave sums all D entries (lane l reads Z[l], Z[l + 64])
+  const float inv = smu > 0.f ? 1.f / smu : 0.f;
+  // n = mean of Z over the mu features: every wave sums all D entries (lane
+  // l reads Z[l], Z[l + 64])
   float n = 0.f;
   if (rec) {
 #pragma unroll
-    for (int d0 = 0; d0 < DIM; d0 += 64) n += rec[DIM * DIM + d0 + (threadIdx.x & 63)];
+    for (int d0 = 0; d0 < DIM; d0 += 64) n += sMuF[d0 + (threadIdx.x & 63)] * rec[DIM * DIM + d0 + (threadIdx.x & 63)];
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) n += __shfl_xor(n, off, 64);
-    n *= 1.f / DIM;
+    n *= inv;
   }
+  float mud[G::NTL];  // mu of this lane's rows d = 16 n_ + li
+#pragma unroll
+  for (int n_ = 0; n_ < G::NTL; ++n_) mud[n_] = sMuF[16 * n_ + li];
 #pragma unroll
   for (int a = 0; a < G::DT; ++a) {
     const int mt = w * G::DT + a;
@@ -206,22 +213,34 @@ __device__ __forceinline__ float init_split(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>:
     for (int n_ = 0; n_ < G::NTL; ++n_)
 #pragma unroll
       for (int u = 0; u < 4; ++u) X[a][n_][u] = rec ? rec[(16 * n_ + li) * DIM + 16 * mt + 4 * g + u] : 0.f;
-    // U[m] = mean over d = 16 n_ + li: in-lane over n_, then over the 16 li
+    // U[m] = mean over the mu features d = 16 n_ + li: in-lane over n_, then
+    // over the 16 li
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      float s = 0.f;
+      float s_ = 0.f;
 #pragma unroll
-      for (int n_ = 0; n_ < G::NTL; ++n_) s += X[a][n_][u];
+      for (int n_ = 0; n_ < G::NTL; ++n_) s_ += mud[n_] * X[a][n_][u];
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off, 64);
-      y[a][u] = s * (1.f / DIM);
+      for (int off = 1; off < 16; off <<= 1) s_ += __shfl_xor(s_, off, 64);
+      y[a][u] = s_ * inv;
 #pragma unroll
-      for (int n_ = 0; n_ < G::NTL; ++n_) X[a][n_][u] -= y[a][u];
+      for (int n_ = 0; n_ < G::NTL; ++n_) X[a][n_][u] -= mud[n_] * y[a][u];
     }
-    const float z = rec ? rec[DIM * DIM + 16 * mt + li] - n : 0.f;
+    const float z = rec ? rec[DIM * DIM + 16 * mt + li] - sMuF[16 * mt + li] * n : 0.f;
     x[a] = f32x4_t{z, z, z, z};
   }
   return n;
+}
+
+// smu for every lane: the sum of sMuF over the DIM features.
+template <int DIM>
+__device__ __forceinline__ float mu_sum(const float* sMuF) {
+  float m = 0.f;
+#pragma unroll
+  for (int d0 = 0; d0 < DIM; d0 += 64) m += sMuF[d0 + (threadIdx.x & 63)];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) m += __shfl_xor(m, off, 64);
+  return m;
 }
 
 template <int DIM>
@@ -269,20 +288,22 @@ __device__ __forceinline__ void outer_update_y(f32x4_t (&X)[Geo<DIM>::DT][Geo<DI
   }
 }
 
-// Suffix record (R, r) from R = R' + 1 G^T, r = r' + C 1.
+// Suffix record (R, r) from R = R' + mu G^T, r = r' + C mu.
 template <int DIM>
 __device__ __forceinline__ void store_r(float* __restrict__ rec, const f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL],
                                         const f32x4_t (&x)[Geo<DIM>::DT], const f32x4_t (&y)[Geo<DIM>::DT], float C,
-                                        int w, int g, int li) {
+                                        const float* sMuF, int w, int g, int li) {
   using G = Geo<DIM>;
 #pragma unroll
   for (int a = 0; a < G::DT; ++a) {
     const int mt = w * G::DT + a;
 #pragma unroll
-    for (int n = 0; n < G::NTL; ++n)
+    for (int n = 0; n < G::NTL; ++n) {
+      const float mu = sMuF[16 * n + li];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) rec[(16 * n + li) * DIM + 16 * mt + 4 * g + u] = X[a][n][u] + y[a][u];
-    if (g == 0) rec[DIM * DIM + 16 * mt + li] = x[a][0] + C;
+      for (int u = 0; u < 4; ++u) rec[(16 * n + li) * DIM + 16 * mt + 4 * g + u] = X[a][n][u] + mu * y[a][u];
+    }
+    if (g == 0) rec[DIM * DIM + 16 * mt + li] = x[a][0] + sMuF[16 * mt + li] * C;
   }
 }
 
@@ -291,27 +312,28 @@ __device__ __forceinline__ void store_r(float* __restrict__ rec, const f32x4_t (
 // segment's (R, r) aggregate when r_agg != null.
 //
 // grad phi(Q_i) = sum_{j<=i} phi(K_j) b_ij with b_ij = g_i.V_j + c_i, and
-// sum_{j<=i} A_ij b_ij = 0 exactly (that is what out_i is): the gradient is
-// what is left after the ones direction of phi(K) ~ 1 cancels, a few times
-// smaller than its terms.  Rounding phi(K), S or b to bf16 puts an error
-// into that ones direction which the cancellation then amplifies, so this
-// kernel writes phi(K_j) = 1 + E_j with E = elu carried as bf16 and every
-// ones-direction term in fp32:
-//   grad phi(Q_i) = beta_i 1 + S' g_i + c_i Z' + sum_{j<=i in chunk} E_j b_ij
+// sum_{j<=i} A_ij b_ij = 0 exactly (that is what out_i is): where phi(K) ~ 1
+// the gradient is what is left after that ones direction cancels, a few
+// times smaller than its terms.  Rounding phi(K), S or b to bf16 puts an
+// error into that direction which the cancellation then amplifies, so this
+// kernel writes phi = mu + E, with mu in {0, 1} per feature (1 where the
+// segment's keys have phi ~ 1, 0 where phi << 1: decide_mu) and E carried as
+// bf16, and keeps every mu-direction term in fp32:
+//   grad phi(Q_i) = beta_i mu + S' g_i + c_i Z' + sum_{j<=i in chunk} E_j b_ij
 //   beta_i = sum_{j<=i} b_ij = g_i.U + n_i c_i + sum_{j in chunk} g_i.V_j
 // with (S', Z', U) the state before the chunk (split as above), n_i the
 // number of keys j <= i, and g_i = bf16(dout_i / den_i).  The same split of
-// phi(Q_i) = 1 + E_i gives the scores and the denominator in fp32 from
-// bf16 E's:
-//   A_ij = D + sum_d E_i + sum_d E_j + E_i.E_j
-//   den_i = sum_{j in chunk} A_ij + n0 (D + sum_d E_i) + sum_d (1 + E_i) Z'
+// phi(Q_i) = mu + E_i gives the scores and the denominator in fp32 from
+// bf16 E's (mu.mu = smu, the number of mu features):
+//   A_ij = smu + mu.E_i + mu.E_j + E_i.E_j
+//   den_i = sum_{j in chunk} A_ij + n0 (smu + mu.E_i) + sum_d (mu + E_i) Z'
 // and c_i = -(g_i . num_i) / den_i from the same pieces:
-//   g_i . num_i = sum_j A_ij (g_i.V_j) + (D + sum_d E_i)(g_i.U)
-//                 + sum_d (1 + E_i)[d] (S' g_i)[d].
+//   g_i . num_i = sum_j A_ij (g_i.V_j) + (smu + mu.E_i)(g_i.U)
+//                 + sum_d (mu + E_i)[d] (S' g_i)[d].
 // The query, g and c tiles are double-buffered so that the (R, r) aggregate
 // of a chunk is summed after the chunk's last barrier: two barriers per
-// chunk.  R and r are accumulated the same way, R = 1 G^T + sum_i E_i g_i^T
-// and r = C 1 + sum_i c_i E_i with G = sum_i g_i, C = sum_i c_i.
+// chunk.  R and r are accumulated the same way, R = mu G^T + sum_i E_i g_i^T
+// and r = C mu + sum_i c_i E_i with G = sum_i g_i, C = sum_i c_i.
 // ---------------------------------------------------------------------------
 // FUSED_R: the (R, r) aggregate is summed here (D = 64); at D = 128 the two
 // fp32 128 x 128 states do not fit one wave's registers together, and
@@ -320,7 +342,51 @@ __device__ __forceinline__ void store_r(float* __restrict__ rec, const f32x4_t (
 // row tile (the triangle of key tiles) resolves at compile time, and the
 // chunk body becomes one stretch of code to schedule (the dq sweep is
 // bound by its instruction issue; 162 -> 153 us at B=8 H=16 N=8192 D=64).
-template <int DIM, bool CAUSAL, bool FUSED_R, int RW>
+// MU1: every mu of the segment is 1 (the usual case), and the mu terms are
+// compile-time constants; otherwise they come from LDS (dq_decide_mu ran
+// first in either case).
+// Where the dq sweep keeps mu in LDS: after its tiles, state, c pairs and
+// output staging (the layout dq_body carves and lds_dq sizes).
+template <int DIM>
+__device__ __forceinline__ float* dq_mu_lds(uint16_t* smem) {
+  constexpr int LD = Geo<DIM>::LD;
+  uint16_t* sS = smem + 6 * T * LD;
+  float* sRed = reinterpret_cast<float*>(sS + DIM * LD) + 2 * DIM;
+  uint16_t* sStage = reinterpret_cast<uint16_t*>(sRed + 4) + 4 * T;
+  return reinterpret_cast<float*>(sStage + 4 * 16 * LD);
+}
+
+// The split constant mu of one segment's dq sweep into LDS (fp32 and bf16):
+// decide_mu over the segment's first chunk of keys (causal), or from the
+// mean phi(K) of the carried totals, Z / N (non-causal).  Returns the number
+// of mu features.  Ends with a barrier.
+template <int DIM, bool CAUSAL>
+__device__ __forceinline__ float dq_decide_mu(const bf16_t* __restrict__ k, const float* __restrict__ carry_s,
+                                              int64_t N, int P, int seg_len, int64_t bh, int seg) {
+  using G = Geo<DIM>;
+  extern __shared__ __align__(16) uint16_t smem[];
+  float* sMuF = dq_mu_lds<DIM>(smem);
+  uint16_t* sMuB = reinterpret_cast<uint16_t*>(sMuF + DIM);
+  const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
+  const int64_t r1 = min(N, r0 + seg_len);
+  if constexpr (CAUSAL) {
+    i32x4 kraw[G::PC];
+    bload_tile<DIM>(kraw, make_rsrc(k + bh * N * DIM, N * DIM * 2), static_cast<int>(r0 * DIM * 2));
+    store_tile_e<DIM>(smem, kraw);  // the E(K) tile's place; the sweep overwrites it
+    __syncthreads();
+    decide_mu<DIM, G::LD>(smem, static_cast<int>(min(static_cast<int64_t>(T), r1 - r0)), sMuF, sMuB);
+  } else if (threadIdx.x < DIM) {
+    constexpr int64_t ER = static_cast<int64_t>(DIM) * DIM + DIM;
+    const float* cs = carry_s ? carry_s + bh * ER : nullptr;
+    const float mu = (cs && cs[DIM * DIM + threadIdx.x] < 0.5f * static_cast<float>(N)) ? 0.f : 1.f;
+    sMuF[threadIdx.x] = mu;
+    sMuB[threadIdx.x] = mu != 0.f ? 0x3f80 : 0;
+  }
+  __syncthreads();
+  return mu_sum<DIM>(sMuF);
+}
+
+template <int DIM, bool CAUSAL, bool FUSED_R, int RW, bool MU1>
 __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                         const bf16_t* __restrict__ dout, const float* __restrict__ carry_s,
                                         bf16_t* __restrict__ dq, float* __restrict__ r_agg, float* __restrict__ c_out,
@@ -339,6 +405,8 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
   float* sRed = sU + DIM;              // 4 floats: per-wave sums of c
   uint16_t* sCh2 = reinterpret_cast<uint16_t*>(sRed + 4);  // c hi/lo, two buffers of 2T
   uint16_t* sStage = sCh2 + 4 * T;     // per-wave dq staging, 16 x LD each
+  const float* sMuF = dq_mu_lds<DIM>(smem);  // the split constant mu, fp32 (dq_decide_mu)
+  const uint16_t* sMuB = reinterpret_cast<const uint16_t*>(sMuF + DIM);  // and as bf16
 
   // w is made wave-uniform (an SGPR) so that branches on it are scalar: an
   // MFMA under an EXEC-masked branch still writes every lane.
@@ -359,8 +427,6 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
   const int i = 16 * rw + li;
   const int cc = 4 * (li % 4);
   uint16_t* sDQ = sStage + w * 16 * LD;
-  const short one = 0x3f80;  // bf16 1.0
-  const i16x8 ones = {one, one, one, one, one, one, one, one};
   // causal mask of key j = 16t + 4g + u against query i = 16w + li, as 0 / 1
   // factors (kept in VGPRs: as per-(t, u) lane masks they would not fit in
   // the scalar registers)
@@ -369,15 +435,6 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int u = 0; u < 4; ++u) mt[t][u] = (t < rw || (t == rw && 4 * g + u <= li)) ? 1.f : 0.f;
-
-  f32x4_t Sacc[DT][NTL], zacc[DT], uacc[DT];
-  // n0: the ones-direction count of the state before the current chunk
-  float n0 = init_split<DIM>(Sacc, zacc, uacc, cs, w, g, li);
-  f32x4_t Racc[FUSED_R ? DT : 1][FUSED_R ? NTL : 1], racc[FUSED_R ? DT : 1], gacc[FUSED_R ? DT : 1];
-  if constexpr (FUSED_R) init_split<DIM>(Racc, racc, gacc, nullptr, w, g, li);
-  write_xt<DIM>(sS, sZ, Sacc, zacc, w, g, li);
-  write_y<DIM>(sU, uacc, w, g, li);
-  float csum = 0.f;
 
   int64_t c0 = r0;
   int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
@@ -392,16 +449,35 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
   };
   fetch(static_cast<int>(c0 * DIM * 2));
 
+  const float smu = MU1 ? static_cast<float>(DIM) : mu_sum<DIM>(sMuF);
+  MuOff moff;
+  if constexpr (!MU1) moff = mu_offsets<DIM>(sMuF);
+  const short one = 0x3f80;  // bf16 1.0
+  const i16x8 ones = {one, one, one, one, one, one, one, one};
+
+  f32x4_t Sacc[DT][NTL], zacc[DT], uacc[DT];
+  // n0: the mu-direction count of the state before the current chunk
+  float n0 = init_split<DIM>(Sacc, zacc, uacc, cs, sMuF, smu, w, g, li);
+  f32x4_t Racc[FUSED_R ? DT : 1][FUSED_R ? NTL : 1], racc[FUSED_R ? DT : 1], gacc[FUSED_R ? DT : 1];
+  if constexpr (FUSED_R) init_split<DIM>(Racc, racc, gacc, nullptr, sMuF, smu, w, g, li);
+  write_xt<DIM>(sS, sZ, Sacc, zacc, w, g, li);
+  write_y<DIM>(sU, uacc, w, g, li);
+  float csum = 0.f;
+
   int buf = 0;
   while (c0 < r1) {
     uint16_t* sQe = sQe2 + buf * T * LD;
     uint16_t* sG = sG2 + buf * T * LD;
     uint16_t* sCh = sCh2 + buf * 2 * T;
-    if (CAUSAL) {
-      store_tile_e<DIM>(sKe, kraw);
-      store_tile_v<DIM>(sV, vraw);
+    // rows past the head's end were loaded as zero (elu(0) = 0)
+    if constexpr (MU1) {
+      if (CAUSAL) store_tile_e<DIM>(sKe, kraw);
+      store_tile_e<DIM>(sQe, qraw);
+    } else {
+      if (CAUSAL) store_tile_emu<DIM>(sKe, kraw, nrow, moff);
+      store_tile_emu<DIM>(sQe, qraw, nrow, moff);
     }
-    store_tile_e<DIM>(sQe, qraw);
+    if (CAUSAL) store_tile_v<DIM>(sV, vraw);
     __syncthreads();
     const bool valid = i < nrow;
     i32x4 gcur[KS];
@@ -425,18 +501,23 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
     f32x4_t qd[NTL];
 #pragma unroll
     for (int n = 0; n < NTL; ++n) qd[n] = unpack4(*reinterpret_cast<const i16x4*>(sQe + i * LD + 16 * n + 4 * g));
-    // phi(Q_i) = 1 + E in the accumulator layout (an arithmetic result, so
+    // phi(Q_i) = mu + E in the accumulator layout (an arithmetic result, so
     // the min below needs no NaN canonicalisation)
     f32x4_t pq[NTL];
 #pragma unroll
-    for (int n = 0; n < NTL; ++n) pq[n] = 1.f + qd[n];
-    // sum_d phi(Q_i) = D + sum_d E(Q_i), through the MFMA against ones
+    for (int n = 0; n < NTL; ++n)
+      pq[n] = (MU1 ? f32x4_t{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4_t*>(sMuF + 16 * n + 4 * g)) + qd[n];
+    // mu as an MFMA operand (features 8g + 32s + e, the same in every row)
+    i16x8 mub[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) mub[s] = MU1 ? ones : lds8(sMuB + 8 * g + 32 * s);
+    // sum_d mu_d phi(Q_i) = smu + sum_d mu_d E(Q_i), through the MFMA against mu
     f32x4_t sq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < KS; ++s) sq = mfma(ones, qf[s], sq);
-    const float dq_i = static_cast<float>(DIM) + sq[0];
-    // --- scores A^T[j][i] = (D + sq_i) + sk_j + E_j.E_i, masked j <= i: the
-    // key row sums sk_j come from the same MFMA chain against ones
+    for (int s = 0; s < KS; ++s) sq = mfma(mub[s], qf[s], sq);
+    const float dq_i = smu + sq[0];
+    // --- scores A^T[j][i] = (smu + sq_i) + sk_j + E_j.E_i, masked j <= i:
+    // sk_j = sum_d mu_d E(K_j) from the same MFMA chain against mu
     f32x4_t at[4];
     float rs = 0.f;
     if (CAUSAL) {
@@ -448,7 +529,7 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
             const i16x8 ka = lds8(sKe + (16 * t + li) * LD + 8 * g + 32 * s);
-            at[t] = mfma(ka, ones, at[t]);
+            at[t] = mfma(ka, mub[s], at[t]);
             at[t] = mfma(ka, qf[s], at[t]);
           }
           at[t] *= mt[t];
@@ -528,7 +609,7 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
         dh[c0 + i] = den;
       }
     }
-    // --- grad phi(Q)^T[d][i] = beta + S'g + c Z'[d] + E(K)^T b, times phi'(q)
+    // --- grad phi(Q)^T[d][i] = mu_d beta + S'g + c Z'[d] + E(K)^T b, times phi'(q)
     if (CAUSAL) {
       i16x4 bt[4];
 #pragma unroll
@@ -548,10 +629,11 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
 #pragma unroll
     for (int n = 0; n < NTL; ++n) {
       const f32x4_t z = *reinterpret_cast<const f32x4_t*>(sZ + 16 * n + 4 * g);
+      const f32x4_t mu4 = MU1 ? f32x4_t{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4_t*>(sMuF + 16 * n + 4 * g);
       f32x4_t r;
       // phi'(q) = min(phi(q), 1)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) r[u] = (beta + o[n][u] + c * z[u]) * fminf(pq[n][u], 1.f);
+      for (int u = 0; u < 4; ++u) r[u] = (mu4[u] * beta + o[n][u] + c * z[u]) * fminf(pq[n][u], 1.f);
       stage_piece<DIM>(sDQ, pack4(r), li, g, n);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -580,7 +662,7 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
       if (l == 0) sRed[rw] = csum;
       __syncthreads();
       const float C = sRed[0] + sRed[1] + sRed[2] + sRed[3];
-      store_r<DIM>(r_agg + (bh * P + seg) * ER, Racc, racc, gacc, C, w, g, li);
+      store_r<DIM>(r_agg + (bh * P + seg) * ER, Racc, racc, gacc, C, sMuF, w, g, li);
     }
   }
 }
@@ -595,11 +677,22 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
   // does t + 1 key tiles); odd workgroups map wave w to tile 3 - w, so two
   // workgroups sharing a CU give every SIMD the same total.
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t bh = blockIdx.x / P;
+  const int seg = static_cast<int>(blockIdx.x % P);
+  // the same value in every thread (read from LDS after a barrier)
+  const bool mu1 = __builtin_amdgcn_readfirstlane(
+                       dq_decide_mu<DIM, CAUSAL>(k, carry_s, N, P, seg_len, bh, seg) == static_cast<float>(DIM)
+                           ? 1
+                           : 0) != 0;
   switch ((blockIdx.x & 1) ? 3 - w : w) {
-#define LA_DQ_BODY(RW_) \
-  case RW_:                                                                                              \
-    dq_body<DIM, CAUSAL, FUSED_R, RW_>(q, k, v, dout, carry_s, dq, r_agg, c_out, den_out, N, P, seg_len,   \
-                                       blockIdx.x / P, static_cast<int>(blockIdx.x % P));                 \
+#define LA_DQ_BODY(RW_)                                                                                          \
+  case RW_:                                                                                                      \
+    if (mu1)                                                                                                     \
+      dq_body<DIM, CAUSAL, FUSED_R, RW_, true>(q, k, v, dout, carry_s, dq, r_agg, c_out, den_out, N, P, seg_len, \
+                                               bh, seg);                                                         \
+    else                                                                                                         \
+      dq_body<DIM, CAUSAL, FUSED_R, RW_, false>(q, k, v, dout, carry_s, dq, r_agg, c_out, den_out, N, P,        \
+                                                seg_len, bh, seg);                                               \
     break
     LA_DQ_BODY(0);
     LA_DQ_BODY(1);
@@ -612,8 +705,9 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
 // ---------------------------------------------------------------------------
 // The segment's (R, r) aggregate as its own pass (used at D = 128): the same
 // g_i = bf16(dout_i / den_i) and c_i the forward sweep used (den, c read from
-// its outputs), summed exactly as the fused version sums them, so the
-// aggregate is the same bit for bit.
+// its outputs), summed as the fused version sums them, with R = mu G^T +
+// sum_i E(Q_i) g_i^T for a split constant mu chosen from the segment's first
+// chunk of queries (the aggregate is a whole record, so any mu gives it).
 // ---------------------------------------------------------------------------
 template <int DIM>
 __global__ __launch_bounds__(NT, 2) void k_bwd_ragg_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout,
@@ -627,6 +721,8 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_ragg_mfma(const bf16_t* __restric
   uint16_t* sG = sQe + T * LD;
   float* sRed = reinterpret_cast<float*>(sG + T * LD);
   uint16_t* sCh = reinterpret_cast<uint16_t*>(sRed + 4);
+  float* sMuF = reinterpret_cast<float*>(sCh + 2 * T);
+  uint16_t* sMuB = reinterpret_cast<uint16_t*>(sMuF + DIM);
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t bh = blockIdx.x / P;
@@ -640,19 +736,29 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_ragg_mfma(const bf16_t* __restric
   const float* denh = den_in + bh * N;
   const float* chh = c_in + bh * N;
   const int i = 16 * w + li;
+  i32x4 qraw[PC], graw[KS];
+  {
+    // the split constant from the first chunk of queries
+    bload_tile<DIM>(qraw, rq, static_cast<int>(r0 * DIM * 2));
+    store_tile_e<DIM>(sQe, qraw);
+    __syncthreads();
+    decide_mu<DIM, LD>(sQe, static_cast<int>(min(static_cast<int64_t>(T), r1 - r0)), sMuF, sMuB);
+    __syncthreads();
+  }
+  const float smu = mu_sum<DIM>(sMuF);
+  const MuOff moff = mu_offsets<DIM>(sMuF);
   f32x4_t Racc[DT][NTL], racc[DT], gacc[DT];
-  init_split<DIM>(Racc, racc, gacc, nullptr, w, g, li);
+  init_split<DIM>(Racc, racc, gacc, nullptr, sMuF, smu, w, g, li);
   float csum = 0.f;
   for (int64_t c0 = r0; c0 < r1; c0 += T) {
     const int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
     const int soff = static_cast<int>(c0 * DIM * 2);
-    i32x4 qraw[PC], graw[KS];
     bload_tile<DIM>(qraw, rq, soff);
     bload_q<DIM>(graw, rg, soff, i, g);
     const bool valid = i < nrow;
     const float inv = valid ? __builtin_amdgcn_rcpf(denh[c0 + i]) : 0.f;  // as in the forward sweep
     const float c = valid ? chh[c0 + i] : 0.f;
-    store_tile_e<DIM>(sQe, qraw);
+    store_tile_emu<DIM>(sQe, qraw, nrow, moff);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       *reinterpret_cast<i16x8*>(sG + i * LD + 8 * g + 32 * s) = pack8(unpack8(__builtin_bit_cast(i16x8, graw[s])) * inv);
@@ -667,7 +773,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_ragg_mfma(const bf16_t* __restric
   if (l == 0) sRed[w] = csum;
   __syncthreads();
   const float C = sRed[0] + sRed[1] + sRed[2] + sRed[3];
-  store_r<DIM>(r_agg + (bh * P + seg) * ER, Racc, racc, gacc, C, w, g, li);
+  store_r<DIM>(r_agg + (bh * P + seg) * ER, Racc, racc, gacc, C, sMuF, w, g, li);
 }
 
 // ---------------------------------------------------------------------------
@@ -913,10 +1019,17 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_fused_mfma(
   const int rw = (blockIdx.x & 1) ? 3 - w : w;
   // segment 0's aggregate would only feed the total, which is not needed
   float* ragg = seg > 0 ? r_agg : nullptr;
+  const bool mu1 =
+      __builtin_amdgcn_readfirstlane(
+          dq_decide_mu<DIM, true>(k, carry_s, N, P, seg_len, bh, seg) == static_cast<float>(DIM) ? 1 : 0) != 0;
   switch (rw) {
-#define LA_FUSED_DQ(RW_)                                                                                     \
-  case RW_:                                                                                                  \
-    dq_body<DIM, true, true, RW_>(q, k, v, dout, carry_s, dq, ragg, c_ws, den_ws, N, P, seg_len, bh, seg); \
+#define LA_FUSED_DQ(RW_)                                                                                           \
+  case RW_:                                                                                                        \
+    if (mu1)                                                                                                       \
+      dq_body<DIM, true, true, RW_, true>(q, k, v, dout, carry_s, dq, ragg, c_ws, den_ws, N, P, seg_len, bh, seg); \
+    else                                                                                                           \
+      dq_body<DIM, true, true, RW_, false>(q, k, v, dout, carry_s, dq, ragg, c_ws, den_ws, N, P, seg_len, bh,     \
+                                           seg);                                                                   \
     break
     LA_FUSED_DQ(0);
     LA_FUSED_DQ(1);
@@ -960,10 +1073,15 @@ size_t lds_bwd(int dim) {
   return (4 * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t) + (dim + T) * sizeof(float) +
          2 * T * sizeof(uint16_t) + 4 * 2 * 16 * (dim + kLdsPad) * sizeof(uint16_t);  // + output staging
 }
-size_t lds_ragg(int dim) { return 2 * T * (dim + kLdsPad) * sizeof(uint16_t) + 4 * sizeof(float) + 2 * T * sizeof(uint16_t); }
+// (+ the split constant mu as fp32 and bf16)
+size_t lds_ragg(int dim) {
+  return 2 * T * (dim + kLdsPad) * sizeof(uint16_t) + 4 * sizeof(float) + 2 * T * sizeof(uint16_t) +
+         dim * (sizeof(float) + sizeof(uint16_t));
+}
 size_t lds_dq(int dim) {
   return (6 * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t) + (2 * dim + 4) * sizeof(float) +
-         4 * T * sizeof(uint16_t) + 4 * 16 * (dim + kLdsPad) * sizeof(uint16_t);  // + output staging
+         4 * T * sizeof(uint16_t) + 4 * 16 * (dim + kLdsPad) * sizeof(uint16_t) +  // + output staging
+         dim * (sizeof(float) + sizeof(uint16_t));
 }
 
 #define LA_MLAUNCH(kernel, grid, lds, st, ...)                                                              \

@@ -666,19 +666,36 @@ def test_misaligned_bf16_views_take_the_generic_kernels(D):
 
 
 # --------------------------------------- strongly negative features -----
+FEATURE_SHIFTS = {
+    # q, k ~ N(-3, 1): phi = e^x small in every feature
+    "negative": (lambda x: x - 3.0, lambda x: x - 3.0),
+    # every other feature shifted down by 3, in q and k alike
+    "mixed": (lambda x: x - 3.0 * (np.arange(x.shape[-1]) % 2 == 0), lambda x: x - 3.0 * (np.arange(x.shape[-1]) % 2 == 0)),
+    # keys strongly negative, queries centred
+    "keys_negative": (lambda x: x, lambda x: x - 3.0),
+}
+
+
 @pytest.mark.parametrize("D", [64, 128])
-def test_mfma_backward_negative_mean_inputs(D):
-    # Features mostly far below 0 (q, k ~ N(-3, 1)): phi = e^x is small, the
-    # regime in which the dq sweep's phi = 1 + elu split (elu carried in bf16)
-    # holds phi to an absolute rather than a relative 2^-9.  The gradients
-    # must still meet the bf16 tolerance.
+@pytest.mark.parametrize("kind", list(FEATURE_SHIFTS))
+def test_mfma_backward_shifted_features(D, kind):
+    # Features far below 0 (phi = e^x small) in all, half or only the key
+    # features.  The bf16 kernels split phi = mu + E per feature, mu chosen
+    # per segment (1 where phi ~ 1, 0 where phi << 1), so that E in bf16 keeps
+    # phi to a relative rather than an absolute 2^-9 in either regime; the
+    # gradients must meet the same bar as on centred inputs (4x the bf16
+    # rounding of the exact gradients), with several segments so that the
+    # carried records are exercised.
     B, H, N = 1, 2, 1500
+    fq, fk = FEATURE_SHIFTS[kind]
     q, k, v, g = numpy_inputs(B, H, N, D, D, seed=61 + D, scale=1.0)
-    q, k = q - 3.0, k - 3.0
+    q, k = fq(q), fk(k)
     v = v / np.sqrt(D)
     tq, tk, tv, tg = (to_torch(x, "bf16", DEV) for x in (q, k, v, g))
-    check_forward(tq, tk, tv, True, "bf16", null_guard=True)
-    check_backward(tq, tk, tv, tg, True, "bf16")
+    plan = dict(kernel=2, segments=3)
+    check_forward(tq, tk, tv, True, "bf16", plan=plan, null_guard=True)
+    check_backward(tq, tk, tv, tg, True, "bf16", plan=plan, floor_factor=4.0)
+    check_backward(tq, tk, tv, tg, False, "bf16", plan=plan, floor_factor=4.0)
 
 
 # ------------------------------------------- one-launch causal backward ---
