@@ -282,6 +282,23 @@ def timed_steps(la, torch, step, steps, warmup, settle=0.0, nbreak=3):
     return t0.elapsed_time(t1) / steps, prof, kname, tot_ms / nl
 
 
+def per_iteration_ms(torch, fn, n, warmup=3):
+    """Median and min over n iterations, each bracketed by HIP events on
+    the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2]), t[0]
+
+
 def kernel_table(prof, nbreak, B, H, N, D, M, es, P, ceil=None):
     """Per-kernel breakdown: launches per step, average time and the
     kernel's own HBM I/O (inputs it reads once, outputs it writes once)."""
@@ -460,6 +477,18 @@ def bench_fwdbwd(la, torch, args, ceil):
                                        "each of its launches inside the timed region"}
     log(f"step roofline: {roof['achieved']:.0f} GB/s of section 8(d) bytes = {roof['frac']:.3f} of 8 TB/s; "
         f"counter traffic / algorithmic = {roof['traffic_over_alg']}")
+    # each half alone (the forward keeps den and the prefix states; the
+    # backward reads the ones the last forward left), and the step, per
+    # iteration: median and min of 20
+    phases = {}
+    for name, fn in (("forward", lambda: la.forward(q, k, v, causal=True, out=out, den=den, return_den=True,
+                                                    workspace=ws_f, saved=saved)),
+                     ("backward", lambda: la.backward(q, k, v, out, g, den=den, causal=True, workspace=ws_b,
+                                                      saved=saved)),
+                     ("step", step)):
+        med, mn = per_iteration_ms(torch, fn, 20)
+        phases[name] = {"median_ms": round(med, 4), "min_ms": round(mn, 4)}
+    log("per iteration (median / min ms): " + ", ".join(f"{n} {v['median_ms']} / {v['min_ms']}" for n, v in phases.items()))
     result = {
         "metric": "causal linear-attn fwd+bwd tokens/sec",
         "value": round(value, 1),
@@ -478,6 +507,7 @@ def bench_fwdbwd(la, torch, args, ceil):
                    "plan_forward": plan_f, "plan_backward": plan_b},
         "roofline": roof,
         "kernels": kernels,
+        "phases": phases,
     }
     if ceil:
         mix = KERNEL_MIX.get(kname)
