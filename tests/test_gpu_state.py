@@ -33,10 +33,14 @@ def f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def case(B, H, N, D, M, dtype, seed, prefix):
+def case(B, H, N, D, M, dtype, seed, prefix, shift=0.0):
     """Device tensors for N tokens, and the fp64 state of `prefix` earlier
-    tokens of the same sequence (zero state when prefix == 0)."""
+    tokens of the same sequence (zero state when prefix == 0).  shift moves
+    q and k (unscaled N(0, 1) then) so that phi = e^x is small in every
+    feature."""
     q, k, v, g = numpy_inputs(B, H, N + prefix, D, M, seed=seed, scale=1.0 / np.sqrt(D))
+    if shift:
+        q, k = q * np.sqrt(D) + shift, k * np.sqrt(D) + shift
     tq, tk, tv, tg = (to_torch(x[..., prefix:, :], dtype, DEV) for x in (q, k, v, g))
     if prefix:
         pk, pv = (f64(to_torch(x[..., :prefix, :], dtype, DEV)) for x in (k, v))
@@ -47,19 +51,22 @@ def case(B, H, N, D, M, dtype, seed, prefix):
 
 
 STATE_CASES = [
-    # (B, H, N, D, M, dtype, prefix): generic fp32 (D != M), MFMA bf16 D = 64 / 128;
-    # N spans several chunks and segments, with a ragged tail
-    (2, 2, 333, 32, 16, "f32", 100),
-    (2, 2, 700, 64, 64, "bf16", 300),
-    (1, 2, 1100, 128, 128, "bf16", 257),
-    (1, 1, 1, 64, 64, "bf16", 50),
-    (2, 1, 90, 64, 64, "bf16", 0),
+    # (B, H, N, D, M, dtype, prefix, shift): generic fp32 (D != M), MFMA bf16
+    # D = 64 / 128; N spans several chunks and segments, with a ragged tail;
+    # shifted features (phi << 1 everywhere, the per-feature split's mu = 0)
+    (2, 2, 333, 32, 16, "f32", 100, 0.0),
+    (2, 2, 700, 64, 64, "bf16", 300, 0.0),
+    (1, 2, 1100, 128, 128, "bf16", 257, 0.0),
+    (1, 1, 1, 64, 64, "bf16", 50, 0.0),
+    (2, 1, 90, 64, 64, "bf16", 0, 0.0),
+    (1, 2, 700, 64, 64, "bf16", 300, -3.0),
+    (1, 1, 1100, 128, 128, "bf16", 257, -3.0),
 ]
 
 
-@pytest.mark.parametrize("B,H,N,D,M,dtype,prefix", STATE_CASES)
-def test_forward_state_matches_oracle(B, H, N, D, M, dtype, prefix):
-    tq, tk, tv, _, S0, Z0 = case(B, H, N, D, M, dtype, seed=N + D + prefix, prefix=prefix)
+@pytest.mark.parametrize("B,H,N,D,M,dtype,prefix,shift", STATE_CASES)
+def test_forward_state_matches_oracle(B, H, N, D, M, dtype, prefix, shift):
+    tq, tk, tv, _, S0, Z0 = case(B, H, N, D, M, dtype, seed=N + D + prefix, prefix=prefix, shift=shift)
     tS0 = torch.tensor(S0, dtype=torch.float32, device=DEV)
     tZ0 = torch.tensor(Z0, dtype=torch.float32, device=DEV)
     out, S, Z, den = la.forward_state(tq, tk, tv, tS0, tZ0, return_den=True)
@@ -68,7 +75,7 @@ def test_forward_state_matches_oracle(B, H, N, D, M, dtype, prefix):
     ref, rden, rS, rZ = oracle.forward_recurrent(q64, k64, v64, True, S0, Z0)
     e = {"out": rel_l2(f64(out), ref), "den": rel_l2(f64(den), rden), "S": rel_l2(f64(S), rS),
          "Z": rel_l2(f64(Z), rZ)}
-    say(f"forward_state {(B, H, N, D, M)} {dtype} prefix={prefix} " + " ".join(f"{n}={x:.2e}" for n, x in e.items()))
+    say(f"forward_state {(B, H, N, D, M)} {dtype} prefix={prefix} shift={shift} " + " ".join(f"{n}={x:.2e}" for n, x in e.items()))
     for n, x in e.items():
         assert x < TOL[dtype], (n, x)
     # the final state comes from the fp32 segment sums (elu carried as bf16 on
@@ -77,9 +84,9 @@ def test_forward_state_matches_oracle(B, H, N, D, M, dtype, prefix):
     assert e["Z"] < (1e-5 if dtype == "f32" else 2e-3)
 
 
-@pytest.mark.parametrize("B,H,N,D,M,dtype,prefix", STATE_CASES)
-def test_backward_state_matches_oracle(B, H, N, D, M, dtype, prefix):
-    tq, tk, tv, tg, S0, Z0 = case(B, H, N, D, M, dtype, seed=N + D + prefix + 1, prefix=prefix)
+@pytest.mark.parametrize("B,H,N,D,M,dtype,prefix,shift", STATE_CASES)
+def test_backward_state_matches_oracle(B, H, N, D, M, dtype, prefix, shift):
+    tq, tk, tv, tg, S0, Z0 = case(B, H, N, D, M, dtype, seed=N + D + prefix + 1, prefix=prefix, shift=shift)
     tS0 = torch.tensor(S0, dtype=torch.float32, device=DEV)
     tZ0 = torch.tensor(Z0, dtype=torch.float32, device=DEV)
     out, _, _ = la.forward_state(tq, tk, tv, tS0, tZ0)
@@ -95,7 +102,7 @@ def test_backward_state_matches_oracle(B, H, N, D, M, dtype, prefix):
 
     e = {n: err(x, r) for n, x, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv), ("dS0", dS0, rS),
                                      ("dZ0", dZ0, rZ))}
-    say(f"backward_state {(B, H, N, D, M)} {dtype} prefix={prefix} " + " ".join(f"{n}={x:.2e}" for n, x in e.items()))
+    say(f"backward_state {(B, H, N, D, M)} {dtype} prefix={prefix} shift={shift} " + " ".join(f"{n}={x:.2e}" for n, x in e.items()))
     for n, x in e.items():
         assert x < TOL[dtype], (n, x)
     if dtype == "bf16":
