@@ -175,26 +175,26 @@ __device__ __forceinline__ void outer_update(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>
 }
 
 // Variants of the helpers above for the forward sweep, which writes
-// phi = mu + E (mu in {0, 1} per feature, chosen per segment: decide_mu)
-// and keeps the prefix state split as
+// phi = mu + E (mu per feature, chosen per segment: mu_rule) and keeps the
+// prefix state split as
 //   S = mu U^T + S',  Z = n mu + Z'.
 // The split is exact for any U and n; it pays when S' and Z' are small, i.e.
 // when U and n carry the mu direction of S and Z.  Within the sweep the
 // kernel keeps U = sum_j V_j, n = number of tokens, S' = sum_j E(K_j) V_j^T,
-// Z' = sum_j E(K_j); for a carried-in state (S, Z) it takes U = mean of
-// S[d][:] and n = mean of Z[d] over the features with mu_d = 1 (for a state
-// built from tokens these leave S', Z' no larger than the token sums do, and
-// they need nothing but S and Z; with no such feature U = 0, n = 0).  y
-// holds, for the wave's column tiles, a vector over m in the X^T accumulator
-// layout: lane holds y[16mt + 4g + u].  smu = sum of mu.
+// Z' = sum_j E(K_j); for a carried-in state (S, Z) it takes the least-squares
+// U = sum_d mu_d S[d][:] / smu2 and n = sum_d mu_d Z[d] / smu2 (smu2 = mu.mu;
+// for a state built from tokens these leave S', Z' no larger than the token
+// sums do, and they need nothing but S and Z; with mu = 0, U = 0 and n = 0).
+// y holds, for the wave's column tiles, a vector over m in the X^T
+// accumulator layout: lane holds y[16mt + 4g + u].
 template <int DIM>
 __device__ __forceinline__ float init_split(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&x)[Geo<DIM>::DT],
                                             f32x4_t (&y)[Geo<DIM>::DT], const float* __restrict__ rec,
-                                            const float* sMuF, float smu, int w, int g, int li) {
+                                            const float* sMuF, float smu2, int w, int g, int li) {
   using G = Geo<DIM>;
-  const float inv = smu > 0.f ? 1.f / smu : 0.f;
-  // n = mean of Z over the mu features: every wave sums all D entries (lane
-  // l reads Z[l], Z[l + 64])
+  const float inv = smu2 > 0.f ? 1.f / smu2 : 0.f;
+  // n = mu.Z / mu.mu: every wave sums all D entries (lane l reads Z[l],
+  // Z[l + 64])
   float n = 0.f;
   if (rec) {
 #pragma unroll
@@ -213,8 +213,8 @@ __device__ __forceinline__ float init_split(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>:
     for (int n_ = 0; n_ < G::NTL; ++n_)
 #pragma unroll
       for (int u = 0; u < 4; ++u) X[a][n_][u] = rec ? rec[(16 * n_ + li) * DIM + 16 * mt + 4 * g + u] : 0.f;
-    // U[m] = mean over the mu features d = 16 n_ + li: in-lane over n_, then
-    // over the 16 li
+    // U[m] = sum_d mu_d S[d][m] / mu.mu over d = 16 n_ + li: in-lane over n_,
+    // then over the 16 li
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       float s_ = 0.f;
@@ -232,14 +232,22 @@ __device__ __forceinline__ float init_split(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>:
   return n;
 }
 
-// smu for every lane: the sum of sMuF over the DIM features.
+// For every lane: mu.mu over the DIM features, and whether every mu is 1.
 template <int DIM>
-__device__ __forceinline__ float mu_sum(const float* sMuF) {
-  float m = 0.f;
+__device__ __forceinline__ float mu_sq_sum(const float* sMuF, bool* all_one) {
+  float m = 0.f, off1 = 0.f;
 #pragma unroll
-  for (int d0 = 0; d0 < DIM; d0 += 64) m += sMuF[d0 + (threadIdx.x & 63)];
+  for (int d0 = 0; d0 < DIM; d0 += 64) {
+    const float mu = sMuF[d0 + (threadIdx.x & 63)];
+    m += mu * mu;
+    off1 += mu != 1.f ? 1.f : 0.f;
+  }
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) m += __shfl_xor(m, off, 64);
+  for (int off = 1; off < 64; off <<= 1) {
+    m += __shfl_xor(m, off, 64);
+    off1 += __shfl_xor(off1, off, 64);
+  }
+  *all_one = off1 == 0.f;
   return m;
 }
 
@@ -316,19 +324,19 @@ __device__ __forceinline__ void store_r(float* __restrict__ rec, const f32x4_t (
 // the gradient is what is left after that ones direction cancels, a few
 // times smaller than its terms.  Rounding phi(K), S or b to bf16 puts an
 // error into that direction which the cancellation then amplifies, so this
-// kernel writes phi = mu + E, with mu in {0, 1} per feature (1 where the
-// segment's keys have phi ~ 1, 0 where phi << 1: decide_mu) and E carried as
-// bf16, and keeps every mu-direction term in fp32:
+// kernel writes phi = mu + E, with mu per feature (the segment's mean phi of
+// its first chunk of keys, or 1 where that is close to 1: mu_rule) and E
+// carried as bf16, and keeps every mu-direction term in fp32:
 //   grad phi(Q_i) = beta_i mu + S' g_i + c_i Z' + sum_{j<=i in chunk} E_j b_ij
 //   beta_i = sum_{j<=i} b_ij = g_i.U + n_i c_i + sum_{j in chunk} g_i.V_j
 // with (S', Z', U) the state before the chunk (split as above), n_i the
 // number of keys j <= i, and g_i = bf16(dout_i / den_i).  The same split of
 // phi(Q_i) = mu + E_i gives the scores and the denominator in fp32 from
-// bf16 E's (mu.mu = smu, the number of mu features):
-//   A_ij = smu + mu.E_i + mu.E_j + E_i.E_j
-//   den_i = sum_{j in chunk} A_ij + n0 (smu + mu.E_i) + sum_d (mu + E_i) Z'
+// bf16 E's (smu2 = mu.mu):
+//   A_ij = smu2 + mu.E_i + mu.E_j + E_i.E_j
+//   den_i = sum_{j in chunk} A_ij + n0 (smu2 + mu.E_i) + sum_d (mu + E_i) Z'
 // and c_i = -(g_i . num_i) / den_i from the same pieces:
-//   g_i . num_i = sum_j A_ij (g_i.V_j) + (smu + mu.E_i)(g_i.U)
+//   g_i . num_i = sum_j A_ij (g_i.V_j) + (smu2 + mu.E_i)(g_i.U)
 //                 + sum_d (mu + E_i)[d] (S' g_i)[d].
 // The query, g and c tiles are double-buffered so that the (R, r) aggregate
 // of a chunk is summed after the chunk's last barrier: two barriers per
@@ -342,9 +350,9 @@ __device__ __forceinline__ void store_r(float* __restrict__ rec, const f32x4_t (
 // row tile (the triangle of key tiles) resolves at compile time, and the
 // chunk body becomes one stretch of code to schedule (the dq sweep is
 // bound by its instruction issue; 162 -> 153 us at B=8 H=16 N=8192 D=64).
-// MU1: every mu of the segment is 1 (the usual case), and the mu terms are
-// compile-time constants; otherwise they come from LDS (dq_decide_mu ran
-// first in either case).
+// MU1: every mu of the segment is 1 (the usual case: centred inputs), and
+// the mu terms are compile-time constants; otherwise they come from LDS
+// (dq_decide_mu ran first in either case).
 // Where the dq sweep keeps mu in LDS: after its tiles, state, c pairs and
 // output staging (the layout dq_body carves and lds_dq sizes).
 template <int DIM>
@@ -357,11 +365,11 @@ __device__ __forceinline__ float* dq_mu_lds(uint16_t* smem) {
 }
 
 // The split constant mu of one segment's dq sweep into LDS (fp32 and bf16):
-// decide_mu over the segment's first chunk of keys (causal), or from the
-// mean phi(K) of the carried totals, Z / N (non-causal).  Returns the number
-// of mu features.  Ends with a barrier.
+// decide_mu over the segment's first chunk of keys (causal), or mu_rule on
+// the mean phi(K) of the carried totals, Z / N (non-causal).  Returns whether
+// every mu is 1.  Ends with a barrier.
 template <int DIM, bool CAUSAL>
-__device__ __forceinline__ float dq_decide_mu(const bf16_t* __restrict__ k, const float* __restrict__ carry_s,
+__device__ __forceinline__ bool dq_decide_mu(const bf16_t* __restrict__ k, const float* __restrict__ carry_s,
                                               int64_t N, int P, int seg_len, int64_t bh, int seg) {
   using G = Geo<DIM>;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -378,12 +386,14 @@ __device__ __forceinline__ float dq_decide_mu(const bf16_t* __restrict__ k, cons
   } else if (threadIdx.x < DIM) {
     constexpr int64_t ER = static_cast<int64_t>(DIM) * DIM + DIM;
     const float* cs = carry_s ? carry_s + bh * ER : nullptr;
-    const float mu = (cs && cs[DIM * DIM + threadIdx.x] < 0.5f * static_cast<float>(N)) ? 0.f : 1.f;
+    const float mu = cs ? mu_rule(cs[DIM * DIM + threadIdx.x] / static_cast<float>(N)) : 1.f;
     sMuF[threadIdx.x] = mu;
-    sMuB[threadIdx.x] = mu != 0.f ? 0x3f80 : 0;
+    sMuB[threadIdx.x] = static_cast<uint16_t>(bf(mu));
   }
   __syncthreads();
-  return mu_sum<DIM>(sMuF);
+  bool all_one = false;
+  mu_sq_sum<DIM>(sMuF, &all_one);
+  return all_one;
 }
 
 template <int DIM, bool CAUSAL, bool FUSED_R, int RW, bool MU1>
@@ -449,7 +459,8 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
   };
   fetch(static_cast<int>(c0 * DIM * 2));
 
-  const float smu = MU1 ? static_cast<float>(DIM) : mu_sum<DIM>(sMuF);
+  bool all_one_;
+  const float smu2 = MU1 ? static_cast<float>(DIM) : mu_sq_sum<DIM>(sMuF, &all_one_);
   MuOff moff;
   if constexpr (!MU1) moff = mu_offsets<DIM>(sMuF);
   const short one = 0x3f80;  // bf16 1.0
@@ -457,9 +468,9 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
 
   f32x4_t Sacc[DT][NTL], zacc[DT], uacc[DT];
   // n0: the mu-direction count of the state before the current chunk
-  float n0 = init_split<DIM>(Sacc, zacc, uacc, cs, sMuF, smu, w, g, li);
+  float n0 = init_split<DIM>(Sacc, zacc, uacc, cs, sMuF, smu2, w, g, li);
   f32x4_t Racc[FUSED_R ? DT : 1][FUSED_R ? NTL : 1], racc[FUSED_R ? DT : 1], gacc[FUSED_R ? DT : 1];
-  if constexpr (FUSED_R) init_split<DIM>(Racc, racc, gacc, nullptr, sMuF, smu, w, g, li);
+  if constexpr (FUSED_R) init_split<DIM>(Racc, racc, gacc, nullptr, sMuF, smu2, w, g, li);
   write_xt<DIM>(sS, sZ, Sacc, zacc, w, g, li);
   write_y<DIM>(sU, uacc, w, g, li);
   float csum = 0.f;
@@ -511,12 +522,12 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
     i16x8 mub[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) mub[s] = MU1 ? ones : lds8(sMuB + 8 * g + 32 * s);
-    // sum_d mu_d phi(Q_i) = smu + sum_d mu_d E(Q_i), through the MFMA against mu
+    // sum_d mu_d phi(Q_i) = smu2 + sum_d mu_d E(Q_i), through the MFMA against mu
     f32x4_t sq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) sq = mfma(mub[s], qf[s], sq);
-    const float dq_i = smu + sq[0];
-    // --- scores A^T[j][i] = (smu + sq_i) + sk_j + E_j.E_i, masked j <= i:
+    const float dq_i = smu2 + sq[0];
+    // --- scores A^T[j][i] = (smu2 + sq_i) + sk_j + E_j.E_i, masked j <= i:
     // sk_j = sum_d mu_d E(K_j) from the same MFMA chain against mu
     f32x4_t at[4];
     float rs = 0.f;
@@ -680,10 +691,7 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf1
   const int64_t bh = blockIdx.x / P;
   const int seg = static_cast<int>(blockIdx.x % P);
   // the same value in every thread (read from LDS after a barrier)
-  const bool mu1 = __builtin_amdgcn_readfirstlane(
-                       dq_decide_mu<DIM, CAUSAL>(k, carry_s, N, P, seg_len, bh, seg) == static_cast<float>(DIM)
-                           ? 1
-                           : 0) != 0;
+  const bool mu1 = __builtin_amdgcn_readfirstlane(dq_decide_mu<DIM, CAUSAL>(k, carry_s, N, P, seg_len, bh, seg) ? 1 : 0) != 0;
   switch ((blockIdx.x & 1) ? 3 - w : w) {
 #define LA_DQ_BODY(RW_)                                                                                          \
   case RW_:                                                                                                      \
@@ -745,10 +753,9 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_ragg_mfma(const bf16_t* __restric
     decide_mu<DIM, LD>(sQe, static_cast<int>(min(static_cast<int64_t>(T), r1 - r0)), sMuF, sMuB);
     __syncthreads();
   }
-  const float smu = mu_sum<DIM>(sMuF);
   const MuOff moff = mu_offsets<DIM>(sMuF);
   f32x4_t Racc[DT][NTL], racc[DT], gacc[DT];
-  init_split<DIM>(Racc, racc, gacc, nullptr, sMuF, smu, w, g, li);
+  init_split<DIM>(Racc, racc, gacc, nullptr, sMuF, 0.f, w, g, li);  // no carried record: zeros
   float csum = 0.f;
   for (int64_t c0 = r0; c0 < r1; c0 += T) {
     const int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
@@ -1019,9 +1026,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_fused_mfma(
   const int rw = (blockIdx.x & 1) ? 3 - w : w;
   // segment 0's aggregate would only feed the total, which is not needed
   float* ragg = seg > 0 ? r_agg : nullptr;
-  const bool mu1 =
-      __builtin_amdgcn_readfirstlane(
-          dq_decide_mu<DIM, true>(k, carry_s, N, P, seg_len, bh, seg) == static_cast<float>(DIM) ? 1 : 0) != 0;
+  const bool mu1 = __builtin_amdgcn_readfirstlane(dq_decide_mu<DIM, true>(k, carry_s, N, P, seg_len, bh, seg) ? 1 : 0) != 0;
   switch (rw) {
 #define LA_FUSED_DQ(RW_)                                                                                           \
   case RW_:                                                                                                        \

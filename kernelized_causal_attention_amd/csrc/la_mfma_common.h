@@ -290,29 +290,37 @@ __device__ __forceinline__ void store_tile_e(uint16_t* lds, const i32x4 (&raw)[(
 }
 
 // The split phi = mu + E that the backward's dq sweep and the segment
-// aggregates carry, with one constant mu_f in {0, 1} per feature f: the
-// mu part is summed in fp32 and only E = phi - mu is rounded to bf16.
-// mu_f = 1 where phi ~ 1 (E = elu small: a bf16 rounding relative to the
-// spread, not to 1), mu_f = 0 where phi << 1 (E = phi itself: a rounding
-// relative to phi, where elu ~ -1 would hold phi to an absolute 2^-9).
-// decide_mu takes mu_f = 0 where the mean phi of column f of a chunk (the
-// bf16 elu tile sE, rows < nrow) is below 1/2; one thread per feature, so
-// the sum has a fixed order.  sMuF gets mu as fp32, sMuB as bf16.
+// aggregates carry, with one constant mu_f per feature f: the mu part is
+// summed in fp32 and only E = phi - mu is rounded to bf16.  Where a sum over
+// keys cancels along a direction in which phi is nearly constant (every
+// key's phi close to mu), a bf16 rounding of phi itself would leave an error
+// of 2^-9 phi that the cancellation amplifies; E = phi - mu keeps the
+// rounding relative to the spread instead.  mu_rule takes mu_f = 1 where the
+// mean phi m of feature f is within 1/8 of 1 (then E = elu, and a segment
+// whose features all have mu = 1 runs the plain split), and m rounded to
+// bf16 otherwise (so that mu is exact as an MFMA operand).
+__device__ __forceinline__ float mu_rule(float m) {
+  return fabsf(m - 1.f) <= 0.125f ? 1.f : fb(bf(m));
+}
+
+// decide_mu over a chunk: the mean phi of column f of the bf16 elu tile sE
+// (rows < nrow), one thread per feature so the sum has a fixed order.  sMuF
+// gets mu as fp32, sMuB as bf16 bits (the same value).
 template <int DIM, int LD>
 __device__ __forceinline__ void decide_mu(const uint16_t* sE, int nrow, float* sMuF, uint16_t* sMuB) {
   const int d = threadIdx.x;
   if (d < DIM) {
     float s = 0.f;
     for (int j = 0; j < nrow; ++j) s += fb(static_cast<short>(sE[j * LD + d]));
-    const float mu = (nrow > 0 && s < -0.5f * static_cast<float>(nrow)) ? 0.f : 1.f;
+    const float mu = nrow > 0 ? mu_rule(1.f + s / static_cast<float>(nrow)) : 1.f;
     sMuF[d] = mu;
-    sMuB[d] = mu != 0.f ? 0x3f80 : 0;
+    sMuB[d] = static_cast<uint16_t>(bf(mu));
   }
 }
 
-// The thread's offsets 1 - mu for the eight features of its tile pieces
-// (feature 8 (p % ROW8) + e, the same for all of a thread's pieces since the
-// workgroup size is a multiple of ROW8), as fp32 0 or 1.
+// The thread's mu for the eight features of its tile pieces (feature
+// 8 (p % ROW8) + e, the same for all of a thread's pieces since the
+// workgroup size is a multiple of ROW8).
 struct MuOff {
   float c[8];
 };
@@ -321,18 +329,15 @@ __device__ __forceinline__ MuOff mu_offsets(const float* sMuF) {
   const int c8 = threadIdx.x % Geo<DIM, NW>::ROW8;
   MuOff m;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) m.c[e] = 1.f - sMuF[8 * c8 + e];
+  for (int e = 0; e < 8; ++e) m.c[e] = sMuF[8 * c8 + e];
   return m;
 }
 
-// E = phi(x) - mu = elu(x) + (1 - mu) for a raw bf16 piece: elu where
-// mu = 1, phi where mu = 0 (branch-free; for x < 0 the phi = (e^x - 1) + 1
-// it forms carries fp32's absolute 2^-24 or so, far below the bf16 rounding
-// that follows wherever phi is not itself negligible).
+// E = phi(x) - mu for a raw bf16 piece, in fp32 and then rounded to bf16.
 __device__ __forceinline__ i16x8 emu8(i32x4 raw, const MuOff& m) {
   f32x8_t x = unpack8(__builtin_bit_cast(i16x8, raw));
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = elu_fast(x[e]) + m.c[e];
+  for (int e = 0; e < 8; ++e) x[e] = phi_fast(x[e]) - m.c[e];
   return pack8(x);
 }
 
