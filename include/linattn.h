@@ -182,14 +182,16 @@ size_t la_saved_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
  * all-ones direction several times over, so dq would lose about a decimal
  * digit.
  * Precision (bf16): the MFMA kernels feed bf16 operands to the matrix cores
- * with fp32 accumulation; where a sum would cancel along the all-ones
- * direction of phi ~ 1 they split phi = mu + E per feature (mu = 1 where a
- * segment's keys have phi ~ 1, 0 where phi << 1) and keep the mu part in
- * fp32.  Against the fp64 result the gradients' relative L2 error measures
- * 2e-3 to 4e-3 for q, k ~ N(0, 1/D) or N(0, 1), for q, k ~ N(-3, 1), with
- * every other feature shifted to -3, and with only the keys shifted
- * (v ~ N(0, 1/D) or N(0, 1), dout ~ N(0, 1)); features below about -12,
- * where phi < 1e-5 is held to fp32's absolute rounding, are not covered.
+ * with fp32 accumulation; where a sum would cancel along a direction in
+ * which phi is nearly constant they split phi = mu + E per feature (mu the
+ * mean phi of a segment's first chunk, rounded to bf16, or 1 where that mean
+ * is within 1/8 of 1) and keep the mu part in fp32, so E's bf16 rounding is
+ * relative to phi's spread rather than its size.  Against the fp64 result
+ * the gradients' relative L2 error measures 2e-3 to 4e-3 for q, k ~ N(0,
+ * 1/D) or N(0, 1), for q, k ~ N(-3, 1), with every other feature shifted to
+ * -3, with only the keys shifted, and for q, k ~ N(s, 1/D) with s = -3, -1
+ * or +2 (v ~ N(0, 1/D) or N(0, 1), dout ~ N(0, 1)); features below about
+ * -12, where phi < 1e-5 is held to fp32's absolute rounding, are not covered.
  * fp32 inputs: ~1e-6. */
 la_status la_backward(const void* q, const void* k, const void* v, const void* out,
                       const void* dout, const float* den, void* dq, void* dk, void* dv,
