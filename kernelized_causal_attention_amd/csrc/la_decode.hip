@@ -192,7 +192,10 @@ __global__ __launch_bounds__(NT) void k_decode_vec(float* __restrict__ S, float*
       const int d = r0 + rg + u * RPI;
       const int dc = guard ? min(d, C - 1) : d;
       const f32x4 s = (MODE == kRet ? gam * sv[u] : sv[u]) + feat<MODE>(kf_s, dc, lgD) * vv;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s), Sr, voff, (r0 + u * RPI) * M * 4,
+      // (all of the offset in the VGPR, none in the SGPR: the compiler then
+      // keeps the stored VGPRs from being overwritten before the store has
+      // read them, which it does not do for a store with an SGPR offset)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s), Sr, voff + (r0 + u * RPI) * M * 4, 0,
                                              kNonTemporal);
       if (!guard || d < C) acc += feat<MODE>(qf_s, dc, lgD) * s;
     }

@@ -118,6 +118,84 @@ __device__ __forceinline__ void init_state(f32x4_t (&Sacc)[(Geo<DIM, NW>::DT)][(
   }
 }
 
+// One chunk's outputs for this wave: query tile rt (phi(Q) rows in qf),
+// output column tiles nb .. nb + NTW - 1.  Intra-chunk scores (masked, as a
+// bf16 hi + lo pair), the denominator, the inter-chunk product S^T phi(Q)^T
+// and the intra-chunk V^T A^T; returns den for query row li.
+template <int DIM, int NW, bool CAUSAL, int NTW>
+__device__ __forceinline__ float chunk_outputs(f32x4_t (&o)[NTW], const i16x8 (&qf)[(Geo<DIM, NW>::KS)],
+                                               const uint16_t* sKf, const uint16_t* sV, const uint16_t* sST,
+                                               const uint16_t* sZ, int rt, int nb, int g, int li) {
+  using G = Geo<DIM, NW>;
+  constexpr int LD = G::LD, KS = G::KS;
+  const short one = 0x3f80;  // bf16 1.0
+  const i16x8 ones = {one, one, one, one, one, one, one, one};
+  // Intra-chunk scores A^T (key tiles t <= rt), masked.  With phi ~ 1 + x
+  // the scores sit near D with a small spread, so one bf16 rounding would
+  // lose most of that spread; each score is carried as hi + lo, two bf16
+  // values whose sum keeps ~16 significant bits, and both enter the MFMA.
+  i16x4 ahi[4], alo[4];
+  if (CAUSAL) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      ahi[t] = i16x4{0, 0, 0, 0};
+      alo[t] = i16x4{0, 0, 0, 0};
+      if (t <= rt) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = mfma(lds8(sKf + (16 * t + li) * LD + 8 * g + 32 * s), qf[s], acc);
+        if (t == rt) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (4 * g + u > li) acc[u] = 0.f;
+        }
+        ahi[t] = pack4(acc);
+        alo[t] = pack4(acc - unpack4(ahi[t]));
+      }
+    }
+  }
+  // The denominator on the MFMA: the inter-chunk part phi(Q_i)^T Z with
+  // every row of the A operand equal to Z (as its bf16 hi and lo parts, ~16
+  // significant bits), and below the intra-chunk part, the sum of the same
+  // hi + lo scores the numerator uses, against a ones operand.  Every row
+  // of dz ends up holding den for query li.
+  f32x4_t dz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    dz = mfma(lds8(sZ + 8 * g + 32 * s), qf[s], dz);
+    dz = mfma(lds8(sZ + DIM + 8 * g + 32 * s), qf[s], dz);
+  }
+
+  // O^T = S^T phi(Q)^T (+ V^T A^T), this wave's output tiles
+#pragma unroll
+  for (int n = 0; n < NTW; ++n) {
+    o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) o[n] = mfma(lds8(sST + (16 * (nb + n) + li) * LD + 8 * g + 32 * s), qf[s], o[n]);
+  }
+  if (CAUSAL) {
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) {
+      if (2 * tp <= rt) {
+        const i16x8 bhi = cat(ahi[2 * tp], ahi[2 * tp + 1]);
+        const i16x8 blo = cat(alo[2 * tp], alo[2 * tp + 1]);
+        dz = mfma(ones, bhi, dz);
+        dz = mfma(ones, blo, dz);
+        const int jr = 32 * tp + 4 * g + li / 4;
+        const int cc = 4 * (li % 4);
+#pragma unroll
+        for (int n = 0; n < NTW; ++n) {
+          const int m0 = 16 * (nb + n) + cc;
+          const i16x8 a = cat(lds_tr(sV + jr * LD + m0), lds_tr(sV + (jr + 16) * LD + m0));
+          o[n] = mfma(a, bhi, o[n]);
+          o[n] = mfma(a, blo, o[n]);
+        }
+      }
+    }
+  }
+  return dz[0];
+}
+
 // ---------------------------------------------------------------------------
 template <int DIM, bool CAUSAL>
 __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -157,14 +235,19 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_
   const int64_t r1 = min(N, r0 + seg_len);
   constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;
   const float* cs = carry ? (CAUSAL ? carry + (bh * P + seg) * E : carry + bh * E) : nullptr;
-  const bf16_t* qh = q + bh * N * DIM;
-  const bf16_t* kh = k + bh * N * DIM;
-  const bf16_t* vh = v + bh * N * DIM;
+  // Buffer loads and stores over the head's rows (past its end: zero / dropped),
+  // so that no load or store sits under a branch: every chunk issues the same
+  // memory operations, and the wait for the prefetched tiles at the top of
+  // the loop need not also wait for the previous chunk's stores.
+  const rsrc_t rq = make_rsrc(q + bh * N * DIM, N * DIM * 2);
+  const rsrc_t rk = make_rsrc(k + bh * N * DIM, N * DIM * 2);
+  const rsrc_t rv = make_rsrc(v + bh * N * DIM, N * DIM * 2);
   const rsrc_t ro = make_rsrc(out ? out + bh * N * DIM : nullptr, out ? N * DIM * 2 : 0);
-  float* dh = den_out ? den_out + bh * N : nullptr;
+  const rsrc_t rd = make_rsrc(den_out ? den_out + bh * N : nullptr, den_out ? N * 4 : 0);
   const int i = 16 * rt + li;  // this lane's query row within the chunk
-  const short one = 0x3f80;  // bf16 1.0
-  const i16x8 ones = {one, one, one, one, one, one, one, one};
+  // den is stored by the 16 lanes of group 0 of the waves holding column
+  // tile 0; the other lanes aim past the range
+  const int den_voff = (g == 0 && nb == 0) ? 4 * i : static_cast<int>(4 * N);
   uint16_t* sO = sOut + w * 16 * (OC + kLdsPad);
 
   f32x4_t Sacc[DT][NTL];
@@ -176,19 +259,31 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_
   int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
   constexpr int QN = kQInLds ? PC : KS;  // q pieces held per lane
   i32x4 kraw[PC], vraw[PC], qraw[QN];
-  auto fetch_q = [&](int64_t cc0, int nr) {
+  // Rows of a chunk past the segment's end lie past the head's end (segments
+  // are whole chunks), so the buffer range check zeroes them.  The loads
+  // keep one order (K, V, Q: the scheduler may not move them), and the first
+  // chunk runs as a copy of the loop body ahead of the loop, so that every
+  // path into the loop's top has the same memory operations after the
+  // prefetch: the wait for the tiles then counts the previous chunk's
+  // stores as still in flight instead of waiting for them too.
+  auto fetch = [&](int64_t cc0) {
+    const int soff = static_cast<int>(cc0 * DIM * 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (CAUSAL) {
+      bload_tile<DIM, NW>(kraw, rk, soff);
+      __builtin_amdgcn_sched_barrier(0);
+      bload_tile<DIM, NW>(vraw, rv, soff);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if constexpr (kQInLds)
-      load_tile<DIM, NW>(qraw, qh, cc0, nr);
+      bload_tile<DIM, NW>(qraw, rq, soff);
     else
-      load_q<DIM>(qraw, qh, cc0, nr, i, g);
+      bload_q<DIM>(qraw, rq, soff, i, g);
+    __builtin_amdgcn_sched_barrier(0);
   };
-  if (CAUSAL) {
-    load_tile<DIM, NW>(kraw, kh, c0, nrow);
-    load_tile<DIM, NW>(vraw, vh, c0, nrow);
-  }
-  fetch_q(c0, nrow);
+  fetch(c0);
 
-  while (c0 < r1) {
+  auto chunk_step = [&]() __attribute__((always_inline)) {
     if (CAUSAL) {
       store_tile<DIM, true, NW>(sKf, kraw, nrow);
       store_tile<DIM, false, NW>(sV, vraw, nrow);
@@ -208,94 +303,141 @@ __global__ __launch_bounds__(64 * kFwdWaves<DIM>, 2) void k_fwd_mfma(const bf16_
     // prefetch the next chunk while this one computes
     const int64_t c1 = c0 + T;
     const int nrow1 = c1 < r1 ? static_cast<int>(min(static_cast<int64_t>(T), r1 - c1)) : 0;
-    if (nrow1 > 0) {
-      if (CAUSAL) {
-        load_tile<DIM, NW>(kraw, kh, c1, nrow1);
-        load_tile<DIM, NW>(vraw, vh, c1, nrow1);
-      }
-      fetch_q(c1, nrow1);
-    }
+    if (nrow1 > 0) fetch(c1);
 
-    // Intra-chunk scores A^T (key tiles t <= rt), masked.  With phi ~ 1 + x
-    // the scores sit near D with a small spread, so one bf16 rounding would
-    // lose most of that spread; each score is carried as hi + lo, two bf16
-    // values whose sum keeps ~16 significant bits, and both enter the MFMA.
-    i16x4 ahi[4], alo[4];
-    if (CAUSAL) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        ahi[t] = i16x4{0, 0, 0, 0};
-        alo[t] = i16x4{0, 0, 0, 0};
-        if (t <= rt) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < KS; ++s) acc = mfma(lds8(sKf + (16 * t + li) * LD + 8 * g + 32 * s), qf[s], acc);
-          if (t == rt) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (4 * g + u > li) acc[u] = 0.f;
-          }
-          ahi[t] = pack4(acc);
-          alo[t] = pack4(acc - unpack4(ahi[t]));
-        }
-      }
-    }
-    // The denominator on the MFMA: the inter-chunk part phi(Q_i)^T Z with
-    // every row of the A operand equal to Z (as its bf16 hi and lo parts, ~16
-    // significant bits), and below the intra-chunk part, the sum of the same
-    // hi + lo scores the numerator uses, against a ones operand.  Every row
-    // of dz ends up holding den for query li.
-    f32x4_t dz = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      dz = mfma(lds8(sZ + 8 * g + 32 * s), qf[s], dz);
-      dz = mfma(lds8(sZ + DIM + 8 * g + 32 * s), qf[s], dz);
-    }
-
-    // O^T = S^T phi(Q)^T (+ V^T A^T), this wave's output tiles
     f32x4_t o[NTW];
+    const float den = chunk_outputs<DIM, NW, CAUSAL, NTW>(o, qf, sKf, sV, sST, sZ, rt, nb, g, li);
+    // rows past the head's end (den may be 0 there) are dropped by the
+    // stores' range check
+    const float inv = 1.f / den;
 #pragma unroll
-    for (int n = 0; n < NTW; ++n) {
-      o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) o[n] = mfma(lds8(sST + (16 * (nb + n) + li) * LD + 8 * g + 32 * s), qf[s], o[n]);
-    }
-    if (CAUSAL) {
-#pragma unroll
-      for (int tp = 0; tp < 2; ++tp) {
-        if (2 * tp <= rt) {
-          const i16x8 bhi = cat(ahi[2 * tp], ahi[2 * tp + 1]);
-          const i16x8 blo = cat(alo[2 * tp], alo[2 * tp + 1]);
-          dz = mfma(ones, bhi, dz);
-          dz = mfma(ones, blo, dz);
-          const int jr = 32 * tp + 4 * g + li / 4;
-          const int cc = 4 * (li % 4);
-#pragma unroll
-          for (int n = 0; n < NTW; ++n) {
-            const int m0 = 16 * (nb + n) + cc;
-            const i16x8 a = cat(lds_tr(sV + jr * LD + m0), lds_tr(sV + (jr + 16) * LD + m0));
-            o[n] = mfma(a, bhi, o[n]);
-            o[n] = mfma(a, blo, o[n]);
-          }
-        }
-      }
-    }
-    const float den = dz[0];
-    if (out) {
-      // rows past the head's end (den may be 0 there) are dropped by the
-      // store's range check
-      const float inv = 1.f / den;
-#pragma unroll
-      for (int n = 0; n < NTW; ++n) stage_piece<OC>(sO, pack4(o[n] * inv), li, g, n);
-      store_staged<OC, DIM>(sO, ro, 16 * rt, 16 * nb, static_cast<int>(c0 * DIM * 2));
-    }
-    if (i < nrow && dh && g == 0 && nb == 0) dh[c0 + i] = den;
+    for (int n = 0; n < NTW; ++n) stage_piece<OC>(sO, pack4(o[n] * inv), li, g, n);
+    store_staged<OC, DIM>(sO, ro, 16 * rt, 16 * nb, static_cast<int>(c0 * DIM * 2));
+    bstore4(rd, den, den_voff, static_cast<int>(c0 * 4));
 
     if (CAUSAL) state_update<DIM, NW>(Sacc, zacc, sKf, sV, w, g, li);
     __syncthreads();
     if (CAUSAL) write_state<DIM, NW>(sST, sZ, Sacc, zacc, w, g, li);
     c0 = c1;
     nrow = nrow1;
+  };
+  chunk_step();  // segments are never empty
+  while (c0 < r1) chunk_step();
+}
+
+// ---------------------------------------------------------------------------
+// The causal D = 128 forward with double-buffered chunk tiles.  Same
+// arithmetic and work split as k_fwd_mfma<128, true> (eight waves, a pair of
+// waves per 16-row query tile splitting the output columns, every wave one
+// 16-row slab of the fp32 state), but the next chunk's phi(K), V and phi(Q)
+// go into the other half of a double buffer at the end of the current
+// chunk's work instead of after a barrier.  A chunk then has one long phase
+// (outputs, state update, the next chunk's tiles) and a short one (S^T and Z
+// written back), so the waves' VALU work (phi, the hi / lo splits) overlaps
+// other waves' matrix and LDS work instead of running while the matrix
+// cores idle.  One workgroup per CU (155 KB of LDS).
+__global__ __launch_bounds__(512, 1) void k_fwd_mfma_db(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                       const bf16_t* __restrict__ v, bf16_t* __restrict__ out,
+                                                       float* __restrict__ den_out, const float* __restrict__ carry,
+                                                       int64_t N, int P, int seg_len) {
+  constexpr int DIM = 128, NW = 8;
+  using G = Geo<DIM, NW>;
+  constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
+  constexpr int NTW = NTL / 2;  // output tiles per wave
+  constexpr int OC = NTW * 16;
+  constexpr int TILE = T * LD;
+  extern __shared__ __align__(16) uint16_t smem[];
+  // [phi(K) 0, V 0, phi(Q) 0][phi(K) 1, V 1, phi(Q) 1][S^T][Z hi, lo][output staging]
+  uint16_t* sST = smem + 6 * TILE;
+  uint16_t* sZ = sST + DIM * LD;
+  uint16_t* sOut = sZ + 2 * DIM;
+
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rt = w & 3;         // query row tile
+  const int nb = (w >> 2) * NTW;  // first output tile of this wave
+  const int64_t bh = blockIdx.x / P;
+  const int seg = blockIdx.x % P;
+  const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
+  const int64_t r1 = min(N, r0 + seg_len);
+  constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;
+  const float* cs = carry ? carry + (bh * P + seg) * E : nullptr;
+  const rsrc_t rq = make_rsrc(q + bh * N * DIM, N * DIM * 2);
+  const rsrc_t rk = make_rsrc(k + bh * N * DIM, N * DIM * 2);
+  const rsrc_t rv = make_rsrc(v + bh * N * DIM, N * DIM * 2);
+  const rsrc_t ro = make_rsrc(out ? out + bh * N * DIM : nullptr, out ? N * DIM * 2 : 0);
+  const rsrc_t rd = make_rsrc(den_out ? den_out + bh * N : nullptr, den_out ? N * 4 : 0);
+  const int i = 16 * rt + li;
+  const int den_voff = (g == 0 && nb == 0) ? 4 * i : static_cast<int>(4 * N);
+  uint16_t* sO = sOut + w * 16 * (OC + kLdsPad);
+
+  f32x4_t Sacc[DT][NTL];
+  f32x4_t zacc[DT];
+  init_state<DIM, NW>(Sacc, zacc, cs, w, g, li);
+  write_state<DIM, NW>(sST, sZ, Sacc, zacc, w, g, li);
+
+  // Rows of a chunk past the segment's end lie past the head's end
+  // (segments are whole chunks): the buffer range check zeroes them, and
+  // store_tile zeroes phi(K) and phi(Q) there.
+  i32x4 kraw[PC], vraw[PC], qraw[PC];
+  auto fetch = [&](int64_t cc0) {
+    const int soff = static_cast<int>(cc0 * DIM * 2);
+    bload_tile<DIM, NW>(kraw, rk, soff);
+    bload_tile<DIM, NW>(vraw, rv, soff);
+    bload_tile<DIM, NW>(qraw, rq, soff);
+  };
+  auto put = [&](uint16_t* tiles, int nr) {
+    store_tile<DIM, true, NW>(tiles, kraw, nr);
+    store_tile<DIM, false, NW>(tiles + TILE, vraw, nr);
+    store_tile<DIM, true, NW>(tiles + 2 * TILE, qraw, nr);
+  };
+
+  int64_t c0 = r0;
+  int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
+  fetch(c0);
+  put(smem, nrow);
+  __syncthreads();
+  int buf = 0;
+  while (c0 < r1) {
+    const uint16_t* sKf = smem + buf * 3 * TILE;
+    const uint16_t* sV = sKf + TILE;
+    const uint16_t* sQf = sKf + 2 * TILE;
+    const int64_t c1 = c0 + T;
+    const int nrow1 = c1 < r1 ? static_cast<int>(min(static_cast<int64_t>(T), r1 - c1)) : 0;
+    if (nrow1 > 0) fetch(c1);
+
+    i16x8 qf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = lds8(sQf + i * LD + 8 * g + 32 * s);
+    f32x4_t o[NTW];
+    const float den = chunk_outputs<DIM, NW, true, NTW>(o, qf, sKf, sV, sST, sZ, rt, nb, g, li);
+    const float inv = 1.f / den;
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) stage_piece<OC>(sO, pack4(o[n] * inv), li, g, n);
+    store_staged<OC, DIM>(sO, ro, 16 * rt, 16 * nb, static_cast<int>(c0 * DIM * 2));
+    bstore4(rd, den, den_voff, static_cast<int>(c0 * 4));
+
+    // The state update, then the next chunk's tiles into the other half
+    // (last read in the previous chunk, before its barriers).  A whole next
+    // chunk (wave-uniform test) takes a copy without row guards, so that the
+    // phi arithmetic and the update's MFMAs share one basic block and the
+    // scheduler can interleave them.
+    uint16_t* nxt = smem + (buf ^ 1) * 3 * TILE;
+    if (nrow1 == T) {
+      state_update<DIM, NW>(Sacc, zacc, sKf, sV, w, g, li);
+      store_tile_full<DIM, true, NW>(nxt, kraw);
+      store_tile_full<DIM, false, NW>(nxt + TILE, vraw);
+      store_tile_full<DIM, true, NW>(nxt + 2 * TILE, qraw);
+    } else {
+      state_update<DIM, NW>(Sacc, zacc, sKf, sV, w, g, li);
+      if (nrow1 > 0) put(nxt, nrow1);
+    }
+    __syncthreads();  // every read of S^T, Z and this half done
+    write_state<DIM, NW>(sST, sZ, Sacc, zacc, w, g, li);
+    __syncthreads();  // S^T, Z and the next half written
+    c0 = c1;
+    nrow = nrow1;
+    buf ^= 1;
   }
 }
 
@@ -714,6 +856,9 @@ size_t lds_fwd(int dim) {
   return (tiles * T * (dim + kLdsPad) + dim * (dim + kLdsPad) + waves * 16 * (64 + kLdsPad)) * sizeof(uint16_t) +
          dim * sizeof(float);
 }
+size_t lds_fwd_db() {
+  return (6 * T * (128 + kLdsPad) + 128 * (128 + kLdsPad) + 2 * 128 + 8 * 16 * (64 + kLdsPad)) * sizeof(uint16_t);
+}
 size_t lds_fwd_t128() {
   return (2 * T2 * (64 + kLdsPad) + 64 * (64 + kLdsPad) + 2 * 64 + 4 * 16 * (64 + kLdsPad)) * sizeof(uint16_t);
 }
@@ -764,7 +909,7 @@ hipError_t launch_forward_mfma(int causal, const SegGeom& g, const void* q, cons
     LA_MLAUNCH((k_fwd_mfma<64, false>), 64 * kFwdWaves<64>, grid, lds_fwd(64), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
   }
   if (g.D == 128) {
-    if (causal) LA_MLAUNCH((k_fwd_mfma<128, true>), 64 * kFwdWaves<128>, grid, lds_fwd(128), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
+    if (causal) LA_MLAUNCH(k_fwd_mfma_db, 512, grid, lds_fwd_db(), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
     LA_MLAUNCH((k_fwd_mfma<128, false>), 64 * kFwdWaves<128>, grid, lds_fwd(128), st, Q, K, V, O, den_out, carry, g.N, g.P, g.seg_len);
   }
   return hipErrorNotSupported;
