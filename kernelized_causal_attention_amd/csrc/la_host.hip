@@ -51,8 +51,10 @@ hipError_t launch_ret_bwd_dkdv(const SegGeom& g, const void* q, const void* k, c
                                float* anch_y, hipStream_t st);
 hipError_t launch_ret_dlg(const SegGeom& g, const float* a, const float* carry_s, const float* r_agg,
                           const float* anch_y, float* dlg, hipStream_t st);
+// raw_carry: `carry` holds the segments' own aggregates (no scan ran); each
+// segment sums those before it
 hipError_t launch_forward_f32mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
-                                  void* out, float* den_out, const float* carry, hipStream_t st);
+                                  void* out, float* den_out, const float* carry, hipStream_t st, int raw_carry = 0);
 hipError_t launch_seg_state_f32mfma(const SegGeom& g, const void* k, const void* v, float* s_out,
                                     int64_t s_stride, float* z_out, int64_t z_stride, hipStream_t st);
 hipError_t launch_bwd_dq_mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
@@ -522,14 +524,14 @@ hipError_t seg_state(int dtype, const Plan& p, const la::SegGeom& gbase, const v
 
 hipError_t fwd_pass(int dtype, int causal, const Plan& p, const la::SegGeom& gbase, const void* q,
                     const void* k, const void* v, void* out, float* den_out, const float* carry,
-                    hipStream_t st) {
+                    hipStream_t st, int raw_carry = 0) {
   const bool t128 = p.kernel == LA_KERNEL_MFMA && gbase.chunk == 128;
   const char* name = t128 ? (out ? "mfma.forward_t128" : "mfma.forward_t128_den")
                      : out ? kname(p.kernel, "generic.forward", "mfma.forward")
                            : kname(p.kernel, "generic.forward_den", "mfma.forward_den");
   if (p.kernel == LA_KERNEL_MFMA)
     return timed(name, st, [&] {
-      return dtype == LA_F32 ? la::launch_forward_f32mfma(causal, gbase, q, k, v, out, den_out, carry, st)
+      return dtype == LA_F32 ? la::launch_forward_f32mfma(causal, gbase, q, k, v, out, den_out, carry, st, raw_carry)
                              : la::launch_forward_mfma(causal, gbase, q, k, v, out, den_out, carry, st);
     });
   la::SegGeom g = gbase;
@@ -647,6 +649,13 @@ la_status do_forward(const void* q, const void* k, const void* v, void* out, int
       // reads its (unset) record only into the discarded total
       float* agg = sv ? sv : at(workspace, w.aggS);
       if ((e = seg_state(dtype, p, without_last(g), k, v, agg, stream))) return dev(e, "segment state");
+      // The fp32 MFMA forward sums its carry from the raw aggregates itself
+      // (in the scan's order: the same bits) when no prefix records are to be
+      // kept and there are few segments: one launch fewer, which at this
+      // kernel's sizes is worth more than the repeated record reads (segment
+      // s reads s records, P (P - 1) / 2 per head in all).
+      if (dtype == LA_F32 && p.kernel == LA_KERNEL_MFMA && !sv && p.P <= 8)
+        return dev(fwd_pass(dtype, 1, p, g, q, k, v, out, den_out, agg, stream, 1), "forward");
       if ((e = scan(agg, BH, p.P, g.D, g.M, 0, nullptr, 0, nullptr, 0, stream)))
         return dev(e, "segment scan");
       carry = agg;

@@ -97,7 +97,7 @@ template <bool CAUSAL>
 __global__ __launch_bounds__(NT, 2) void k_fwd_f32mfma(const float* __restrict__ q, const float* __restrict__ k,
                                                        const float* __restrict__ v, float* __restrict__ out,
                                                        float* __restrict__ den_out, const float* __restrict__ carry,
-                                                       int64_t N, int P, int seg_len) {
+                                                       int64_t N, int P, int seg_len, int raw_carry) {
   extern __shared__ __align__(16) float smf[];
   float* sKf = smf;
   float* sV = sKf + T * LDF;
@@ -113,7 +113,11 @@ __global__ __launch_bounds__(NT, 2) void k_fwd_f32mfma(const float* __restrict__
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
   const int64_t r1 = min(N, r0 + seg_len);
   constexpr int64_t E = static_cast<int64_t>(DF) * DF + DF;
-  const float* cs = carry ? (CAUSAL ? carry + (bh * P + seg) * E : carry + bh * E) : nullptr;
+  // raw_carry (causal): `carry` holds the segments' own aggregates, and this
+  // segment's carry-in is their sum over the segments before it, added in
+  // segment order as the scan adds them (the same bits as the scanned record)
+  const float* cs = carry ? (CAUSAL ? carry + (bh * P + (raw_carry ? 0 : seg)) * E : carry + bh * E) : nullptr;
+  const int nadd = !cs ? 0 : (CAUSAL && raw_carry) ? seg : 1;
   const float* qh = q + bh * N * DF;
   const float* kh = k + bh * N * DF;
   const float* vh = v + bh * N * DF;
@@ -124,10 +128,20 @@ __global__ __launch_bounds__(NT, 2) void k_fwd_f32mfma(const float* __restrict__
   f32x4_t Sacc[4], zacc;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int d = 16 * w + 4 * g + u;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) Sacc[n][u] = cs ? cs[d * DF + 16 * n + li] : 0.f;
-    zacc[u] = cs ? cs[DF * DF + d] : 0.f;
+    for (int n = 0; n < 4; ++n) Sacc[n][u] = 0.f;
+    zacc[u] = 0.f;
+  }
+#pragma unroll 4
+  for (int t = 0; t < nadd; ++t) {
+    const float* rec = cs + t * E;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d = 16 * w + 4 * g + u;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) Sacc[n][u] += rec[d * DF + 16 * n + li];
+      zacc[u] += rec[DF * DF + d];
+    }
   }
   write_state_f32(sS, sZ, Sacc, zacc, w, g, li);
 
@@ -335,7 +349,7 @@ constexpr size_t lds_seg_f32(int dim) { return 2 * T * (dim + 4) * sizeof(float)
 }  // namespace
 
 hipError_t launch_forward_f32mfma(int causal, const SegGeom& g, const void* q, const void* k, const void* v,
-                                  void* out, float* den_out, const float* carry, hipStream_t st) {
+                                  void* out, float* den_out, const float* carry, hipStream_t st, int raw_carry) {
   if (g.D != DF || g.M != DF) return hipErrorNotSupported;
   const dim3 grid(static_cast<unsigned>(g.BH * g.P));
   const float* Q = static_cast<const float*>(q);
@@ -348,10 +362,10 @@ hipError_t launch_forward_f32mfma(int causal, const SegGeom& g, const void* q, c
   if (e != hipSuccess) return e;
   if (causal)
     hipLaunchKernelGGL((k_fwd_f32mfma<true>), grid, dim3(NT), kLdsFwd, st, Q, K, V, O, den_out, carry, g.N, g.P,
-                       g.seg_len);
+                       g.seg_len, raw_carry);
   else
     hipLaunchKernelGGL((k_fwd_f32mfma<false>), grid, dim3(NT), kLdsFwd, st, Q, K, V, O, den_out, carry, g.N, g.P,
-                       g.seg_len);
+                       g.seg_len, 0);
   return hipGetLastError();
 }
 

@@ -499,6 +499,29 @@ def test_backward_reads_saved_states(causal, kernel, dtype, D, segments):
         assert e < TOL[dtype], (n, e)
 
 
+@pytest.mark.parametrize("segments", [2, 3, 8, 16])
+def test_f32_forward_own_carry_matches_scanned_carry(segments):
+    # Without saved states and with up to 8 segments the fp32 MFMA forward
+    # sums each segment's carry from the raw aggregates itself instead of a
+    # scan launch (16 segments: the scan); it adds them in the scan's order,
+    # so out and den equal bit for bit those of the call that keeps the
+    # scanned records (saved states), and the oracle's.
+    B, H, N, D = 2, 3, 1500, 64
+    tq, tk, tv, _ = host_case(B, H, N, D, D, "f32", seed=segments + 90, scale=1.0 / np.sqrt(D))
+    plan = dict(kernel=2, segments=segments)
+    nb = la.saved_bytes(B, H, N, D, D, True, "f32", plan)
+    assert nb > 0
+    saved = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    out_s, den_s = la.forward(tq, tk, tv, causal=True, return_den=True, plan=plan, saved=saved)
+    out_p, den_p = la.forward(tq, tk, tv, causal=True, return_den=True, plan=plan)
+    torch.cuda.synchronize()
+    assert torch.equal(out_s, out_p) and torch.equal(den_s, den_p)
+    ref = oracle.forward_recurrent(f64(tq), f64(tk), f64(tv), True)[0]
+    e = rel_l2(f64(out_p), ref)
+    say(f"f32 forward, {segments} segments, own carry: out={e:.2e}")
+    assert e < TOL["f32"]
+
+
 def test_saved_states_rejected_when_too_small():
     tq, tk, tv, tg = host_case(1, 1, 256, 64, 64, "bf16", seed=3, scale=0.125)
     plan = dict(kernel=2, segments=4)
