@@ -354,7 +354,9 @@ __global__ __launch_bounds__(512, 1) void k_fwd_mfma_db(const bf16_t* __restrict
 
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rt = w & 3;         // query row tile
+  // query row tile: waves w and w + 4 share a SIMD, so the second four take
+  // the tiles in reverse and every SIMD gets one short and one long triangle
+  const int rt = w < 4 ? w : 3 - (w & 3);
   const int nb = (w >> 2) * NTW;  // first output tile of this wave
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
