@@ -35,12 +35,12 @@ __device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t c) {
 __device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
 // Global fp32 [T x 64] tile -> LDS (phi applied when asked); rows past nrow
-// are zero.  256 threads, four 16-byte pieces each.
-template <bool PHI>
-__device__ __forceinline__ void stage_f32(float* lds, int nrow, const f32x4 (&raw)[4]) {
+// are zero.  NTH threads, T * 16 / NTH 16-byte pieces each.
+template <bool PHI, int NTH = NT>
+__device__ __forceinline__ void stage_f32(float* lds, int nrow, const f32x4 (&raw)[T * 16 / NTH]) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int p = threadIdx.x + NT * r;
+  for (int r = 0; r < T * 16 / NTH; ++r) {
+    const int p = threadIdx.x + NTH * r;
     const int j = p / 16, c4 = p % 16;
     f32x4 x = raw[r];
     if (j < nrow) {
@@ -55,59 +55,78 @@ __device__ __forceinline__ void stage_f32(float* lds, int nrow, const f32x4 (&ra
   }
 }
 
-__device__ __forceinline__ void load_f32(f32x4 (&raw)[4], const float* __restrict__ src, int64_t c0, int nrow) {
+template <int NTH = NT>
+__device__ __forceinline__ void load_f32(f32x4 (&raw)[T * 16 / NTH], const float* __restrict__ src, int64_t c0,
+                                         int nrow) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int p = threadIdx.x + NT * r;
+  for (int r = 0; r < T * 16 / NTH; ++r) {
+    const int p = threadIdx.x + NTH * r;
     const int j = p / 16, c4 = p % 16;
     raw[r] = j < nrow ? *reinterpret_cast<const f32x4*>(src + (c0 + j) * DF + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
-// State update for this wave's 16 state rows d = 16w + (row): S[d][m] +=
-// sum_j phi(K_j)[d] V_j[m], Z[d] += sum_j phi(K_j)[d] (64 keys, j = 16g + s).
-// Sacc[n] holds S[16w + 4g + u][16n + li]; zacc holds Z[16w + 4g + u].
-__device__ __forceinline__ void state_update_f32(f32x4_t (&Sacc)[4], f32x4_t& zacc, const float* sKf,
-                                                 const float* sV, int w, int g, int li) {
+// ---------------------------------------------------------------------------
+// Forward.  Eight waves, two per SIMD: wave w takes query rows 16 rt .. + 15
+// of each 64-token chunk (rt = w for the first four, 3 - (w & 3) for the
+// rest, so that the two waves of a SIMD carry one short and one long
+// triangle) and output columns 32 ch .. + 31 (ch = w >> 2), and owns state
+// rows 16 (w & 3) .. + 15, columns 32 ch .. + 31 (the Z part of those rows
+// in the ch = 0 waves).  The two waves of a query tile both form its scores.
+//
+// Every MFMA operand read from LDS comes four at a time (16-byte reads along
+// the contraction index): phi(K) is staged twice, token-major for the scores
+// (contraction over features) and feature-major for the state update
+// (contraction over tokens); V and S only feature-major (S^T), the layouts
+// their products contract over.  One-element reads would put an LDS round
+// trip in front of every other MFMA.
+// ---------------------------------------------------------------------------
+constexpr int NTF = 512;  // threads of the forward
+constexpr int PCF = T * 16 / NTF;  // 16-byte pieces per thread per T x 64 fp32 tile
+
+// A tile's pieces into a feature-major LDS tile ldsT[feature][token] (phi
+// applied when asked, rows past nrow zero), and, when given, the same values
+// token-major into lds[token][feature].
+template <bool PHI>
+__device__ __forceinline__ void stage_f32_fm(float* ldsT, float* lds, int nrow, const f32x4 (&raw)[PCF]) {
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    const int j = 16 * g + s;
-    const float a = sKf[j * LDF + 16 * w + li];
-    zacc = mfma4(a, 1.f, zacc);
+  for (int r = 0; r < PCF; ++r) {
+    const int p = threadIdx.x + NTF * r;
+    const int j = p / 16, c4 = p % 16;
+    f32x4 x = raw[r];
+    if (j < nrow) {
+      if (PHI) {
 #pragma unroll
-    for (int n = 0; n < 4; ++n) Sacc[n] = mfma4(a, sV[j * LDF + 16 * n + li], Sacc[n]);
+        for (int e = 0; e < 4; ++e) x[e] = phi_f(x[e]);
+      }
+    } else {
+      x = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (lds) *reinterpret_cast<f32x4*>(lds + j * LDF + 4 * c4) = x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ldsT[(4 * c4 + e) * LDF + j] = x[e];
   }
 }
 
-__device__ __forceinline__ void write_state_f32(float* sS, float* sZ, const f32x4_t (&Sacc)[4], const f32x4_t& zacc,
-                                                int w, int g, int li) {
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int d = 16 * w + 4 * g + u;
-#pragma unroll
-    for (int n = 0; n < 4; ++n) sS[d * LDF + 16 * n + li] = Sacc[n][u];
-    if (li == 0) sZ[d] = zacc[u];
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Forward.  Wave w owns query rows 16w .. 16w + 15 of each 64-token chunk.
-// ---------------------------------------------------------------------------
 template <bool CAUSAL>
-__global__ __launch_bounds__(NT, 2) void k_fwd_f32mfma(const float* __restrict__ q, const float* __restrict__ k,
-                                                       const float* __restrict__ v, float* __restrict__ out,
-                                                       float* __restrict__ den_out, const float* __restrict__ carry,
-                                                       int64_t N, int P, int seg_len, int raw_carry) {
+__global__ __launch_bounds__(NTF, 1) void k_fwd_f32mfma(const float* __restrict__ q, const float* __restrict__ k,
+                                                        const float* __restrict__ v, float* __restrict__ out,
+                                                        float* __restrict__ den_out, const float* __restrict__ carry,
+                                                        int64_t N, int P, int seg_len, int raw_carry) {
   extern __shared__ __align__(16) float smf[];
-  float* sKf = smf;
-  float* sV = sKf + T * LDF;
-  float* sQf = sV + T * LDF;
-  float* sS = sQf + T * LDF;
-  float* sZ = sS + DF * LDF;
+  float* sKf = smf;                // phi(K), token-major
+  float* sKT = sKf + T * LDF;      // phi(K), feature-major
+  float* sVT = sKT + DF * LDF;     // V, feature-major
+  float* sQf = sVT + DF * LDF;     // phi(Q), token-major
+  float* sST = sQf + T * LDF;      // S^T
+  float* sZ = sST + DF * LDF;
   // w is wave-uniform (an SGPR): an MFMA under an EXEC-masked branch would
   // still write every lane.
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rt = w < 4 ? w : 3 - (w & 3);  // query row tile
+  const int ch = w >> 2;                   // column half (output and state)
+  const int sl = w & 3;                    // state row slab
   const int64_t bh = blockIdx.x / P;
   const int seg = blockIdx.x % P;
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
@@ -123,13 +142,14 @@ __global__ __launch_bounds__(NT, 2) void k_fwd_f32mfma(const float* __restrict__
   const float* vh = v + bh * N * DF;
   float* oh = out ? out + bh * N * DF : nullptr;
   float* dh = den_out ? den_out + bh * N : nullptr;
-  const int i = 16 * w + li;
+  const int i = 16 * rt + li;
 
-  f32x4_t Sacc[4], zacc;
+  // this wave's state part: Sacc[nn] holds S[16 sl + 4g + u][32 ch + 16 nn + li],
+  // zacc Z[16 sl + 4g + u]
+  f32x4_t Sacc[2], zacc;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-#pragma unroll
-    for (int n = 0; n < 4; ++n) Sacc[n][u] = 0.f;
+    Sacc[0][u] = Sacc[1][u] = 0.f;
     zacc[u] = 0.f;
   }
 #pragma unroll 4
@@ -137,37 +157,46 @@ __global__ __launch_bounds__(NT, 2) void k_fwd_f32mfma(const float* __restrict__
     const float* rec = cs + t * E;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int d = 16 * w + 4 * g + u;
+      const int d = 16 * sl + 4 * g + u;
 #pragma unroll
-      for (int n = 0; n < 4; ++n) Sacc[n][u] += rec[d * DF + 16 * n + li];
+      for (int nn = 0; nn < 2; ++nn) Sacc[nn][u] += rec[d * DF + 32 * ch + 16 * nn + li];
       zacc[u] += rec[DF * DF + d];
     }
   }
-  write_state_f32(sS, sZ, Sacc, zacc, w, g, li);
+  auto write_state = [&]() {
+#pragma unroll
+    for (int nn = 0; nn < 2; ++nn)
+      *reinterpret_cast<f32x4_t*>(sST + (32 * ch + 16 * nn + li) * LDF + 16 * sl + 4 * g) = Sacc[nn];
+    if (ch == 0 && li == 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sZ[16 * sl + 4 * g + u] = zacc[u];
+    }
+  };
+  write_state();
 
   int64_t c0 = r0;
   int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
-  f32x4 kraw[4], vraw[4], qraw[4];
+  f32x4 kraw[PCF], vraw[PCF], qraw[PCF];
   if (CAUSAL) {
-    load_f32(kraw, kh, c0, nrow);
-    load_f32(vraw, vh, c0, nrow);
+    load_f32<NTF>(kraw, kh, c0, nrow);
+    load_f32<NTF>(vraw, vh, c0, nrow);
   }
-  load_f32(qraw, qh, c0, nrow);
+  load_f32<NTF>(qraw, qh, c0, nrow);
   while (c0 < r1) {
     if (CAUSAL) {
-      stage_f32<true>(sKf, nrow, kraw);
-      stage_f32<false>(sV, nrow, vraw);
+      stage_f32_fm<true>(sKT, sKf, nrow, kraw);
+      stage_f32_fm<false>(sVT, nullptr, nrow, vraw);
     }
-    stage_f32<true>(sQf, nrow, qraw);
+    stage_f32<true, NTF>(sQf, nrow, qraw);
     __syncthreads();
     const int64_t c1 = c0 + T;
     const int nrow1 = c1 < r1 ? static_cast<int>(min(static_cast<int64_t>(T), r1 - c1)) : 0;
     if (nrow1 > 0) {
       if (CAUSAL) {
-        load_f32(kraw, kh, c1, nrow1);
-        load_f32(vraw, vh, c1, nrow1);
+        load_f32<NTF>(kraw, kh, c1, nrow1);
+        load_f32<NTF>(vraw, vh, c1, nrow1);
       }
-      load_f32(qraw, qh, c1, nrow1);
+      load_f32<NTF>(qraw, qh, c1, nrow1);
     }
     // this lane's phi(Q_i) features 16g .. 16g + 15
     float qv[16];
@@ -177,14 +206,14 @@ __global__ __launch_bounds__(NT, 2) void k_fwd_f32mfma(const float* __restrict__
 #pragma unroll
       for (int e = 0; e < 4; ++e) qv[4 * s4 + e] = x[e];
     }
-    // scores A^T[j][i] for key tiles t <= w, masked j <= i
+    // scores A^T[j][i] for key tiles t <= rt, masked j <= i
     f32x4_t at[4];
     float rs = 0.f;
     if (CAUSAL) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         at[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (t <= w) {
+        if (t <= rt) {
 #pragma unroll
           for (int s4 = 0; s4 < 4; ++s4) {
             const f32x4 kx = *reinterpret_cast<const f32x4*>(sKf + (16 * t + li) * LDF + 16 * g + 4 * s4);
@@ -193,7 +222,7 @@ __global__ __launch_bounds__(NT, 2) void k_fwd_f32mfma(const float* __restrict__
           }
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            if (t == w && 4 * g + u > li) at[t][u] = 0.f;
+            if (t == rt && 4 * g + u > li) at[t][u] = 0.f;
             rs += at[t][u];
           }
         }
@@ -204,23 +233,28 @@ __global__ __launch_bounds__(NT, 2) void k_fwd_f32mfma(const float* __restrict__
 #pragma unroll
     for (int s = 0; s < 16; ++s) di += qv[s] * sZ[16 * g + s];
     const float den = shfl_sum_groups(rs + di);
-    // O^T[m][i] = sum_d S[d][m] phi(Q_i)[d] + sum_j V[j][m] A^T[j][i]
-    f32x4_t o[4];
+    // O^T[m][i] = sum_d S[d][m] phi(Q_i)[d] + sum_j V[j][m] A^T[j][i], m in this wave's half
+    f32x4_t o[2];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nn = 0; nn < 2; ++nn) {
+      o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const float* srow = sST + (32 * ch + 16 * nn + li) * LDF + 16 * g;
 #pragma unroll
-      for (int s = 0; s < 16; ++s) o[n] = mfma4(sS[(16 * g + s) * LDF + 16 * n + li], qv[s], o[n]);
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const f32x4 sx = *reinterpret_cast<const f32x4*>(srow + 4 * s4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[nn] = mfma4(sx[e], qv[4 * s4 + e], o[nn]);
+      }
     }
     if (CAUSAL) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        if (t <= w) {
+        if (t <= rt) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int j = 16 * t + 4 * g + u;
+          for (int nn = 0; nn < 2; ++nn) {
+            const f32x4 vx = *reinterpret_cast<const f32x4*>(sVT + (32 * ch + 16 * nn + li) * LDF + 16 * t + 4 * g);
 #pragma unroll
-            for (int n = 0; n < 4; ++n) o[n] = mfma4(sV[j * LDF + 16 * n + li], at[t][u], o[n]);
+            for (int u = 0; u < 4; ++u) o[nn] = mfma4(vx[u], at[t][u], o[nn]);
           }
         }
       }
@@ -229,13 +263,31 @@ __global__ __launch_bounds__(NT, 2) void k_fwd_f32mfma(const float* __restrict__
       if (oh) {
         const float inv = 1.f / den;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) *reinterpret_cast<f32x4*>(oh + (c0 + i) * DF + 16 * n + 4 * g) = o[n] * inv;
+        for (int nn = 0; nn < 2; ++nn)
+          *reinterpret_cast<f32x4*>(oh + (c0 + i) * DF + 32 * ch + 16 * nn + 4 * g) = o[nn] * inv;
       }
-      if (dh && g == 0) dh[c0 + i] = den;
+      if (dh && ch == 0 && g == 0) dh[c0 + i] = den;
     }
-    if (CAUSAL) state_update_f32(Sacc, zacc, sKf, sV, w, g, li);
+    if (CAUSAL) {
+      // S[d][m] += sum_j phi(K_j)[d] V_j[m], Z[d] += sum_j phi(K_j)[d] (64 keys, j = 16g + s)
+      const float* krow = sKT + (16 * sl + li) * LDF + 16 * g;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(krow + 4 * s4);
+        f32x4 b[2];
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn)
+          b[nn] = *reinterpret_cast<const f32x4*>(sVT + (32 * ch + 16 * nn + li) * LDF + 16 * g + 4 * s4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (ch == 0) zacc = mfma4(a[e], 1.f, zacc);
+#pragma unroll
+          for (int nn = 0; nn < 2; ++nn) Sacc[nn] = mfma4(a[e], b[nn][e], Sacc[nn]);
+        }
+      }
+    }
     __syncthreads();
-    if (CAUSAL) write_state_f32(sS, sZ, Sacc, zacc, w, g, li);
+    if (CAUSAL) write_state();
     c0 = c1;
     nrow = nrow1;
   }
@@ -343,7 +395,7 @@ __global__ __launch_bounds__(NT, 2) void k_seg_state_f32mfma(const float* __rest
     }
 }
 
-constexpr size_t kLdsFwd = (3 * T * LDF + DF * LDF + DF) * sizeof(float);
+constexpr size_t kLdsFwd = (2 * T * LDF + 3 * DF * LDF + DF) * sizeof(float);  // phi(K) twice, V^T, phi(Q), S^T, Z
 constexpr size_t lds_seg_f32(int dim) { return 2 * T * (dim + 4) * sizeof(float); }
 
 }  // namespace
@@ -361,10 +413,10 @@ hipError_t launch_forward_f32mfma(int causal, const SegGeom& g, const void* q, c
   const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsFwd));
   if (e != hipSuccess) return e;
   if (causal)
-    hipLaunchKernelGGL((k_fwd_f32mfma<true>), grid, dim3(NT), kLdsFwd, st, Q, K, V, O, den_out, carry, g.N, g.P,
+    hipLaunchKernelGGL((k_fwd_f32mfma<true>), grid, dim3(NTF), kLdsFwd, st, Q, K, V, O, den_out, carry, g.N, g.P,
                        g.seg_len, raw_carry);
   else
-    hipLaunchKernelGGL((k_fwd_f32mfma<false>), grid, dim3(NT), kLdsFwd, st, Q, K, V, O, den_out, carry, g.N, g.P,
+    hipLaunchKernelGGL((k_fwd_f32mfma<false>), grid, dim3(NTF), kLdsFwd, st, Q, K, V, O, den_out, carry, g.N, g.P,
                        g.seg_len, 0);
   return hipGetLastError();
 }
