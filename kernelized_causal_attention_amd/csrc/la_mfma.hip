@@ -380,33 +380,44 @@ __global__ __launch_bounds__(512, 1) void k_fwd_mfma_db(const bf16_t* __restrict
 
   // Rows of a chunk past the segment's end lie past the head's end
   // (segments are whole chunks): the buffer range check zeroes them, and
-  // store_tile zeroes phi(K) and phi(Q) there.
-  i32x4 kraw[PC], vraw[PC], qraw[PC];
-  auto fetch = [&](int64_t cc0) {
-    const int soff = static_cast<int>(cc0 * DIM * 2);
-    bload_tile<DIM, NW>(kraw, rk, soff);
-    bload_tile<DIM, NW>(vraw, rv, soff);
-    bload_tile<DIM, NW>(qraw, rq, soff);
+  // store_tile zeroes phi(K) and phi(Q) there.  Two chunks are in flight:
+  // while chunk c computes, one register set holds chunk c + 1 (staged into
+  // the other LDS half at the end of chunk c, then refilled with chunk
+  // c + 3) and the other is receiving chunk c + 2.  A load for a chunk past
+  // the segment's end is still issued, at an offset past the head's range
+  // (zeros, no memory traffic), so that every trip issues the same memory
+  // operations and the waits for one set leave the other's loads in flight.
+  struct Raw {
+    i32x4 k[PC], v[PC], q[PC];
   };
-  auto put = [&](uint16_t* tiles, int nr) {
-    store_tile<DIM, true, NW>(tiles, kraw, nr);
-    store_tile<DIM, false, NW>(tiles + TILE, vraw, nr);
-    store_tile<DIM, true, NW>(tiles + 2 * TILE, qraw, nr);
+  Raw ra, rb;
+  const int hbytes = static_cast<int>(N * DIM * 2);
+  auto fetch = [&](Raw& x, int64_t cc0) {
+    const int soff = cc0 < r1 ? static_cast<int>(cc0 * DIM * 2) : hbytes;
+    bload_tile<DIM, NW>(x.k, rk, soff);
+    bload_tile<DIM, NW>(x.v, rv, soff);
+    bload_tile<DIM, NW>(x.q, rq, soff);
   };
+  auto put = [&](uint16_t* tiles, const Raw& x, int nr) {
+    store_tile<DIM, true, NW>(tiles, x.k, nr);
+    store_tile<DIM, false, NW>(tiles + TILE, x.v, nr);
+    store_tile<DIM, true, NW>(tiles + 2 * TILE, x.q, nr);
+  };
+  auto rows_of = [&](int64_t cc0) { return cc0 < r1 ? static_cast<int>(min(static_cast<int64_t>(T), r1 - cc0)) : 0; };
 
   int64_t c0 = r0;
-  int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
-  fetch(c0);
-  put(smem, nrow);
+  fetch(ra, c0);
+  put(smem, ra, rows_of(c0));
+  fetch(ra, c0 + T);
+  fetch(rb, c0 + 2 * T);
   __syncthreads();
   int buf = 0;
-  while (c0 < r1) {
+  // one chunk; `nx` holds chunk c0 + T on entry and chunk c0 + 3T on exit
+  auto step = [&](Raw& nx) __attribute__((always_inline)) {
     const uint16_t* sKf = smem + buf * 3 * TILE;
     const uint16_t* sV = sKf + TILE;
     const uint16_t* sQf = sKf + 2 * TILE;
-    const int64_t c1 = c0 + T;
-    const int nrow1 = c1 < r1 ? static_cast<int>(min(static_cast<int64_t>(T), r1 - c1)) : 0;
-    if (nrow1 > 0) fetch(c1);
+    const int nrow1 = rows_of(c0 + T);
 
     i16x8 qf[KS];
 #pragma unroll
@@ -427,19 +438,24 @@ __global__ __launch_bounds__(512, 1) void k_fwd_mfma_db(const bf16_t* __restrict
     uint16_t* nxt = smem + (buf ^ 1) * 3 * TILE;
     if (nrow1 == T) {
       state_update<DIM, NW>(Sacc, zacc, sKf, sV, w, g, li);
-      store_tile_full<DIM, true, NW>(nxt, kraw);
-      store_tile_full<DIM, false, NW>(nxt + TILE, vraw);
-      store_tile_full<DIM, true, NW>(nxt + 2 * TILE, qraw);
+      store_tile_full<DIM, true, NW>(nxt, nx.k);
+      store_tile_full<DIM, false, NW>(nxt + TILE, nx.v);
+      store_tile_full<DIM, true, NW>(nxt + 2 * TILE, nx.q);
     } else {
       state_update<DIM, NW>(Sacc, zacc, sKf, sV, w, g, li);
-      if (nrow1 > 0) put(nxt, nrow1);
+      if (nrow1 > 0) put(nxt, nx, nrow1);
     }
+    fetch(nx, c0 + 3 * T);
     __syncthreads();  // every read of S^T, Z and this half done
     write_state<DIM, NW>(sST, sZ, Sacc, zacc, w, g, li);
     __syncthreads();  // S^T, Z and the next half written
-    c0 = c1;
-    nrow = nrow1;
+    c0 += T;
     buf ^= 1;
+  };
+  while (c0 < r1) {
+    step(ra);
+    if (c0 >= r1) break;
+    step(rb);
   }
 }
 
