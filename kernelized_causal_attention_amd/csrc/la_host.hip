@@ -212,7 +212,14 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
   // calls with this plan
   if (chunk == 128 && !(kernel == LA_KERNEL_MFMA && dtype == LA_BF16 && D == 64 && M == 64))
     return fail(LA_ERR_INVALID, "plan.chunk=128 is the bf16 MFMA forward at D = M = 64 only");
-  const int unit = kernel == LA_KERNEL_MFMA ? (chunk == 128 ? 128 : 64) : 32;  // segment granularity
+  // The backward cuts its segments as the forward of the same call does, so
+  // that the forward's saved records fit it: where the automatic plan runs
+  // the MFMA forward but has no MFMA backward (fp32 at D = M = 64), the
+  // generic backward runs over the MFMA forward's segments.
+  bool mfma_seg = kernel == LA_KERNEL_MFMA;
+  if (op == LA_OP_BACKWARD && kernel == LA_KERNEL_GENERIC && (!req || req->kernel == LA_KERNEL_AUTO))
+    mfma_seg = la::mfma_supported(LA_OP_FORWARD, D, M, dtype) && N * std::max(D, M) * 2 < (int64_t(1) << 31);
+  const int unit = mfma_seg ? (chunk == 128 ? 128 : 64) : 32;  // segment granularity
   if (demoted) {
     kernel = LA_KERNEL_GENERIC;
     chunk = 0;
@@ -239,7 +246,7 @@ la_status resolve(int op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
     // two workgroups per CU (measured best on the B=8, H=16, N=8192, D=64
     // step: 512 beats 1024, 768 and 2048).  Segments keep at least 4 units;
     // more segments only add scan work.
-    const int64_t target = (kernel == LA_KERNEL_MFMA || demoted) ? 512 : 1024;
+    const int64_t target = (kernel == LA_KERNEL_MFMA || mfma_seg) ? 512 : 1024;
     const int64_t want = (target + BH - 1) / BH;
     P = std::min<int64_t>(want, std::max<int64_t>(1, nunits / 4));
     // (the retention backward anchors its gate gradients every kRetAnchor

@@ -93,6 +93,28 @@ def test_resolve_plan(lib):
     assert lib.la_resolve_plan(0, 1, 1, 1 << 23, 128, 128, 1, 1, ctypes.byref(mf), ctypes.byref(out)) == 2
 
 
+def test_backward_plan_cuts_segments_like_the_forward(lib):
+    # The forward's saved records are per segment of its plan, so the
+    # backward of the same call must cut the sequence the same way, also where
+    # the two ops run different kernel families: fp32 at D = M = 64 has an
+    # MFMA forward but only the generic backward.  Checked through the
+    # resolved segment counts and the saved-state size the forward reports.
+    fwd, bwd = _native.la_plan(), _native.la_plan()
+    for dtype, D in ((0, 64), (0, 32), (0, 128), (1, 64), (1, 128), (1, 48)):
+        for causal in (1, 0):
+            for N in (1104, 1435, 2048, 700, 64, 33):
+                for segs in (0, 1, 3, 5):
+                    req = _native.la_plan(0, segs, 0)
+                    assert lib.la_resolve_plan(0, 2, 2, N, D, D, causal, dtype, ctypes.byref(req), ctypes.byref(fwd)) == 0
+                    assert lib.la_resolve_plan(1, 2, 2, N, D, D, causal, dtype, ctypes.byref(req), ctypes.byref(bwd)) == 0
+                    assert fwd.segments == bwd.segments, (dtype, D, causal, N, segs, fwd.segments, bwd.segments)
+    # fp32 D = 64: MFMA forward, generic backward, on the forward's segments
+    req = _native.la_plan(0, 5, 0)
+    assert lib.la_resolve_plan(0, 2, 2, 1104, 64, 64, 1, 0, ctypes.byref(req), ctypes.byref(fwd)) == 0
+    assert lib.la_resolve_plan(1, 2, 2, 1104, 64, 64, 1, 0, ctypes.byref(req), ctypes.byref(bwd)) == 0
+    assert (fwd.kernel, bwd.kernel, fwd.segments, bwd.segments) == (2, 1, 5, 5)
+
+
 def test_resolve_plan_chunk_128(lib):
     # 128-token chunks: the bf16 MFMA forward at D = M = 64 only; segments are
     # whole 128-token chunks (for every op of a call with that plan, so the
@@ -259,6 +281,23 @@ def test_saved_state_arguments_are_validated(lib):
 
     assert bwd(ssz=need - 4) == 1 and b"saved too small" in lib.la_last_error()
     assert bwd(dq=S) == 1 and b"overlaps input saved" in lib.la_last_error()
+
+
+@nogpu
+def test_fp32_backward_takes_the_forwards_saved_states(lib):
+    # fp32 D = M = 64 on the automatic plan: the MFMA forward keeps its
+    # segment states, and the generic backward must accept them (the same
+    # segments).  The call is given a workspace that is too small, so it stops
+    # after the saved-state checks, before any HIP call: the error it reports
+    # is the workspace's, not a segment mismatch.
+    A, Bp, C, Dp, E, F, G, H_, S, W = (0x10000000 * (n + 1) for n in range(10))
+    for N, causal, segs in ((1104, 1, 5), (1435, 0, 0), (2048, 1, 0), (700, 1, 3)):
+        plan = _native.la_plan(0, segs, 0)
+        ssz = lib.la_saved_bytes(2, 2, N, 64, 64, causal, 0, ctypes.byref(plan))
+        assert ssz > 0
+        st = lib.la_backward_ex(A, Bp, C, Dp, E, None, S, ssz, F, G, H_, 2, 2, N, 64, 64, causal, 0, W, 1, None,
+                                ctypes.byref(plan))
+        assert st == 1 and b"workspace too small" in lib.la_last_error(), (N, causal, segs, lib.la_last_error())
 
 
 @nogpu

@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 DEV = "cuda"
-NCASES = 64
+NCASES = 128
 
 
 def say(*a):
