@@ -52,14 +52,16 @@ __device__ __forceinline__ void put_c(uint16_t* sCh, int i, float c) {
 }
 
 // Per-wave state layout used by both kernels: X^T accumulators (X = S or R)
-// for the wave's column tiles mt = w*MT + a, all row tiles n:
+// for the wave's column tiles mt = w*DT + a, all row tiles n:
 //   lane holds X[d = 16n + li][m = 16mt + 4g + u];
 // vector accumulators (Z or r) for the wave's row tiles dt = w*DT + b:
 //   lane holds x[16dt + li] (the same in all four u).
-template <int DIM>
-__device__ __forceinline__ void init_xt(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&x)[Geo<DIM>::DT],
+// NW waves share the state: DT = D / 16 / NW tiles each (two at D = 128 with
+// four waves, one with eight).
+template <int DIM, int NW = 4>
+__device__ __forceinline__ void init_xt(f32x4_t (&X)[(Geo<DIM, NW>::DT)][(Geo<DIM, NW>::NTL)], f32x4_t (&x)[(Geo<DIM, NW>::DT)],
                                         const float* __restrict__ src, int w, int g, int li) {
-  using G = Geo<DIM>;
+  using G = Geo<DIM, NW>;
 #pragma unroll
   for (int a = 0; a < G::DT; ++a) {
     const int mt = w * G::DT + a;
@@ -76,11 +78,11 @@ __device__ __forceinline__ void init_xt(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL
 // aggregate records recs[P - 1], recs[P - 2], ..., recs[seg + 1] -- summed in
 // that order from zero, as the reverse exclusive scan of the records forms
 // it -- in the layout of init_xt.
-template <int DIM>
-__device__ __forceinline__ void init_xt_suffix(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&x)[Geo<DIM>::DT],
+template <int DIM, int NW = 4>
+__device__ __forceinline__ void init_xt_suffix(f32x4_t (&X)[(Geo<DIM, NW>::DT)][(Geo<DIM, NW>::NTL)], f32x4_t (&x)[(Geo<DIM, NW>::DT)],
                                                const float* __restrict__ recs, int seg, int P, int w, int g,
                                                int li) {
-  using G = Geo<DIM>;
+  using G = Geo<DIM, NW>;
   constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;
 #pragma unroll
   for (int a = 0; a < G::DT; ++a) {
@@ -105,10 +107,10 @@ __device__ __forceinline__ void init_xt_suffix(f32x4_t (&X)[Geo<DIM>::DT][Geo<DI
 }
 
 // bf16 row-major copy X[d][m] and fp32 vector x[d] into LDS.
-template <int DIM>
-__device__ __forceinline__ void write_xt(uint16_t* sX, float* sx, const f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL],
-                                         const f32x4_t (&x)[Geo<DIM>::DT], int w, int g, int li) {
-  using G = Geo<DIM>;
+template <int DIM, int NW = 4>
+__device__ __forceinline__ void write_xt(uint16_t* sX, float* sx, const f32x4_t (&X)[(Geo<DIM, NW>::DT)][(Geo<DIM, NW>::NTL)],
+                                         const f32x4_t (&x)[(Geo<DIM, NW>::DT)], int w, int g, int li) {
+  using G = Geo<DIM, NW>;
 #pragma unroll
   for (int a = 0; a < G::DT; ++a) {
     const int mt = w * G::DT + a;
@@ -119,10 +121,10 @@ __device__ __forceinline__ void write_xt(uint16_t* sX, float* sx, const f32x4_t 
   }
 }
 
-template <int DIM>
-__device__ __forceinline__ void store_xt(float* __restrict__ rec, const f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL],
-                                         const f32x4_t (&x)[Geo<DIM>::DT], int w, int g, int li) {
-  using G = Geo<DIM>;
+template <int DIM, int NW = 4>
+__device__ __forceinline__ void store_xt(float* __restrict__ rec, const f32x4_t (&X)[(Geo<DIM, NW>::DT)][(Geo<DIM, NW>::NTL)],
+                                         const f32x4_t (&x)[(Geo<DIM, NW>::DT)], int w, int g, int li) {
+  using G = Geo<DIM, NW>;
 #pragma unroll
   for (int a = 0; a < G::DT; ++a) {
     const int mt = w * G::DT + a;
@@ -138,11 +140,11 @@ __device__ __forceinline__ void store_xt(float* __restrict__ rec, const f32x4_t 
 // x[d] += sum_j w_j B[j][d] (w = ones, or c as the hi + lo pair in sCh when
 // WC; every row of that A operand is the same, so the MFMA result is
 // sum_j c_j B[j][col]).
-template <int DIM, bool WC>
-__device__ __forceinline__ void outer_update(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&x)[Geo<DIM>::DT],
+template <int DIM, bool WC, int NW = 4>
+__device__ __forceinline__ void outer_update(f32x4_t (&X)[(Geo<DIM, NW>::DT)][(Geo<DIM, NW>::NTL)], f32x4_t (&x)[(Geo<DIM, NW>::DT)],
                                              const uint16_t* sA, const uint16_t* sB, const uint16_t* sCh, int w,
                                              int g, int li) {
-  using G = Geo<DIM>;
+  using G = Geo<DIM, NW>;
   const short one = 0x3f80;
   const i16x8 ones = {one, one, one, one, one, one, one, one};
 #pragma unroll
@@ -187,11 +189,11 @@ __device__ __forceinline__ void outer_update(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>
 // sums do, and they need nothing but S and Z; with mu = 0, U = 0 and n = 0).
 // y holds, for the wave's column tiles, a vector over m in the X^T
 // accumulator layout: lane holds y[16mt + 4g + u].
-template <int DIM>
-__device__ __forceinline__ float init_split(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&x)[Geo<DIM>::DT],
-                                            f32x4_t (&y)[Geo<DIM>::DT], const float* __restrict__ rec,
+template <int DIM, int NW = 4>
+__device__ __forceinline__ float init_split(f32x4_t (&X)[(Geo<DIM, NW>::DT)][(Geo<DIM, NW>::NTL)], f32x4_t (&x)[(Geo<DIM, NW>::DT)],
+                                            f32x4_t (&y)[(Geo<DIM, NW>::DT)], const float* __restrict__ rec,
                                             const float* sMuF, float smu2, int w, int g, int li) {
-  using G = Geo<DIM>;
+  using G = Geo<DIM, NW>;
   const float inv = smu2 > 0.f ? 1.f / smu2 : 0.f;
   // n = mu.Z / mu.mu: every wave sums all D entries (lane l reads Z[l],
   // Z[l + 64])
@@ -251,19 +253,19 @@ __device__ __forceinline__ float mu_sq_sum(const float* sMuF, bool* all_one) {
   return m;
 }
 
-template <int DIM>
-__device__ __forceinline__ void write_y(float* sy, const f32x4_t (&y)[Geo<DIM>::DT], int w, int g, int li) {
+template <int DIM, int NW = 4>
+__device__ __forceinline__ void write_y(float* sy, const f32x4_t (&y)[(Geo<DIM, NW>::DT)], int w, int g, int li) {
 #pragma unroll
-  for (int a = 0; a < Geo<DIM>::DT; ++a)
-    if (li == 0) *reinterpret_cast<f32x4_t*>(sy + 16 * (w * Geo<DIM>::DT + a) + 4 * g) = y[a];
+  for (int a = 0; a < Geo<DIM, NW>::DT; ++a)
+    if (li == 0) *reinterpret_cast<f32x4_t*>(sy + 16 * (w * Geo<DIM, NW>::DT + a) + 4 * g) = y[a];
 }
 
 // outer_update plus y[m] += sum_j A[j][m] (column sums of the A side).
-template <int DIM, bool WC>
-__device__ __forceinline__ void outer_update_y(f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL], f32x4_t (&x)[Geo<DIM>::DT],
-                                               f32x4_t (&y)[Geo<DIM>::DT], const uint16_t* sA, const uint16_t* sB,
+template <int DIM, bool WC, int NW = 4>
+__device__ __forceinline__ void outer_update_y(f32x4_t (&X)[(Geo<DIM, NW>::DT)][(Geo<DIM, NW>::NTL)], f32x4_t (&x)[(Geo<DIM, NW>::DT)],
+                                               f32x4_t (&y)[(Geo<DIM, NW>::DT)], const uint16_t* sA, const uint16_t* sB,
                                                const uint16_t* sCh, int w, int g, int li) {
-  using G = Geo<DIM>;
+  using G = Geo<DIM, NW>;
   const short one = 0x3f80;
   const i16x8 ones = {one, one, one, one, one, one, one, one};
 #pragma unroll
@@ -297,11 +299,11 @@ __device__ __forceinline__ void outer_update_y(f32x4_t (&X)[Geo<DIM>::DT][Geo<DI
 }
 
 // Suffix record (R, r) from R = R' + mu G^T, r = r' + C mu.
-template <int DIM>
-__device__ __forceinline__ void store_r(float* __restrict__ rec, const f32x4_t (&X)[Geo<DIM>::DT][Geo<DIM>::NTL],
-                                        const f32x4_t (&x)[Geo<DIM>::DT], const f32x4_t (&y)[Geo<DIM>::DT], float C,
+template <int DIM, int NW = 4>
+__device__ __forceinline__ void store_r(float* __restrict__ rec, const f32x4_t (&X)[(Geo<DIM, NW>::DT)][(Geo<DIM, NW>::NTL)],
+                                        const f32x4_t (&x)[(Geo<DIM, NW>::DT)], const f32x4_t (&y)[(Geo<DIM, NW>::DT)], float C,
                                         const float* sMuF, int w, int g, int li) {
-  using G = Geo<DIM>;
+  using G = Geo<DIM, NW>;
 #pragma unroll
   for (int a = 0; a < G::DT; ++a) {
     const int mt = w * G::DT + a;
@@ -353,15 +355,39 @@ __device__ __forceinline__ void store_r(float* __restrict__ rec, const f32x4_t (
 // MU1: every mu of the segment is 1 (the usual case: centred inputs), and
 // the mu terms are compile-time constants; otherwise they come from LDS
 // (dq_decide_mu ran first in either case).
-// Where the dq sweep keeps mu in LDS: after its tiles, state, c pairs and
-// output staging (the layout dq_body carves and lds_dq sizes).
+// Waves per workgroup of the two sweeps.  D = 64: four, two workgroups per
+// CU.  D = 128: with four waves each wave held two 16-column slabs of the
+// fp32 128 x 128 state besides its chunk work (~420 registers: one wave per
+// SIMD, nothing to hide its waits), so the sweeps run eight waves in one
+// workgroup per CU: every wave owns one state slab, and the two waves of a
+// pair take the same 16 rows of the chunk and half of the output columns
+// each (both form the rows' scores, den and c).
+template <int DIM>
+constexpr int kBwdWaves = DIM == 128 ? 8 : 4;
+
+// LDS of the dq sweep (byte offsets): E(K), V and E(Q) tiles (E(Q) twice and
+// the g tile twice when the (R, r) aggregate is fused, so that it is summed
+// after the chunk's last barrier), bf16 S', fp32 Z' and U, four floats of
+// c sums, with eight waves the pair's partial dot products (2 x T floats),
+// c hi/lo pairs (two buffers of 2T), per-wave output staging (16 rows of the
+// wave's SC columns), and mu as fp32 and bf16.
+template <int DIM>
+struct DqLds {
+  static constexpr int NW = kBwdWaves<DIM>, LD = DIM + kLdsPad;
+  static constexpr int NQ = DIM == 64 ? 2 : 1, NG = DIM == 64 ? 2 : 0;  // E(Q), g buffers
+  static constexpr int SC = 4 * DIM / NW;                               // output columns per wave
+  static constexpr int TILE = T * LD * 2;
+  static constexpr int KE = 0, V = TILE, QE = 2 * TILE, G = QE + NQ * TILE, S = G + NG * TILE;
+  static constexpr int Z = S + DIM * LD * 2, U = Z + DIM * 4, RED = U + DIM * 4, DOT = RED + 4 * 4;
+  static constexpr int CH = DOT + (NW == 8 ? 2 * T * 4 : 0), STAGE = CH + 4 * T * 2;
+  static constexpr int MUF = STAGE + NW * 16 * (SC + kLdsPad) * 2, MUB = MUF + DIM * 4, BYTES = MUB + DIM * 2;
+  static_assert(Z % 16 == 0 && DOT % 16 == 0 && STAGE % 16 == 0 && MUF % 16 == 0, "16-byte LDS accesses");
+};
+
+// Where the dq sweep keeps mu in LDS (the layout above).
 template <int DIM>
 __device__ __forceinline__ float* dq_mu_lds(uint16_t* smem) {
-  constexpr int LD = Geo<DIM>::LD;
-  uint16_t* sS = smem + 6 * T * LD;
-  float* sRed = reinterpret_cast<float*>(sS + DIM * LD) + 2 * DIM;
-  uint16_t* sStage = reinterpret_cast<uint16_t*>(sRed + 4) + 4 * T;
-  return reinterpret_cast<float*>(sStage + 4 * 16 * LD);
+  return reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(smem) + DqLds<DIM>::MUF);
 }
 
 // The split constant mu of one segment's dq sweep into LDS (fp32 and bf16):
@@ -371,7 +397,8 @@ __device__ __forceinline__ float* dq_mu_lds(uint16_t* smem) {
 template <int DIM, bool CAUSAL>
 __device__ __forceinline__ bool dq_decide_mu(const bf16_t* __restrict__ k, const float* __restrict__ carry_s,
                                               int64_t N, int P, int seg_len, int64_t bh, int seg) {
-  using G = Geo<DIM>;
+  constexpr int NW = kBwdWaves<DIM>;
+  using G = Geo<DIM, NW>;
   extern __shared__ __align__(16) uint16_t smem[];
   float* sMuF = dq_mu_lds<DIM>(smem);
   uint16_t* sMuB = reinterpret_cast<uint16_t*>(sMuF + DIM);
@@ -379,8 +406,8 @@ __device__ __forceinline__ bool dq_decide_mu(const bf16_t* __restrict__ k, const
   const int64_t r1 = min(N, r0 + seg_len);
   if constexpr (CAUSAL) {
     i32x4 kraw[G::PC];
-    bload_tile<DIM>(kraw, make_rsrc(k + bh * N * DIM, N * DIM * 2), static_cast<int>(r0 * DIM * 2));
-    store_tile_e<DIM>(smem, kraw);  // the E(K) tile's place; the sweep overwrites it
+    bload_tile<DIM, NW>(kraw, make_rsrc(k + bh * N * DIM, N * DIM * 2), static_cast<int>(r0 * DIM * 2));
+    store_tile_e<DIM, NW>(smem, kraw);  // the E(K) tile's place; the sweep overwrites it
     __syncthreads();
     decide_mu<DIM, G::LD>(smem, static_cast<int>(min(static_cast<int64_t>(T), r1 - r0)), sMuF, sMuB);
   } else if (threadIdx.x < DIM) {
@@ -396,27 +423,36 @@ __device__ __forceinline__ bool dq_decide_mu(const bf16_t* __restrict__ k, const
   return all_one;
 }
 
-template <int DIM, bool CAUSAL, bool FUSED_R, int RW, bool MU1>
+template <int DIM, bool CAUSAL, bool FUSED_R, int RW, int H, bool MU1>
 __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                         const bf16_t* __restrict__ dout, const float* __restrict__ carry_s,
                                         bf16_t* __restrict__ dq, float* __restrict__ r_agg, float* __restrict__ c_out,
                                         float* __restrict__ den_out, int64_t N, int P, int seg_len, int64_t bh,
                                         int seg) {
-  using G = Geo<DIM>;
+  using L = DqLds<DIM>;
+  constexpr int NW = L::NW, SC = L::SC;
+  using G = Geo<DIM, NW>;
   constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
+  // this wave's output column tiles NB .. NB + NH - 1: all of them with four
+  // waves, half H of them with eight
+  constexpr int NH = SC / 16, NB = H * NH;
+  static_assert(!(FUSED_R && NW != 4), "the fused aggregate runs with four waves");
   extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t* sKe = smem;                // E(K) chunk tile
-  uint16_t* sV = sKe + T * LD;
-  uint16_t* sQe2 = sV + T * LD;        // E(Q), two buffers
-  uint16_t* sG2 = sQe2 + 2 * T * LD;   // g, two buffers
-  uint16_t* sS = sG2 + 2 * T * LD;     // bf16 S'
-  float* sZ = reinterpret_cast<float*>(sS + DIM * LD);  // Z'
-  float* sU = sZ + DIM;                // U
-  float* sRed = sU + DIM;              // 4 floats: per-wave sums of c
-  uint16_t* sCh2 = reinterpret_cast<uint16_t*>(sRed + 4);  // c hi/lo, two buffers of 2T
-  uint16_t* sStage = sCh2 + 4 * T;     // per-wave dq staging, 16 x LD each
-  const float* sMuF = dq_mu_lds<DIM>(smem);  // the split constant mu, fp32 (dq_decide_mu)
-  const uint16_t* sMuB = reinterpret_cast<const uint16_t*>(sMuF + DIM);  // and as bf16
+  unsigned char* lds = reinterpret_cast<unsigned char*>(smem);
+  uint16_t* sKe = reinterpret_cast<uint16_t*>(lds + L::KE);   // E(K) chunk tile
+  uint16_t* sV = reinterpret_cast<uint16_t*>(lds + L::V);
+  uint16_t* sQe2 = reinterpret_cast<uint16_t*>(lds + L::QE);  // E(Q), NQ buffers
+  uint16_t* sG2 = reinterpret_cast<uint16_t*>(lds + L::G);    // g, NG buffers
+  uint16_t* sS = reinterpret_cast<uint16_t*>(lds + L::S);     // bf16 S'
+  float* sZ = reinterpret_cast<float*>(lds + L::Z);           // Z'
+  float* sU = reinterpret_cast<float*>(lds + L::U);           // U
+  float* sRed = reinterpret_cast<float*>(lds + L::RED);       // 4 floats: per-wave sums of c
+  float* sDot = reinterpret_cast<float*>(lds + L::DOT);       // eight waves: the halves' dots
+  uint16_t* sCh2 = reinterpret_cast<uint16_t*>(lds + L::CH);  // c hi/lo, two buffers of 2T
+  uint16_t* sStage = reinterpret_cast<uint16_t*>(lds + L::STAGE);  // per-wave dq staging
+  const float* sMuF = reinterpret_cast<const float*>(lds + L::MUF);  // the split constant mu (dq_decide_mu)
+  const uint16_t* sMuB = reinterpret_cast<const uint16_t*>(lds + L::MUB);  // and as bf16
+  (void)sDot;
 
   // w is made wave-uniform (an SGPR) so that branches on it are scalar: an
   // MFMA under an EXEC-masked branch still writes every lane.
@@ -436,7 +472,7 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
   const bool want_r = FUSED_R && r_agg != nullptr;
   const int i = 16 * rw + li;
   const int cc = 4 * (li % 4);
-  uint16_t* sDQ = sStage + w * 16 * LD;
+  uint16_t* sDQ = sStage + w * 16 * (SC + kLdsPad);
   // causal mask of key j = 16t + 4g + u against query i = 16w + li, as 0 / 1
   // factors (kept in VGPRs: as per-(t, u) lane masks they would not fit in
   // the scalar registers)
@@ -451,10 +487,10 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
   i32x4 kraw[PC], vraw[PC], qraw[PC], graw[KS];
   auto fetch = [&](int soff) {
     if (CAUSAL) {
-      bload_tile<DIM>(kraw, rk, soff);
-      bload_tile<DIM>(vraw, rv, soff);
+      bload_tile<DIM, NW>(kraw, rk, soff);
+      bload_tile<DIM, NW>(vraw, rv, soff);
     }
-    bload_tile<DIM>(qraw, rq, soff);
+    bload_tile<DIM, NW>(qraw, rq, soff);
     bload_q<DIM>(graw, rg, soff, i, g);
   };
   fetch(static_cast<int>(c0 * DIM * 2));
@@ -462,33 +498,33 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
   bool all_one_;
   const float smu2 = MU1 ? static_cast<float>(DIM) : mu_sq_sum<DIM>(sMuF, &all_one_);
   MuOff moff;
-  if constexpr (!MU1) moff = mu_offsets<DIM>(sMuF);
+  if constexpr (!MU1) moff = mu_offsets<DIM, NW>(sMuF);
   const short one = 0x3f80;  // bf16 1.0
   const i16x8 ones = {one, one, one, one, one, one, one, one};
 
   f32x4_t Sacc[DT][NTL], zacc[DT], uacc[DT];
   // n0: the mu-direction count of the state before the current chunk
-  float n0 = init_split<DIM>(Sacc, zacc, uacc, cs, sMuF, smu2, w, g, li);
+  float n0 = init_split<DIM, NW>(Sacc, zacc, uacc, cs, sMuF, smu2, w, g, li);
   f32x4_t Racc[FUSED_R ? DT : 1][FUSED_R ? NTL : 1], racc[FUSED_R ? DT : 1], gacc[FUSED_R ? DT : 1];
   if constexpr (FUSED_R) init_split<DIM>(Racc, racc, gacc, nullptr, sMuF, smu2, w, g, li);
-  write_xt<DIM>(sS, sZ, Sacc, zacc, w, g, li);
-  write_y<DIM>(sU, uacc, w, g, li);
+  write_xt<DIM, NW>(sS, sZ, Sacc, zacc, w, g, li);
+  write_y<DIM, NW>(sU, uacc, w, g, li);
   float csum = 0.f;
 
   int buf = 0;
   while (c0 < r1) {
-    uint16_t* sQe = sQe2 + buf * T * LD;
-    uint16_t* sG = sG2 + buf * T * LD;
+    uint16_t* sQe = sQe2 + (L::NQ == 2 ? buf : 0) * T * LD;
+    uint16_t* sG = sG2 + (L::NG == 2 ? buf : 0) * T * LD;
     uint16_t* sCh = sCh2 + buf * 2 * T;
     // rows past the head's end were loaded as zero (elu(0) = 0)
     if constexpr (MU1) {
-      if (CAUSAL) store_tile_e<DIM>(sKe, kraw);
-      store_tile_e<DIM>(sQe, qraw);
+      if (CAUSAL) store_tile_e<DIM, NW>(sKe, kraw);
+      store_tile_e<DIM, NW>(sQe, qraw);
     } else {
-      if (CAUSAL) store_tile_emu<DIM>(sKe, kraw, nrow, moff);
-      store_tile_emu<DIM>(sQe, qraw, nrow, moff);
+      if (CAUSAL) store_tile_emu<DIM, NW>(sKe, kraw, nrow, moff);
+      store_tile_emu<DIM, NW>(sQe, qraw, nrow, moff);
     }
-    if (CAUSAL) store_tile_v<DIM>(sV, vraw);
+    if (CAUSAL) store_tile_v<DIM, NW>(sV, vraw);
     __syncthreads();
     const bool valid = i < nrow;
     i32x4 gcur[KS];
@@ -573,13 +609,14 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
       for (int e = 0; e < 8; ++e) gu += gv[e] * uv[e];
     }
     gu = shfl_sum_groups(gu);
-    // --- S' g_i  (dQ^T[d][i] inter term) and Bv^T[j][i] = g_i . V_j
-    f32x4_t o[NTL];
+    // --- S' g_i  (dQ^T[d][i] inter term, this wave's columns) and
+    // Bv^T[j][i] = g_i . V_j
+    f32x4_t o[NH];
 #pragma unroll
-    for (int n = 0; n < NTL; ++n) {
-      o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < NH; ++a) {
+      o[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) o[n] = mfma(lds8(sS + (16 * n + li) * LD + 8 * g + 32 * s), gq[s], o[n]);
+      for (int s = 0; s < KS; ++s) o[a] = mfma(lds8(sS + (16 * (NB + a) + li) * LD + 8 * g + 32 * s), gq[s], o[a]);
     }
     f32x4_t bv[4];
     if (CAUSAL) {
@@ -595,9 +632,17 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
     // --- c_i = -(sum_j A_ij bv_ij + (D + sq_i) g.U + sum_d (1 + E_i) (S'g)) / den_i
     float dot = 0.f, sbv = 0.f;
 #pragma unroll
-    for (int n = 0; n < NTL; ++n)
+    for (int a = 0; a < NH; ++a)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) dot += pq[n][u] * o[n][u];
+      for (int u = 0; u < 4; ++u) dot += pq[NB + a][u] * o[a][u];
+    if constexpr (NW == 8) {
+      // the pair's two halves of sum_d phi(Q_i)[d] (S'g)[d], added in half
+      // order so that both waves form the same c
+      const float half = shfl_sum_groups(dot);
+      if (g == 0) sDot[H * T + i] = half;
+      dot = 0.f;
+      __syncthreads();
+    }
     if (CAUSAL) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -609,11 +654,12 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
           }
         }
     }
-    const float c = -(shfl_sum_groups(dot) + dq_i * gu) * inv;
+    const float dsum = NW == 8 ? (sDot[i] + sDot[T + i]) + shfl_sum_groups(dot) : shfl_sum_groups(dot);
+    const float c = -(dsum + dq_i * gu) * inv;
     // beta_i = g.U + n_i c_i + sum_{j in chunk} g.V_j, n_i = n0 + (i + 1)
     const float beta = gu + c * (n0 + (CAUSAL ? static_cast<float>(i + 1) : 0.f)) + shfl_sum_groups(sbv);
     csum += c;
-    if (g == 0) {
+    if (g == 0 && H == 0) {
       if constexpr (FUSED_R) put_c(sCh, i, c);
       if (valid) {
         ch[c0 + i] = c;
@@ -626,37 +672,39 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
 #pragma unroll
       for (int t = 0; t < 4; ++t) bt[t] = pack4((bv[t] + c) * mt[t]);
 #pragma unroll
-      for (int n = 0; n < NTL; ++n) {
+      for (int a_ = 0; a_ < NH; ++a_) {
+        const int n = NB + a_;
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {
           if (2 * tp <= rw) {
             const int jr = 32 * tp + 4 * g + li / 4;
             const i16x8 a = cat(lds_tr(sKe + jr * LD + 16 * n + cc), lds_tr(sKe + (jr + 16) * LD + 16 * n + cc));
-            o[n] = mfma(a, cat(bt[2 * tp], bt[2 * tp + 1]), o[n]);
+            o[a_] = mfma(a, cat(bt[2 * tp], bt[2 * tp + 1]), o[a_]);
           }
         }
       }
     }
 #pragma unroll
-    for (int n = 0; n < NTL; ++n) {
+    for (int a = 0; a < NH; ++a) {
+      const int n = NB + a;
       const f32x4_t z = *reinterpret_cast<const f32x4_t*>(sZ + 16 * n + 4 * g);
       const f32x4_t mu4 = MU1 ? f32x4_t{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4_t*>(sMuF + 16 * n + 4 * g);
       f32x4_t r;
       // phi'(q) = min(phi(q), 1)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) r[u] = (mu4[u] * beta + o[n][u] + c * z[u]) * fminf(pq[n][u], 1.f);
-      stage_piece<DIM>(sDQ, pack4(r), li, g, n);
+      for (int u = 0; u < 4; ++u) r[u] = (mu4[u] * beta + o[a][u] + c * z[u]) * fminf(pq[n][u], 1.f);
+      stage_piece<SC>(sDQ, pack4(r), li, g, a);
     }
     __builtin_amdgcn_s_setprio(0);
-    store_staged<DIM, DIM>(sDQ, rdq, 16 * rw, 0, soff);
-    if (CAUSAL) outer_update_y<DIM, false>(Sacc, zacc, uacc, sV, sKe, nullptr, w, g, li);
+    store_staged<SC, DIM>(sDQ, rdq, 16 * rw, SC * H, soff);
+    if (CAUSAL) outer_update_y<DIM, false, NW>(Sacc, zacc, uacc, sV, sKe, nullptr, w, g, li);
     __syncthreads();
     // this chunk's g, E(Q) and c rows are complete: sum its (R, r) part
     if constexpr (FUSED_R)
       if (want_r) outer_update_y<DIM, true>(Racc, racc, gacc, sG, sQe, sCh, w, g, li);
     if (CAUSAL) {
-      write_xt<DIM>(sS, sZ, Sacc, zacc, w, g, li);
-      write_y<DIM>(sU, uacc, w, g, li);
+      write_xt<DIM, NW>(sS, sZ, Sacc, zacc, w, g, li);
+      write_y<DIM, NW>(sU, uacc, w, g, li);
     }
     if (CAUSAL) n0 += static_cast<float>(nrow);
     c0 = c1;
@@ -679,35 +727,52 @@ __device__ __forceinline__ void dq_body(const bf16_t* __restrict__ q, const bf16
 }
 
 template <int DIM, bool CAUSAL, bool FUSED_R>
-__global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                                                       const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
-                                                       const float* __restrict__ carry_s, bf16_t* __restrict__ dq,
-                                                       float* __restrict__ r_agg, float* __restrict__ c_out,
-                                                       float* __restrict__ den_out, int64_t N, int P, int seg_len) {
+__global__ __launch_bounds__(64 * kBwdWaves<DIM>, DIM == 64 ? 2 : 1) void k_bwd_dq_mfma(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, const float* __restrict__ carry_s, bf16_t* __restrict__ dq,
+    float* __restrict__ r_agg, float* __restrict__ c_out, float* __restrict__ den_out, int64_t N, int P,
+    int seg_len) {
   // The triangular intra-chunk work grows with a wave's row tile (tile t
-  // does t + 1 key tiles); odd workgroups map wave w to tile 3 - w, so two
-  // workgroups sharing a CU give every SIMD the same total.
+  // does t + 1 key tiles).  Four waves: odd workgroups map wave w to tile
+  // 3 - w, so two workgroups sharing a CU give every SIMD the same total.
+  // Eight waves (one workgroup per CU, waves w and w + 4 on one SIMD): wave
+  // w < 4 takes tile w and the first half of the columns, wave w >= 4 tile
+  // 7 - w and the second half, so every SIMD pairs a short and a long
+  // triangle and the two waves on tile t are t and 7 - t.
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t bh = blockIdx.x / P;
   const int seg = static_cast<int>(blockIdx.x % P);
   // the same value in every thread (read from LDS after a barrier)
   const bool mu1 = __builtin_amdgcn_readfirstlane(dq_decide_mu<DIM, CAUSAL>(k, carry_s, N, P, seg_len, bh, seg) ? 1 : 0) != 0;
-  switch ((blockIdx.x & 1) ? 3 - w : w) {
-#define LA_DQ_BODY(RW_)                                                                                          \
-  case RW_:                                                                                                      \
+#define LA_DQ_BODY(CASE_, RW_, H_)                                                                               \
+  case CASE_:                                                                                                    \
     if (mu1)                                                                                                     \
-      dq_body<DIM, CAUSAL, FUSED_R, RW_, true>(q, k, v, dout, carry_s, dq, r_agg, c_out, den_out, N, P, seg_len, \
-                                               bh, seg);                                                         \
+      dq_body<DIM, CAUSAL, FUSED_R, RW_, H_, true>(q, k, v, dout, carry_s, dq, r_agg, c_out, den_out, N, P,     \
+                                                   seg_len, bh, seg);                                            \
     else                                                                                                         \
-      dq_body<DIM, CAUSAL, FUSED_R, RW_, false>(q, k, v, dout, carry_s, dq, r_agg, c_out, den_out, N, P,        \
-                                                seg_len, bh, seg);                                               \
+      dq_body<DIM, CAUSAL, FUSED_R, RW_, H_, false>(q, k, v, dout, carry_s, dq, r_agg, c_out, den_out, N, P,    \
+                                                    seg_len, bh, seg);                                           \
     break
-    LA_DQ_BODY(0);
-    LA_DQ_BODY(1);
-    LA_DQ_BODY(2);
-    LA_DQ_BODY(3);
-#undef LA_DQ_BODY
+  if constexpr (kBwdWaves<DIM> == 4) {
+    switch ((blockIdx.x & 1) ? 3 - w : w) {
+      LA_DQ_BODY(0, 0, 0);
+      LA_DQ_BODY(1, 1, 0);
+      LA_DQ_BODY(2, 2, 0);
+      LA_DQ_BODY(3, 3, 0);
+    }
+  } else {
+    switch (w) {
+      LA_DQ_BODY(0, 0, 0);
+      LA_DQ_BODY(1, 1, 0);
+      LA_DQ_BODY(2, 2, 0);
+      LA_DQ_BODY(3, 3, 0);
+      LA_DQ_BODY(4, 3, 1);
+      LA_DQ_BODY(5, 2, 1);
+      LA_DQ_BODY(6, 1, 1);
+      LA_DQ_BODY(7, 0, 1);
+    }
   }
+#undef LA_DQ_BODY
 }
 
 // ---------------------------------------------------------------------------
@@ -794,9 +859,14 @@ __device__ __forceinline__ void dkdv_body(const bf16_t* __restrict__ q, const bf
                                           const float* __restrict__ den_in, const float* __restrict__ c_in,
                                           const float* __restrict__ carry_r, bf16_t* __restrict__ dk,
                                           bf16_t* __restrict__ dv, int64_t N, int P, int seg_len, int carry_raw,
-                                          int64_t bh, int seg, int rw, bool poison) {
-  using G = Geo<DIM>;
+                                          int64_t bh, int seg, int rw, int h, bool poison) {
+  constexpr int NW = kBwdWaves<DIM>;
+  using G = Geo<DIM, NW>;
   constexpr int LD = G::LD, NTL = G::NTL, KS = G::KS, PC = G::PC, DT = G::DT;
+  // this wave's output column tiles nb .. nb + NH - 1 (all of them with four
+  // waves; half h of them with eight, h = 0 also staging the rows' g and c)
+  constexpr int SC = 4 * DIM / NW, NH = SC / 16;
+  const int nb = h * NH;
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* sKf = smem;
   uint16_t* sV = sKf + T * LD;
@@ -812,9 +882,9 @@ __device__ __forceinline__ void dkdv_body(const bf16_t* __restrict__ q, const bf
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   (void)l;
-  // this wave's staging tiles for its dv and dk rows
-  uint16_t* sDV = sCh + 2 * T + w * 2 * 16 * LD;
-  uint16_t* sDK = sDV + 16 * LD;
+  // this wave's staging tiles for its dv and dk rows and columns
+  uint16_t* sDV = sCh + 2 * T + w * 2 * 16 * (SC + kLdsPad);
+  uint16_t* sDK = sDV + 16 * (SC + kLdsPad);
   const int64_t r0 = static_cast<int64_t>(seg) * seg_len;
   const int64_t r1 = min(N, r0 + seg_len);
   constexpr int64_t E = static_cast<int64_t>(DIM) * DIM + DIM;  // R, r record
@@ -839,9 +909,9 @@ __device__ __forceinline__ void dkdv_body(const bf16_t* __restrict__ q, const bf
   if (CAUSAL && carry_raw && carry_r)
     // carry_r holds the raw suffix aggregates: the carry is summed here (no
     // separate scan launch)
-    init_xt_suffix<DIM>(Racc, racc, carry_r + bh * P * E, seg, P, w, g, li);
+    init_xt_suffix<DIM, NW>(Racc, racc, carry_r + bh * P * E, seg, P, w, g, li);
   else
-    init_xt<DIM>(Racc, racc, cr, w, g, li);
+    init_xt<DIM, NW>(Racc, racc, cr, w, g, li);
   if (poison) {
     const float nan = __builtin_nanf("");
 #pragma unroll
@@ -851,7 +921,7 @@ __device__ __forceinline__ void dkdv_body(const bf16_t* __restrict__ q, const bf
       for (int n = 0; n < NTL; ++n) Racc[a][n] = racc[a];
     }
   }
-  write_xt<DIM>(sR, sRv, Racc, racc, w, g, li);
+  write_xt<DIM, NW>(sR, sRv, Racc, racc, w, g, li);
 
   const int64_t nch = (r1 - r0 + T - 1) / T;
   int64_t ci = nch - 1;
@@ -861,31 +931,35 @@ __device__ __forceinline__ void dkdv_body(const bf16_t* __restrict__ q, const bf
   float dnr = 1.f, cnr = 0.f;
   auto fetch = [&](int64_t cc0, int nr) {
     const int soff = static_cast<int>(cc0 * DIM * 2);
-    bload_tile<DIM>(kraw, rk, soff);
-    bload_tile<DIM>(vraw, rv, soff);
+    bload_tile<DIM, NW>(kraw, rk, soff);
+    bload_tile<DIM, NW>(vraw, rv, soff);
     if (CAUSAL) {
-      bload_tile<DIM>(qraw, rq, soff);
-      bload_q<DIM>(graw, rg, soff, j, g);
-      dnr = j < nr ? denh[cc0 + j] : 1.f;
-      cnr = j < nr ? chh[cc0 + j] : 0.f;
+      bload_tile<DIM, NW>(qraw, rq, soff);
+      if (h == 0) {
+        bload_q<DIM>(graw, rg, soff, j, g);
+        dnr = j < nr ? denh[cc0 + j] : 1.f;
+        cnr = j < nr ? chh[cc0 + j] : 0.f;
+      }
     }
   };
   fetch(c0, nrow);
 
   while (ci >= 0) {
-    store_tile<DIM, true>(sKf, kraw, nrow);
-    store_tile_v<DIM>(sV, vraw);
+    store_tile<DIM, true, NW>(sKf, kraw, nrow);
+    store_tile_v<DIM, NW>(sV, vraw);
     if (CAUSAL) {
       // the same g_i = bf16(dout_i / den_i) and c_i as the forward sweep used
-      store_tile<DIM, true>(sQf, qraw, nrow);
-      const float inv = j < nrow ? __builtin_amdgcn_rcpf(dnr) : 0.f;  // as in the forward sweep
+      store_tile<DIM, true, NW>(sQf, qraw, nrow);
+      if (h == 0) {
+        const float inv = j < nrow ? __builtin_amdgcn_rcpf(dnr) : 0.f;  // as in the forward sweep
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        *reinterpret_cast<i16x8*>(sG + j * LD + 8 * g + 32 * s) =
-            pack8(unpack8(__builtin_bit_cast(i16x8, graw[s])) * inv);
-      if (g == 0) {
-        sC[j] = cnr;
-        put_c(sCh, j, cnr);
+        for (int s = 0; s < KS; ++s)
+          *reinterpret_cast<i16x8*>(sG + j * LD + 8 * g + 32 * s) =
+              pack8(unpack8(__builtin_bit_cast(i16x8, graw[s])) * inv);
+        if (g == 0) {
+          sC[j] = cnr;
+          put_c(sCh, j, cnr);
+        }
       }
     }
     __syncthreads();
@@ -923,7 +997,8 @@ __device__ __forceinline__ void dkdv_body(const bf16_t* __restrict__ q, const bf
     }
     const int cc = 4 * (li % 4);
 #pragma unroll
-    for (int n = 0; n < NTL; ++n) {
+    for (int a_ = 0; a_ < NH; ++a_) {
+      const int n = nb + a_;
       // grad V^T[m][j] = R^T phi(K_j) (+ g^T A)
       f32x4_t ov = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -955,14 +1030,14 @@ __device__ __forceinline__ void dkdv_body(const bf16_t* __restrict__ q, const bf
       f32x4_t rk;
 #pragma unroll
       for (int u = 0; u < 4; ++u) rk[u] = (ok[u] + rr[u]) * fminf(kv[u], 1.f);
-      stage_piece<DIM>(sDV, pack4(ov), li, g, n);
-      stage_piece<DIM>(sDK, pack4(rk), li, g, n);
+      stage_piece<SC>(sDV, pack4(ov), li, g, a_);
+      stage_piece<SC>(sDK, pack4(rk), li, g, a_);
     }
-    store_staged<DIM, DIM>(sDV, rdv, 16 * rw, 0, soff);
-    store_staged<DIM, DIM>(sDK, rdk, 16 * rw, 0, soff);
-    if (CAUSAL) outer_update<DIM, true>(Racc, racc, sG, sQf, sCh, w, g, li);
+    store_staged<SC, DIM>(sDV, rdv, 16 * rw, SC * h, soff);
+    store_staged<SC, DIM>(sDK, rdk, 16 * rw, SC * h, soff);
+    if (CAUSAL) outer_update<DIM, true, NW>(Racc, racc, sG, sQf, sCh, w, g, li);
     __syncthreads();
-    if (CAUSAL) write_xt<DIM>(sR, sRv, Racc, racc, w, g, li);
+    if (CAUSAL) write_xt<DIM, NW>(sR, sRv, Racc, racc, w, g, li);
     --ci;
     c0 = cp;
     nrow = nrowp;
@@ -970,7 +1045,7 @@ __device__ __forceinline__ void dkdv_body(const bf16_t* __restrict__ q, const bf
 }
 
 template <int DIM, bool CAUSAL>
-__global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+__global__ __launch_bounds__(64 * kBwdWaves<DIM>, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                       const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
                                                       const float* __restrict__ den_in,
                                                       const float* __restrict__ c_in,
@@ -978,11 +1053,13 @@ __global__ __launch_bounds__(NT, DIM == 64 ? 2 : 1) void k_bwd_dkdv_mfma(const b
                                                       bf16_t* __restrict__ dv, int64_t N, int P, int seg_len,
                                                       int carry_raw) {
   // The triangular intra-chunk work grows with a wave's row tile (tile t
-  // does t + 1 key tiles); odd workgroups map wave w to tile 3 - w, so two
-  // workgroups sharing a CU give every SIMD the same total.
+  // does 4 - t query tiles): the row tiles and column halves are mapped to
+  // the waves as in the dq sweep.
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rt = kBwdWaves<DIM> == 4 ? ((blockIdx.x & 1) ? 3 - w : w) : (w < 4 ? w : 7 - w);
+  const int h = kBwdWaves<DIM> == 4 ? 0 : w >> 2;
   dkdv_body<DIM, CAUSAL>(q, k, v, dout, den_in, c_in, carry_r, dk, dv, N, P, seg_len, carry_raw, blockIdx.x / P,
-                         static_cast<int>(blockIdx.x % P), (blockIdx.x & 1) ? 3 - w : w, false);
+                         static_cast<int>(blockIdx.x % P), rt, h, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -1031,10 +1108,11 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_fused_mfma(
 #define LA_FUSED_DQ(RW_)                                                                                           \
   case RW_:                                                                                                        \
     if (mu1)                                                                                                       \
-      dq_body<DIM, true, true, RW_, true>(q, k, v, dout, carry_s, dq, ragg, c_ws, den_ws, N, P, seg_len, bh, seg); \
+      dq_body<DIM, true, true, RW_, 0, true>(q, k, v, dout, carry_s, dq, ragg, c_ws, den_ws, N, P, seg_len, bh,  \
+                                             seg);                                                               \
     else                                                                                                           \
-      dq_body<DIM, true, true, RW_, false>(q, k, v, dout, carry_s, dq, ragg, c_ws, den_ws, N, P, seg_len, bh,     \
-                                           seg);                                                                   \
+      dq_body<DIM, true, true, RW_, 0, false>(q, k, v, dout, carry_s, dq, ragg, c_ws, den_ws, N, P, seg_len, bh, \
+                                              seg);                                                              \
     break
     LA_FUSED_DQ(0);
     LA_FUSED_DQ(1);
@@ -1065,7 +1143,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_fused_mfma(
   }
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  dkdv_body<DIM, true>(q, k, v, dout, den_ws, c_ws, r_agg, dk, dv, N, P, seg_len, 1, bh, seg, rw, s_ok == 0);
+  dkdv_body<DIM, true>(q, k, v, dout, den_ws, c_ws, r_agg, dk, dv, N, P, seg_len, 1, bh, seg, rw, 0, s_ok == 0);
 }
 
 __global__ __launch_bounds__(256) void k_fill_u32(unsigned* __restrict__ p, int64_t n, unsigned val) {
@@ -1075,26 +1153,23 @@ __global__ __launch_bounds__(256) void k_fill_u32(unsigned* __restrict__ p, int6
 }
 
 size_t lds_bwd(int dim) {
+  const int nw = dim == 128 ? kBwdWaves<128> : kBwdWaves<64>, sc = 4 * dim / nw;
   return (4 * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t) + (dim + T) * sizeof(float) +
-         2 * T * sizeof(uint16_t) + 4 * 2 * 16 * (dim + kLdsPad) * sizeof(uint16_t);  // + output staging
+         2 * T * sizeof(uint16_t) + nw * 2 * 16 * (sc + kLdsPad) * sizeof(uint16_t);  // + output staging
 }
 // (+ the split constant mu as fp32 and bf16)
 size_t lds_ragg(int dim) {
   return 2 * T * (dim + kLdsPad) * sizeof(uint16_t) + 4 * sizeof(float) + 2 * T * sizeof(uint16_t) +
          dim * (sizeof(float) + sizeof(uint16_t));
 }
-size_t lds_dq(int dim) {
-  return (6 * T * (dim + kLdsPad) + dim * (dim + kLdsPad)) * sizeof(uint16_t) + (2 * dim + 4) * sizeof(float) +
-         4 * T * sizeof(uint16_t) + 4 * 16 * (dim + kLdsPad) * sizeof(uint16_t) +  // + output staging
-         dim * (sizeof(float) + sizeof(uint16_t));
-}
+size_t lds_dq(int dim) { return dim == 128 ? DqLds<128>::BYTES : DqLds<64>::BYTES; }
 
-#define LA_MLAUNCH(kernel, grid, lds, st, ...)                                                              \
+#define LA_MLAUNCH(kernel, threads, grid, lds, st, ...)                                                     \
   do {                                                                                                      \
     hipError_t e_ = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),                              \
                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)); \
     if (e_ != hipSuccess) return e_;                                                                        \
-    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(NT), lds, st, __VA_ARGS__);          \
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(threads), lds, st, __VA_ARGS__);     \
     return hipGetLastError();                                                                               \
   } while (0)
 
@@ -1105,9 +1180,9 @@ hipError_t launch_bwd_dq_mfma(int causal, const SegGeom& g, const void* q, const
                               float* den_out, hipStream_t st) {
   const int64_t grid = g.BH * g.P;
 #define LA_DQ(D, C, F)                                                                                       \
-  LA_MLAUNCH((k_bwd_dq_mfma<D, C, F>), grid, lds_dq(D), st, static_cast<const bf16_t*>(q),                 \
-             static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), \
-             carry_s, static_cast<bf16_t*>(dq), r_agg, c_out, den_out, g.N, g.P, g.seg_len)
+  LA_MLAUNCH((k_bwd_dq_mfma<D, C, F>), 64 * kBwdWaves<D>, grid, lds_dq(D), st,                              \
+             static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),   \
+             static_cast<const bf16_t*>(dout), carry_s, static_cast<bf16_t*>(dq), r_agg, c_out, den_out, g.N, g.P, g.seg_len)
   if (g.D == 64) {
     if (causal) LA_DQ(64, true, true);
     LA_DQ(64, false, true);
@@ -1118,7 +1193,7 @@ hipError_t launch_bwd_dq_mfma(int causal, const SegGeom& g, const void* q, const
     LA_DQ(128, false, false);
   }();
   if (e != hipSuccess || !r_agg) return e;
-  LA_MLAUNCH((k_bwd_ragg_mfma<128>), grid, lds_ragg(128), st, static_cast<const bf16_t*>(q),
+  LA_MLAUNCH((k_bwd_ragg_mfma<128>), NT, grid, lds_ragg(128), st, static_cast<const bf16_t*>(q),
              static_cast<const bf16_t*>(dout), den_out, c_out, r_agg, g.N, g.P, g.seg_len);
 #undef LA_DQ
 }
@@ -1156,7 +1231,7 @@ hipError_t launch_bwd_fused_mfma(const SegGeom& g, const void* q, const void* k,
                      dim3(256), 0, st, flags, nflags, 0u);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  LA_MLAUNCH((k_bwd_fused_mfma<64>), g.BH * g.P, lds_bwd_fused(64), st, static_cast<const bf16_t*>(q),
+  LA_MLAUNCH((k_bwd_fused_mfma<64>), NT, g.BH * g.P, lds_bwd_fused(64), st, static_cast<const bf16_t*>(q),
              static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout),
              carry_s, static_cast<bf16_t*>(dq), static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), r_agg, c_ws,
              den_ws, flags, err, want, spin_ticks, g.N, g.P, g.seg_len);
@@ -1167,9 +1242,9 @@ hipError_t launch_bwd_dkdv_mfma(int causal, const SegGeom& g, const void* q, con
                                 void* dk, void* dv, hipStream_t st, int carry_raw) {
   const int64_t grid = g.BH * g.P;
 #define LA_KV(D, C)                                                                                          \
-  LA_MLAUNCH((k_bwd_dkdv_mfma<D, C>), grid, lds_bwd(D), st, static_cast<const bf16_t*>(q),                  \
-             static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), \
-             den, c, carry_r, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), g.N, g.P, g.seg_len, carry_raw)
+  LA_MLAUNCH((k_bwd_dkdv_mfma<D, C>), 64 * kBwdWaves<D>, grid, lds_bwd(D), st,                              \
+             static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),   \
+             static_cast<const bf16_t*>(dout), den, c, carry_r, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), g.N, g.P, g.seg_len, carry_raw)
   if (g.D == 64) {
     if (causal) LA_KV(64, true);
     LA_KV(64, false);
