@@ -822,14 +822,23 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_ragg_mfma(const bf16_t* __restric
   f32x4_t Racc[DT][NTL], racc[DT], gacc[DT];
   init_split<DIM>(Racc, racc, gacc, nullptr, sMuF, 0.f, w, g, li);  // no carried record: zeros
   float csum = 0.f;
-  for (int64_t c0 = r0; c0 < r1; c0 += T) {
-    const int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
-    const int soff = static_cast<int>(c0 * DIM * 2);
+  // the next chunk's q tile, g rows, den and c are loaded while this one is
+  // summed (rows past the segment read as zero, den as 1)
+  float dn = 1.f, cn = 0.f;
+  auto fetch = [&](int64_t cc0) {
+    const int soff = static_cast<int>(cc0 * DIM * 2);
     bload_tile<DIM>(qraw, rq, soff);
     bload_q<DIM>(graw, rg, soff, i, g);
+    const bool ok = cc0 + i < r1;
+    dn = ok ? denh[cc0 + i] : 1.f;
+    cn = ok ? chh[cc0 + i] : 0.f;
+  };
+  fetch(r0);
+  for (int64_t c0 = r0; c0 < r1; c0 += T) {
+    const int nrow = static_cast<int>(min(static_cast<int64_t>(T), r1 - c0));
     const bool valid = i < nrow;
-    const float inv = valid ? __builtin_amdgcn_rcpf(denh[c0 + i]) : 0.f;  // as in the forward sweep
-    const float c = valid ? chh[c0 + i] : 0.f;
+    const float inv = valid ? __builtin_amdgcn_rcpf(dn) : 0.f;  // as in the forward sweep
+    const float c = valid ? cn : 0.f;
     store_tile_emu<DIM>(sQe, qraw, nrow, moff);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
@@ -837,6 +846,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_ragg_mfma(const bf16_t* __restric
     if (g == 0) put_c(sCh, i, c);
     csum += c;
     __syncthreads();
+    if (c0 + T < r1) fetch(c0 + T);
     outer_update_y<DIM, true>(Racc, racc, gacc, sG, sQe, sCh, w, g, li);
     __syncthreads();
   }
