@@ -340,14 +340,18 @@ __device__ __forceinline__ void store_r(float* __restrict__ rec, const f32x4_t (
 // and c_i = -(g_i . num_i) / den_i from the same pieces:
 //   g_i . num_i = sum_j A_ij (g_i.V_j) + (smu2 + mu.E_i)(g_i.U)
 //                 + sum_d (mu + E_i)[d] (S' g_i)[d].
-// The query, g and c tiles are double-buffered so that the (R, r) aggregate
-// of a chunk is summed after the chunk's last barrier: two barriers per
-// chunk.  R and r are accumulated the same way, R = mu G^T + sum_i E_i g_i^T
+// With the aggregate fused (D = 64) the query, g and c tiles are
+// double-buffered so that the (R, r) aggregate of a chunk is summed after
+// the chunk's last barrier: two barriers per chunk (three with eight waves,
+// whose pairs exchange half sums of the c numerator).  R and r are accumulated the same way, R = mu G^T + sum_i E_i g_i^T
 // and r = C mu + sum_i c_i E_i with G = sum_i g_i, C = sum_i c_i.
 // ---------------------------------------------------------------------------
-// FUSED_R: the (R, r) aggregate is summed here (D = 64); at D = 128 the two
-// fp32 128 x 128 states do not fit one wave's registers together, and
-// k_bwd_ragg_mfma sums the aggregate in a pass of its own.
+// FUSED_R: the (R, r) aggregate is summed here (D = 64).  At D = 128 the
+// second fp32 128 x 128 state costs each of the eight waves 40 more
+// registers than the two waves per SIMD leave (the fused variant spilled
+// and ran 0.555 ms against 0.495 for the sweep and the separate pass on
+// B=1 H=16 N=65536), and k_bwd_ragg_mfma sums the aggregate in a pass of
+// its own.
 // The sweep for one query row tile RW of the chunk: every branch on the
 // row tile (the triangle of key tiles) resolves at compile time, and the
 // chunk body becomes one stretch of code to schedule (the dq sweep is
