@@ -130,6 +130,8 @@ __global__ __launch_bounds__(NT) void k_seg_state(const TIn* __restrict__ k, con
 // ---------------------------------------------------------------------------
 // Exclusive scan of per-segment records along the segment axis, fixed order.
 // ---------------------------------------------------------------------------
+constexpr int kScanBatch = 8;
+
 __global__ __launch_bounds__(NT) void k_seg_scan(float* __restrict__ agg, int P, int64_t E, int64_t nb,
                                                  int reverse, int64_t DM, const float* init_s, const float* init_z,
                                                  float* tot_s, int64_t ts_stride, float* tot_z, int64_t tz_stride) {
@@ -139,14 +141,29 @@ __global__ __launch_bounds__(NT) void k_seg_scan(float* __restrict__ agg, int P,
   // (init and tot may be the same memory: each element is read here, by the
   // thread that writes its total below)
   float carry = init_s ? (e < DM ? init_s[bh * DM + e] : init_z[bh * (E - DM) + (e - DM)]) : 0.f;
-  for (int p = 0; p < P; ++p) {
-    const int s = reverse ? P - 1 - p : p;
-    float* ptr = agg + (bh * P + s) * E + e;
-    // without a total the last record's aggregate is never needed (and may
-    // not have been computed): it is not read
-    const float x = (tot_s || p + 1 < P) ? *ptr : 0.f;
-    *ptr = carry;
-    carry += x;
+  // Records are read kScanBatch at a time before any of them is overwritten:
+  // the compiler cannot order a record's load ahead of the previous record's
+  // store by itself (it cannot rule out that they alias), so a one-record
+  // loop would wait out a memory round trip per segment.
+  for (int p0 = 0; p0 < P; p0 += kScanBatch) {
+    float x[kScanBatch];
+#pragma unroll
+    for (int j = 0; j < kScanBatch; ++j) {
+      const int p = p0 + j;
+      const int s = reverse ? P - 1 - p : p;
+      // without a total the last record's aggregate is never needed (and
+      // may not have been computed): it is not read
+      x[j] = (p < P && (tot_s || p + 1 < P)) ? agg[(bh * P + s) * E + e] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kScanBatch; ++j) {
+      const int p = p0 + j;
+      if (p < P) {
+        const int s = reverse ? P - 1 - p : p;
+        agg[(bh * P + s) * E + e] = carry;
+        carry += x[j];
+      }
+    }
   }
   if (tot_s) {
     if (e < DM)

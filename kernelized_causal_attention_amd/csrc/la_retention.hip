@@ -466,6 +466,8 @@ __global__ __launch_bounds__(NT, 2) void k_ret_seg_wave64(const bf16_t* __restri
   if (tid == 0) rec[DIM * DIM] = lam * kLn2;
 }
 
+constexpr int kRetScanBatch = 8;
+
 // Decayed exclusive scan over segments, in place on the S part of the
 // records: C_0 = S0 (or 0), C_{p+1} = exp(Lambda_p) C_p + dS_p; record p
 // receives C_p; the total C_P goes to tot (when not null; tot may be S0).
@@ -475,18 +477,27 @@ __global__ __launch_bounds__(NT) void k_ret_scan(float* __restrict__ recs, int P
   const int64_t e = (blockIdx.x % nb) * NT + threadIdx.x;
   if (e >= DM) return;
   float carry = init ? init[bh * DM + e] : 0.f;
-  for (int p = 0; p < P; ++p) {
-    float* rec = recs + (bh * P + p) * E;
-    // without a total the last record's aggregate is never needed (and may
-    // not have been computed): it is not read
-    if (p + 1 == P && !tot) {
-      rec[e] = carry;
-      break;
+  // records read kRetScanBatch at a time before any is overwritten (the
+  // compiler cannot move a load past the previous record's store itself)
+  for (int p0 = 0; p0 < P; p0 += kRetScanBatch) {
+    float x[kRetScanBatch], lam[kRetScanBatch];
+#pragma unroll
+    for (int j = 0; j < kRetScanBatch; ++j) {
+      const int p = p0 + j;
+      // without a total the last record's aggregate is never needed (and
+      // may not have been computed): it is not read
+      const bool rd = p < P && (p + 1 < P || tot);
+      x[j] = rd ? recs[(bh * P + p) * E + e] : 0.f;
+      lam[j] = rd ? recs[(bh * P + p) * E + DM] : 0.f;
     }
-    const float x = rec[e];
-    const float lam = rec[DM];
-    rec[e] = carry;
-    carry = __expf(lam) * carry + x;
+#pragma unroll
+    for (int j = 0; j < kRetScanBatch; ++j) {
+      const int p = p0 + j;
+      if (p < P) {
+        recs[(bh * P + p) * E + e] = carry;
+        carry = __expf(lam[j]) * carry + x[j];
+      }
+    }
   }
   if (tot) tot[bh * DM + e] = carry;
 }
@@ -988,12 +999,22 @@ __global__ __launch_bounds__(NT) void k_ret_rscan(float* __restrict__ recs, int 
   const int64_t e = (blockIdx.x % nb) * NT + threadIdx.x;
   if (e >= DM) return;
   float carry = 0.f;
-  for (int p = P - 1; p >= 0; --p) {
-    float* rec = recs + (bh * P + p) * E;
-    const float x = rec[e];
-    const float lam = rec[DM];
-    rec[e] = carry;
-    carry = x + __expf(lam) * carry;
+  for (int p0 = P - 1; p0 >= 0; p0 -= kRetScanBatch) {
+    float x[kRetScanBatch], lam[kRetScanBatch];
+#pragma unroll
+    for (int j = 0; j < kRetScanBatch; ++j) {
+      const int p = p0 - j;
+      x[j] = p >= 0 ? recs[(bh * P + p) * E + e] : 0.f;
+      lam[j] = p >= 0 ? recs[(bh * P + p) * E + DM] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kRetScanBatch; ++j) {
+      const int p = p0 - j;
+      if (p >= 0) {
+        recs[(bh * P + p) * E + e] = carry;
+        carry = x[j] + __expf(lam[j]) * carry;
+      }
+    }
   }
   if (tot) tot[bh * DM + e] = carry;
 }
