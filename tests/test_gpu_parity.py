@@ -499,6 +499,26 @@ def test_backward_reads_saved_states(causal, kernel, dtype, D, segments):
         assert e < TOL[dtype], (n, e)
 
 
+@pytest.mark.parametrize("P", [9, 13])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_scan_over_more_than_eight_segments(P, dtype):
+    # The segment scan reads its records eight at a time before it stores
+    # any of them: 9 and 13 segments take one full batch and a partial one.
+    # Segments of one 64-token chunk each, the last one ragged; causal and
+    # non-causal forward (the latter scans to the totals) and, in bf16, the
+    # backward, which scans the prefix states again.
+    B, H, D = 2, 2, 64
+    N = 64 * P - 5
+    plan = dict(kernel=2, segments=P)
+    assert la.resolve_plan("forward", B, H, N, D, D, True, dtype, plan)["segments"] == P
+    tq, tk, tv, tg = host_case(B, H, N, D, D, dtype, seed=400 + P, scale=1.0 / np.sqrt(D))
+    say(f"scan batches: {dtype} segments={P}")
+    check_forward(tq, tk, tv, True, dtype, plan=plan, null_guard=True)
+    check_forward(tq, tk, tv, False, dtype, plan=plan)
+    if dtype == "bf16":
+        check_backward(tq, tk, tv, tg, True, dtype, plan=plan, floor_factor=4.0)
+
+
 @pytest.mark.parametrize("segments", [2, 3, 8, 16])
 def test_f32_forward_own_carry_matches_scanned_carry(segments):
     # Without saved states and with up to 8 segments the fp32 MFMA forward

@@ -48,7 +48,10 @@ def check(y, ref, what):
 
 
 RET_SHAPES = [(1, 1, 1, 64), (1, 2, 63, 64), (2, 1, 64, 64), (1, 1, 65, 64), (2, 3, 333, 64), (1, 2, 1000, 64),
-              (1, 1, 127, 128), (1, 2, 1100, 128)]
+              (1, 1, 127, 128), (1, 2, 1100, 128),
+              # nine segments: the decayed scans read a full batch of eight
+              # records and a partial one
+              (1, 1, 2600, 64)]
 
 
 @pytest.mark.parametrize("shape", RET_SHAPES)

@@ -61,6 +61,9 @@ STATE_CASES = [
     (2, 1, 90, 64, 64, "bf16", 0, 0.0),
     (1, 2, 700, 64, 64, "bf16", 300, -3.0),
     (1, 1, 1100, 128, 128, "bf16", 257, -3.0),
+    # ten segments: the scan from (S0, Z0) reads a full batch of eight
+    # records and a partial one
+    (1, 1, 2500, 64, 64, "bf16", 200, 0.0),
 ]
 
 
