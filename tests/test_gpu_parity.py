@@ -258,6 +258,38 @@ def test_long_bf16_workload():
     check_rows("out", f64(out[0, hi]), refs["out"], boundary_rows(w.N, -(-w.N // plan["segments"])), 2e-2)
 
 
+def test_long_bf16_backward():
+    # The long-sequence shape through the training backward (the workload is
+    # a forward; this is its backward at full size): the automatic plan, 32
+    # segments of 2048 tokens, the eight-wave D = 128 sweeps and the separate
+    # (R, r) aggregate pass.  2 of the 16 heads against the oracle, gradients
+    # within 4x the bf16 rounding of the exact ones, and the rows next to
+    # segment and chunk boundaries held against the others; the backward
+    # that reads the forward's saved prefix states (as a training step does)
+    # gives the same gradients bit for bit.
+    w = WORKLOADS["long_bf16"]
+    tq, tk, tv, tg = device_inputs(w.B, w.H, w.N, w.D, w.M, "bf16", seed=1, scale=1.0 / np.sqrt(w.D))
+    heads = [(0, 3), (0, 12)]
+    plan = la.resolve_plan("backward", w.B, w.H, w.N, w.D, w.M, True, "bf16")
+    assert plan == la.resolve_plan("forward", w.B, w.H, w.N, w.D, w.M, True, "bf16")
+    assert plan["kernel"] == 2 and plan["segments"] == 32
+    say(f"long-sequence backward: plan {plan}")
+    refs = {}
+    dq, dk, dv = check_backward(tq, tk, tv, tg, True, "bf16", heads=heads, floor_factor=4.0, refs=refs)
+    hi = [h for _, h in heads]
+    rows = boundary_rows(w.N, -(-w.N // plan["segments"]))
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        check_rows(n, f64(t[0, hi]), refs[n], rows, 2e-2)
+    saved = torch.empty(la.saved_bytes(w.B, w.H, w.N, w.D, w.M, True, "bf16"), dtype=torch.uint8, device=DEV)
+    out, den = la.forward(tq, tk, tv, causal=True, return_den=True, saved=saved)
+    g_saved = la.backward(tq, tk, tv, out, tg, den=den, causal=True, saved=saved)
+    torch.cuda.synchronize()
+    for n, a, b in (("dq", g_saved[0], dq), ("dk", g_saved[1], dk), ("dv", g_saved[2], dv)):
+        assert torch.equal(a, b), n
+    del tq, tk, tv, tg, dq, dk, dv, out, den, saved, g_saved
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_forward_largest_mfma_head(D):
     # The largest head the bf16 MFMA kernels take (2^31 bytes per tensor per
