@@ -364,3 +364,36 @@ def test_retention_saved_too_small_is_rejected():
         la.retention_forward(tq, tk, tv, tl, saved=short)
     with pytest.raises(la.LinAttnError, match="INVALID"):
         la.retention_backward(tq, tk, tv, tl, tg, saved=short)
+
+
+def test_retention_fwdbwd_workload():
+    # The benchmark's retention step at full size (B=8, H=16, N=8192,
+    # D=M=64, bf16, gates gamma_t ~ U(0.6, 1), automatic plan: 4 segments,
+    # the forward keeping its segment states for the backward), checked on 4
+    # heads spread over b and h against the oracle's recurrence and its
+    # backward.
+    from workloads import device_inputs
+
+    B, H, N, D = 8, 16, 8192, 64
+    tq, tk, tv, tg = device_inputs(B, H, N, D, D, "bf16", seed=2, scale=1.0 / np.sqrt(D))
+    gen = torch.Generator(device=DEV).manual_seed(3)
+    tl = torch.log(torch.rand(B, H, N, device=DEV, generator=gen) * 0.4 + 0.6)
+    assert la.resolve_plan("retention_backward", B, H, N, D, D, True, "bf16")["segments"] == 4
+    saved = torch.empty(la.retention_saved_bytes(B, H, N, D, D), dtype=torch.uint8, device=DEV)
+    y = la.retention_forward(tq, tk, tv, tl, saved=saved)
+    got = la.retention_backward(tq, tk, tv, tl, tg, saved=saved)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (2, 9), (5, 4), (7, 15)]
+    bi = [b for b, _ in heads]
+    hi = [h for _, h in heads]
+
+    def pick(t):
+        return f64(t[bi, hi])[None]
+
+    q64, k64, v64, g64, l64 = (pick(t) for t in (tq, tk, tv, tg, tl))
+    say(f"retention workload: {B}x{H}x{N} D={D}, heads {heads}")
+    check(y[bi, hi][None], ret.recurrent(q64, k64, v64, l64)[0], "workload forward")
+    want = ret.backward(q64, k64, v64, l64, g64)
+    check_grads([t[bi, hi][None] for t in got], want, "workload backward", q=tq[bi, hi][None])
+    del tq, tk, tv, tg, tl, saved, y, got
+    torch.cuda.empty_cache()
