@@ -97,11 +97,22 @@ __device__ __forceinline__ i16x8 phi8(i32x4 raw) {
   return pack8(x);
 }
 
+// Sum over the four 16-lane groups (lanes li, li+16, li+32, li+48), every
+// lane receiving it, with the gfx950 lane swaps instead of LDS permutes.
+// v_permlane16_swap(a, b) exchanges the odd 16-lane rows of a with the even
+// rows of b, v_permlane32_swap(a, b) the upper 32 lanes of a with the lower
+// 32 of b (checked on the hardware); with a = b = x, a + b is x plus its
+// lane ^ 16 (then lane ^ 32) partner, the pairs and order of two xor
+// shuffles, so the sums are the same bits.  The s_nop covers the wait a
+// permlane needs after a VALU write of its operands.
 __device__ __forceinline__ float shfl_sum_groups(float x) {
-  // sum over the four 16-lane groups (lanes li, li+16, li+32, li+48)
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
+  float a = x, b = x;
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  x = a + b;
+  a = x;
+  b = x;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return a + b;
 }
 
 // x from another lane of the same 16-lane row by a DPP control whose every
